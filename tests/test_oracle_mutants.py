@@ -1,0 +1,85 @@
+"""Plant plausible mistakes into copies of the CPU oracle and check the pins catch each.
+
+Every mutant is a textual edit of ``oracle/qmm_oracle.c`` compiled with gcc
+into a temporary directory; the pin checks then run against it.  A mutant
+that passes every pin would mean the pins leave that part of the oracle
+unchecked.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "qmm_oracle.c")
+
+# (id, original text, replacement): each is a mistake one could plausibly make.
+MUTANTS = [
+    ("round_half_away", "float t = rintf(v[i] / s) + (float)z;", "float t = roundf(v[i] / s) + (float)z;"),
+    ("no_zero_in_range", "float lo = 0.0f, hi = 0.0f;", "float lo = v[0], hi = v[0];"),
+    ("zero_point_sign", "float neg_lo = -lo;", "float neg_lo = lo;"),
+    ("levels_2pow_b", "const float qmax = (float)((1 << bits) - 1);", "const float qmax = (float)(1 << bits);"),
+    ("dequant_drops_zero", "float d = (float)((int)q[r * cols + c] - (int)zeros[gi]);",
+     "float d = (float)((int)q[r * cols + c]);"),
+    ("scale_zero_to_tiny", "if (s == 0.0f) s = 1.0f;", "if (s == 0.0f) s = 1e-8f;"),
+    ("clamp_before_zero", "float t = rintf(v[i] / s) + (float)z;",
+     "float t = rintf(v[i] / s); if (t < 0.0f) t = 0.0f; t += (float)z;"),
+    ("sym_levels", "const float qpos = (float)((1 << (bits - 1)) - 1);",
+     "const float qpos = (float)(1 << (bits - 1));"),
+    ("sym_no_floor", "if (amax < floor_) amax = floor_;", ""),
+    ("sym_round_trunc", "float t = rintf(v[i] / s);", "float t = truncf(v[i] / s);"),
+    ("pack_swapped_nibbles", "out[r * bytes + j] = (uint8_t)(lo | (hi << 4));",
+     "out[r * bytes + j] = (uint8_t)(hi | (lo << 4));"),
+    ("matmul_transposed", "acc += (double)a[i * k + t] * (double)b[j * k + t];",
+     "acc += (double)a[i * k + t] * (double)b[t * n + j % n];"),
+    ("matmul_f32_sum", "double acc = 0.0;", "float acc = 0.0f;"),
+    ("int8_wrong_operand", "s += (int64_t)qa[i * k + t] * (int64_t)qb[j * k + t];",
+     "s += (int64_t)qa[i * k + t] * (int64_t)qb[i * k + t];"),
+    ("rescale_missing_b", "y[i * n + j] = (double)acc[i * n + j] * (double)a[i] * (double)b[j];",
+     "y[i * n + j] = (double)acc[i * n + j] * (double)a[i];"),
+    ("smooth_inverted", "s[j] = num / den;", "s[j] = den / num;"),
+    ("smooth_no_floor", "float x = cx[j] < fl ? fl : cx[j];", "float x = cx[j];"),
+    ("smooth_div_instead_of_mul", "out[i * cols + j] = a[i * cols + j] * s[j];",
+     "out[i * cols + j] = a[i * cols + j] / s[j];"),
+    ("col_absmax_signed", "float v = fabsf(a[i * cols + j]);", "float v = a[i * cols + j];"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("mid,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(mid, old, new, source, tmp_path):
+    assert source.count(old) >= 1, f"mutation site for {mid} not found"
+    mutated = source.replace(old, new)
+    c_path = tmp_path / f"{mid}.c"
+    so_path = tmp_path / f"{mid}.so"
+    c_path.write_text(mutated)
+    subprocess.check_call(["gcc", *oracle.GCC_FLAGS, "-o", str(so_path), str(c_path), "-lm"])
+    saved = oracle._lib
+    try:
+        oracle._lib = None
+        good_lib = oracle.lib()          # installs argtypes on the real library
+        mutant = ctypes.CDLL(str(so_path))
+        for fn_name in ["oq_asym_quantize", "oq_asym_dequantize", "oq_sym_quantize", "oq_sym_dequantize",
+                        "oq_pack_nibbles", "oq_matmul_nt_f64", "oq_int8_matmul_nt", "oq_rescale_f64",
+                        "oq_col_absmax", "oq_smooth_factors", "oq_scale_columns_mul", "oq_scale_columns_div"]:
+            f = getattr(mutant, fn_name)
+            f.argtypes = getattr(good_lib, fn_name).argtypes
+            f.restype = ctypes.c_int
+        oracle._lib = mutant
+        failures = []
+        for check in oracle_pins.ALL_CHECKS:
+            try:
+                check()
+            except Exception as e:   # a failed assert, an oracle error status, a bad index
+                failures.append((check.__name__, type(e).__name__))
+        assert failures, f"mutant {mid} passed every pin"
+    finally:
+        oracle._lib = saved
