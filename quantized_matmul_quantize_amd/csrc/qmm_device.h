@@ -1,0 +1,214 @@
+// qmm_device.h -- device-side helpers shared by the gfx950 kernels of libqmm.
+//
+// Storage formats (fixed by the C-ABI in include/qmm.h):
+//  * INT4 codes: row-major [N, K/2] bytes; little-endian 32-bit word w of a
+//    row holds elements 8w..8w+7, element 8w+i in bits 4i..4i+3.
+//  * scales: fp32 [N, K/128]; zero-points: nibble-packed [N, ceil(G/2)] bytes,
+//    group 2j in the low nibble of byte j, group 2j+1 in the high nibble.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmm_internal.h"
+
+namespace qmm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 128;
+
+// ---- 16-byte global memory access ------------------------------------------
+// Streaming loads/stores use the nontemporal hint (data touched once).
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) { __builtin_nontemporal_store(v, (u32x4*)p); }
+
+// ---- 16-bit float <-> fp32 ------------------------------------------------
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ float f16lo_to_f32(uint32_t u) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
+}
+__device__ __forceinline__ float f16hi_to_f32(uint32_t u) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+// fp32 -> fp16 bits (hardware conversion, round to nearest even).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b);
+template <>
+__device__ __forceinline__ uint32_t pack2<QMM_BF16>(float a, float b) {
+  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<QMM_F16>(float a, float b) {
+  return f32_to_f16_bits(a) | (f32_to_f16_bits(b) << 16);
+}
+
+// Eight consecutive elements of a 16/32-bit float row as fp32.
+template <int DT>
+struct Vec8;
+template <>
+struct Vec8<QMM_BF16> {
+  static __device__ __forceinline__ void load(const void* p, float v[8]) {
+    const u32x4 u = ld16_nt(p);
+    v[0] = bf16lo_to_f32(u.x); v[1] = bf16hi_to_f32(u.x);
+    v[2] = bf16lo_to_f32(u.y); v[3] = bf16hi_to_f32(u.y);
+    v[4] = bf16lo_to_f32(u.z); v[5] = bf16hi_to_f32(u.z);
+    v[6] = bf16lo_to_f32(u.w); v[7] = bf16hi_to_f32(u.w);
+  }
+};
+template <>
+struct Vec8<QMM_F16> {
+  static __device__ __forceinline__ void load(const void* p, float v[8]) {
+    const u32x4 u = ld16_nt(p);
+    v[0] = f16lo_to_f32(u.x); v[1] = f16hi_to_f32(u.x);
+    v[2] = f16lo_to_f32(u.y); v[3] = f16hi_to_f32(u.y);
+    v[4] = f16lo_to_f32(u.z); v[5] = f16hi_to_f32(u.z);
+    v[6] = f16lo_to_f32(u.w); v[7] = f16hi_to_f32(u.w);
+  }
+};
+template <>
+struct Vec8<QMM_F32> {
+  static __device__ __forceinline__ void load(const void* p, float v[8]) {
+    const u32x4 a = ld16_nt(p);
+    const u32x4 b = ld16_nt(static_cast<const uint8_t*>(p) + 16);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  }
+};
+
+// ---- cross-lane reductions inside a row of 16 lanes (DPP) -------------------
+// quad_perm [1,0,3,2] = xor 1; [2,3,0,1] = xor 2; row_half_mirror pairs the
+// two quads of each half-row; row_mirror pairs the two halves of the row.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_min(float v) {
+  v = fminf(v, dpp_f<kDppXor1>(v));
+  v = fminf(v, dpp_f<kDppXor2>(v));
+  v = fminf(v, dpp_f<kDppHalfMirror>(v));
+  v = fminf(v, dpp_f<kDppMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return v;
+}
+
+// Full-wave sum, result valid in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  v = fmaxf(v, __shfl_xor(v, 32, kWave));
+  return v;
+}
+
+// ---- INT4 unpack -------------------------------------------------------------
+// A 32-bit code word holds elements e0..e7 (nibble i = element i).  The
+// kernels feed 16-bit pairs (e_i, e_{i+4}) to dot / MFMA instructions, with
+// the activations permuted the same way, so a sum over k is unchanged.
+// The pair is built by OR-ing the nibbles into the low mantissa bits of a
+// 16-bit float whose exponent puts the unit in the last place at 1:
+//   bf16 0x4300 = 128.0, so (0x4300 | q) = 128 + q exactly;
+//   fp16 0x6400 = 1024.0, so (0x6400 | q) = 1024 + q exactly.
+// The constant offset is removed per group as offset * sum(x).
+constexpr uint32_t kMagicBf16 = 0x43004300u;
+constexpr float kOffsetBf16 = 128.0f;
+constexpr uint32_t kMagicF16 = 0x64006400u;
+constexpr float kOffsetF16 = 1024.0f;
+
+template <uint32_t MAGIC>
+__device__ __forceinline__ void unpack_pairs(uint32_t w, uint32_t p[4]) {
+  p[0] = (w & 0x000F000Fu) | MAGIC;
+  p[1] = ((w >> 4) & 0x000F000Fu) | MAGIC;
+  p[2] = ((w >> 8) & 0x000F000Fu) | MAGIC;
+  p[3] = ((w >> 12) & 0x000F000Fu) | MAGIC;
+}
+
+// Activation 16-bit values x0..x7 held as 4 words [x0|x1] [x2|x3] [x4|x5]
+// [x6|x7] -> pair order [x0|x4] [x1|x5] [x2|x6] [x3|x7].
+__device__ __forceinline__ void permute_pairs(const uint32_t a[4], uint32_t p[4]) {
+  // v_perm_b32(hi_src, lo_src, sel): selector bytes 0-3 pick lo_src, 4-7 hi_src.
+  p[0] = __builtin_amdgcn_perm(a[2], a[0], 0x05040100u);  // [x0 | x4]
+  p[1] = __builtin_amdgcn_perm(a[2], a[0], 0x07060302u);  // [x1 | x5]
+  p[2] = __builtin_amdgcn_perm(a[3], a[1], 0x05040100u);  // [x2 | x6]
+  p[3] = __builtin_amdgcn_perm(a[3], a[1], 0x07060302u);  // [x3 | x7]
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c);
+template <>
+__device__ __forceinline__ float dot2<QMM_BF16>(uint32_t a, uint32_t b, float c) { return dot2_bf16(a, b, c); }
+template <>
+__device__ __forceinline__ float dot2<QMM_F16>(uint32_t a, uint32_t b, float c) { return dot2_f16(a, b, c); }
+
+template <int DT>
+struct Int4Magic;
+template <>
+struct Int4Magic<QMM_BF16> {
+  static constexpr uint32_t magic = kMagicBf16;
+  static constexpr float offset = kOffsetBf16;
+  static constexpr uint32_t one_pair = 0x3F803F80u;  // (1.0, 1.0)
+};
+template <>
+struct Int4Magic<QMM_F16> {
+  static constexpr uint32_t magic = kMagicF16;
+  static constexpr float offset = kOffsetF16;
+  static constexpr uint32_t one_pair = 0x3C003C00u;
+};
+
+__device__ __forceinline__ uint32_t zero_nibble(const uint8_t* zeros_row, int64_t g) {
+  uint32_t b = zeros_row[g >> 1];
+  return (g & 1) ? (b >> 4) : (b & 0xFu);
+}
+
+}  // namespace qmm

@@ -1,0 +1,238 @@
+// quantize.hip -- group-wise asymmetric INT4 quantization and dequantization.
+//
+// Method: "Quantization Explained: INT8, INT4, GPTQ and AWQ for LLMs", slides
+// "Scale and Zero-Point" and "Manual Group-Wise Quantizer" (per-group min/max,
+// s = (max - min) / 15, z = round(-min / s), q = clamp(round(w / s) + z, 0, 15));
+// "Quantization from Scratch: Scale, Zero-Point, GPTQ and AWQ", section "Scale
+// and zero-point" (w_hat = (q - z) s) and its round-to-nearest listing (a zero
+// scale becomes 1; clip after adding the zero-point).  The range is widened to
+// contain 0 so the zero-point is always a valid 4-bit code.
+//
+// Mapping: one wavefront quantizes a "chunk" of four consecutive groups of one
+// row (512 elements).  Each group is one DPP row of 16 lanes; a lane owns 8
+// consecutive elements, loads them with one 16-byte (bf16/fp16) or two
+// 16-byte (fp32) loads and stores their 8 codes as one 32-bit word, so a
+// wavefront reads 1 KiB (2 KiB) and writes 256 B, both contiguous.
+
+#include "qmm_device.h"
+
+namespace qmm {
+namespace {
+
+constexpr float kLevels = 15.0f;                 // 2^4 - 1
+constexpr float kTieMargin = 0.5f - 0x1p-16f;    // see quantize8
+
+// Codes of 8 elements for one group with scale s and zero-point zf (an
+// integer-valued float), bit-identical to clamp(rint(fl32(v / s)) + z, 0, 15).
+//
+// Fast path: t = fma(v, rcp(s), z).  With v_rcp_f32 accurate to 1 ulp and
+// |v / s| <= 15 (v lies in the group's range), |t - (v / s + z)| < 3e-6.  When
+// t is at least 2^-16 away from a half-integer, v / s + z (and therefore its
+// fp32 rounding, whose error is below 1e-6 at this magnitude) lies strictly
+// inside the same rounding interval, so rint(t) is the exact answer.  Any lane
+// with a value inside the 2^-16 band, or a scale outside [2^-100, 2^100]
+// (where rcp could lose accuracy), recomputes with the correctly rounded
+// division; for Gaussian weights that is roughly one element in 30 000.
+__device__ __forceinline__ uint32_t quantize8(const float v[8], float s, float zf) {
+  const float r = __builtin_amdgcn_rcpf(s);
+  float k[8];
+  float dmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = fmaf(v[i], r, zf);
+    k[i] = rintf(t);
+    dmax = fmaxf(dmax, fabsf(t - k[i]));
+  }
+  const bool fast = (s >= 0x1p-100f) && (s <= 0x1p100f) && (dmax <= kTieMargin);
+  if (!fast) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) k[i] = rintf(v[i] / s) + zf;
+  }
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float c = __builtin_amdgcn_fmed3f(k[i], 0.0f, kLevels);
+    word |= static_cast<uint32_t>(c) << (4 * i);
+  }
+  return word;
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_g128_kernel(const uint8_t* __restrict__ w, int64_t K, int64_t G,
+                                                            int64_t chunks_per_row, int64_t total_chunks,
+                                                            uint32_t* __restrict__ codes,
+                                                            float* __restrict__ scales,
+                                                            uint8_t* __restrict__ zeros, int64_t zeros_row_bytes) {
+  constexpr int kElemBytes = DT == QMM_F32 ? 4 : 2;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gl = lane >> 4;     // group of the chunk handled by this DPP row
+  const int part = lane & 15;   // 8-element slice of the group
+  const int64_t waves_per_block = blockDim.x / kWave;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * waves_per_block;
+
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * waves_per_block + (threadIdx.x / kWave); c < total_chunks;
+       c += nwaves) {
+    const int64_t n = c / chunks_per_row;
+    const int64_t g = (c - n * chunks_per_row) * 4 + gl;
+    const bool active = g < G;
+    const int64_t e = n * K + g * kGroup + part * 8;   // first element of this lane
+
+    float v[8];
+    if (active) {
+      Vec8<DT>::load(w + e * kElemBytes, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    // Group range, widened to contain 0.
+    float lo = fminf(fminf(fminf(0.0f, v[0]), fminf(v[1], v[2])), fminf(fminf(v[3], v[4]), fminf(v[5], v[6])));
+    float hi = fmaxf(fmaxf(fmaxf(0.0f, v[0]), fmaxf(v[1], v[2])), fmaxf(fmaxf(v[3], v[4]), fmaxf(v[5], v[6])));
+    lo = fminf(lo, v[7]);
+    hi = fmaxf(hi, v[7]);
+    lo = row16_min(lo);
+    hi = row16_max(hi);
+
+    float s = (hi - lo) / kLevels;      // correctly rounded fp32 division
+    if (s == 0.0f) s = 1.0f;
+    const float zf = rintf(-lo / s);    // in [0, 15] because lo <= 0 <= hi
+
+    const uint32_t word = quantize8(v, s, zf);
+    // Zero-point of the odd group of each pair, fetched from the next DPP row.
+    const float z_next = __shfl_down(zf, 16, kWave);
+    if (active) {
+      codes[e >> 3] = word;
+      if (part == 0) {
+        scales[n * G + g] = s;
+        if ((gl & 1) == 0) {
+          const uint32_t zo = (g + 1 < G) ? static_cast<uint32_t>(z_next) : 0u;
+          zeros[n * zeros_row_bytes + (g >> 1)] = static_cast<uint8_t>(static_cast<uint32_t>(zf) | (zo << 4));
+        }
+      }
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void dequantize_g128_kernel(const uint32_t* __restrict__ codes,
+                                                              const float* __restrict__ scales,
+                                                              const uint8_t* __restrict__ zeros, int64_t K,
+                                                              int64_t G, int64_t chunks_per_row,
+                                                              int64_t total_chunks, int64_t zeros_row_bytes,
+                                                              uint8_t* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gl = lane >> 4;
+  const int part = lane & 15;
+  const int64_t waves_per_block = blockDim.x / kWave;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * waves_per_block;
+
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * waves_per_block + (threadIdx.x / kWave); c < total_chunks;
+       c += nwaves) {
+    const int64_t n = c / chunks_per_row;
+    const int64_t g = (c - n * chunks_per_row) * 4 + gl;
+    if (g >= G) continue;
+    const int64_t e = n * K + g * kGroup + part * 8;
+    const uint32_t word = __builtin_nontemporal_load(codes + (e >> 3));
+    const float s = scales[n * G + g];
+    const int z = static_cast<int>(zero_nibble(zeros + n * zeros_row_bytes, g));
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = static_cast<int>((word >> (4 * i)) & 0xFu);
+      v[i] = static_cast<float>(q - z) * s;   // one fp32 rounding
+    }
+    if constexpr (DT == QMM_F32) {
+      uint8_t* o = out + e * 4;
+      st16_nt(o, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+      st16_nt(o + 16, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
+    } else {
+      st16_nt(out + e * 2, u32x4{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]), pack2<DT>(v[4], v[5]),
+                                 pack2<DT>(v[6], v[7])});
+    }
+  }
+}
+
+// Persistent grid: enough 256-thread blocks to fill every CU several times,
+// each wavefront striding over chunks.
+int64_t chunk_grid(int64_t total_chunks) {
+  const int64_t blocks = ceil_div(total_chunks, 4);
+  const int64_t cap = static_cast<int64_t>(device_cus()) * 8;
+  return blocks < cap ? blocks : cap;
+}
+
+int check_w4_args(const void* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+                  int bits) {
+  if (!codes || !scales || !zeros) return QMM_EINVAL;
+  if (N <= 0 || K <= 0 || group <= 0 || K % group != 0) return QMM_EINVAL;
+  if (bits != 4 || group != kGroup) return QMM_EUNSUPPORTED;
+  if (!aligned(codes, 16) || !aligned(scales, 4)) return QMM_EALIGN;
+  return QMM_OK;
+}
+
+}  // namespace
+}  // namespace qmm
+
+using namespace qmm;
+
+extern "C" int quantize_groupwise(const void* W, int w_dtype, int64_t N, int64_t K, int group, int bits,
+                                  uint8_t* codes, float* scales, uint8_t* zeros, void* stream) {
+  if (!W) return QMM_EINVAL;
+  if (w_dtype != QMM_F32 && w_dtype != QMM_BF16 && w_dtype != QMM_F16)
+    return w_dtype == QMM_I32 ? QMM_EUNSUPPORTED : QMM_EINVAL;
+  int st = check_w4_args(codes, scales, zeros, N, K, group, bits);
+  if (st != QMM_OK) return st;
+  if (!aligned(W, 16)) return QMM_EALIGN;
+
+  const int64_t G = K / kGroup;
+  const int64_t chunks_per_row = ceil_div(G, 4);
+  const int64_t total = N * chunks_per_row;
+  const int64_t zrow = ceil_div(G, 2);
+  const dim3 grid(static_cast<unsigned>(chunk_grid(total)));
+  const dim3 block(256);
+  hipStream_t s = as_stream(stream);
+  const uint8_t* w = static_cast<const uint8_t*>(W);
+  uint32_t* cw = reinterpret_cast<uint32_t*>(codes);
+  switch (w_dtype) {
+    case QMM_BF16:
+      quantize_g128_kernel<QMM_BF16><<<grid, block, 0, s>>>(w, K, G, chunks_per_row, total, cw, scales, zeros, zrow);
+      break;
+    case QMM_F16:
+      quantize_g128_kernel<QMM_F16><<<grid, block, 0, s>>>(w, K, G, chunks_per_row, total, cw, scales, zeros, zrow);
+      break;
+    default:
+      quantize_g128_kernel<QMM_F32><<<grid, block, 0, s>>>(w, K, G, chunks_per_row, total, cw, scales, zeros, zrow);
+      break;
+  }
+  return launch_status();
+}
+
+extern "C" int dequantize(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                          int group, int bits, void* W_hat, int out_dtype, void* stream) {
+  if (!W_hat) return QMM_EINVAL;
+  if (out_dtype != QMM_F32 && out_dtype != QMM_BF16 && out_dtype != QMM_F16)
+    return out_dtype == QMM_I32 ? QMM_EUNSUPPORTED : QMM_EINVAL;
+  int st = check_w4_args(codes, scales, zeros, N, K, group, bits);
+  if (st != QMM_OK) return st;
+  if (!aligned(W_hat, 16)) return QMM_EALIGN;
+
+  const int64_t G = K / kGroup;
+  const int64_t chunks_per_row = ceil_div(G, 4);
+  const int64_t total = N * chunks_per_row;
+  const int64_t zrow = ceil_div(G, 2);
+  const dim3 grid(static_cast<unsigned>(chunk_grid(total)));
+  const dim3 block(256);
+  hipStream_t s = as_stream(stream);
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes);
+  uint8_t* o = static_cast<uint8_t*>(W_hat);
+  switch (out_dtype) {
+    case QMM_BF16:
+      dequantize_g128_kernel<QMM_BF16><<<grid, block, 0, s>>>(cw, scales, zeros, K, G, chunks_per_row, total, zrow, o);
+      break;
+    case QMM_F16:
+      dequantize_g128_kernel<QMM_F16><<<grid, block, 0, s>>>(cw, scales, zeros, K, G, chunks_per_row, total, zrow, o);
+      break;
+    default:
+      dequantize_g128_kernel<QMM_F32><<<grid, block, 0, s>>>(cw, scales, zeros, K, G, chunks_per_row, total, zrow, o);
+      break;
+  }
+  return launch_status();
+}

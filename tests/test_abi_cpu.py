@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: every declared symbol is exported, the host-only
+entry points compute what they state, and argument errors are reported before
+any HIP call (no kernel is ever launched from here: every call below fails
+validation, and the fake device pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_matmul_quantize_amd as qmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+OK, EINVAL, EUNSUP, EALIGN, EWS, EHIP, ERANGE = 0, -1, -2, -3, -4, -5, -6
+P = 0x7F0000000000          # 16-byte aligned stand-in for a device pointer
+MIS = P + 2                 # misaligned
+BF16, F16, F32, I32 = qmm.BF16, qmm.F16, qmm.F32, qmm.I32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["quantize_groupwise", "dequantize", "w4a16_gemv", "w4a16_gemm", "smooth_quant_w8a8_gemm"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(qmm.library_path)
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    dyn = subprocess.run(["nm", "-D", "--defined-only", qmm.library_path], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in dyn.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, f"{n} is not an unmangled exported symbol"
+
+
+def test_binding_covers_every_symbol():
+    assert set(declared_functions()) <= set(qmm._SIGS)
+
+
+def test_status_strings_and_version():
+    lib = qmm.lib()
+    for st in [OK, EINVAL, EUNSUP, EALIGN, EWS, EHIP, ERANGE, -99]:
+        assert lib.qmm_status_string(st)
+    assert lib.qmm_status_string(EALIGN).startswith(b"QMM_EALIGN")
+    assert lib.qmm_version() >= 10000
+
+
+def test_w4_sizes():
+    assert qmm.w4_sizes(28672, 8192) == (28672 * 4096, 28672 * 64 * 4, 28672 * 32)
+    assert qmm.w4_sizes(3, 384) == (3 * 192, 3 * 3 * 4, 3 * 2)
+    with pytest.raises(qmm.QmmError):
+        qmm.w4_sizes(4, 100)
+    lib = qmm.lib()
+    assert lib.qmm_w4_sizes(0, 128, 128, None, None, None) == EINVAL
+    assert lib.qmm_w4_sizes(4, 128, 0, None, None, None) == EINVAL
+
+
+def test_w4_sizes_match_storage_example():
+    # 0.5 B per weight + per-group scale and 4-bit zero-point; with the page's
+    # 16-bit scale a 70B model is ~36.4 GB ("How quantization works", Exercises 2).
+    n, k = 8192, 8192
+    c, s, z = qmm.w4_sizes(n, k)
+    per_param_fp16_scale = (c + s / 2 + z) / (n * k)
+    assert abs(70e9 * per_param_fp16_scale / 1e9 - 36.4) < 0.05
+
+
+def test_sq_workspace_bytes():
+    lib = qmm.lib()
+    assert lib.sq_workspace_bytes(2048, 4096) == 2048 * 4096 + 2048 * 4
+    assert lib.sq_workspace_bytes(3, 64) == 256 + 12
+    assert lib.sq_workspace_bytes(0, 64) == 0
+
+
+def test_quantize_argument_errors():
+    f = qmm.lib().quantize_groupwise
+    assert f(None, BF16, 4, 256, 128, 4, P, P, P, None) == EINVAL
+    assert f(P, BF16, 4, 256, 128, 4, None, P, P, None) == EINVAL
+    assert f(P, BF16, 0, 256, 128, 4, P, P, P, None) == EINVAL
+    assert f(P, BF16, 4, 200, 128, 4, P, P, P, None) == EINVAL          # K % group
+    assert f(P, 9, 4, 256, 128, 4, P, P, P, None) == EINVAL             # bad dtype
+    assert f(P, I32, 4, 256, 128, 4, P, P, P, None) == EUNSUP
+    assert f(P, BF16, 4, 256, 128, 3, P, P, P, None) == EUNSUP          # bits
+    assert f(P, BF16, 4, 256, 64, 4, P, P, P, None) == EUNSUP           # group
+    assert f(MIS, BF16, 4, 256, 128, 4, P, P, P, None) == EALIGN
+    assert f(P, BF16, 4, 256, 128, 4, MIS, P, P, None) == EALIGN
+
+
+def test_dequantize_argument_errors():
+    f = qmm.lib().dequantize
+    assert f(P, P, P, 4, 256, 128, 4, None, F32, None) == EINVAL
+    assert f(P, P, P, 4, 256, 128, 4, P, I32, None) == EUNSUP
+    assert f(P, P, P, 4, 256, 128, 4, MIS, F32, None) == EALIGN
+    assert f(P, P, P, -1, 256, 128, 4, P, F32, None) == EINVAL
+
+
+def test_gemv_gemm_argument_errors():
+    gemv = qmm.lib().w4a16_gemv
+    gemm = qmm.lib().w4a16_gemm
+    assert gemv(P, P, P, 8, 256, 128, None, BF16, 1, P, BF16, None) == EINVAL
+    assert gemv(P, P, P, 8, 256, 128, P, BF16, 9, P, BF16, None) == EUNSUP    # B > 8
+    assert gemv(P, P, P, 8, 256, 128, P, BF16, 0, P, BF16, None) == EINVAL
+    assert gemv(P, P, P, 8, 256, 128, P, F32, 1, P, F32, None) == EUNSUP      # fp32 activations
+    assert gemv(P, P, P, 8, 256, 128, P, BF16, 1, P, F16, None) == EUNSUP     # mixed 16-bit types
+    assert gemv(P, P, P, 8, 256, 64, P, BF16, 1, P, BF16, None) == EUNSUP
+    assert gemv(P, P, P, 8, 256, 128, MIS, BF16, 1, P, BF16, None) == EALIGN
+    assert gemm(P, P, P, 8, 256, 128, P, F16, 4, P, F16, None) == EUNSUP      # GEMM takes bf16
+    assert gemm(P, P, P, 8, 300, 128, P, BF16, 4, P, BF16, None) == EINVAL
+    assert gemm(P, P, P, 8, 256, 128, P, BF16, 0, P, BF16, None) == EINVAL
+
+
+def test_w8a8_argument_errors():
+    lib = qmm.lib()
+    assert lib.sq_int8_gemm(P, P, P, P, 4, 4, 131072, P, BF16, None) == ERANGE   # int32 bound
+    assert lib.sq_int8_gemm(P, P, P, P, 4, 4, 131136, P, BF16, None) == ERANGE
+    assert lib.sq_int8_gemm(P, P, P, P, 4, 4, 100, P, BF16, None) == EUNSUP      # K % 64
+    assert lib.sq_int8_gemm(P, None, P, P, 4, 4, 128, P, BF16, None) == EINVAL   # scale needed
+    assert lib.sq_int8_gemm(P, P, P, P, 4, 4, 128, P, F16, None) == EUNSUP
+    assert lib.sq_int8_gemm(MIS, P, P, P, 4, 4, 128, P, I32, None) == EALIGN
+    assert lib.sq_quantize_weight(P, BF16, None, 4, 100, P, P, None) == EUNSUP
+    assert lib.sq_quantize_weight(P, I32, None, 4, 128, P, P, None) == EUNSUP
+    assert lib.sq_quantize_activation(None, BF16, None, 4, 128, P, P, None) == EINVAL
+    assert lib.sq_quantize_activation(P, BF16, P + 1, 4, 128, P, P, None) == EALIGN
+    assert lib.sq_smooth_factors(P, BF16, 4, P, BF16, 4, 128, ctypes.c_float(1.5), P, P, P, None) == EINVAL
+    assert lib.sq_smooth_factors(P, BF16, 4, P, BF16, 4, 100, ctypes.c_float(0.5), P, P, P, None) == EUNSUP
+    sq = lib.smooth_quant_w8a8_gemm
+    need = lib.sq_workspace_bytes(4, 128)
+    assert sq(P, BF16, None, P, P, 4, 4, 128, P, BF16, None, need, None) == EWS
+    assert sq(P, BF16, None, P, P, 4, 4, 128, P, BF16, P, need - 1, None) == EWS
+    assert sq(P, BF16, None, P, P, 4, 4, 128, P, BF16, MIS, need, None) == EWS
+    assert sq(P, BF16, None, P, P, 4, 4, 131136, P, BF16, P, 10**9, None) == ERANGE
+
+
+def test_binding_raises_qmm_error():
+    with pytest.raises(qmm.QmmError) as e:
+        qmm._call("sq_int8_gemm", P, P, P, P, 4, 4, 131136, P, BF16, None)
+    assert e.value.status == ERANGE
+    assert "QMM_ERANGE" in str(e.value)

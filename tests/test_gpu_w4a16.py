@@ -1,0 +1,136 @@
+"""GPU parity: W4A16 GEMV / GEMM against the oracle's fp64 product with the dequantized weights."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_matmul_quantize_amd as qmm
+import workloads
+from gpu_util import assert_close, note, random_w4
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def upload_w4(q, s, z):
+    return (torch.from_numpy(oracle.pack_nibbles(q)).to(DEV), torch.from_numpy(np.ascontiguousarray(s)).to(DEV),
+            torch.from_numpy(oracle.pack_nibbles(z)).to(DEV))
+
+
+def gemv_case(q, s, z, x_cpu, ydt, what, gemm=False, rows=None):
+    codes, scales, zeros = upload_w4(q, s, z)
+    note(f"{'w4a16_gemm' if gemm else 'w4a16_gemv'} {what} N={q.shape[0]} K={q.shape[1]} "
+         f"B={x_cpu.shape[0]} x={x_cpu.dtype} y={ydt}")
+    xd = x_cpu.to(DEV)
+    fn = qmm.w4a16_gemm if gemm else qmm.w4a16_gemv
+    y = fn(codes, scales, zeros, xd, out_dtype=ydt)
+    torch.cuda.synchronize()
+    xf = x_cpu.float().numpy()
+    if rows is None:
+        ref = oracle.w4a16_reference(xf, q, s, z)
+        return assert_close(y.cpu(), ref, what)
+    ref = oracle.w4a16_reference(xf, q[rows], s[rows], z[rows])
+    return assert_close(y.cpu()[:, rows], ref, what)
+
+
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+@pytest.mark.parametrize("ysame", [True, False], ids=["y=x", "y=f32"])
+@pytest.mark.parametrize("B", [1, 2, 3, 8])
+@pytest.mark.parametrize("shape", workloads.shapes_for_parity(), ids=lambda s: f"{s[0]}x{s[1]}")
+def test_gemv_small(xdt, ysame, B, shape):
+    n, k = shape
+    q, s, z = random_w4(n, k, seed=n * 31 + k + B)
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(77, n + B), (B, k), 1.0), xdt)
+    gemv_case(q, s, z, x, TDT[xdt] if ysame else torch.float32, f"small {xdt}")
+
+
+def test_gemv_one_row_one_group():
+    q, s, z = random_w4(1, 128, seed=1)
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(1, 1), (1, 128), 1.0), "bf16")
+    gemv_case(q, s, z, x, torch.float32, "1x128")
+
+
+def test_gemv_extreme_codes():
+    # every code and zero-point at the ends of the range, large activations
+    n, k = 40, 1024
+    q = np.where(np.arange(n * k).reshape(n, k) % 3 == 0, 15, 0).astype(np.uint8)
+    z = np.tile(np.array([0, 15], np.uint8), (n, k // 256))
+    s = np.full((n, k // 128), 0.5, np.float32)
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(3, 3), (8, k), 100.0), "bf16")
+    gemv_case(q, s, z, x[:1], torch.float32, "extreme B=1")
+    gemv_case(q, s, z, x, torch.float32, "extreme B=8")
+
+
+def quantized(wl, index):
+    w, _ = workloads.weight(wl, index)
+    q, s, z = oracle.asym_quantize(w.float().numpy())
+    return q, s, z
+
+
+@pytest.mark.parametrize("name,index,B", [("tiny", 0, 1), ("llama7b", 0, 1), ("llama7b", 1, 1),
+                                          ("mlp70b", 0, 1), ("mlp70b", 1, 1), ("mlp70b", 0, 8), ("mlp70b", 1, 8)])
+def test_gemv_full_size(name, index, B):
+    wl = workloads.WORKLOADS[name]
+    q, s, z = quantized(wl, index)
+    n, k = q.shape
+    x = workloads.activations(wl, B, k, salt=index)
+    rows = None if B == 1 else np.sort(workloads.rng(50, n).choice(n, 2048, replace=False))
+    ydt = torch.float16 if wl.x_dtype == "f16" else torch.bfloat16
+    gemv_case(q, s, z, x, torch.float32, f"{name}[{index}] B={B} f32", rows=rows)
+    gemv_case(q, s, z, x, ydt, f"{name}[{index}] B={B} 16-bit", rows=rows)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 64, 100, 256])
+@pytest.mark.parametrize("shape", [(3, 384), (129, 2176), (300, 1024)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_gemm_small(M, shape):
+    n, k = shape
+    q, s, z = random_w4(n, k, seed=M * 13 + n)
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(78, M + n), (M, k), 1.0), "bf16")
+    gemv_case(q, s, z, x, torch.float32, f"gemm small M={M}", gemm=True)
+    gemv_case(q, s, z, x, torch.bfloat16, f"gemm small M={M} bf16", gemm=True)
+
+
+@pytest.mark.parametrize("M", [16, 64, 256])
+def test_gemm_full_size(M):
+    wl = workloads.WORKLOADS["gemm"]
+    q, s, z = quantized(wl, 0)
+    n, k = q.shape
+    x = workloads.activations(wl, M, k)
+    rows = np.sort(workloads.rng(51, M).choice(n, 1024, replace=False))
+    gemv_case(q, s, z, x, torch.bfloat16, f"gemm 14336x4096 M={M}", gemm=True, rows=rows)
+    gemv_case(q, s, z, x, torch.float32, f"gemm 14336x4096 M={M} f32", gemm=True, rows=rows)
+
+
+def test_gemm_m1_equals_gemv():
+    wl = workloads.WORKLOADS["llama7b"]
+    q, s, z = random_w4(257, 4224, seed=4)
+    codes, scales, zeros = upload_w4(q, s, z)
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(5, 5), (1, 4224), 1.0), "bf16").to(DEV)
+    note("gemm M=1 vs gemv")
+    a = qmm.w4a16_gemv(codes, scales, zeros, x, out_dtype=torch.float32).cpu().numpy()
+    b = qmm.w4a16_gemm(codes, scales, zeros, x, out_dtype=torch.float32).cpu().numpy()
+    assert np.allclose(a, b, rtol=1e-5, atol=1e-5 * np.abs(a).max())
+
+
+def test_gemv_gemm_deterministic():
+    q, s, z = random_w4(4096, 4096, seed=9)
+    codes, scales, zeros = upload_w4(q, s, z)
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(6, 6), (64, 4096), 1.0), "bf16").to(DEV)
+    note("determinism gemv/gemm 4096x4096")
+    for fn, xx in [(qmm.w4a16_gemv, x[:1]), (qmm.w4a16_gemv, x[:8]), (qmm.w4a16_gemm, x)]:
+        a = fn(codes, scales, zeros, xx, out_dtype=torch.float32).cpu()
+        b = fn(codes, scales, zeros, xx, out_dtype=torch.float32).cpu()
+        assert torch.equal(a, b)
+
+
+def test_end_to_end_quantize_then_gemv():
+    # GPU quantizer output feeds the GPU GEMV; the oracle does both steps itself.
+    wl = workloads.WORKLOADS["llama7b"]
+    w, _ = workloads.weight(wl, 1)
+    x = workloads.activations(wl, 1, w.shape[1])
+    note("end-to-end quantize + gemv 11008x4096")
+    codes, scales, zeros = qmm.quantize_groupwise(w.to(DEV))
+    y = qmm.w4a16_gemv(codes, scales, zeros, x.to(DEV), out_dtype=torch.float32)
+    q, s, z = oracle.asym_quantize(w.float().numpy())
+    assert_close(y.cpu(), oracle.w4a16_reference(x.float().numpy(), q, s, z), "end-to-end")

@@ -1,0 +1,145 @@
+"""GPU parity: SmoothQuant W8A8 against the oracle (codes and scales bit for bit,
+int32 accumulators exact, rescaled outputs within the stated tolerance)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_matmul_quantize_amd as qmm
+import workloads
+from gpu_util import assert_close, bits_equal, first_diff, note
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def sq_inputs(m, k, n, xdt="bf16", wdt="bf16", seed=0):
+    wl = workloads.WORKLOADS["smoothquant"]
+    if seed == 0 and (m, k, n) == (2048, 4096, 4096):
+        x, _ = workloads.sq_activations(wl, m, k)
+        w, _ = workloads.weight(wl, 0)
+        return x.to(TDT[xdt]) if xdt != "bf16" else x, w.to(TDT[wdt]) if wdt != "bf16" else w
+    x = workloads.gaussian(workloads.rng(400 + seed, m), (m, k), 1.0)
+    workloads.plant_scale_columns(x, workloads.rng(401 + seed, k), min(6, k), 50.0, 100.0)
+    w = workloads.gaussian(workloads.rng(402 + seed, n), (n, k), 0.02)
+    return workloads.to_dtype(x, xdt), workloads.to_dtype(w, wdt)
+
+
+SMALL = [(1, 64, 1), (37, 192, 50), (130, 320, 129), (256, 1024, 300)]
+
+
+@pytest.mark.parametrize("mkn", SMALL + [(2048, 4096, 4096)], ids=lambda t: "x".join(map(str, t)))
+def test_smooth_factors(mkn):
+    m, k, n = mkn
+    x, w = sq_inputs(m, k, n)
+    note(f"sq_smooth_factors M={m} K={k} N={n}")
+    s, cx, cw = qmm.sq_smooth_factors(x.to(DEV), w.to(DEV), 0.5)
+    rcx, rcw = oracle.col_absmax(x.float().numpy()), oracle.col_absmax(w.float().numpy())
+    rs = oracle.smooth_factors(rcx, rcw, 0.5)
+    assert bits_equal(cx.cpu().numpy(), rcx), first_diff(cx.cpu().numpy(), rcx)
+    assert bits_equal(cw.cpu().numpy(), rcw), first_diff(cw.cpu().numpy(), rcw)
+    assert bits_equal(s.cpu().numpy(), rs), first_diff(s.cpu().numpy(), rs)
+
+
+def test_smooth_factors_other_alpha_and_dtypes():
+    x, w = sq_inputs(64, 256, 96, "f32", "f16", seed=3)
+    note("sq_smooth_factors alpha=0.75 f32/f16")
+    s, cx, cw = qmm.sq_smooth_factors(x.to(DEV), w.to(DEV), 0.75)
+    rs = oracle.smooth_factors(oracle.col_absmax(x.float().numpy()), oracle.col_absmax(w.float().numpy()), 0.75)
+    # powf is not correctly rounded on either side: a few ulps
+    assert np.allclose(s.cpu().numpy(), rs, rtol=4e-7 * 8, atol=0)
+
+
+@pytest.mark.parametrize("smoothed", [True, False])
+@pytest.mark.parametrize("mkn", SMALL + [(2048, 4096, 4096)], ids=lambda t: "x".join(map(str, t)))
+def test_quantize_weight_and_activation(mkn, smoothed):
+    m, k, n = mkn
+    x, w = sq_inputs(m, k, n, seed=1)
+    xf, wf = x.float().numpy(), w.float().numpy()
+    rs = oracle.smooth_factors(oracle.col_absmax(xf), oracle.col_absmax(wf), 0.5) if smoothed else None
+    sd = torch.from_numpy(rs).to(DEV) if smoothed else None
+    note(f"sq_quantize_weight/activation M={m} K={k} N={n} smooth={smoothed}")
+    qw, b = qmm.sq_quantize_weight(w.to(DEV), sd)
+    qx, a = qmm.sq_quantize_activation(x.to(DEV), sd)
+    rqw, rb = oracle.sq_quantize_weight(wf, rs)
+    rqx, ra = oracle.sq_quantize_activation(xf, rs)
+    assert bits_equal(b.cpu().numpy(), rb), first_diff(b.cpu().numpy(), rb)
+    assert bits_equal(qw.cpu().numpy(), rqw), first_diff(qw.cpu().numpy(), rqw)
+    assert bits_equal(a.cpu().numpy(), ra), first_diff(a.cpu().numpy(), ra)
+    assert bits_equal(qx.cpu().numpy(), rqx), first_diff(qx.cpu().numpy(), rqx)
+
+
+def test_quantize_activation_long_rows_and_zero_row():
+    # rows longer than the register-resident path (second pass re-reads) and an all-zero row
+    x = workloads.gaussian(workloads.rng(9, 9), (5, 8192), 1.0)
+    x[2] = 0.0
+    xb = workloads.to_dtype(x, "bf16")
+    note("sq_quantize_activation 5x8192 with a zero row")
+    qx, a = qmm.sq_quantize_activation(xb.to(DEV), None)
+    rqx, ra = oracle.sq_quantize_activation(xb.float().numpy(), None)
+    assert bits_equal(a.cpu().numpy(), ra) and bits_equal(qx.cpu().numpy(), rqx)
+
+
+@pytest.mark.parametrize("mnk", [(1, 1, 64), (5, 7, 128), (130, 129, 320), (128, 128, 64), (300, 257, 1024)],
+                         ids=lambda t: "x".join(map(str, t)))
+def test_int8_gemm_exact(mnk):
+    m, n, k = mnk
+    g = np.random.Generator(np.random.PCG64(m * 1000 + n))
+    qa = g.integers(-128, 128, size=(m, k)).astype(np.int8)
+    qb = g.integers(-128, 128, size=(n, k)).astype(np.int8)
+    note(f"sq_int8_gemm int32 M={m} N={n} K={k}")
+    acc = qmm.sq_int8_gemm(torch.from_numpy(qa).to(DEV), None, torch.from_numpy(qb).to(DEV), None,
+                           out_dtype=torch.int32)
+    ref = oracle.int8_matmul_nt(qa, qb)
+    assert np.array_equal(acc.cpu().numpy(), ref), first_diff(acc.cpu().numpy(), ref)
+
+
+def test_int8_gemm_extremes():
+    # all -128 x -128 at the largest K the library accepts: the sums reach
+    # 128 * 128 * K = 2146435072, just inside int32
+    m, n, k = 16, 16, 131008
+    qa = np.full((m, k), -128, np.int8)
+    qb = np.full((n, k), -128, np.int8)
+    qb[1] = 127
+    note("sq_int8_gemm extremes K=131008")
+    acc = qmm.sq_int8_gemm(torch.from_numpy(qa).to(DEV), None, torch.from_numpy(qb).to(DEV), None,
+                           out_dtype=torch.int32).cpu().numpy()
+    assert int(acc[0, 0]) == 128 * 128 * k == 2146435072
+    assert int(acc[3, 1]) == -128 * 127 * k
+
+
+@pytest.mark.parametrize("ydt", ["bf16", "f32"])
+@pytest.mark.parametrize("mkn", SMALL + [(2048, 4096, 4096)], ids=lambda t: "x".join(map(str, t)))
+def test_w8a8_pipeline(mkn, ydt):
+    m, k, n = mkn
+    x, w = sq_inputs(m, k, n, seed=2)
+    xf, wf = x.float().numpy(), w.float().numpy()
+    xd, wd = x.to(DEV), w.to(DEV)
+    note(f"smooth_quant_w8a8_gemm M={m} K={k} N={n} y={ydt}")
+    s, _, _ = qmm.sq_smooth_factors(xd, wd, 0.5)
+    qw, b = qmm.sq_quantize_weight(wd, s)
+    y = qmm.smooth_quant_w8a8_gemm(xd, s, qw, b, out_dtype=TDT[ydt])
+    acc = qmm.sq_int8_gemm(*qmm.sq_quantize_activation(xd, s), qw, b, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    rs = oracle.smooth_factors(oracle.col_absmax(xf), oracle.col_absmax(wf), 0.5)
+    rqw, rb = oracle.sq_quantize_weight(wf, rs)
+    rows = np.arange(m) if m <= 256 else np.sort(workloads.rng(60, m).choice(m, 96, replace=False))
+    rqx, ra = oracle.sq_quantize_activation(xf[rows], rs)
+    racc = oracle.int8_matmul_nt(rqx, rqw)
+    assert np.array_equal(acc.cpu().numpy()[rows], racc)
+    ref = oracle.rescale_f64(racc, ra, rb)
+    assert_close(y.cpu()[rows], ref, f"w8a8 {mkn} {ydt}")
+
+
+def test_w8a8_no_smoothing_and_deterministic():
+    x, w = sq_inputs(130, 320, 129, seed=4)
+    xd, wd = x.to(DEV), w.to(DEV)
+    note("smooth_quant_w8a8_gemm smooth=None")
+    qw, b = qmm.sq_quantize_weight(wd, None)
+    y1 = qmm.smooth_quant_w8a8_gemm(xd, None, qw, b, out_dtype=torch.float32).cpu()
+    y2 = qmm.smooth_quant_w8a8_gemm(xd, None, qw, b, out_dtype=torch.float32).cpu()
+    assert torch.equal(y1, y2)
+    rqw, rb = oracle.sq_quantize_weight(w.float().numpy(), None)
+    _, _, _, ref = oracle.sq_w8a8_reference(x.float().numpy(), None, rqw, rb)
+    assert_close(y1, ref, "w8a8 no smoothing")
