@@ -148,23 +148,39 @@ __device__ __forceinline__ float wave_max(float v) {
 // A 32-bit code word holds elements e0..e7 (nibble i = element i).  The
 // kernels feed 16-bit pairs (e_i, e_{i+4}) to dot / MFMA instructions, with
 // the activations permuted the same way, so a sum over k is unchanged.
-// The pair is built by OR-ing the nibbles into the low mantissa bits of a
-// 16-bit float whose exponent puts the unit in the last place at 1:
-//   bf16 0x4300 = 128.0, so (0x4300 | q) = 128 + q exactly;
-//   fp16 0x6400 = 1024.0, so (0x6400 | q) = 1024 + q exactly.
-// The constant offset is removed per group as offset * sum(x).
-constexpr uint32_t kMagicBf16 = 0x43004300u;
-constexpr float kOffsetBf16 = 128.0f;
-constexpr uint32_t kMagicF16 = 0x64006400u;
-constexpr float kOffsetF16 = 1024.0f;
-
-template <uint32_t MAGIC>
-__device__ __forceinline__ void unpack_pairs(uint32_t w, uint32_t p[4]) {
-  p[0] = (w & 0x000F000Fu) | MAGIC;
-  p[1] = ((w >> 4) & 0x000F000Fu) | MAGIC;
-  p[2] = ((w >> 8) & 0x000F000Fu) | MAGIC;
-  p[3] = ((w >> 12) & 0x000F000Fu) | MAGIC;
-}
+// Each pair is built with a shift and one AND-OR that drop the nibbles into
+// the mantissa of a 16-bit float whose exponent makes one code step worth 1:
+//   bf16: nibble at mantissa bits 0-3 of 0x4300 (128.0)  -> 128 + q exactly;
+//   fp16: nibble at mantissa bits 6-9 of 0x4C00 (16.0)   ->  16 + q exactly.
+// The constant offset is removed per group as offset * sum(x).  (A smaller
+// offset means less cancellation in that subtraction; bf16's 7-bit mantissa
+// has no room to place the nibble higher without an extra shift.)
+template <int DT>
+struct Int4Magic;
+template <>
+struct Int4Magic<QMM_BF16> {
+  static constexpr float offset = 128.0f;
+  static constexpr uint32_t one_pair = 0x3F803F80u;  // (1.0, 1.0)
+  static __device__ __forceinline__ void unpack(uint32_t w, uint32_t p[4]) {
+    constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
+    p[0] = (w & kMask) | kMagic;
+    p[1] = ((w >> 4) & kMask) | kMagic;
+    p[2] = ((w >> 8) & kMask) | kMagic;
+    p[3] = ((w >> 12) & kMask) | kMagic;
+  }
+};
+template <>
+struct Int4Magic<QMM_F16> {
+  static constexpr float offset = 16.0f;
+  static constexpr uint32_t one_pair = 0x3C003C00u;
+  static __device__ __forceinline__ void unpack(uint32_t w, uint32_t p[4]) {
+    constexpr uint32_t kMask = 0x03C003C0u, kMagic = 0x4C004C00u;
+    p[0] = ((w << 6) & kMask) | kMagic;
+    p[1] = ((w << 2) & kMask) | kMagic;
+    p[2] = ((w >> 2) & kMask) | kMagic;
+    p[3] = ((w >> 6) & kMask) | kMagic;
+  }
+};
 
 // Activation 16-bit values x0..x7 held as 4 words [x0|x1] [x2|x3] [x4|x5]
 // [x6|x7] -> pair order [x0|x4] [x1|x5] [x2|x6] [x3|x7].
@@ -190,21 +206,6 @@ template <>
 __device__ __forceinline__ float dot2<QMM_BF16>(uint32_t a, uint32_t b, float c) { return dot2_bf16(a, b, c); }
 template <>
 __device__ __forceinline__ float dot2<QMM_F16>(uint32_t a, uint32_t b, float c) { return dot2_f16(a, b, c); }
-
-template <int DT>
-struct Int4Magic;
-template <>
-struct Int4Magic<QMM_BF16> {
-  static constexpr uint32_t magic = kMagicBf16;
-  static constexpr float offset = kOffsetBf16;
-  static constexpr uint32_t one_pair = 0x3F803F80u;  // (1.0, 1.0)
-};
-template <>
-struct Int4Magic<QMM_F16> {
-  static constexpr uint32_t magic = kMagicF16;
-  static constexpr float offset = kOffsetF16;
-  static constexpr uint32_t one_pair = 0x3C003C00u;
-};
 
 __device__ __forceinline__ uint32_t zero_nibble(const uint8_t* zeros_row, int64_t g) {
   uint32_t b = zeros_row[g >> 1];

@@ -8,8 +8,8 @@
 // so its time is the weight bytes over the bandwidth until the batch is large.
 //
 // Arithmetic used by every kernel here.  A code word's nibbles are turned into
-// 16-bit floats 128 + q (bf16) or 1024 + q (fp16) with one AND-OR (see
-// unpack_pairs), so per group g of 128 weights
+// 16-bit floats 128 + q (bf16) or 16 + q (fp16) with a shift and an AND-OR
+// (Int4Magic::unpack), so per group g of 128 weights
 //   sum_k (q - z) x = sum_k (off + q) x - (off + z) * X_g,   X_g = sum_{k in g} x,
 //   y += s * (that),
 // with the products exact and the sums in fp32.
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           uint32_t p[4];
-          unpack_pairs<Mg::magic>(words[c], p);
+          Mg::unpack(words[c], p);
 #pragma unroll
           for (int b = 0; b < B; ++b) {
             a0[b] = dot2<XDT>(p[0], xp[b][4 * c + 0], a0[b]);
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(1024) void w4_mfma_skinny_kernel(const uint8_t* __r
     for (int rt = 0; rt < RT; ++rt) {
       const uint32_t words[4] = {cw[rt].x, cw[rt].y, cw[rt].z, cw[rt].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) unpack_pairs<Mg::magic>(words[j], &wa[rt][4 * j]);
+      for (int j = 0; j < 4; ++j) Mg::unpack(words[j], &wa[rt][4 * j]);
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -340,10 +340,13 @@ void launch_valu_b(int64_t B, const uint8_t* codes, const float* scales, const u
 
 // Wavefronts per block for the skinny MFMA kernel: split K further when the
 // grid alone would leave compute units short of wavefronts.
-int skinny_waves(int64_t blocks, int64_t G) {
+// The per-block reduction buffer (nw * out_per_wave floats) stays within 64 KiB.
+int skinny_waves(int64_t blocks, int64_t G, int64_t out_per_wave) {
   const int64_t target = static_cast<int64_t>(device_cus()) * 16;   // wavefronts wanted in flight
   int nw = 4;
-  while (nw < 16 && blocks * nw < target && G >= 2 * nw * 2) nw *= 2;
+  while (nw < 16 && blocks * nw < target && G >= 2 * nw * 2 &&
+         2 * nw * out_per_wave * static_cast<int64_t>(sizeof(float)) <= 65536)
+    nw *= 2;
   return nw;
 }
 
@@ -352,7 +355,7 @@ void launch_skinny(const uint8_t* codes, const float* scales, const uint8_t* zer
                    const uint16_t* x, int64_t M, void* y, hipStream_t s) {
   const int64_t bx = ceil_div(N, 16 * RT);
   const int64_t by = ceil_div(M, 16 * MT);
-  const int nw = skinny_waves(bx * by, K / kGroup);
+  const int nw = skinny_waves(bx * by, K / kGroup, static_cast<int64_t>(RT) * MT * 4 * kWave);
   const size_t lds = static_cast<size_t>(nw) * RT * MT * 4 * kWave * sizeof(float);
   w4_mfma_skinny_kernel<XDT, YDT, RT, MT>
       <<<dim3(static_cast<unsigned>(bx), static_cast<unsigned>(by)), dim3(nw * kWave), lds, s>>>(codes, scales, zeros,
