@@ -130,6 +130,42 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Sums eight per-lane values across the wavefront at once (recursive halving):
+// on return lane l holds the 64-lane sum of v[l >> 3].  v_permlane32_swap
+// exchanges lanes 32-63 of its first operand with lanes 0-31 of its second,
+// v_permlane16_swap the odd 16-lane rows of the first with the even rows of
+// the second, so each swap + add halves the lanes per value and packs two
+// values into one register; the last 16 -> 1 steps use DPP mirrors and
+// quad permutes.  18 instructions instead of 8 separate 64-lane sums.
+__device__ __forceinline__ float wave_sum8(const float v[8]) {
+  float u[4], w[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 4]), false, false);
+    u[i] = __uint_as_float(s[0]) + __uint_as_float(s[1]);   // lanes 0-31: v[i], lanes 32-63: v[i+4]
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(u[i]), __float_as_uint(u[i + 2]), false, false);
+    w[i] = __uint_as_float(s[0]) + __uint_as_float(s[1]);   // 16-lane rows: v[i], v[i+2], v[i+4], v[i+6]
+  }
+  const float t0 = w[0] + dpp_f<kDppMirror>(w[0]);
+  const float t1 = w[1] + dpp_f<kDppMirror>(w[1]);
+  float c = (threadIdx.x & 8) ? t1 : t0;                    // 8-lane group g holds v[g]
+  c += dpp_f<kDppHalfMirror>(c);
+  c += dpp_f<kDppXor2>(c);
+  c += dpp_f<kDppXor1>(c);
+  return c;
+}
+
+// Keeps a constant in a VGPR.  gfx9 VOP3 encodings take no 32-bit literal and
+// read at most one SGPR, so a three-operand op such as v_and_or_b32 with two
+// non-inline constants needs one of them in a VGPR; otherwise the compiler
+// splits it into v_and_b32 + v_or_b32.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(c), 0xE4, 0xF, 0xF, false));
+}
+
 // Full-wave sum, result valid in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
   v = row16_sum(v);
@@ -157,28 +193,32 @@ __device__ __forceinline__ float wave_max(float v) {
 // has no room to place the nibble higher without an extra shift.)
 template <int DT>
 struct Int4Magic;
+// `magic` is the kMagic constant held in a VGPR (vgpr_const), so each pair
+// costs one shift and one v_and_or_b32.
 template <>
 struct Int4Magic<QMM_BF16> {
   static constexpr float offset = 128.0f;
   static constexpr uint32_t one_pair = 0x3F803F80u;  // (1.0, 1.0)
-  static __device__ __forceinline__ void unpack(uint32_t w, uint32_t p[4]) {
-    constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
-    p[0] = (w & kMask) | kMagic;
-    p[1] = ((w >> 4) & kMask) | kMagic;
-    p[2] = ((w >> 8) & kMask) | kMagic;
-    p[3] = ((w >> 12) & kMask) | kMagic;
+  static constexpr uint32_t kMagic = 0x43004300u;
+  static __device__ __forceinline__ void unpack(uint32_t w, uint32_t magic, uint32_t p[4]) {
+    constexpr uint32_t kMask = 0x000F000Fu;
+    p[0] = (w & kMask) | magic;
+    p[1] = ((w >> 4) & kMask) | magic;
+    p[2] = ((w >> 8) & kMask) | magic;
+    p[3] = ((w >> 12) & kMask) | magic;
   }
 };
 template <>
 struct Int4Magic<QMM_F16> {
   static constexpr float offset = 16.0f;
   static constexpr uint32_t one_pair = 0x3C003C00u;
-  static __device__ __forceinline__ void unpack(uint32_t w, uint32_t p[4]) {
-    constexpr uint32_t kMask = 0x03C003C0u, kMagic = 0x4C004C00u;
-    p[0] = ((w << 6) & kMask) | kMagic;
-    p[1] = ((w << 2) & kMask) | kMagic;
-    p[2] = ((w >> 2) & kMask) | kMagic;
-    p[3] = ((w >> 6) & kMask) | kMagic;
+  static constexpr uint32_t kMagic = 0x4C004C00u;
+  static __device__ __forceinline__ void unpack(uint32_t w, uint32_t magic, uint32_t p[4]) {
+    constexpr uint32_t kMask = 0x03C003C0u;
+    p[0] = ((w << 6) & kMask) | magic;
+    p[1] = ((w << 2) & kMask) | magic;
+    p[2] = ((w >> 2) & kMask) | magic;
+    p[3] = ((w >> 6) & kMask) | magic;
   }
 };
 

@@ -57,6 +57,63 @@ __device__ __forceinline__ uint32_t quantize8(const float v[8], float s, float z
   return word;
 }
 
+// Flat variant for an even number of groups per row: the matrix is then one
+// array of N*G groups whose codes, scales and zero-point bytes are all
+// consecutive, so a wavefront takes 16 consecutive groups: 4 lanes per group,
+// 32 elements (64 bytes of bf16/fp16) per lane, 4 16-byte loads and one
+// 16-byte code store per lane.  Four lanes share a group's min/max (two DPP
+// steps) and its s and z, so the per-group division costs are spread over 32
+// elements per lane instead of 8.
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_g128_flat_kernel(const uint8_t* __restrict__ w, int64_t total_groups,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 float* __restrict__ scales,
+                                                                 uint8_t* __restrict__ zeros) {
+  constexpr int kElemBytes = DT == QMM_F32 ? 4 : 2;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int part = lane & 3;
+  const int64_t waves_per_block = blockDim.x / kWave;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * waves_per_block;
+  const int64_t nchunks = (total_groups + 15) / 16;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * waves_per_block + (threadIdx.x / kWave); c < nchunks;
+       c += nwaves) {
+    const int64_t gi = c * 16 + (lane >> 2);
+    const bool active = gi < total_groups;
+    const int64_t gl = active ? gi : total_groups - 1;     // in-bounds address for idle lanes
+    const uint8_t* src = w + (gl * kGroup + part * 32) * kElemBytes;
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Vec8<DT>::load(src + q * 8 * kElemBytes, &v[8 * q]);
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      lo = fminf(lo, v[i]);
+      hi = fmaxf(hi, v[i]);
+    }
+    lo = fminf(lo, dpp_f<kDppXor1>(lo));
+    hi = fmaxf(hi, dpp_f<kDppXor1>(hi));
+    lo = fminf(lo, dpp_f<kDppXor2>(lo));
+    hi = fmaxf(hi, dpp_f<kDppXor2>(hi));
+    float s = (hi - lo) / kLevels;      // correctly rounded fp32 division
+    if (s == 0.0f) s = 1.0f;
+    const float zf = rintf(-lo / s);
+    uint32_t out[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[q] = quantize8(&v[8 * q], s, zf);
+    const float z_next = __shfl_down(zf, 4, kWave);   // zero-point of the next (odd) group
+    if (active) {
+      st16_nt(codes + gi * 64 + part * 16, u32x4{out[0], out[1], out[2], out[3]});
+      if (part == 0) {
+        scales[gi] = s;
+        if ((lane & 7) == 0) {
+          const uint32_t zo = (gi + 1 < total_groups) ? static_cast<uint32_t>(z_next) : 0u;
+          zeros[gi >> 1] = static_cast<uint8_t>(static_cast<uint32_t>(zf) | (zo << 4));
+        }
+      }
+    }
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void quantize_g128_kernel(const uint8_t* __restrict__ w, int64_t K, int64_t G,
                                                             int64_t chunks_per_row, int64_t total_chunks,
@@ -78,12 +135,9 @@ __global__ __launch_bounds__(256) void quantize_g128_kernel(const uint8_t* __res
     const int64_t e = n * K + g * kGroup + part * 8;   // first element of this lane
 
     float v[8];
-    if (active) {
-      Vec8<DT>::load(w + e * kElemBytes, v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-    }
+    // Unconditional load (idle lanes re-read this row's first group) so the
+    // load is not split by a branch; idle lanes store nothing.
+    Vec8<DT>::load(w + (active ? e : n * K + part * 8) * kElemBytes, v);
     // Group range, widened to contain 0.
     float lo = fminf(fminf(fminf(0.0f, v[0]), fminf(v[1], v[2])), fminf(fminf(v[3], v[4]), fminf(v[5], v[6])));
     float hi = fmaxf(fmaxf(fmaxf(0.0f, v[0]), fmaxf(v[1], v[2])), fmaxf(fmaxf(v[3], v[4]), fmaxf(v[5], v[6])));
@@ -183,13 +237,27 @@ extern "C" int quantize_groupwise(const void* W, int w_dtype, int64_t N, int64_t
   if (!aligned(W, 16)) return QMM_EALIGN;
 
   const int64_t G = K / kGroup;
+  hipStream_t s = as_stream(stream);
+  const uint8_t* w = static_cast<const uint8_t*>(W);
+  const dim3 block(256);
+  if (G % 2 == 0) {
+    const int64_t T = N * G;
+    const int64_t chunks = ceil_div(T, 16);
+    int64_t blocks = ceil_div(chunks, 4);
+    const int64_t cap = static_cast<int64_t>(device_cus()) * 16;
+    if (blocks > cap) blocks = cap;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    switch (w_dtype) {
+      case QMM_BF16: quantize_g128_flat_kernel<QMM_BF16><<<grid, block, 0, s>>>(w, T, codes, scales, zeros); break;
+      case QMM_F16: quantize_g128_flat_kernel<QMM_F16><<<grid, block, 0, s>>>(w, T, codes, scales, zeros); break;
+      default: quantize_g128_flat_kernel<QMM_F32><<<grid, block, 0, s>>>(w, T, codes, scales, zeros); break;
+    }
+    return launch_status();
+  }
   const int64_t chunks_per_row = ceil_div(G, 4);
   const int64_t total = N * chunks_per_row;
   const int64_t zrow = ceil_div(G, 2);
   const dim3 grid(static_cast<unsigned>(chunk_grid(total)));
-  const dim3 block(256);
-  hipStream_t s = as_stream(stream);
-  const uint8_t* w = static_cast<const uint8_t*>(W);
   uint32_t* cw = reinterpret_cast<uint32_t*>(codes);
   switch (w_dtype) {
     case QMM_BF16:

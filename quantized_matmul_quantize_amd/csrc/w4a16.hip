@@ -58,13 +58,22 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * R;
+  const uint32_t magic = vgpr_const(Mg::kMagic);
   const int64_t G = K / kGroup;
   const int64_t zrow = (G + 1) / 2;
-  const int64_t row_bytes = K / 2;
+  const int kk = static_cast<int>(K);   // K < 2^30 (checked on the host): lane offsets fit 32 bits
 
-  int64_t rows[R];
+  // Row bases are wavefront-uniform (scalar registers); lanes add 32-bit offsets.
+  const uint8_t* crow[R];
+  const float* srow[R];
+  const uint8_t* zrowp[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) rows[r] = (row0 + r < N) ? row0 + r : N - 1;
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = (row0 + r < N) ? row0 + r : N - 1;
+    crow[r] = codes + row * (K / 2);
+    srow[r] = scales + row * G;
+    zrowp[r] = zeros + row * zrow;
+  }
 
   float acc[R][B];
 #pragma unroll
@@ -72,27 +81,39 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
 
-  for (int64_t k0 = 0; k0 < K; k0 += kValuStepK) {
-    const int64_t kb = k0 + static_cast<int64_t>(wave) * (kWave * kLaneK) + lane * kLaneK;
-    if (kb < K) {
+  for (uint32_t k0 = 0; k0 < static_cast<uint32_t>(kk); k0 += static_cast<uint32_t>(kValuStepK)) {
+    const uint32_t kb = k0 + static_cast<uint32_t>(wave * (kWave * kLaneK) + lane * kLaneK);
+    if (kb < static_cast<uint32_t>(kk)) {
       u32x4 cw[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) cw[r] = ld16_nt(codes + rows[r] * row_bytes + kb / 2);
-      const int64_t g = kb >> 7;
-      float sc[R], zo[R];
+      for (int r = 0; r < R; ++r) cw[r] = ld16_nt(crow[r] + (kb >> 1));
+      const uint32_t g = kb >> 7;
+      const uint32_t zshift = (g & 1u) * 4u;
+      float sc[R];
+      uint32_t zb[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        sc[r] = scales[rows[r] * G + g];
-        zo[r] = Mg::offset + static_cast<float>(zero_nibble(zeros + rows[r] * zrow, g));
+        sc[r] = srow[r][g];
+        zb[r] = zrowp[r][g >> 1];
       }
+      u32x4 xraw[B][4];
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xraw[b][c] = ld16(x + b * K + kb + 8 * c);
+      // Every load of the step is issued before any result is consumed, so
+      // the waits count down instead of draining the queue once per row.
+      __builtin_amdgcn_sched_barrier(0);
+      float zo[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) zo[r] = Mg::offset + static_cast<float>((zb[r] >> zshift) & 0xFu);
       uint32_t xp[B][16];
       float xs[B];
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const uint16_t* xv = x + b * K + kb;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const u32x4 a = ld16(xv + 8 * c);
+          const u32x4 a = xraw[b][c];
           const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
           permute_pairs(aw, &xp[b][4 * c]);
         }
@@ -113,7 +134,7 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           uint32_t p[4];
-          Mg::unpack(words[c], p);
+          Mg::unpack(words[c], magic, p);
 #pragma unroll
           for (int b = 0; b < B; ++b) {
             a0[b] = dot2<XDT>(p[0], xp[b][4 * c + 0], a0[b]);
@@ -129,13 +150,23 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
   }
 
   __shared__ float red[kValuWaves][R * B];
+  if constexpr (R * B == 8) {
+    float v8[8];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const float v = wave_sum(acc[r][b]);
-      if (lane == 0) red[wave][r * B + b] = v;
-    }
+      for (int b = 0; b < B; ++b) v8[r * B + b] = acc[r][b];
+    const float v = wave_sum8(v8);          // lane l: sum of value l >> 3
+    if ((lane & 7) == 0) red[wave][lane >> 3] = v;
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float v = wave_sum(acc[r][b]);
+        if (lane == 0) red[wave][r * B + b] = v;
+      }
+  }
   __syncthreads();
   if (threadIdx.x < R * B) {
     const int r = threadIdx.x / B;
@@ -167,121 +198,160 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const uint32_t a[4], const uint32_
 }
 
 // Block: NW = blockDim.x / 64 wavefronts sharing rows [row0, row0 + 16*RT)
-// and tokens [t0, t0 + 16*MT); wavefront w owns a contiguous range of groups.
+// and tokens [t0, t0 + 16); wavefront w owns a contiguous range of groups.
 // MFMA operand layout (16x16x32): lane l supplies A row l%16 and B column
 // l%16, k = 8*(l/16) .. +8 of the instruction; D lane l holds rows
 // 4*(l/16) .. +4 of column l%16.  Here each lane loads one 16-byte code
 // vector = k-chunks 4*(l/16) .. +4 of a group, so instruction j of the group
 // takes chunk 4*(l/16) + j; the activation operand is loaded the same way.
-template <int XDT, int YDT, int RT, int MT>
-__global__ __launch_bounds__(1024) void w4_mfma_skinny_kernel(const uint8_t* __restrict__ codes,
-                                                              const float* __restrict__ scales,
-                                                              const uint8_t* __restrict__ zeros, int64_t N,
-                                                              int64_t K, const uint16_t* __restrict__ x, int64_t M,
-                                                              void* __restrict__ y) {
+// Scale and zero-point: lane l loads those of D row 4*(l/16) + l%4 and the
+// four rows a lane needs are then broadcast inside its quad with DPP.
+// Token columns past M read the last valid token (in bounds) and are never
+// stored.  All addresses are uniform tile bases plus 32-bit lane offsets.
+template <int CTRL>
+__device__ __forceinline__ float quad_bcast(float v) { return dpp_f<CTRL>(v); }
+
+// Group pairs: a wavefront works on two consecutive groups at a time, so each
+// row's 128-byte line of codes (and the zero-point byte, and an 8-byte pair
+// of scales) is consumed in one step instead of being half-read and evicted
+// before the next group comes round.
+template <int RT>
+struct SkinnyLoad {
+  u32x4 cw[RT][2];
+  float sv[RT][2];
+  uint32_t zv[RT];
+  u32x4 xr[2][4];
+};
+
+// EVEN: G is even, so a pair never runs past the row and the pair of scales
+// is one aligned 8-byte load.  Otherwise the last pair's second group reads
+// the first one again (in bounds) with a zero scale.
+template <int RT, bool EVEN>
+__device__ __forceinline__ void skinny_load(SkinnyLoad<RT>& b, int gp, int G, const uint8_t* cbase,
+                                            const uint32_t* coff, const float* sbase, const uint32_t* soff,
+                                            const uint8_t* zbase, const uint32_t* zoff, const uint16_t* xbase,
+                                            uint32_t xoff) {
+  const int g = 2 * gp;
+  const bool second = EVEN || g + 1 < G;
+  const int g1 = second ? g + 1 : g;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    b.cw[rt][0] = ld16_nt(cbase + coff[rt] + g * 64);
+    b.cw[rt][1] = ld16_nt(cbase + coff[rt] + g1 * 64);
+    if constexpr (EVEN) {
+      const float2 sp = *reinterpret_cast<const float2*>(sbase + soff[rt] + g);
+      b.sv[rt][0] = sp.x;
+      b.sv[rt][1] = sp.y;
+    } else {
+      b.sv[rt][0] = sbase[soff[rt] + g];
+      b.sv[rt][1] = second ? sbase[soff[rt] + g1] : 0.0f;
+    }
+    b.zv[rt] = zbase[zoff[rt] + gp];
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) b.xr[0][c] = ld16(xbase + xoff + g * kGroup + 8 * c);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) b.xr[1][c] = ld16(xbase + xoff + g1 * kGroup + 8 * c);
+}
+
+template <int XDT, int RT>
+__device__ __forceinline__ void skinny_compute(const SkinnyLoad<RT>& b, uint32_t magic, f32x4* acc) {
   using Mg = Int4Magic<XDT>;
-  extern __shared__ float red[];   // [NW][RT*MT*4][64]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t xb[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t aw[4] = {b.xr[h][c].x, b.xr[h][c].y, b.xr[h][c].z, b.xr[h][c].w};
+      permute_pairs(aw, &xb[4 * c]);
+    }
+    float xs0 = 0.0f, xs1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      xs0 = dot2<XDT>(xb[j], Mg::one_pair, xs0);
+      xs1 = dot2<XDT>(xb[j + 1], Mg::one_pair, xs1);
+    }
+    float xg = xs0 + xs1;
+    xg += __shfl_xor(xg, 16, kWave);
+    xg += __shfl_xor(xg, 32, kWave);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      uint32_t wa[16];
+      const uint32_t words[4] = {b.cw[rt][h].x, b.cw[rt][h].y, b.cw[rt][h].z, b.cw[rt][h].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Mg::unpack(words[j], magic, &wa[4 * j]);
+      f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p = mfma16x16x32<XDT>(&wa[4 * j], &xb[4 * j], p);
+      const float zo_own = Mg::offset + static_cast<float>((b.zv[rt] >> (4 * h)) & 0xFu);
+      const float sv = b.sv[rt][h];
+      const float s4[4] = {quad_bcast<0x00>(sv), quad_bcast<0x55>(sv), quad_bcast<0xAA>(sv), quad_bcast<0xFF>(sv)};
+      const float z4[4] = {quad_bcast<0x00>(zo_own), quad_bcast<0x55>(zo_own), quad_bcast<0xAA>(zo_own),
+                           quad_bcast<0xFF>(zo_own)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[rt][i] = fmaf(s4[i], fmaf(-z4[i], xg, p[i]), acc[rt][i]);
+    }
+  }
+}
+
+template <int XDT, int YDT, int RT, bool EVEN>
+__global__ __launch_bounds__(512) void w4_mfma_skinny_kernel(const uint8_t* __restrict__ codes,
+                                                             const float* __restrict__ scales,
+                                                             const uint8_t* __restrict__ zeros, int64_t N,
+                                                             int64_t K, const uint16_t* __restrict__ x, int64_t M,
+                                                             void* __restrict__ y) {
+  using Mg = Int4Magic<XDT>;
+  extern __shared__ float red[];   // [NW][RT*4][64]
+  const uint32_t magic = vgpr_const(Mg::kMagic);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int nw = blockDim.x / kWave;
   const int l16 = lane & 15;
   const int quad = lane >> 4;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16 * RT;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * 16 * MT;
-  const int64_t G = K / kGroup;
-  const int64_t zrow = (G + 1) / 2;
-  const int64_t row_bytes = K / 2;
-  const int64_t gper = (G + nw - 1) / nw;
-  const int64_t gbeg = wave * gper;
-  const int64_t gend = (gbeg + gper < G) ? gbeg + gper : G;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * 16;
+  const int G = static_cast<int>(K / kGroup);
+  const int GP = (G + 1) / 2;
+  const int zrow = (G + 1) / 2;
+  const int rb = static_cast<int>(K / 2);
+  const int pper = (GP + nw - 1) / nw;
+  const int pbeg = wave * pper;
+  const int pend = (pbeg + pper < GP) ? pbeg + pper : GP;
 
-  int64_t arow[RT];      // A-operand row of this lane
-  int64_t drow[RT][4];   // D rows of this lane
+  // Uniform bases; lane offsets clamp rows past N (and tokens past M) in bounds.
+  const int rmax = static_cast<int>((N - 1 - row0 < 16 * RT - 1) ? N - 1 - row0 : 16 * RT - 1);
+  const uint8_t* cbase = codes + row0 * rb;
+  const float* sbase = scales + row0 * G;
+  const uint8_t* zbase = zeros + row0 * zrow;
+  uint32_t coff[RT], soff[RT], zoff[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int64_t ra = row0 + 16 * rt + l16;
-    arow[rt] = ra < N ? ra : N - 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t rd = row0 + 16 * rt + 4 * quad + i;
-      drow[rt][i] = rd < N ? rd : N - 1;
-    }
+    const int ra = min(16 * rt + l16, rmax);                  // A-operand row
+    const int rs = min(16 * rt + 4 * quad + (lane & 3), rmax); // scale row loaded by this lane
+    coff[rt] = static_cast<uint32_t>(ra * rb + quad * 16);
+    soff[rt] = static_cast<uint32_t>(rs * G);
+    zoff[rt] = static_cast<uint32_t>(rs * zrow);
   }
-  bool tvalid[MT];
-  int64_t tok[MT];
+  const int tmax = static_cast<int>((M - 1 - t0 < 15) ? M - 1 - t0 : 15);
+  const uint16_t* xbase = x + t0 * K;
+  const uint32_t xoff = static_cast<uint32_t>(min(l16, tmax) * static_cast<int>(K) + quad * 32);
+
+  f32x4 acc[RT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    tok[mt] = t0 + 16 * mt + l16;
-    tvalid[mt] = tok[mt] < M;
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int gp = pbeg; gp < pend; ++gp) {
+    SkinnyLoad<RT> b;
+    skinny_load<RT, EVEN>(b, gp, G, cbase, coff, sbase, soff, zbase, zoff, xbase, xoff);
+    __builtin_amdgcn_sched_barrier(0);
+    skinny_compute<XDT, RT>(b, magic, acc);
   }
 
-  f32x4 acc[RT][MT];
+  constexpr int kOut = RT * 4;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  for (int64_t g = gbeg; g < gend; ++g) {
-    u32x4 cw[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) cw[rt] = ld16_nt(codes + arow[rt] * row_bytes + g * 64 + quad * 16);
-    float sc[RT][4], zo[RT][4];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[rt][i] = scales[drow[rt][i] * G + g];
-        zo[rt][i] = Mg::offset + static_cast<float>(zero_nibble(zeros + drow[rt][i] * zrow, g));
-      }
-    uint32_t wa[RT][16];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const uint32_t words[4] = {cw[rt].x, cw[rt].y, cw[rt].z, cw[rt].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) Mg::unpack(words[j], &wa[rt][4 * j]);
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      uint32_t xb[16];
-      if (tvalid[mt]) {
-        const uint16_t* xv = x + tok[mt] * K + g * kGroup + quad * 32;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 a = ld16(xv + 8 * c);
-          const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-          permute_pairs(aw, &xb[4 * c]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) xb[j] = 0u;
-      }
-      float xs0 = 0.0f, xs1 = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        xs0 = dot2<XDT>(xb[j], Mg::one_pair, xs0);
-        xs1 = dot2<XDT>(xb[j + 1], Mg::one_pair, xs1);
-      }
-      float xg = xs0 + xs1;
-      xg += __shfl_xor(xg, 16, kWave);
-      xg += __shfl_xor(xg, 32, kWave);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p = mfma16x16x32<XDT>(&wa[rt][4 * j], &xb[4 * j], p);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[rt][mt][i] = fmaf(sc[rt][i], fmaf(-zo[rt][i], xg, p[i]), acc[rt][mt][i]);
-      }
-    }
-  }
-
-  constexpr int kOut = RT * MT * 4;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[(wave * kOut + (rt * MT + mt) * 4 + i) * kWave + lane] = acc[rt][mt][i];
+    for (int i = 0; i < 4; ++i) red[(wave * kOut + rt * 4 + i) * kWave + lane] = acc[rt][i];
   __syncthreads();
   for (int o = threadIdx.x; o < kOut * kWave; o += blockDim.x) {
     float v = 0.0f;
@@ -289,10 +359,9 @@ __global__ __launch_bounds__(1024) void w4_mfma_skinny_kernel(const uint8_t* __r
     const int l = o % kWave;
     const int slot = o / kWave;
     const int i = slot % 4;
-    const int mt = (slot / 4) % MT;
-    const int rt = slot / (4 * MT);
+    const int rt = slot / 4;
     const int64_t row = row0 + 16 * rt + 4 * (l >> 4) + i;
-    const int64_t t = t0 + 16 * mt + (l & 15);
+    const int64_t t = t0 + (l & 15);
     if (row < N && t < M) store_y<YDT>(y, t * N + row, v);
   }
 }
@@ -344,31 +413,37 @@ void launch_valu_b(int64_t B, const uint8_t* codes, const float* scales, const u
 int skinny_waves(int64_t blocks, int64_t G, int64_t out_per_wave) {
   const int64_t target = static_cast<int64_t>(device_cus()) * 16;   // wavefronts wanted in flight
   int nw = 4;
-  while (nw < 16 && blocks * nw < target && G >= 2 * nw * 2 &&
+  while (nw < 8 && blocks * nw < target && G >= 4 * nw * 2 &&
          2 * nw * out_per_wave * static_cast<int64_t>(sizeof(float)) <= 65536)
     nw *= 2;
   return nw;
 }
 
-template <int XDT, int YDT, int RT, int MT>
+template <int XDT, int YDT, int RT>
 void launch_skinny(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                    const uint16_t* x, int64_t M, void* y, hipStream_t s) {
   const int64_t bx = ceil_div(N, 16 * RT);
-  const int64_t by = ceil_div(M, 16 * MT);
-  const int nw = skinny_waves(bx * by, K / kGroup, static_cast<int64_t>(RT) * MT * 4 * kWave);
-  const size_t lds = static_cast<size_t>(nw) * RT * MT * 4 * kWave * sizeof(float);
-  w4_mfma_skinny_kernel<XDT, YDT, RT, MT>
-      <<<dim3(static_cast<unsigned>(bx), static_cast<unsigned>(by)), dim3(nw * kWave), lds, s>>>(codes, scales, zeros,
-                                                                                                 N, K, x, M, y);
+  const int64_t by = ceil_div(M, 16);
+  const int64_t G = K / kGroup;
+  const int nw = skinny_waves(bx * by, ceil_div(G, 2) * 2, static_cast<int64_t>(RT) * 4 * kWave);
+  const size_t lds = static_cast<size_t>(nw) * RT * 4 * kWave * sizeof(float);
+  const dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(by));
+  if (G % 2 == 0)
+    w4_mfma_skinny_kernel<XDT, YDT, RT, true><<<grid, dim3(nw * kWave), lds, s>>>(codes, scales, zeros, N, K, x, M, y);
+  else
+    w4_mfma_skinny_kernel<XDT, YDT, RT, false><<<grid, dim3(nw * kWave), lds, s>>>(codes, scales, zeros, N, K, x, M,
+                                                                                  y);
 }
 
+// Four 16-row tiles per wavefront halve the activation re-reads per code
+// byte; narrow matrices keep two so that enough blocks exist.
 template <int XDT, int YDT>
 void launch_skinny_m(int64_t M, const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N,
                      int64_t K, const uint16_t* x, void* y, hipStream_t s) {
-  if (M <= 16)
-    launch_skinny<XDT, YDT, 2, 1>(codes, scales, zeros, N, K, x, M, y, s);
+  if (N >= static_cast<int64_t>(device_cus()) * 64)
+    launch_skinny<XDT, YDT, 4>(codes, scales, zeros, N, K, x, M, y, s);
   else
-    launch_skinny<XDT, YDT, 2, 4>(codes, scales, zeros, N, K, x, M, y, s);
+    launch_skinny<XDT, YDT, 2>(codes, scales, zeros, N, K, x, M, y, s);
 }
 
 }  // namespace
@@ -392,8 +467,8 @@ extern "C" int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8
       else launch_valu_b<QMM_F16, QMM_F16>(B, codes, scales, zeros, N, K, xp, y, s);
     }
   } else {
-    if (y_dtype == QMM_F32) launch_skinny<QMM_BF16, QMM_F32, 2, 1>(codes, scales, zeros, N, K, xp, B, y, s);
-    else launch_skinny<QMM_BF16, QMM_BF16, 2, 1>(codes, scales, zeros, N, K, xp, B, y, s);
+    if (y_dtype == QMM_F32) launch_skinny_m<QMM_BF16, QMM_F32>(B, codes, scales, zeros, N, K, xp, y, s);
+    else launch_skinny_m<QMM_BF16, QMM_BF16>(B, codes, scales, zeros, N, K, xp, y, s);
   }
   return launch_status();
 }
