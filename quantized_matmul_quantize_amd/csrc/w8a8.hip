@@ -170,86 +170,168 @@ __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restric
 
 // ----------------------------------------------------------------------------
 // INT8 GEMM on v_mfma_i32_16x16x64_i8: C[m, n] = sum_k A[m, k] B[n, k], exact
-// in int32.  Block tile 128 x 128, k-step 64, four wavefronts of 64 x 64
-// (4 x 4 instructions each).  Operand layout (16x16x64): lane l supplies row
+// in int32.  Block tile 256 x 128, k-step 128 (two 64-wide MFMA chunks), four
+// wavefronts of 128 x 64 (8 x 4 instructions per chunk; 128 int32
+// accumulators per lane).  Operand layout (16x16x64): lane l supplies row
 // l%16 of A (column l%16 of B) and k = 16*(l/16) .. +16; D lane l holds rows
-// 4*(l/16) .. +4 of column l%16.  Epilogue: Y = acc * a[m] * b[n] in fp32.
+// 4*(l/16) .. +4 of column l%16.
+//
+// LDS layout: for each 64-wide chunk, each 16-row slice is stored
+// fragment-major, [k-part (4)][row (16)][16 bytes], so the 16-byte fragment of
+// lane l sits at slice_base + 16*l.  The cooperative global->LDS copy uses the
+// same order (copy vector v lands at byte 16*v), so LDS stores and fragment
+// reads are lane-linear and free of bank conflicts, while each copy
+// instruction still reads 16 rows x 64 contiguous bytes of global memory.
+//
+// Pipeline: two k-steps of LDS and two register sets.  During step t the
+// MFMAs read LDS buffer t%2 while the global loads of step t+2 are in flight;
+// the registers of step t+1 (issued one step earlier) are then written to the
+// other LDS buffer, so every load has two k-steps of MFMA work to arrive.
+// Tiles are ordered so that the blocks sharing an XCD (block id mod 8) cover a
+// compact 4 x 8 patch of the output and reuse A and B rows in that XCD's L2.
+// Epilogue: Y = acc * a[m] * b[n] in fp32 (or the raw int32 accumulator).
 // ----------------------------------------------------------------------------
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLdsRow = kBK + 16;   // padded row (bytes) to spread LDS banks
+constexpr int kBM = 256, kBN = 128, kBK = 128;
+constexpr int kAVec = kBM * kBK / 16 / 256;   // 16-byte copy vectors per thread per step: 8
+constexpr int kBVec = kBN * kBK / 16 / 256;   // 4
+constexpr int kStageA = kBM * kBK;             // bytes per LDS stage
+constexpr int kStageB = kBN * kBK;
+constexpr size_t kGemmLds = 2 * (kStageA + kStageB);   // 96 KiB
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ void xcd_tile(int64_t b, int64_t tm, int64_t tn, int64_t* m_tile, int64_t* n_tile,
+                                         bool* valid) {
+  const int64_t T = tm * tn;
+  const int64_t per = (T + kXcds - 1) / kXcds;
+  const int64_t t = (b % kXcds) * per + b / kXcds;
+  *valid = t < T;
+  const int64_t gm_band = 4;
+  const int64_t band = t / (gm_band * tn);
+  const int64_t gm = (tm - band * gm_band < gm_band) ? tm - band * gm_band : gm_band;
+  const int64_t r = t - band * gm_band * tn;
+  *m_tile = band * gm_band + (gm > 0 ? r % gm : 0);
+  *n_tile = gm > 0 ? r / gm : 0;
+}
+
+// Copy vector v of a k-step over R rows: 64-wide chunk h = v / (4R), slice
+// (v % 4R) / 64, row slice*16 + v%16, 16-byte part (v/16)%4.  Returns the
+// global offset from the tile's first row at k = 0 without the chunk's 64*h
+// (added at load time, where h is a compile-time constant).
+__device__ __forceinline__ uint32_t copy_offset(int v, int vecs_per_chunk, int rmax, int kk) {
+  const int rem = v % vecs_per_chunk;
+  const int row = min((rem >> 6) * 16 + (rem & 15), rmax);
+  return static_cast<uint32_t>(row * kk + ((rem >> 4) & 3) * 16);
+}
 
 template <int YDT>
 __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__ A, const float* __restrict__ ascale,
                                                       const int8_t* __restrict__ B, const float* __restrict__ bscale,
                                                       int64_t M, int64_t N, int64_t K, void* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) int8_t sa[kBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) int8_t sb[kBN * kLdsRow];
+  extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+  // LDS: A stages at [0, 2*kStageA), B stages after them.
+  int8_t* const sb0 = lds + 2 * kStageA;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int wm = (wave >> 1) * 64;   // wavefront sub-tile origin
-  const int wn = (wave & 1) * 64;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kBN;
+  const int wm = (wave & 1) * 128;   // wavefront sub-tile origin
+  const int wn = (wave >> 1) * 64;
+  int64_t mt, nt;
+  bool valid;
+  xcd_tile(blockIdx.x, (M + kBM - 1) / kBM, (N + kBN - 1) / kBN, &mt, &nt, &valid);
+  if (!valid) return;
+  const int64_t m0 = mt * kBM;
+  const int64_t n0 = nt * kBN;
+  const int kk = static_cast<int>(K);
 
-  // Global -> LDS: each thread moves 2 x 16 bytes of A and of B per k-step.
-  // 128 rows x 64 bytes = 512 vectors per operand; thread t takes vectors t, t+256.
-  int64_t arow[2], brow[2];
-  int vcol[2], vrow[2];
+  // Rows past M / N re-read the last valid row (their results are never stored).
+  const int8_t* abase = A + m0 * K;
+  const int8_t* bbase = B + n0 * K;
+  const int amax = static_cast<int>((M - 1 - m0 < kBM - 1) ? M - 1 - m0 : kBM - 1);
+  const int bmax = static_cast<int>((N - 1 - n0 < kBN - 1) ? N - 1 - n0 : kBN - 1);
+  uint32_t aoff[kAVec], boff[kBVec];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int v = tid + 256 * j;
-    vrow[j] = v >> 2;
-    vcol[j] = (v & 3) * 16;
-    const int64_t am = m0 + vrow[j];
-    const int64_t bn = n0 + vrow[j];
-    arow[j] = am < M ? am : M - 1;
-    brow[j] = bn < N ? bn : N - 1;
-  }
+  for (int j = 0; j < kAVec; ++j) aoff[j] = copy_offset(tid + 256 * j, kBM * 4, amax, kk);
+#pragma unroll
+  for (int j = 0; j < kBVec; ++j) boff[j] = copy_offset(tid + 256 * j, kBN * 4, bmax, kk);
 
-  i32x4 acc[4][4];
+  i32x4 acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-  const int l16 = lane & 15;
-  const int kq = (lane >> 4) * 16;
-  for (int64_t k0 = 0; k0 < K; k0 += kBK) {
-    u32x4 va[2], vb[2];
+  u32x4 ra[2][kAVec], rb[2][kBVec];
+  // When K % 128 == 64 the second chunk of the last step lies past K: it
+  // re-reads the first chunk (in bounds) and its MFMAs are skipped.
+  auto gload = [&](int set, int step) {
+    const uint32_t k0 = static_cast<uint32_t>(step * kBK);
+    const uint32_t k1 = (k0 + 64 < static_cast<uint32_t>(kk)) ? k0 + 64 : k0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      va[j] = ld16_nt(A + arow[j] * K + k0 + vcol[j]);
-      vb[j] = ld16(B + brow[j] * K + k0 + vcol[j]);
+    for (int j = 0; j < kAVec; ++j) ra[set][j] = ld16(abase + aoff[j] + (j < kAVec / 2 ? k0 : k1));
+#pragma unroll
+    for (int j = 0; j < kBVec; ++j) rb[set][j] = ld16(bbase + boff[j] + (j < kBVec / 2 ? k0 : k1));
+  };
+  auto lstore = [&](int set, int buf) {
+#pragma unroll
+    for (int j = 0; j < kAVec; ++j) *reinterpret_cast<u32x4*>(lds + buf * kStageA + (tid + 256 * j) * 16) = ra[set][j];
+#pragma unroll
+    for (int j = 0; j < kBVec; ++j) *reinterpret_cast<u32x4*>(sb0 + buf * kStageB + (tid + 256 * j) * 16) = rb[set][j];
+  };
+
+  const int nsteps = (kk + kBK - 1) / kBK;
+  const int last_chunks = (kk % kBK) ? 1 : 2;
+  gload(0, 0);
+  gload(1, min(1, nsteps - 1));
+  lstore(0, 0);
+  __syncthreads();
+
+  // One k-step on LDS buffer / register set `cur`; called with a literal so
+  // the register-set index is a compile-time constant after inlining.
+  auto kstep = [&](const int cur, const int t) {
+    // Set `cur` held step t, already in LDS.  Loads and stores are issued on
+    // every step (past the end they repeat the last step, in bounds, and are
+    // never read) so that the number of loads in flight is the same at every
+    // wait and the compiler's wait counts stay exact.
+    gload(cur, min(t + 2, nsteps - 1));
+    const int chunks = (t + 1 < nsteps) ? 2 : last_chunks;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h >= chunks) break;
+      const int8_t* a_h = lds + cur * kStageA + h * (kBM * 64);
+      const int8_t* b_h = sb0 + cur * kStageB + h * (kBN * 64);
+      i32x4 fa[8], fb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const i32x4*>(b_h + ((wn >> 4) + j) * 1024 + lane * 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fa[i] = *reinterpret_cast<const i32x4*>(a_h + ((wm >> 4) + i) * 1024 + lane * 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
+    lstore(cur ^ 1, cur ^ 1);   // step t+1 (loaded during step t-1)
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *reinterpret_cast<u32x4*>(sa + vrow[j] * kLdsRow + vcol[j]) = va[j];
-      *reinterpret_cast<u32x4*>(sb + vrow[j] * kLdsRow + vcol[j]) = vb[j];
-    }
-    __syncthreads();
-    i32x4 fa[4], fb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[i] = *reinterpret_cast<const i32x4*>(sa + (wm + 16 * i + l16) * kLdsRow + kq);
-      fb[i] = *reinterpret_cast<const i32x4*>(sb + (wn + 16 * i + l16) * kLdsRow + kq);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  // Pairs of steps, then an odd last step outside the loop: no path leaves
+  // the loop body half way, so every iteration starts with the same loads in
+  // flight.
+  int t = 0;
+  for (; t + 1 < nsteps; t += 2) {
+    kstep(0, t);
+    kstep(1, t + 1);
   }
+  if (t < nsteps) kstep(0, t);
 
   // D tile (i, j): rows m0 + wm + 16i + 4*(lane/16) + r, column n0 + wn + 16j + lane%16.
+  const int l16 = lane & 15;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + wn + 16 * j + l16;
+    if (n >= N) continue;
+    float bs = 1.0f;
+    if constexpr (YDT != QMM_I32) bs = bscale[n];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn + 16 * j + l16;
-      if (n >= N) continue;
-      float bs = 1.0f;
-      if constexpr (YDT != QMM_I32) bs = bscale[n];
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t m = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
@@ -264,6 +346,7 @@ __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__
         }
       }
     }
+  }
 }
 
 bool float_dtype(int dt) { return dt == QMM_F32 || dt == QMM_BF16 || dt == QMM_F16; }
@@ -306,14 +389,24 @@ int check_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float*
   return QMM_OK;
 }
 
+template <int YDT>
+void launch_gemm_t(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
+                   int64_t K, void* Y, hipStream_t s) {
+  // 96 KiB of dynamic LDS; the attribute is cheap to set and idempotent, so it
+  // is set on every launch (no per-device bookkeeping).
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&i8_gemm_kernel<YDT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGemmLds));
+  const int64_t tiles = ceil_div(M, kBM) * ceil_div(N, kBN);
+  const dim3 grid(static_cast<unsigned>(ceil_div(tiles, kXcds) * kXcds));
+  i8_gemm_kernel<YDT><<<grid, dim3(256), kGemmLds, s>>>(qX, xs, qW, ws, M, N, K, Y);
+}
+
 void launch_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
                  int64_t K, void* Y, int ydt, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(ceil_div(N, kBN)), static_cast<unsigned>(ceil_div(M, kBM)));
-  const dim3 block(256);
   switch (ydt) {
-    case QMM_I32: i8_gemm_kernel<QMM_I32><<<grid, block, 0, s>>>(qX, xs, qW, ws, M, N, K, Y); break;
-    case QMM_F32: i8_gemm_kernel<QMM_F32><<<grid, block, 0, s>>>(qX, xs, qW, ws, M, N, K, Y); break;
-    default: i8_gemm_kernel<QMM_BF16><<<grid, block, 0, s>>>(qX, xs, qW, ws, M, N, K, Y); break;
+    case QMM_I32: launch_gemm_t<QMM_I32>(qX, xs, qW, ws, M, N, K, Y, s); break;
+    case QMM_F32: launch_gemm_t<QMM_F32>(qX, xs, qW, ws, M, N, K, Y, s); break;
+    default: launch_gemm_t<QMM_BF16>(qX, xs, qW, ws, M, N, K, Y, s); break;
   }
 }
 

@@ -81,7 +81,8 @@ def test_quantize_activation_long_rows_and_zero_row():
     assert bits_equal(a.cpu().numpy(), ra) and bits_equal(qx.cpu().numpy(), rqx)
 
 
-@pytest.mark.parametrize("mnk", [(1, 1, 64), (5, 7, 128), (130, 129, 320), (128, 128, 64), (300, 257, 1024)],
+@pytest.mark.parametrize("mnk", [(1, 1, 64), (5, 7, 128), (130, 129, 320), (128, 128, 64), (300, 257, 1024),
+                                 (64, 300, 384), (513, 130, 256), (257, 129, 448)],
                          ids=lambda t: "x".join(map(str, t)))
 def test_int8_gemm_exact(mnk):
     m, n, k = mnk
