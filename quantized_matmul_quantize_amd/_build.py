@@ -26,6 +26,11 @@ ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "quantize.hip", "w4a16.hip", "w8a8.hip"]
 
+# Per-source extra flags.  The INT8 GEMM keeps its MFMA accumulators in
+# ordinary VGPRs: with the default accumulator-register form the register
+# allocator copies accumulators between registers on every loop iteration.
+EXTRA = {"w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
@@ -36,7 +41,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:

@@ -170,34 +170,53 @@ __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restric
 
 // ----------------------------------------------------------------------------
 // INT8 GEMM on v_mfma_i32_16x16x64_i8: C[m, n] = sum_k A[m, k] B[n, k], exact
-// in int32.  Block tile 256 x 128, k-step 128 (two 64-wide MFMA chunks), four
-// wavefronts of 128 x 64 (8 x 4 instructions per chunk; 128 int32
-// accumulators per lane).  Operand layout (16x16x64): lane l supplies row
-// l%16 of A (column l%16 of B) and k = 16*(l/16) .. +16; D lane l holds rows
-// 4*(l/16) .. +4 of column l%16.
+// in int32.  Operand layout (16x16x64): lane l supplies row l%16 of A (row
+// l%16 of B, i.e. column l%16 of C) and k = 16*(l/16) .. +16; D lane l holds
+// rows 4*(l/16) .. +4 of column l%16.
 //
-// LDS layout: for each 64-wide chunk, each 16-row slice is stored
-// fragment-major, [k-part (4)][row (16)][16 bytes], so the 16-byte fragment of
-// lane l sits at slice_base + 16*l.  The cooperative global->LDS copy uses the
-// same order (copy vector v lands at byte 16*v), so LDS stores and fragment
-// reads are lane-linear and free of bank conflicts, while each copy
-// instruction still reads 16 rows x 64 contiguous bytes of global memory.
+// Block tile 256 x 128, k-step 128 (two 64-wide chunks), four wavefronts each
+// owning 64 rows x all 128 columns (4 x 8 instructions per chunk).
 //
-// Pipeline: two k-steps of LDS and two register sets.  During step t the
-// MFMAs read LDS buffer t%2 while the global loads of step t+2 are in flight;
-// the registers of step t+1 (issued one step earlier) are then written to the
-// other LDS buffer, so every load has two k-steps of MFMA work to arrive.
-// Tiles are ordered so that the blocks sharing an XCD (block id mod 8) cover a
-// compact 4 x 8 patch of the output and reuse A and B rows in that XCD's L2.
-// Epilogue: Y = acc * a[m] * b[n] in fp32 (or the raw int32 accumulator).
+// Global -> LDS: buffer loads that write LDS directly (16 bytes per lane,
+// lane l of an instruction lands at byte 16 l of its destination), so no
+// registers stage the operands.  Eight consecutive lanes fetch the eight
+// 16-byte chunks of one row's 128-byte k-step (a whole cache line), in an
+// order chosen so that the LDS image is XOR-swizzled: within each 16-row
+// slice (2 KiB) row r, chunk c sits at 16-byte slot 8 r + (c ^ g(r)) with
+// g(r) = (r & 7) ^ (r >> 3).  Fragment reads (16 rows, one 16-byte part each
+// per 16 lanes) are then free of bank conflicts.
+//
+// Pipeline, three LDS stages of A and B (48 KiB each) and one barrier per
+// k-step t, placed between its two chunks:
+//   chunk 0: MFMAs on fragments (t, 0) | read fragments (t, 1) | issue the
+//            loads of step t+2 into the stage step t-1 used;
+//   wait for this wave's loads of step t+1, barrier;
+//   chunk 1: MFMAs on fragments (t, 1) | read fragments (t+1, 0).
+// Every load is issued on every step (clamped past the end, never read), so
+// the explicit wait count is exact.  Rows past M / N lie beyond the buffer
+// resource and read as zero; when K % 128 == 64 the second B chunk of the
+// last step is likewise fetched out of range, so its MFMAs add zero.  Tiles
+// are ordered so that the blocks sharing an XCD (block id mod 8) cover a
+// compact 4 x 8 patch of the output and share A and B rows in that XCD's L2.
+//
+// Epilogue: Y = acc * a[m] * b[n] in fp32 (or the raw int32 accumulator),
+// staged through LDS per wavefront so that global stores are whole 16-byte
+// row segments.
 // ----------------------------------------------------------------------------
 constexpr int kBM = 256, kBN = 128, kBK = 128;
-constexpr int kAVec = kBM * kBK / 16 / 256;   // 16-byte copy vectors per thread per step: 8
-constexpr int kBVec = kBN * kBK / 16 / 256;   // 4
-constexpr int kStageA = kBM * kBK;             // bytes per LDS stage
-constexpr int kStageB = kBN * kBK;
-constexpr size_t kGemmLds = 2 * (kStageA + kStageB);   // 96 KiB
+constexpr int kSlice = 16 * kBK;               // one 16-row slice of a stage: 2 KiB
+constexpr int kStageA = kBM * kBK;             // 32 KiB
+constexpr int kStage = (kBM + kBN) * kBK;      // A then B: 48 KiB
+constexpr int kLoadsA = kBM * kBK / 1024 / 4;  // 1 KiB load instructions per wavefront per step: 8
+constexpr int kLoadsB = kBN * kBK / 1024 / 4;  // 4
+constexpr int kPitch2 = 272;                   // epilogue LDS row pitch, 2-byte outputs (64 rows)
+constexpr int kPitch4 = 528;                   // 4-byte outputs (32 rows per pass)
+constexpr int kEpiWave = 64 * kPitch2;         // per-wavefront epilogue region
+constexpr size_t kGemmLds = 3 * kStage;        // 144 KiB
 constexpr int kXcds = 8;
+constexpr int kBufferWord3 = 0x00020000;       // raw buffer resource, 32-bit data format
+constexpr int kOutOfRange = 0x40000000;        // added to a lane offset: reads zero
+static_assert(32 * kPitch4 <= kEpiWave && 4 * kEpiWave <= static_cast<int>(kGemmLds), "epilogue must fit");
 
 __device__ __forceinline__ void xcd_tile(int64_t b, int64_t tm, int64_t tn, int64_t* m_tile, int64_t* n_tile,
                                          bool* valid) {
@@ -213,28 +232,25 @@ __device__ __forceinline__ void xcd_tile(int64_t b, int64_t tm, int64_t tn, int6
   *n_tile = gm > 0 ? r / gm : 0;
 }
 
-// Copy vector v of a k-step over R rows: 64-wide chunk h = v / (4R), slice
-// (v % 4R) / 64, row slice*16 + v%16, 16-byte part (v/16)%4.  Returns the
-// global offset from the tile's first row at k = 0 without the chunk's 64*h
-// (added at load time, where h is a compile-time constant).
-__device__ __forceinline__ uint32_t copy_offset(int v, int vecs_per_chunk, int rmax, int kk) {
-  const int rem = v % vecs_per_chunk;
-  const int row = min((rem >> 6) * 16 + (rem & 15), rmax);
-  return static_cast<uint32_t>(row * kk + ((rem >> 4) & 3) * 16);
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ (r >> 3); }
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int YDT>
 __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__ A, const float* __restrict__ ascale,
                                                       const int8_t* __restrict__ B, const float* __restrict__ bscale,
                                                       int64_t M, int64_t N, int64_t K, void* __restrict__ Y) {
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
-  // LDS: A stages at [0, 2*kStageA), B stages after them.
-  int8_t* const sb0 = lds + 2 * kStageA;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int wm = (wave & 1) * 128;   // wavefront sub-tile origin
-  const int wn = (wave >> 1) * 64;
   int64_t mt, nt;
   bool valid;
   xcd_tile(blockIdx.x, (M + kBM - 1) / kBM, (N + kBN - 1) / kBN, &mt, &nt, &valid);
@@ -243,108 +259,207 @@ __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__
   const int64_t n0 = nt * kBN;
   const int kk = static_cast<int>(K);
 
-  // Rows past M / N re-read the last valid row (their results are never stored).
-  const int8_t* abase = A + m0 * K;
-  const int8_t* bbase = B + n0 * K;
-  const int amax = static_cast<int>((M - 1 - m0 < kBM - 1) ? M - 1 - m0 : kBM - 1);
-  const int bmax = static_cast<int>((N - 1 - n0 < kBN - 1) ? N - 1 - n0 : kBN - 1);
-  uint32_t aoff[kAVec], boff[kBVec];
-#pragma unroll
-  for (int j = 0; j < kAVec; ++j) aoff[j] = copy_offset(tid + 256 * j, kBM * 4, amax, kk);
-#pragma unroll
-  for (int j = 0; j < kBVec; ++j) boff[j] = copy_offset(tid + 256 * j, kBN * 4, bmax, kk);
+  // One scalar buffer resource per operand tile, sized to its valid rows.
+  const int64_t arows = (M - m0 < kBM) ? M - m0 : kBM;
+  const int64_t brows = (N - n0 < kBN) ? N - n0 : kBN;
+  const __amdgpu_buffer_rsrc_t arsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(A + m0 * K), 0, static_cast<int>(arows * K), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t brsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(B + n0 * K), 0, static_cast<int>(brows * K), kBufferWord3);
 
-  i32x4 acc[8][4];
+  // Load instruction q of this wavefront fills half-slice I = 4 * wave + q of
+  // A (wave's A quarter: 8 instructions over half-slices 8 wave .. +8) or of
+  // B; lane l writes slot 64 (I & 1) + l of slice I / 2, i.e. row
+  // r = 8 (I & 1) + l / 8 of that slice, chunk (l % 8) ^ g(r).
+  int aoff[kLoadsA], boff[kLoadsB], bz[kLoadsB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
-
-  u32x4 ra[2][kAVec], rb[2][kBVec];
-  // When K % 128 == 64 the second chunk of the last step lies past K: it
-  // re-reads the first chunk (in bounds) and its MFMAs are skipped.
-  auto gload = [&](int set, int step) {
-    const uint32_t k0 = static_cast<uint32_t>(step * kBK);
-    const uint32_t k1 = (k0 + 64 < static_cast<uint32_t>(kk)) ? k0 + 64 : k0;
-#pragma unroll
-    for (int j = 0; j < kAVec; ++j) ra[set][j] = ld16(abase + aoff[j] + (j < kAVec / 2 ? k0 : k1));
-#pragma unroll
-    for (int j = 0; j < kBVec; ++j) rb[set][j] = ld16(bbase + boff[j] + (j < kBVec / 2 ? k0 : k1));
-  };
-  auto lstore = [&](int set, int buf) {
-#pragma unroll
-    for (int j = 0; j < kAVec; ++j) *reinterpret_cast<u32x4*>(lds + buf * kStageA + (tid + 256 * j) * 16) = ra[set][j];
-#pragma unroll
-    for (int j = 0; j < kBVec; ++j) *reinterpret_cast<u32x4*>(sb0 + buf * kStageB + (tid + 256 * j) * 16) = rb[set][j];
-  };
-
-  const int nsteps = (kk + kBK - 1) / kBK;
-  const int last_chunks = (kk % kBK) ? 1 : 2;
-  gload(0, 0);
-  gload(1, min(1, nsteps - 1));
-  lstore(0, 0);
-  __syncthreads();
-
-  // One k-step on LDS buffer / register set `cur`; called with a literal so
-  // the register-set index is a compile-time constant after inlining.
-  auto kstep = [&](const int cur, const int t) {
-    // Set `cur` held step t, already in LDS.  Loads and stores are issued on
-    // every step (past the end they repeat the last step, in bounds, and are
-    // never read) so that the number of loads in flight is the same at every
-    // wait and the compiler's wait counts stay exact.
-    gload(cur, min(t + 2, nsteps - 1));
-    const int chunks = (t + 1 < nsteps) ? 2 : last_chunks;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (h >= chunks) break;
-      const int8_t* a_h = lds + cur * kStageA + h * (kBM * 64);
-      const int8_t* b_h = sb0 + cur * kStageB + h * (kBN * 64);
-      i32x4 fa[8], fb[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const i32x4*>(b_h + ((wn >> 4) + j) * 1024 + lane * 16);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) fa[i] = *reinterpret_cast<const i32x4*>(a_h + ((wm >> 4) + i) * 1024 + lane * 16);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    lstore(cur ^ 1, cur ^ 1);   // step t+1 (loaded during step t-1)
-    __syncthreads();
-  };
-  // Pairs of steps, then an odd last step outside the loop: no path leaves
-  // the loop body half way, so every iteration starts with the same loads in
-  // flight.
-  int t = 0;
-  for (; t + 1 < nsteps; t += 2) {
-    kstep(0, t);
-    kstep(1, t + 1);
+  for (int q = 0; q < kLoadsA; ++q) {
+    const int I = kLoadsA * wave + q;
+    const int r = 8 * (I & 1) + (lane >> 3);
+    const int row = 16 * (I >> 1) + r;
+    aoff[q] = row * kk + (((lane & 7) ^ swz(r)) * 16);
   }
-  if (t < nsteps) kstep(0, t);
+#pragma unroll
+  for (int q = 0; q < kLoadsB; ++q) {
+    const int I = kLoadsB * wave + q;
+    const int r = 8 * (I & 1) + (lane >> 3);
+    const int row = 16 * (I >> 1) + r;
+    const int c = (lane & 7) ^ swz(r);
+    boff[q] = row * kk + c * 16;
+    bz[q] = (c >= 4) ? kOutOfRange : 0;   // second 64-wide chunk
+  }
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const int nsteps = (kk + kBK - 1) / kBK;
+  auto issue = [&](int step, int stage) {
+    const int st = min(step, nsteps - 1);
+    const int k0 = st * kBK;
+    const bool tail = k0 + 64 >= kk;   // only when K % 128 == 64, on the last step
+    const uint32_t sbase = lds_base + static_cast<uint32_t>(stage * kStage);
+#pragma unroll
+    for (int q = 0; q < kLoadsA; ++q) {
+      const int I = kLoadsA * wave + q;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_ptr_t)(uintptr_t)(sbase + (I >> 1) * kSlice + (I & 1) * 1024),
+                                               16, aoff[q], k0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < kLoadsB; ++q) {
+      const int I = kLoadsB * wave + q;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          brsrc, (lds_ptr_t)(uintptr_t)(sbase + kStageA + (I >> 1) * kSlice + (I & 1) * 1024), 16,
+          boff[q] + (tail ? bz[q] : 0), k0, 0, 0);
+    }
+  };
 
-  // D tile (i, j): rows m0 + wm + 16i + 4*(lane/16) + r, column n0 + wn + 16j + lane%16.
-  const int l16 = lane & 15;
+  // Fragment read offsets: lane l reads row l%16, part l/16 of chunk h.
+  const int fr = lane & 15;
+  const int rd0 = (8 * fr + ((lane >> 4) ^ swz(fr))) * 16;
+  const int rd1 = (8 * fr + ((4 + (lane >> 4)) ^ swz(fr))) * 16;
+  i32x4 fa0[4], fb0[8], fa1[4], fb1[8];
+  auto read_chunk = [&](i32x4 (&fa)[4], i32x4 (&fb)[8], int stage, int rd) {
+    const int8_t* sa = lds + stage * kStage + (4 * wave) * kSlice + rd;
+    const int8_t* sb = lds + stage * kStage + kStageA + rd;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn + 16 * j + l16;
-    if (n >= N) continue;
-    float bs = 1.0f;
-    if constexpr (YDT != QMM_I32) bs = bscale[n];
+    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const i32x4*>(sa + i * kSlice);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int j = 0; j < 8; ++j) fb[j] = *reinterpret_cast<const i32x4*>(sb + j * kSlice);
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  };
+
+  i32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+  // Prologue: loads of steps 0 and 1; wait for step 0, barrier, fragments (0, 0).
+  issue(0, 0);
+  issue(1, 1);
+  wait_vmcnt<kLoadsA + kLoadsB>();
+  barrier();
+  read_chunk(fa0, fb0, 0, rd0);
+
+  int s0 = 0;   // stage of step t; step t+1 uses (s0+1)%3, step t+2 (s0+2)%3
+  for (int t = 0; t < nsteps; ++t) {
+    const int s1 = (s0 == 2) ? 0 : s0 + 1;
+    const int s2 = (s1 == 2) ? 0 : s1 + 1;
+    read_chunk(fa1, fb1, s0, rd1);
+    issue(t + 2, s2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa0[i], fb0[j], acc[i][j], 0, 0, 0);
+    // 12 groups of 2 MFMAs, each followed by one fragment read and one load.
+#pragma unroll
+    for (int g = 0; g < 12; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    // This wave's loads of step t+1 are complete once only step t+2's remain.
+    wait_vmcnt<kLoadsA + kLoadsB>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): fragments (t, 1) have landed
+    barrier();
+    read_chunk(fa0, fb0, s1, rd0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa1[i], fb1[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < 12; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    s0 = s1;
+  }
+  wait_vmcnt<0>();
+  __syncthreads();   // the epilogue reuses the LDS
+
+  // Epilogue.  Tile (i, j), register r: row 16 i + 4 (lane/16) + r of the
+  // wavefront's 64, column 16 j + lane%16 of the block's 128.
+  int8_t* region = lds + wave * kEpiWave;
+  const int64_t mw = m0 + 64 * wave;
+  float bs[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t n = n0 + 16 * j + (lane & 15);
+    bs[j] = (YDT == QMM_I32) ? 1.0f : bscale[n < N ? n : N - 1];
+  }
+  if constexpr (YDT == QMM_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
-        if (m >= M) continue;
-        const int32_t v = acc[i][j][r];
-        if constexpr (YDT == QMM_I32) {
-          static_cast<int32_t*>(Y)[m * N + n] = v;
-        } else {
-          const float f = static_cast<float>(v) * ascale[m] * bs;
-          if constexpr (YDT == QMM_F32) static_cast<float*>(Y)[m * N + n] = f;
-          else static_cast<uint16_t*>(Y)[m * N + n] = static_cast<uint16_t>(f32_to_bf16_bits(f));
+        const int lr = 16 * i + 4 * (lane >> 4) + r;
+        const int64_t m = mw + lr;
+        const float as = ascale[m < M ? m : M - 1];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float f = static_cast<float>(acc[i][j][r]) * as * bs[j];
+          *reinterpret_cast<uint16_t*>(region + lr * kPitch2 + (16 * j + (lane & 15)) * 2) =
+              static_cast<uint16_t>(f32_to_bf16_bits(f));
         }
       }
+    }
+    __syncthreads();
+    const bool vec = (N % 8 == 0) && ((reinterpret_cast<uintptr_t>(Y) & 15) == 0);
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int lr = 4 * it + (lane >> 4);
+      const int64_t m = mw + lr;
+      const int64_t n = n0 + (lane & 15) * 8;
+      if (m >= M || n >= N) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region + lr * kPitch2 + (lane & 15) * 16);
+      uint16_t* dst = static_cast<uint16_t*>(Y) + m * N + n;
+      if (vec && n + 8 <= N) {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  } else {
+    const bool vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(Y) & 15) == 0);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * half + ii;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lr = 16 * ii + 4 * (lane >> 4) + r;   // row within this 32-row pass
+          const int64_t m = mw + 32 * half + lr;
+          float as = 1.0f;
+          if constexpr (YDT == QMM_F32) as = ascale[m < M ? m : M - 1];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            uint32_t bits;
+            if constexpr (YDT == QMM_I32) bits = static_cast<uint32_t>(acc[i][j][r]);
+            else bits = __float_as_uint(static_cast<float>(acc[i][j][r]) * as * bs[j]);
+            *reinterpret_cast<uint32_t*>(region + lr * kPitch4 + (16 * j + (lane & 15)) * 4) = bits;
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int lr = 2 * it + (lane >> 5);
+        const int64_t m = mw + 32 * half + lr;
+        const int64_t n = n0 + (lane & 31) * 4;
+        if (m < M && n < N) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(region + lr * kPitch4 + (lane & 31) * 16);
+          uint32_t* dst = static_cast<uint32_t*>(Y) + m * N + n;
+          if (vec && n + 4 <= N) {
+            *reinterpret_cast<u32x4*>(dst) = v;
+          } else {
+            for (int e = 0; e < 4 && n + e < N; ++e) dst[e] = v[e];
+          }
+        }
+      }
+      __syncthreads();
     }
   }
 }
@@ -392,8 +507,8 @@ int check_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float*
 template <int YDT>
 void launch_gemm_t(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
                    int64_t K, void* Y, hipStream_t s) {
-  // 96 KiB of dynamic LDS; the attribute is cheap to set and idempotent, so it
-  // is set on every launch (no per-device bookkeeping).
+  // 144 KiB of dynamic LDS; the attribute is cheap to set and idempotent, so
+  // it is set on every launch (no per-device bookkeeping).
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&i8_gemm_kernel<YDT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGemmLds));
   const int64_t tiles = ceil_div(M, kBM) * ceil_div(N, kBN);
