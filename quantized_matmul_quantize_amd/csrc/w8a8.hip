@@ -359,6 +359,7 @@ __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);   // chunk-0 work stays ahead of the wait
     // This wave's loads of step t+1 are complete once only step t+2's remain.
     wait_vmcnt<kLoadsA + kLoadsB>();
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): fragments (t, 1) have landed
