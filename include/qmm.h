@@ -109,8 +109,8 @@ int dequantize(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  * Is Faster"); "Quantization from Scratch" ("What it buys at decode").
  * x : [B, K] of x_dtype (QMM_BF16 or QMM_F16), 1 <= B <= 8.
  * y : [B, N] of y_dtype (x_dtype or QMM_F32).
- * group 128.  B == 1 runs on the vector ALUs only; 2 <= B <= 8 contracts on
- * the matrix cores (bf16 activations; fp16 activations use the vector path).
+ * group 128.  B == 1 runs on the vector ALUs only (no matrix cores);
+ * 2 <= B <= 8 contracts on the matrix cores (the kernel of w4a16_gemm).
  * ------------------------------------------------------------------------- */
 int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                int group, const void* x, int x_dtype, int64_t B, void* y, int y_dtype, void* stream);
@@ -120,7 +120,10 @@ int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  * batch): Y[M, N] = X[M, K] W_hat^T, bf16 MFMA with fp32 accumulation.
  * Source: "How quantization works" ("Inference view"); "Quantization from
  * Scratch" ("What it buys at decode", growing batch).
- * X : [M, K] QMM_BF16.  Y : [M, N] QMM_BF16 or QMM_F32.  M >= 1, group 128.
+ * X : [M, K] QMM_BF16 or QMM_F16.  Y : [M, N] of X's type or QMM_F32.
+ * M >= 1, group 128.  The block tile keeps the zero points of 64 weight rows
+ * in LDS: K <= 53248 for M > 16 (K <= 179968 for M <= 16); beyond that bf16
+ * runs a slower kernel without the table and fp16 returns QMM_EUNSUPPORTED.
  * ------------------------------------------------------------------------- */
 int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                int group, const void* X, int x_dtype, int64_t M, void* Y, int y_dtype, void* stream);

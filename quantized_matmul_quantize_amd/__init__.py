@@ -148,7 +148,7 @@ def w4a16_gemv(codes, scales, zeros, x: torch.Tensor, out_dtype: Optional[torch.
 
 def w4a16_gemm(codes, scales, zeros, X: torch.Tensor, out_dtype: Optional[torch.dtype] = None,
                group: int = GROUP, out: Optional[torch.Tensor] = None):
-    """Y [M, N] = X [M, K] @ W_hat^T (bf16 activations, fp32 accumulation)."""
+    """Y [M, N] = X [M, K] @ W_hat^T (bf16 or fp16 activations, fp32 accumulation)."""
     _check(codes, "codes")
     _check(X, "X")
     N, K = codes.shape[0], codes.shape[1] * 2

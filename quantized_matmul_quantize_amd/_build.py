@@ -26,10 +26,12 @@ ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "quantize.hip", "w4a16.hip", "w8a8.hip"]
 
-# Per-source extra flags.  The INT8 GEMM keeps its MFMA accumulators in
+# Per-source extra flags.  The MFMA kernels keep their accumulators in
 # ordinary VGPRs: with the default accumulator-register form the register
-# allocator copies accumulators between registers on every loop iteration.
-EXTRA = {"w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# allocator copies accumulators between registers on every loop iteration,
+# and results folded on the vector ALUs would be copied out of AGPRs.
+EXTRA = {"w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

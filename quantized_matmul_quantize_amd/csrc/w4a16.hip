@@ -367,6 +367,261 @@ __global__ __launch_bounds__(512) void w4_mfma_skinny_kernel(const uint8_t* __re
 }
 
 // ----------------------------------------------------------------------------
+// LDS-tiled MFMA kernel for 2 <= tokens (batched decode and prefill).
+//
+// Block: 4 wavefronts, output tile MT tokens x 64 weight rows.  The
+// wavefronts split K by quantization group (wavefront w takes groups w, w+4,
+// ...), so every activation and weight byte of the tile is read from LDS by
+// exactly one wavefront, and the four partial tiles are summed through LDS at
+// the end in a fixed order.
+//
+// Operands reach LDS by buffer loads that write LDS directly, each wavefront
+// into rings of its own (no block barrier in the main loop):
+//  * activations, one group = MT rows x 256 bytes: sixteen lanes fetch one
+//    row's 256 bytes; 16-byte chunk j of row r sits at position j ^ (r & 15);
+//  * codes, one group = 64 rows x 64 bytes: four lanes fetch one row's 64
+//    bytes; 16-byte part p of row r (of a 16-row slice) sits at slot
+//    4 r + (p ^ h(r)), h(r) = ((r >> 1) ^ (r >> 3)) & 3;
+//  * scales, one group = 64 floats;
+// and the block's zero-point bytes are copied to LDS once.  Both swizzles make
+// the fragment reads below free of bank conflicts.
+//
+// MFMA v_mfma_f32_16x16x32_{bf16,f16}: activations are the A operand (lane l:
+// token l%16), codes the B operand (lane l: weight row l%16); lane group
+// p = l/16 of chunk c in 0..3 covers k = 32 p + 8 c .. +8 of the group, held
+// in pair order (k, k+4) on both sides (Int4Magic::unpack / permute_pairs).
+// The group's column sums X_g come from one more MFMA against a ones operand,
+// and each group is folded as  acc += s * (P - (off + z) * X_g).
+// ----------------------------------------------------------------------------
+constexpr int kLdsWaves = 4;
+constexpr int kLdsRows = 64;                  // weight rows per block
+constexpr int kXRing = 3;                     // activation groups in flight per wavefront
+constexpr int kCodeGroupBytes = kLdsRows * kGroup / 2;   // 4 KiB
+constexpr size_t kLdsBytesMax = 160 * 1024;
+constexpr int kScaleGroupBytes = kLdsRows * 4;           // 256 B
+
+template <int MT>
+struct LdsCfg {
+  static constexpr int kWRing = MT <= 16 ? 4 : 3;        // code/scale ring positions (>= 3)
+  static constexpr int kXBytes = MT * kGroup * 2;        // one activation group
+  static constexpr int kWaveBytes = kXRing * kXBytes + kWRing * (kCodeGroupBytes + kScaleGroupBytes);
+  static constexpr int kXLoads = MT / 4;                 // 1 KiB load instructions per activation group
+  static constexpr int kLoadsPerGroup = kXLoads + 4 + 1;
+  static constexpr int kPartPitch = 68;                  // floats per row of a partial tile
+};
+
+__device__ __forceinline__ int code_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource, 32-bit data format
+
+// Host and device: it is called from lambdas, which HIP compiles for both sides.
+__host__ __device__ inline lds_ptr_t lds_at(uint32_t byte) { return (lds_ptr_t)(uintptr_t)byte; }
+
+template <int XDT, int YDT, int MT>
+__global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__ codes,
+                                                     const float* __restrict__ scales,
+                                                     const uint8_t* __restrict__ zeros, int64_t N, int64_t K,
+                                                     const uint16_t* __restrict__ x, int64_t M,
+                                                     void* __restrict__ y) {
+  using Cfg = LdsCfg<MT>;
+  using Mg = Int4Magic<XDT>;
+  constexpr int WR = Cfg::kWRing;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  // Wave-uniform by construction; readfirstlane makes it a scalar so every
+  // buffer-load offset and LDS destination derived from it stays scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int G = static_cast<int>(K / kGroup);
+  const int zb = (G + 1) / 2;
+
+  // Tile order: the blocks of one XCD (block id mod 8) take consecutive tiles,
+  // token tiles fastest, so the token tiles of one weight slice run together
+  // on one XCD and the slice's codes come from HBM once.
+  const int64_t mtiles = (M + MT - 1) / MT;
+  const int64_t ntiles = (N + kLdsRows - 1) / kLdsRows;
+  const int64_t T = mtiles * ntiles;
+  const int64_t per = (T + 7) / 8;
+  const int64_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= T) return;
+  const int64_t n0 = (t / mtiles) * kLdsRows;
+  const int64_t m0 = (t % mtiles) * MT;
+  const int64_t nrows = (N - n0 < kLdsRows) ? N - n0 : kLdsRows;
+  const int64_t mrows = (M - m0 < MT) ? M - m0 : MT;
+
+  // LDS: per-wavefront rings, then the zero-point table [64][zb].
+  const uint32_t lbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const uint32_t wbase = lbase + wave * Cfg::kWaveBytes;
+  const uint32_t xring = wbase;
+  const uint32_t cring = wbase + kXRing * Cfg::kXBytes;
+  const uint32_t sring = cring + WR * kCodeGroupBytes;
+  uint8_t* const ztab = lds + kLdsWaves * Cfg::kWaveBytes;
+
+  // Buffer resources sized to the tile's valid rows: rows past M / N read 0.
+  const int kb2 = static_cast<int>(K) * 2;   // activation row bytes
+  const int kh = static_cast<int>(K / 2);    // code row bytes
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + m0 * K), 0, static_cast<int>(mrows) * kb2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(codes + n0 * (K / 2)), 0, static_cast<int>(nrows) * kh, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scales + n0 * G), 0, static_cast<int>(nrows) * G * 4, kBufferWord3);
+
+  // Fixed-size offset arrays: HIP drops the host stub of this kernel when an
+  // element of a template-dependent-size array is passed to the buffer-load
+  // builtin inside a lambda.
+  static_assert(Cfg::kXLoads <= 8, "activation loads per group");
+  int xoff[8], coff[4];
+#pragma unroll
+  for (int q = 0; q < Cfg::kXLoads; ++q) {
+    const int r = 4 * q + (lane >> 4);
+    xoff[q] = r * kb2 + (((lane & 15) ^ (r & 15)) * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = lane >> 2;
+    coff[q] = (16 * q + r) * kh + (((lane & 3) ^ code_swz(r)) * 16);
+  }
+  const int soff = lane * G * 4;
+
+  const int ng = (G > wave) ? (G - wave + kLdsWaves - 1) / kLdsWaves : 0;   // this wave's groups
+  auto grp = [&](int i) { return wave + kLdsWaves * min(i, max(ng - 1, 0)); };   // clamped, in range
+  auto issue_x = [&](int i) {
+    const int g = min(grp(i), G - 1);
+    const uint32_t dst = xring + (i % kXRing) * Cfg::kXBytes;
+#pragma unroll
+    for (int q = 0; q < Cfg::kXLoads; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, lds_at(dst + q * 1024), 16, xoff[q], g * 256, 0, 0);
+  };
+  auto issue_w = [&](int i) {
+    const int g = min(grp(i), G - 1);
+    const uint32_t dst = cring + (i % WR) * kCodeGroupBytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, lds_at(dst + q * 1024), 16, coff[q], g * 64, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, lds_at(sring + (i % WR) * kScaleGroupBytes), 4, soff, g * 4, 0, 0);
+  };
+
+  // Issue slots j = -2, -1, 0, 1, ...: slot j loads the activations of
+  // group j + 2 into the ring position group j - 1 used, and the codes and
+  // scales of group j + WR - 1 likewise; codes of groups 0 .. WR-4 go first.
+  // Before group i is computed every slot <= i - 2 must have landed.
+  for (int i = 0; i < WR - 3; ++i) issue_w(i);
+  issue_x(0);
+  issue_w(WR - 3);
+  issue_x(1);
+  issue_w(WR - 2);
+  for (int i = tid; i < kLdsRows * zb; i += 256) {
+    const int r = i / zb;
+    ztab[i] = (r < nrows) ? zeros[(n0 + r) * zb + (i - r * zb)] : 0;
+  }
+  __syncthreads();   // zero-point table
+
+  f32x4 acc[MT / 16][4];
+#pragma unroll
+  for (int mt = 0; mt < MT / 16; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint32_t magic = vgpr_const(Mg::kMagic);
+  const uint32_t ones[4] = {Mg::one_pair, Mg::one_pair, Mg::one_pair, Mg::one_pair};
+  const int fr = lane & 15;
+  const int fp = lane >> 4;
+  const int crd = (4 * fr + (fp ^ code_swz(fr))) * 16;   // code fragment slot (per 16-row slice)
+
+  for (int i = 0; i < ng; ++i) {
+    issue_x(i + 2);
+    issue_w(i + WR - 1);
+    wait_vm<2 * Cfg::kLoadsPerGroup>();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int g = wave + kLdsWaves * i;
+    const uint8_t* xg = lds + (xring - lbase) + (i % kXRing) * Cfg::kXBytes;
+    const uint8_t* cg = lds + (cring - lbase) + (i % WR) * kCodeGroupBytes;
+    const float* sg = reinterpret_cast<const float*>(lds + (sring - lbase) + (i % WR) * kScaleGroupBytes);
+    u32x4 cw[4];
+    float sv[4], zo[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      cw[nt] = *reinterpret_cast<const u32x4*>(cg + nt * 1024 + crd);
+      sv[nt] = sg[16 * nt + fr];
+      const uint32_t zbyte = ztab[(16 * nt + fr) * zb + (g >> 1)];
+      zo[nt] = Mg::offset + static_cast<float>((g & 1) ? (zbyte >> 4) : (zbyte & 15u));
+    }
+    f32x4 part[MT / 16][4], xs[MT / 16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t xa[MT / 16][4];
+#pragma unroll
+      for (int mt = 0; mt < MT / 16; ++mt) {
+        const int r = 16 * mt + fr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xg + r * 256 + (((4 * fp + c) ^ fr) * 16));
+        const uint32_t aw[4] = {v.x, v.y, v.z, v.w};
+        permute_pairs(aw, xa[mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT / 16; ++mt)
+        xs[mt] = mfma16x16x32<XDT>(xa[mt], ones, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : xs[mt]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        uint32_t wb[4];
+        Mg::unpack(cw[nt][c], magic, wb);
+#pragma unroll
+        for (int mt = 0; mt < MT / 16; ++mt)
+          part[mt][nt] = mfma16x16x32<XDT>(xa[mt], wb, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : part[mt][nt]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT / 16; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mt][nt][e] = fmaf(sv[nt], fmaf(-zo[nt], xs[mt][e], part[mt][nt][e]), acc[mt][nt][e]);
+  }
+  wait_vm<0>();
+  __syncthreads();   // every ring is drained; the LDS now holds the partial tiles
+
+  // Partial tile of wavefront w: [MT][kPartPitch] floats; D lane l holds
+  // tokens 16 mt + 4 (l/16) + e, weight row 16 nt + l%16.
+  float* parts = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int mt = 0; mt < MT / 16; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        parts[(wave * MT + 16 * mt + 4 * fp + e) * Cfg::kPartPitch + 16 * nt + fr] = acc[mt][nt][e];
+  __syncthreads();
+  // Sum the four partials (wavefront order 0..3) and store: thread -> token
+  // row tid / 8 (+32 per pass), 8 consecutive weight rows.
+  for (int o = tid; o < MT * 8; o += 256) {
+    const int r = o >> 3;
+    const int c0 = (o & 7) * 8;
+    const int64_t m = m0 + r;
+    if (m >= M) continue;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float a = parts[(0 * MT + r) * Cfg::kPartPitch + c0 + j];
+      a += parts[(1 * MT + r) * Cfg::kPartPitch + c0 + j];
+      a += parts[(2 * MT + r) * Cfg::kPartPitch + c0 + j];
+      a += parts[(3 * MT + r) * Cfg::kPartPitch + c0 + j];
+      v[j] = a;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t n = n0 + c0 + j;
+      if (n < N) store_y<YDT>(y, m * N + n, v[j]);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Host side.
 // ----------------------------------------------------------------------------
 int check_common(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
@@ -446,6 +701,46 @@ void launch_skinny_m(int64_t M, const uint8_t* codes, const float* scales, const
     launch_skinny<XDT, YDT, 2>(codes, scales, zeros, N, K, x, M, y, s);
 }
 
+// LDS-tiled kernel: MT = 16 for up to 16 tokens, else 32.  Returns false
+// (nothing launched) when the zero-point table would not fit in LDS.
+template <int XDT, int YDT, int MT>
+bool launch_lds_t(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                  const uint16_t* x, int64_t M, void* y, hipStream_t s) {
+  using Cfg = LdsCfg<MT>;
+  const int64_t G = K / kGroup;
+  const size_t lds = static_cast<size_t>(kLdsWaves) * Cfg::kWaveBytes + static_cast<size_t>(kLdsRows) * ((G + 1) / 2);
+  if (lds > kLdsBytesMax) return false;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_lds_kernel<XDT, YDT, MT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  const int64_t tiles = ceil_div(M, MT) * ceil_div(N, kLdsRows);
+  const dim3 grid(static_cast<unsigned>(ceil_div(tiles, 8) * 8));
+  w4_lds_kernel<XDT, YDT, MT><<<grid, dim3(kLdsWaves * kWave), lds, s>>>(codes, scales, zeros, N, K, x, M, y);
+  return true;
+}
+
+template <int XDT, int YDT>
+bool launch_lds(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                const uint16_t* x, int64_t M, void* y, hipStream_t s) {
+  if (M <= 16) return launch_lds_t<XDT, YDT, 16>(codes, scales, zeros, N, K, x, M, y, s);
+  return launch_lds_t<XDT, YDT, 32>(codes, scales, zeros, N, K, x, M, y, s);
+}
+
+// Tokens >= 2 (or the GEMM): the LDS-tiled kernel, else the skinny kernel
+// (bf16) when its zero-point table does not fit.
+bool launch_mfma(int x_dtype, int y_dtype, const uint8_t* codes, const float* scales, const uint8_t* zeros,
+                 int64_t N, int64_t K, const uint16_t* x, int64_t M, void* y, hipStream_t s) {
+  if (x_dtype == QMM_BF16) {
+    const bool ok = (y_dtype == QMM_F32) ? launch_lds<QMM_BF16, QMM_F32>(codes, scales, zeros, N, K, x, M, y, s)
+                                         : launch_lds<QMM_BF16, QMM_BF16>(codes, scales, zeros, N, K, x, M, y, s);
+    if (ok) return true;
+    if (y_dtype == QMM_F32) launch_skinny_m<QMM_BF16, QMM_F32>(M, codes, scales, zeros, N, K, x, y, s);
+    else launch_skinny_m<QMM_BF16, QMM_BF16>(M, codes, scales, zeros, N, K, x, y, s);
+    return true;
+  }
+  return (y_dtype == QMM_F32) ? launch_lds<QMM_F16, QMM_F32>(codes, scales, zeros, N, K, x, M, y, s)
+                              : launch_lds<QMM_F16, QMM_F16>(codes, scales, zeros, N, K, x, M, y, s);
+}
+
 }  // namespace
 }  // namespace qmm
 
@@ -458,17 +753,13 @@ extern "C" int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8
   if (B > 8) return QMM_EUNSUPPORTED;
   hipStream_t s = as_stream(stream);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
-  if (B == 1 || x_dtype == QMM_F16) {
-    if (x_dtype == QMM_BF16) {
-      if (y_dtype == QMM_F32) launch_valu_b<QMM_BF16, QMM_F32>(B, codes, scales, zeros, N, K, xp, y, s);
-      else launch_valu_b<QMM_BF16, QMM_BF16>(B, codes, scales, zeros, N, K, xp, y, s);
-    } else {
-      if (y_dtype == QMM_F32) launch_valu_b<QMM_F16, QMM_F32>(B, codes, scales, zeros, N, K, xp, y, s);
-      else launch_valu_b<QMM_F16, QMM_F16>(B, codes, scales, zeros, N, K, xp, y, s);
-    }
+  if (B >= 2 && launch_mfma(x_dtype, y_dtype, codes, scales, zeros, N, K, xp, B, y, s)) return launch_status();
+  if (x_dtype == QMM_BF16) {
+    if (y_dtype == QMM_F32) launch_valu_b<QMM_BF16, QMM_F32>(B, codes, scales, zeros, N, K, xp, y, s);
+    else launch_valu_b<QMM_BF16, QMM_BF16>(B, codes, scales, zeros, N, K, xp, y, s);
   } else {
-    if (y_dtype == QMM_F32) launch_skinny_m<QMM_BF16, QMM_F32>(B, codes, scales, zeros, N, K, xp, y, s);
-    else launch_skinny_m<QMM_BF16, QMM_BF16>(B, codes, scales, zeros, N, K, xp, y, s);
+    if (y_dtype == QMM_F32) launch_valu_b<QMM_F16, QMM_F32>(B, codes, scales, zeros, N, K, xp, y, s);
+    else launch_valu_b<QMM_F16, QMM_F16>(B, codes, scales, zeros, N, K, xp, y, s);
   }
   return launch_status();
 }
@@ -477,10 +768,8 @@ extern "C" int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8
                           int group, const void* X, int x_dtype, int64_t M, void* Y, int y_dtype, void* stream) {
   int st = check_common(codes, scales, zeros, N, K, group, X, x_dtype, M, Y, y_dtype);
   if (st != QMM_OK) return st;
-  if (x_dtype != QMM_BF16) return QMM_EUNSUPPORTED;
   hipStream_t s = as_stream(stream);
   const uint16_t* xp = static_cast<const uint16_t*>(X);
-  if (y_dtype == QMM_F32) launch_skinny_m<QMM_BF16, QMM_F32>(M, codes, scales, zeros, N, K, xp, Y, s);
-  else launch_skinny_m<QMM_BF16, QMM_BF16>(M, codes, scales, zeros, N, K, xp, Y, s);
+  if (!launch_mfma(x_dtype, y_dtype, codes, scales, zeros, N, K, xp, M, Y, s)) return QMM_EUNSUPPORTED;
   return launch_status();
 }

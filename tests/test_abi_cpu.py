@@ -115,7 +115,8 @@ def test_gemv_gemm_argument_errors():
     assert gemv(P, P, P, 8, 256, 128, P, BF16, 1, P, F16, None) == EUNSUP     # mixed 16-bit types
     assert gemv(P, P, P, 8, 256, 64, P, BF16, 1, P, BF16, None) == EUNSUP
     assert gemv(P, P, P, 8, 256, 128, MIS, BF16, 1, P, BF16, None) == EALIGN
-    assert gemm(P, P, P, 8, 256, 128, P, F16, 4, P, F16, None) == EUNSUP      # GEMM takes bf16
+    assert gemm(P, P, P, 8, 256, 128, P, F32, 4, P, F32, None) == EUNSUP      # fp32 activations
+    assert gemm(P, P, P, 8, 256, 128, P, F16, 4, P, BF16, None) == EUNSUP     # mixed 16-bit types
     assert gemm(P, P, P, 8, 300, 128, P, BF16, 4, P, BF16, None) == EINVAL
     assert gemm(P, P, P, 8, 256, 128, P, BF16, 0, P, BF16, None) == EINVAL
 

@@ -81,14 +81,18 @@ def test_gemv_full_size(name, index, B):
     gemv_case(q, s, z, x, ydt, f"{name}[{index}] B={B} 16-bit", rows=rows)
 
 
-@pytest.mark.parametrize("M", [1, 5, 16, 17, 64, 100, 256])
-@pytest.mark.parametrize("shape", [(3, 384), (129, 2176), (300, 1024)], ids=lambda s: f"{s[0]}x{s[1]}")
-def test_gemm_small(M, shape):
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 33, 64, 100, 256])
+@pytest.mark.parametrize("shape", [(3, 384), (129, 2176), (300, 1024), (64, 128), (65, 640)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_gemm_small(xdt, M, shape):
+    # weight rows around the 64-row block tile, K from one group (fewer groups
+    # than the block's four wavefronts) to 17 groups (uneven split)
     n, k = shape
     q, s, z = random_w4(n, k, seed=M * 13 + n)
-    x = workloads.to_dtype(workloads.gaussian(workloads.rng(78, M + n), (M, k), 1.0), "bf16")
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(78, M + n), (M, k), 1.0), xdt)
     gemv_case(q, s, z, x, torch.float32, f"gemm small M={M}", gemm=True)
-    gemv_case(q, s, z, x, torch.bfloat16, f"gemm small M={M} bf16", gemm=True)
+    gemv_case(q, s, z, x, TDT[xdt], f"gemm small M={M} {xdt}", gemm=True)
 
 
 @pytest.mark.parametrize("M", [16, 64, 256])
