@@ -113,7 +113,7 @@ def build_ops(dev):
                 assert st == 0, st
             ops.append(dict(name=f"w4a16_gemv B={B} {n}x{k}", fn=gemv, bytes=wb(n, k) + B * k * 2 + B * n * 2,
                             flops=2 * B * n * k, bound="hbm",
-                            kernel="gemv_valu_kernel" if B == 1 else "w4_mfma_skinny_kernel"))
+                            kernel="gemv_valu_kernel" if B == 1 else "w4_lds_kernel"))
 
     # Batched GEMM.
     wl3 = workloads.WORKLOADS["gemm"]
@@ -133,7 +133,7 @@ def build_ops(dev):
             assert st == 0, st
         bound = "mfma" if M >= 128 else "hbm"
         ops.append(dict(name=f"w4a16_gemm M={M} {n3}x{k3}", fn=gemm, bytes=wb(n3, k3) + M * k3 * 2 + M * n3 * 2,
-                        flops=2 * M * n3 * k3, bound=bound, kernel="w4_mfma_skinny_kernel"))
+                        flops=2 * M * n3 * k3, bound=bound, kernel="w4_lds_kernel"))
 
     # SmoothQuant W8A8.
     wl4 = workloads.WORKLOADS["smoothquant"]
@@ -175,6 +175,23 @@ def build_ops(dev):
     return ops, mats
 
 
+def gemv_traffic():
+    """HBM bytes per B=1 GEMV launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemv_valu_kernel_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    launches = list(rec["per_launch"].values())
+    return round(sum(v["hbm_read_bytes"] + v["hbm_write_bytes"] for v in launches) / len(launches))
+
+
 def cpu_baseline(mats, min_seconds=10.0, max_reps=8):
     """The CPU oracle's B=1 product for both 70B-class matrices, timed on the host."""
     import oracle  # test infrastructure: only this baseline leg uses it
@@ -207,6 +224,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 256 MiB (5 times), to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -214,6 +233,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        nbytes = 256 << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": nbytes, "calibrate_copy_bytes_written": nbytes,
+                          "copies": 5}), flush=True)
+        return
     print("bench: generating inputs and quantizing (untimed)", file=sys.stderr, flush=True)
     ops, mats = build_ops(dev)
     torch.cuda.synchronize()
@@ -289,7 +318,8 @@ def main():
             "weight_copies_rotated": COPIES,
         },
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": gemv_traffic(),
+                     "alg_bytes_per_launch": round(g_bytes / len(gemv1)),
                      "kernel": "gemv_valu_kernel (w4a16_gemv B=1), both matrices"},
         "breakdown": breakdown,
     }
