@@ -17,8 +17,9 @@
  *    launched and no output is written.  Argument errors are detected on the
  *    host before any HIP call.  Nothing throws or aborts across the ABI.
  *  * Pointers must be 16-byte aligned (QMM_EALIGN otherwise), except the
- *    per-row / per-column vectors (scales, zero-points, smoothing factors)
- *    which need only their element alignment.
+ *    per-row / per-column vectors (scales, zero-points, column maxima) which
+ *    need only their element alignment; the smoothing factors passed to the
+ *    INT8 quantizers are read 16 bytes at a time and must be 16-byte aligned.
  *
  * INT4 storage format (one format for every entry point):
  *  * codes  : uint8 [N, K/2].  Byte j of a row holds element 2j in bits 0-3

@@ -150,14 +150,16 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
   }
 
   __shared__ float red[kValuWaves][R * B];
-  if constexpr (R * B == 8) {
-    float v8[8];
+  if constexpr ((R * B) % 8 == 0) {
+    // Eight sums per wave_sum8: lane l ends up with the sum of value l >> 3.
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int h = 0; h < R * B / 8; ++h) {
+      float v8[8];
 #pragma unroll
-      for (int b = 0; b < B; ++b) v8[r * B + b] = acc[r][b];
-    const float v = wave_sum8(v8);          // lane l: sum of value l >> 3
-    if ((lane & 7) == 0) red[wave][lane >> 3] = v;
+      for (int i = 0; i < 8; ++i) v8[i] = acc[(8 * h + i) / B][(8 * h + i) % B];
+      const float v = wave_sum8(v8);
+      if ((lane & 7) == 0) red[wave][8 * h + (lane >> 3)] = v;
+    }
   } else {
 #pragma unroll
     for (int r = 0; r < R; ++r)

@@ -28,10 +28,16 @@ constexpr float kSmoothFloor = 1e-5f;
 constexpr int64_t kMaxK = 131008;
 
 // ----------------------------------------------------------------------------
-// Column absolute maxima (calibration statistics).  Thread = 8 consecutive
-// columns of a band of rows; one atomicMax per column per thread on the
-// float's bit pattern (non-negative floats order like unsigned integers).
+// Column absolute maxima (calibration statistics).  Block = 512 columns x a
+// band of 128 rows: lane l of wavefront w takes columns 8 l .. +8 of rows
+// 32 w .. +32 of the band, eight rows per batch of loads (each row read is 1
+// KiB contiguous per wavefront); the four wavefronts' maxima are combined in
+// LDS and each column gets one atomicMax per block, on the float's bit
+// pattern (non-negative floats order like unsigned integers).
 // ----------------------------------------------------------------------------
+constexpr int kCmCols = 512;
+constexpr int64_t kCmBand = 128;
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -39,36 +45,56 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p
 }
 
 template <int DT>
-__device__ __forceinline__ void colmax_band(const uint8_t* __restrict__ a, int64_t rows, int64_t cols, int64_t col8,
-                                            int64_t r0, int64_t r1, uint32_t* __restrict__ out) {
+__device__ __forceinline__ void colmax_band(const uint8_t* __restrict__ a, int64_t cols, int64_t col8, int64_t r0,
+                                            int64_t r1, float m[8]) {
   constexpr int kElem = DT == QMM_F32 ? 4 : 2;
-  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t r = r0; r < r1; ++r) {
-    float v[8];
-    Vec8<DT>::load(a + (r * cols + col8) * kElem, v);
+  constexpr int kRows = 8;   // rows loaded together, so their latencies overlap
+  for (int64_t rb = r0; rb < r1; rb += kRows) {
+    float v[kRows][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+    for (int j = 0; j < kRows; ++j) {
+      const int64_t r = (rb + j < r1) ? rb + j : r1 - 1;   // repeats the last row: max unchanged
+      Vec8<DT>::load(a + (r * cols + col8) * kElem, v[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kRows; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[j][i]));
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) atomicMax(out + col8 + i, __float_as_uint(m[i]));
 }
 
-// grid.x: column blocks of 2048; grid.y: row bands of the two matrices
-// (first `bands_x` bands belong to X, the rest to W).
+// grid.x: column blocks of 512; grid.y: row bands of the two matrices (the
+// first `bands_x` bands belong to X, the rest to W).
 template <int XDT, int WDT>
 __global__ __launch_bounds__(256) void colmax2_kernel(const uint8_t* __restrict__ X, int64_t M,
                                                       const uint8_t* __restrict__ W, int64_t N, int64_t K,
-                                                      int64_t band, int64_t bands_x, uint32_t* __restrict__ cx,
+                                                      int64_t bands_x, uint32_t* __restrict__ cx,
                                                       uint32_t* __restrict__ cw) {
-  const int64_t col8 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
-  if (col8 >= K) return;
+  __shared__ float red[4][kCmCols];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kCmCols;
+  const int64_t col8 = c0 + lane * 8;
   const int64_t yb = blockIdx.y;
-  if (yb < bands_x) {
-    const int64_t r0 = yb * band, r1 = (r0 + band < M) ? r0 + band : M;
-    colmax_band<XDT>(X, M, K, col8, r0, r1, cx);
-  } else {
-    const int64_t r0 = (yb - bands_x) * band, r1 = (r0 + band < N) ? r0 + band : N;
-    colmax_band<WDT>(W, N, K, col8, r0, r1, cw);
+  const bool isx = yb < bands_x;
+  const int64_t rows = isx ? M : N;
+  const int64_t band0 = (isx ? yb : yb - bands_x) * kCmBand;
+  const int64_t r0 = band0 + wave * (kCmBand / 4);
+  const int64_t r1e = r0 + kCmBand / 4;
+  const int64_t r1 = r1e < rows ? r1e : rows;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (col8 < K && r0 < r1) {
+    if (isx) colmax_band<XDT>(X, K, col8, r0, r1, m);
+    else colmax_band<WDT>(W, K, col8, r0, r1, m);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = m[i];
+  __syncthreads();
+  uint32_t* out = isx ? cx : cw;
+  for (int c = threadIdx.x; c < kCmCols; c += 256) {
+    if (c0 + c >= K) break;
+    const float v = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+    atomicMax(out + c0 + c, __float_as_uint(v));
   }
 }
 
@@ -93,20 +119,82 @@ __global__ __launch_bounds__(256) void smooth_finalize_kernel(const float* __res
 // ----------------------------------------------------------------------------
 // Per-row symmetric INT8 quantization with column smoothing.  One wavefront
 // per row; MODE 0 multiplies by the smoothing factor (weights), MODE 1
-// divides (activations); smooth == nullptr skips the smoothing.  The row is
-// processed in 8-element slices, twice: pass 1 finds the absmax of the
-// smoothed row, pass 2 recomputes the same smoothed values and quantizes.
-// CH slices per lane are kept in registers between the passes when the row
-// fits (K <= 512 * CH), otherwise pass 2 re-reads the row.
+// divides (activations, a correctly rounded division per element); SM false
+// skips the smoothing.  The row is read in batches of kRqChunks 8-element
+// chunks per lane (4096 elements), every load of a batch issued before any is
+// used.  Pass 1 finds the absmax of the smoothed row; pass 2 quantizes the
+// values kept in registers (rows of up to 4096) or re-reads the batch.
 // ----------------------------------------------------------------------------
-template <int MODE>
-__device__ __forceinline__ float smooth_op(float v, const float* smooth, int64_t k) {
-  if (smooth == nullptr) return v;
-  const float sj = smooth[k];
-  return MODE == 0 ? v * sj : v / sj;
+constexpr int kRqChunks = 8;
+constexpr int64_t kRqBatch = static_cast<int64_t>(kWave) * 8 * kRqChunks;   // 4096
+constexpr float kQ8Margin = 0.5f - 0x1p-12f;
+
+// clamp(rint(v / s), -128, 127) for 8 values, bit-identical to the correctly
+// rounded division.  Fast path t = v * rcp(s): with v_rcp_f32 within 1 ulp
+// and |v / s| <= 127 (|v| <= absmax = 127 s, or below the floor), |t - v/s|
+// is below 4e-5 and the fp32 rounding of v / s moves it by less than 8e-6, so
+// a t more than 2^-12 away from a half-integer rounds like v / s.  Chunks with
+// a value in that band, or a scale outside [2^-100, 2^100], divide exactly.
+__device__ __forceinline__ void quant8_int8(const float v[8], float s, float r, uint32_t* lo, uint32_t* hi) {
+  float k[8];
+  float dmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = v[i] * r;
+    k[i] = rintf(t);
+    dmax = fmaxf(dmax, fabsf(t - k[i]));
+  }
+  if (!((s >= 0x1p-100f) && (s <= 0x1p100f) && (dmax <= kQ8Margin))) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) k[i] = rintf(v[i] / s);
+  }
+  uint32_t l = 0, h = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float c = __builtin_amdgcn_fmed3f(k[i], -128.0f, kQ8);
+    const uint32_t byte = static_cast<uint32_t>(static_cast<int32_t>(c)) & 0xFFu;
+    if (i < 4) l |= byte << (8 * i);
+    else h |= byte << (8 * (i - 4));
+  }
+  *lo = l;
+  *hi = h;
 }
 
-template <int DT, int MODE, int CH>
+// Loads chunk c of the batch starting at `base` for every lane (zeros past K)
+// and applies the smoothing; all loads are issued before any arithmetic.
+template <int DT, int MODE, bool SM>
+__device__ __forceinline__ void rq_load_batch(const uint8_t* arow, const float* smooth, int64_t K, int64_t base,
+                                              int lane, float v[kRqChunks][8]) {
+  constexpr int kElem = DT == QMM_F32 ? 4 : 2;
+  float4 sm[kRqChunks][2];
+#pragma unroll
+  for (int c = 0; c < kRqChunks; ++c) {
+    const int64_t k = base + static_cast<int64_t>(c) * (kWave * 8) + lane * 8;
+    const int64_t kc = k < K ? k : K - 8;   // in bounds; the values are discarded below
+    Vec8<DT>::load(arow + kc * kElem, v[c]);
+    if constexpr (SM) {
+      sm[c][0] = *reinterpret_cast<const float4*>(smooth + kc);
+      sm[c][1] = *reinterpret_cast<const float4*>(smooth + kc + 4);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < kRqChunks; ++c) {
+    const int64_t k = base + static_cast<int64_t>(c) * (kWave * 8) + lane * 8;
+    if constexpr (SM) {
+      const float f[8] = {sm[c][0].x, sm[c][0].y, sm[c][0].z, sm[c][0].w,
+                          sm[c][1].x, sm[c][1].y, sm[c][1].z, sm[c][1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[c][i] = MODE == 0 ? v[c][i] * f[i] : v[c][i] / f[i];
+    }
+    if (k >= K) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[c][i] = 0.0f;
+    }
+  }
+}
+
+template <int DT, int MODE, bool SM>
 __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restrict__ a, const float* __restrict__ smooth,
                                                         int64_t rows, int64_t K, int8_t* __restrict__ q,
                                                         float* __restrict__ scale) {
@@ -115,56 +203,33 @@ __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restric
   const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (row >= rows) return;
   const uint8_t* arow = a + row * K * kElem;
-  const bool resident = K <= static_cast<int64_t>(kWave) * 8 * CH;
+  const bool resident = K <= kRqBatch;
 
-  float keep[CH][8];
+  float v[kRqChunks][8];
   float amax = 0.0f;
-  int ch = 0;
-  for (int64_t k = static_cast<int64_t>(lane) * 8; k < K; k += kWave * 8, ++ch) {
-    float v[8];
-    Vec8<DT>::load(arow + k * kElem, v);
+  for (int64_t base = 0; base < K; base += kRqBatch) {
+    rq_load_batch<DT, MODE, SM>(arow, smooth, K, base, lane, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[i] = smooth_op<MODE>(v[i], smooth, k + i);
-      amax = fmaxf(amax, fabsf(v[i]));
-    }
-    if (resident) {
+    for (int c = 0; c < kRqChunks; ++c)
 #pragma unroll
-      for (int c = 0; c < CH; ++c)
-        if (c == ch) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) keep[c][i] = v[i];
-        }
-    }
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
   }
   amax = wave_max(amax);
   const float s = fmaxf(amax, kAbsFloor) / kQ8;
   if (lane == 0) scale[row] = s;
+  const float r = __builtin_amdgcn_rcpf(s);
 
-  ch = 0;
-  for (int64_t k = static_cast<int64_t>(lane) * 8; k < K; k += kWave * 8, ++ch) {
-    float v[8];
-    if (resident) {
+  for (int64_t base = 0; base < K; base += kRqBatch) {
+    if (!resident) rq_load_batch<DT, MODE, SM>(arow, smooth, K, base, lane, v);
 #pragma unroll
-      for (int c = 0; c < CH; ++c)
-        if (c == ch) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = keep[c][i];
-        }
-    } else {
-      Vec8<DT>::load(arow + k * kElem, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = smooth_op<MODE>(v[i], smooth, k + i);
+    for (int c = 0; c < kRqChunks; ++c) {
+      const int64_t k = base + static_cast<int64_t>(c) * (kWave * 8) + lane * 8;
+      if (k < K) {
+        uint32_t lo, hi;
+        quant8_int8(v[c], s, r, &lo, &hi);
+        *reinterpret_cast<uint2*>(q + row * K + k) = make_uint2(lo, hi);
+      }
     }
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float t = __builtin_amdgcn_fmed3f(rintf(v[i] / s), -128.0f, kQ8);
-      const uint32_t b = static_cast<uint32_t>(static_cast<int32_t>(t)) & 0xFFu;
-      if (i < 4) lo |= b << (8 * i);
-      else hi |= b << (8 * (i - 4));
-    }
-    *reinterpret_cast<uint2*>(q + row * K + k) = make_uint2(lo, hi);
   }
 }
 
@@ -473,10 +538,18 @@ int launch_rowquant(const void* a, int dt, const float* smooth, int64_t rows, in
   const dim3 grid(static_cast<unsigned>(ceil_div(rows, 4)));
   const dim3 block(256);
   const uint8_t* p = static_cast<const uint8_t*>(a);
-  switch (dt) {
-    case QMM_BF16: rowquant8_kernel<QMM_BF16, MODE, 8><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
-    case QMM_F16: rowquant8_kernel<QMM_F16, MODE, 8><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
-    default: rowquant8_kernel<QMM_F32, MODE, 8><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+  if (smooth) {
+    switch (dt) {
+      case QMM_BF16: rowquant8_kernel<QMM_BF16, MODE, true><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      case QMM_F16: rowquant8_kernel<QMM_F16, MODE, true><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      default: rowquant8_kernel<QMM_F32, MODE, true><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+    }
+  } else {
+    switch (dt) {
+      case QMM_BF16: rowquant8_kernel<QMM_BF16, MODE, false><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      case QMM_F16: rowquant8_kernel<QMM_F16, MODE, false><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      default: rowquant8_kernel<QMM_F32, MODE, false><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+    }
   }
   return launch_status();
 }
@@ -487,7 +560,7 @@ int check_rowquant(const void* a, int dt, const float* smooth, int64_t rows, int
   if (rows <= 0 || K <= 0) return QMM_EINVAL;
   if (!float_dtype(dt)) return dt == QMM_I32 ? QMM_EUNSUPPORTED : QMM_EINVAL;
   if (K % 64 != 0) return QMM_EUNSUPPORTED;
-  if (!aligned(a, 16) || !aligned(q, 16) || !aligned(scale, 4) || (smooth && !aligned(smooth, 4)))
+  if (!aligned(a, 16) || !aligned(q, 16) || !aligned(scale, 4) || (smooth && !aligned(smooth, 16)))
     return QMM_EALIGN;
   return QMM_OK;
 }
@@ -547,13 +620,12 @@ extern "C" int sq_smooth_factors(const void* X, int x_dtype, int64_t M, const vo
   const unsigned fill_blocks = static_cast<unsigned>(ceil_div(K, 256));
   fill_zero_kernel<<<fill_blocks, 256, 0, s>>>(cx, K);
   fill_zero_kernel<<<fill_blocks, 256, 0, s>>>(cw, K);
-  const int64_t band = 32;
-  const int64_t bands_x = ceil_div(M, band);
-  const int64_t bands_w = ceil_div(N, band);
-  const dim3 grid(static_cast<unsigned>(ceil_div(K, 2048)), static_cast<unsigned>(bands_x + bands_w));
+  const int64_t bands_x = ceil_div(M, kCmBand);
+  const int64_t bands_w = ceil_div(N, kCmBand);
+  const dim3 grid(static_cast<unsigned>(ceil_div(K, kCmCols)), static_cast<unsigned>(bands_x + bands_w));
   const uint8_t* xp = static_cast<const uint8_t*>(X);
   const uint8_t* wp = static_cast<const uint8_t*>(W);
-#define QMM_COLMAX(XD, WD) colmax2_kernel<XD, WD><<<grid, 256, 0, s>>>(xp, M, wp, N, K, band, bands_x, cx, cw)
+#define QMM_COLMAX(XD, WD) colmax2_kernel<XD, WD><<<grid, 256, 0, s>>>(xp, M, wp, N, K, bands_x, cx, cw)
   if (x_dtype == QMM_BF16 && w_dtype == QMM_BF16) QMM_COLMAX(QMM_BF16, QMM_BF16);
   else if (x_dtype == QMM_F16 && w_dtype == QMM_F16) QMM_COLMAX(QMM_F16, QMM_F16);
   else if (x_dtype == QMM_F32 && w_dtype == QMM_F32) QMM_COLMAX(QMM_F32, QMM_F32);
@@ -608,7 +680,7 @@ extern "C" int smooth_quant_w8a8_gemm(const void* X, int x_dtype, const float* s
   if (K > kMaxK) return QMM_ERANGE;
   if (!workspace || workspace_bytes < sq_workspace_bytes(M, K) || !aligned(workspace, 16)) return QMM_EWORKSPACE;
   if (!aligned(X, 16) || !aligned(qW, 16) || !aligned(w_scale, 4) || !aligned(Y, 4) ||
-      (smooth && !aligned(smooth, 4)))
+      (smooth && !aligned(smooth, 16)))
     return QMM_EALIGN;
   int8_t* qX = static_cast<int8_t*>(workspace);
   float* xs = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
