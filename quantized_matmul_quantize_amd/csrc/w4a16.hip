@@ -378,13 +378,14 @@ __global__ __launch_bounds__(512) void w4_mfma_skinny_kernel(const uint8_t* __re
 // the end in a fixed order.
 //
 // Operands reach LDS by buffer loads that write LDS directly, each wavefront
-// into rings of its own (no block barrier in the main loop):
+// into rings of its own, D groups ahead (no block barrier in the main loop):
 //  * activations, one group = MT rows x 256 bytes: sixteen lanes fetch one
 //    row's 256 bytes; 16-byte chunk j of row r sits at position j ^ (r & 15);
-//  * codes, one group = 64 rows x 64 bytes: four lanes fetch one row's 64
-//    bytes; 16-byte part p of row r (of a 16-row slice) sits at slot
+//  * codes, one group = 16 NT rows x 64 bytes (NT = 2 or 4 slices of 16
+//    weight rows per block): four lanes fetch one row's 64 bytes; 16-byte part p of row r (of a 16-row slice) sits at slot
 //    4 r + (p ^ h(r)), h(r) = ((r >> 1) ^ (r >> 3)) & 3;
-//  * scales, one group = 64 floats;
+//  * scales, one group = 16 NT floats (one 4-byte load per lane; lanes past
+//    the block's rows fall outside the buffer and read 0);
 // and the block's zero-point bytes are copied to LDS once.  Both swizzles make
 // the fragment reads below free of bank conflicts.
 //
@@ -396,20 +397,25 @@ __global__ __launch_bounds__(512) void w4_mfma_skinny_kernel(const uint8_t* __re
 // and each group is folded as  acc += s * (P - (off + z) * X_g).
 // ----------------------------------------------------------------------------
 constexpr int kLdsWaves = 4;
-constexpr int kLdsRows = 64;                  // weight rows per block
-constexpr int kXRing = 3;                     // activation groups in flight per wavefront
-constexpr int kCodeGroupBytes = kLdsRows * kGroup / 2;   // 4 KiB
+constexpr int kLdsRows = 64;                  // weight rows per block (NT = 4 slices of 16)
 constexpr size_t kLdsBytesMax = 160 * 1024;
-constexpr int kScaleGroupBytes = kLdsRows * 4;           // 256 B
+constexpr int kScaleGroupBytes = 64 * 4;      // one scale load: 64 lanes x 4 bytes
 
-template <int MT>
+template <int MT, int NT>
 struct LdsCfg {
-  static constexpr int kWRing = MT <= 16 ? 4 : 3;        // code/scale ring positions (>= 3)
+  static constexpr int kRows = 16 * NT;                    // weight rows per block
+  static constexpr int kCodeGroupBytes = kRows * kGroup / 2;
+  // Groups loaded ahead per wavefront (ring depth D + 1 for activations,
+  // codes and scales alike).  D = 1 for 16 tokens keeps a block at ~66 KiB of
+  // LDS, so two blocks share a compute unit.
+  static constexpr int kD = MT <= 16 ? 1 : 2;
+  static constexpr int kRing = kD + 1;
   static constexpr int kXBytes = MT * kGroup * 2;        // one activation group
-  static constexpr int kWaveBytes = kXRing * kXBytes + kWRing * (kCodeGroupBytes + kScaleGroupBytes);
+  static constexpr int kWaveBytes = kRing * (kXBytes + kCodeGroupBytes + kScaleGroupBytes);
   static constexpr int kXLoads = MT / 4;                 // 1 KiB load instructions per activation group
-  static constexpr int kLoadsPerGroup = kXLoads + 4 + 1;
-  static constexpr int kPartPitch = 68;                  // floats per row of a partial tile
+  static constexpr int kLoadsPerGroup = kXLoads + NT + 1;
+  static constexpr int kPartPitch = kRows + 4;           // floats per row of a partial tile
+  static_assert(kLdsWaves * MT * kPartPitch * 4 <= kLdsWaves * kWaveBytes, "partial tiles fit the rings");
 };
 
 __device__ __forceinline__ int code_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -426,15 +432,18 @@ constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource, 32-bit data f
 // Host and device: it is called from lambdas, which HIP compiles for both sides.
 __host__ __device__ inline lds_ptr_t lds_at(uint32_t byte) { return (lds_ptr_t)(uintptr_t)byte; }
 
-template <int XDT, int YDT, int MT>
+template <int XDT, int YDT, int MT, int NT>
 __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__ codes,
                                                      const float* __restrict__ scales,
                                                      const uint8_t* __restrict__ zeros, int64_t N, int64_t K,
                                                      const uint16_t* __restrict__ x, int64_t M,
                                                      void* __restrict__ y) {
-  using Cfg = LdsCfg<MT>;
+  using Cfg = LdsCfg<MT, NT>;
+  constexpr int kRows = Cfg::kRows;
+  constexpr int kCodeGroupBytes = Cfg::kCodeGroupBytes;
   using Mg = Int4Magic<XDT>;
-  constexpr int WR = Cfg::kWRing;
+  constexpr int RG = Cfg::kRing;
+  constexpr int D = Cfg::kD;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -448,22 +457,22 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
   // token tiles fastest, so the token tiles of one weight slice run together
   // on one XCD and the slice's codes come from HBM once.
   const int64_t mtiles = (M + MT - 1) / MT;
-  const int64_t ntiles = (N + kLdsRows - 1) / kLdsRows;
+  const int64_t ntiles = (N + kRows - 1) / kRows;
   const int64_t T = mtiles * ntiles;
   const int64_t per = (T + 7) / 8;
   const int64_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= T) return;
-  const int64_t n0 = (t / mtiles) * kLdsRows;
+  const int64_t n0 = (t / mtiles) * kRows;
   const int64_t m0 = (t % mtiles) * MT;
-  const int64_t nrows = (N - n0 < kLdsRows) ? N - n0 : kLdsRows;
+  const int64_t nrows = (N - n0 < kRows) ? N - n0 : kRows;
   const int64_t mrows = (M - m0 < MT) ? M - m0 : MT;
 
-  // LDS: per-wavefront rings, then the zero-point table [64][zb].
+  // LDS: per-wavefront rings, then the zero-point table [kRows][zb].
   const uint32_t lbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const uint32_t wbase = lbase + wave * Cfg::kWaveBytes;
   const uint32_t xring = wbase;
-  const uint32_t cring = wbase + kXRing * Cfg::kXBytes;
-  const uint32_t sring = cring + WR * kCodeGroupBytes;
+  const uint32_t cring = wbase + RG * Cfg::kXBytes;
+  const uint32_t sring = cring + RG * kCodeGroupBytes;
   uint8_t* const ztab = lds + kLdsWaves * Cfg::kWaveBytes;
 
   // Buffer resources sized to the tile's valid rows: rows past M / N read 0.
@@ -487,7 +496,7 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
     xoff[q] = r * kb2 + (((lane & 15) ^ (r & 15)) * 16);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NT; ++q) {
     const int r = lane >> 2;
     coff[q] = (16 * q + r) * kh + (((lane & 3) ^ code_swz(r)) * 16);
   }
@@ -497,40 +506,38 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
   auto grp = [&](int i) { return wave + kLdsWaves * min(i, max(ng - 1, 0)); };   // clamped, in range
   auto issue_x = [&](int i) {
     const int g = min(grp(i), G - 1);
-    const uint32_t dst = xring + (i % kXRing) * Cfg::kXBytes;
+    const uint32_t dst = xring + (i % RG) * Cfg::kXBytes;
 #pragma unroll
     for (int q = 0; q < Cfg::kXLoads; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, lds_at(dst + q * 1024), 16, xoff[q], g * 256, 0, 0);
   };
   auto issue_w = [&](int i) {
     const int g = min(grp(i), G - 1);
-    const uint32_t dst = cring + (i % WR) * kCodeGroupBytes;
+    const uint32_t dst = cring + (i % RG) * kCodeGroupBytes;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < NT; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, lds_at(dst + q * 1024), 16, coff[q], g * 64, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, lds_at(sring + (i % WR) * kScaleGroupBytes), 4, soff, g * 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, lds_at(sring + (i % RG) * kScaleGroupBytes), 4, soff, g * 4, 0, 0);
   };
 
-  // Issue slots j = -2, -1, 0, 1, ...: slot j loads the activations of
-  // group j + 2 into the ring position group j - 1 used, and the codes and
-  // scales of group j + WR - 1 likewise; codes of groups 0 .. WR-4 go first.
-  // Before group i is computed every slot <= i - 2 must have landed.
-  for (int i = 0; i < WR - 3; ++i) issue_w(i);
-  issue_x(0);
-  issue_w(WR - 3);
-  issue_x(1);
-  issue_w(WR - 2);
-  for (int i = tid; i < kLdsRows * zb; i += 256) {
+  // Iteration i issues the loads of group i + D into the ring position group
+  // i - 1 used; the prologue issues groups 0 .. D-1.  Before group i is
+  // computed only the loads of the last D iterations may be in flight.
+  for (int i = 0; i < D; ++i) {
+    issue_x(i);
+    issue_w(i);
+  }
+  for (int i = tid; i < kRows * zb; i += 256) {
     const int r = i / zb;
     ztab[i] = (r < nrows) ? zeros[(n0 + r) * zb + (i - r * zb)] : 0;
   }
   __syncthreads();   // zero-point table
 
-  f32x4 acc[MT / 16][4];
+  f32x4 acc[MT / 16][NT];
 #pragma unroll
   for (int mt = 0; mt < MT / 16; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const uint32_t magic = vgpr_const(Mg::kMagic);
   const uint32_t ones[4] = {Mg::one_pair, Mg::one_pair, Mg::one_pair, Mg::one_pair};
   const int fr = lane & 15;
@@ -538,24 +545,24 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
   const int crd = (4 * fr + (fp ^ code_swz(fr))) * 16;   // code fragment slot (per 16-row slice)
 
   for (int i = 0; i < ng; ++i) {
-    issue_x(i + 2);
-    issue_w(i + WR - 1);
-    wait_vm<2 * Cfg::kLoadsPerGroup>();
+    issue_x(i + D);
+    issue_w(i + D);
+    wait_vm<D * Cfg::kLoadsPerGroup>();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int g = wave + kLdsWaves * i;
-    const uint8_t* xg = lds + (xring - lbase) + (i % kXRing) * Cfg::kXBytes;
-    const uint8_t* cg = lds + (cring - lbase) + (i % WR) * kCodeGroupBytes;
-    const float* sg = reinterpret_cast<const float*>(lds + (sring - lbase) + (i % WR) * kScaleGroupBytes);
-    u32x4 cw[4];
-    float sv[4], zo[4];
+    const uint8_t* xg = lds + (xring - lbase) + (i % RG) * Cfg::kXBytes;
+    const uint8_t* cg = lds + (cring - lbase) + (i % RG) * kCodeGroupBytes;
+    const float* sg = reinterpret_cast<const float*>(lds + (sring - lbase) + (i % RG) * kScaleGroupBytes);
+    u32x4 cw[NT];
+    float sv[NT], zo[NT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       cw[nt] = *reinterpret_cast<const u32x4*>(cg + nt * 1024 + crd);
       sv[nt] = sg[16 * nt + fr];
       const uint32_t zbyte = ztab[(16 * nt + fr) * zb + (g >> 1)];
       zo[nt] = Mg::offset + static_cast<float>((g & 1) ? (zbyte >> 4) : (zbyte & 15u));
     }
-    f32x4 part[MT / 16][4], xs[MT / 16];
+    f32x4 part[MT / 16][NT], xs[MT / 16];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint32_t xa[MT / 16][4];
@@ -570,7 +577,7 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
       for (int mt = 0; mt < MT / 16; ++mt)
         xs[mt] = mfma16x16x32<XDT>(xa[mt], ones, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : xs[mt]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         uint32_t wb[4];
         Mg::unpack(cw[nt][c], magic, wb);
 #pragma unroll
@@ -581,7 +588,7 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
 #pragma unroll
     for (int mt = 0; mt < MT / 16; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[mt][nt][e] = fmaf(sv[nt], fmaf(-zo[nt], xs[mt][e], part[mt][nt][e]), acc[mt][nt][e]);
   }
@@ -594,16 +601,17 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
 #pragma unroll
   for (int mt = 0; mt < MT / 16; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         parts[(wave * MT + 16 * mt + 4 * fp + e) * Cfg::kPartPitch + 16 * nt + fr] = acc[mt][nt][e];
   __syncthreads();
-  // Sum the four partials (wavefront order 0..3) and store: thread -> token
-  // row tid / 8 (+32 per pass), 8 consecutive weight rows.
-  for (int o = tid; o < MT * 8; o += 256) {
-    const int r = o >> 3;
-    const int c0 = (o & 7) * 8;
+  // Sum the four partials (wavefront order 0..3) and store: a thread takes 8
+  // consecutive weight rows of one token row.
+  constexpr int kOct = kRows / 8;
+  for (int o = tid; o < MT * kOct; o += 256) {
+    const int r = o / kOct;
+    const int c0 = (o % kOct) * 8;
     const int64_t m = m0 + r;
     if (m >= M) continue;
     float v[8];
@@ -705,26 +713,36 @@ void launch_skinny_m(int64_t M, const uint8_t* codes, const float* scales, const
 
 // LDS-tiled kernel: MT = 16 for up to 16 tokens, else 32.  Returns false
 // (nothing launched) when the zero-point table would not fit in LDS.
-template <int XDT, int YDT, int MT>
+template <int XDT, int YDT, int MT, int NT>
 bool launch_lds_t(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                   const uint16_t* x, int64_t M, void* y, hipStream_t s) {
-  using Cfg = LdsCfg<MT>;
+  using Cfg = LdsCfg<MT, NT>;
   const int64_t G = K / kGroup;
-  const size_t lds = static_cast<size_t>(kLdsWaves) * Cfg::kWaveBytes + static_cast<size_t>(kLdsRows) * ((G + 1) / 2);
+  const size_t lds = static_cast<size_t>(kLdsWaves) * Cfg::kWaveBytes + static_cast<size_t>(Cfg::kRows) * ((G + 1) / 2);
   if (lds > kLdsBytesMax) return false;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_lds_kernel<XDT, YDT, MT>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_lds_kernel<XDT, YDT, MT, NT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  const int64_t tiles = ceil_div(M, MT) * ceil_div(N, kLdsRows);
+  const int64_t tiles = ceil_div(M, MT) * ceil_div(N, Cfg::kRows);
   const dim3 grid(static_cast<unsigned>(ceil_div(tiles, 8) * 8));
-  w4_lds_kernel<XDT, YDT, MT><<<grid, dim3(kLdsWaves * kWave), lds, s>>>(codes, scales, zeros, N, K, x, M, y);
+  w4_lds_kernel<XDT, YDT, MT, NT><<<grid, dim3(kLdsWaves * kWave), lds, s>>>(codes, scales, zeros, N, K, x, M, y);
   return true;
+}
+
+// 32 weight rows per block instead of 64 when 64-row tiles would leave
+// compute units without a block.
+template <int XDT, int YDT, int MT>
+bool launch_lds_m(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                  const uint16_t* x, int64_t M, void* y, hipStream_t s) {
+  if (ceil_div(M, MT) * ceil_div(N, kLdsRows) < static_cast<int64_t>(device_cus()))
+    return launch_lds_t<XDT, YDT, MT, 2>(codes, scales, zeros, N, K, x, M, y, s);
+  return launch_lds_t<XDT, YDT, MT, 4>(codes, scales, zeros, N, K, x, M, y, s);
 }
 
 template <int XDT, int YDT>
 bool launch_lds(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                 const uint16_t* x, int64_t M, void* y, hipStream_t s) {
-  if (M <= 16) return launch_lds_t<XDT, YDT, 16>(codes, scales, zeros, N, K, x, M, y, s);
-  return launch_lds_t<XDT, YDT, 32>(codes, scales, zeros, N, K, x, M, y, s);
+  if (M <= 16) return launch_lds_m<XDT, YDT, 16>(codes, scales, zeros, N, K, x, M, y, s);
+  return launch_lds_m<XDT, YDT, 32>(codes, scales, zeros, N, K, x, M, y, s);
 }
 
 // Tokens >= 2 (or the GEMM): the LDS-tiled kernel, else the skinny kernel

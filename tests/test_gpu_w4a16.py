@@ -95,6 +95,17 @@ def test_gemm_small(xdt, M, shape):
     gemv_case(q, s, z, x, TDT[xdt], f"gemm small M={M} {xdt}", gemm=True)
 
 
+@pytest.mark.parametrize("M", [5, 40])
+def test_gemm_wide_ragged(M):
+    # enough weight rows that a block takes 64 of them (the small shapes above
+    # get 32-row blocks), with a 37-row tail
+    n, k = 257 * 64 + 37 - 64, 384
+    q, s, z = random_w4(n, k, seed=M + 3)
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(79, M), (M, k), 1.0), "bf16")
+    gemv_case(q, s, z, x, torch.float32, f"gemm wide M={M}", gemm=True)
+    gemv_case(q, s, z, x, torch.bfloat16, f"gemm wide M={M} bf16", gemm=True)
+
+
 @pytest.mark.parametrize("M", [16, 64, 256])
 def test_gemm_full_size(M):
     wl = workloads.WORKLOADS["gemm"]
