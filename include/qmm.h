@@ -122,11 +122,10 @@ int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  * Source: "How quantization works" ("Inference view"); "Quantization from
  * Scratch" ("What it buys at decode", growing batch).
  * X : [M, K] QMM_BF16 or QMM_F16.  Y : [M, N] of X's type or QMM_F32.
- * M >= 1, group 128.  A block keeps the zero points of its 32 or 64 weight
- * rows in LDS, which bounds K: K <= 53248 is always served for M > 16 and
- * K <= 385024 for M <= 16 (more when the block takes 32 rows); beyond that
- * bf16 runs a slower kernel without the table and fp16 returns
- * QMM_EUNSUPPORTED.
+ * M >= 1, group 128.  A block keeps the zero points of its weight rows in
+ * LDS, which bounds K: K <= 53248 is always served for M > 16 and
+ * K <= 385024 for M <= 16; beyond that bf16 runs a slower kernel without the
+ * table and fp16 returns QMM_EUNSUPPORTED.
  * ------------------------------------------------------------------------- */
 int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                int group, const void* X, int x_dtype, int64_t M, void* Y, int y_dtype, void* stream);

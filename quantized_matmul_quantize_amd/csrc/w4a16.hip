@@ -632,6 +632,215 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
 }
 
 // ----------------------------------------------------------------------------
+// MFMA kernel for larger token counts: a block computes a BM x 128 tile of Y
+// (BM = 64 tokens), its four wavefronts each BM tokens x 32 weight
+// rows, walking K one group at a time in lock step.  The activation tile of a
+// group is loaded to LDS once per block and shared by the four wavefronts;
+// each wavefront loads the codes and scales of its own 32 rows.  Groups are
+// staged kTileD ahead in kTileD + 1 slots, with one block barrier per group.
+// LDS layout of a slot (same swizzles as the kernel above):
+//  * activations, BM rows x 256 bytes, chunk j of row r at position j ^ (r & 15);
+//  * codes, 8 slices of 16 rows x 64 bytes, part p of row r at 4 r + (p ^ h(r));
+//  * scales, 256 bytes per wavefront: its 32 rows, loaded twice over.
+// Two blocks of BM = 64 fit a compute unit (about 75 KiB each at K = 4096),
+// so each SIMD interleaves the ALU work of one wavefront with the matrix work
+// of another.
+// ----------------------------------------------------------------------------
+constexpr int kTileN = 128;
+constexpr int kTileD = 2;
+constexpr int kTileSlots = kTileD + 1;
+
+template <int BM>
+struct TileCfg {
+  static constexpr int kXBytes = BM * kGroup * 2;
+  static constexpr int kCodeBytes = kTileN * kGroup / 2;          // 8 KiB
+  static constexpr int kScaleBytes = kLdsWaves * 256;
+  static constexpr int kSlotBytes = kXBytes + kCodeBytes + kScaleBytes;
+  static constexpr int kXLoads = BM / 16;                          // per wavefront per group
+  static constexpr int kLoads = kXLoads + 2 + 1;
+  static constexpr int kPartPitch = kTileN + 4;
+  static_assert(BM * kPartPitch * 4 <= kTileSlots * kSlotBytes, "output tile fits the slots");
+};
+
+// Loads of group i (clamped to the last group: past the end it reloads a
+// group that is never read) into slot i % kTileSlots, kLoads instructions.
+// (The LDS destinations are cast in place: in the host pass a function
+// template that calls lds_at is dropped from overload resolution.)
+template <int BM>
+__device__ __forceinline__ void tile_issue(int i, int G, int wave, uint32_t lbase, __amdgpu_buffer_rsrc_t xr,
+                                           __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr, const int* xoff,
+                                           const int* coff, int soff) {
+  using Cfg = TileCfg<BM>;
+  const int g = min(i, G - 1);
+  const uint32_t slot = lbase + (i % kTileSlots) * Cfg::kSlotBytes;
+#pragma unroll
+  for (int q = 0; q < Cfg::kXLoads; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(uintptr_t)(slot + (wave * Cfg::kXLoads + q) * 1024), 16,
+                                             xoff[q], g * 256, 0, 0);
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_ptr_t)(uintptr_t)(slot + Cfg::kXBytes + (2 * wave + q) * 1024),
+                                             16, coff[q], g * 64, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      sr, (lds_ptr_t)(uintptr_t)(slot + Cfg::kXBytes + Cfg::kCodeBytes + wave * 256), 4, soff, g * 4, 0, 0);
+}
+
+template <int XDT, int YDT, int BM>
+__global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict__ codes,
+                                                      const float* __restrict__ scales,
+                                                      const uint8_t* __restrict__ zeros, int64_t N, int64_t K,
+                                                      const uint16_t* __restrict__ x, int64_t M,
+                                                      void* __restrict__ y) {
+  using Cfg = TileCfg<BM>;
+  using Mg = Int4Magic<XDT>;
+  constexpr int MT = BM / 16;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int G = static_cast<int>(K / kGroup);
+  const int zb = (G + 1) / 2;
+
+  // Tile order as in the kernel above: consecutive tiles per XCD, token tiles
+  // fastest, so the blocks sharing a weight slice run together on one XCD.
+  const int64_t mtiles = (M + BM - 1) / BM;
+  const int64_t ntiles = (N + kTileN - 1) / kTileN;
+  const int64_t T = mtiles * ntiles;
+  const int64_t per = (T + 7) / 8;
+  const int64_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= T) return;
+  const int64_t n0 = (t / mtiles) * kTileN;
+  const int64_t m0 = (t % mtiles) * BM;
+  const int64_t nrows = (N - n0 < kTileN) ? N - n0 : kTileN;
+  const int64_t mrows = (M - m0 < BM) ? M - m0 : BM;
+
+  const uint32_t lbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  uint8_t* const ztab = lds + kTileSlots * Cfg::kSlotBytes;
+
+  // Buffer resources sized to the tile's valid rows: rows past M / N read 0.
+  const int kb2 = static_cast<int>(K) * 2;
+  const int kh = static_cast<int>(K / 2);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + m0 * K), 0, static_cast<int>(mrows) * kb2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(codes + n0 * (K / 2)), 0, static_cast<int>(nrows) * kh, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scales + n0 * G), 0, static_cast<int>(nrows) * G * 4, kBufferWord3);
+
+  // Load q of this wavefront: activation rows 4 (wave MT + q) .. +4, code
+  // slice 2 wave + q, and its 32 scale rows (lane l: row 32 wave + l % 32).
+  int xoff[4], coff[2];
+  static_assert(Cfg::kXLoads <= 4, "activation loads per group");
+#pragma unroll
+  for (int q = 0; q < Cfg::kXLoads; ++q) {
+    const int r = 4 * (wave * Cfg::kXLoads + q) + (lane >> 4);
+    xoff[q] = r * kb2 + (((lane & 15) ^ (r & 15)) * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = lane >> 2;
+    coff[q] = (16 * (2 * wave + q) + r) * kh + (((lane & 3) ^ code_swz(r)) * 16);
+  }
+  const int soff = (32 * wave + (lane & 31)) * G * 4;
+
+
+  for (int i = 0; i < kTileD; ++i) tile_issue<BM>(i, G, wave, lbase, xr, cr, sr, xoff, coff, soff);
+  for (int i = tid; i < kTileN * zb; i += 256) {
+    const int r = i / zb;
+    ztab[i] = (r < nrows) ? zeros[(n0 + r) * zb + (i - r * zb)] : 0;
+  }
+
+  f32x4 acc[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint32_t magic = vgpr_const(Mg::kMagic);
+  const uint32_t ones[4] = {Mg::one_pair, Mg::one_pair, Mg::one_pair, Mg::one_pair};
+  const int fr = lane & 15;
+  const int fp = lane >> 4;
+  const int crd = (4 * fr + (fp ^ code_swz(fr))) * 16;
+
+  for (int i = 0; i < G; ++i) {
+    // Group i has landed for this wavefront (only group i + 1's loads may be
+    // outstanding); after the barrier it has landed for every wavefront, and
+    // every wavefront is done with the slot of group i - 1, which group
+    // i + kTileD now refills.
+    wait_vm<(kTileD - 1) * Cfg::kLoads>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    tile_issue<BM>(i + kTileD, G, wave, lbase, xr, cr, sr, xoff, coff, soff);
+    const uint8_t* xg = lds + (i % kTileSlots) * Cfg::kSlotBytes;
+    const uint8_t* cg = xg + Cfg::kXBytes;
+    const float* sg = reinterpret_cast<const float*>(cg + Cfg::kCodeBytes + wave * 256);
+    u32x4 cw[2];
+    float sv[2], zo[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      cw[nt] = *reinterpret_cast<const u32x4*>(cg + (2 * wave + nt) * 1024 + crd);
+      sv[nt] = sg[16 * nt + fr];
+      const uint32_t zbyte = ztab[(32 * wave + 16 * nt + fr) * zb + (i >> 1)];
+      zo[nt] = Mg::offset + static_cast<float>((i & 1) ? (zbyte >> 4) : (zbyte & 15u));
+    }
+    f32x4 part[MT][2], xs[MT];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t xa[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xg + (16 * mt + fr) * 256 + (((4 * fp + c) ^ fr) * 16));
+        const uint32_t aw[4] = {v.x, v.y, v.z, v.w};
+        permute_pairs(aw, xa[mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        xs[mt] = mfma16x16x32<XDT>(xa[mt], ones, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : xs[mt]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        uint32_t wb[4];
+        Mg::unpack(cw[nt][c], magic, wb);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          part[mt][nt] = mfma16x16x32<XDT>(xa[mt], wb, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : part[mt][nt]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mt][nt][e] = fmaf(sv[nt], fmaf(-zo[nt], xs[mt][e], part[mt][nt][e]), acc[mt][nt][e]);
+  }
+  wait_vm<0>();
+  __syncthreads();   // every slot is drained; the LDS now holds the output tile
+
+  // Output tile [BM][kPartPitch] floats: D lane l of (mt, nt) holds tokens
+  // 16 mt + 4 (l / 16) + e, weight row 32 wave + 16 nt + l % 16.
+  float* tile = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        tile[(16 * mt + 4 * fp + e) * Cfg::kPartPitch + 32 * wave + 16 * nt + fr] = acc[mt][nt][e];
+  __syncthreads();
+  // A thread stores 8 consecutive weight rows of one token row.
+  for (int o = tid; o < BM * (kTileN / 8); o += 256) {
+    const int r = o / (kTileN / 8);
+    const int c0 = (o % (kTileN / 8)) * 8;
+    const int64_t m = m0 + r;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t n = n0 + c0 + j;
+      if (n < N) store_y<YDT>(y, m * N + n, tile[r * Cfg::kPartPitch + c0 + j]);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Host side.
 // ----------------------------------------------------------------------------
 int check_common(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
@@ -738,10 +947,30 @@ bool launch_lds_m(const uint8_t* codes, const float* scales, const uint8_t* zero
   return launch_lds_t<XDT, YDT, MT, 4>(codes, scales, zeros, N, K, x, M, y, s);
 }
 
+template <int XDT, int YDT, int BM>
+bool launch_tile_t(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                   const uint16_t* x, int64_t M, void* y, hipStream_t s) {
+  using Cfg = TileCfg<BM>;
+  const int64_t G = K / kGroup;
+  const size_t lds = static_cast<size_t>(kTileSlots) * Cfg::kSlotBytes + static_cast<size_t>(kTileN) * ((G + 1) / 2);
+  if (lds > kLdsBytesMax) return false;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_tile_kernel<XDT, YDT, BM>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  const int64_t tiles = ceil_div(M, BM) * ceil_div(N, kTileN);
+  const dim3 grid(static_cast<unsigned>(ceil_div(tiles, 8) * 8));
+  w4_tile_kernel<XDT, YDT, BM><<<grid, dim3(kLdsWaves * kWave), lds, s>>>(codes, scales, zeros, N, K, x, M, y);
+  return true;
+}
+
 template <int XDT, int YDT>
 bool launch_lds(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                 const uint16_t* x, int64_t M, void* y, hipStream_t s) {
   if (M <= 16) return launch_lds_m<XDT, YDT, 16>(codes, scales, zeros, N, K, x, M, y, s);
+  // The shared-tile kernel once its 64 x 128 tiles give every compute unit a
+  // block; below that the split-K kernel's smaller tiles keep more units busy.
+  if (M > 32 && ceil_div(M, 64) * ceil_div(N, kTileN) >= static_cast<int64_t>(device_cus()) &&
+      launch_tile_t<XDT, YDT, 64>(codes, scales, zeros, N, K, x, M, y, s))
+    return true;
   return launch_lds_m<XDT, YDT, 32>(codes, scales, zeros, N, K, x, M, y, s);
 }
 

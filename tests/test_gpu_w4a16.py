@@ -95,10 +95,11 @@ def test_gemm_small(xdt, M, shape):
     gemv_case(q, s, z, x, TDT[xdt], f"gemm small M={M} {xdt}", gemm=True)
 
 
-@pytest.mark.parametrize("M", [5, 40])
+@pytest.mark.parametrize("M", [5, 40, 100, 200])
 def test_gemm_wide_ragged(M):
-    # enough weight rows that a block takes 64 of them (the small shapes above
-    # get 32-row blocks), with a 37-row tail
+    # enough weight rows that the split-K kernel takes 64 rows per block (the
+    # small shapes above get 32-row blocks) and, for M = 100 and 200, that the
+    # shared-tile kernel runs (64 x 128 tiles, ragged in M); a 37-row tail
     n, k = 257 * 64 + 37 - 64, 384
     q, s, z = random_w4(n, k, seed=M + 3)
     x = workloads.to_dtype(workloads.gaussian(workloads.rng(79, M), (M, k), 1.0), "bf16")
