@@ -22,9 +22,13 @@
  *    INT8 quantizers are read 16 bytes at a time and must be 16-byte aligned.
  *
  * INT4 storage format (one format for every entry point):
- *  * codes  : uint8 [N, K/2].  Byte j of a row holds element 2j in bits 0-3
- *             and element 2j+1 in bits 4-7 (so 32-bit word w holds elements
- *             8w..8w+7, element 8w+i at bits 4i..4i+3).
+ *  * codes  : uint8 [N, K/2], read as little-endian 32-bit words: word w of
+ *             a row holds elements 8w..8w+7, element 8w+2i in bits 4i..4i+3
+ *             and element 8w+2i+1 in bits 16+4i..16+4i+3 (i = 0..3).  So
+ *             byte 0 holds elements 0 and 2, byte 1 elements 4 and 6, byte 2
+ *             elements 1 and 3, byte 3 elements 5 and 7 (low nibble first).
+ *             This order lets the kernels expand a word into four pairs of
+ *             consecutive weights with one shift and one AND-OR per pair.
  *  * scales : float32 [N, G], G = K / group.
  *  * zeros  : uint8 [N, ceil(G/2)], zero-point of group 2j in the low nibble
  *             of byte j and of group 2j+1 in the high nibble (an odd G leaves

@@ -49,6 +49,7 @@ def lib() -> ctypes.CDLL:
             "oq_sym_quantize": [P, I64, I64, I64, I, F, P, P],
             "oq_sym_dequantize": [P, P, I64, I64, I64, P],
             "oq_pack_nibbles": [P, I64, I64, P],
+            "oq_pack_codes": [P, I64, I64, P],
             "oq_matmul_nt_f64": [P, P, I64, I64, I64, P],
             "oq_int8_matmul_nt": [P, P, I64, I64, I64, P],
             "oq_rescale_f64": [P, P, P, I64, I64, P],
@@ -121,10 +122,23 @@ def pack_nibbles(vals) -> np.ndarray:
     return out
 
 
+def pack_codes(vals) -> np.ndarray:
+    """Row-wise code words: per run of 8 elements one little-endian 32-bit word,
+    element 2i in bits 4i.., element 2i+1 in bits 16+4i.. (the layout of the
+    library's weight codes; the pages fix only half a byte per weight)."""
+    vals = np.ascontiguousarray(vals, np.uint8)
+    if vals.ndim == 1:
+        vals = vals[None, :]
+    rows, count = vals.shape
+    out = np.empty((rows, count // 2), np.uint8)
+    _check(lib().oq_pack_codes(_p(vals), rows, count, _p(out)), "pack_codes")
+    return out
+
+
 def quantize_groupwise_packed(w, group: int = 128):
     """The stored INT4 format: (codes [N, K/2] u8, scales [N, G] f32, zeros [N, ceil(G/2)] u8)."""
     q, s, z = asym_quantize(w, group, 4)
-    return pack_nibbles(q), s, pack_nibbles(z)
+    return pack_codes(q), s, pack_nibbles(z)
 
 
 # --------------------------------------------------------------------------

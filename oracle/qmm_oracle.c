@@ -182,6 +182,29 @@ int oq_pack_nibbles(const uint8_t* vals, int64_t rows, int64_t count, uint8_t* o
 }
 
 /* ------------------------------------------------------------------------ */
+/* Weight codes: the pages fix half a byte per weight but no order, so this  */
+/* follows the library's stated layout.  Each run of 8 elements of a row is  */
+/* one little-endian 32-bit word holding element 2i of the run in bits       */
+/* 4i..4i+3 and element 2i+1 in bits 16+4i..16+4i+3 (i = 0..3).  count must  */
+/* be a multiple of 8.                                                       */
+/* ------------------------------------------------------------------------ */
+int oq_pack_codes(const uint8_t* vals, int64_t rows, int64_t count, uint8_t* out)
+{
+    if (!vals || !out || rows < 0 || count < 0 || count % 8 != 0) return OQ_BAD_ARG;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t w = 0; w < count / 8; ++w) {
+            const uint8_t* e = vals + r * count + 8 * w;
+            uint32_t word = 0;
+            for (int i = 0; i < 4; ++i) {
+                word |= (uint32_t)(e[2 * i] & 0xF) << (4 * i);
+                word |= (uint32_t)(e[2 * i + 1] & 0xF) << (16 + 4 * i);
+            }
+            for (int b = 0; b < 4; ++b) out[r * (count / 2) + 4 * w + b] = (uint8_t)(word >> (8 * b));
+        }
+    return OQ_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Reference product C[m][n] = sum_k A[m][k] * B[n][k] in fp64 (B is stored  */
 /* [N, K] like a weight matrix, so C = A B^T).  For the W4A16 matmuls A is   */
 /* the activations and B the dequantized weights: the plain definition of   */

@@ -180,17 +180,21 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// ---- INT4 unpack -------------------------------------------------------------
-// A 32-bit code word holds elements e0..e7 (nibble i = element i).  The
-// kernels feed 16-bit pairs (e_i, e_{i+4}) to dot / MFMA instructions, with
-// the activations permuted the same way, so a sum over k is unchanged.
-// Each pair is built with a shift and one AND-OR that drop the nibbles into
-// the mantissa of a 16-bit float whose exponent makes one code step worth 1:
+// ---- INT4 code layout and unpack --------------------------------------------
+// A 32-bit code word holds 8 consecutive elements e0..e7 of a row, element i
+// in nibble code_nibble(i): the even elements in nibbles 0-3, the odd ones in
+// nibbles 4-7, so nibbles j and j + 4 hold the consecutive pair (e_2j, e_2j+1).
+// Each pair is built with a shift and one AND-OR that drop both nibbles into
+// the mantissas of a 16-bit float pair whose exponent makes one code step
+// worth 1:
 //   bf16: nibble at mantissa bits 0-3 of 0x4300 (128.0)  -> 128 + q exactly;
-//   fp16: nibble at mantissa bits 6-9 of 0x4C00 (16.0)   ->  16 + q exactly.
-// The constant offset is removed per group as offset * sum(x).  (A smaller
-// offset means less cancellation in that subtraction; bf16's 7-bit mantissa
-// has no room to place the nibble higher without an extra shift.)
+//   fp16: nibble at mantissa bits 6-9 of 0x4C00 (16.0)   ->  16 + q exactly,
+// ready for dot / MFMA instructions against the activations as loaded.  The
+// constant offset is removed per group as offset * sum(x).  (A smaller offset
+// means less cancellation in that subtraction; bf16's 7-bit mantissa has no
+// room to place the nibble higher without an extra shift.)
+__host__ __device__ constexpr int code_nibble(int i) { return (i >> 1) | ((i & 1) << 2); }
+
 template <int DT>
 struct Int4Magic;
 // `magic` is the kMagic constant held in a VGPR (vgpr_const), so each pair
@@ -221,16 +225,6 @@ struct Int4Magic<QMM_F16> {
     p[3] = ((w >> 6) & kMask) | magic;
   }
 };
-
-// Activation 16-bit values x0..x7 held as 4 words [x0|x1] [x2|x3] [x4|x5]
-// [x6|x7] -> pair order [x0|x4] [x1|x5] [x2|x6] [x3|x7].
-__device__ __forceinline__ void permute_pairs(const uint32_t a[4], uint32_t p[4]) {
-  // v_perm_b32(hi_src, lo_src, sel): selector bytes 0-3 pick lo_src, 4-7 hi_src.
-  p[0] = __builtin_amdgcn_perm(a[2], a[0], 0x05040100u);  // [x0 | x4]
-  p[1] = __builtin_amdgcn_perm(a[2], a[0], 0x07060302u);  // [x1 | x5]
-  p[2] = __builtin_amdgcn_perm(a[3], a[1], 0x05040100u);  // [x2 | x6]
-  p[3] = __builtin_amdgcn_perm(a[3], a[1], 0x07060302u);  // [x3 | x7]
-}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,

@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t quantize8(const float v[8], float s, float z
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float c = __builtin_amdgcn_fmed3f(k[i], 0.0f, kLevels);
-    word |= static_cast<uint32_t>(c) << (4 * i);
+    word |= static_cast<uint32_t>(c) << (4 * code_nibble(i));
   }
   return word;
 }
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void dequantize_g128_kernel(const uint32_t* __
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int q = static_cast<int>((word >> (4 * i)) & 0xFu);
+      const int q = static_cast<int>((word >> (4 * code_nibble(i))) & 0xFu);
       v[i] = static_cast<float>(q - z) * s;   // one fp32 rounding
     }
     if constexpr (DT == QMM_F32) {

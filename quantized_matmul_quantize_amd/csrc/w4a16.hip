@@ -114,8 +114,10 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const u32x4 a = xraw[b][c];
-          const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-          permute_pairs(aw, &xp[b][4 * c]);
+          xp[b][4 * c] = a.x;
+          xp[b][4 * c + 1] = a.y;
+          xp[b][4 * c + 2] = a.z;
+          xp[b][4 * c + 3] = a.w;
         }
         float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
@@ -264,8 +266,10 @@ __device__ __forceinline__ void skinny_compute(const SkinnyLoad<RT>& b, uint32_t
     uint32_t xb[16];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t aw[4] = {b.xr[h][c].x, b.xr[h][c].y, b.xr[h][c].z, b.xr[h][c].w};
-      permute_pairs(aw, &xb[4 * c]);
+      xb[4 * c] = b.xr[h][c].x;
+      xb[4 * c + 1] = b.xr[h][c].y;
+      xb[4 * c + 2] = b.xr[h][c].z;
+      xb[4 * c + 3] = b.xr[h][c].w;
     }
     float xs0 = 0.0f, xs1 = 0.0f;
 #pragma unroll
@@ -391,8 +395,9 @@ __global__ __launch_bounds__(512) void w4_mfma_skinny_kernel(const uint8_t* __re
 //
 // MFMA v_mfma_f32_16x16x32_{bf16,f16}: activations are the A operand (lane l:
 // token l%16), codes the B operand (lane l: weight row l%16); lane group
-// p = l/16 of chunk c in 0..3 covers k = 32 p + 8 c .. +8 of the group, held
-// in pair order (k, k+4) on both sides (Int4Magic::unpack / permute_pairs).
+// p = l/16 of chunk c in 0..3 covers k = 32 p + 8 c .. +8 of the group, in
+// natural order on both sides (the code layout makes Int4Magic::unpack yield
+// consecutive pairs, so activations go to the MFMA exactly as loaded).
 // The group's column sums X_g come from one more MFMA against a ones operand,
 // and each group is folded as  acc += s * (P - (off + z) * X_g).
 // ----------------------------------------------------------------------------
@@ -570,8 +575,10 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
       for (int mt = 0; mt < MT / 16; ++mt) {
         const int r = 16 * mt + fr;
         const u32x4 v = *reinterpret_cast<const u32x4*>(xg + r * 256 + (((4 * fp + c) ^ fr) * 16));
-        const uint32_t aw[4] = {v.x, v.y, v.z, v.w};
-        permute_pairs(aw, xa[mt]);
+        xa[mt][0] = v.x;
+        xa[mt][1] = v.y;
+        xa[mt][2] = v.z;
+        xa[mt][3] = v.w;
       }
 #pragma unroll
       for (int mt = 0; mt < MT / 16; ++mt)
@@ -790,8 +797,10 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(xg + (16 * mt + fr) * 256 + (((4 * fp + c) ^ fr) * 16));
-        const uint32_t aw[4] = {v.x, v.y, v.z, v.w};
-        permute_pairs(aw, xa[mt]);
+        xa[mt][0] = v.x;
+        xa[mt][1] = v.y;
+        xa[mt][2] = v.z;
+        xa[mt][3] = v.w;
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)

@@ -214,6 +214,21 @@ def check_packing():
     assert p[1].tolist() == [8 | (9 << 4), 10 | (11 << 4), 12]
 
 
+def check_code_words():
+    # Two runs of 8 codes, the second reversed; expected bytes written out by
+    # hand from the stated layout (element 2i at bits 4i, 2i+1 at bits 16+4i).
+    vals = np.array([[1, 2, 3, 4, 5, 6, 7, 8, 15, 14, 13, 12, 11, 10, 9, 0]], np.uint8)
+    p = oracle.pack_codes(vals)
+    assert p.shape == (1, 8)
+    # run 1 -> word 0x86427531; run 2: even elements 15, 13, 11, 9 give bits
+    # 0-15 = 0x9BDF, odd elements 14, 12, 10, 0 give bits 16-31 = 0x0ACE
+    assert p[0].tolist() == [0x31, 0x75, 0x42, 0x86, 0xDF, 0x9B, 0xCE, 0x0A]
+    # unpacking by the same rule returns the codes
+    words = p.view("<u4").reshape(-1)
+    back = [(int(w) >> (4 * (e // 2) + 16 * (e % 2))) & 0xF for w in words for e in range(8)]
+    assert back == vals[0].tolist()
+
+
 def check_storage_70b():
     g = _golden("storage_70b.json")
     n, k = 8, 1024
@@ -347,7 +362,7 @@ def check_sym_zero_row_floor():
 ALL_CHECKS = [
     check_six_weights, check_eight_weights, check_int8_outlier, check_int4_symmetric_exercise,
     check_int4_outlier_slide, check_round_half_even, check_degenerate_groups, check_error_bound_and_zero,
-    check_nearest_grid_point, check_granularity_special_cases, check_packing, check_storage_70b,
+    check_nearest_grid_point, check_granularity_special_cases, check_packing, check_code_words, check_storage_70b,
     check_matmul_against_blas, check_w4a16_integer_case, check_int8_matmul, check_smoothquant_invariants,
     check_smoothquant_error_ordering, check_sym_error_bound, check_sym_zero_row_floor,
 ]

@@ -121,7 +121,7 @@ def test_dequantize(dtype, shape):
     s = (g.standard_normal((n, k // 128)).astype(np.float32) * np.float32(0.01))
     s = np.abs(s) + np.float32(1e-5)
     ref = oracle.asym_dequantize(q, s, z)
-    codes = torch.from_numpy(oracle.pack_nibbles(q)).to(DEV)
+    codes = torch.from_numpy(oracle.pack_codes(q)).to(DEV)
     zeros = torch.from_numpy(oracle.pack_nibbles(z)).to(DEV)
     note(f"dequantize {shape} -> {dtype}")
     out = qmm.dequantize(codes, torch.from_numpy(s).to(DEV), zeros, dtype=TDT[dtype])

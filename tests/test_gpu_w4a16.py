@@ -14,7 +14,7 @@ TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 def upload_w4(q, s, z):
-    return (torch.from_numpy(oracle.pack_nibbles(q)).to(DEV), torch.from_numpy(np.ascontiguousarray(s)).to(DEV),
+    return (torch.from_numpy(oracle.pack_codes(q)).to(DEV), torch.from_numpy(np.ascontiguousarray(s)).to(DEV),
             torch.from_numpy(oracle.pack_nibbles(z)).to(DEV))
 
 

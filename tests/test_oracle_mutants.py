@@ -33,6 +33,8 @@ MUTANTS = [
     ("sym_round_trunc", "float t = rintf(v[i] / s);", "float t = truncf(v[i] / s);"),
     ("pack_swapped_nibbles", "out[r * bytes + j] = (uint8_t)(lo | (hi << 4));",
      "out[r * bytes + j] = (uint8_t)(hi | (lo << 4));"),
+    ("codes_plain_order", "word |= (uint32_t)(e[2 * i + 1] & 0xF) << (16 + 4 * i);",
+     "word |= (uint32_t)(e[2 * i + 1] & 0xF) << (8 * i + 4);"),
     ("matmul_transposed", "acc += (double)a[i * k + t] * (double)b[j * k + t];",
      "acc += (double)a[i * k + t] * (double)b[t * n + j % n];"),
     ("matmul_f32_sum", "double acc = 0.0;", "float acc = 0.0f;"),
@@ -68,7 +70,7 @@ def test_pins_catch_mutant(mid, old, new, source, tmp_path):
         good_lib = oracle.lib()          # installs argtypes on the real library
         mutant = ctypes.CDLL(str(so_path))
         for fn_name in ["oq_asym_quantize", "oq_asym_dequantize", "oq_sym_quantize", "oq_sym_dequantize",
-                        "oq_pack_nibbles", "oq_matmul_nt_f64", "oq_int8_matmul_nt", "oq_rescale_f64",
+                        "oq_pack_nibbles", "oq_pack_codes", "oq_matmul_nt_f64", "oq_int8_matmul_nt", "oq_rescale_f64",
                         "oq_col_absmax", "oq_smooth_factors", "oq_scale_columns_mul", "oq_scale_columns_div"]:
             f = getattr(mutant, fn_name)
             f.argtypes = getattr(good_lib, fn_name).argtypes
