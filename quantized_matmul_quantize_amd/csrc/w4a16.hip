@@ -19,10 +19,15 @@
 //    no matrix cores: a lane streams 16 bytes (32 weights) per row per step,
 //    R rows at a time so R x 16 bytes are in flight, with the activation slice
 //    held in registers across those rows.  Used for B == 1 (decode).
-//  * w4_mfma_skinny_kernel: up to 16*MT tokens per block on
-//    v_mfma_f32_16x16x32_{bf16,f16}; the weights are the A operand (16 rows x
-//    32 k per instruction, one code word per lane) and never touch LDS; the
-//    wavefronts of a block split K and are summed through LDS at the end.
+//  * w4_lds_kernel: 2..32 tokens (and larger batches whose 64 x 128 tiles
+//    would not fill the chip) on v_mfma_f32_16x16x32_{bf16,f16}; a block
+//    takes 16 or 32 tokens x 32 or 64 weight rows, its four wavefronts split
+//    K, each with its own LDS rings filled by direct-to-LDS buffer loads.
+//  * w4_tile_kernel: larger batches; 64 x 128 tiles whose activation tile is
+//    shared by the four wavefronts through LDS, one barrier per group.
+//  * w4_mfma_skinny_kernel: bf16 fallback when K is too large for the LDS
+//    zero-point table of the kernels above; the weights are the A operand and
+//    never touch LDS.
 
 #include "qmm_device.h"
 
@@ -39,6 +44,28 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
     static_cast<uint16_t*>(y)[idx] = static_cast<uint16_t>(f32_to_bf16_bits(v));
   } else {
     static_cast<uint16_t*>(y)[idx] = static_cast<uint16_t>(f32_to_f16_bits(v));
+  }
+}
+
+// Copies `total` elements starting at src into LDS; elements at or past
+// `valid` become 0.  Each pass issues all of a thread's loads before any
+// store, so a copy costs one memory round trip per pass rather than one per
+// element; the indexes are clamped into the valid range, so every load is in
+// bounds.  Used for a block's rows of scales or zero points, which are
+// consecutive in memory.
+template <typename T, int NTHREADS>
+__device__ __forceinline__ void copy_to_lds(T* dst, const T* __restrict__ src, int total, int valid, int tid) {
+  constexpr int kPer = 8;
+  for (int base = 0; base < total; base += kPer * NTHREADS) {
+    T v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (base + j * NTHREADS < total) v[j] = src[min(base + j * NTHREADS + tid, valid - 1)];   // uniform test
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int idx = base + j * NTHREADS + tid;
+      if (idx < total) dst[idx] = (idx < valid) ? v[j] : T(0);
+    }
   }
 }
 
@@ -82,8 +109,14 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
     for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
 
   for (uint32_t k0 = 0; k0 < static_cast<uint32_t>(kk); k0 += static_cast<uint32_t>(kValuStepK)) {
-    const uint32_t kb = k0 + static_cast<uint32_t>(wave * (kWave * kLaneK) + lane * kLaneK);
-    if (kb < static_cast<uint32_t>(kk)) {
+    // A wavefront with no lane inside K skips the step; in a partly covered
+    // step the lanes past K load the last 32 weights (in bounds) and take
+    // zero activations, so the step runs without a divergent branch.
+    if (k0 + static_cast<uint32_t>(wave * (kWave * kLaneK)) >= static_cast<uint32_t>(kk)) break;
+    const uint32_t kb_raw = k0 + static_cast<uint32_t>(wave * (kWave * kLaneK) + lane * kLaneK);
+    const bool inside = kb_raw < static_cast<uint32_t>(kk);
+    const uint32_t kb = inside ? kb_raw : static_cast<uint32_t>(kk - kLaneK);
+    {
       u32x4 cw[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) cw[r] = ld16_nt(crow[r] + (kb >> 1));
@@ -104,6 +137,12 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
       // Every load of the step is issued before any result is consumed, so
       // the waits count down instead of draining the queue once per row.
       __builtin_amdgcn_sched_barrier(0);
+      if (!inside) {
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) xraw[b][c] = u32x4{0u, 0u, 0u, 0u};
+      }
       float zo[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) zo[r] = Mg::offset + static_cast<float>((zb[r] >> zshift) & 0xFu);
@@ -532,10 +571,7 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
     issue_x(i);
     issue_w(i);
   }
-  for (int i = tid; i < kRows * zb; i += 256) {
-    const int r = i / zb;
-    ztab[i] = (r < nrows) ? zeros[(n0 + r) * zb + (i - r * zb)] : 0;
-  }
+  copy_to_lds<uint8_t, 256>(ztab, zeros + n0 * zb, kRows * zb, static_cast<int>(nrows) * zb, tid);
   __syncthreads();   // zero-point table
 
   f32x4 acc[MT / 16][NT];
@@ -752,10 +788,7 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
 
 
   for (int i = 0; i < kTileD; ++i) tile_issue<BM>(i, G, wave, lbase, xr, cr, sr, xoff, coff, soff);
-  for (int i = tid; i < kTileN * zb; i += 256) {
-    const int r = i / zb;
-    ztab[i] = (r < nrows) ? zeros[(n0 + r) * zb + (i - r * zb)] : 0;
-  }
+  copy_to_lds<uint8_t, 256>(ztab, zeros + n0 * zb, kTileN * zb, static_cast<int>(nrows) * zb, tid);
 
   f32x4 acc[MT][2];
 #pragma unroll
