@@ -156,8 +156,11 @@ def build_ops(dev):
                                       qmm._ptr(Y), qmm.BF16, qmm._stream(X))
             assert st == 0, st
         bound = "mfma" if M >= 128 else "hbm"
+        # the library takes the shared-tile kernel once its 64 x 128 tiles give every CU a block
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        tile = M > 32 and -(-M // 64) * -(-n3 // 128) >= cus
         ops.append(dict(name=f"w4a16_gemm M={M} {n3}x{k3}", fn=gemm, bytes=wb(n3, k3) + M * k3 * 2 + M * n3 * 2,
-                        flops=2 * M * n3 * k3, bound=bound, kernel="w4_lds_kernel"))
+                        flops=2 * M * n3 * k3, bound=bound, kernel="w4_tile_kernel" if tile else "w4_lds_kernel"))
 
     # SmoothQuant W8A8.
     wl4 = workloads.WORKLOADS["smoothquant"]
