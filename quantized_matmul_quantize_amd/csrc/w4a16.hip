@@ -117,9 +117,15 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
     const bool inside = kb_raw < static_cast<uint32_t>(kk);
     const uint32_t kb = inside ? kb_raw : static_cast<uint32_t>(kk - kLaneK);
     {
-      u32x4 cw[R];
+      // Every load of the step is issued before any result is consumed, in
+      // the order they are needed (activations, scales and zero points, then
+      // the codes row by row), so row r is computed as soon as its codes
+      // arrive while the later rows are still in flight.
+      u32x4 xraw[B][4];
 #pragma unroll
-      for (int r = 0; r < R; ++r) cw[r] = ld16_nt(crow[r] + (kb >> 1));
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xraw[b][c] = ld16(x + b * K + kb + 8 * c);
       const uint32_t g = kb >> 7;
       const uint32_t zshift = (g & 1u) * 4u;
       float sc[R];
@@ -129,13 +135,9 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
         sc[r] = srow[r][g];
         zb[r] = zrowp[r][g >> 1];
       }
-      u32x4 xraw[B][4];
+      u32x4 cw[R];
 #pragma unroll
-      for (int b = 0; b < B; ++b)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) xraw[b][c] = ld16(x + b * K + kb + 8 * c);
-      // Every load of the step is issued before any result is consumed, so
-      // the waits count down instead of draining the queue once per row.
+      for (int r = 0; r < R; ++r) cw[r] = ld16_nt(crow[r] + (kb >> 1));
       __builtin_amdgcn_sched_barrier(0);
       if (!inside) {
 #pragma unroll
