@@ -45,6 +45,18 @@ def test_gemv_small(xdt, ysame, B, shape):
     gemv_case(q, s, z, x, TDT[xdt] if ysame else torch.float32, f"small {xdt}")
 
 
+@pytest.mark.parametrize("k", [8320, 12672, 18560, 28672])
+def test_gemv_long_k(k):
+    # K beyond one 8192-wide step: the single-token kernel pipelines its steps,
+    # with partly covered and skipped last steps per wavefront
+    n = 37
+    q, s, z = random_w4(n, k, seed=k)
+    for xdt in ("bf16", "f16"):
+        x = workloads.to_dtype(workloads.gaussian(workloads.rng(80, k), (1, k), 1.0), xdt)
+        gemv_case(q, s, z, x, torch.float32, f"long K {xdt}")
+        gemv_case(q, s, z, x, TDT[xdt], f"long K {xdt} 16-bit")
+
+
 def test_gemv_one_row_one_group():
     q, s, z = random_w4(1, 128, seed=1)
     x = workloads.to_dtype(workloads.gaussian(workloads.rng(1, 1), (1, 128), 1.0), "bf16")
