@@ -2,7 +2,8 @@
 //
 // Storage formats (fixed by the C-ABI in include/qmm.h):
 //  * INT4 codes: row-major [N, K/2] bytes; little-endian 32-bit word w of a
-//    row holds elements 8w..8w+7, element 8w+i in bits 4i..4i+3.
+//    row holds elements 8w..8w+7, element 8w+2i in bits 4i..4i+3 and element
+//    8w+2i+1 in bits 16+4i..16+4i+3 (see code_nibble).
 //  * scales: fp32 [N, K/128]; zero-points: nibble-packed [N, ceil(G/2)] bytes,
 //    group 2j in the low nibble of byte j, group 2j+1 in the high nibble.
 #pragma once
@@ -23,6 +24,19 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kGroup = 128;
+
+// ---- buffer loads straight into LDS ------------------------------------------
+// Word 3 of a raw buffer resource (32-bit data format); offsets at or past the
+// resource's byte count read as zero, which the kernels use for ragged tiles.
+constexpr int kBufferWord3 = 0x00020000;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // ---- 16-byte global memory access ------------------------------------------
 // Streaming loads/stores use the nontemporal hint (data touched once).

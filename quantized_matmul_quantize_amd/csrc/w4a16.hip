@@ -466,15 +466,6 @@ struct LdsCfg {
 
 __device__ __forceinline__ int code_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource, 32-bit data format
-
 // Host and device: it is called from lambdas, which HIP compiles for both sides.
 __host__ __device__ inline lds_ptr_t lds_at(uint32_t byte) { return (lds_ptr_t)(uintptr_t)byte; }
 

@@ -279,7 +279,6 @@ constexpr int kPitch4 = 528;                   // 4-byte outputs (32 rows per pa
 constexpr int kEpiWave = 64 * kPitch2;         // per-wavefront epilogue region
 constexpr size_t kGemmLds = 3 * kStage;        // 144 KiB
 constexpr int kXcds = 8;
-constexpr int kBufferWord3 = 0x00020000;       // raw buffer resource, 32-bit data format
 constexpr int kOutOfRange = 0x40000000;        // added to a lane offset: reads zero
 static_assert(32 * kPitch4 <= kEpiWave && 4 * kEpiWave <= static_cast<int>(kGemmLds), "epilogue must fit");
 
@@ -299,14 +298,6 @@ __device__ __forceinline__ void xcd_tile(int64_t b, int64_t tm, int64_t tn, int6
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ (r >> 3); }
 
-// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int YDT>
 __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__ A, const float* __restrict__ ascale,
@@ -402,7 +393,7 @@ __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__
   // Prologue: loads of steps 0 and 1; wait for step 0, barrier, fragments (0, 0).
   issue(0, 0);
   issue(1, 1);
-  wait_vmcnt<kLoadsA + kLoadsB>();
+  wait_vm<kLoadsA + kLoadsB>();
   barrier();
   read_chunk(fa0, fb0, 0, rd0);
 
@@ -426,7 +417,7 @@ __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);   // chunk-0 work stays ahead of the wait
     // This wave's loads of step t+1 are complete once only step t+2's remain.
-    wait_vmcnt<kLoadsA + kLoadsB>();
+    wait_vm<kLoadsA + kLoadsB>();
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): fragments (t, 1) have landed
     barrier();
     read_chunk(fa0, fb0, s1, rd0);
@@ -442,7 +433,7 @@ __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     s0 = s1;
   }
-  wait_vmcnt<0>();
+  wait_vm<0>();
   __syncthreads();   // the epilogue reuses the LDS
 
   // Epilogue.  Tile (i, j), register r: row 16 i + 4 (lane/16) + r of the
