@@ -126,7 +126,7 @@ def build_ops(dev):
                                         qmm._ptr(s), qmm._ptr(z), qmm._stream(m["w"]))
             assert st == 0, st
         ops.append(dict(name=f"quantize {n}x{k}", fn=quant, bytes=n * k * 2 + wb(n, k), flops=0, bound="hbm",
-                        kernel="quantize_g128_kernel"))
+                        kernel="quantize_g128_lds_kernel"))
 
     for m in mats:
         n, k = m["n"], m["k"]
