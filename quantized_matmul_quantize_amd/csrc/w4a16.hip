@@ -668,6 +668,194 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
 }
 
 // ----------------------------------------------------------------------------
+// MFMA kernel for up to 16 tokens (decode with a small batch).  The block
+// tile is 16 tokens x 16 NT weight rows; K advances 4 groups (512 k) per step
+// and wavefront w computes group 4 step + w, so the four wavefronts split K
+// as in w4_lds_kernel.  The difference is how the weights arrive: the block
+// loads each step's code tile (16 NT rows x 256 bytes) cooperatively, every
+// buffer load covering 4 rows x 256 contiguous bytes, where w4_lds_kernel
+// fetches 64-byte pieces of 16 rows per instruction (a measurably slower
+// stream from HBM).  Activations (16 tokens x 1 KiB per step, one token row
+// per load) and scales (one group of 64 rows per load) come the same way.
+// S LDS stages (loads S - 1 steps ahead), one barrier per step.  Swizzles: 16-byte piece p of code
+// row r sits at position p ^ (r & 15) of the row, piece p of token row t at
+// p ^ (t & 15), so the fragment reads of 16 rows (tokens) are conflict-free.
+// ----------------------------------------------------------------------------
+template <int NT, int S>
+struct RowsCfg {
+  static constexpr int kRows = 16 * NT;
+  static constexpr int kCodeBytes = kRows * 256;        // 4 groups x 64 bytes per row
+  static constexpr int kXBytes = 16 * 1024;             // 16 tokens x 512 k x 2 bytes
+  static constexpr int kScaleBytes = 4 * 64 * 4;        // 4 groups x 64 rows
+  static constexpr int kStageBytes = kCodeBytes + kXBytes + kScaleBytes;
+  static constexpr int kLoads = NT + 4 + 1;              // per wavefront per step
+  static constexpr int kPartPitch = kRows + 4;
+  static_assert(4 * 16 * kPartPitch * 4 <= S * kStageBytes, "partial tiles fit the stages");
+};
+
+template <int XDT, int YDT, int NT, int S>
+__global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict__ codes,
+                                                      const float* __restrict__ scales,
+                                                      const uint8_t* __restrict__ zeros, int64_t N, int64_t K,
+                                                      const uint16_t* __restrict__ x, int64_t M,
+                                                      void* __restrict__ y) {
+  using Cfg = RowsCfg<NT, S>;
+  constexpr int D = S - 1;
+  using Mg = Int4Magic<XDT>;
+  constexpr int kRows = Cfg::kRows;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int G = static_cast<int>(K / kGroup);
+  const int zb = (G + 1) / 2;
+  const int nsteps = (G + 3) / 4;
+
+  const int64_t mtiles = (M + 15) / 16;
+  const int64_t ntiles = (N + kRows - 1) / kRows;
+  const int64_t T = mtiles * ntiles;
+  const int64_t per = (T + 7) / 8;
+  const int64_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= T) return;
+  const int64_t n0 = (t / mtiles) * kRows;
+  const int64_t m0 = (t % mtiles) * 16;
+  const int64_t nrows = (N - n0 < kRows) ? N - n0 : kRows;
+  const int64_t mrows = (M - m0 < 16) ? M - m0 : 16;
+
+  const uint32_t lbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  uint8_t* const ztab = lds + S * Cfg::kStageBytes;
+
+  const int kb2 = static_cast<int>(K) * 2;
+  const int kh = static_cast<int>(K / 2);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + m0 * K), 0, static_cast<int>(mrows) * kb2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(codes + n0 * (K / 2)), 0, static_cast<int>(nrows) * kh, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scales + n0 * G), 0, static_cast<int>(nrows) * G * 4, kBufferWord3);
+
+  // Load offsets.  Codes: load q of wavefront w covers rows 4 (NT w + q) ..
+  // +4, lane l row + l/16, piece (l%16) ^ (row & 15).  Activations: load q of
+  // wavefront w is token row 4 w + q, lane l piece l ^ (token & 15).  Scales:
+  // wavefront w loads group 4 step + w of rows 0..63 (lane l: row l).
+  int coff[4], xoff[4];
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    const int r = 4 * (NT * wave + q) + (lane >> 4);
+    coff[q] = r * kh + (((lane & 15) ^ (r & 15)) * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int tr = 4 * wave + q;
+    xoff[q] = tr * kb2 + ((lane ^ (tr & 15)) * 16);
+  }
+  const int soff = lane * G * 4;
+  auto issue = [&](int st) {
+    const int sc = min(st, nsteps - 1);   // past the end: reload the last step (never read)
+    const uint32_t stage = lbase + (st % S) * Cfg::kStageBytes;
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_ptr_t)(uintptr_t)(stage + (NT * wave + q) * 1024), 16,
+                                               coff[q], sc * 256, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(uintptr_t)(stage + Cfg::kCodeBytes + (4 * wave + q) * 1024),
+                                               16, xoff[q], sc * 1024, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        sr, (lds_ptr_t)(uintptr_t)(stage + Cfg::kCodeBytes + Cfg::kXBytes + wave * 256), 4, soff, (4 * sc + wave) * 4,
+        0, 0);
+  };
+
+  for (int st = 0; st < D; ++st) issue(st);
+  copy_to_lds<uint8_t, 256>(ztab, zeros + n0 * zb, kRows * zb, static_cast<int>(nrows) * zb, tid);
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint32_t magic = vgpr_const(Mg::kMagic);
+  const uint32_t ones[4] = {Mg::one_pair, Mg::one_pair, Mg::one_pair, Mg::one_pair};
+  const int fr = lane & 15;
+  const int fp = lane >> 4;
+
+  for (int st = 0; st < nsteps; ++st) {
+    // This wavefront's loads of step st have landed (only those of the next
+    // D - 1 steps may be in flight); after the barrier every wavefront's
+    // have, and all are done with the stage of step st - 1, which step
+    // st + D now fills (past the end: a reload that is never read).
+    wait_vm<(D - 1) * Cfg::kLoads>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    issue(st + D);
+    const int g = 4 * st + wave;
+    if (g < G) {
+      const uint8_t* cg = lds + (st % S) * Cfg::kStageBytes;
+      const uint8_t* xg = cg + Cfg::kCodeBytes;
+      const float* sg = reinterpret_cast<const float*>(xg + Cfg::kXBytes + wave * 256);
+      const int cp = 4 * wave + fp;   // this lane's 16-byte piece of a code row
+      u32x4 cw[NT];
+      float sv[NT], zo[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int r = 16 * nt + fr;
+        cw[nt] = *reinterpret_cast<const u32x4*>(cg + r * 256 + ((cp ^ fr) * 16));
+        sv[nt] = sg[r];
+        const uint32_t zbyte = ztab[r * zb + (g >> 1)];
+        zo[nt] = Mg::offset + static_cast<float>((g & 1) ? (zbyte >> 4) : (zbyte & 15u));
+      }
+      f32x4 part[NT], xs;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int xp = 16 * wave + 4 * fp + c;   // piece of the token row
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xg + fr * 1024 + ((xp ^ fr) * 16));
+        const uint32_t xa[4] = {v.x, v.y, v.z, v.w};
+        xs = mfma16x16x32<XDT>(xa, ones, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : xs);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          uint32_t wb[4];
+          Mg::unpack(cw[nt][c], magic, wb);
+          part[nt] = mfma16x16x32<XDT>(xa, wb, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : part[nt]);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[nt][e] = fmaf(sv[nt], fmaf(-zo[nt], xs[e], part[nt][e]), acc[nt][e]);
+    }
+  }
+  wait_vm<0>();
+  __syncthreads();   // every stage is idle; the LDS now holds the partial tiles
+
+  float* parts = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) parts[(wave * 16 + 4 * fp + e) * Cfg::kPartPitch + 16 * nt + fr] = acc[nt][e];
+  __syncthreads();
+  constexpr int kOct = kRows / 8;
+  for (int o = tid; o < 16 * kOct; o += 256) {
+    const int r = o / kOct;
+    const int c0 = (o % kOct) * 8;
+    const int64_t m = m0 + r;
+    if (m >= M) continue;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float a = parts[(0 * 16 + r) * Cfg::kPartPitch + c0 + j];
+      a += parts[(1 * 16 + r) * Cfg::kPartPitch + c0 + j];
+      a += parts[(2 * 16 + r) * Cfg::kPartPitch + c0 + j];
+      a += parts[(3 * 16 + r) * Cfg::kPartPitch + c0 + j];
+      v[j] = a;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t n = n0 + c0 + j;
+      if (n < N) store_y<YDT>(y, m * N + n, v[j]);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // MFMA kernel for larger token counts: a block computes a BM x 128 tile of Y
 // (BM = 64 tokens), its four wavefronts each BM tokens x 32 weight
 // rows, walking K one group at a time in lock step.  The activation tile of a
@@ -997,10 +1185,42 @@ bool launch_tile_t(const uint8_t* codes, const float* scales, const uint8_t* zer
   return true;
 }
 
+template <int XDT, int YDT, int NT, int S>
+bool launch_rows_t(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                   const uint16_t* x, int64_t M, void* y, hipStream_t s) {
+  using Cfg = RowsCfg<NT, S>;
+  const int64_t G = K / kGroup;
+  const size_t lds = S * static_cast<size_t>(Cfg::kStageBytes) + static_cast<size_t>(Cfg::kRows) * ((G + 1) / 2);
+  if (lds > kLdsBytesMax) return false;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_rows_kernel<XDT, YDT, NT, S>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  const int64_t tiles = ceil_div(M, 16) * ceil_div(N, Cfg::kRows);
+  const dim3 grid(static_cast<unsigned>(ceil_div(tiles, 8) * 8));
+  w4_rows_kernel<XDT, YDT, NT, S><<<grid, dim3(kLdsWaves * kWave), lds, s>>>(codes, scales, zeros, N, K, x, M, y);
+  return true;
+}
+
+// Up to 16 tokens.  The cooperative-load kernel with 64 weight rows per
+// block when that gives every compute unit a block, with 32 rows when that
+// gives most units two; otherwise (few rows, long K: one block per unit would
+// serialize its steps on the barrier) the split-K kernel whose wavefronts run
+// independently.  Two stages: measured faster than three to five, which cost
+// blocks per compute unit.
+template <int XDT, int YDT>
+bool launch_rows(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                 const uint16_t* x, int64_t M, void* y, hipStream_t s) {
+  const int64_t cus = device_cus();
+  const int64_t mt = ceil_div(M, 16);
+  if (mt * ceil_div(N, 64) >= cus && launch_rows_t<XDT, YDT, 4, 2>(codes, scales, zeros, N, K, x, M, y, s)) return true;
+  if (2 * mt * ceil_div(N, 32) >= 3 * cus && launch_rows_t<XDT, YDT, 2, 2>(codes, scales, zeros, N, K, x, M, y, s))
+    return true;
+  return launch_lds_m<XDT, YDT, 16>(codes, scales, zeros, N, K, x, M, y, s);
+}
+
 template <int XDT, int YDT>
 bool launch_lds(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                 const uint16_t* x, int64_t M, void* y, hipStream_t s) {
-  if (M <= 16) return launch_lds_m<XDT, YDT, 16>(codes, scales, zeros, N, K, x, M, y, s);
+  if (M <= 16) return launch_rows<XDT, YDT>(codes, scales, zeros, N, K, x, M, y, s);
   // The shared-tile kernel once its 64 x 128 tiles give every compute unit a
   // block; below that the split-K kernel's smaller tiles keep more units busy.
   if (M > 32 && ceil_div(M, 64) * ceil_div(N, kTileN) >= static_cast<int64_t>(device_cus()) &&

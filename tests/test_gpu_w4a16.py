@@ -119,6 +119,18 @@ def test_gemm_wide_ragged(M):
     gemv_case(q, s, z, x, torch.bfloat16, f"gemm wide M={M} bf16", gemm=True)
 
 
+@pytest.mark.parametrize("n", [12321, 16421], ids=["32-row blocks", "64-row blocks"])
+@pytest.mark.parametrize("M", [3, 16])
+def test_gemm_few_tokens_cooperative(n, M):
+    # enough weight rows for the cooperative-load kernel (up to 16 tokens),
+    # K = 5 groups so its second 4-group step is partly past K; ragged N
+    k = 640
+    q, s, z = random_w4(n, k, seed=n + M)
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(81, n + M), (M, k), 1.0), "bf16")
+    gemv_case(q, s, z, x, torch.float32, f"gemm few tokens n={n} M={M}", gemm=True)
+    gemv_case(q, s, z, x, torch.bfloat16, f"gemm few tokens n={n} M={M} bf16", gemm=True)
+
+
 @pytest.mark.parametrize("M", [16, 64, 256])
 def test_gemm_full_size(M):
     wl = workloads.WORKLOADS["gemm"]
