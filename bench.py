@@ -91,6 +91,21 @@ class HipEvent:
         return ms.value
 
 
+
+def w4_kernel_name(M, N, dev):
+    """Which W4A16 MFMA kernel the library picks for M tokens and N weight rows
+    (the rule in w4a16.hip's launchers), for labelling only."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    cdiv = lambda a, b: -(-a // b)
+    if M <= 16:
+        mt = cdiv(M, 16)
+        if mt * cdiv(N, 64) >= cus or 2 * mt * cdiv(N, 32) >= 3 * cus:
+            return "w4_rows_kernel"
+        return "w4_lds_kernel"
+    if M > 32 and cdiv(M, 64) * cdiv(N, 128) >= cus:
+        return "w4_tile_kernel"
+    return "w4_lds_kernel"
+
 def w4_bytes(n, k):
     c, s, z = qmm.w4_sizes(n, k)
     return c + s + z
@@ -156,11 +171,8 @@ def build_ops(dev):
                                       qmm._ptr(Y), qmm.BF16, qmm._stream(X))
             assert st == 0, st
         bound = "mfma" if M >= 128 else "hbm"
-        # the library takes the shared-tile kernel once its 64 x 128 tiles give every CU a block
-        cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        tile = M > 32 and -(-M // 64) * -(-n3 // 128) >= cus
         ops.append(dict(name=f"w4a16_gemm M={M} {n3}x{k3}", fn=gemm, bytes=wb(n3, k3) + M * k3 * 2 + M * n3 * 2,
-                        flops=2 * M * n3 * k3, bound=bound, kernel="w4_tile_kernel" if tile else "w4_lds_kernel"))
+                        flops=2 * M * n3 * k3, bound=bound, kernel=w4_kernel_name(M, n3, dev)))
 
     # SmoothQuant W8A8.
     wl4 = workloads.WORKLOADS["smoothquant"]
@@ -214,7 +226,7 @@ def build_ops(dev):
                 assert st == 0, st
             ops.append(dict(name=f"w4a16_gemv B={B} {n}x{k}", fn=gemv, bytes=wb(n, k) + B * k * 2 + B * n * 2,
                             flops=2 * B * n * k, bound="hbm",
-                            kernel="gemv_valu_kernel" if B == 1 else "w4_lds_kernel",
+                            kernel="gemv_valu_kernel" if B == 1 else w4_kernel_name(B, n, dev),
                             group="gemv_b1" if B == 1 else None))
 
     return ops, mats
