@@ -97,10 +97,10 @@ def w4_kernel_name(M, N, dev):
     (the rule in w4a16.hip's launchers), for labelling only."""
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     cdiv = lambda a, b: -(-a // b)
+    mt = cdiv(M, 16)
+    if M <= 64 and (mt * cdiv(N, 64) >= cus or 2 * mt * cdiv(N, 32) >= 3 * cus):
+        return "w4_rows_kernel"
     if M <= 16:
-        mt = cdiv(M, 16)
-        if mt * cdiv(N, 64) >= cus or 2 * mt * cdiv(N, 32) >= 3 * cus:
-            return "w4_rows_kernel"
         return "w4_lds_kernel"
     if M > 32 and cdiv(M, 64) * cdiv(N, 128) >= cus:
         return "w4_tile_kernel"

@@ -1200,27 +1200,27 @@ bool launch_rows_t(const uint8_t* codes, const float* scales, const uint8_t* zer
   return true;
 }
 
-// Up to 16 tokens.  The cooperative-load kernel with 64 weight rows per
-// block when that gives every compute unit a block, with 32 rows when that
-// gives most units two; otherwise (few rows, long K: one block per unit would
-// serialize its steps on the barrier) the split-K kernel whose wavefronts run
-// independently.  Two stages: measured faster than three to five, which cost
-// blocks per compute unit.
+// The cooperative-load kernel (16-token tiles, up to 64 tokens): 64 weight
+// rows per block when that gives every compute unit a block, 32 rows when
+// that gives most units two; otherwise false (few rows, long K: one block per
+// unit would serialize its steps on the barrier), and the split-K kernel,
+// whose wavefronts run independently, takes the call.  Two stages: measured
+// faster than three to five, which cost blocks per compute unit.
 template <int XDT, int YDT>
 bool launch_rows(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                  const uint16_t* x, int64_t M, void* y, hipStream_t s) {
   const int64_t cus = device_cus();
   const int64_t mt = ceil_div(M, 16);
-  if (mt * ceil_div(N, 64) >= cus && launch_rows_t<XDT, YDT, 4, 2>(codes, scales, zeros, N, K, x, M, y, s)) return true;
-  if (2 * mt * ceil_div(N, 32) >= 3 * cus && launch_rows_t<XDT, YDT, 2, 2>(codes, scales, zeros, N, K, x, M, y, s))
-    return true;
-  return launch_lds_m<XDT, YDT, 16>(codes, scales, zeros, N, K, x, M, y, s);
+  if (mt * ceil_div(N, 64) >= cus) return launch_rows_t<XDT, YDT, 4, 2>(codes, scales, zeros, N, K, x, M, y, s);
+  if (2 * mt * ceil_div(N, 32) >= 3 * cus) return launch_rows_t<XDT, YDT, 2, 2>(codes, scales, zeros, N, K, x, M, y, s);
+  return false;
 }
 
 template <int XDT, int YDT>
 bool launch_lds(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                 const uint16_t* x, int64_t M, void* y, hipStream_t s) {
-  if (M <= 16) return launch_rows<XDT, YDT>(codes, scales, zeros, N, K, x, M, y, s);
+  if (M <= 64 && launch_rows<XDT, YDT>(codes, scales, zeros, N, K, x, M, y, s)) return true;
+  if (M <= 16) return launch_lds_m<XDT, YDT, 16>(codes, scales, zeros, N, K, x, M, y, s);
   // The shared-tile kernel once its 64 x 128 tiles give every compute unit a
   // block; below that the split-K kernel's smaller tiles keep more units busy.
   if (M > 32 && ceil_div(M, 64) * ceil_div(N, kTileN) >= static_cast<int64_t>(device_cus()) &&

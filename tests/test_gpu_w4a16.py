@@ -120,9 +120,9 @@ def test_gemm_wide_ragged(M):
 
 
 @pytest.mark.parametrize("n", [12321, 16421], ids=["32-row blocks", "64-row blocks"])
-@pytest.mark.parametrize("M", [3, 16])
+@pytest.mark.parametrize("M", [3, 16, 40])
 def test_gemm_few_tokens_cooperative(n, M):
-    # enough weight rows for the cooperative-load kernel (up to 16 tokens),
+    # enough weight rows for the cooperative-load kernel (up to 64 tokens),
     # K = 5 groups so its second 4-group step is partly past K; ragged N
     k = 640
     q, s, z = random_w4(n, k, seed=n + M)
