@@ -116,6 +116,7 @@ int dequantize(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  * y : [B, N] of y_dtype (x_dtype or QMM_F32).
  * group 128.  B == 1 runs on the vector ALUs only (no matrix cores);
  * 2 <= B <= 8 contracts on the matrix cores (the kernel of w4a16_gemm).
+ * K <= 2^24 and N < 2^31 (QMM_ERANGE otherwise): tile offsets are 32-bit.
  * ------------------------------------------------------------------------- */
 int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                int group, const void* x, int x_dtype, int64_t B, void* y, int y_dtype, void* stream);
@@ -126,7 +127,8 @@ int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  * Source: "How quantization works" ("Inference view"); "Quantization from
  * Scratch" ("What it buys at decode", growing batch).
  * X : [M, K] QMM_BF16 or QMM_F16.  Y : [M, N] of X's type or QMM_F32.
- * M >= 1, group 128.  A block keeps the zero points of its weight rows in
+ * M >= 1, group 128, K <= 2^24, N and M < 2^31 (QMM_ERANGE otherwise).
+ * A block keeps the zero points of its weight rows in
  * LDS, which bounds K: K <= 53248 is always served for M > 16 and
  * K <= 385024 for M <= 16; beyond that bf16 runs a slower kernel without the
  * table and fp16 returns QMM_EUNSUPPORTED.

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
   const uint32_t magic = vgpr_const(Mg::kMagic);
   const int64_t G = K / kGroup;
   const int64_t zrow = (G + 1) / 2;
-  const int kk = static_cast<int>(K);   // K < 2^30 (checked on the host): lane offsets fit 32 bits
+  const int kk = static_cast<int>(K);   // K <= 2^24 (checked on the host): lane offsets fit 32 bits
 
   // Row bases are wavefront-uniform (scalar registers); lanes add 32-bit offsets.
   const uint8_t* crow[R];
@@ -1066,6 +1066,8 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
 // ----------------------------------------------------------------------------
 // Host side.
 // ----------------------------------------------------------------------------
+constexpr int64_t kMaxW4K = int64_t{1} << 24;
+
 int check_common(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
                  const void* x, int x_dtype, int64_t M, const void* y, int y_dtype) {
   if (!codes || !scales || !zeros || !x || !y) return QMM_EINVAL;
@@ -1074,6 +1076,9 @@ int check_common(const uint8_t* codes, const float* scales, const uint8_t* zeros
       (y_dtype != QMM_BF16 && y_dtype != QMM_F16 && y_dtype != QMM_F32 && y_dtype != QMM_I32))
     return QMM_EINVAL;
   if (group != kGroup) return QMM_EUNSUPPORTED;
+  // Lane and buffer offsets within a tile are 32-bit: at most 64 rows of
+  // K / 2 code bytes or K x 2 activation bytes each stay below 2^31.
+  if (K > kMaxW4K || N > INT32_MAX || M > INT32_MAX) return QMM_ERANGE;
   if (x_dtype != QMM_BF16 && x_dtype != QMM_F16) return QMM_EUNSUPPORTED;
   if (y_dtype != x_dtype && y_dtype != QMM_F32) return QMM_EUNSUPPORTED;
   if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(scales, 4) || !aligned(y, y_dtype == QMM_F32 ? 4 : 2))

@@ -119,6 +119,8 @@ def test_gemv_gemm_argument_errors():
     assert gemm(P, P, P, 8, 256, 128, P, F16, 4, P, BF16, None) == EUNSUP     # mixed 16-bit types
     assert gemm(P, P, P, 8, 300, 128, P, BF16, 4, P, BF16, None) == EINVAL
     assert gemm(P, P, P, 8, 256, 128, P, BF16, 0, P, BF16, None) == EINVAL
+    assert gemv(P, P, P, 8, (1 << 24) + 128, 128, P, BF16, 1, P, BF16, None) == ERANGE   # K past 2^24
+    assert gemm(P, P, P, 1 << 31, 256, 128, P, BF16, 4, P, BF16, None) == ERANGE
 
 
 def test_w8a8_argument_errors():
