@@ -20,33 +20,34 @@ namespace qmm {
 namespace {
 
 constexpr float kLevels = 15.0f;                 // 2^4 - 1
-constexpr float kTieMargin = 0.5f - 0x1p-16f;    // see quantize8
 
-// Codes of 8 elements for one group with scale s and zero-point zf (an
-// integer-valued float), bit-identical to clamp(rint(fl32(v / s)) + z, 0, 15).
-//
-// Fast path: t = fma(v, rcp(s), z).  With v_rcp_f32 accurate to 1 ulp and
-// |v / s| <= 15 (v lies in the group's range), |t - (v / s + z)| < 3e-6.  When
-// t is at least 2^-16 away from a half-integer, v / s + z (and therefore its
-// fp32 rounding, whose error is below 1e-6 at this magnitude) lies strictly
-// inside the same rounding interval, so rint(t) is the exact answer.  Any lane
-// with a value inside the 2^-16 band, or a scale outside [2^-100, 2^100]
-// (where rcp could lose accuracy), recomputes with the correctly rounded
-// division; for Gaussian weights that is roughly one element in 30 000.
-__device__ __forceinline__ uint32_t quantize8(const float v[8], float s, float zf) {
-  const float r = __builtin_amdgcn_rcpf(s);
+// Codes of 8 elements of a group with scale s, y = RN(1/s) (one correctly
+// rounded division per group, by the caller) and zero-point zf (an
+// integer-valued float): clamp(rint(fl32(v / s)) + z, 0, 15), bit-identical to
+// dividing each element, without dividing each element.  q0 = RN(v y) is
+// within one ulp of v / s, the residual r = v - q0 s is exact through fma, and
+// q1 = RN(q0 + r y) is then exactly RN(v / s) (Markstein's theorem for
+// division by a correctly rounded reciprocal; it needs no overflow or
+// underflow, which the scale range [2^-100, 2^100] guarantees for every
+// element whose quotient reaches 1/4 in magnitude -- smaller quotients round
+// to 0 either way).  Groups with a scale outside that range divide exactly.
+// (16-bit weights put about 2 quotients in 1000 exactly on a half-integer,
+// where only the exact quotient rounds correctly, half to even.)
+__device__ __forceinline__ uint32_t quantize8(const float v[8], float s, float y, float zf) {
+  const bool scale_ok = (s >= 0x1p-100f) && (s <= 0x1p100f);
   float k[8];
-  float dmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float t = fmaf(v[i], r, zf);
-    k[i] = rintf(t);
-    dmax = fmaxf(dmax, fabsf(t - k[i]));
+    const float q0 = v[i] * y;
+    const float r = fmaf(-q0, s, v[i]);
+    k[i] = rintf(fmaf(r, y, q0)) + zf;
   }
-  const bool fast = (s >= 0x1p-100f) && (s <= 0x1p100f) && (dmax <= kTieMargin);
-  if (!fast) {
+  if (__builtin_amdgcn_ballot_w64(!scale_ok)) {   // wavefront-uniform, practically never taken
 #pragma unroll
-    for (int i = 0; i < 8; ++i) k[i] = rintf(v[i] / s) + zf;
+    for (int i = 0; i < 8; ++i) {
+      const float e = rintf(v[i] / s) + zf;
+      if (!scale_ok) k[i] = e;
+    }
   }
   uint32_t word = 0;
 #pragma unroll
@@ -97,9 +98,10 @@ __global__ __launch_bounds__(256) void quantize_g128_flat_kernel(const uint8_t* 
     float s = (hi - lo) / kLevels;      // correctly rounded fp32 division
     if (s == 0.0f) s = 1.0f;
     const float zf = rintf(-lo / s);
+    const float y = 1.0f / s;           // correctly rounded reciprocal
     uint32_t out[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) out[q] = quantize8(&v[8 * q], s, zf);
+    for (int q = 0; q < 4; ++q) out[q] = quantize8(&v[8 * q], s, y, zf);
     const float z_next = __shfl_down(zf, 4, kWave);   // zero-point of the next (odd) group
     if (active) {
       st16_nt(codes + gi * 64 + part * 16, u32x4{out[0], out[1], out[2], out[3]});
@@ -205,9 +207,10 @@ __global__ __launch_bounds__(256) void quantize_g128_lds_kernel(const uint8_t* _
     float sc = (hi - lo) / kLevels;      // correctly rounded fp32 division
     if (sc == 0.0f) sc = 1.0f;
     const float zf = rintf(-lo / sc);
+    const float y = 1.0f / sc;          // correctly rounded reciprocal
     uint32_t out[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) out[q] = quantize8(&v[8 * q], sc, zf);
+    for (int q = 0; q < 4; ++q) out[q] = quantize8(&v[8 * q], sc, y, zf);
     const float z_next = __shfl_down(zf, 4, kWave);   // zero-point of the next (odd) group
     if (active) {
       st16_nt(codes + gi * 64 + part * 16, u32x4{out[0], out[1], out[2], out[3]});
@@ -257,8 +260,9 @@ __global__ __launch_bounds__(256) void quantize_g128_kernel(const uint8_t* __res
     float s = (hi - lo) / kLevels;      // correctly rounded fp32 division
     if (s == 0.0f) s = 1.0f;
     const float zf = rintf(-lo / s);    // in [0, 15] because lo <= 0 <= hi
+    const float y = 1.0f / s;           // correctly rounded reciprocal
 
-    const uint32_t word = quantize8(v, s, zf);
+    const uint32_t word = quantize8(v, s, y, zf);
     // Zero-point of the odd group of each pair, fetched from the next DPP row.
     const float z_next = __shfl_down(zf, 16, kWave);
     if (active) {

@@ -127,24 +127,23 @@ __global__ __launch_bounds__(256) void smooth_finalize_kernel(const float* __res
 // ----------------------------------------------------------------------------
 constexpr int kRqChunks = 8;
 constexpr int64_t kRqBatch = static_cast<int64_t>(kWave) * 8 * kRqChunks;   // 4096
-constexpr float kQ8Margin = 0.5f - 0x1p-12f;
 
-// clamp(rint(v / s), -128, 127) for 8 values, bit-identical to the correctly
-// rounded division.  Fast path t = v * rcp(s): with v_rcp_f32 within 1 ulp
-// and |v / s| <= 127 (|v| <= absmax = 127 s, or below the floor), |t - v/s|
-// is below 4e-5 and the fp32 rounding of v / s moves it by less than 8e-6, so
-// a t more than 2^-12 away from a half-integer rounds like v / s.  Chunks with
-// a value in that band, or a scale outside [2^-100, 2^100], divide exactly.
-__device__ __forceinline__ void quant8_int8(const float v[8], float s, float r, uint32_t* lo, uint32_t* hi) {
+// clamp(rint(fl32(v / s)), -128, 127) for 8 values, bit-identical to the
+// correctly rounded division, from y = RN(1/s) (one division per row, by the
+// caller): q0 = RN(v y), exact residual r = v - q0 s (fma), q1 = RN(q0 + r y)
+// = RN(v / s) by Markstein's theorem (no overflow or underflow for scales in
+// [2^-100, 2^100] and quotients of magnitude at least 1/4; smaller ones round
+// to 0 either way).  Rows with a scale outside that range divide exactly.
+__device__ __forceinline__ void quant8_int8(const float v[8], float s, float y, uint32_t* lo, uint32_t* hi) {
+  const bool scale_ok = (s >= 0x1p-100f) && (s <= 0x1p100f);
   float k[8];
-  float dmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float t = v[i] * r;
-    k[i] = rintf(t);
-    dmax = fmaxf(dmax, fabsf(t - k[i]));
+    const float q0 = v[i] * y;
+    const float r = fmaf(-q0, s, v[i]);
+    k[i] = rintf(fmaf(r, y, q0));
   }
-  if (!((s >= 0x1p-100f) && (s <= 0x1p100f) && (dmax <= kQ8Margin))) {
+  if (!scale_ok) {   // uniform: one scale per row
 #pragma unroll
     for (int i = 0; i < 8; ++i) k[i] = rintf(v[i] / s);
   }
@@ -217,7 +216,7 @@ __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restric
   amax = wave_max(amax);
   const float s = fmaxf(amax, kAbsFloor) / kQ8;
   if (lane == 0) scale[row] = s;
-  const float r = __builtin_amdgcn_rcpf(s);
+  const float r = 1.0f / s;   // correctly rounded reciprocal
 
   for (int64_t base = 0; base < K; base += kRqBatch) {
     if (!resident) rq_load_batch<DT, MODE, SM>(arow, smooth, K, base, lane, v);
