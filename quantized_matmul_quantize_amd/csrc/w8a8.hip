@@ -38,10 +38,14 @@ constexpr int64_t kMaxK = 131008;
 constexpr int kCmCols = 512;
 constexpr int64_t kCmBand = 128;
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
+// Zeroes two arrays of n words in one launch (the column maxima targets).
+__global__ __launch_bounds__(256) void fill_zero2_kernel(uint32_t* __restrict__ p, uint32_t* __restrict__ q,
+                                                         int64_t n) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     p[i] = 0u;
+    q[i] = 0u;
+  }
 }
 
 template <int DT>
@@ -608,8 +612,7 @@ extern "C" int sq_smooth_factors(const void* X, int x_dtype, int64_t M, const vo
   uint32_t* cx = reinterpret_cast<uint32_t*>(x_colmax);
   uint32_t* cw = reinterpret_cast<uint32_t*>(w_colmax);
   const unsigned fill_blocks = static_cast<unsigned>(ceil_div(K, 256));
-  fill_zero_kernel<<<fill_blocks, 256, 0, s>>>(cx, K);
-  fill_zero_kernel<<<fill_blocks, 256, 0, s>>>(cw, K);
+  fill_zero2_kernel<<<fill_blocks, 256, 0, s>>>(cx, cw, K);
   const int64_t bands_x = ceil_div(M, kCmBand);
   const int64_t bands_w = ceil_div(N, kCmBand);
   const dim3 grid(static_cast<unsigned>(ceil_div(K, kCmCols)), static_cast<unsigned>(bands_x + bands_w));
