@@ -425,10 +425,10 @@ __global__ __launch_bounds__(512) void w4_mfma_skinny_kernel(const uint8_t* __re
 // Operands reach LDS by buffer loads that write LDS directly, each wavefront
 // into rings of its own, D groups ahead (no block barrier in the main loop):
 //  * activations, one group = MT rows x 256 bytes: sixteen lanes fetch one
-//    row's 256 bytes; 16-byte chunk j of row r sits at position j ^ (r & 15);
+//    row's 256 bytes; 16-byte chunk j of row r sits at position j ^ row_swz(r);
 //  * codes, one group = 16 NT rows x 64 bytes (NT = 2 or 4 slices of 16
 //    weight rows per block): four lanes fetch one row's 64 bytes; 16-byte part p of row r (of a 16-row slice) sits at slot
-//    4 r + (p ^ h(r)), h(r) = ((r >> 1) ^ (r >> 3)) & 3;
+//    4 r + (p ^ code_swz(r));
 //  * scales, one group = 16 NT floats (one 4-byte load per lane; lanes past
 //    the block's rows fall outside the buffer and read 0);
 // and the block's zero-point bytes are copied to LDS once.  Both swizzles make
@@ -464,7 +464,15 @@ struct LdsCfg {
   static_assert(kLdsWaves * MT * kPartPitch * 4 <= kLdsWaves * kWaveBytes, "partial tiles fit the rings");
 };
 
-__device__ __forceinline__ int code_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// LDS swizzles.  A ds_read_b128 is served in passes over groups of lanes
+// that are not simply 16 consecutive lanes: measured on gfx950 (bank-conflict
+// counter), the layout "chunk j of row r at j ^ (r & 15)" still costs two
+// passes per read where these cost one.  row_swz: 16-byte chunk j of a
+// 256-byte row r sits at j ^ row_swz(r) (the two low bits of r move to the
+// high bits of the position).  code_swz: 16-byte part p of a 64-byte row r of
+// a 16-row slice sits at slot 4 r + (p ^ code_swz(r)).
+__host__ __device__ constexpr int row_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__host__ __device__ constexpr int code_swz(int r) { return ((r >> 2) ^ ((r >> 1) & 2)) & 3; }
 
 // Host and device: it is called from lambdas, which HIP compiles for both sides.
 __host__ __device__ inline lds_ptr_t lds_at(uint32_t byte) { return (lds_ptr_t)(uintptr_t)byte; }
@@ -530,7 +538,7 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
 #pragma unroll
   for (int q = 0; q < Cfg::kXLoads; ++q) {
     const int r = 4 * q + (lane >> 4);
-    xoff[q] = r * kb2 + (((lane & 15) ^ (r & 15)) * 16);
+    xoff[q] = r * kb2 + (((lane & 15) ^ row_swz(r & 15)) * 16);
   }
 #pragma unroll
   for (int q = 0; q < NT; ++q) {
@@ -603,7 +611,7 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
 #pragma unroll
       for (int mt = 0; mt < MT / 16; ++mt) {
         const int r = 16 * mt + fr;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(xg + r * 256 + (((4 * fp + c) ^ fr) * 16));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xg + r * 256 + (((4 * fp + c) ^ row_swz(fr)) * 16));
         xa[mt][0] = v.x;
         xa[mt][1] = v.y;
         xa[mt][2] = v.z;
@@ -678,8 +686,9 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
 // stream from HBM).  Activations (16 tokens x 1 KiB per step, one token row
 // per load) and scales (one group of 64 rows per load) come the same way.
 // S LDS stages (loads S - 1 steps ahead), one barrier per step.  Swizzles: 16-byte piece p of code
-// row r sits at position p ^ (r & 15) of the row, piece p of token row t at
-// p ^ (t & 15), so the fragment reads of 16 rows (tokens) are conflict-free.
+// row r sits at position p ^ (r & 15) of the row (a lane reads piece 4 w + p
+// of row l % 16, so this is already conflict-free), piece p of token row t at
+// p ^ row_swz(t & 15).
 // ----------------------------------------------------------------------------
 template <int NT, int S>
 struct RowsCfg {
@@ -736,7 +745,7 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
 
   // Load offsets.  Codes: load q of wavefront w covers rows 4 (NT w + q) ..
   // +4, lane l row + l/16, piece (l%16) ^ (row & 15).  Activations: load q of
-  // wavefront w is token row 4 w + q, lane l piece l ^ (token & 15).  Scales:
+  // wavefront w is token row 4 w + q, lane l piece l ^ row_swz(token & 15).  Scales:
   // wavefront w loads group 4 step + w of rows 0..63 (lane l: row l).
   int coff[4], xoff[4];
 #pragma unroll
@@ -747,7 +756,7 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int tr = 4 * wave + q;
-    xoff[q] = tr * kb2 + ((lane ^ (tr & 15)) * 16);
+    xoff[q] = tr * kb2 + ((lane ^ row_swz(tr & 15)) * 16);
   }
   const int soff = lane * G * 4;
   auto issue = [&](int st) {
@@ -807,7 +816,7 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int xp = 16 * wave + 4 * fp + c;   // piece of the token row
-        const u32x4 v = *reinterpret_cast<const u32x4*>(xg + fr * 1024 + ((xp ^ fr) * 16));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xg + fr * 1024 + ((xp ^ row_swz(fr)) * 16));
         const uint32_t xa[4] = {v.x, v.y, v.z, v.w};
         xs = mfma16x16x32<XDT>(xa, ones, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : xs);
 #pragma unroll
@@ -863,8 +872,8 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
 // each wavefront loads the codes and scales of its own 32 rows.  Groups are
 // staged kTileD ahead in kTileD + 1 slots, with one block barrier per group.
 // LDS layout of a slot (same swizzles as the kernel above):
-//  * activations, BM rows x 256 bytes, chunk j of row r at position j ^ (r & 15);
-//  * codes, 8 slices of 16 rows x 64 bytes, part p of row r at 4 r + (p ^ h(r));
+//  * activations, BM rows x 256 bytes, chunk j of row r at position j ^ row_swz(r);
+//  * codes, 8 slices of 16 rows x 64 bytes, part p of row r at 4 r + (p ^ code_swz(r));
 //  * scales, 256 bytes per wavefront: its 32 rows, loaded twice over.
 // Two blocks of BM = 64 fit a compute unit (about 75 KiB each at K = 4096),
 // so each SIMD interleaves the ALU work of one wavefront with the matrix work
@@ -958,7 +967,7 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
 #pragma unroll
   for (int q = 0; q < Cfg::kXLoads; ++q) {
     const int r = 4 * (wave * Cfg::kXLoads + q) + (lane >> 4);
-    xoff[q] = r * kb2 + (((lane & 15) ^ (r & 15)) * 16);
+    xoff[q] = r * kb2 + (((lane & 15) ^ row_swz(r & 15)) * 16);
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -1010,7 +1019,7 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
       uint32_t xa[MT][4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(xg + (16 * mt + fr) * 256 + (((4 * fp + c) ^ fr) * 16));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xg + (16 * mt + fr) * 256 + (((4 * fp + c) ^ row_swz(fr)) * 16));
         xa[mt][0] = v.x;
         xa[mt][1] = v.y;
         xa[mt][2] = v.z;
