@@ -684,7 +684,8 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
 // buffer load covering 4 rows x 256 contiguous bytes, where w4_lds_kernel
 // fetches 64-byte pieces of 16 rows per instruction (a measurably slower
 // stream from HBM).  Activations (16 tokens x 1 KiB per step, one token row
-// per load) and scales (one group of 64 rows per load) come the same way.
+// per load) and scales (four groups of 16 rows per load, 16 bytes per row)
+// come the same way.
 // S LDS stages (loads S - 1 steps ahead), one barrier per step.  Swizzles: 16-byte piece p of code
 // row r sits at position p ^ (r & 15) of the row (a lane reads piece 4 w + p
 // of row l % 16, so this is already conflict-free), piece p of token row t at
@@ -695,7 +696,7 @@ struct RowsCfg {
   static constexpr int kRows = 16 * NT;
   static constexpr int kCodeBytes = kRows * 256;        // 4 groups x 64 bytes per row
   static constexpr int kXBytes = 16 * 1024;             // 16 tokens x 512 k x 2 bytes
-  static constexpr int kScaleBytes = 4 * 64 * 4;        // 4 groups x 64 rows
+  static constexpr int kScaleBytes = 4 * 64 * 4;        // 64 rows x 4 groups
   static constexpr int kStageBytes = kCodeBytes + kXBytes + kScaleBytes;
   static constexpr int kLoads = NT + 4 + 1;              // per wavefront per step
   static constexpr int kPartPitch = kRows + 4;
@@ -745,8 +746,9 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
 
   // Load offsets.  Codes: load q of wavefront w covers rows 4 (NT w + q) ..
   // +4, lane l row + l/16, piece (l%16) ^ (row & 15).  Activations: load q of
-  // wavefront w is token row 4 w + q, lane l piece l ^ row_swz(token & 15).  Scales:
-  // wavefront w loads group 4 step + w of rows 0..63 (lane l: row l).
+  // wavefront w is token row 4 w + q, lane l piece l ^ row_swz(token & 15).
+  // Scales: wavefront w loads the step's four groups of rows 16 w .. + 16
+  // (lane l: row 16 w + l / 4, group l % 4), 16 contiguous bytes per row.
   int coff[4], xoff[4];
 #pragma unroll
   for (int q = 0; q < NT; ++q) {
@@ -758,7 +760,7 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
     const int tr = 4 * wave + q;
     xoff[q] = tr * kb2 + ((lane ^ row_swz(tr & 15)) * 16);
   }
-  const int soff = lane * G * 4;
+  const int soff = (16 * wave + (lane >> 2)) * G * 4 + (lane & 3) * 4;
   auto issue = [&](int st) {
     const int sc = min(st, nsteps - 1);   // past the end: reload the last step (never read)
     const uint32_t stage = lbase + (st % S) * Cfg::kStageBytes;
@@ -771,8 +773,7 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(uintptr_t)(stage + Cfg::kCodeBytes + (4 * wave + q) * 1024),
                                                16, xoff[q], sc * 1024, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        sr, (lds_ptr_t)(uintptr_t)(stage + Cfg::kCodeBytes + Cfg::kXBytes + wave * 256), 4, soff, (4 * sc + wave) * 4,
-        0, 0);
+        sr, (lds_ptr_t)(uintptr_t)(stage + Cfg::kCodeBytes + Cfg::kXBytes + wave * 256), 4, soff, sc * 16, 0, 0);
   };
 
   for (int st = 0; st < D; ++st) issue(st);
@@ -800,7 +801,7 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
     if (g < G) {
       const uint8_t* cg = lds + (st % S) * Cfg::kStageBytes;
       const uint8_t* xg = cg + Cfg::kCodeBytes;
-      const float* sg = reinterpret_cast<const float*>(xg + Cfg::kXBytes + wave * 256);
+      const float* sg = reinterpret_cast<const float*>(xg + Cfg::kXBytes);   // [row][4 groups]
       const int cp = 4 * wave + fp;   // this lane's 16-byte piece of a code row
       u32x4 cw[NT];
       float sv[NT], zo[NT];
@@ -808,7 +809,7 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
       for (int nt = 0; nt < NT; ++nt) {
         const int r = 16 * nt + fr;
         cw[nt] = *reinterpret_cast<const u32x4*>(cg + r * 256 + ((cp ^ fr) * 16));
-        sv[nt] = sg[r];
+        sv[nt] = sg[4 * r + wave];
         const uint32_t zbyte = ztab[r * zb + (g >> 1)];
         zo[nt] = Mg::offset + static_cast<float>((g & 1) ? (zbyte >> 4) : (zbyte & 15u));
       }

