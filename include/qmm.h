@@ -129,8 +129,8 @@ int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  * X : [M, K] QMM_BF16 or QMM_F16.  Y : [M, N] of X's type or QMM_F32.
  * M >= 1, group 128, K <= 2^24, N and M < 2^31 (QMM_ERANGE otherwise).
  * A block keeps the zero points of its weight rows in
- * LDS, which bounds K: K <= 53248 is always served for M > 16 and
- * K <= 385024 for M <= 16; beyond that bf16 runs a slower kernel without the
+ * LDS, which bounds K: K <= 52224 is always served for M > 16 and
+ * K <= 384000 for M <= 16; beyond that bf16 runs a slower kernel without the
  * table and fp16 returns QMM_EUNSUPPORTED.
  * ------------------------------------------------------------------------- */
 int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,

@@ -47,24 +47,34 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
   }
 }
 
-// Copies `total` elements starting at src into LDS; elements at or past
-// `valid` become 0.  Each pass issues all of a thread's loads before any
-// store, so a copy costs one memory round trip per pass rather than one per
-// element; the indexes are clamped into the valid range, so every load is in
-// bounds.  Used for a block's rows of scales or zero points, which are
-// consecutive in memory.
-template <typename T, int NTHREADS>
-__device__ __forceinline__ void copy_to_lds(T* dst, const T* __restrict__ src, int total, int valid, int tid) {
+// Row pitch of a block's zero-point table in LDS: the zb bytes of a row
+// rounded up to an odd number of dwords, so that the 16 rows of a fragment
+// read fall in 16 different banks (with zb a multiple of 32 bytes, rows r and
+// r + 8 would share one).
+__host__ __device__ constexpr int zero_pitch(int zb) { return 4 * (((zb + 3) / 4) | 1); }
+
+// The block's zero-point bytes (rows x zb, contiguous in memory) into LDS at
+// row pitch zp; rows from `valid` on read 0.  Each pass issues all of a
+// thread's loads before any store (one memory round trip per pass, not per
+// byte); indexes are clamped into the valid range, so every load is in bounds.
+template <int NTHREADS>
+__device__ __forceinline__ void copy_zeros_to_lds(uint8_t* dst, const uint8_t* __restrict__ src, int rows, int zb,
+                                                  int zp, int valid, int tid) {
   constexpr int kPer = 8;
+  const int total = rows * zb;
+  const int lim = valid * zb;
   for (int base = 0; base < total; base += kPer * NTHREADS) {
-    T v[kPer];
+    uint8_t v[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-      if (base + j * NTHREADS < total) v[j] = src[min(base + j * NTHREADS + tid, valid - 1)];   // uniform test
+      if (base + j * NTHREADS < total) v[j] = src[min(base + j * NTHREADS + tid, lim - 1)];   // uniform test
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int idx = base + j * NTHREADS + tid;
-      if (idx < total) dst[idx] = (idx < valid) ? v[j] : T(0);
+      if (idx < total) {
+        const int r = idx / zb;
+        dst[r * zp + (idx - r * zb)] = (idx < lim) ? v[j] : uint8_t(0);
+      }
     }
   }
 }
@@ -572,7 +582,8 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
     issue_x(i);
     issue_w(i);
   }
-  copy_to_lds<uint8_t, 256>(ztab, zeros + n0 * zb, kRows * zb, static_cast<int>(nrows) * zb, tid);
+  const int zp = zero_pitch(zb);
+  copy_zeros_to_lds<256>(ztab, zeros + n0 * zb, kRows, zb, zp, static_cast<int>(nrows), tid);
   __syncthreads();   // zero-point table
 
   f32x4 acc[MT / 16][NT];
@@ -601,7 +612,7 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
     for (int nt = 0; nt < NT; ++nt) {
       cw[nt] = *reinterpret_cast<const u32x4*>(cg + nt * 1024 + crd);
       sv[nt] = sg[16 * nt + fr];
-      const uint32_t zbyte = ztab[(16 * nt + fr) * zb + (g >> 1)];
+      const uint32_t zbyte = ztab[(16 * nt + fr) * zp + (g >> 1)];
       zo[nt] = Mg::offset + static_cast<float>((g & 1) ? (zbyte >> 4) : (zbyte & 15u));
     }
     f32x4 part[MT / 16][NT], xs[MT / 16];
@@ -777,7 +788,8 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
   };
 
   for (int st = 0; st < D; ++st) issue(st);
-  copy_to_lds<uint8_t, 256>(ztab, zeros + n0 * zb, kRows * zb, static_cast<int>(nrows) * zb, tid);
+  const int zp = zero_pitch(zb);
+  copy_zeros_to_lds<256>(ztab, zeros + n0 * zb, kRows, zb, zp, static_cast<int>(nrows), tid);
 
   f32x4 acc[NT];
 #pragma unroll
@@ -810,7 +822,7 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
         const int r = 16 * nt + fr;
         cw[nt] = *reinterpret_cast<const u32x4*>(cg + r * 256 + ((cp ^ fr) * 16));
         sv[nt] = sg[4 * r + wave];
-        const uint32_t zbyte = ztab[r * zb + (g >> 1)];
+        const uint32_t zbyte = ztab[r * zp + (g >> 1)];
         zo[nt] = Mg::offset + static_cast<float>((g & 1) ? (zbyte >> 4) : (zbyte & 15u));
       }
       f32x4 part[NT], xs;
@@ -979,7 +991,8 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
 
 
   for (int i = 0; i < kTileD; ++i) tile_issue<BM>(i, G, wave, lbase, xr, cr, sr, xoff, coff, soff);
-  copy_to_lds<uint8_t, 256>(ztab, zeros + n0 * zb, kTileN * zb, static_cast<int>(nrows) * zb, tid);
+  const int zp = zero_pitch(zb);
+  copy_zeros_to_lds<256>(ztab, zeros + n0 * zb, kTileN, zb, zp, static_cast<int>(nrows), tid);
 
   f32x4 acc[MT][2];
 #pragma unroll
@@ -1011,7 +1024,7 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
     for (int nt = 0; nt < 2; ++nt) {
       cw[nt] = *reinterpret_cast<const u32x4*>(cg + (2 * wave + nt) * 1024 + crd);
       sv[nt] = sg[16 * nt + fr];
-      const uint32_t zbyte = ztab[(32 * wave + 16 * nt + fr) * zb + (i >> 1)];
+      const uint32_t zbyte = ztab[(32 * wave + 16 * nt + fr) * zp + (i >> 1)];
       zo[nt] = Mg::offset + static_cast<float>((i & 1) ? (zbyte >> 4) : (zbyte & 15u));
     }
     f32x4 part[MT][2], xs[MT];
@@ -1165,7 +1178,8 @@ bool launch_lds_t(const uint8_t* codes, const float* scales, const uint8_t* zero
                   const uint16_t* x, int64_t M, void* y, hipStream_t s) {
   using Cfg = LdsCfg<MT, NT>;
   const int64_t G = K / kGroup;
-  const size_t lds = static_cast<size_t>(kLdsWaves) * Cfg::kWaveBytes + static_cast<size_t>(Cfg::kRows) * ((G + 1) / 2);
+  const size_t lds = static_cast<size_t>(kLdsWaves) * Cfg::kWaveBytes +
+                    static_cast<size_t>(Cfg::kRows) * zero_pitch(static_cast<int>((G + 1) / 2));
   if (lds > kLdsBytesMax) return false;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_lds_kernel<XDT, YDT, MT, NT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -1190,7 +1204,8 @@ bool launch_tile_t(const uint8_t* codes, const float* scales, const uint8_t* zer
                    const uint16_t* x, int64_t M, void* y, hipStream_t s) {
   using Cfg = TileCfg<BM>;
   const int64_t G = K / kGroup;
-  const size_t lds = static_cast<size_t>(kTileSlots) * Cfg::kSlotBytes + static_cast<size_t>(kTileN) * ((G + 1) / 2);
+  const size_t lds = static_cast<size_t>(kTileSlots) * Cfg::kSlotBytes +
+                    static_cast<size_t>(kTileN) * zero_pitch(static_cast<int>((G + 1) / 2));
   if (lds > kLdsBytesMax) return false;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_tile_kernel<XDT, YDT, BM>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -1205,7 +1220,8 @@ bool launch_rows_t(const uint8_t* codes, const float* scales, const uint8_t* zer
                    const uint16_t* x, int64_t M, void* y, hipStream_t s) {
   using Cfg = RowsCfg<NT, S>;
   const int64_t G = K / kGroup;
-  const size_t lds = S * static_cast<size_t>(Cfg::kStageBytes) + static_cast<size_t>(Cfg::kRows) * ((G + 1) / 2);
+  const size_t lds = S * static_cast<size_t>(Cfg::kStageBytes) +
+                    static_cast<size_t>(Cfg::kRows) * zero_pitch(static_cast<int>((G + 1) / 2));
   if (lds > kLdsBytesMax) return false;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_rows_kernel<XDT, YDT, NT, S>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
