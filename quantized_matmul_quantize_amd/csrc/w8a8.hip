@@ -242,8 +242,11 @@ __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restric
 // l%16 of B, i.e. column l%16 of C) and k = 16*(l/16) .. +16; D lane l holds
 // rows 4*(l/16) .. +4 of column l%16.
 //
-// Block tile 256 x 128, k-step 128 (two 64-wide chunks), four wavefronts each
-// owning 64 rows x all 128 columns (4 x 8 instructions per chunk).
+// Block tile 256 x 128, k-step 128 (two 64-wide chunks), eight wavefronts:
+// wavefront w = 4 wn + wm owns rows 64 wm .. + 64 and columns 64 wn .. + 64
+// (4 x 4 instructions per chunk).  Two wavefronts share each SIMD, so one's
+// MFMAs run while the other waits on LDS or on the barrier (measured 36.4 us
+// against 41.8 us for four wavefronts of 64 x 128 at 2048 x 4096 x 4096).
 //
 // Global -> LDS: buffer loads that write LDS directly (16 bytes per lane,
 // lane l of an instruction lands at byte 16 l of its destination), so no
@@ -277,15 +280,9 @@ constexpr int kBM = 256, kBN = 128, kBK = 128;
 constexpr int kSlice = 16 * kBK;               // one 16-row slice of a stage: 2 KiB
 constexpr int kStageA = kBM * kBK;             // 32 KiB
 constexpr int kStage = (kBM + kBN) * kBK;      // A then B: 48 KiB
-constexpr int kLoadsA = kBM * kBK / 1024 / 4;  // 1 KiB load instructions per wavefront per step: 8
-constexpr int kLoadsB = kBN * kBK / 1024 / 4;  // 4
-constexpr int kPitch2 = 272;                   // epilogue LDS row pitch, 2-byte outputs (64 rows)
-constexpr int kPitch4 = 528;                   // 4-byte outputs (32 rows per pass)
-constexpr int kEpiWave = 64 * kPitch2;         // per-wavefront epilogue region
 constexpr size_t kGemmLds = 3 * kStage;        // 144 KiB
 constexpr int kXcds = 8;
 constexpr int kOutOfRange = 0x40000000;        // added to a lane offset: reads zero
-static_assert(32 * kPitch4 <= kEpiWave && 4 * kEpiWave <= static_cast<int>(kGemmLds), "epilogue must fit");
 
 __device__ __forceinline__ void xcd_tile(int64_t b, int64_t tm, int64_t tn, int64_t* m_tile, int64_t* n_tile,
                                          bool* valid) {
@@ -304,14 +301,23 @@ __device__ __forceinline__ void xcd_tile(int64_t b, int64_t tm, int64_t tn, int6
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 
+constexpr int kLoadsA8 = kBM * kBK / 1024 / 8;  // 1 KiB load instructions per wavefront per step: 4
+constexpr int kLoadsB8 = kBN * kBK / 1024 / 8;  // 2
+constexpr int kP2 = 144;                        // epilogue row pitch, 64 x 2-byte outputs
+constexpr int kP4 = 272;                        // 64 x 4-byte outputs
+constexpr int kEpiWave = 64 * kP4;              // per-wavefront epilogue region (64 rows)
+static_assert(64 * kP2 <= kEpiWave && 8 * kEpiWave <= static_cast<int>(kGemmLds), "epilogue must fit");
+
 template <int YDT>
-__global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__ A, const float* __restrict__ ascale,
-                                                      const int8_t* __restrict__ B, const float* __restrict__ bscale,
-                                                      int64_t M, int64_t N, int64_t K, void* __restrict__ Y) {
+__global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__ A, const float* __restrict__ ascale,
+                                                       const int8_t* __restrict__ B, const float* __restrict__ bscale,
+                                                       int64_t M, int64_t N, int64_t K, void* __restrict__ Y) {
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave & 3;
+  const int wn = wave >> 2;
   int64_t mt, nt;
   bool valid;
   xcd_tile(blockIdx.x, (M + kBM - 1) / kBM, (N + kBN - 1) / kBN, &mt, &nt, &valid);
@@ -320,7 +326,6 @@ __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__
   const int64_t n0 = nt * kBN;
   const int kk = static_cast<int>(K);
 
-  // One scalar buffer resource per operand tile, sized to its valid rows.
   const int64_t arows = (M - m0 < kBM) ? M - m0 : kBM;
   const int64_t brows = (N - n0 < kBN) ? N - n0 : kBN;
   const __amdgpu_buffer_rsrc_t arsrc =
@@ -328,81 +333,78 @@ __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__
   const __amdgpu_buffer_rsrc_t brsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(B + n0 * K), 0, static_cast<int>(brows * K), kBufferWord3);
 
-  // Load instruction q of this wavefront fills half-slice I = 4 * wave + q of
-  // A (wave's A quarter: 8 instructions over half-slices 8 wave .. +8) or of
-  // B; lane l writes slot 64 (I & 1) + l of slice I / 2, i.e. row
-  // r = 8 (I & 1) + l / 8 of that slice, chunk (l % 8) ^ g(r).
-  int aoff[kLoadsA], boff[kLoadsB], bz[kLoadsB];
+  // Load q of this wavefront fills half-slice I = loads * wave + q of A (4
+  // per wavefront) or of B (2); lane l writes slot 64 (I & 1) + l of slice
+  // I / 2, i.e. row r = 8 (I & 1) + l / 8 of that slice, chunk (l % 8) ^ g(r).
+  int aoff[kLoadsA8], boff[kLoadsB8], bz[kLoadsB8];
 #pragma unroll
-  for (int q = 0; q < kLoadsA; ++q) {
-    const int I = kLoadsA * wave + q;
+  for (int q = 0; q < kLoadsA8; ++q) {
+    const int I = kLoadsA8 * wave + q;
     const int r = 8 * (I & 1) + (lane >> 3);
     const int row = 16 * (I >> 1) + r;
     aoff[q] = row * kk + (((lane & 7) ^ swz(r)) * 16);
   }
 #pragma unroll
-  for (int q = 0; q < kLoadsB; ++q) {
-    const int I = kLoadsB * wave + q;
+  for (int q = 0; q < kLoadsB8; ++q) {
+    const int I = kLoadsB8 * wave + q;
     const int r = 8 * (I & 1) + (lane >> 3);
     const int row = 16 * (I >> 1) + r;
     const int c = (lane & 7) ^ swz(r);
     boff[q] = row * kk + c * 16;
-    bz[q] = (c >= 4) ? kOutOfRange : 0;   // second 64-wide chunk
+    bz[q] = (c >= 4) ? kOutOfRange : 0;
   }
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const int nsteps = (kk + kBK - 1) / kBK;
   auto issue = [&](int step, int stage) {
     const int st = min(step, nsteps - 1);
     const int k0 = st * kBK;
-    const bool tail = k0 + 64 >= kk;   // only when K % 128 == 64, on the last step
+    const bool tail = k0 + 64 >= kk;
     const uint32_t sbase = lds_base + static_cast<uint32_t>(stage * kStage);
 #pragma unroll
-    for (int q = 0; q < kLoadsA; ++q) {
-      const int I = kLoadsA * wave + q;
+    for (int q = 0; q < kLoadsA8; ++q) {
+      const int I = kLoadsA8 * wave + q;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_ptr_t)(uintptr_t)(sbase + (I >> 1) * kSlice + (I & 1) * 1024),
                                                16, aoff[q], k0, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < kLoadsB; ++q) {
-      const int I = kLoadsB * wave + q;
+    for (int q = 0; q < kLoadsB8; ++q) {
+      const int I = kLoadsB8 * wave + q;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           brsrc, (lds_ptr_t)(uintptr_t)(sbase + kStageA + (I >> 1) * kSlice + (I & 1) * 1024), 16,
           boff[q] + (tail ? bz[q] : 0), k0, 0, 0);
     }
   };
 
-  // Fragment read offsets: lane l reads row l%16, part l/16 of chunk h.
   const int fr = lane & 15;
   const int rd0 = (8 * fr + ((lane >> 4) ^ swz(fr))) * 16;
   const int rd1 = (8 * fr + ((4 + (lane >> 4)) ^ swz(fr))) * 16;
-  i32x4 fa0[4], fb0[8], fa1[4], fb1[8];
-  auto read_chunk = [&](i32x4 (&fa)[4], i32x4 (&fb)[8], int stage, int rd) {
-    const int8_t* sa = lds + stage * kStage + (4 * wave) * kSlice + rd;
-    const int8_t* sb = lds + stage * kStage + kStageA + rd;
+  i32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto read_chunk = [&](i32x4 (&fa)[4], i32x4 (&fb)[4], int stage, int rd) {
+    const int8_t* sa = lds + stage * kStage + (4 * wm) * kSlice + rd;
+    const int8_t* sb = lds + stage * kStage + kStageA + (4 * wn) * kSlice + rd;
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const i32x4*>(sa + i * kSlice);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) fb[j] = *reinterpret_cast<const i32x4*>(sb + j * kSlice);
+    for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const i32x4*>(sb + j * kSlice);
   };
   auto barrier = [&]() {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   };
 
-  i32x4 acc[4][8];
+  i32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-  // Prologue: loads of steps 0 and 1; wait for step 0, barrier, fragments (0, 0).
   issue(0, 0);
   issue(1, 1);
-  wait_vm<kLoadsA + kLoadsB>();
+  wait_vm<kLoadsA8 + kLoadsB8>();
   barrier();
   read_chunk(fa0, fb0, 0, rd0);
 
-  int s0 = 0;   // stage of step t; step t+1 uses (s0+1)%3, step t+2 (s0+2)%3
+  int s0 = 0;
   for (int t = 0; t < nsteps; ++t) {
     const int s1 = (s0 == 2) ? 0 : s0 + 1;
     const int s2 = (s1 == 2) ? 0 : s1 + 1;
@@ -411,71 +413,70 @@ __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa0[i], fb0[j], acc[i][j], 0, 0, 0);
-    // 12 groups of 2 MFMAs, each followed by one fragment read and one load.
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa0[i], fb0[j], acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int g = 0; g < 12; ++g) {
+    for (int g = 0; g < 6; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);   // chunk-0 work stays ahead of the wait
-    // This wave's loads of step t+1 are complete once only step t+2's remain.
-    wait_vm<kLoadsA + kLoadsB>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): fragments (t, 1) have landed
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<kLoadsA8 + kLoadsB8>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     barrier();
     read_chunk(fa0, fb0, s1, rd0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa1[i], fb1[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa1[i], fb1[j], acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int g = 0; g < 12; ++g) {
+    for (int g = 0; g < 8; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     s0 = s1;
   }
   wait_vm<0>();
   __syncthreads();   // the epilogue reuses the LDS
 
-  // Epilogue.  Tile (i, j), register r: row 16 i + 4 (lane/16) + r of the
-  // wavefront's 64, column 16 j + lane%16 of the block's 128.
+  // Epilogue: tile (i, j), register r: row 16 i + 4 (lane/16) + r of the
+  // wavefront's 64, column 16 j + lane%16 of its 64.
   int8_t* region = lds + wave * kEpiWave;
-  const int64_t mw = m0 + 64 * wave;
-  float bs[8];
+  const int64_t mw = m0 + 64 * wm;
+  const int64_t nw = n0 + 64 * wn;
+  float bs[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t n = n0 + 16 * j + (lane & 15);
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = nw + 16 * j + (lane & 15);
     bs[j] = (YDT == QMM_I32) ? 1.0f : bscale[n < N ? n : N - 1];
   }
   if constexpr (YDT == QMM_BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int lr = 16 * i + 4 * (lane >> 4) + r;
         const int64_t m = mw + lr;
         const float as = ascale[m < M ? m : M - 1];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
           const float f = static_cast<float>(acc[i][j][r]) * as * bs[j];
-          *reinterpret_cast<uint16_t*>(region + lr * kPitch2 + (16 * j + (lane & 15)) * 2) =
+          *reinterpret_cast<uint16_t*>(region + lr * kP2 + (16 * j + (lane & 15)) * 2) =
               static_cast<uint16_t>(f32_to_bf16_bits(f));
         }
       }
-    }
     __syncthreads();
     const bool vec = (N % 8 == 0) && ((reinterpret_cast<uintptr_t>(Y) & 15) == 0);
 #pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-      const int lr = 4 * it + (lane >> 4);
+    for (int it = 0; it < 8; ++it) {
+      const int lr = 8 * it + (lane >> 3);
       const int64_t m = mw + lr;
-      const int64_t n = n0 + (lane & 15) * 8;
+      const int64_t n = nw + (lane & 7) * 8;
       if (m >= M || n >= N) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(region + lr * kPitch2 + (lane & 15) * 16);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region + lr * kP2 + (lane & 7) * 16);
       uint16_t* dst = static_cast<uint16_t*>(Y) + m * N + n;
       if (vec && n + 8 <= N) {
         *reinterpret_cast<u32x4*>(dst) = v;
@@ -484,44 +485,38 @@ __global__ __launch_bounds__(256) void i8_gemm_kernel(const int8_t* __restrict__
       }
     }
   } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = 16 * i + 4 * (lane >> 4) + r;
+        const int64_t m = mw + lr;
+        float as = 1.0f;
+        if constexpr (YDT == QMM_F32) as = ascale[m < M ? m : M - 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t bits;
+          if constexpr (YDT == QMM_I32) bits = static_cast<uint32_t>(acc[i][j][r]);
+          else bits = __float_as_uint(static_cast<float>(acc[i][j][r]) * as * bs[j]);
+          *reinterpret_cast<uint32_t*>(region + lr * kP4 + (16 * j + (lane & 15)) * 4) = bits;
+        }
+      }
+    __syncthreads();
     const bool vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(Y) & 15) == 0);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * half + ii;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lr = 16 * ii + 4 * (lane >> 4) + r;   // row within this 32-row pass
-          const int64_t m = mw + 32 * half + lr;
-          float as = 1.0f;
-          if constexpr (YDT == QMM_F32) as = ascale[m < M ? m : M - 1];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            uint32_t bits;
-            if constexpr (YDT == QMM_I32) bits = static_cast<uint32_t>(acc[i][j][r]);
-            else bits = __float_as_uint(static_cast<float>(acc[i][j][r]) * as * bs[j]);
-            *reinterpret_cast<uint32_t*>(region + lr * kPitch4 + (16 * j + (lane & 15)) * 4) = bits;
-          }
-        }
-      }
-      __syncthreads();
 #pragma unroll 4
-      for (int it = 0; it < 16; ++it) {
-        const int lr = 2 * it + (lane >> 5);
-        const int64_t m = mw + 32 * half + lr;
-        const int64_t n = n0 + (lane & 31) * 4;
-        if (m < M && n < N) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(region + lr * kPitch4 + (lane & 31) * 16);
-          uint32_t* dst = static_cast<uint32_t*>(Y) + m * N + n;
-          if (vec && n + 4 <= N) {
-            *reinterpret_cast<u32x4*>(dst) = v;
-          } else {
-            for (int e = 0; e < 4 && n + e < N; ++e) dst[e] = v[e];
-          }
+    for (int it = 0; it < 16; ++it) {
+      const int lr = 4 * it + (lane >> 4);
+      const int64_t m = mw + lr;
+      const int64_t n = nw + (lane & 15) * 4;
+      if (m < M && n < N) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(region + lr * kP4 + (lane & 15) * 16);
+        uint32_t* dst = static_cast<uint32_t*>(Y) + m * N + n;
+        if (vec && n + 4 <= N) {
+          *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+          for (int e = 0; e < 4 && n + e < N; ++e) dst[e] = v[e];
         }
       }
-      __syncthreads();
     }
   }
 }
@@ -583,7 +578,7 @@ void launch_gemm_t(const int8_t* qX, const float* xs, const int8_t* qW, const fl
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGemmLds));
   const int64_t tiles = ceil_div(M, kBM) * ceil_div(N, kBN);
   const dim3 grid(static_cast<unsigned>(ceil_div(tiles, kXcds) * kXcds));
-  i8_gemm_kernel<YDT><<<grid, dim3(256), kGemmLds, s>>>(qX, xs, qW, ws, M, N, K, Y);
+  i8_gemm_kernel<YDT><<<grid, dim3(512), kGemmLds, s>>>(qX, xs, qW, ws, M, N, K, Y);
 }
 
 void launch_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
