@@ -398,6 +398,26 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
+  // The epilogue's scales, fetched now so that their latency hides behind
+  // the main loop: tile (i, j) register r of lane l is row 16 i + l % 16 and
+  // column 16 j + 4 (l / 16) + r of the wavefront's 64 x 64 (the MFMAs take
+  // B as their first operand, so D is the transposed tile).
+  const int64_t mw = m0 + 64 * wm;
+  const int64_t nw = n0 + 64 * wn;
+  float as[4], bs[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = mw + 16 * i + (lane & 15);
+    as[i] = (YDT == QMM_I32) ? 1.0f : ascale[m < M ? m : M - 1];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t n = nw + 16 * j + 4 * (lane >> 4) + r;
+      bs[j][r] = (YDT == QMM_I32) ? 1.0f : bscale[n < N ? n : N - 1];
+    }
+
   issue(0, 0);
   issue(1, 1);
   wait_vm<kLoadsA8 + kLoadsB8>();
@@ -413,7 +433,7 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa0[i], fb0[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
 #pragma unroll
     for (int g = 0; g < 6; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
@@ -431,7 +451,7 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa1[i], fb1[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
@@ -442,31 +462,24 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
   wait_vm<0>();
   __syncthreads();   // the epilogue reuses the LDS
 
-  // Epilogue: tile (i, j), register r: row 16 i + 4 (lane/16) + r of the
-  // wavefront's 64, column 16 j + lane%16 of its 64.
+  // Epilogue: Y = acc * a[m] * b[n], four consecutive columns per lane and
+  // tile, staged through LDS so that global stores are whole 16-byte row
+  // segments.
   int8_t* region = lds + wave * kEpiWave;
-  const int64_t mw = m0 + 64 * wm;
-  const int64_t nw = n0 + 64 * wn;
-  float bs[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = nw + 16 * j + (lane & 15);
-    bs[j] = (YDT == QMM_I32) ? 1.0f : bscale[n < N ? n : N - 1];
-  }
   if constexpr (YDT == QMM_BF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int lr = 16 * i + 4 * (lane >> 4) + r;
-        const int64_t m = mw + lr;
-        const float as = ascale[m < M ? m : M - 1];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float f = static_cast<float>(acc[i][j][r]) * as * bs[j];
-          *reinterpret_cast<uint16_t*>(region + lr * kP2 + (16 * j + (lane & 15)) * 2) =
-              static_cast<uint16_t>(f32_to_bf16_bits(f));
-        }
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 f = {static_cast<float>(acc[i][j][0]) * as[i] * bs[j][0],
+                         static_cast<float>(acc[i][j][1]) * as[i] * bs[j][1],
+                         static_cast<float>(acc[i][j][2]) * as[i] * bs[j][2],
+                         static_cast<float>(acc[i][j][3]) * as[i] * bs[j][3]};
+        // Round to nearest even, two values per conversion.
+        const bf16x2_t lo = __builtin_convertvector(f.xy, bf16x2_t);
+        const bf16x2_t hi = __builtin_convertvector(f.zw, bf16x2_t);
+        const uint2 v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        *reinterpret_cast<uint2*>(region + (16 * i + (lane & 15)) * kP2 + (16 * j + 4 * (lane >> 4)) * 2) = v;
       }
     __syncthreads();
     const bool vec = (N % 8 == 0) && ((reinterpret_cast<uintptr_t>(Y) & 15) == 0);
@@ -488,18 +501,14 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int lr = 16 * i + 4 * (lane >> 4) + r;
-        const int64_t m = mw + lr;
-        float as = 1.0f;
-        if constexpr (YDT == QMM_F32) as = ascale[m < M ? m : M - 1];
+      for (int j = 0; j < 4; ++j) {
+        u32x4 v;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t bits;
-          if constexpr (YDT == QMM_I32) bits = static_cast<uint32_t>(acc[i][j][r]);
-          else bits = __float_as_uint(static_cast<float>(acc[i][j][r]) * as * bs[j]);
-          *reinterpret_cast<uint32_t*>(region + lr * kP4 + (16 * j + (lane & 15)) * 4) = bits;
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (YDT == QMM_I32) v[r] = static_cast<uint32_t>(acc[i][j][r]);
+          else v[r] = __float_as_uint(static_cast<float>(acc[i][j][r]) * as[i] * bs[j][r]);
         }
+        *reinterpret_cast<u32x4*>(region + (16 * i + (lane & 15)) * kP4 + (16 * j + 4 * (lane >> 4)) * 4) = v;
       }
     __syncthreads();
     const bool vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(Y) & 15) == 0);
