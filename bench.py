@@ -227,10 +227,10 @@ def build_ops(dev):
 
     ops.append(dict(name=f"sq_int8_gemm {m4}x{n4}x{k4}", fn=sq_gemm,
                     bytes=m4 * k4 + m4 * 4 + n4 * k4 + n4 * 4 + m4 * n4 * 2,
-                    flops=2 * m4 * n4 * k4, bound="mfma", kernel="i8_gemm_kernel"))
+                    flops=2 * m4 * n4 * k4, bound="mfma", kernel="i8_gemm_kernel", peak=I8_PEAK_TOPS))
     ops.append(dict(name=f"smooth_quant_w8a8_gemm {m4}x{n4}x{k4}", fn=sq_online,
                     bytes=m4 * k4 * 2 + k4 * 4 + (m4 * k4 + m4 * 4) * 2 + n4 * k4 + n4 * 4 + m4 * n4 * 2,
-                    flops=2 * m4 * n4 * k4, bound="mfma", kernel="i8_gemm_kernel + rowquant8_kernel"))
+                    flops=2 * m4 * n4 * k4, bound="mfma", kernel="i8_gemm_kernel + rowquant8_kernel", peak=I8_PEAK_TOPS))
     # Decode GEMVs last, back to back (B=8 then B=1), after the read-mostly
     # GEMMs: in a decode step a GEMV follows other matmuls, not the
     # dequantizer's ~0.9 GB of writes, whose write-back would overlap it.
@@ -373,7 +373,7 @@ def main():
                "hbm_frac": round(op["bytes"] / avg_us / 1e3 / HBM_PEAK_GBPS, 4)}
         if op["flops"]:
             rec["TFLOPs"] = round(op["flops"] / avg_us / 1e6, 2)
-            peak = I8_PEAK_TOPS if "w8a8" in op["name"] else BF16_PEAK_TFLOPS
+            peak = op.get("peak", BF16_PEAK_TFLOPS)
             rec["mfma_frac"] = round(op["flops"] / avg_us / 1e6 / peak, 4)
         rec["bound"] = op["bound"]
         if size > 1:
