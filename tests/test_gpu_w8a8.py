@@ -81,6 +81,29 @@ def test_quantize_activation_long_rows_and_zero_row():
     assert bits_equal(a.cpu().numpy(), ra) and bits_equal(qx.cpu().numpy(), rqx)
 
 
+def test_quantize_activation_extreme_smoothing():
+    # Activations divide by the smoothing factors through a reciprocal table:
+    # factors outside [2^-100, 2^100] must take the exact division, quotients
+    # far below 2^-102 (where the table form may differ in the last place)
+    # must change no code and no scale, and a row under the 1e-8 absmax floor
+    # keeps its floored scale.  fp32 input, so subnormals reach the kernel.
+    k = 512
+    g = np.random.Generator(np.random.PCG64(77))
+    x = g.standard_normal((8, k)).astype(np.float32)
+    sm = (g.random(k) + 0.5).astype(np.float32)
+    sm[3], sm[17], sm[40], sm[41], sm[300] = 1e-33, 3e33, 2.0 ** -100, 2.0 ** 100, 2.0 ** -101
+    x[1] *= np.float32(1e-36)            # quotients around 1e-36 and below
+    x[2] *= np.float32(1e-40)            # subnormal inputs
+    x[3] = np.float32(3e-9) * np.sign(x[3])   # absmax under the floor
+    x[4] *= np.float32(1e4)              # quotients up to ~3e37 in the 1e-33 column
+    x[5, ::3] = np.float32(1.5e-45)      # smallest subnormal among normal values
+    note("sq_quantize_activation 8x512 fp32, extreme smoothing factors")
+    qx, a = qmm.sq_quantize_activation(torch.from_numpy(x).to(DEV), torch.from_numpy(sm).to(DEV))
+    rqx, ra = oracle.sq_quantize_activation(x, sm)
+    assert bits_equal(a.cpu().numpy(), ra), first_diff(a.cpu().numpy(), ra)
+    assert bits_equal(qx.cpu().numpy(), rqx), first_diff(qx.cpu().numpy(), rqx)
+
+
 @pytest.mark.parametrize("mnk", [(1, 1, 64), (5, 7, 128), (130, 129, 320), (128, 128, 64), (300, 257, 1024),
                                  (64, 300, 384), (513, 130, 256), (257, 129, 448)],
                          ids=lambda t: "x".join(map(str, t)))
