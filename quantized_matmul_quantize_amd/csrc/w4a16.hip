@@ -19,10 +19,15 @@
 //    no matrix cores: a lane streams 16 bytes (32 weights) per row per step,
 //    R rows at a time so R x 16 bytes are in flight, with the activation slice
 //    held in registers across those rows.  Used for B == 1 (decode).
-//  * w4_lds_kernel: 2..32 tokens (and larger batches whose 64 x 128 tiles
-//    would not fill the chip) on v_mfma_f32_16x16x32_{bf16,f16}; a block
-//    takes 16 or 32 tokens x 32 or 64 weight rows, its four wavefronts split
-//    K, each with its own LDS rings filled by direct-to-LDS buffer loads.
+//  * w4_rows_kernel: 2..64 tokens in 16-token tiles when the weight rows give
+//    every compute unit a block (64 rows) or most of them two (32 rows) on
+//    v_mfma_f32_16x16x32_{bf16,f16}; the block loads each step's codes 4 rows
+//    x 256 contiguous bytes per instruction, its four wavefronts split K.
+//  * w4_lds_kernel: 2..32 tokens where the rows kernel would leave compute
+//    units idle (and larger batches whose 64 x 128 tiles would not fill the
+//    chip); a block takes 16 or 32 tokens x 32 or 64 weight rows, its four
+//    wavefronts split K, each with its own LDS rings filled by direct-to-LDS
+//    buffer loads.
 //  * w4_tile_kernel: larger batches; 64 x 128 tiles whose activation tile is
 //    shared by the four wavefronts through LDS, one barrier per group.
 //  * w4_mfma_skinny_kernel: bf16 fallback when K is too large for the LDS
