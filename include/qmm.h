@@ -129,9 +129,9 @@ int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  * X : [M, K] QMM_BF16 or QMM_F16.  Y : [M, N] of X's type or QMM_F32.
  * M >= 1, group 128, K <= 2^24, N and M < 2^31 (QMM_ERANGE otherwise).
  * A block keeps the zero points of its weight rows in
- * LDS, which bounds K: K <= 52224 is always served for M > 16 and
- * K <= 384000 for M <= 16; beyond that bf16 runs a slower kernel without the
- * table and fp16 returns QMM_EUNSUPPORTED.
+ * LDS, which bounds K for those kernels: K <= 52224 for M > 16 and
+ * K <= 384000 for M <= 16; beyond that a slower kernel without the table
+ * serves both activation types.
  * ------------------------------------------------------------------------- */
 int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                int group, const void* X, int x_dtype, int64_t M, void* Y, int y_dtype, void* stream);

@@ -30,7 +30,7 @@
 //    buffer loads.
 //  * w4_tile_kernel: larger batches; 64 x 128 tiles whose activation tile is
 //    shared by the four wavefronts through LDS, one barrier per group.
-//  * w4_mfma_skinny_kernel: bf16 fallback when K is too large for the LDS
+//  * w4_mfma_skinny_kernel: fallback when K is too large for the LDS
 //    zero-point table of the kernels above; the weights are the A operand and
 //    never touch LDS.
 
@@ -1265,20 +1265,24 @@ bool launch_lds(const uint8_t* codes, const float* scales, const uint8_t* zeros,
   return launch_lds_m<XDT, YDT, 32>(codes, scales, zeros, N, K, x, M, y, s);
 }
 
-// Tokens >= 2 (or the GEMM): the LDS-tiled kernel, else the skinny kernel
-// (bf16) when its zero-point table does not fit.
-bool launch_mfma(int x_dtype, int y_dtype, const uint8_t* codes, const float* scales, const uint8_t* zeros,
+// Tokens >= 2 (or the GEMM): the LDS-tiled kernels, else the skinny kernel
+// when their zero-point table does not fit in LDS.
+template <int XDT, int YDT>
+void launch_mfma_t(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                   const uint16_t* x, int64_t M, void* y, hipStream_t s) {
+  if (!launch_lds<XDT, YDT>(codes, scales, zeros, N, K, x, M, y, s))
+    launch_skinny_m<XDT, YDT>(M, codes, scales, zeros, N, K, x, y, s);
+}
+
+void launch_mfma(int x_dtype, int y_dtype, const uint8_t* codes, const float* scales, const uint8_t* zeros,
                  int64_t N, int64_t K, const uint16_t* x, int64_t M, void* y, hipStream_t s) {
   if (x_dtype == QMM_BF16) {
-    const bool ok = (y_dtype == QMM_F32) ? launch_lds<QMM_BF16, QMM_F32>(codes, scales, zeros, N, K, x, M, y, s)
-                                         : launch_lds<QMM_BF16, QMM_BF16>(codes, scales, zeros, N, K, x, M, y, s);
-    if (ok) return true;
-    if (y_dtype == QMM_F32) launch_skinny_m<QMM_BF16, QMM_F32>(M, codes, scales, zeros, N, K, x, y, s);
-    else launch_skinny_m<QMM_BF16, QMM_BF16>(M, codes, scales, zeros, N, K, x, y, s);
-    return true;
+    if (y_dtype == QMM_F32) launch_mfma_t<QMM_BF16, QMM_F32>(codes, scales, zeros, N, K, x, M, y, s);
+    else launch_mfma_t<QMM_BF16, QMM_BF16>(codes, scales, zeros, N, K, x, M, y, s);
+  } else {
+    if (y_dtype == QMM_F32) launch_mfma_t<QMM_F16, QMM_F32>(codes, scales, zeros, N, K, x, M, y, s);
+    else launch_mfma_t<QMM_F16, QMM_F16>(codes, scales, zeros, N, K, x, M, y, s);
   }
-  return (y_dtype == QMM_F32) ? launch_lds<QMM_F16, QMM_F32>(codes, scales, zeros, N, K, x, M, y, s)
-                              : launch_lds<QMM_F16, QMM_F16>(codes, scales, zeros, N, K, x, M, y, s);
 }
 
 }  // namespace
@@ -1293,7 +1297,10 @@ extern "C" int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8
   if (B > 8) return QMM_EUNSUPPORTED;
   hipStream_t s = as_stream(stream);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
-  if (B >= 2 && launch_mfma(x_dtype, y_dtype, codes, scales, zeros, N, K, xp, B, y, s)) return launch_status();
+  if (B >= 2) {
+    launch_mfma(x_dtype, y_dtype, codes, scales, zeros, N, K, xp, B, y, s);
+    return launch_status();
+  }
   if (x_dtype == QMM_BF16) {
     if (y_dtype == QMM_F32) launch_valu_b<QMM_BF16, QMM_F32>(B, codes, scales, zeros, N, K, xp, y, s);
     else launch_valu_b<QMM_BF16, QMM_BF16>(B, codes, scales, zeros, N, K, xp, y, s);
@@ -1310,6 +1317,6 @@ extern "C" int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8
   if (st != QMM_OK) return st;
   hipStream_t s = as_stream(stream);
   const uint16_t* xp = static_cast<const uint16_t*>(X);
-  if (!launch_mfma(x_dtype, y_dtype, codes, scales, zeros, N, K, xp, M, Y, s)) return QMM_EUNSUPPORTED;
+  launch_mfma(x_dtype, y_dtype, codes, scales, zeros, N, K, xp, M, Y, s);
   return launch_status();
 }

@@ -131,6 +131,19 @@ def test_gemm_few_tokens_cooperative(n, M):
     gemv_case(q, s, z, x, torch.bfloat16, f"gemm few tokens n={n} M={M} bf16", gemm=True)
 
 
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+@pytest.mark.parametrize("M,k", [(20, 53376), (7, 384128)], ids=["M20-K53376", "M7-K384128"])
+def test_gemm_long_k_fallback(xdt, M, k):
+    # K past what the LDS zero-point table of the tiled kernels holds (52224
+    # for more than 16 tokens, 384000 for up to 16): the table-free kernel
+    # serves both activation types; 37 rows, ragged against its row tiles
+    n = 37
+    q, s, z = random_w4(n, k, seed=k + M)
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(82, k + M), (M, k), 1.0), xdt)
+    gemv_case(q, s, z, x, torch.float32, f"gemm long K {xdt}", gemm=True)
+    gemv_case(q, s, z, x, TDT[xdt], f"gemm long K {xdt} 16-bit", gemm=True)
+
+
 @pytest.mark.parametrize("M", [16, 64, 256])
 def test_gemm_full_size(M):
     wl = workloads.WORKLOADS["gemm"]
