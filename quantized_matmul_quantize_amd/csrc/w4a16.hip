@@ -18,7 +18,7 @@
 //  * gemv_valu_kernel: B <= 8 tokens on the vector ALUs (v_dot2_f32_{bf16,f16}),
 //    no matrix cores: a lane streams 16 bytes (32 weights) per row per step,
 //    R rows at a time so R x 16 bytes are in flight, with the activation slice
-//    held in registers across those rows.  Used for B == 1 (decode).
+//    held in registers across those rows.  Used for B <= 2 (decode).
 //  * w4_rows_kernel: 2..64 tokens in 16-token tiles when the weight rows give
 //    every compute unit a block (64 rows) or most of them two (32 rows) on
 //    v_mfma_f32_16x16x32_{bf16,f16}; the block loads each step's codes 4 rows
@@ -1117,7 +1117,7 @@ int check_common(const uint8_t* codes, const float* scales, const uint8_t* zeros
 template <int XDT, int YDT, int B>
 void launch_valu(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                  const uint16_t* x, void* y, hipStream_t s) {
-  constexpr int R = B == 1 ? 8 : (B <= 4 ? 4 : 2);
+  constexpr int R = 8;   // rows per block: 8 x 16 bytes in flight per lane
   const dim3 grid(static_cast<unsigned>(ceil_div(N, R)));
   gemv_valu_kernel<XDT, YDT, B, R><<<grid, dim3(kValuWaves * kWave), 0, s>>>(codes, scales, zeros, N, K, x, y);
 }
@@ -1125,16 +1125,9 @@ void launch_valu(const uint8_t* codes, const float* scales, const uint8_t* zeros
 template <int XDT, int YDT>
 void launch_valu_b(int64_t B, const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                    const uint16_t* x, void* y, hipStream_t s) {
-  switch (B) {
-    case 1: launch_valu<XDT, YDT, 1>(codes, scales, zeros, N, K, x, y, s); break;
-    case 2: launch_valu<XDT, YDT, 2>(codes, scales, zeros, N, K, x, y, s); break;
-    case 3: launch_valu<XDT, YDT, 3>(codes, scales, zeros, N, K, x, y, s); break;
-    case 4: launch_valu<XDT, YDT, 4>(codes, scales, zeros, N, K, x, y, s); break;
-    case 5: launch_valu<XDT, YDT, 5>(codes, scales, zeros, N, K, x, y, s); break;
-    case 6: launch_valu<XDT, YDT, 6>(codes, scales, zeros, N, K, x, y, s); break;
-    case 7: launch_valu<XDT, YDT, 7>(codes, scales, zeros, N, K, x, y, s); break;
-    default: launch_valu<XDT, YDT, 8>(codes, scales, zeros, N, K, x, y, s); break;
-  }
+  // One or two tokens (more go to the MFMA kernels).
+  if (B == 1) launch_valu<XDT, YDT, 1>(codes, scales, zeros, N, K, x, y, s);
+  else launch_valu<XDT, YDT, 2>(codes, scales, zeros, N, K, x, y, s);
 }
 
 // Wavefronts per block for the skinny MFMA kernel: split K further when the
@@ -1297,7 +1290,10 @@ extern "C" int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8
   if (B > 8) return QMM_EUNSUPPORTED;
   hipStream_t s = as_stream(stream);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
-  if (B >= 2) {
+  // Two tokens still stream the weights fastest on the vector ALUs (measured
+  // 26-28 us against 30-35 us for the MFMA kernels on the 70B-class
+  // matrices); from three on the MFMA kernels win.
+  if (B >= 3) {
     launch_mfma(x_dtype, y_dtype, codes, scales, zeros, N, K, xp, B, y, s);
     return launch_status();
   }

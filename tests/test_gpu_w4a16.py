@@ -81,7 +81,8 @@ def quantized(wl, index):
 
 
 @pytest.mark.parametrize("name,index,B", [("tiny", 0, 1), ("llama7b", 0, 1), ("llama7b", 1, 1),
-                                          ("mlp70b", 0, 1), ("mlp70b", 1, 1), ("mlp70b", 0, 8), ("mlp70b", 1, 8)])
+                                          ("mlp70b", 0, 1), ("mlp70b", 1, 1), ("mlp70b", 0, 2), ("mlp70b", 1, 2),
+                                          ("mlp70b", 0, 8), ("mlp70b", 1, 8)])
 def test_gemv_full_size(name, index, B):
     wl = workloads.WORKLOADS[name]
     q, s, z = quantized(wl, index)
