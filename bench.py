@@ -7,6 +7,7 @@ are resident in HBM before timing starts:
   70B-class MLP, bf16 weights 28672x8192 and 8192x28672 (N(0, 0.015),
   0.1% of entries x10):
     quantize_groupwise on both matrices      (group min/max, s, z, codes, packing)
+    quantize_groupwise_symmetric on the first (symmetric grid, same format)
     dequantize to bf16 on both matrices
   batched W4A16 GEMM, 14336x4096 INT4 G128, X bf16 [M, 4096], M = 16, 64, 256
   SmoothQuant W8A8, X 2048x4096 (6 outlier channels x50..100), W 4096x4096:
@@ -145,6 +146,20 @@ def build_ops(dev):
             assert st == 0, st
         ops.append(dict(name=f"quantize {n}x{k}", fn=quant, bytes=n * k * 2 + wb(n, k), flops=0, bound="hbm",
                         kernel="quantize_g128_lds_kernel"))
+
+    # Symmetric INT4 on the first matrix, into buffers of its own (same
+    # format; not part of quantize_GBps).
+    m0 = mats[0]
+    sym_out = qmm.quantize_groupwise(m0["w"], symmetric=True)
+
+    def quant_sym(i, m=m0):
+        c, s, z = sym_out
+        st = lib.quantize_groupwise_symmetric(qmm._ptr(m["w"]), qmm.BF16, m["n"], m["k"], 128, 4, qmm._ptr(c),
+                                              qmm._ptr(s), qmm._ptr(z), qmm._stream(m["w"]))
+        assert st == 0, st
+    ops.append(dict(name=f"quantize_symmetric {m0['n']}x{m0['k']}", fn=quant_sym,
+                    bytes=m0["n"] * m0["k"] * 2 + wb(m0["n"], m0["k"]), flops=0, bound="hbm",
+                    kernel="quantize_g128_lds_kernel (symmetric)"))
 
     for m in mats:
         n, k = m["n"], m["k"]

@@ -96,6 +96,25 @@ int quantize_groupwise(const void* W, int w_dtype, int64_t N, int64_t K, int gro
                        uint8_t* codes, float* scales, uint8_t* zeros, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * quantize_groupwise_symmetric -- symmetric per-group quantization of W into
+ * the same INT4 format, so dequantize, w4a16_gemv and w4a16_gemm consume it
+ * unchanged.  For every row n and group g:
+ *   s    = max(max_k |W|, 1e-8) / (2^(bits-1) - 1)
+ *   q    = clamp(round(W / s), -2^(bits-1), 2^(bits-1) - 1)
+ *   code = q + 2^(bits-1), stored zero-point 2^(bits-1)   ((code - z) s = q s)
+ * in IEEE fp32 with correctly rounded division and round-half-to-even.
+ * Sources: "How quantization works" ("The math of quantization", symmetric
+ * form); "Quantization from Scratch" ("Scale and zero-point": the symmetric
+ * grid, 15 of the 16 levels at 4 bits, the 16th an extra negative level).
+ * The 1e-8 floor of an all-zero group's absmax is the one the INT8 path uses
+ * ("How quantization works", fake-quantization listing).
+ * Arguments, layouts and errors as quantize_groupwise; every stored
+ * zero-point nibble is 8.
+ * ------------------------------------------------------------------------- */
+int quantize_groupwise_symmetric(const void* W, int w_dtype, int64_t N, int64_t K, int group, int bits,
+                                 uint8_t* codes, float* scales, uint8_t* zeros, void* stream);
+
+/* ---------------------------------------------------------------------------
  * dequantize -- W_hat = (q - z) * s, one fp32 rounding, then rounded to
  * out_dtype (QMM_F32, QMM_BF16 or QMM_F16; round to nearest even).
  * Sources: "Quantization from Scratch" ("Scale and zero-point"); "Quantization

@@ -141,6 +141,17 @@ def quantize_groupwise_packed(w, group: int = 128):
     return pack_codes(q), s, pack_nibbles(z)
 
 
+def sym_quantize_int4_packed(w, group: int = 128):
+    """Symmetric INT4 per group ("How quantization works", "The math of
+    quantization"; absmax floored at 1e-8 as in the INT8 path), stored in the
+    same format as quantize_groupwise_packed: code q + 8 and zero-point 8.
+    Returns (codes [N, K/2] u8, scales [N, G] f32, zeros [N, ceil(G/2)] u8,
+    q int8 [N, K])."""
+    q, s = sym_quantize(w, group, 4, 1e-8)
+    z = np.full(s.shape, 8, np.uint8)
+    return pack_codes((q.astype(np.int16) + 8).astype(np.uint8)), s, pack_nibbles(z), q
+
+
 # --------------------------------------------------------------------------
 # Symmetric quantization ("How quantization works", "The math of
 # quantization" and the fake-quantization listing's 1e-8 absmax floor).

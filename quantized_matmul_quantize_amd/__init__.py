@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "QmmError", "lib", "library_path", "F32", "F16", "BF16", "I32", "GROUP",
-    "w4_sizes", "quantize_groupwise", "dequantize", "w4a16_gemv", "w4a16_gemm",
+    "w4_sizes", "quantize_groupwise", "quantize_groupwise_symmetric", "dequantize", "w4a16_gemv", "w4a16_gemm",
     "sq_smooth_factors", "sq_quantize_weight", "sq_quantize_activation", "sq_int8_gemm",
     "sq_workspace_bytes", "smooth_quant_w8a8_gemm",
 ]
@@ -46,6 +46,7 @@ _SIGS = {
     "qmm_version": ([], _I),
     "qmm_w4_sizes": ([_I64, _I64, _I, _P, _P, _P], _I),
     "quantize_groupwise": ([_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _P], _I),
+    "quantize_groupwise_symmetric": ([_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _P], _I),
     "dequantize": ([_P, _P, _P, _I64, _I64, _I, _I, _P, _I, _P], _I),
     "w4a16_gemv": ([_P, _P, _P, _I64, _I64, _I, _P, _I, _I64, _P, _I, _P], _I),
     "w4a16_gemm": ([_P, _P, _P, _I64, _I64, _I, _P, _I, _I64, _P, _I, _P], _I),
@@ -108,16 +109,17 @@ def w4_sizes(N: int, K: int, group: int = GROUP) -> Tuple[int, int, int]:
     return c.value, s.value, z.value
 
 
-def quantize_groupwise(W: torch.Tensor, group: int = GROUP, bits: int = 4):
-    """W [N, K] (fp32 / bf16 / fp16) -> codes u8 [N, K/2], scales f32 [N, G], zeros u8 [N, ceil(G/2)]."""
+def quantize_groupwise(W: torch.Tensor, group: int = GROUP, bits: int = 4, symmetric: bool = False):
+    """W [N, K] (fp32 / bf16 / fp16) -> codes u8 [N, K/2], scales f32 [N, G], zeros u8 [N, ceil(G/2)].
+    symmetric=True: the symmetric grid, stored with zero-point 8 in the same format."""
     _check(W, "W")
     N, K = W.shape
     G = K // group if group > 0 else 0
     codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
     scales = torch.empty((N, max(G, 1)), dtype=torch.float32, device=W.device)
     zeros = torch.empty((N, max((G + 1) // 2, 1)), dtype=torch.uint8, device=W.device)
-    _call("quantize_groupwise", _ptr(W), _dt(W.dtype), N, K, group, bits, _ptr(codes), _ptr(scales), _ptr(zeros),
-          _stream(W))
+    _call("quantize_groupwise_symmetric" if symmetric else "quantize_groupwise", _ptr(W), _dt(W.dtype), N, K, group,
+          bits, _ptr(codes), _ptr(scales), _ptr(zeros), _stream(W))
     return codes, scales, zeros
 
 

@@ -20,6 +20,9 @@ namespace qmm {
 namespace {
 
 constexpr float kLevels = 15.0f;                 // 2^4 - 1
+constexpr float kSymLevels = 7.0f;               // 2^(4-1) - 1
+constexpr float kSymFloor = 1e-8f;               // absmax floor of the symmetric grid
+constexpr float kSymZero = 8.0f;                 // stored zero-point of symmetric codes
 
 // Codes of 8 elements of a group with scale s, y = RN(1/s) (one correctly
 // rounded division per group, by the caller) and zero-point zf (an
@@ -58,6 +61,27 @@ __device__ __forceinline__ uint32_t quantize8(const float v[8], float s, float y
   return word;
 }
 
+// Scale and zero-point of a group from its range, lo = min(min w, 0) and
+// hi = max(max w, 0).  Asymmetric ("Quantization from Scratch", "Scale and
+// zero-point"; "How quantization works", "The math of quantization"):
+// s = fl32((hi - lo) / 15), 1 for an all-zero group, z = rint(fl32(-lo / s)).
+// Symmetric (the same sections' symmetric grid): s = fl32(max|w| / 7) with
+// max|w| floored at 1e-8, q = clamp(rint(fl32(w / s)), -8, 7), stored as the
+// code q + 8 with the zero-point 8, so the dequantizer and the matmuls read
+// it unchanged ((code - 8) s = q s).
+template <bool SYM>
+__device__ __forceinline__ void group_params(float lo, float hi, float* s, float* zf) {
+  if constexpr (SYM) {
+    *s = fmaxf(fmaxf(hi, -lo), kSymFloor) / kSymLevels;   // correctly rounded fp32 division
+    *zf = kSymZero;
+  } else {
+    float sc = (hi - lo) / kLevels;                         // correctly rounded fp32 division
+    if (sc == 0.0f) sc = 1.0f;
+    *s = sc;
+    *zf = rintf(-lo / sc);                                  // in [0, 15] because lo <= 0 <= hi
+  }
+}
+
 // Flat variant for an even number of groups per row: the matrix is then one
 // array of N*G groups whose codes, scales and zero-point bytes are all
 // consecutive, so a wavefront takes 16 consecutive groups: 4 lanes per group,
@@ -65,7 +89,7 @@ __device__ __forceinline__ uint32_t quantize8(const float v[8], float s, float y
 // 16-byte code store per lane.  Four lanes share a group's min/max (two DPP
 // steps) and its s and z, so the per-group division costs are spread over 32
 // elements per lane instead of 8.
-template <int DT>
+template <int DT, bool SYM>
 __global__ __launch_bounds__(256) void quantize_g128_flat_kernel(const uint8_t* __restrict__ w, int64_t total_groups,
                                                                  uint8_t* __restrict__ codes,
                                                                  float* __restrict__ scales,
@@ -95,9 +119,8 @@ __global__ __launch_bounds__(256) void quantize_g128_flat_kernel(const uint8_t* 
     hi = fmaxf(hi, dpp_f<kDppXor1>(hi));
     lo = fminf(lo, dpp_f<kDppXor2>(lo));
     hi = fmaxf(hi, dpp_f<kDppXor2>(hi));
-    float s = (hi - lo) / kLevels;      // correctly rounded fp32 division
-    if (s == 0.0f) s = 1.0f;
-    const float zf = rintf(-lo / s);
+    float s, zf;
+    group_params<SYM>(lo, hi, &s, &zf);
     const float y = 1.0f / s;           // correctly rounded reciprocal
     uint32_t out[4];
 #pragma unroll
@@ -128,7 +151,7 @@ __global__ __launch_bounds__(256) void quantize_g128_flat_kernel(const uint8_t* 
 // the four reads of each lane are free of bank conflicts.
 constexpr int kQChunkBytes = 16 * kGroup * 2;   // 4 KiB of 16-bit weights
 
-template <int DT>
+template <int DT, bool SYM>
 __global__ __launch_bounds__(256) void quantize_g128_lds_kernel(const uint8_t* __restrict__ w, int64_t total_groups,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales,
@@ -204,9 +227,8 @@ __global__ __launch_bounds__(256) void quantize_g128_lds_kernel(const uint8_t* _
     hi = fmaxf(hi, dpp_f<kDppXor1>(hi));
     lo = fminf(lo, dpp_f<kDppXor2>(lo));
     hi = fmaxf(hi, dpp_f<kDppXor2>(hi));
-    float sc = (hi - lo) / kLevels;      // correctly rounded fp32 division
-    if (sc == 0.0f) sc = 1.0f;
-    const float zf = rintf(-lo / sc);
+    float sc, zf;
+    group_params<SYM>(lo, hi, &sc, &zf);
     const float y = 1.0f / sc;          // correctly rounded reciprocal
     uint32_t out[4];
 #pragma unroll
@@ -225,7 +247,7 @@ __global__ __launch_bounds__(256) void quantize_g128_lds_kernel(const uint8_t* _
   }
 }
 
-template <int DT>
+template <int DT, bool SYM>
 __global__ __launch_bounds__(256) void quantize_g128_kernel(const uint8_t* __restrict__ w, int64_t K, int64_t G,
                                                             int64_t chunks_per_row, int64_t total_chunks,
                                                             uint32_t* __restrict__ codes,
@@ -257,9 +279,8 @@ __global__ __launch_bounds__(256) void quantize_g128_kernel(const uint8_t* __res
     lo = row16_min(lo);
     hi = row16_max(hi);
 
-    float s = (hi - lo) / kLevels;      // correctly rounded fp32 division
-    if (s == 0.0f) s = 1.0f;
-    const float zf = rintf(-lo / s);    // in [0, 15] because lo <= 0 <= hi
+    float s, zf;
+    group_params<SYM>(lo, hi, &s, &zf);
     const float y = 1.0f / s;           // correctly rounded reciprocal
 
     const uint32_t word = quantize8(v, s, y, zf);
@@ -339,8 +360,12 @@ int check_w4_args(const void* codes, const float* scales, const uint8_t* zeros, 
 
 using namespace qmm;
 
-extern "C" int quantize_groupwise(const void* W, int w_dtype, int64_t N, int64_t K, int group, int bits,
-                                  uint8_t* codes, float* scales, uint8_t* zeros, void* stream) {
+namespace qmm {
+namespace {
+
+template <bool SYM>
+int quantize_launch(const void* W, int w_dtype, int64_t N, int64_t K, int group, int bits, uint8_t* codes,
+                    float* scales, uint8_t* zeros, void* stream) {
   if (!W) return QMM_EINVAL;
   if (w_dtype != QMM_F32 && w_dtype != QMM_BF16 && w_dtype != QMM_F16)
     return w_dtype == QMM_I32 ? QMM_EUNSUPPORTED : QMM_EINVAL;
@@ -360,9 +385,9 @@ extern "C" int quantize_groupwise(const void* W, int w_dtype, int64_t N, int64_t
     if (blocks > cap) blocks = cap;
     const dim3 grid(static_cast<unsigned>(blocks));
     switch (w_dtype) {
-      case QMM_BF16: quantize_g128_lds_kernel<QMM_BF16><<<grid, block, 0, s>>>(w, T, codes, scales, zeros); break;
-      case QMM_F16: quantize_g128_lds_kernel<QMM_F16><<<grid, block, 0, s>>>(w, T, codes, scales, zeros); break;
-      default: quantize_g128_flat_kernel<QMM_F32><<<grid, block, 0, s>>>(w, T, codes, scales, zeros); break;
+      case QMM_BF16: quantize_g128_lds_kernel<QMM_BF16, SYM><<<grid, block, 0, s>>>(w, T, codes, scales, zeros); break;
+      case QMM_F16: quantize_g128_lds_kernel<QMM_F16, SYM><<<grid, block, 0, s>>>(w, T, codes, scales, zeros); break;
+      default: quantize_g128_flat_kernel<QMM_F32, SYM><<<grid, block, 0, s>>>(w, T, codes, scales, zeros); break;
     }
     return launch_status();
   }
@@ -373,16 +398,29 @@ extern "C" int quantize_groupwise(const void* W, int w_dtype, int64_t N, int64_t
   uint32_t* cw = reinterpret_cast<uint32_t*>(codes);
   switch (w_dtype) {
     case QMM_BF16:
-      quantize_g128_kernel<QMM_BF16><<<grid, block, 0, s>>>(w, K, G, chunks_per_row, total, cw, scales, zeros, zrow);
+      quantize_g128_kernel<QMM_BF16, SYM><<<grid, block, 0, s>>>(w, K, G, chunks_per_row, total, cw, scales, zeros, zrow);
       break;
     case QMM_F16:
-      quantize_g128_kernel<QMM_F16><<<grid, block, 0, s>>>(w, K, G, chunks_per_row, total, cw, scales, zeros, zrow);
+      quantize_g128_kernel<QMM_F16, SYM><<<grid, block, 0, s>>>(w, K, G, chunks_per_row, total, cw, scales, zeros, zrow);
       break;
     default:
-      quantize_g128_kernel<QMM_F32><<<grid, block, 0, s>>>(w, K, G, chunks_per_row, total, cw, scales, zeros, zrow);
+      quantize_g128_kernel<QMM_F32, SYM><<<grid, block, 0, s>>>(w, K, G, chunks_per_row, total, cw, scales, zeros, zrow);
       break;
   }
   return launch_status();
+}
+
+}  // namespace
+}  // namespace qmm
+
+extern "C" int quantize_groupwise(const void* W, int w_dtype, int64_t N, int64_t K, int group, int bits,
+                                  uint8_t* codes, float* scales, uint8_t* zeros, void* stream) {
+  return quantize_launch<false>(W, w_dtype, N, K, group, bits, codes, scales, zeros, stream);
+}
+
+extern "C" int quantize_groupwise_symmetric(const void* W, int w_dtype, int64_t N, int64_t K, int group, int bits,
+                                            uint8_t* codes, float* scales, uint8_t* zeros, void* stream) {
+  return quantize_launch<true>(W, w_dtype, N, K, group, bits, codes, scales, zeros, stream);
 }
 
 extern "C" int dequantize(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,

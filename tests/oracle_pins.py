@@ -359,7 +359,47 @@ def check_sym_zero_row_floor():
     assert (oracle.sym_dequantize(q, s, 64)[0] == 0).all()
 
 
+def check_sym_int4_stored_groups():
+    # Symmetric INT4 per group of 128 in the stored format: the scale is the
+    # closed form fl32(max(max|w|, 1e-8) / 7), every code is q + 8 with q in
+    # [-7, 7] (|w/s| <= 7, so nothing is clipped and the extra level -8 is
+    # unused), the group's largest magnitude maps to +-7, zero maps to code 8
+    # and back to exactly 0, the error is at most half a step, each code is
+    # the nearest of the 16 grid points, and every zero-point nibble is 8.
+    w = _random_groups(n_groups=600)
+    w[5] = 0.0                                          # an all-zero group
+    codes, s, zeros, q = oracle.sym_quantize_int4_packed(w.reshape(300, 256), 128)
+    codes, s, zeros, q = codes.reshape(600, 64), s.reshape(600, 1), zeros, q.reshape(600, 128)
+    amax = np.abs(w).max(axis=1)
+    expect = np.maximum(amax, np.float32(1e-8)).astype(np.float32) / np.float32(7)
+    assert np.array_equal(s[:, 0], expect)
+    assert q.min() >= -7 and q.max() <= 7
+    big = np.abs(w).argmax(axis=1)
+    rows = np.nonzero(amax > 0)[0]
+    assert (np.abs(q[rows, big[rows]]) == 7).all()
+    assert (q[w == 0.0] == 0).all() and (q[5] == 0).all()
+    # storage: low/high nibbles of the code words hold q + 8 (layout as the
+    # asymmetric codes), zero-points all 8
+    unpacked = np.empty(q.shape, np.int16)
+    words = codes.view(np.uint32)
+    for i in range(8):
+        nib = (i >> 1) + ((i & 1) << 2)
+        unpacked[:, i::8] = (words >> np.uint32(4 * nib)) & np.uint32(15)
+    assert np.array_equal(unpacked, q.astype(np.int16) + 8)
+    assert zeros.shape == (300, 1) and (zeros == 0x88).all()
+    # an odd group count leaves the last byte's high nibble as padding (0)
+    assert (oracle.sym_quantize_int4_packed(w[:4].reshape(4, 128), 128)[2] == 0x08).all()
+    back = (q.astype(np.float64)) * s.astype(np.float64)
+    err = np.abs(back - w.astype(np.float64))
+    assert (err <= s.astype(np.float64) / 2 * (1 + 1e-6) + 1e-12).all()
+    grid = np.arange(-8, 8, dtype=np.float64)[None, None, :] * s.astype(np.float64)[:, :, None]
+    d = np.abs(w.astype(np.float64)[:, :, None] - grid)
+    chosen = np.take_along_axis(d, (q.astype(np.int64) + 8)[:, :, None], axis=2)[:, :, 0]
+    assert (chosen <= d.min(axis=2) + 8 * np.spacing(np.float32(1.0)) * s.astype(np.float64)).all()
+
+
 ALL_CHECKS = [
+    check_sym_int4_stored_groups,
     check_six_weights, check_eight_weights, check_int8_outlier, check_int4_symmetric_exercise,
     check_int4_outlier_slide, check_round_half_even, check_degenerate_groups, check_error_bound_and_zero,
     check_nearest_grid_point, check_granularity_special_cases, check_packing, check_code_words, check_storage_70b,

@@ -142,3 +142,67 @@ def test_roundtrip_error_bound():
     err = (back - wd.float()).abs().reshape(w.shape[0], -1, 128)
     bound = scales.unsqueeze(-1) / 2 * (1 + 1e-5) + 1e-7
     assert bool((err <= bound).all())
+
+
+# --------------------------------------------------------------------------
+# Symmetric INT4 ("How quantization works", "The math of quantization"),
+# stored in the same format with zero-point 8.
+# --------------------------------------------------------------------------
+def run_and_compare_sym(w_cpu: torch.Tensor, what: str):
+    note(f"quantize_groupwise_symmetric {what} shape={tuple(w_cpu.shape)} dtype={w_cpu.dtype}")
+    codes, scales, zeros = qmm.quantize_groupwise(w_cpu.to(DEV), symmetric=True)
+    torch.cuda.synchronize()
+    rc, rs, rz, _ = oracle.sym_quantize_int4_packed(w_cpu.float().numpy())
+    c, s, z = codes.cpu().numpy(), scales.cpu().numpy(), zeros.cpu().numpy()
+    assert bits_equal(s, rs), f"{what} scales: {first_diff(s, rs)}"
+    assert bits_equal(z, rz), f"{what} zeros: {first_diff(z, rz)}"
+    assert bits_equal(c, rc), f"{what} codes: {first_diff(c, rc)}"
+    return codes, scales, zeros
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", workloads.shapes_for_parity(), ids=lambda s: f"{s[0]}x{s[1]}")
+def test_quantize_symmetric_small(dtype, shape):
+    g = workloads.rng(98, shape[0] * 7 + shape[1])
+    w = workloads.gaussian(g, shape, 0.02)
+    workloads.plant_scale_entries(w, g, 0.01, 10.0)
+    run_and_compare_sym(workloads.to_dtype(w, dtype), f"sym small-{dtype}")
+
+
+def test_quantize_symmetric_edge_cases():
+    # the worked examples, all-zero / one-signed / constant groups and exact
+    # half-step ties, in fp32 (odd and even group counts follow from K = 1024
+    # and the 3-group slice)
+    rows = _edge_rows()
+    w = torch.from_numpy(rows)
+    run_and_compare_sym(w, "sym edge f32")
+    run_and_compare_sym(w[:, :384].contiguous(), "sym edge f32, 3 groups")
+    rows[4] = np.clip(rows[4], -3e38, 3e38)
+    run_and_compare_sym(workloads.to_dtype(rows, "bf16"), "sym edge bf16")
+
+
+@pytest.mark.parametrize("name,index", [("llama7b", 1), ("mlp70b", 0)])
+def test_quantize_symmetric_full_size(name, index):
+    wl = workloads.WORKLOADS[name]
+    w, _ = workloads.weight(wl, index)
+    run_and_compare_sym(w, f"sym {name}[{index}]")
+
+
+def test_symmetric_codes_feed_the_matmuls():
+    # the stored symmetric format goes through dequantize, the GEMV (B = 1, 2)
+    # and the GEMM unchanged: compare with the oracle on (q + 8, s, 8)
+    g = workloads.rng(97, 3)
+    n, k = 300, 1152
+    w = workloads.to_dtype(workloads.gaussian(g, (n, k), 0.02), "bf16")
+    codes, scales, zeros = run_and_compare_sym(w, "sym for matmuls")
+    _, rs, _, q = oracle.sym_quantize_int4_packed(w.float().numpy())
+    qu = (q.astype(np.int16) + 8).astype(np.uint8)
+    zu = np.full(rs.shape, 8, np.uint8)
+    back = qmm.dequantize(codes, scales, zeros, torch.float32).cpu().numpy()
+    assert bits_equal(back, oracle.asym_dequantize(qu, rs, zu, 128)), "sym dequantize"
+    from gpu_util import assert_close
+    for B, fn in ((1, qmm.w4a16_gemv), (2, qmm.w4a16_gemv), (33, qmm.w4a16_gemm)):
+        x = workloads.to_dtype(workloads.gaussian(workloads.rng(96, B), (B, k), 1.0), "bf16")
+        note(f"w4a16 on symmetric codes B={B}")
+        y = fn(codes, scales, zeros, x.to(DEV), out_dtype=torch.float32).cpu()
+        assert_close(y, oracle.w4a16_reference(x.float().numpy(), qu, rs, zu), f"sym codes B={B}")
