@@ -11,7 +11,8 @@ are resident in HBM before timing starts:
     dequantize to bf16 on both matrices
   batched W4A16 GEMM, 14336x4096 INT4 G128, X bf16 [M, 4096], M = 16, 64, 256
   SmoothQuant W8A8, X 2048x4096 (6 outlier channels x50..100), W 4096x4096:
-    sq_smooth_factors, sq_quantize_weight, sq_int8_gemm alone (i8-MFMA GEMM
+    sq_smooth_factors, sq_quantize_weight, per-tensor activation quantization
+    (the W8A8 baseline: X read twice), sq_int8_gemm alone (i8-MFMA GEMM
     and rescale to bf16 on activations quantized before timing), and
     smooth_quant_w8a8_gemm (per-token smoothing + INT8 quantization, then the
     same GEMM): config.int8_gemm_TOPS is the GEMM alone, w8a8_online_TOPS the
@@ -240,6 +241,17 @@ def build_ops(dev):
                               qmm.BF16, qmm._stream(x4))
         assert st == 0, st
 
+    qx4t = torch.empty((m4, k4), dtype=torch.int8, device=dev)
+    xsc4t = torch.empty(m4, dtype=torch.float32, device=dev)
+
+    def sq_act_tensor(i):
+        st = lib.sq_quantize_activation_per_tensor(qmm._ptr(x4), qmm.BF16, qmm._ptr(smooth), m4, k4, qmm._ptr(qx4t),
+                                                   qmm._ptr(xsc4t), qmm._stream(x4))
+        assert st == 0, st
+
+    ops.append(dict(name=f"sq_quantize_activation_per_tensor {m4}x{k4}", fn=sq_act_tensor,
+                    bytes=2 * m4 * k4 * 2 + k4 * 4 + m4 * k4 + m4 * 4, flops=0, bound="hbm",
+                    kernel="rowquant8_kernel x2 + tensor_scale_kernel"))
     ops.append(dict(name=f"sq_int8_gemm {m4}x{n4}x{k4}", fn=sq_gemm,
                     bytes=m4 * k4 + m4 * 4 + n4 * k4 + n4 * 4 + m4 * n4 * 2,
                     flops=2 * m4 * n4 * k4, bound="mfma", kernel="i8_gemm_kernel", peak=I8_PEAK_TOPS))

@@ -186,6 +186,17 @@ int sq_quantize_weight(const void* W, int w_dtype, const float* smooth, int64_t 
 int sq_quantize_activation(const void* X, int x_dtype, const float* smooth, int64_t M, int64_t K,
                            int8_t* qX, float* x_scale, void* stream);
 
+/* Per-tensor activation quantization, the W8A8 baseline that the per-token
+ * form improves on ("How quantization works", "Activation quantization and
+ * outliers": one scale for the whole activation matrix, set by its largest
+ * entry).  Xs = X / smooth[k] (fp32), a = max(max_{m,k} |Xs|, 1e-8) / 127,
+ * qX = clamp(round(Xs / a), -128, 127); a is written to every x_scale[m], so
+ * sq_int8_gemm consumes the result unchanged.  Three launches on the stream
+ * (row maxima into x_scale, the tensor scale, quantization); X is read
+ * twice.  Arguments and errors as sq_quantize_activation. */
+int sq_quantize_activation_per_tensor(const void* X, int x_dtype, const float* smooth, int64_t M, int64_t K,
+                                      int8_t* qX, float* x_scale, void* stream);
+
 /* INT8 GEMM: acc[m,n] = sum_k qX[m,k] qW[n,k] exactly in int32 (i8 MFMA), then
  * Y = acc * x_scale[m] * w_scale[n] rounded to y_dtype (QMM_BF16 or QMM_F32), or
  * the raw int32 acc when y_dtype is QMM_I32 (x_scale / w_scale ignored, may be NULL).

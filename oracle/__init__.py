@@ -272,6 +272,15 @@ def sq_quantize_activation(x, s) -> Tuple[np.ndarray, np.ndarray]:
     return q, a.reshape(-1)
 
 
+def sq_quantize_activation_per_tensor(x, s) -> Tuple[np.ndarray, np.ndarray]:
+    """Xs = X / s (columns); one symmetric INT8 scale for the whole tensor
+    ("How quantization works", "Activation quantization and outliers", per-tensor
+    form) -> (qX int8 [M,K], a f32 [M], every entry the tensor's scale)."""
+    xs = scale_columns_div(x, s) if s is not None else _f32(x)
+    q, a = sym_quantize(xs.reshape(1, -1), xs.size, 8, 1e-8)
+    return q.reshape(xs.shape), np.full(xs.shape[0], a.reshape(-1)[0], np.float32)
+
+
 def sq_w8a8_reference(x, s, qw, b):
     """Online W8A8 step: quantize X per token, exact int32 product, rescale.
     Returns (qX, a, acc int32, y fp64)."""

@@ -18,7 +18,8 @@ import torch
 __all__ = [
     "QmmError", "lib", "library_path", "F32", "F16", "BF16", "I32", "GROUP",
     "w4_sizes", "quantize_groupwise", "quantize_groupwise_symmetric", "dequantize", "w4a16_gemv", "w4a16_gemm",
-    "sq_smooth_factors", "sq_quantize_weight", "sq_quantize_activation", "sq_int8_gemm",
+    "sq_smooth_factors", "sq_quantize_weight", "sq_quantize_activation", "sq_quantize_activation_per_tensor",
+    "sq_int8_gemm",
     "sq_workspace_bytes", "smooth_quant_w8a8_gemm",
 ]
 
@@ -53,6 +54,7 @@ _SIGS = {
     "sq_smooth_factors": ([_P, _I, _I64, _P, _I, _I64, _I64, _F, _P, _P, _P, _P], _I),
     "sq_quantize_weight": ([_P, _I, _P, _I64, _I64, _P, _P, _P], _I),
     "sq_quantize_activation": ([_P, _I, _P, _I64, _I64, _P, _P, _P], _I),
+    "sq_quantize_activation_per_tensor": ([_P, _I, _P, _I64, _I64, _P, _P, _P], _I),
     "sq_int8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "sq_workspace_bytes": ([_I64, _I64], _SZ),
     "smooth_quant_w8a8_gemm": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
@@ -186,13 +188,14 @@ def sq_quantize_weight(W: torch.Tensor, smooth: Optional[torch.Tensor] = None):
     return q, s
 
 
-def sq_quantize_activation(X: torch.Tensor, smooth: Optional[torch.Tensor] = None):
-    """-> (qX int8 [M, K], x_scale f32 [M])."""
+def sq_quantize_activation(X: torch.Tensor, smooth: Optional[torch.Tensor] = None, per_tensor: bool = False):
+    """-> (qX int8 [M, K], x_scale f32 [M]); per_tensor=True: one scale for the whole X, repeated per row."""
     _check(X, "X")
     M, K = X.shape
     q = torch.empty((M, K), dtype=torch.int8, device=X.device)
     s = torch.empty(M, dtype=torch.float32, device=X.device)
-    _call("sq_quantize_activation", _ptr(X), _dt(X.dtype), _ptr(smooth), M, K, _ptr(q), _ptr(s), _stream(X))
+    _call("sq_quantize_activation_per_tensor" if per_tensor else "sq_quantize_activation", _ptr(X), _dt(X.dtype),
+          _ptr(smooth), M, K, _ptr(q), _ptr(s), _stream(X))
     return q, s
 
 

@@ -197,7 +197,11 @@ __device__ __forceinline__ void rq_load_batch(const uint8_t* arow, const float* 
   }
 }
 
-template <int DT, int MODE, bool SM>
+// PHASE 0: one pass per row (per-row scale).  For one scale over the whole
+// tensor: PHASE 1 writes each row's absmax to scale[row]; tensor_scale_kernel
+// turns them into the tensor's scale, stored for every row; PHASE 2 then
+// quantizes each row with scale[row].
+template <int DT, int MODE, bool SM, int PHASE>
 __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restrict__ a, const float* __restrict__ smooth,
                                                         int64_t rows, int64_t K, int8_t* __restrict__ q,
                                                         float* __restrict__ scale) {
@@ -209,21 +213,30 @@ __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restric
   const bool resident = K <= kRqBatch;
 
   float v[kRqChunks][8];
-  float amax = 0.0f;
-  for (int64_t base = 0; base < K; base += kRqBatch) {
-    rq_load_batch<DT, MODE, SM>(arow, smooth, K, base, lane, v);
+  float s;
+  if constexpr (PHASE == 2) {
+    s = scale[row];
+  } else {
+    float amax = 0.0f;
+    for (int64_t base = 0; base < K; base += kRqBatch) {
+      rq_load_batch<DT, MODE, SM>(arow, smooth, K, base, lane, v);
 #pragma unroll
-    for (int c = 0; c < kRqChunks; ++c)
+      for (int c = 0; c < kRqChunks; ++c)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+    }
+    amax = wave_max(amax);
+    if constexpr (PHASE == 1) {
+      if (lane == 0) scale[row] = amax;
+      return;
+    }
+    s = fmaxf(amax, kAbsFloor) / kQ8;
+    if (lane == 0) scale[row] = s;
   }
-  amax = wave_max(amax);
-  const float s = fmaxf(amax, kAbsFloor) / kQ8;
-  if (lane == 0) scale[row] = s;
   const float r = 1.0f / s;   // correctly rounded reciprocal
 
   for (int64_t base = 0; base < K; base += kRqBatch) {
-    if (!resident) rq_load_batch<DT, MODE, SM>(arow, smooth, K, base, lane, v);
+    if (PHASE == 2 || !resident) rq_load_batch<DT, MODE, SM>(arow, smooth, K, base, lane, v);
 #pragma unroll
     for (int c = 0; c < kRqChunks; ++c) {
       const int64_t k = base + static_cast<int64_t>(c) * (kWave * 8) + lane * 8;
@@ -234,6 +247,22 @@ __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restric
       }
     }
   }
+}
+
+// The tensor's scale from the rows' absmax values in scale[0..rows): a =
+// fl32(max(max_m absmax_m, 1e-8) / 127), then written to every scale[m].  One
+// block; the maximum is exact, so the order of the reduction does not matter.
+__global__ __launch_bounds__(256) void tensor_scale_kernel(float* __restrict__ scale, int64_t rows) {
+  __shared__ float part[256 / kWave];
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < rows; i += blockDim.x) m = fmaxf(m, scale[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = m;
+  __syncthreads();
+  float a = part[0];
+  for (int w = 1; w < static_cast<int>(blockDim.x / kWave); ++w) a = fmaxf(a, part[w]);
+  a = fmaxf(a, kAbsFloor) / kQ8;
+  for (int64_t i = threadIdx.x; i < rows; i += blockDim.x) scale[i] = a;
 }
 
 // ----------------------------------------------------------------------------
@@ -532,7 +561,7 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 
 bool float_dtype(int dt) { return dt == QMM_F32 || dt == QMM_BF16 || dt == QMM_F16; }
 
-template <int MODE>
+template <int MODE, int PHASE = 0>
 int launch_rowquant(const void* a, int dt, const float* smooth, int64_t rows, int64_t K, int8_t* q, float* scale,
                     hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(ceil_div(rows, 4)));
@@ -540,15 +569,15 @@ int launch_rowquant(const void* a, int dt, const float* smooth, int64_t rows, in
   const uint8_t* p = static_cast<const uint8_t*>(a);
   if (smooth) {
     switch (dt) {
-      case QMM_BF16: rowquant8_kernel<QMM_BF16, MODE, true><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
-      case QMM_F16: rowquant8_kernel<QMM_F16, MODE, true><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
-      default: rowquant8_kernel<QMM_F32, MODE, true><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      case QMM_BF16: rowquant8_kernel<QMM_BF16, MODE, true, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      case QMM_F16: rowquant8_kernel<QMM_F16, MODE, true, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      default: rowquant8_kernel<QMM_F32, MODE, true, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
     }
   } else {
     switch (dt) {
-      case QMM_BF16: rowquant8_kernel<QMM_BF16, MODE, false><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
-      case QMM_F16: rowquant8_kernel<QMM_F16, MODE, false><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
-      default: rowquant8_kernel<QMM_F32, MODE, false><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      case QMM_BF16: rowquant8_kernel<QMM_BF16, MODE, false, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      case QMM_F16: rowquant8_kernel<QMM_F16, MODE, false, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      default: rowquant8_kernel<QMM_F32, MODE, false, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
     }
   }
   return launch_status();
@@ -651,6 +680,19 @@ extern "C" int sq_quantize_activation(const void* X, int x_dtype, const float* s
   int st = check_rowquant(X, x_dtype, smooth, M, K, qX, x_scale);
   if (st != QMM_OK) return st;
   return launch_rowquant<1>(X, x_dtype, smooth, M, K, qX, x_scale, as_stream(stream));
+}
+
+extern "C" int sq_quantize_activation_per_tensor(const void* X, int x_dtype, const float* smooth, int64_t M,
+                                                 int64_t K, int8_t* qX, float* x_scale, void* stream) {
+  int st = check_rowquant(X, x_dtype, smooth, M, K, qX, x_scale);
+  if (st != QMM_OK) return st;
+  hipStream_t s = as_stream(stream);
+  st = launch_rowquant<1, 1>(X, x_dtype, smooth, M, K, qX, x_scale, s);
+  if (st != QMM_OK) return st;
+  tensor_scale_kernel<<<1, 256, 0, s>>>(x_scale, M);
+  st = launch_status();
+  if (st != QMM_OK) return st;
+  return launch_rowquant<1, 2>(X, x_dtype, smooth, M, K, qX, x_scale, s);
 }
 
 extern "C" int sq_int8_gemm(const int8_t* qX, const float* x_scale, const int8_t* qW, const float* w_scale, int64_t M,

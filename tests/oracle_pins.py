@@ -398,7 +398,38 @@ def check_sym_int4_stored_groups():
     assert (chosen <= d.min(axis=2) + 8 * np.spacing(np.float32(1.0)) * s.astype(np.float64)).all()
 
 
+def check_per_tensor_activation():
+    # Per-tensor INT8 activations against the (pinned) per-token form:
+    # fl32(m / 127) is monotonic in m, so the tensor's scale is the largest
+    # per-token scale; with equal row maxima the two forms agree exactly; and
+    # one outlier row sets the tensor's scale and coarsens every other row,
+    # so the per-tensor error exceeds the per-token error ("Activation
+    # quantization and outliers").
+    g = np.random.Generator(np.random.PCG64(21))
+    x = g.standard_normal((64, 256)).astype(np.float32)
+    sm = (g.random(256) + 0.5).astype(np.float32)
+    qt, at = oracle.sq_quantize_activation_per_tensor(x, sm)
+    qr, ar = oracle.sq_quantize_activation(x, sm)
+    assert (at == ar.max()).all()
+    xe = x.copy()
+    xe[:, 0] = np.float32(100.0)                    # every row's absmax is column 0 after smoothing
+    xe[:, 0] *= sm[0]
+    qt2, at2 = oracle.sq_quantize_activation_per_tensor(xe, sm)
+    qr2, ar2 = oracle.sq_quantize_activation(xe, sm)
+    assert np.array_equal(at2, ar2) and np.array_equal(qt2, qr2)
+    xo = x.copy()
+    xo[7] *= np.float32(50.0)                       # an outlier token
+    xs = oracle.scale_columns_div(xo, sm).astype(np.float64)
+    qt3, at3 = oracle.sq_quantize_activation_per_tensor(xo, sm)
+    qr3, ar3 = oracle.sq_quantize_activation(xo, sm)
+    others = np.arange(64) != 7
+    et = np.abs(qt3 * at3[:, None].astype(np.float64) - xs)[others].mean()
+    er = np.abs(qr3 * ar3[:, None].astype(np.float64) - xs)[others].mean()
+    assert et > 5 * er, (et, er)
+
+
 ALL_CHECKS = [
+    check_per_tensor_activation,
     check_sym_int4_stored_groups,
     check_six_weights, check_eight_weights, check_int8_outlier, check_int4_symmetric_exercise,
     check_int4_outlier_slide, check_round_half_even, check_degenerate_groups, check_error_bound_and_zero,

@@ -167,3 +167,45 @@ def test_w8a8_no_smoothing_and_deterministic():
     rqw, rb = oracle.sq_quantize_weight(w.float().numpy(), None)
     _, _, _, ref = oracle.sq_w8a8_reference(x.float().numpy(), None, rqw, rb)
     assert_close(y1, ref, "w8a8 no smoothing")
+
+
+@pytest.mark.parametrize("smoothed", [True, False])
+@pytest.mark.parametrize("mkn", SMALL + [(2048, 4096, 4096)], ids=lambda t: "x".join(map(str, t)))
+def test_quantize_activation_per_tensor(mkn, smoothed):
+    # one INT8 scale for the whole activation matrix, repeated per row
+    m, k, n = mkn
+    x, w = sq_inputs(m, k, n, seed=3)
+    xf, wf = x.float().numpy(), w.float().numpy()
+    rs = oracle.smooth_factors(oracle.col_absmax(xf), oracle.col_absmax(wf), 0.5) if smoothed else None
+    sd = torch.from_numpy(rs).to(DEV) if smoothed else None
+    note(f"sq_quantize_activation_per_tensor M={m} K={k} smooth={smoothed}")
+    qx, a = qmm.sq_quantize_activation(x.to(DEV), sd, per_tensor=True)
+    rqx, ra = oracle.sq_quantize_activation_per_tensor(xf, rs)
+    assert bits_equal(a.cpu().numpy(), ra), first_diff(a.cpu().numpy(), ra)
+    assert bits_equal(qx.cpu().numpy(), rqx), first_diff(qx.cpu().numpy(), rqx)
+
+
+def test_w8a8_per_tensor_pipeline_and_fp32_rows():
+    # per-tensor activations through the INT8 GEMM (consumed like per-token
+    # scales), and fp32 input with rows longer than the register-resident path
+    m, k, n = 300, 1024, 257
+    x, w = sq_inputs(m, k, n, seed=4)
+    xf, wf = x.float().numpy(), w.float().numpy()
+    rs = oracle.smooth_factors(oracle.col_absmax(xf), oracle.col_absmax(wf), 0.5)
+    sd = torch.from_numpy(rs).to(DEV)
+    qw, b = qmm.sq_quantize_weight(w.to(DEV), sd)
+    qx, a = qmm.sq_quantize_activation(x.to(DEV), sd, per_tensor=True)
+    rqx, ra = oracle.sq_quantize_activation_per_tensor(xf, rs)
+    rqw, rb = oracle.sq_quantize_weight(wf, rs)
+    note("w8a8 per-tensor activations through sq_int8_gemm")
+    y = qmm.sq_int8_gemm(qx, a, qw, b, out_dtype=torch.float32).cpu()
+    ref = oracle.rescale_f64(oracle.int8_matmul_nt(rqx, rqw), ra, rb)
+    from gpu_util import assert_close
+    assert_close(y, ref, "w8a8 per-tensor")
+    g = np.random.Generator(np.random.PCG64(8))
+    xl = (g.standard_normal((9, 8192)) * 3).astype(np.float32)
+    xl[4] = 0.0
+    note("sq_quantize_activation_per_tensor 9x8192 fp32")
+    qx2, a2 = qmm.sq_quantize_activation(torch.from_numpy(xl).to(DEV), None, per_tensor=True)
+    rq2, ra2 = oracle.sq_quantize_activation_per_tensor(xl, None)
+    assert bits_equal(a2.cpu().numpy(), ra2) and bits_equal(qx2.cpu().numpy(), rq2)
