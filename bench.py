@@ -275,6 +275,21 @@ def build_ops(dev):
                             flops=2 * B * n * k, bound="hbm",
                             kernel="gemv_valu_kernel" if B == 1 else w4_kernel_name(B, n, dev),
                             group="gemv_b1" if B == 1 else None))
+    # Weight-only INT8 decode on the same matrices (per-channel codes from
+    # the on-device quantizer), after the INT4 GEMVs.
+    for B in (1, 8):
+        for m in mats:
+            n, k = m["n"], m["k"]
+            if "q8" not in m:
+                m["q8"], m["b8"] = qmm.sq_quantize_weight(m["w"])
+
+            def w8(i, m=m, B=B):
+                x, y = m[f"x{B}"], m[f"y{B}"]
+                st = qmm.lib().w8a16_gemv(qmm._ptr(m["q8"]), qmm._ptr(m["b8"]), m["n"], m["k"], qmm._ptr(x),
+                                          qmm.BF16, B, qmm._ptr(y), qmm.BF16, qmm._stream(x))
+                assert st == 0, st
+            ops.append(dict(name=f"w8a16_gemv B={B} {n}x{k}", fn=w8, bytes=n * k + n * 4 + B * k * 2 + B * n * 2,
+                            flops=2 * B * n * k, bound="hbm", kernel="w8_gemv_kernel"))
 
     return ops, mats
 

@@ -156,6 +156,23 @@ int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
                int group, const void* X, int x_dtype, int64_t M, void* Y, int y_dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * w8a16_gemv -- weight-only INT8 decode matmul:
+ *   y[b, n] = w_scale[n] * sum_k x[b, k] * qW[n, k]
+ * with per-output-channel INT8 weights (sq_quantize_weight with smooth NULL
+ * writes them) and 16-bit activations, accumulated in fp32 on the vector ALUs
+ * (each weight byte is converted exactly to a 16-bit float pair element).
+ * Source: "How quantization works" ("Mainstream schemes at a glance": W8A16
+ * halves the weight bytes of decode while computing in 16 bits).
+ * qW : int8 [N, K] row-major, 16-byte aligned.  w_scale : float32 [N].
+ * x  : [B, K] of x_dtype (QMM_BF16 or QMM_F16), 16-byte aligned, 1 <= B <= 8.
+ * y  : [B, N] of y_dtype (x_dtype or QMM_F32).
+ * K a multiple of 64 (QMM_EUNSUPPORTED otherwise), K <= 2^24 and N < 2^31
+ * (QMM_ERANGE).  Errors are detected on the host before any launch.
+ * ------------------------------------------------------------------------- */
+int w8a16_gemv(const int8_t* qW, const float* w_scale, int64_t N, int64_t K, const void* x, int x_dtype,
+               int64_t B, void* y, int y_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
  * SmoothQuant W8A8.
  * Sources: "How quantization works" ("Activation quantization and outliers":
  * per-row INT8 weights, the smoothing factor with alpha and its 1e-5 floor);

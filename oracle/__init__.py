@@ -201,6 +201,15 @@ def w4a16_reference(x, q, s, z, group: int = 128) -> np.ndarray:
     return matmul_nt_f64(x, asym_dequantize(q, s, z, group))
 
 
+def w8a16_reference(x, qw, b) -> np.ndarray:
+    """Weight-only INT8 ("How quantization works", "Mainstream schemes at a
+    glance", W8A16 row): y[t, n] = sum_k x[t, k] * (qW[n, k] * b[n]), summed in
+    fp64 as b[n] * sum_k x[t, k] qW[n, k] (the integers are exact in fp32)."""
+    qw = np.ascontiguousarray(qw, np.int8).astype(np.float32)
+    b = _f32(b).reshape(-1).astype(np.float64)
+    return matmul_nt_f64(x, qw) * b[None, :]
+
+
 def int8_matmul_nt(qa, qb) -> np.ndarray:
     qa = np.ascontiguousarray(qa, np.int8)
     qb = np.ascontiguousarray(qb, np.int8)

@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "QmmError", "lib", "library_path", "F32", "F16", "BF16", "I32", "GROUP",
     "w4_sizes", "quantize_groupwise", "quantize_groupwise_symmetric", "dequantize", "w4a16_gemv", "w4a16_gemm",
+    "w8a16_gemv",
     "sq_smooth_factors", "sq_quantize_weight", "sq_quantize_activation", "sq_quantize_activation_per_tensor",
     "sq_int8_gemm",
     "sq_workspace_bytes", "smooth_quant_w8a8_gemm",
@@ -51,6 +52,7 @@ _SIGS = {
     "dequantize": ([_P, _P, _P, _I64, _I64, _I, _I, _P, _I, _P], _I),
     "w4a16_gemv": ([_P, _P, _P, _I64, _I64, _I, _P, _I, _I64, _P, _I, _P], _I),
     "w4a16_gemm": ([_P, _P, _P, _I64, _I64, _I, _P, _I, _I64, _P, _I, _P], _I),
+    "w8a16_gemv": ([_P, _P, _I64, _I64, _P, _I, _I64, _P, _I, _P], _I),
     "sq_smooth_factors": ([_P, _I, _I64, _P, _I, _I64, _I64, _F, _P, _P, _P, _P], _I),
     "sq_quantize_weight": ([_P, _I, _P, _I64, _I64, _P, _P, _P], _I),
     "sq_quantize_activation": ([_P, _I, _P, _I64, _I64, _P, _P, _P], _I),
@@ -125,6 +127,11 @@ def quantize_groupwise(W: torch.Tensor, group: int = GROUP, bits: int = 4, symme
     return codes, scales, zeros
 
 
+def quantize_groupwise_symmetric(W: torch.Tensor, group: int = GROUP, bits: int = 4):
+    """Symmetric per-group INT4 in the asymmetric storage format (zero-point 8)."""
+    return quantize_groupwise(W, group, bits, symmetric=True)
+
+
 def dequantize(codes, scales, zeros, dtype: torch.dtype = torch.float32, group: int = GROUP, bits: int = 4):
     """INT4 format -> W_hat [N, K] in dtype."""
     _check(codes, "codes")
@@ -164,6 +171,21 @@ def w4a16_gemm(codes, scales, zeros, X: torch.Tensor, out_dtype: Optional[torch.
     return out
 
 
+def w8a16_gemv(qW, w_scale, x: torch.Tensor, out_dtype: Optional[torch.dtype] = None,
+               out: Optional[torch.Tensor] = None):
+    """y [B, N] = w_scale[n] * (x [B, K] @ qW^T) for B <= 8 (weight-only INT8 decode)."""
+    _check(qW, "qW")
+    _check(x, "x")
+    x2 = x if x.dim() == 2 else x.reshape(1, -1)
+    N, K = qW.shape
+    B = x2.shape[0]
+    if out is None:
+        out = torch.empty((B, N), dtype=out_dtype or x.dtype, device=x.device)
+    _call("w8a16_gemv", _ptr(qW), _ptr(w_scale), N, K, _ptr(x2), _dt(x2.dtype), B, _ptr(out), _dt(out.dtype),
+          _stream(x))
+    return out
+
+
 def sq_smooth_factors(X: torch.Tensor, W: torch.Tensor, alpha: float = 0.5):
     """-> (smooth [K], x_colmax [K], w_colmax [K]) float32."""
     _check(X, "X")
@@ -197,6 +219,11 @@ def sq_quantize_activation(X: torch.Tensor, smooth: Optional[torch.Tensor] = Non
     _call("sq_quantize_activation_per_tensor" if per_tensor else "sq_quantize_activation", _ptr(X), _dt(X.dtype),
           _ptr(smooth), M, K, _ptr(q), _ptr(s), _stream(X))
     return q, s
+
+
+def sq_quantize_activation_per_tensor(X: torch.Tensor, smooth: Optional[torch.Tensor] = None):
+    """-> (qX int8 [M, K], x_scale f32 [M]) with one scale for the whole X, repeated per row."""
+    return sq_quantize_activation(X, smooth, per_tensor=True)
 
 
 def sq_int8_gemm(qX, x_scale, qW, w_scale, out_dtype: torch.dtype = torch.bfloat16,

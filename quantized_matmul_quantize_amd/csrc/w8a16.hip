@@ -1,0 +1,213 @@
+// w8a16.hip -- weight-only INT8 decode matmul (W8A16):
+//   y[b, n] = w_scale[n] * sum_k x[b, k] * qW[n, k]
+// with the per-channel INT8 weights that sq_quantize_weight writes (no
+// smoothing) and 16-bit activations.  Weight-only INT8 halves the bytes of a
+// 16-bit weight read while the arithmetic stays in 16-bit floats ("How
+// quantization works", "Mainstream schemes at a glance": the W8A16 / W4A16
+// row, which speeds up weight reads at small batch).
+//
+// Kernel (vector ALUs only; decode is a stream of weight bytes, not a dense
+// contraction):
+//  * w8_gemv_kernel: a block of four wavefronts takes R = 8 weight rows; per
+//    step a lane loads 16 bytes (16 weights) of each row, so 8 x 16 bytes are
+//    in flight per lane, and the matching 16 activations per token.  A weight
+//    byte becomes an fp32 integer in one instruction (sign-extending byte
+//    select), two of them one 16-bit pair (exact: |q| <= 128 has at most 8
+//    significant bits), and v_dot2_f32_{bf16,f16} multiplies that pair with
+//    the activation pair as loaded.  The per-channel scale multiplies the
+//    row's total once.
+
+#include "qmm_device.h"
+
+namespace qmm {
+namespace {
+
+constexpr int kW8Waves = 4;
+constexpr int kW8LaneK = 16;                                  // weights per lane per row per step
+constexpr int64_t kW8StepK = kW8Waves * kWave * kW8LaneK;     // 4096
+constexpr int kW8Rows = 8;                                    // rows per block
+constexpr int64_t kW8MaxK = int64_t(1) << 24;                 // lane offsets stay 32-bit
+
+template <int YDT>
+__device__ __forceinline__ void store_out(void* y, int64_t idx, float v) {
+  if constexpr (YDT == QMM_F32) {
+    static_cast<float*>(y)[idx] = v;
+  } else if constexpr (YDT == QMM_BF16) {
+    static_cast<uint16_t*>(y)[idx] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+  } else {
+    static_cast<uint16_t*>(y)[idx] = static_cast<uint16_t>(f32_to_f16_bits(v));
+  }
+}
+
+// Bytes 2i and 2i+1 of w (signed) as one pair of 16-bit floats of type DT,
+// element 2i in the low half.  Both conversions are exact.
+template <int DT, int I>
+__device__ __forceinline__ uint32_t i8_pair(uint32_t w) {
+  const float lo = static_cast<float>(static_cast<int8_t>(w >> (16 * I)));
+  const float hi = static_cast<float>(static_cast<int8_t>(w >> (16 * I + 8)));
+  if constexpr (DT == QMM_BF16) {
+    // An integer of at most 8 significant bits has zero low 16 bits in fp32:
+    // its bfloat16 is the high half.
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+}
+
+template <int XDT, int YDT, int B, int R>
+__global__ __launch_bounds__(256) void w8_gemv_kernel(const int8_t* __restrict__ qW,
+                                                      const float* __restrict__ w_scale, int64_t N, int64_t K,
+                                                      const uint16_t* __restrict__ x, void* __restrict__ y) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * R;
+  const int kk = static_cast<int>(K);
+
+  const int8_t* wrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = (row0 + r < N) ? row0 + r : N - 1;
+    wrow[r] = qW + row * K;
+  }
+
+  float acc[R][B];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+
+  for (uint32_t k0 = 0; k0 < static_cast<uint32_t>(kk); k0 += static_cast<uint32_t>(kW8StepK)) {
+    // A wavefront with no lane inside K leaves the loop; in a partly covered
+    // step the lanes past K load the last 16 weights of the row (in bounds)
+    // and take zero activations.
+    if (k0 + static_cast<uint32_t>(wave * (kWave * kW8LaneK)) >= static_cast<uint32_t>(kk)) break;
+    const uint32_t kb_raw = k0 + static_cast<uint32_t>(wave * (kWave * kW8LaneK) + lane * kW8LaneK);
+    const bool inside = kb_raw < static_cast<uint32_t>(kk);
+    const uint32_t kb = inside ? kb_raw : static_cast<uint32_t>(kk - kW8LaneK);
+
+    // All loads of the step before any use: activations, then the rows in
+    // the order they are consumed.
+    u32x4 xraw[B][2];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      xraw[b][0] = ld16(x + b * K + kb);
+      xraw[b][1] = ld16(x + b * K + kb + 8);
+    }
+    u32x4 cw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) cw[r] = ld16_nt(wrow[r] + kb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!inside) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) xraw[b][0] = xraw[b][1] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // Activation word j holds elements kb + 2j (low half) and kb + 2j + 1.
+    uint32_t xp[B][8];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      xp[b][0] = xraw[b][0].x;
+      xp[b][1] = xraw[b][0].y;
+      xp[b][2] = xraw[b][0].z;
+      xp[b][3] = xraw[b][0].w;
+      xp[b][4] = xraw[b][1].x;
+      xp[b][5] = xraw[b][1].y;
+      xp[b][6] = xraw[b][1].z;
+      xp[b][7] = xraw[b][1].w;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      // Weight word c holds elements kb + 4c .. kb + 4c + 3 (byte i = element 4c + i).
+      const uint32_t words[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+      float a0[B], a1[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) a0[b] = a1[b] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t p0 = i8_pair<XDT, 0>(words[c]);
+        const uint32_t p1 = i8_pair<XDT, 1>(words[c]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          a0[b] = dot2<XDT>(p0, xp[b][2 * c], a0[b]);
+          a1[b] = dot2<XDT>(p1, xp[b][2 * c + 1], a1[b]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[r][b] += a0[b] + a1[b];
+    }
+  }
+
+  __shared__ float red[kW8Waves][R * B];
+  static_assert((R * B) % 8 == 0, "rows x tokens must be a multiple of 8");
+#pragma unroll
+  for (int h = 0; h < R * B / 8; ++h) {
+    float v8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v8[i] = acc[(8 * h + i) / B][(8 * h + i) % B];
+    const float v = wave_sum8(v8);   // lane l holds the sum of value l >> 3
+    if ((lane & 7) == 0) red[wave][8 * h + (lane >> 3)] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < R * B) {
+    const int r = threadIdx.x / B;
+    const int b = threadIdx.x % B;
+    const int64_t row = row0 + r;
+    if (row < N) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kW8Waves; ++w) v += red[w][threadIdx.x];
+      store_out<YDT>(y, static_cast<int64_t>(b) * N + row, v * w_scale[row]);
+    }
+  }
+}
+
+template <int XDT, int YDT, int B>
+void launch_w8_b(const int8_t* qW, const float* ws, int64_t N, int64_t K, const uint16_t* x, void* y,
+                 hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(ceil_div(N, kW8Rows)));
+  w8_gemv_kernel<XDT, YDT, B, kW8Rows><<<grid, dim3(kW8Waves * kWave), 0, s>>>(qW, ws, N, K, x, y);
+}
+
+template <int XDT, int YDT>
+void launch_w8(int64_t B, const int8_t* qW, const float* ws, int64_t N, int64_t K, const uint16_t* x, void* y,
+               hipStream_t s) {
+  switch (B) {
+    case 1: launch_w8_b<XDT, YDT, 1>(qW, ws, N, K, x, y, s); break;
+    case 2: launch_w8_b<XDT, YDT, 2>(qW, ws, N, K, x, y, s); break;
+    case 3: launch_w8_b<XDT, YDT, 3>(qW, ws, N, K, x, y, s); break;
+    case 4: launch_w8_b<XDT, YDT, 4>(qW, ws, N, K, x, y, s); break;
+    case 5: launch_w8_b<XDT, YDT, 5>(qW, ws, N, K, x, y, s); break;
+    case 6: launch_w8_b<XDT, YDT, 6>(qW, ws, N, K, x, y, s); break;
+    case 7: launch_w8_b<XDT, YDT, 7>(qW, ws, N, K, x, y, s); break;
+    default: launch_w8_b<XDT, YDT, 8>(qW, ws, N, K, x, y, s); break;
+  }
+}
+
+}  // namespace
+}  // namespace qmm
+
+using namespace qmm;
+
+extern "C" int w8a16_gemv(const int8_t* qW, const float* w_scale, int64_t N, int64_t K, const void* x, int x_dtype,
+                          int64_t B, void* y, int y_dtype, void* stream) {
+  if (!qW || !w_scale || !x || !y) return QMM_EINVAL;
+  if (N <= 0 || K <= 0 || B <= 0) return QMM_EINVAL;
+  if ((x_dtype != QMM_BF16 && x_dtype != QMM_F16 && x_dtype != QMM_F32 && x_dtype != QMM_I32) ||
+      (y_dtype != QMM_BF16 && y_dtype != QMM_F16 && y_dtype != QMM_F32 && y_dtype != QMM_I32))
+    return QMM_EINVAL;
+  if (x_dtype != QMM_BF16 && x_dtype != QMM_F16) return QMM_EUNSUPPORTED;
+  if (y_dtype != x_dtype && y_dtype != QMM_F32) return QMM_EUNSUPPORTED;
+  if (B > 8 || K % 64 != 0) return QMM_EUNSUPPORTED;
+  if (K > kW8MaxK || N > INT32_MAX) return QMM_ERANGE;
+  if (!aligned(qW, 16) || !aligned(x, 16) || !aligned(w_scale, 4) || !aligned(y, y_dtype == QMM_F32 ? 4 : 2))
+    return QMM_EALIGN;
+  hipStream_t s = as_stream(stream);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  if (x_dtype == QMM_BF16) {
+    if (y_dtype == QMM_F32) launch_w8<QMM_BF16, QMM_F32>(B, qW, w_scale, N, K, xp, y, s);
+    else launch_w8<QMM_BF16, QMM_BF16>(B, qW, w_scale, N, K, xp, y, s);
+  } else {
+    if (y_dtype == QMM_F32) launch_w8<QMM_F16, QMM_F32>(B, qW, w_scale, N, K, xp, y, s);
+    else launch_w8<QMM_F16, QMM_F16>(B, qW, w_scale, N, K, xp, y, s);
+  }
+  return launch_status();
+}

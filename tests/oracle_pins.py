@@ -428,8 +428,37 @@ def check_per_tensor_activation():
     assert et > 5 * er, (et, er)
 
 
+def check_w8a16_reference():
+    # Weight-only INT8 matmul ("How quantization works", "Mainstream schemes
+    # at a glance", W8A16 row).  (1) Brute force on small integers with
+    # power-of-two scales, where every product and sum is exact: distinct
+    # shapes for tokens, rows and K and a distinct scale per row catch a
+    # transposed operand or a scale taken from the wrong index.  (2) The
+    # rounding bound of the pinned per-channel quantizer: each weight moves by
+    # at most half its row's step, so |y - x W^T| <= b[n]/2 * sum_k |x[t, k]|.
+    g = np.random.Generator(np.random.PCG64(31))
+    T, N, K = 3, 5, 7
+    x = g.integers(-9, 10, (T, K))
+    q = g.integers(-128, 128, (N, K))
+    b = np.array([2.0 ** -e for e in range(N)])
+    y = oracle.w8a16_reference(x.astype(np.float32), q.astype(np.int8), b.astype(np.float32))
+    for t in range(T):
+        for n in range(N):
+            exact = sum(int(x[t, k]) * int(q[n, k]) for k in range(K)) * b[n]
+            assert y[t, n] == exact, (t, n, y[t, n], exact)
+    w = (g.standard_normal((48, 320)) * np.linspace(0.1, 3.0, 48)[:, None]).astype(np.float32)
+    xs = g.standard_normal((4, 320)).astype(np.float32)
+    qw, bw = oracle.sq_quantize_weight(w, None)
+    yq = oracle.w8a16_reference(xs, qw, bw)
+    yr = xs.astype(np.float64) @ w.astype(np.float64).T
+    bound = 0.5 * bw.astype(np.float64)[None, :] * np.abs(xs.astype(np.float64)).sum(1)[:, None]
+    assert (np.abs(yq - yr) <= bound * (1 + 1e-6)).all()
+    assert np.abs(yq - yr).max() > 0
+
+
 ALL_CHECKS = [
     check_per_tensor_activation,
+    check_w8a16_reference,
     check_sym_int4_stored_groups,
     check_six_weights, check_eight_weights, check_int8_outlier, check_int4_symmetric_exercise,
     check_int4_outlier_slide, check_round_half_even, check_degenerate_groups, check_error_bound_and_zero,

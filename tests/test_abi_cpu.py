@@ -49,6 +49,30 @@ def test_binding_covers_every_symbol():
     assert set(declared_functions()) <= set(qmm._SIGS)
 
 
+def test_binding_names_match_the_header():
+    # every C entry point has a Python function of the same name, and every
+    # name the package exports resolves
+    for n in declared_functions():
+        if n not in ("qmm_status_string", "qmm_version", "qmm_w4_sizes", "sq_workspace_bytes"):
+            assert callable(getattr(qmm, n, None)), n
+    for n in qmm.__all__:
+        assert hasattr(qmm, n), n
+
+
+def test_w8a16_argument_errors():
+    f = qmm.lib().w8a16_gemv
+    assert f(None, P, 8, 256, P, BF16, 1, P, BF16, None) == EINVAL
+    assert f(P, P, 0, 256, P, BF16, 1, P, BF16, None) == EINVAL
+    assert f(P, P, 8, 256, P, BF16, 0, P, BF16, None) == EINVAL
+    assert f(P, P, 8, 256, P, BF16, 9, P, BF16, None) == EUNSUP     # B > 8
+    assert f(P, P, 8, 200, P, BF16, 1, P, BF16, None) == EUNSUP     # K % 64
+    assert f(P, P, 8, 256, P, F32, 1, P, F32, None) == EUNSUP       # fp32 activations
+    assert f(P, P, 8, 256, P, BF16, 1, P, F16, None) == EUNSUP      # mixed 16-bit types
+    assert f(P, P, 8, 256, P, 7, 1, P, BF16, None) == EINVAL        # bad dtype value
+    assert f(P, P, 8, (1 << 24) + 64, P, BF16, 1, P, BF16, None) == ERANGE
+    assert f(P, P, 8, 256, MIS, BF16, 1, P, BF16, None) == EALIGN
+
+
 def test_status_strings_and_version():
     lib = qmm.lib()
     for st in [OK, EINVAL, EUNSUP, EALIGN, EWS, EHIP, ERANGE, -99]:
