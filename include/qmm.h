@@ -159,8 +159,9 @@ int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  * w8a16_gemv -- weight-only INT8 decode matmul:
  *   y[b, n] = w_scale[n] * sum_k x[b, k] * qW[n, k]
  * with per-output-channel INT8 weights (sq_quantize_weight with smooth NULL
- * writes them) and 16-bit activations, accumulated in fp32 on the vector ALUs
- * (each weight byte is converted exactly to a 16-bit float pair element).
+ * writes them) and 16-bit activations, accumulated in fp32; each weight byte
+ * is converted exactly to a 16-bit float.  B <= 2 runs on the vector ALUs
+ * (dot2), 3 <= B <= 8 on bf16/fp16 matrix cores with the weights as operand.
  * Source: "How quantization works" ("Mainstream schemes at a glance": W8A16
  * halves the weight bytes of decode while computing in 16 bits).
  * qW : int8 [N, K] row-major, 16-byte aligned.  w_scale : float32 [N].

@@ -31,7 +31,8 @@ SOURCES = ["abi.hip", "quantize.hip", "w4a16.hip", "w8a8.hip", "w8a16.hip"]
 # allocator copies accumulators between registers on every loop iteration,
 # and results folded on the vector ALUs would be copied out of AGPRs.
 EXTRA = {"w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-         "w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+         "w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "w8a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

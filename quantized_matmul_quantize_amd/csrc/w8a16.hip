@@ -15,7 +15,13 @@
 //    select), two of them one 16-bit pair (exact: |q| <= 128 has at most 8
 //    significant bits), and v_dot2_f32_{bf16,f16} multiplies that pair with
 //    the activation pair as loaded.  The per-channel scale multiplies the
-//    row's total once.
+//    row's total once.  Used for B <= 2.
+//  * w8_mfma_kernel: 3..8 tokens, where the dot products of the kernel above
+//    (one per weight pair and token) outrun the weight stream.  The weights
+//    are the A operand of v_mfma_f32_16x16x32_{bf16,f16} straight from
+//    registers (converted as above), the activations the B operand as loaded;
+//    a block of four wavefronts owns 16 rows, each wavefront a contiguous
+//    quarter of K, summed through LDS at the end.
 
 #include "qmm_device.h"
 
@@ -160,6 +166,90 @@ __global__ __launch_bounds__(256) void w8_gemv_kernel(const int8_t* __restrict__
   }
 }
 
+// MFMA kernel.  Operand layout of v_mfma_f32_16x16x32: lane l supplies A row
+// l%16 and B column l%16 with k = 8*(l/16) .. +8 of the instruction; D lane l
+// holds rows 4*(l/16) .. +4 of column l%16.  Chunk j of a wavefront's step is
+// 64 k; lane l loads 16 weight bytes of row l%16 at k = 16*(l/16) within it
+// and feeds bytes 0..7 to one instruction and 8..15 to the next, with the
+// activations of token l%16 at the same k (16 bytes each), so both operands
+// cover the same k in the same order.
+constexpr int kW8MfmaU = 8;   // 64-k chunks per step: 8 x 16 weight bytes in flight per lane
+
+template <int XDT>
+__device__ __forceinline__ f32x4 mfma16x16x32_w8(const uint32_t a[4], u32x4 b, f32x4 c) {
+  const u32x4 av = {a[0], a[1], a[2], a[3]};
+  if constexpr (XDT == QMM_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  } else {
+    typedef _Float16 f16x8_w8 __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_w8, av), __builtin_bit_cast(f16x8_w8, b), c,
+                                                  0, 0, 0);
+  }
+}
+
+template <int XDT, int YDT, int NW>
+__global__ __launch_bounds__(NW * 64) void w8_mfma_kernel(const int8_t* __restrict__ qW, const float* __restrict__ w_scale,
+                                                      int64_t N, int64_t K, const uint16_t* __restrict__ x, int64_t B,
+                                                      void* __restrict__ y) {
+  __shared__ float red[NW][4][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int l16 = lane & 15;
+  const int quad = lane >> 4;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t ra = (row0 + l16 < N) ? row0 + l16 : N - 1;        // rows past N read the last row
+  const int64_t ta = (l16 < B) ? l16 : B - 1;                      // tokens past B repeat the last token
+  const int nchunks = static_cast<int>(K / 64);
+  const int cper = (nchunks + NW - 1) / NW;
+  const int cbeg = wave * cper;
+  const int cend = (cbeg + cper < nchunks) ? cbeg + cper : nchunks;
+  const int8_t* wp = qW + ra * K + 16 * quad;
+  const uint16_t* xp = x + ta * K + 16 * quad;
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = cbeg; c0 < cend; c0 += kW8MfmaU) {
+    u32x4 wv[kW8MfmaU], xv[kW8MfmaU][2];
+#pragma unroll
+    for (int u = 0; u < kW8MfmaU; ++u) {
+      if (c0 + u < cend) {   // wavefront-uniform
+        const int64_t k = static_cast<int64_t>(c0 + u) * 64;
+        xv[u][0] = ld16(xp + k);
+        xv[u][1] = ld16(xp + k + 8);
+        wv[u] = ld16_nt(wp + k);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kW8MfmaU; ++u) {
+      if (c0 + u < cend) {
+        const uint32_t a0[4] = {i8_pair<XDT, 0>(wv[u].x), i8_pair<XDT, 1>(wv[u].x), i8_pair<XDT, 0>(wv[u].y),
+                                i8_pair<XDT, 1>(wv[u].y)};
+        const uint32_t a1[4] = {i8_pair<XDT, 0>(wv[u].z), i8_pair<XDT, 1>(wv[u].z), i8_pair<XDT, 0>(wv[u].w),
+                                i8_pair<XDT, 1>(wv[u].w)};
+        acc = mfma16x16x32_w8<XDT>(a0, xv[u][0], acc);
+        acc = mfma16x16x32_w8<XDT>(a1, xv[u][1], acc);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < 4 * kWave) {
+    const int i = threadIdx.x >> 6;          // 256 threads: one D value each
+    const int l = threadIdx.x & (kWave - 1);
+    const int64_t row = row0 + 4 * (l >> 4) + i;
+    const int64_t t = l & 15;
+    if (row < N && t < B) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w][i][l];
+      store_out<YDT>(y, t * N + row, v * w_scale[row]);
+    }
+  }
+}
+
 template <int XDT, int YDT, int B>
 void launch_w8_b(const int8_t* qW, const float* ws, int64_t N, int64_t K, const uint16_t* x, void* y,
                  hipStream_t s) {
@@ -170,15 +260,16 @@ void launch_w8_b(const int8_t* qW, const float* ws, int64_t N, int64_t K, const 
 template <int XDT, int YDT>
 void launch_w8(int64_t B, const int8_t* qW, const float* ws, int64_t N, int64_t K, const uint16_t* x, void* y,
                hipStream_t s) {
-  switch (B) {
-    case 1: launch_w8_b<XDT, YDT, 1>(qW, ws, N, K, x, y, s); break;
-    case 2: launch_w8_b<XDT, YDT, 2>(qW, ws, N, K, x, y, s); break;
-    case 3: launch_w8_b<XDT, YDT, 3>(qW, ws, N, K, x, y, s); break;
-    case 4: launch_w8_b<XDT, YDT, 4>(qW, ws, N, K, x, y, s); break;
-    case 5: launch_w8_b<XDT, YDT, 5>(qW, ws, N, K, x, y, s); break;
-    case 6: launch_w8_b<XDT, YDT, 6>(qW, ws, N, K, x, y, s); break;
-    case 7: launch_w8_b<XDT, YDT, 7>(qW, ws, N, K, x, y, s); break;
-    default: launch_w8_b<XDT, YDT, 8>(qW, ws, N, K, x, y, s); break;
+  // One or two tokens stream fastest on the vector ALUs; from three on the
+  // dot products would outrun the weight stream, so the MFMA kernel takes over.
+  if (B == 1) {
+    launch_w8_b<XDT, YDT, 1>(qW, ws, N, K, x, y, s);
+  } else if (B == 2) {
+    launch_w8_b<XDT, YDT, 2>(qW, ws, N, K, x, y, s);
+  } else {
+    // Four wavefronts per block (eight measured no faster on 8192 x 28672).
+    const dim3 grid(static_cast<unsigned>(ceil_div(N, 16)));
+    w8_mfma_kernel<XDT, YDT, 4><<<grid, dim3(4 * kWave), 0, s>>>(qW, ws, N, K, x, B, y);
   }
 }
 
