@@ -85,3 +85,31 @@ def test_pins_catch_mutant(mid, old, new, source, tmp_path):
         assert failures, f"mutant {mid} passed every pin"
     finally:
         oracle._lib = saved
+
+
+def _w8a16_mutants():
+    import numpy as np
+
+    def f32(q):
+        return np.ascontiguousarray(q, np.int8).astype(np.float32)
+
+    def b64(b):
+        return np.asarray(b, np.float32).reshape(-1).astype(np.float64)
+
+    return [
+        ("w8a16_no_scale", lambda x, q, b: oracle.matmul_nt_f64(x, f32(q))),
+        ("w8a16_scale_divides", lambda x, q, b: oracle.matmul_nt_f64(x, f32(q)) / b64(b)[None, :]),
+        ("w8a16_unsigned_codes",
+         lambda x, q, b: oracle.matmul_nt_f64(x, np.ascontiguousarray(q, np.int8).view(np.uint8).astype(np.float32))
+         * b64(b)[None, :]),
+        ("w8a16_scales_reversed", lambda x, q, b: oracle.matmul_nt_f64(x, f32(q)) * b64(b)[::-1][None, :]),
+    ]
+
+
+@pytest.mark.parametrize("mid,fn", _w8a16_mutants(), ids=[m[0] for m in _w8a16_mutants()])
+def test_w8a16_pin_catches_mutant(mid, fn, monkeypatch):
+    # the weight-only INT8 product lives in the Python layer of the oracle:
+    # replace it by a plausible mistake and check its pin fails
+    monkeypatch.setattr(oracle, "w8a16_reference", fn)
+    with pytest.raises(Exception):
+        oracle_pins.check_w8a16_reference()
