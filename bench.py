@@ -18,7 +18,9 @@ are resident in HBM before timing starts:
     same GEMM): config.int8_gemm_TOPS is the GEMM alone, w8a8_online_TOPS the
     whole online call
   70B-class MLP decode: w4a16_gemv B=8 then B=1 on both matrices (B=1 is the
-    headline kernel), back to back at the end of the step
+    headline kernel), back to back, then weight-only INT8 (w8a16_gemv,
+    per-channel codes from sq_quantize_weight) at B=1 and B=8 on the same
+    matrices, at the end of the step
 
 The packed weights exist in 3 copies per matrix and successive steps rotate
 through them, so a kernel never finds its operands left in the 256 MB
