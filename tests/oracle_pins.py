@@ -313,9 +313,66 @@ def check_smoothquant_invariants():
     assert abs(float(s0[0]) - np.sqrt(1e-5) / np.sqrt(float(cw[0]))) < 1e-6 * float(s0[0])
 
 
+def _smooth_listing_columns():
+    """Column maxima over nine decades, plus the floor cases: a weight column
+    below the 1e-5 floor, an activation column below it, both below it, both
+    zero, and each exactly at it."""
+    g = np.random.Generator(np.random.PCG64(41))
+    cx = (10.0 ** g.uniform(-7, 2.5, 4000)).astype(np.float32)
+    cw = (10.0 ** g.uniform(-7, 0, 4000)).astype(np.float32)
+    fl = np.float32(1e-5)
+    cx[:6] = [np.float32(3.0), np.float32(2e-7), np.float32(4e-6), 0.0, fl, np.float32(0.5)]
+    cw[:6] = [np.float32(1e-7), np.float32(0.02), np.float32(3e-6), 0.0, np.float32(0.1), fl]
+    return cx, cw
+
+
+def check_smooth_factors_listing():
+    # "How quantization works", "Activation quantization and outliers": the
+    # listing computes, on float32 tensors,
+    #   s = clamp(max|X_j|, min=1e-5) ** alpha / clamp(max|W_j|, min=1e-5) ** (1 - alpha).
+    # (1) alpha = 1/2, bit for bit against that expression evaluated in numpy
+    # float32 (its ** 0.5 is the correctly rounded IEEE square root, its '/'
+    # the correctly rounded division), each maximum floored first.  The set
+    # holds columns where the one-root form fl32(sqrt(cx/cw)) rounds
+    # differently, so the two-root order of the listing is what is pinned.
+    cx, cw = _smooth_listing_columns()
+    fl = np.float32(1e-5)
+    xf, wf = np.maximum(cx, fl), np.maximum(cw, fl)
+    listing = (xf ** np.float32(0.5)) / (wf ** np.float32(1.0 - 0.5))
+    assert listing.dtype == np.float32
+    # the square roots are the correctly rounded ones (fp64 root, one rounding)
+    assert np.array_equal(xf ** np.float32(0.5), np.sqrt(xf.astype(np.float64)).astype(np.float32))
+    s = oracle.smooth_factors(cx, cw, 0.5)
+    assert np.array_equal(s.view(np.uint32), listing.view(np.uint32)), np.nonzero(s != listing)[0][:5]
+    one_root = np.sqrt(xf / wf).astype(np.float32)
+    assert (one_root != listing).sum() > 100
+    # the floor cases by their closed values
+    assert s[0] == np.float32(np.sqrt(np.float32(3.0))) / np.float32(np.sqrt(fl))
+    assert s[3] == np.float32(1.0) and s[4] == np.float32(np.sqrt(fl)) / np.float32(np.sqrt(np.float32(0.1)))
+    # (2) torch's CPU evaluation of the same listing (whose float32 square
+    # root is within one ulp but not always correctly rounded) agrees to an ulp.
+    import torch
+    tx, tw = torch.from_numpy(cx), torch.from_numpy(cw)
+    ts = (tx.clamp(min=1e-5) ** 0.5 / tw.clamp(min=1e-5) ** (1 - 0.5)).numpy()
+    assert np.abs(ts.view(np.int32).astype(np.int64) - s.view(np.int32).astype(np.int64)).max() <= 2
+    # (3) alpha = 3/4 (the powf branch) against the closed form
+    # xf^0.75 / wf^0.25 in fp64 and against torch's float32 listing, each to
+    # a few ulps.
+    s75 = oracle.smooth_factors(cx, cw, 0.75)
+    exact = xf.astype(np.float64) ** 0.75 / wf.astype(np.float64) ** 0.25
+    assert (np.abs(s75.astype(np.float64) - exact) <= 4 * np.spacing(np.abs(s75)).astype(np.float64)).all()
+    t75 = (tx.clamp(min=1e-5) ** 0.75 / tw.clamp(min=1e-5) ** (1 - 0.75)).numpy()
+    assert np.abs(t75.view(np.int32).astype(np.int64) - s75.view(np.int32).astype(np.int64)).max() <= 4
+    # s(3/4) / s(1/2) = (xf wf)^(1/4): larger exactly where xf wf > 1
+    prod = xf.astype(np.float64) * wf.astype(np.float64)
+    assert (s75[prod > 1.01] > s[prod > 1.01]).all() and (s75[prod < 0.99] < s[prod < 0.99]).all()
+
+
 def check_smoothquant_error_ordering():
     # "How quantization works", activation-outlier experiment: weight-only INT8
-    # error < SmoothQuant W8A8 error < plain W8A8 error.
+    # error < SmoothQuant W8A8 error < plain W8A8 error.  The listing there
+    # quantizes the activations with one scale per tensor; the per-token form
+    # (the online path of the W8A8 GEMM) keeps the same ordering.
     wl = workloads.WORKLOADS["smoothquant"]
     x, _ = workloads.sq_activations(wl, 256, 1024)
     w, _ = workloads.weight(wl, 0, shape=(256, 1024))
@@ -335,6 +392,17 @@ def check_smoothquant_error_ordering():
     _, _, _, y_sq = oracle.sq_w8a8_reference(x, s, qws, bs)
     err_plain, err_sq = rel(y_plain), rel(y_sq)
     assert err_w8 < err_sq < err_plain, (err_w8, err_sq, err_plain)
+
+    # the listing's own form: q8_per_tensor on the activations
+    def per_tensor(xv, sv, qwv, bv):
+        qx, a = oracle.sq_quantize_activation_per_tensor(xv, sv)
+        return oracle.rescale_f64(oracle.int8_matmul_nt(qx, qwv), a, bv)
+
+    err_plain_t = rel(per_tensor(x, None, qw, b))
+    err_sq_t = rel(per_tensor(x, s, qws, bs))
+    assert err_w8 < err_sq_t < err_plain_t, (err_w8, err_sq_t, err_plain_t)
+    # the page reports SmoothQuant cutting the per-tensor W8A8 error to about a third
+    assert err_sq_t < 0.5 * err_plain_t, (err_sq_t, err_plain_t)
 
 
 def check_sym_error_bound():
@@ -464,5 +532,5 @@ ALL_CHECKS = [
     check_int4_outlier_slide, check_round_half_even, check_degenerate_groups, check_error_bound_and_zero,
     check_nearest_grid_point, check_granularity_special_cases, check_packing, check_code_words, check_storage_70b,
     check_matmul_against_blas, check_w4a16_integer_case, check_int8_matmul, check_smoothquant_invariants,
-    check_smoothquant_error_ordering, check_sym_error_bound, check_sym_zero_row_floor,
+    check_smooth_factors_listing, check_smoothquant_error_ordering, check_sym_error_bound, check_sym_zero_row_floor,
 ]

@@ -44,6 +44,9 @@ MUTANTS = [
      "y[i * n + j] = (double)acc[i * n + j] * (double)a[i];"),
     ("smooth_inverted", "s[j] = num / den;", "s[j] = den / num;"),
     ("smooth_no_floor", "float x = cx[j] < fl ? fl : cx[j];", "float x = cx[j];"),
+    ("cw_no_floor", "float w = cw[j] < fl ? fl : cw[j];", "float w = cw[j];"),
+    ("sqrt_of_ratio", "num = sqrtf(x);\n            den = sqrtf(w);", "num = sqrtf(x / w);\n            den = 1.0f;"),
+    ("powf_alpha_swapped", "den = powf(w, 1.0f - alpha);", "den = powf(w, alpha);"),
     ("smooth_div_instead_of_mul", "out[i * cols + j] = a[i * cols + j] * s[j];",
      "out[i * cols + j] = a[i * cols + j] / s[j];"),
     ("col_absmax_signed", "float v = fabsf(a[i * cols + j]);", "float v = a[i * cols + j];"),
