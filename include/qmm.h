@@ -235,6 +235,27 @@ int smooth_quant_w8a8_gemm(const void* X, int x_dtype, const float* smooth, cons
                            const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int y_dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the library's own device scratch used by smooth_quant_w8a8_gemm_noalloc. */
+#define QMM_SQ_STATIC_SCRATCH_BYTES ((size_t)16 * 1024 * 1024 + (size_t)64 * 1024)
+
+/* ---------------------------------------------------------------------------
+ * smooth_quant_w8a8_gemm_noalloc -- smooth_quant_w8a8_gemm for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It computes the same result with
+ * the same kernels, but qX and x_scale live in a device array inside the
+ * library (QMM_SQ_STATIC_SCRATCH_BYTES per GPU, held until the process ends)
+ * instead of a caller workspace; the call itself allocates and frees nothing.
+ * Its device address is looked up on the first call on each device.
+ * Arguments and errors as smooth_quant_w8a8_gemm, without the workspace;
+ * QMM_ERANGE when sq_workspace_bytes(M, K) > QMM_SQ_STATIC_SCRATCH_BYTES
+ * (e.g. M * K above about 16.7 million), QMM_EHIP if the address lookup fails.
+ * All calls on one GPU share the array: calls that overlap in time on one GPU
+ * (other streams, other threads) race and must be serialized by the caller.
+ * ------------------------------------------------------------------------- */
+int smooth_quant_w8a8_gemm_noalloc(const void* X, int x_dtype, const float* smooth, const int8_t* qW,
+                                   const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int y_dtype,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ __all__ = [
     "w8a16_gemv",
     "sq_smooth_factors", "sq_quantize_weight", "sq_quantize_activation", "sq_quantize_activation_per_tensor",
     "sq_int8_gemm",
-    "sq_workspace_bytes", "smooth_quant_w8a8_gemm",
+    "sq_workspace_bytes", "smooth_quant_w8a8_gemm", "smooth_quant_w8a8_gemm_noalloc", "SQ_STATIC_SCRATCH_BYTES",
 ]
 
 F32, F16, BF16, I32 = 0, 1, 2, 3
@@ -60,7 +60,11 @@ _SIGS = {
     "sq_int8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "sq_workspace_bytes": ([_I64, _I64], _SZ),
     "smooth_quant_w8a8_gemm": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
+    "smooth_quant_w8a8_gemm_noalloc": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
 }
+
+# Device scratch of smooth_quant_w8a8_gemm_noalloc (QMM_SQ_STATIC_SCRATCH_BYTES).
+SQ_STATIC_SCRATCH_BYTES = 16 * 1024 * 1024 + 64 * 1024
 
 
 def lib() -> ctypes.CDLL:
@@ -258,4 +262,18 @@ def smooth_quant_w8a8_gemm(X: torch.Tensor, smooth: Optional[torch.Tensor], qW, 
         out = torch.empty((M, N), dtype=out_dtype, device=X.device)
     _call("smooth_quant_w8a8_gemm", _ptr(X), _dt(X.dtype), _ptr(smooth), _ptr(qW), _ptr(w_scale), M, N, K,
           _ptr(out), _dt(out.dtype), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(X))
+    return out
+
+
+def smooth_quant_w8a8_gemm_noalloc(X: torch.Tensor, smooth: Optional[torch.Tensor], qW, w_scale,
+                                   out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """smooth_quant_w8a8_gemm with the library's own device scratch instead of a
+    workspace (for callers that cannot allocate; pass `out` to allocate nothing)."""
+    _check(X, "X")
+    M, K = X.shape
+    N = qW.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    _call("smooth_quant_w8a8_gemm_noalloc", _ptr(X), _dt(X.dtype), _ptr(smooth), _ptr(qW), _ptr(w_scale), M, N, K,
+          _ptr(out), _dt(out.dtype), _stream(X))
     return out

@@ -16,6 +16,9 @@
 // operations with correctly rounded division, and codes use round-half-to-
 // even, so the INT8 codes and scales are reproducible bit for bit.
 
+#include <atomic>
+#include <mutex>
+
 #include "qmm_device.h"
 
 namespace qmm {
@@ -709,9 +712,12 @@ extern "C" size_t sq_workspace_bytes(int64_t M, int64_t K) {
   return (q + 255u) / 256u * 256u + static_cast<size_t>(M) * 4u;
 }
 
-extern "C" int smooth_quant_w8a8_gemm(const void* X, int x_dtype, const float* smooth, const int8_t* qW,
-                                      const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int y_dtype,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+namespace qmm {
+namespace {
+
+// Arguments of the online W8A8 call other than its workspace.
+int check_online(const void* X, int x_dtype, const float* smooth, const int8_t* qW, const float* w_scale, int64_t M,
+                 int64_t N, int64_t K, void* Y, int y_dtype) {
   if (!X || !qW || !w_scale || !Y) return QMM_EINVAL;
   if (M <= 0 || N <= 0 || K <= 0) return QMM_EINVAL;
   if (!float_dtype(x_dtype)) return x_dtype == QMM_I32 ? QMM_EUNSUPPORTED : QMM_EINVAL;
@@ -719,16 +725,98 @@ extern "C" int smooth_quant_w8a8_gemm(const void* X, int x_dtype, const float* s
     return y_dtype == QMM_F16 ? QMM_EUNSUPPORTED : QMM_EINVAL;
   if (K % 64 != 0) return QMM_EUNSUPPORTED;
   if (K > kMaxK) return QMM_ERANGE;
-  if (!workspace || workspace_bytes < sq_workspace_bytes(M, K) || !aligned(workspace, 16)) return QMM_EWORKSPACE;
   if (!aligned(X, 16) || !aligned(qW, 16) || !aligned(w_scale, 4) || !aligned(Y, 4) ||
       (smooth && !aligned(smooth, 16)))
     return QMM_EALIGN;
-  int8_t* qX = static_cast<int8_t*>(workspace);
-  float* xs = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+  return QMM_OK;
+}
+
+// Per-token smoothing + INT8 quantization of X into the workspace (qX, then
+// x_scale at the next 256-byte boundary), then the INT8 GEMM.  Every byte of
+// qX and x_scale is written before it is read, so the workspace needs no
+// clearing.
+int online_launch(const void* X, int x_dtype, const float* smooth, const int8_t* qW, const float* w_scale, int64_t M,
+                  int64_t N, int64_t K, void* Y, int y_dtype, uint8_t* workspace, hipStream_t s) {
+  int8_t* qX = reinterpret_cast<int8_t*>(workspace);
+  float* xs = reinterpret_cast<float*>(workspace +
                                        (static_cast<size_t>(M) * static_cast<size_t>(K) + 255u) / 256u * 256u);
-  hipStream_t s = as_stream(stream);
   int st = launch_rowquant<1>(X, x_dtype, smooth, M, K, qX, xs, s);
   if (st != QMM_OK) return st;
   launch_gemm(qX, xs, qW, w_scale, M, N, K, Y, y_dtype, s);
   return launch_status();
+}
+
+}  // namespace
+}  // namespace qmm
+
+extern "C" int smooth_quant_w8a8_gemm(const void* X, int x_dtype, const float* smooth, const int8_t* qW,
+                                      const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int y_dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_online(X, x_dtype, smooth, qW, w_scale, M, N, K, Y, y_dtype);
+  if (st != QMM_OK) return st;
+  if (!workspace || workspace_bytes < sq_workspace_bytes(M, K) || !aligned(workspace, 16)) return QMM_EWORKSPACE;
+  return online_launch(X, x_dtype, smooth, qW, w_scale, M, N, K, Y, y_dtype, static_cast<uint8_t*>(workspace),
+                       as_stream(stream));
+}
+
+// ----------------------------------------------------------------------------
+// Allocation-free variant: the workspace is this file-scope device array, one
+// copy per GPU, resident until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// its device address is looked up once per device with hipGetSymbolAddress,
+// with that device current, and that address is what the kernels receive.
+// Calls on one GPU share the array, so calls that overlap in time on one GPU
+// (different streams, or threads) race on it.
+static __device__ __align__(256) uint8_t scratch[QMM_SQ_STATIC_SCRATCH_BYTES];
+
+namespace qmm {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+std::atomic<uint8_t*> scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the device that `stream` belongs to (the
+// current device for the null stream), looked up on the first call on that
+// device.  QMM_EHIP if a HIP query fails.
+int scratch_for(hipStream_t stream, uint8_t** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return QMM_EHIP;
+  int dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return QMM_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return QMM_EHIP;
+  uint8_t* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p) {
+    *out = p;
+    return QMM_OK;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  p = scratch_addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return QMM_EHIP;
+    void* addr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return QMM_EHIP;
+    if (e != hipSuccess || !addr) return QMM_EHIP;
+    p = static_cast<uint8_t*>(addr);
+    scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return QMM_OK;
+}
+
+}  // namespace
+}  // namespace qmm
+
+extern "C" int smooth_quant_w8a8_gemm_noalloc(const void* X, int x_dtype, const float* smooth, const int8_t* qW,
+                                              const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y,
+                                              int y_dtype, void* stream) {
+  int st = check_online(X, x_dtype, smooth, qW, w_scale, M, N, K, Y, y_dtype);
+  if (st != QMM_OK) return st;
+  if (sq_workspace_bytes(M, K) > QMM_SQ_STATIC_SCRATCH_BYTES) return QMM_ERANGE;
+  hipStream_t s = as_stream(stream);
+  uint8_t* ws = nullptr;
+  st = scratch_for(s, &ws);
+  if (st != QMM_OK) return st;
+  return online_launch(X, x_dtype, smooth, qW, w_scale, M, N, K, Y, y_dtype, ws, s);
 }
