@@ -1,40 +1,47 @@
 #!/usr/bin/env python3
 """Benchmark of the INT4 / INT8 quantized-matmul hot path on one MI355X.
 
-One step runs every stage of the path once on synthetic, seeded inputs that
-are resident in HBM before timing starts:
+One step runs every stage of the path once, on synthetic seeded inputs that
+are resident in HBM before timing starts, for all five workloads:
 
-  70B-class MLP, bf16 weights 28672x8192 and 8192x28672 (N(0, 0.015),
-  0.1% of entries x10):
-    quantize_groupwise on both matrices      (group min/max, s, z, codes, packing)
-    quantize_groupwise_symmetric on the first (symmetric grid, same format)
-    dequantize to bf16 on both matrices
-  batched W4A16 GEMM, 14336x4096 INT4 G128, X bf16 [M, 4096], M = 16, 64, 256
+  70B-class MLP, bf16 weights 28672x8192 and 8192x28672 (N(0, 0.015), 0.1% of
+  entries x10): quantize_groupwise on both, quantize_groupwise_symmetric on
+  the first, dequantize to bf16 on both;
+  single 512x512 fp32 weight (4 planted +-0.5 outliers): quantize, then the
+  fp16 B=1 GEMV;
+  Llama-7B-like decode layer, bf16 4096x4096 and 11008x4096: quantize both,
+  then the B=1 GEMV on both;
+  batched W4A16 GEMM, bf16 14336x4096: quantize, then X bf16 [M, 4096] for
+  M = 16, 64, 256;
   SmoothQuant W8A8, X 2048x4096 (6 outlier channels x50..100), W 4096x4096:
-    sq_smooth_factors, sq_quantize_weight, per-tensor activation quantization
-    (the W8A8 baseline: X read twice), sq_int8_gemm alone (i8-MFMA GEMM
-    and rescale to bf16 on activations quantized before timing), and
-    smooth_quant_w8a8_gemm (per-token smoothing + INT8 quantization, then the
-    same GEMM): config.int8_gemm_TOPS is the GEMM alone, w8a8_online_TOPS the
-    whole online call
+  sq_smooth_factors, sq_quantize_weight, per-tensor activation quantization
+  (the W8A8 baseline: X read twice), sq_int8_gemm alone (i8-MFMA GEMM and
+  rescale to bf16, on activations quantized before timing) and
+  smooth_quant_w8a8_gemm (per-token smoothing + INT8 quantization, then the
+  same GEMM);
   70B-class MLP decode: w4a16_gemv B=8 then B=1 on both matrices (B=1 is the
-    headline kernel), back to back, then weight-only INT8 (w8a16_gemv,
-    per-channel codes from sq_quantize_weight) at B=1 and B=8 on the same
-    matrices, at the end of the step
+  headline), then weight-only INT8 (w8a16_gemv) at B=1 and B=8.
 
-The packed weights exist in 3 copies per matrix and successive steps rotate
-through them, so a kernel never finds its operands left in the 256 MB
-last-level cache by the previous use (every copy is touched once per 3 steps,
-with GBs of other traffic in between).
+Cache: the last-level cache is 256 MB.  No op reads an operand that anything
+touched within the last 512 MB of traffic: every op reads buffers of its own
+(the packed 70B weights exist in 4 copies per matrix, the 14336x4096 weight in
+3, the Llama-7B-like and 512x512 ones in 2, the SmoothQuant operands in one
+copy per reading op) and the copies rotate between steps.  The bench computes
+each op's reuse distance from this bookkeeping (bytes of algorithmic traffic
+since any of its inputs was last touched, over a steady-state run of steps),
+reports it per op (`reuse_MB`) and fails if an HBM-bound op falls under
+512 MB.
 
-Every kernel is bracketed by events on the stream it runs on (the library
-launches on torch's current stream), so per-kernel times come from the timed
-steps themselves; the two B=1 GEMVs run back to back inside one event pair
-(an event between them would add the second launch's dispatch latency to its
-time) and share its time.  `value` is the effective bandwidth of the B=1
-GEMVs: algorithmic bytes (packed codes, scales, zero-points, activations in,
-outputs out) over their kernel time.  The CPU baseline times the plain C oracle's
-reference product for the same GEMVs on the host.
+Timing: every op is bracketed by events on the stream it runs on (the
+library launches on torch's current stream), created without the system
+fence so that recording them leaves the caches alone; the two B=1 GEMVs of
+the 70B matrices run back to back inside one event pair and share its time.
+`value` is their effective bandwidth: algorithmic bytes (packed codes,
+scales, zero-points, activations in, outputs out) over kernel time.
+
+CPU baseline: the plain C oracle's reference for the same B=1 GEMVs
+(dequantize + fp64 product), single-threaded, and its OpenMP build over all
+the threads the host grants (OMP_NUM_THREADS); both on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 Prints one JSON line.
@@ -60,7 +67,8 @@ import workloads  # noqa: E402
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0       # dense bf16 MFMA, published
 I8_PEAK_TOPS = 5000.0           # dense int8 MFMA, published
-COPIES = 3
+COLD_BYTES = 512e6              # twice the 256 MB last-level cache
+COPIES_70B = 4
 
 
 class HipEvent:
@@ -98,10 +106,11 @@ class HipEvent:
         return ms.value
 
 
-
 def w4_kernel_name(M, N, dev):
-    """Which W4A16 MFMA kernel the library picks for M tokens and N weight rows
+    """Which W4A16 kernel the library picks for M tokens and N weight rows
     (the rule in w4a16.hip's launchers), for labelling only."""
+    if M <= 2:
+        return "gemv_valu_kernel"
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     cdiv = lambda a, b: -(-a // b)
     mt = cdiv(M, 16)
@@ -113,186 +122,247 @@ def w4_kernel_name(M, N, dev):
         return "w4_tile_kernel"
     return "w4_lds_kernel"
 
+
+def w8_kernel_name(B):
+    """w8a16_gemv's dispatch: vector ALUs for one or two tokens, matrix cores from three."""
+    return "w8_gemv_kernel" if B <= 2 else "w8_mfma_kernel"
+
+
 def w4_bytes(n, k):
     c, s, z = qmm.w4_sizes(n, k)
     return c + s + z
 
 
+def P(t):
+    return qmm._ptr(t)
+
+
+def S(t):
+    return qmm._stream(t)
+
+
+def ok(st):
+    assert st == 0, qmm.lib().qmm_status_string(st).decode()
+
+
+class Ops:
+    """The ordered ops of one step plus the buffers each reads and writes."""
+
+    def __init__(self):
+        self.ops = []
+
+    def add(self, name, fn, nbytes, bound, kernel, config, reads, writes=lambda i: [], flops=0, peak=None,
+            group=None):
+        self.ops.append(dict(name=name, fn=fn, bytes=nbytes, bound=bound, kernel=kernel, config=config,
+                             reads=reads, writes=writes, flops=flops, peak=peak, group=group))
+
+    def reuse_distances(self, steps=12, settle=4):
+        """Minimum over steady-state steps of the algorithmic traffic between
+        the last touch of any input of an op and the op itself."""
+        pos, last = 0, {}
+        dmin = {op["name"]: float("inf") for op in self.ops}
+        for i in range(steps):
+            for op in self.ops:
+                for b in op["reads"](i):
+                    if i >= settle and b in last:
+                        dmin[op["name"]] = min(dmin[op["name"]], pos - last[b])
+                pos += op["bytes"]
+                for b in list(op["reads"](i)) + list(op["writes"](i)):
+                    last[b] = pos
+        return dmin
+
+
+def quant_op(ops, lib, name, w, dt, n, k, outs, cfg, wkey, okey, kernel, sym=False):
+    """quantize_groupwise(_symmetric) of w into outs[i % len(outs)]."""
+    fn_c = lib.quantize_groupwise_symmetric if sym else lib.quantize_groupwise
+    elem = 4 if dt == qmm.F32 else 2
+
+    def run(i):
+        c, s, z = outs[i % len(outs)]
+        ok(fn_c(P(w), dt, n, k, 128, 4, P(c), P(s), P(z), S(w)))
+    ops.add(name, run, n * k * elem + w4_bytes(n, k), "hbm", kernel, cfg, reads=lambda i: [wkey],
+            writes=lambda i: [f"{okey}[{i % len(outs)}]"])
+
+
+def gemv_op(ops, lib, name, copies, sel, okey, n, k, x, y, B, xdt, cfg, xkey, group=None):
+    """w4a16_gemv on copy sel(i) of the packed weight."""
+    def run(i):
+        c, s, z = copies[sel(i)]
+        ok(lib.w4a16_gemv(P(c), P(s), P(z), n, k, 128, P(x), xdt, B, P(y), xdt, S(x)))
+    ops.add(name, run, w4_bytes(n, k) + B * k * 2 + B * n * 2, "hbm", w4_kernel_name(B, n, x.device), cfg,
+            reads=lambda i: [f"{okey}[{sel(i)}]", xkey], flops=2 * B * n * k, group=group)
+
+
 def build_ops(dev):
     """Allocate every input/output and return the ordered list of timed ops."""
-    ops = []
+    lib = qmm.lib()
+    ops = Ops()
+
+    # ---- 70B-class MLP matrices: quantizers and dequantizer ----------------
     wl5 = workloads.WORKLOADS["mlp70b"]
     mats = []
     for idx, (n, k) in enumerate(wl5.weights):
         w_cpu, _ = workloads.weight(wl5, idx)
         w = w_cpu.to(dev)
         del w_cpu
-        copies = [qmm.quantize_groupwise(w) for _ in range(COPIES)]
-        what = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
-        x1 = workloads.activations(wl5, 1, k, salt=idx).to(dev)
-        x8 = workloads.activations(wl5, 8, k, salt=idx).to(dev)
-        y1 = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
-        y8 = torch.empty((8, n), dtype=torch.bfloat16, device=dev)
-        mats.append(dict(n=n, k=k, w=w, copies=copies, what=what, x1=x1, x8=x8, y1=y1, y8=y8))
-    wb = w4_bytes  # shorthand
-
-    # Copy use per step i: the quantizer writes copy i%3, the dequantizer reads
-    # copy (i+2)%3, the GEMVs read copy (i+1)%3 (written two steps earlier).
+        copies = [qmm.quantize_groupwise(w) for _ in range(COPIES_70B)]
+        mats.append(dict(idx=idx, n=n, k=k, w=w, copies=copies, key=f"w4_70b{idx}"))
+    cfg5 = "70B-class MLP decode"
+    C = COPIES_70B
+    # copy use per step i: the quantizer writes i%4, the dequantizer reads
+    # (i+3)%4, the B=8 GEMV (i+1)%4 and the B=1 GEMV (i+2)%4, so between two
+    # uses of a copy there is at least a whole step of other traffic
     for m in mats:
-        n, k = m["n"], m["k"]
-        lib = qmm.lib()
-
-        def quant(i, m=m):
-            c, s, z = m["copies"][i % COPIES]
-            st = lib.quantize_groupwise(qmm._ptr(m["w"]), qmm.BF16, m["n"], m["k"], 128, 4, qmm._ptr(c),
-                                        qmm._ptr(s), qmm._ptr(z), qmm._stream(m["w"]))
-            assert st == 0, st
-        ops.append(dict(name=f"quantize {n}x{k}", fn=quant, bytes=n * k * 2 + wb(n, k), flops=0, bound="hbm",
-                        kernel="quantize_g128_lds_kernel"))
-
-    # Symmetric INT4 on the first matrix, into buffers of its own (same
-    # format; not part of quantize_GBps).
+        quant_op(ops, lib, f"quantize {m['n']}x{m['k']}", m["w"], qmm.BF16, m["n"], m["k"], m["copies"], cfg5,
+                 f"bf16_70b{m['idx']}", m["key"], "quantize_g128_lds_kernel")
     m0 = mats[0]
-    sym_out = qmm.quantize_groupwise(m0["w"], symmetric=True)
-
-    def quant_sym(i, m=m0):
-        c, s, z = sym_out
-        st = lib.quantize_groupwise_symmetric(qmm._ptr(m["w"]), qmm.BF16, m["n"], m["k"], 128, 4, qmm._ptr(c),
-                                              qmm._ptr(s), qmm._ptr(z), qmm._stream(m["w"]))
-        assert st == 0, st
-    ops.append(dict(name=f"quantize_symmetric {m0['n']}x{m0['k']}", fn=quant_sym,
-                    bytes=m0["n"] * m0["k"] * 2 + wb(m0["n"], m0["k"]), flops=0, bound="hbm",
-                    kernel="quantize_g128_lds_kernel (symmetric)"))
-
+    sym_out = [qmm.quantize_groupwise(m0["w"], symmetric=True)]
+    quant_op(ops, lib, f"quantize_symmetric {m0['n']}x{m0['k']}", m0["w"], qmm.BF16, m0["n"], m0["k"], sym_out, cfg5,
+             "bf16_70b0", "sym_70b0", "quantize_g128_lds_kernel (symmetric)", sym=True)
     for m in mats:
-        n, k = m["n"], m["k"]
+        m["what"] = torch.empty((m["n"], m["k"]), dtype=torch.bfloat16, device=dev)
 
         def deq(i, m=m):
-            c, s, z = m["copies"][(i + 2) % COPIES]
-            st = qmm.lib().dequantize(qmm._ptr(c), qmm._ptr(s), qmm._ptr(z), m["n"], m["k"], 128, 4,
-                                      qmm._ptr(m["what"]), qmm.BF16, qmm._stream(c))
-            assert st == 0, st
-        ops.append(dict(name=f"dequantize {n}x{k}", fn=deq, bytes=wb(n, k) + n * k * 2, flops=0, bound="hbm",
-                        kernel="dequantize_g128_kernel"))
+            c, s, z = m["copies"][(i + 3) % C]
+            ok(lib.dequantize(P(c), P(s), P(z), m["n"], m["k"], 128, 4, P(m["what"]), qmm.BF16, S(c)))
+        ops.add(f"dequantize {m['n']}x{m['k']}", deq, w4_bytes(m["n"], m["k"]) + m["n"] * m["k"] * 2, "hbm",
+                "dequantize_g128_kernel", cfg5, reads=lambda i, m=m: [f"{m['key']}[{(i + 3) % C}]"],
+                writes=lambda i, m=m: [f"what_70b{m['idx']}"])
 
-    # Batched GEMM.
+    # ---- single 512x512 fp32 weight: quantize, fp16 GEMV --------------------
+    wl1 = workloads.WORKLOADS["tiny"]
+    n1, k1 = wl1.weights[0]
+    w1 = workloads.weight(wl1, 0)[0].to(dev)
+    c1 = [qmm.quantize_groupwise(w1) for _ in range(2)]
+    x1 = workloads.activations(wl1, 1, k1).to(dev)
+    y1 = torch.empty((1, n1), dtype=torch.float16, device=dev)
+    cfg1 = "single 512x512 fp32 weight"
+    quant_op(ops, lib, f"quantize {n1}x{k1} fp32", w1, qmm.F32, n1, k1, c1, cfg1, "f32_tiny", "w4_tiny",
+             "quantize_g128_flat_kernel")
+    gemv_op(ops, lib, f"w4a16_gemv B=1 {n1}x{k1} fp16", c1, lambda i: (i + 1) % 2, "w4_tiny", n1, k1, x1, y1, 1,
+            qmm.F16, cfg1, "x_tiny")
+
+    # ---- Llama-7B-like decode layer: quantize, B=1 GEMV ----------------------
+    wl2 = workloads.WORKLOADS["llama7b"]
+    l7 = []
+    for idx, (n, k) in enumerate(wl2.weights):
+        w = workloads.weight(wl2, idx)[0].to(dev)
+        l7.append(dict(idx=idx, n=n, k=k, w=w, copies=[qmm.quantize_groupwise(w) for _ in range(2)],
+                       x=workloads.activations(wl2, 1, k, salt=idx).to(dev),
+                       y=torch.empty((1, n), dtype=torch.bfloat16, device=dev)))
+    cfg2 = "Llama-7B-like decode layer"
+    for m in l7:
+        quant_op(ops, lib, f"quantize {m['n']}x{m['k']}", m["w"], qmm.BF16, m["n"], m["k"], m["copies"], cfg2,
+                 f"bf16_l7{m['idx']}", f"w4_l7{m['idx']}", "quantize_g128_lds_kernel")
+    for m in l7:
+        gemv_op(ops, lib, f"w4a16_gemv B=1 {m['n']}x{m['k']}", m["copies"], lambda i: (i + 1) % 2,
+                f"w4_l7{m['idx']}", m["n"], m["k"], m["x"], m["y"], 1, qmm.BF16, cfg2, f"x_l7{m['idx']}")
+
+    # ---- batched W4A16 GEMM: quantize, M = 16 / 64 / 256 ---------------------
     wl3 = workloads.WORKLOADS["gemm"]
     n3, k3 = wl3.weights[0]
-    w3, _ = workloads.weight(wl3, 0)
-    w3d = w3.to(dev)
-    g3 = [qmm.quantize_groupwise(w3d) for _ in range(COPIES)]
-    del w3d
-    for M in wl3.batches:
+    w3 = workloads.weight(wl3, 0)[0].to(dev)
+    g3 = [qmm.quantize_groupwise(w3) for _ in range(3)]
+    q3 = [qmm.quantize_groupwise(w3)]
+    cfg3 = "batched W4A16 GEMM 14336x4096"
+    quant_op(ops, lib, f"quantize {n3}x{k3}", w3, qmm.BF16, n3, k3, q3, cfg3, "bf16_gemm", "w4_gemm_q",
+             "quantize_g128_lds_kernel")
+    for j, M in enumerate(wl3.batches):
         X = workloads.activations(wl3, M, k3).to(dev)
         Y = torch.empty((M, n3), dtype=torch.bfloat16, device=dev)
 
-        def gemm(i, X=X, Y=Y, M=M):
-            c, s, z = g3[i % COPIES]
-            st = qmm.lib().w4a16_gemm(qmm._ptr(c), qmm._ptr(s), qmm._ptr(z), n3, k3, 128, qmm._ptr(X), qmm.BF16, M,
-                                      qmm._ptr(Y), qmm.BF16, qmm._stream(X))
-            assert st == 0, st
-        bound = "mfma" if M >= 128 else "hbm"
-        ops.append(dict(name=f"w4a16_gemm M={M} {n3}x{k3}", fn=gemm, bytes=wb(n3, k3) + M * k3 * 2 + M * n3 * 2,
-                        flops=2 * M * n3 * k3, bound=bound, kernel=w4_kernel_name(M, n3, dev)))
+        def gemm(i, X=X, Y=Y, M=M, j=j):
+            c, s, z = g3[(i + j) % 3]
+            ok(lib.w4a16_gemm(P(c), P(s), P(z), n3, k3, 128, P(X), qmm.BF16, M, P(Y), qmm.BF16, S(X)))
+        ops.add(f"w4a16_gemm M={M} {n3}x{k3}", gemm, w4_bytes(n3, k3) + M * k3 * 2 + M * n3 * 2,
+                "mfma" if M >= 128 else "hbm", w4_kernel_name(M, n3, dev), cfg3,
+                reads=lambda i, j=j, M=M: [f"w4_gemm[{(i + j) % 3}]", f"x_gemm{M}"], flops=2 * M * n3 * k3)
 
-    # SmoothQuant W8A8.
+    # ---- SmoothQuant W8A8 ---------------------------------------------------
     wl4 = workloads.WORKLOADS["smoothquant"]
     n4, k4 = wl4.weights[0]
     m4 = wl4.batches[0]
     x4c, _ = workloads.sq_activations(wl4, m4, k4)
     w4c, _ = workloads.weight(wl4, 0)
-    x4, w4 = x4c.to(dev), w4c.to(dev)
+    x4 = [x4c.to(dev) for _ in range(3)]        # factors, per-tensor quantizer, online call
+    w4 = [w4c.to(dev) for _ in range(2)]        # factors, weight quantizer
+    cfg4 = "SmoothQuant W8A8 2048x4096x4096"
     smooth = torch.empty(k4, dtype=torch.float32, device=dev)
     cx, cw = torch.empty_like(smooth), torch.empty_like(smooth)
-    qw = torch.empty((n4, k4), dtype=torch.int8, device=dev)
-    wsc = torch.empty(n4, dtype=torch.float32, device=dev)
-    y4 = torch.empty((m4, n4), dtype=torch.bfloat16, device=dev)
+    ok(lib.sq_smooth_factors(P(x4[0]), qmm.BF16, m4, P(w4[0]), qmm.BF16, n4, k4, 0.5, P(cx), P(cw), P(smooth),
+                             S(x4[0])))
+    # each reader of the smoothing factors has its own copy of them
+    sm_w, sm_a, sm_o = smooth.clone(), smooth.clone(), smooth.clone()
+    qw_out = torch.empty((n4, k4), dtype=torch.int8, device=dev)
+    wsc_out = torch.empty(n4, dtype=torch.float32, device=dev)
+    qw_a, wsc_a = qmm.sq_quantize_weight(w4[1], smooth)        # read by the INT8 GEMM alone
+    qw_b, wsc_b = qmm.sq_quantize_weight(w4[1], smooth)        # read by the online call
+    qx_pre, xsc_pre = qmm.sq_quantize_activation(x4[0], smooth)
+    qx_t = torch.empty((m4, k4), dtype=torch.int8, device=dev)
+    xsc_t = torch.empty(m4, dtype=torch.float32, device=dev)
+    y4a = torch.empty((m4, n4), dtype=torch.bfloat16, device=dev)
+    y4b = torch.empty((m4, n4), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(qmm.sq_workspace_bytes(m4, k4), dtype=torch.uint8, device=dev)
-    lib = qmm.lib()
 
     def sq_factors(i):
-        st = lib.sq_smooth_factors(qmm._ptr(x4), qmm.BF16, m4, qmm._ptr(w4), qmm.BF16, n4, k4, 0.5, qmm._ptr(cx),
-                                   qmm._ptr(cw), qmm._ptr(smooth), qmm._stream(x4))
-        assert st == 0, st
+        ok(lib.sq_smooth_factors(P(x4[0]), qmm.BF16, m4, P(w4[0]), qmm.BF16, n4, k4, 0.5, P(cx), P(cw), P(smooth),
+                                 S(x4[0])))
 
     def sq_weight(i):
-        st = lib.sq_quantize_weight(qmm._ptr(w4), qmm.BF16, qmm._ptr(smooth), n4, k4, qmm._ptr(qw), qmm._ptr(wsc),
-                                    qmm._stream(w4))
-        assert st == 0, st
-
-    def sq_online(i):
-        st = lib.smooth_quant_w8a8_gemm(qmm._ptr(x4), qmm.BF16, qmm._ptr(smooth), qmm._ptr(qw), qmm._ptr(wsc), m4,
-                                        n4, k4, qmm._ptr(y4), qmm.BF16, qmm._ptr(ws), ws.numel(), qmm._stream(x4))
-        assert st == 0, st
-
-    ops.append(dict(name=f"sq_smooth_factors {m4}x{k4} / {n4}x{k4}", fn=sq_factors,
-                    bytes=(m4 + n4) * k4 * 2 + 3 * k4 * 4, flops=0, bound="hbm", kernel="colmax2_kernel"))
-    ops.append(dict(name=f"sq_quantize_weight {n4}x{k4}", fn=sq_weight, bytes=n4 * k4 * 3 + k4 * 4 + n4 * 4,
-                    flops=0, bound="hbm", kernel="rowquant8_kernel"))
-    # The INT8 GEMM alone, on weights and activations quantized once here
-    # (untimed; every step recomputes the same smoothing and weights).
-    qx4 = torch.empty((m4, k4), dtype=torch.int8, device=dev)
-    xsc4 = torch.empty(m4, dtype=torch.float32, device=dev)
-    sq_factors(0)
-    sq_weight(0)
-    assert lib.sq_quantize_activation(qmm._ptr(x4), qmm.BF16, qmm._ptr(smooth), m4, k4, qmm._ptr(qx4),
-                                      qmm._ptr(xsc4), qmm._stream(x4)) == 0
-
-    def sq_gemm(i):
-        st = lib.sq_int8_gemm(qmm._ptr(qx4), qmm._ptr(xsc4), qmm._ptr(qw), qmm._ptr(wsc), m4, n4, k4, qmm._ptr(y4),
-                              qmm.BF16, qmm._stream(x4))
-        assert st == 0, st
-
-    qx4t = torch.empty((m4, k4), dtype=torch.int8, device=dev)
-    xsc4t = torch.empty(m4, dtype=torch.float32, device=dev)
+        ok(lib.sq_quantize_weight(P(w4[1]), qmm.BF16, P(sm_w), n4, k4, P(qw_out), P(wsc_out), S(w4[1])))
 
     def sq_act_tensor(i):
-        st = lib.sq_quantize_activation_per_tensor(qmm._ptr(x4), qmm.BF16, qmm._ptr(smooth), m4, k4, qmm._ptr(qx4t),
-                                                   qmm._ptr(xsc4t), qmm._stream(x4))
-        assert st == 0, st
+        ok(lib.sq_quantize_activation_per_tensor(P(x4[1]), qmm.BF16, P(sm_a), m4, k4, P(qx_t), P(xsc_t),
+                                                 S(x4[1])))
 
-    ops.append(dict(name=f"sq_quantize_activation_per_tensor {m4}x{k4}", fn=sq_act_tensor,
-                    bytes=2 * m4 * k4 * 2 + k4 * 4 + m4 * k4 + m4 * 4, flops=0, bound="hbm",
-                    kernel="rowquant8_kernel x2 + tensor_scale_kernel"))
-    ops.append(dict(name=f"sq_int8_gemm {m4}x{n4}x{k4}", fn=sq_gemm,
-                    bytes=m4 * k4 + m4 * 4 + n4 * k4 + n4 * 4 + m4 * n4 * 2,
-                    flops=2 * m4 * n4 * k4, bound="mfma", kernel="i8_gemm_kernel", peak=I8_PEAK_TOPS))
-    ops.append(dict(name=f"smooth_quant_w8a8_gemm {m4}x{n4}x{k4}", fn=sq_online,
-                    bytes=m4 * k4 * 2 + k4 * 4 + (m4 * k4 + m4 * 4) * 2 + n4 * k4 + n4 * 4 + m4 * n4 * 2,
-                    flops=2 * m4 * n4 * k4, bound="mfma", kernel="i8_gemm_kernel + rowquant8_kernel", peak=I8_PEAK_TOPS))
-    # Decode GEMVs last, back to back (B=8 then B=1), after the read-mostly
-    # GEMMs: in a decode step a GEMV follows other matmuls, not the
-    # dequantizer's ~0.9 GB of writes, whose write-back would overlap it.
-    for B in (8, 1):
+    def sq_gemm(i):
+        ok(lib.sq_int8_gemm(P(qx_pre), P(xsc_pre), P(qw_a), P(wsc_a), m4, n4, k4, P(y4a), qmm.BF16, S(qx_pre)))
+
+    def sq_online(i):
+        ok(lib.smooth_quant_w8a8_gemm(P(x4[2]), qmm.BF16, P(sm_o), P(qw_b), P(wsc_b), m4, n4, k4, P(y4b), qmm.BF16,
+                                      P(ws), ws.numel(), S(x4[2])))
+
+    ops.add(f"sq_smooth_factors {m4}x{k4} / {n4}x{k4}", sq_factors, (m4 + n4) * k4 * 2 + 3 * k4 * 4, "hbm",
+            "colmax2_kernel + smooth_finalize_kernel", cfg4, reads=lambda i: ["x4[0]", "w4[0]"],
+            writes=lambda i: ["smooth"])
+    ops.add(f"sq_quantize_weight {n4}x{k4}", sq_weight, n4 * k4 * 3 + k4 * 4 + n4 * 4, "hbm", "rowquant8_kernel",
+            cfg4, reads=lambda i: ["w4[1]", "sm_w"], writes=lambda i: ["qw_out"])
+    ops.add(f"sq_quantize_activation_per_tensor {m4}x{k4}", sq_act_tensor,
+            2 * m4 * k4 * 2 + k4 * 4 + m4 * k4 + m4 * 4, "hbm", "rowquant8_kernel x2 + tensor_scale_kernel", cfg4,
+            reads=lambda i: ["x4[1]", "sm_a"], writes=lambda i: ["qx_t"])
+    ops.add(f"sq_int8_gemm {m4}x{n4}x{k4}", sq_gemm, m4 * k4 + m4 * 4 + n4 * k4 + n4 * 4 + m4 * n4 * 2, "mfma",
+            "i8_gemm_kernel", cfg4, reads=lambda i: ["qx_pre", "qw_a"], writes=lambda i: ["y4a"],
+            flops=2 * m4 * n4 * k4, peak=I8_PEAK_TOPS)
+    ops.add(f"smooth_quant_w8a8_gemm {m4}x{n4}x{k4}", sq_online,
+            m4 * k4 * 2 + k4 * 4 + (m4 * k4 + m4 * 4) * 2 + n4 * k4 + n4 * 4 + m4 * n4 * 2, "mfma",
+            "rowquant8_kernel + i8_gemm_kernel", cfg4, reads=lambda i: ["x4[2]", "qw_b", "sm_o"],
+            writes=lambda i: ["y4b"], flops=2 * m4 * n4 * k4, peak=I8_PEAK_TOPS)
+
+    # ---- 70B-class MLP decode: W4A16 B=8 then B=1, then W8A16 --------------
+    for m in mats:
+        for B in (1, 8):
+            for use in ("w4", "w8"):
+                m[f"x{B}{use}"] = workloads.activations(wl5, B, m["k"], salt=m["idx"]).to(dev)
+                m[f"y{B}{use}"] = torch.empty((B, m["n"]), dtype=torch.bfloat16, device=dev)
+    for B, sel in ((8, lambda i: (i + 1) % C), (1, lambda i: (i + 2) % C)):
         for m in mats:
-            n, k = m["n"], m["k"]
-
-            def gemv(i, m=m, B=B):
-                c, s, z = m["copies"][(i + 1) % COPIES]
-                x, y = m[f"x{B}"], m[f"y{B}"]
-                st = qmm.lib().w4a16_gemv(qmm._ptr(c), qmm._ptr(s), qmm._ptr(z), m["n"], m["k"], 128, qmm._ptr(x),
-                                          qmm.BF16, B, qmm._ptr(y), qmm.BF16, qmm._stream(x))
-                assert st == 0, st
-            ops.append(dict(name=f"w4a16_gemv B={B} {n}x{k}", fn=gemv, bytes=wb(n, k) + B * k * 2 + B * n * 2,
-                            flops=2 * B * n * k, bound="hbm",
-                            kernel="gemv_valu_kernel" if B == 1 else w4_kernel_name(B, n, dev),
-                            group="gemv_b1" if B == 1 else None))
-    # Weight-only INT8 decode on the same matrices (per-channel codes from
-    # the on-device quantizer), after the INT4 GEMVs.
-    for B in (1, 8):
+            gemv_op(ops, lib, f"w4a16_gemv B={B} {m['n']}x{m['k']}", m["copies"], sel, m["key"], m["n"], m["k"],
+                    m[f"x{B}w4"], m[f"y{B}w4"], B, qmm.BF16, cfg5, f"x{B}w4_70b{m['idx']}",
+                    group="gemv_b1" if B == 1 else None)
+    # weight-only INT8 on the same matrices: per-channel codes from the
+    # on-device quantizer, one copy for B=1 and one for B=8
+    for m in mats:
+        m["q8"] = [qmm.sq_quantize_weight(m["w"]) for _ in range(2)]
+    for j, B in enumerate((1, 8)):
         for m in mats:
-            n, k = m["n"], m["k"]
-            if "q8" not in m:
-                m["q8"], m["b8"] = qmm.sq_quantize_weight(m["w"])
-
-            def w8(i, m=m, B=B):
-                x, y = m[f"x{B}"], m[f"y{B}"]
-                st = qmm.lib().w8a16_gemv(qmm._ptr(m["q8"]), qmm._ptr(m["b8"]), m["n"], m["k"], qmm._ptr(x),
-                                          qmm.BF16, B, qmm._ptr(y), qmm.BF16, qmm._stream(x))
-                assert st == 0, st
-            ops.append(dict(name=f"w8a16_gemv B={B} {n}x{k}", fn=w8, bytes=n * k + n * 4 + B * k * 2 + B * n * 2,
-                            flops=2 * B * n * k, bound="hbm", kernel="w8_gemv_kernel"))
-
+            def w8(i, m=m, B=B, j=j):
+                q, b = m["q8"][j]
+                ok(lib.w8a16_gemv(P(q), P(b), m["n"], m["k"], P(m[f"x{B}w8"]), qmm.BF16, B, P(m[f"y{B}w8"]),
+                                  qmm.BF16, S(q)))
+            ops.add(f"w8a16_gemv B={B} {m['n']}x{m['k']}", w8,
+                    m["n"] * m["k"] + m["n"] * 4 + B * m["k"] * 2 + B * m["n"] * 2, "hbm", w8_kernel_name(B), cfg5,
+                    reads=lambda i, m=m, j=j, B=B: [f"w8_70b{m['idx']}[{j}]", f"x{B}w8_70b{m['idx']}"],
+                    flops=2 * B * m["n"] * m["k"])
     return ops, mats
 
 
@@ -313,8 +383,19 @@ def gemv_traffic():
     return round(sum(v["hbm_read_bytes"] + v["hbm_write_bytes"] for v in launches) / len(launches))
 
 
-def cpu_baseline(mats, min_seconds=12.0, max_reps=40):
-    """The CPU oracle's B=1 product for both 70B-class matrices, timed on the host."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(min_seconds=(8.0, 6.0), max_reps=40):
+    """The CPU oracle's B=1 product (dequantize + fp64 dot products) for both
+    70B-class matrices on the host: the serial oracle, then its OpenMP build."""
     import oracle  # test infrastructure: only this baseline leg uses it
 
     wl5 = workloads.WORKLOADS["mlp70b"]
@@ -325,18 +406,31 @@ def cpu_baseline(mats, min_seconds=12.0, max_reps=40):
         del w_cpu
         x = workloads.activations(wl5, 1, k, salt=idx).float().numpy()
         cases.append((q, s, z, x, w4_bytes(n, k) + k * 2 + n * 2))
-    reps, elapsed, nbytes = 0, 0.0, 0
-    while reps < max_reps and (elapsed < min_seconds or reps == 0):
-        for q, s, z, x, b in cases:
-            t0 = time.perf_counter()
-            oracle.w4a16_reference(x, q, s, z)
-            elapsed += time.perf_counter() - t0
-            nbytes += b
-        reps += 1
-    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+
+    def leg(parallel, budget):
+        reps, elapsed, nbytes = 0, 0.0, 0
+        while reps < max_reps and (elapsed < budget or reps == 0):
+            for q, s, z, x, b in cases:
+                t0 = time.perf_counter()
+                oracle.w4a16_reference(x, q, s, z, parallel=parallel)
+                elapsed += time.perf_counter() - t0
+                nbytes += b
+            reps += 1
+        return nbytes / elapsed / 1e9, reps, elapsed
+
+    serial, r1, e1 = leg(False, min_seconds[0])
+    par, r2, e2 = leg(True, min_seconds[1])
+    threads = oracle.threads(parallel=True)
+    model = cpu_model()
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"value": round(par, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"plain-C oracle W4A16 B=1 reference (dequantize + fp64 product) on both 70B-class MLP "
-                      f"matrices (28672x8192 and 8192x28672), {reps} repetition(s), {elapsed:.1f} s, one thread "
-                      f"of {os.cpu_count()} ({platform.processor() or platform.machine()})"}
+                      f"matrices (28672x8192 and 8192x28672): OpenMP build (output rows split over {threads} "
+                      f"threads, results bit-identical to the serial oracle) {r2} repetition(s) in {e2:.1f} s; "
+                      f"host {model}, {nproc} CPUs available",
+            "single_thread": {"value": round(serial, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"the serial oracle, {r1} repetition(s) in {e1:.1f} s"},
+            "cpu_model": model, "nproc": nproc}
 
 
 def main():
@@ -365,7 +459,12 @@ def main():
                           "copies": 5}), flush=True)
         return
     print("bench: generating inputs and quantizing (untimed)", file=sys.stderr, flush=True)
-    ops, mats = build_ops(dev)
+    table, mats = build_ops(dev)
+    ops = table.ops
+    reuse = table.reuse_distances()
+    warm = [o["name"] for o in ops if o["bound"] == "hbm" and reuse[o["name"]] < COLD_BYTES]
+    if warm:
+        raise SystemExit(f"bench: these HBM-bound ops would read cache-warm operands: {warm}")
     torch.cuda.synchronize()
 
     # Ops of a group (the two B=1 GEMVs) run back to back between one pair of
@@ -386,8 +485,7 @@ def main():
             if events is not None and last_of_group(j):
                 events[j][1].record()
 
-    print(f"bench: {args.warmup} warmup + {args.steps} timed steps of {len(ops)} kernels",
-          file=sys.stderr, flush=True)
+    print(f"bench: {args.warmup} warmup + {args.steps} timed steps of {len(ops)} ops", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i, None)
     torch.cuda.synchronize()
@@ -401,6 +499,7 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    print("bench: timed steps done", file=sys.stderr, flush=True)
 
     breakdown = {}
     for j, op in enumerate(ops):
@@ -412,26 +511,32 @@ def main():
         size = j1 - j0 + 1
         ms = [per_step_events[i][j0][0].elapsed_time(per_step_events[i][j1][1]) / size for i in range(args.steps)]
         avg_us = 1e3 * float(np.mean(ms))
-        rec = {"kernel": op["kernel"], "avg_us": round(avg_us, 3), "median_us": round(1e3 * float(np.median(ms)), 3),
-               "alg_bytes": op["bytes"], "GBps": round(op["bytes"] / avg_us / 1e3, 2),
+        rec = {"config": op["config"], "kernel": op["kernel"], "avg_us": round(avg_us, 3),
+               "median_us": round(1e3 * float(np.median(ms)), 3), "alg_bytes": op["bytes"],
+               "GBps": round(op["bytes"] / avg_us / 1e3, 2),
                "hbm_frac": round(op["bytes"] / avg_us / 1e3 / HBM_PEAK_GBPS, 4)}
         if op["flops"]:
+            peak = op["peak"] or BF16_PEAK_TFLOPS
             rec["TFLOPs"] = round(op["flops"] / avg_us / 1e6, 2)
-            peak = op.get("peak", BF16_PEAK_TFLOPS)
             rec["mfma_frac"] = round(op["flops"] / avg_us / 1e6 / peak, 4)
         rec["bound"] = op["bound"]
+        rec["reuse_MB"] = round(reuse[op["name"]] / 1e6) if reuse[op["name"]] != float("inf") else None
         if size > 1:
             rec["timing"] = f"back to back with {size - 1} other launch(es), one event pair, time split evenly"
         breakdown[op["name"]] = rec
 
-    gemv1 = [k for k in breakdown if k.startswith("w4a16_gemv B=1")]
+    gemv1 = [k for k in breakdown if k.startswith("w4a16_gemv B=1 28672") or k.startswith("w4a16_gemv B=1 8192")]
     g_bytes = sum(breakdown[k]["alg_bytes"] for k in gemv1)
     g_us = sum(breakdown[k]["avg_us"] for k in gemv1)
     value = g_bytes / g_us / 1e3
-    quant = [k for k in breakdown if k.startswith("quantize ")]
-    q_gbps = sum(breakdown[k]["alg_bytes"] for k in quant) / sum(breakdown[k]["avg_us"] for k in quant) / 1e3
+
+    def gbps(prefixes):
+        ks = [k for k in breakdown if any(k.startswith(p) for p in prefixes)]
+        return round(sum(breakdown[k]["alg_bytes"] for k in ks) / sum(breakdown[k]["avg_us"] for k in ks) / 1e3, 2)
+
     sq = breakdown[[k for k in breakdown if k.startswith("smooth_quant_w8a8_gemm")][0]]
     i8 = breakdown[[k for k in breakdown if k.startswith("sq_int8_gemm")][0]]
+    gemm = {k.split()[1]: breakdown[k] for k in breakdown if k.startswith("w4a16_gemm")}
 
     result = {
         "metric": "W4A16 GEMV effective GB/s & % of HBM peak; quantize GB/s; INT8 GEMM TOPS",
@@ -449,23 +554,29 @@ def main():
         "config": {
             "workload": "70B-class MLP decode: W4A16 GEMV B=1 on INT4 group-128 28672x8192 and 8192x28672 "
                         "(bf16 activations, fp32 accumulation); the same step also runs their quantizer, "
-                        "dequantizer and B=8 GEMV, the 14336x4096 W4A16 GEMM at M=16/64/256 and the "
-                        "SmoothQuant W8A8 2048x4096x4096 path",
+                        "dequantizer, B=8 GEMV and W8A16 GEMV, the 512x512 fp32 and Llama-7B-like quantize + "
+                        "B=1 GEMV, the 14336x4096 quantize + W4A16 GEMM at M=16/64/256 and the SmoothQuant W8A8 "
+                        "2048x4096x4096 path",
             "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
-            "quantize_GBps": round(q_gbps, 2),
+            "quantize_GBps": gbps(["quantize 28672x8192", "quantize 8192x28672"]),
+            "quantize_GBps_llama7b": gbps(["quantize 4096x4096", "quantize 11008x4096"]),
+            "quantize_GBps_gemm_14336x4096": gbps(["quantize 14336x4096"]),
+            "gemv_b1_GBps_llama7b": gbps(["w4a16_gemv B=1 4096x4096", "w4a16_gemv B=1 11008x4096"]),
+            "gemm_TFLOPs": {k: v.get("TFLOPs") for k, v in gemm.items()},
             "int8_gemm_TOPS": i8.get("TFLOPs"),
             "w8a8_online_TOPS": sq.get("TFLOPs"),
-            "weight_copies_rotated": COPIES,
+            "weight_copies_rotated_70b": COPIES_70B,
+            "min_reuse_MB_hbm_ops": round(min(reuse[o["name"]] for o in ops if o["bound"] == "hbm") / 1e6),
         },
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": gemv_traffic(),
                      "alg_bytes_per_launch": round(g_bytes / len(gemv1)),
-                     "kernel": "gemv_valu_kernel (w4a16_gemv B=1), both matrices"},
+                     "kernel": "gemv_valu_kernel (w4a16_gemv B=1), both 70B-class matrices"},
         "breakdown": breakdown,
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(mats)
+        result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
 
 

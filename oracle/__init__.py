@@ -21,26 +21,33 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmm_oracle.c")
 _LIB = os.path.join(_HERE, "libqmm_oracle.so")
+_LIB_OMP = os.path.join(_HERE, "libqmm_oracle_omp.so")
 
-GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-std=c99", "-Wall"]
+GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-std=c99", "-Wall",
+             "-Wno-unknown-pragmas"]
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (no FMA contraction, no fast-math)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = False, parallel: bool = False) -> str:
+    """Compile the oracle with gcc (no FMA contraction, no fast-math).
+    parallel=True builds the timing-only variant with the row loops of the
+    dequantizer and the matmul reference split over OpenMP threads."""
+    path = _LIB_OMP if parallel else _LIB
+    if force or not os.path.exists(path):
+        tmp = path + ".tmp"
+        subprocess.check_call(["gcc", *GCC_FLAGS, *(["-fopenmp"] if parallel else []), "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, path)
+    return path
 
 
 _lib = None
+_lib_omp = None
 
 
-def lib() -> ctypes.CDLL:
-    global _lib
-    if _lib is None:
-        _lib = ctypes.CDLL(build())
+def lib(parallel: bool = False) -> ctypes.CDLL:
+    """The oracle library; parallel=True the OpenMP build (timing only)."""
+    global _lib, _lib_omp
+    if (_lib_omp if parallel else _lib) is None:
+        l = ctypes.CDLL(build(parallel=parallel))
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         F = ctypes.c_float
         sigs = {
@@ -57,12 +64,17 @@ def lib() -> ctypes.CDLL:
             "oq_smooth_factors": [P, P, I64, F, P],
             "oq_scale_columns_mul": [P, P, I64, I64, P],
             "oq_scale_columns_div": [P, P, I64, I64, P],
+            "oq_threads": [],
         }
         for name, argtypes in sigs.items():
-            fn = getattr(_lib, name)
+            fn = getattr(l, name)
             fn.argtypes = argtypes
             fn.restype = ctypes.c_int
-    return _lib
+        if parallel:
+            _lib_omp = l
+        else:
+            _lib = l
+    return _lib_omp if parallel else _lib
 
 
 def _p(a: np.ndarray) -> ctypes.c_void_p:
@@ -101,13 +113,13 @@ def asym_quantize(w, group: int = 128, bits: int = 4) -> Tuple[np.ndarray, np.nd
     return q, s, z
 
 
-def asym_dequantize(q, s, z, group: int = 128) -> np.ndarray:
+def asym_dequantize(q, s, z, group: int = 128, parallel: bool = False) -> np.ndarray:
     q = np.ascontiguousarray(q, np.uint8)
     s = _f32(s)
     z = np.ascontiguousarray(z, np.uint8)
     rows, cols = q.shape
     out = np.empty((rows, cols), np.float32)
-    _check(lib().oq_asym_dequantize(_p(q), _p(s), _p(z), rows, cols, group, _p(out)), "asym_dequantize")
+    _check(lib(parallel).oq_asym_dequantize(_p(q), _p(s), _p(z), rows, cols, group, _p(out)), "asym_dequantize")
     return out
 
 
@@ -182,7 +194,7 @@ def sym_dequantize(q, s, group: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Matmul references.
 # --------------------------------------------------------------------------
-def matmul_nt_f64(a, b) -> np.ndarray:
+def matmul_nt_f64(a, b, parallel: bool = False) -> np.ndarray:
     """C = A B^T summed in fp64 (A [M,K], B [N,K])."""
     a = _f32(a)
     b = _f32(b)
@@ -192,13 +204,19 @@ def matmul_nt_f64(a, b) -> np.ndarray:
     n, k2 = b.shape
     assert k == k2
     c = np.empty((m, n), np.float64)
-    _check(lib().oq_matmul_nt_f64(_p(a), _p(b), m, n, k, _p(c)), "matmul_nt_f64")
+    _check(lib(parallel).oq_matmul_nt_f64(_p(a), _p(b), m, n, k, _p(c)), "matmul_nt_f64")
     return c
 
 
-def w4a16_reference(x, q, s, z, group: int = 128) -> np.ndarray:
-    """y[b, n] = sum_k x[b, k] * w_hat[n, k] with w_hat = (q - z) s, summed in fp64."""
-    return matmul_nt_f64(x, asym_dequantize(q, s, z, group))
+def w4a16_reference(x, q, s, z, group: int = 128, parallel: bool = False) -> np.ndarray:
+    """y[b, n] = sum_k x[b, k] * w_hat[n, k] with w_hat = (q - z) s, summed in fp64.
+    parallel=True runs the OpenMP build (same loops per output, timing only)."""
+    return matmul_nt_f64(x, asym_dequantize(q, s, z, group, parallel), parallel)
+
+
+def threads(parallel: bool = True) -> int:
+    """Threads the row loops of the given build use."""
+    return int(lib(parallel).oq_threads())
 
 
 def w8a16_reference(x, qw, b) -> np.ndarray:

@@ -7,7 +7,11 @@
  *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fPIC -shared (x86-64 SSE
  * scalar float, so every float expression below is one IEEE binary32 operation
- * rounded to nearest-even; no FMA contraction).
+ * rounded to nearest-even; no FMA contraction).  The same file built with
+ * -fopenmp gives the timing-only all-cores variant: the `omp parallel for`
+ * lines split the independent output rows of the dequantizer and of the
+ * matmul reference across threads (each output is still computed by the same
+ * sequential loop, so results are identical); the serial build ignores them.
  *
  * Sources (page title, then section / slide / equation):
  *  [HQ]  "How quantization works" (AI-infra handbook): "The math of
@@ -45,45 +49,117 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define OQ_OK 0
 #define OQ_BAD_ARG (-1)
 #define OQ_OVERFLOW (-2)
 
 /* ------------------------------------------------------------------------ */
-/* Asymmetric (affine) quantization, one (scale, zero-point) per group of    */
-/* `group` consecutive elements along a row.  [HQ] "The math of              */
-/* quantization" (asymmetric form); [QE] "Scale and Zero-Point": s = (max -  */
-/* min) / (2^b - 1), z = round(-min / s); [QE] "Uniform Affine               */
-/* Quantization" and "Manual Group-Wise Quantizer": q = clamp(round(w / s) + */
-/* z, 0, 2^b - 1).  group == cols gives per-channel; a single row with       */
-/* group == cols gives per-tensor ([HQ] "Granularity").                      */
-/* Outputs: q[rows*cols] codes (unpacked, one per byte), scales and zeros    */
-/* [rows * (cols / group)].                                                  */
+/* binary16 storage of a scale ([HQ] Exercise 2 and [QS] "Where to put the   */
+/* scales" count one 16-bit scale per group).  Conversion from fp32 by the    */
+/* IEEE 754 definition: round to nearest, ties to even, in the subnormal      */
+/* range too; magnitudes at or above the largest finite binary16 (65504)      */
+/* saturate to it (reading R24).  Input finite.                               */
 /* ------------------------------------------------------------------------ */
-int oq_asym_quantize(const float* w, int64_t rows, int64_t cols, int64_t group, int bits,
-                     uint8_t* q, float* scales, uint8_t* zeros)
+uint16_t oq_f32_to_f16_bits(float f)
+{
+    const uint16_t sign = signbit(f) ? 0x8000u : 0u;
+    double a = fabs((double)f);
+    if (a >= 65504.0) return (uint16_t)(sign | 0x7BFFu);
+    if (a < ldexp(1.0, -14)) {                       /* subnormal: units of 2^-24 */
+        double r = nearbyint(a * ldexp(1.0, 24));    /* exact scaling, then RNE   */
+        return (uint16_t)(sign | (uint16_t)r);       /* r == 1024 is the smallest normal */
+    }
+    int ex;
+    frexp(a, &ex);                                   /* a = m 2^ex, m in [0.5, 1) */
+    int e = ex - 1;                                  /* a in [2^e, 2^(e+1))       */
+    double r = nearbyint(ldexp(a, 10 - e));          /* significand in [1024, 2048] */
+    if (r == 2048.0) {
+        r = 1024.0;
+        e += 1;
+    }
+    if (e > 15) return (uint16_t)(sign | 0x7BFFu);
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(r - 1024.0));
+}
+
+float oq_f16_bits_to_f32(uint16_t h)
+{
+    const int e = (h >> 10) & 0x1F;
+    const int m = h & 0x3FF;
+    double v = (e == 0) ? ldexp((double)m, -24) : ldexp((double)(1024 + m), e - 25);
+    return (float)((h & 0x8000u) ? -v : v);          /* exact: 11 significant bits */
+}
+
+/* A scale kept in 16 bits: the binary16 value of s, and 1 when that is 0     */
+/* (the [QS] listing's rule for an unusable scale, applied to the stored one; */
+/* reading R24).                                                              */
+static float f16_scale(float s)
+{
+    float s16 = oq_f16_bits_to_f32(oq_f32_to_f16_bits(s));
+    if (s16 == 0.0f) s16 = 1.0f;
+    return s16;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Group-wise quantization, one (scale, zero-point) per group of `group`     */
+/* consecutive elements along a row, `bits` bits per code.                   */
+/* Asymmetric (affine): [HQ] "The math of quantization" (asymmetric form);   */
+/* [QE] "Scale and Zero-Point": s = (max - min) / (2^b - 1), z = round(-min  */
+/* / s); [QE] "Uniform Affine Quantization" and "Manual Group-Wise           */
+/* Quantizer": q = clamp(round(w / s) + z, 0, 2^b - 1).                      */
+/* Symmetric: [HQ] "The math of quantization": s = max|w| / (2^(b-1) - 1)    */
+/* (absmax floored at 1e-8, R8), q = clamp(round(w / s), -2^(b-1),           */
+/* 2^(b-1) - 1), stored as the code q + 2^(b-1) with that zero-point (R22).  */
+/* scale_f16: the scale is stored in binary16 and the codes are computed     */
+/* with the stored value ([HQ] Exercise 2; [QS] "Where to put the scales").  */
+/* group == cols gives per-channel; a single row with group == cols gives    */
+/* per-tensor ([HQ] "Granularity").                                          */
+/* Outputs: q[rows*cols] codes (unpacked, one per byte), scales (the stored  */
+/* value, as float) and zeros [rows * (cols / group)].                       */
+/* ------------------------------------------------------------------------ */
+int oq_quantize_format(const float* w, int64_t rows, int64_t cols, int64_t group, int bits, int symmetric,
+                       int scale_f16, uint8_t* q, float* scales, uint8_t* zeros)
 {
     if (!w || !q || !scales || !zeros || rows < 0 || cols < 0 || group <= 0 || cols % group != 0 ||
-        bits < 1 || bits > 8)
+        bits < 2 || bits > 8)
         return OQ_BAD_ARG;
     const int64_t groups_per_row = cols / group;
     const float qmax = (float)((1 << bits) - 1);
+    const float half = (float)(1 << (bits - 1));
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t g = 0; g < groups_per_row; ++g) {
             const float* v = w + r * cols + g * group;
-            /* R1: the range always contains 0. */
-            float lo = 0.0f, hi = 0.0f;
-            for (int64_t i = 0; i < group; ++i) {
-                if (v[i] < lo) lo = v[i];
-                if (v[i] > hi) hi = v[i];
+            float s, zf;
+            if (!symmetric) {
+                /* R1: the range always contains 0. */
+                float lo = 0.0f, hi = 0.0f;
+                for (int64_t i = 0; i < group; ++i) {
+                    if (v[i] < lo) lo = v[i];
+                    if (v[i] > hi) hi = v[i];
+                }
+                float range = hi - lo;           /* one fp32 subtraction */
+                s = range / qmax;                /* one fp32 division    */
+                if (s == 0.0f) s = 1.0f;         /* R2 */
+                if (scale_f16) s = f16_scale(s);
+                float neg_lo = -lo;
+                zf = rintf(neg_lo / s);          /* R3, R5 */
+                /* beyond the code range only when a 16-bit scale saturated */
+                if (scale_f16 && zf > qmax) zf = qmax;
+                if (zf < 0.0f || zf > qmax) return OQ_BAD_ARG;  /* impossible under R1 */
+            } else {
+                float amax = 0.0f;
+                for (int64_t i = 0; i < group; ++i) {
+                    float a = fabsf(v[i]);
+                    if (a > amax) amax = a;
+                }
+                if (amax < 1e-8f) amax = 1e-8f;  /* R8 */
+                s = amax / (half - 1.0f);
+                if (scale_f16) s = f16_scale(s);
+                zf = half;                       /* R22 */
             }
-            float range = hi - lo;           /* one fp32 subtraction */
-            float s = range / qmax;          /* one fp32 division    */
-            if (s == 0.0f) s = 1.0f;         /* R2 */
-            float neg_lo = -lo;
-            float zf = rintf(neg_lo / s);    /* R3, R5 */
-            if (zf < 0.0f || zf > qmax) return OQ_BAD_ARG;  /* impossible under R1 */
             int z = (int)zf;
             scales[r * groups_per_row + g] = s;
             zeros[r * groups_per_row + g] = (uint8_t)z;
@@ -98,6 +174,14 @@ int oq_asym_quantize(const float* w, int64_t rows, int64_t cols, int64_t group, 
     return OQ_OK;
 }
 
+/* The asymmetric quantizer with fp32 scales (the format of every workload). */
+int oq_asym_quantize(const float* w, int64_t rows, int64_t cols, int64_t group, int bits,
+                     uint8_t* q, float* scales, uint8_t* zeros)
+{
+    if (bits < 2) return OQ_BAD_ARG;
+    return oq_quantize_format(w, rows, cols, group, bits, 0, 0, q, scales, zeros);
+}
+
 /* Dequantization w_hat = (q - z) * s, one fp32 rounding.  [QS] "Scale and   */
 /* zero-point"; [QE] "Uniform Affine Quantization".                          */
 int oq_asym_dequantize(const uint8_t* q, const float* scales, const uint8_t* zeros, int64_t rows,
@@ -105,6 +189,7 @@ int oq_asym_dequantize(const uint8_t* q, const float* scales, const uint8_t* zer
 {
     if (!q || !scales || !zeros || !out || group <= 0 || cols % group != 0) return OQ_BAD_ARG;
     const int64_t groups_per_row = cols / group;
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c) {
             int64_t gi = r * groups_per_row + c / group;
@@ -205,6 +290,30 @@ int oq_pack_codes(const uint8_t* vals, int64_t rows, int64_t count, uint8_t* out
 }
 
 /* ------------------------------------------------------------------------ */
+/* 3-bit codes: the row is a little-endian bit string, element i in bits     */
+/* 3i..3i+2, i.e. each run of 32 elements fills three 32-bit words.  (The    */
+/* pages count bits per weight, not an order; consecutive packing is the     */
+/* plain one.)  count must be a multiple of 32.                              */
+/* ------------------------------------------------------------------------ */
+int oq_pack_codes3(const uint8_t* vals, int64_t rows, int64_t count, uint8_t* out)
+{
+    if (!vals || !out || rows < 0 || count < 0 || count % 32 != 0) return OQ_BAD_ARG;
+    const int64_t row_bytes = count * 3 / 8;
+    for (int64_t r = 0; r < rows; ++r) {
+        uint8_t* o = out + r * row_bytes;
+        for (int64_t b = 0; b < row_bytes; ++b) o[b] = 0;
+        for (int64_t i = 0; i < count; ++i) {
+            uint32_t v = vals[r * count + i] & 7u;
+            for (int t = 0; t < 3; ++t) {
+                int64_t bit = 3 * i + t;
+                if (v >> t & 1u) o[bit / 8] |= (uint8_t)(1u << (bit % 8));
+            }
+        }
+    }
+    return OQ_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Reference product C[m][n] = sum_k A[m][k] * B[n][k] in fp64 (B is stored  */
 /* [N, K] like a weight matrix, so C = A B^T).  For the W4A16 matmuls A is   */
 /* the activations and B the dequantized weights: the plain definition of   */
@@ -214,6 +323,7 @@ int oq_pack_codes(const uint8_t* vals, int64_t rows, int64_t count, uint8_t* out
 int oq_matmul_nt_f64(const float* a, const float* b, int64_t m, int64_t n, int64_t k, double* c)
 {
     if (!a || !b || !c || m < 0 || n < 0 || k < 0) return OQ_BAD_ARG;
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t i = 0; i < m; ++i)
         for (int64_t j = 0; j < n; ++j) {
             double acc = 0.0;
@@ -305,4 +415,14 @@ int oq_scale_columns_div(const float* a, const float* s, int64_t rows, int64_t c
     for (int64_t i = 0; i < rows; ++i)
         for (int64_t j = 0; j < cols; ++j) out[i * cols + j] = a[i * cols + j] / s[j];
     return OQ_OK;
+}
+
+/* Threads the row loops above use: 1 in the serial build. */
+int oq_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
