@@ -65,6 +65,10 @@ def lib(parallel: bool = False) -> ctypes.CDLL:
             "oq_scale_columns_mul": [P, P, I64, I64, P],
             "oq_scale_columns_div": [P, P, I64, I64, P],
             "oq_threads": [],
+            "oq_quantize_format": [P, I64, I64, I64, I, I, I, P, P, P],
+            "oq_pack_codes3": [P, I64, I64, P],
+            "oq_f32_to_f16_array": [P, I64, P],
+            "oq_f16_to_f32_array": [P, I64, P],
         }
         for name, argtypes in sigs.items():
             fn = getattr(l, name)
@@ -145,6 +149,78 @@ def pack_codes(vals) -> np.ndarray:
     out = np.empty((rows, count // 2), np.uint8)
     _check(lib().oq_pack_codes(_p(vals), rows, count, _p(out)), "pack_codes")
     return out
+
+
+def quantize_format(w, group: int = 128, bits: int = 4, symmetric: bool = False, scale_f16: bool = False):
+    """Group-wise quantization in any of the stored formats (asymmetric or
+    symmetric grid, bits in 2..8, fp32 or binary16 scales): returns (codes
+    uint8 [rows, cols] unpacked, scales f32 [rows, G] holding the stored value,
+    zeros uint8 [rows, G]).  "How quantization works", "The math of
+    quantization" and Exercise 2 (16-bit scales); "Quantization Explained",
+    "Scale and Zero-Point", "Manual Group-Wise Quantizer"."""
+    w = _f32(w)
+    if w.ndim == 1:
+        w = w[None, :]
+    rows, cols = w.shape
+    if group <= 0 or cols % group:
+        raise ValueError("cols must be a multiple of group")
+    g = cols // group
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, g), np.float32)
+    z = np.empty((rows, g), np.uint8)
+    _check(lib().oq_quantize_format(_p(w), rows, cols, group, bits, int(symmetric), int(scale_f16), _p(q), _p(s),
+                                    _p(z)), "quantize_format")
+    return q, s, z
+
+
+def f32_to_f16(a) -> np.ndarray:
+    """IEEE binary16 of each float32 (round to nearest even, saturating at 65504), as np.float16."""
+    a = _f32(a)
+    out = np.empty(a.shape, np.uint16)
+    _check(lib().oq_f32_to_f16_array(_p(a), a.size, _p(out)), "f32_to_f16")
+    return out.view(np.float16)
+
+
+def f16_to_f32(h) -> np.ndarray:
+    h = np.ascontiguousarray(h).view(np.uint16)
+    out = np.empty(h.shape, np.float32)
+    _check(lib().oq_f16_to_f32_array(_p(h), h.size, _p(out)), "f16_to_f32")
+    return out
+
+
+def pack_codes3(vals) -> np.ndarray:
+    """3-bit codes packed along each row as a little-endian bit string (element i in bits 3i..3i+2)."""
+    vals = np.ascontiguousarray(vals, np.uint8)
+    if vals.ndim == 1:
+        vals = vals[None, :]
+    rows, count = vals.shape
+    out = np.empty((rows, count * 3 // 8), np.uint8)
+    _check(lib().oq_pack_codes3(_p(vals), rows, count, _p(out)), "pack_codes3")
+    return out
+
+
+def pack_format(q, s, z, bits: int, scale_f16: bool):
+    """Stored form of quantize_format's output: codes (4 bits: the code words
+    of pack_codes; 8 bits: one byte each; 3 bits: pack_codes3), scales (float32
+    or binary16) and zero-points (two per byte up to 4 bits, else one byte)."""
+    q = np.ascontiguousarray(q, np.uint8)
+    if bits == 4:
+        codes = pack_codes(q)
+    elif bits == 8:
+        codes = q.copy()
+    elif bits == 3:
+        codes = pack_codes3(q)
+    else:
+        raise ValueError("stored formats have 3, 4 or 8 bits")
+    scales = f32_to_f16(s) if scale_f16 else _f32(s).copy()
+    zeros = pack_nibbles(z) if bits <= 4 else np.ascontiguousarray(z, np.uint8).copy()
+    return codes, scales, zeros
+
+
+def quantize_format_packed(w, group: int = 128, bits: int = 4, symmetric: bool = False, scale_f16: bool = False):
+    """The stored format of any variant: (codes, scales, zeros) as pack_format."""
+    q, s, z = quantize_format(w, group, bits, symmetric, scale_f16)
+    return pack_format(q, s, z, bits, scale_f16)
 
 
 def quantize_groupwise_packed(w, group: int = 128):

@@ -93,6 +93,21 @@ float oq_f16_bits_to_f32(uint16_t h)
     return (float)((h & 0x8000u) ? -v : v);          /* exact: 11 significant bits */
 }
 
+/* Elementwise forms of the two conversions above (for marshalling). */
+int oq_f32_to_f16_array(const float* a, int64_t n, uint16_t* out)
+{
+    if (!a || !out || n < 0) return OQ_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i) out[i] = oq_f32_to_f16_bits(a[i]);
+    return OQ_OK;
+}
+
+int oq_f16_to_f32_array(const uint16_t* h, int64_t n, float* out)
+{
+    if (!h || !out || n < 0) return OQ_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i) out[i] = oq_f16_bits_to_f32(h[i]);
+    return OQ_OK;
+}
+
 /* A scale kept in 16 bits: the binary16 value of s, and 1 when that is 0     */
 /* (the [QS] listing's rule for an unusable scale, applied to the stored one; */
 /* reading R24).                                                              */

@@ -524,7 +524,172 @@ def check_w8a16_reference():
     assert np.abs(yq - yr).max() > 0
 
 
+# --------------------------------------------------------------------------
+# Format variants: 16-bit scales, group sizes, 3- and 8-bit codes.
+# --------------------------------------------------------------------------
+def check_f16_conversion():
+    # binary16 storage of scales ("How quantization works", Exercise 2: one
+    # 16-bit scale per group).  Against numpy's IEEE conversion (round to
+    # nearest even) on values over the whole range, on exact ties between
+    # neighbours (normal and subnormal), and the saturation reading (R24):
+    # at or above the largest finite value the result is 65504, not infinity.
+    g = np.random.Generator(np.random.PCG64(51))
+    a = (g.standard_normal(200000) * 10.0 ** g.uniform(-9, 4.8, 200000)).astype(np.float32)
+    a = a[np.abs(a) < 65504]
+    assert np.array_equal(oracle.f32_to_f16(a).view(np.uint16), a.astype(np.float16).view(np.uint16))
+    # ties: halfway between consecutive binary16 values goes to the even one
+    h = np.arange(1, 0x7BFF, 7, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    mid = ((lo + hi) / 2).astype(np.float32)
+    assert (mid.astype(np.float64) == (lo + hi) / 2).all()
+    got = oracle.f32_to_f16(mid).view(np.uint16)
+    assert np.array_equal(got, np.where(h % 2 == 0, h, h + 1).astype(np.uint16))
+    sat = oracle.f32_to_f16(np.float32([65504.0, 65519.0, 65520.0, 1e9, -1e9])).view(np.uint16)
+    assert sat.tolist() == [0x7BFF, 0x7BFF, 0x7BFF, 0x7BFF, 0xFBFF]
+    assert oracle.f32_to_f16(np.float32([2.0 ** -25, 3 * 2.0 ** -25, 2.0 ** -24])).view(np.uint16).tolist() == [0, 2, 1]
+    back = oracle.f16_to_f32(np.arange(0, 0x7C00, dtype=np.uint16))
+    assert np.array_equal(back, np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32))
+
+
+def check_f16_scale_grid():
+    # 16-bit scales: the stored scale is the binary16 value of the fp32 scale
+    # (1 if that is 0), and the codes are computed with the stored value, so
+    # dequantizing with what is stored rounds each weight to its nearest grid
+    # point (unclipped weights within half a stored step) and requantizing
+    # the dequantized weights returns the codes.
+    w = _random_groups(n_groups=800)
+    w[3] = 0.0
+    w[4] = np.float32(1e-9) * np.sign(w[4])          # a range below binary16's smallest step
+    for sym in (False, True):
+        q, s, z = oracle.quantize_format(w, 128, 4, symmetric=sym, scale_f16=True)
+        qf, sf, zf = oracle.quantize_format(w, 128, 4, symmetric=sym, scale_f16=False)
+        s16 = sf.astype(np.float16).astype(np.float32)
+        s16[s16 == 0] = 1.0
+        assert np.array_equal(s, s16)
+        assert float(s[3, 0]) == 1.0 and float(s[4, 0]) == 1.0
+        back = oracle.asym_dequantize(q, s, z, 128).astype(np.float64)
+        levels = np.arange(16, dtype=np.float64)
+        grid = (levels[None, :] - z.astype(np.float64)) * s.astype(np.float64)
+        d = np.abs(w.astype(np.float64)[:, :, None] - grid[:, None, :])
+        chosen = np.take_along_axis(d, q.astype(np.int64)[:, :, None], axis=2)[:, :, 0]
+        assert (chosen <= d.min(axis=2) + 8 * np.spacing(np.float32(1.0)) * s.astype(np.float64)).all()
+        inner = (q > 0) & (q < 15)
+        err = np.abs(back - w.astype(np.float64))
+        assert (err[inner] <= (s.astype(np.float64) / 2 * (1 + 1e-6) + 1e-12).repeat(1, 1)[
+            np.nonzero(inner)[0], 0]).all()
+        q2 = np.clip(np.rint(back.astype(np.float32) / s) + z, 0, 15)
+        assert np.array_equal(q2.astype(np.uint8), q)
+        # the stored format: two bytes per scale
+        codes, ss, zz = oracle.pack_format(q, s, z, 4, True)
+        assert ss.dtype == np.float16 and np.array_equal(ss.astype(np.float32), s)
+    # the page's 70B storage estimate is this format: 0.5 B of codes, a 16-bit
+    # scale and a 4-bit zero-point per 128 weights
+    gld = _golden("storage_70b.json")
+    codes, ss, zz = oracle.quantize_format_packed(np.zeros((8, 1024), np.float32), 128, 4, False, True)
+    per_param = (codes.nbytes + ss.nbytes + zz.nbytes) / (8 * 1024)
+    assert abs(per_param - (0.5 + 2.5 / 128)) < 1e-12
+    assert abs(gld["params"] * per_param / 1e9 - gld["total_gb"]) < 0.05
+
+
+def check_group_size_sweep():
+    # "Quantization Explained", "Measuring Your Own Error": on a random normal
+    # matrix the error rises as groups grow (32, 64, 128, 1024), and one huge
+    # value makes it jump; "The Cost of Small Groups": a 16-bit scale and a
+    # 4-bit zero-point cost (16 + 4) / group bits per weight.
+    g = np.random.Generator(np.random.PCG64(52))
+    w = g.standard_normal((64, 4096)).astype(np.float32)
+    mse = []
+    for group in (32, 64, 128, 1024):
+        q, s, z = oracle.quantize_format(w, group, 4)
+        mse.append(float(np.mean((oracle.asym_dequantize(q, s, z, group) - w) ** 2)))
+        codes, ss, zz = oracle.quantize_format_packed(w, group, 4, False, True)
+        assert abs((codes.nbytes + ss.nbytes + zz.nbytes) * 8 / w.size - (4 + 20 / group)) < 1e-12
+    assert mse[0] < mse[1] < mse[2] < mse[3], mse
+    wo = w.copy()
+    wo[5, 77] = np.float32(50.0)
+    q, s, z = oracle.quantize_format(wo, 128, 4)
+    group_err = np.mean((oracle.asym_dequantize(q, s, z, 128)[5, :128] - wo[5, :128]) ** 2)
+    q, s, z = oracle.quantize_format(w, 128, 4)
+    clean_err = np.mean((oracle.asym_dequantize(q, s, z, 128)[5, :128] - w[5, :128]) ** 2)
+    assert group_err > 20 * clean_err, (group_err, clean_err)
+
+
+def check_bit_width_errors():
+    # "Quantization from Scratch", "Measured on two real layers": with
+    # group-128 scales the output error at 8, 4 and 3 bits was 0.64%, 10.98%,
+    # 23.31% (layer 12) and 0.63%, 10.64%, 22.62% (layer 22): ratios of about
+    # 2.1 (3 vs 4 bits) and 17 (4 vs 8 bits), which is what a rounding error
+    # proportional to the step (hi - lo) / (2^b - 1) predicts (15/7 and
+    # 255/15).  The same ratios on Gaussian weights and inputs, asymmetric and
+    # symmetric, with each code the nearest of the 2^b grid points.
+    g = np.random.Generator(np.random.PCG64(53))
+    w = (g.standard_normal((96, 1024)) * 0.02).astype(np.float32)
+    x = g.standard_normal((64, 1024)).astype(np.float32)
+    y = x.astype(np.float64) @ w.astype(np.float64).T
+    for sym in (False, True):
+        err = {}
+        for bits in (3, 4, 8):
+            q, s, z = oracle.quantize_format(w, 128, bits, symmetric=sym)
+            assert q.max() <= 2 ** bits - 1
+            wq = oracle.asym_dequantize(q, s, z, 128).astype(np.float64)
+            err[bits] = np.linalg.norm(x.astype(np.float64) @ wq.T - y) / np.linalg.norm(y)
+            levels = np.arange(2 ** bits, dtype=np.float64)
+            grid = (levels[None, :] - z.reshape(-1, 1).astype(np.float64)) * s.reshape(-1, 1).astype(np.float64)
+            wg = w.reshape(-1, 128).astype(np.float64)
+            d = np.abs(wg[:, :, None] - grid[:, None, :])
+            chosen = np.take_along_axis(d, q.reshape(-1, 128).astype(np.int64)[:, :, None], axis=2)[:, :, 0]
+            # slack: the fp32 rounding of w / s (quotients up to 2^b)
+            tol = 4 * np.spacing(np.abs(wg).astype(np.float32)).astype(np.float64) + \
+                8 * np.spacing(np.float32(1.0)) * s.reshape(-1, 1)
+            assert (chosen <= d.min(axis=2) + tol).all()
+        assert 1.8 < err[3] / err[4] < 2.5, err
+        assert 13.0 < err[4] / err[8] < 21.0, err
+        if not sym:
+            assert 0.05 < err[4] < 0.2 and err[8] < 0.01, err
+
+
+def check_codes3_packing():
+    # 3-bit codes, a little-endian bit string along the row; the expected
+    # bytes of one run of 32 codes written out by hand.
+    vals = np.array([[1, 2, 3, 4, 5, 6, 7, 0] * 4], np.uint8)
+    p = oracle.pack_codes3(vals)
+    assert p.shape == (1, 12)
+    # codes 1,2,3,4,5,6,7,0 at bits 0,3,6,...: the 24-bit value
+    # 1 + 2*8 + 3*64 + 4*512 + 5*4096 + 6*32768 + 7*262144 = 0x1F58D1,
+    # bytes D1 58 1F (little-endian), repeated for each group of eight codes
+    assert p[0].tolist() == [0xD1, 0x58, 0x1F] * 4
+    v2 = np.zeros((1, 32), np.uint8)
+    v2[0, 10] = 7          # bits 30..32: crosses the first 32-bit word
+    v2[0, 21] = 5          # bits 63..65: crosses the second
+    p2 = oracle.pack_codes3(v2)
+    words = p2.view("<u4")[0]
+    assert words.tolist() == [0xC0000000, 0x80000001, 0x00000002]
+    back = [(int.from_bytes(p2[0].tobytes(), "little") >> (3 * i)) & 7 for i in range(32)]
+    assert back == v2[0].tolist()
+
+
+def check_symmetric_format():
+    # The symmetric grid in the stored format (R22) is the pinned symmetric
+    # quantizer ("How quantization works", "The math of quantization") shifted
+    # by 2^(b-1): same scale, code q + 2^(b-1), zero-point 2^(b-1), so the
+    # dequantized value (code - z) s is exactly q s.
+    w = _random_groups(n_groups=300)
+    w[7] = 0.0
+    for bits in (3, 4, 8):
+        q, s = oracle.sym_quantize(w, 128, bits, 1e-8)
+        c, sf, zf = oracle.quantize_format(w, 128, bits, symmetric=True)
+        assert np.array_equal(sf, s)
+        assert (zf == 2 ** (bits - 1)).all()
+        assert np.array_equal(c.astype(np.int16), q.astype(np.int16) + 2 ** (bits - 1))
+        back = oracle.asym_dequantize(c, sf, zf, 128)
+        assert np.array_equal(back, oracle.sym_dequantize(q, s, 128))
+
+
 ALL_CHECKS = [
+    check_symmetric_format,
+    check_f16_conversion, check_f16_scale_grid, check_group_size_sweep, check_bit_width_errors,
+    check_codes3_packing,
     check_per_tensor_activation,
     check_w8a16_reference,
     check_sym_int4_stored_groups,

@@ -50,6 +50,14 @@ MUTANTS = [
     ("smooth_div_instead_of_mul", "out[i * cols + j] = a[i * cols + j] * s[j];",
      "out[i * cols + j] = a[i * cols + j] / s[j];"),
     ("col_absmax_signed", "float v = fabsf(a[i * cols + j]);", "float v = a[i * cols + j];"),
+    ("f16_round_half_away", "double r = nearbyint(ldexp(a, 10 - e));", "double r = round(ldexp(a, 10 - e));"),
+    ("f16_subnormal_truncated", "double r = nearbyint(a * ldexp(1.0, 24));", "double r = floor(a * ldexp(1.0, 24));"),
+    ("f16_saturate_to_inf", "if (a >= 65504.0) return (uint16_t)(sign | 0x7BFFu);",
+     "if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);"),
+    ("f16_scale_zero_kept", "if (s16 == 0.0f) s16 = 1.0f;", ""),
+    ("codes_from_f32_scale", "if (scale_f16) s = f16_scale(s);", ""),
+    ("codes3_bit_order", "int64_t bit = 3 * i + t;", "int64_t bit = 3 * i + (2 - t);"),
+    ("sym_zero_point_off_by_one", "zf = half;                       /* R22 */", "zf = half - 1.0f;"),
 ]
 
 
@@ -74,7 +82,9 @@ def test_pins_catch_mutant(mid, old, new, source, tmp_path):
         mutant = ctypes.CDLL(str(so_path))
         for fn_name in ["oq_asym_quantize", "oq_asym_dequantize", "oq_sym_quantize", "oq_sym_dequantize",
                         "oq_pack_nibbles", "oq_pack_codes", "oq_matmul_nt_f64", "oq_int8_matmul_nt", "oq_rescale_f64",
-                        "oq_col_absmax", "oq_smooth_factors", "oq_scale_columns_mul", "oq_scale_columns_div"]:
+                        "oq_col_absmax", "oq_smooth_factors", "oq_scale_columns_mul", "oq_scale_columns_div",
+                        "oq_threads", "oq_quantize_format", "oq_pack_codes3", "oq_f32_to_f16_array",
+                        "oq_f16_to_f32_array"]:
             f = getattr(mutant, fn_name)
             f.argtypes = getattr(good_lib, fn_name).argtypes
             f.restype = ctypes.c_int
