@@ -89,8 +89,9 @@ int qmm_w4_sizes(int64_t N, int64_t K, int group, size_t* codes_bytes, size_t* s
  * it changes nothing for groups that straddle 0.
  *
  * W      : [N, K] of w_dtype (QMM_F32, QMM_BF16 or QMM_F16).
- * codes, scales, zeros : outputs in the INT4 format above.
- * bits must be 4 and group 128 (QMM_EUNSUPPORTED otherwise).
+ * codes, scales, zeros : outputs in the INT4 format above (bits 4, group
+ *          128); other group sizes and bit widths write the formats of
+ *          quantize_groupwise_ex with fp32 scales.
  * ------------------------------------------------------------------------- */
 int quantize_groupwise(const void* W, int w_dtype, int64_t N, int64_t K, int group, int bits,
                        uint8_t* codes, float* scales, uint8_t* zeros, void* stream);
@@ -119,7 +120,8 @@ int quantize_groupwise_symmetric(const void* W, int w_dtype, int64_t N, int64_t 
  * out_dtype (QMM_F32, QMM_BF16 or QMM_F16; round to nearest even).
  * Sources: "Quantization from Scratch" ("Scale and zero-point"); "Quantization
  * Explained" (slide "Uniform Affine Quantization").
- * W_hat : [N, K] output.  bits 4, group 128.
+ * W_hat : [N, K] output.  Other group sizes and bit widths: as dequantize_ex
+ * with fp32 scales.
  * ------------------------------------------------------------------------- */
 int dequantize(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                int group, int bits, void* W_hat, int out_dtype, void* stream);
@@ -133,7 +135,8 @@ int dequantize(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  * Is Faster"); "Quantization from Scratch" ("What it buys at decode").
  * x : [B, K] of x_dtype (QMM_BF16 or QMM_F16), 1 <= B <= 8.
  * y : [B, N] of y_dtype (x_dtype or QMM_F32).
- * group 128.  B == 1 runs on the vector ALUs only (no matrix cores);
+ * group 128 (other group sizes: as wxa16_gemv with 4 bits and fp32 scales).
+ * B == 1 runs on the vector ALUs only (no matrix cores);
  * 2 <= B <= 8 contracts on the matrix cores (the kernel of w4a16_gemm).
  * K <= 2^24 and N < 2^31 (QMM_ERANGE otherwise): tile offsets are 32-bit.
  * ------------------------------------------------------------------------- */
@@ -146,7 +149,8 @@ int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  * Source: "How quantization works" ("Inference view"); "Quantization from
  * Scratch" ("What it buys at decode", growing batch).
  * X : [M, K] QMM_BF16 or QMM_F16.  Y : [M, N] of X's type or QMM_F32.
- * M >= 1, group 128, K <= 2^24, N and M < 2^31 (QMM_ERANGE otherwise).
+ * M >= 1, group 128 (other group sizes: as wxa16_gemm with 4 bits and fp32
+ * scales), K <= 2^24, N and M < 2^31 (QMM_ERANGE otherwise).
  * A block keeps the zero points of its weight rows in
  * LDS, which bounds K for those kernels: K <= 52224 for M > 16 and
  * K <= 384000 for M <= 16; beyond that a slower kernel without the table
@@ -154,6 +158,72 @@ int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  * ------------------------------------------------------------------------- */
 int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                int group, const void* X, int x_dtype, int64_t M, void* Y, int y_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Other stored formats: group sizes, 3- and 8-bit codes, 16-bit scales.
+ *
+ * The same method (asymmetric s = (hi - lo) / (2^bits - 1), z = round(-lo / s),
+ * or the symmetric grid with code q + 2^(bits-1)) with:
+ *  * group  : 32, 64, 128, 256, 512 or 1024 consecutive weights of a row
+ *             ("Quantization Explained", "Measuring Your Own Error": group sizes
+ *             from 32 to 1024);
+ *  * bits   : 3, 4 or 8 ("Quantization from Scratch", "Measured on two real
+ *             layers": 8-, 4- and 3-bit codes with group scales);
+ *  * scale_dtype : QMM_F32, or QMM_F16 for one binary16 scale per group ("How
+ *             quantization works", Exercise 2; "Quantization from Scratch",
+ *             "Where to put the scales").  The codes are computed with the
+ *             stored value: the fp32 scale rounded to nearest even, saturating
+ *             at 65504, and 1 if that is 0.
+ * Storage:
+ *  * codes  : 4 bits -- the code words described above; 8 bits -- one byte per
+ *             weight, [N, K]; 3 bits -- each row a little-endian bit string,
+ *             element i in bits 3i..3i+2, [N, 3K/8] bytes (K % 32 == 0 follows
+ *             from the group sizes).
+ *  * scales : [N, G] of scale_dtype.
+ *  * zeros  : [N, ceil(G/2)] nibble pairs for 3 and 4 bits (as above), [N, G]
+ *             bytes for 8 bits.
+ * group 128 with 4 bits and fp32 scales is the format above and runs its
+ * kernels.  Errors: QMM_EUNSUPPORTED for other groups / bits / scale types,
+ * otherwise as the 4-bit calls.
+ * ------------------------------------------------------------------------- */
+
+/* Byte sizes of a stored format (any output pointer may be NULL).  Host-only. */
+int qmm_wq_sizes(int64_t N, int64_t K, int group, int bits, int scale_dtype, size_t* codes_bytes,
+                 size_t* scales_bytes, size_t* zeros_bytes);
+
+/* Quantize W [N, K] (QMM_F32 / QMM_BF16 / QMM_F16) into a stored format;
+ * symmetric != 0 selects the symmetric grid.  codes 16-byte aligned, scales
+ * aligned to their element. */
+int quantize_groupwise_ex(const void* W, int w_dtype, int64_t N, int64_t K, int group, int bits, int scale_dtype,
+                          int symmetric, uint8_t* codes, void* scales, uint8_t* zeros, void* stream);
+
+/* W_hat = (q - z) s in fp32 (one rounding), then out_dtype (QMM_F32 / QMM_BF16 / QMM_F16). */
+int dequantize_ex(const uint8_t* codes, const void* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+                  int bits, int scale_dtype, void* W_hat, int out_dtype, void* stream);
+
+/* y [B, N] = x [B, K] W_hat^T for 1 <= B <= 8, x QMM_BF16 / QMM_F16, y of x's
+ * type or QMM_F32, fp32 accumulation with each group's scale applied to its
+ * exact partial sums.  B <= 2 on the vector ALUs, B >= 3 on the matrix cores.
+ * K <= 2^24 (QMM_ERANGE). */
+int wxa16_gemv(const uint8_t* codes, const void* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+               int bits, int scale_dtype, const void* x, int x_dtype, int64_t B, void* y, int y_dtype, void* stream);
+
+/* Y [M, N] = X [M, K] W_hat^T for any M >= 1 (matrix cores from 3 tokens). */
+int wxa16_gemm(const uint8_t* codes, const void* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+               int bits, int scale_dtype, const void* X, int x_dtype, int64_t M, void* Y, int y_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Repack of 4-bit codes between plain nibble order (byte j of a row holds
+ * element 2j in its low nibble and 2j+1 in its high nibble) and the library's
+ * code words (above), both [N, K/2] bytes; K % 8 == 0, 16-byte aligned
+ * pointers.  The pages fix half a byte per weight but no order; weights
+ * packed in plain order by other tools go through repack_from_plain before
+ * dequantize / w4a16_gemv / w4a16_gemm.  Input and output may be the same
+ * buffer (each word is read before it is written by the same thread);
+ * otherwise they must not overlap.
+ * ------------------------------------------------------------------------- */
+int qmm_w4_repack_from_plain(const uint8_t* plain, uint8_t* codes, int64_t N, int64_t K, void* stream);
+int qmm_w4_repack_to_plain(const uint8_t* codes, uint8_t* plain, int64_t N, int64_t K, void* stream);
 
 /* ---------------------------------------------------------------------------
  * w8a16_gemv -- weight-only INT8 decode matmul:

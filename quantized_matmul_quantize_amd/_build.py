@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libqmm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "quantize.hip", "w4a16.hip", "w8a8.hip", "w8a16.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "w4a16.hip", "w8a8.hip", "w8a16.hip", "formats.hip"]
 
 # Per-source extra flags.  The MFMA kernels keep their accumulators in
 # ordinary VGPRs: with the default accumulator-register form the register
@@ -32,7 +32,8 @@ SOURCES = ["abi.hip", "quantize.hip", "w4a16.hip", "w8a8.hip", "w8a16.hip"]
 # and results folded on the vector ALUs would be copied out of AGPRs.
 EXTRA = {"w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-         "w8a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+         "w8a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "formats.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -19,4 +19,13 @@ int device_cus();
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The stored formats other than 4-bit codes with fp32 scales per 128 weights
+// (formats.hip); the 4-bit / group-128 entry points hand other formats here.
+int quantize_fmt(const void* W, int w_dtype, int64_t N, int64_t K, int group, int bits, int scale_dtype,
+                 int symmetric, uint8_t* codes, void* scales, uint8_t* zeros, void* stream);
+int dequantize_fmt(const uint8_t* codes, const void* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+                   int bits, int scale_dtype, void* W_hat, int out_dtype, void* stream);
+int matmul_fmt(const uint8_t* codes, const void* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+               int bits, int scale_dtype, const void* x, int x_dtype, int64_t M, void* y, int y_dtype, void* stream);
+
 }  // namespace qmm

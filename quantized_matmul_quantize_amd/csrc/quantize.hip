@@ -369,6 +369,9 @@ int quantize_launch(const void* W, int w_dtype, int64_t N, int64_t K, int group,
   if (!W) return QMM_EINVAL;
   if (w_dtype != QMM_F32 && w_dtype != QMM_BF16 && w_dtype != QMM_F16)
     return w_dtype == QMM_I32 ? QMM_EUNSUPPORTED : QMM_EINVAL;
+  // other group sizes and bit widths: the stored formats with fp32 scales
+  if (group != kGroup || bits != 4)
+    return quantize_fmt(W, w_dtype, N, K, group, bits, QMM_F32, SYM ? 1 : 0, codes, scales, zeros, stream);
   int st = check_w4_args(codes, scales, zeros, N, K, group, bits);
   if (st != QMM_OK) return st;
   if (!aligned(W, 16)) return QMM_EALIGN;
@@ -428,6 +431,8 @@ extern "C" int dequantize(const uint8_t* codes, const float* scales, const uint8
   if (!W_hat) return QMM_EINVAL;
   if (out_dtype != QMM_F32 && out_dtype != QMM_BF16 && out_dtype != QMM_F16)
     return out_dtype == QMM_I32 ? QMM_EUNSUPPORTED : QMM_EINVAL;
+  if (group != kGroup || bits != 4)
+    return dequantize_fmt(codes, scales, zeros, N, K, group, bits, QMM_F32, W_hat, out_dtype, stream);
   int st = check_w4_args(codes, scales, zeros, N, K, group, bits);
   if (st != QMM_OK) return st;
   if (!aligned(W_hat, 16)) return QMM_EALIGN;

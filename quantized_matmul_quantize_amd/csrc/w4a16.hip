@@ -1285,6 +1285,10 @@ using namespace qmm;
 
 extern "C" int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                           int group, const void* x, int x_dtype, int64_t B, void* y, int y_dtype, void* stream) {
+  if (group != kGroup) {   // other group sizes: the stored formats with fp32 scales
+    if (B > 8) return QMM_EUNSUPPORTED;
+    return matmul_fmt(codes, scales, zeros, N, K, group, 4, QMM_F32, x, x_dtype, B, y, y_dtype, stream);
+  }
   int st = check_common(codes, scales, zeros, N, K, group, x, x_dtype, B, y, y_dtype);
   if (st != QMM_OK) return st;
   if (B > 8) return QMM_EUNSUPPORTED;
@@ -1309,6 +1313,8 @@ extern "C" int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8
 
 extern "C" int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                           int group, const void* X, int x_dtype, int64_t M, void* Y, int y_dtype, void* stream) {
+  if (group != kGroup)
+    return matmul_fmt(codes, scales, zeros, N, K, group, 4, QMM_F32, X, x_dtype, M, Y, y_dtype, stream);
   int st = check_common(codes, scales, zeros, N, K, group, X, x_dtype, M, Y, y_dtype);
   if (st != QMM_OK) return st;
   hipStream_t s = as_stream(stream);

@@ -53,8 +53,10 @@ def test_binding_names_match_the_header():
     # every C entry point has a Python function of the same name, and every
     # name the package exports resolves
     for n in declared_functions():
-        if n not in ("qmm_status_string", "qmm_version", "qmm_w4_sizes", "sq_workspace_bytes"):
-            assert callable(getattr(qmm, n, None)), n
+        if n in ("qmm_status_string", "qmm_version", "sq_workspace_bytes"):
+            continue
+        py = n[4:] if n.startswith("qmm_") else n
+        assert callable(getattr(qmm, py, None)), n
     for n in qmm.__all__:
         assert hasattr(qmm, n), n
 
@@ -115,8 +117,8 @@ def test_quantize_argument_errors():
     assert f(P, BF16, 4, 200, 128, 4, P, P, P, None) == EINVAL          # K % group
     assert f(P, 9, 4, 256, 128, 4, P, P, P, None) == EINVAL             # bad dtype
     assert f(P, I32, 4, 256, 128, 4, P, P, P, None) == EUNSUP
-    assert f(P, BF16, 4, 256, 128, 3, P, P, P, None) == EUNSUP          # bits
-    assert f(P, BF16, 4, 256, 64, 4, P, P, P, None) == EUNSUP           # group
+    assert f(P, BF16, 4, 256, 128, 5, P, P, P, None) == EUNSUP          # bits
+    assert f(P, BF16, 4, 4096, 2048, 4, P, P, P, None) == EUNSUP        # group
     assert f(MIS, BF16, 4, 256, 128, 4, P, P, P, None) == EALIGN
     assert f(P, BF16, 4, 256, 128, 4, MIS, P, P, None) == EALIGN
 
@@ -137,7 +139,8 @@ def test_gemv_gemm_argument_errors():
     assert gemv(P, P, P, 8, 256, 128, P, BF16, 0, P, BF16, None) == EINVAL
     assert gemv(P, P, P, 8, 256, 128, P, F32, 1, P, F32, None) == EUNSUP      # fp32 activations
     assert gemv(P, P, P, 8, 256, 128, P, BF16, 1, P, F16, None) == EUNSUP     # mixed 16-bit types
-    assert gemv(P, P, P, 8, 256, 64, P, BF16, 1, P, BF16, None) == EUNSUP
+    assert gemv(P, P, P, 8, 256, 256, P, BF16, 9, P, BF16, None) == EUNSUP   # B > 8, other group
+    assert gemv(P, P, P, 8, 4096, 2048, P, BF16, 1, P, BF16, None) == EUNSUP # group
     assert gemv(P, P, P, 8, 256, 128, MIS, BF16, 1, P, BF16, None) == EALIGN
     assert gemm(P, P, P, 8, 256, 128, P, F32, 4, P, F32, None) == EUNSUP      # fp32 activations
     assert gemm(P, P, P, 8, 256, 128, P, F16, 4, P, BF16, None) == EUNSUP     # mixed 16-bit types
