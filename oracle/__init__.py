@@ -69,6 +69,10 @@ def lib(parallel: bool = False) -> ctypes.CDLL:
             "oq_pack_codes3": [P, I64, I64, P],
             "oq_f32_to_f16_array": [P, I64, P],
             "oq_f16_to_f32_array": [P, I64, P],
+            "oq_e4m3_array": [P, I64, P],
+            "oq_e4m3_decode_array": [P, I64, P],
+            "oq_fp8_quantize": [P, I64, I64, I64, P, P],
+            "oq_fp8_matmul_nt": [P, P, I64, I64, I64, P],
         }
         for name, argtypes in sigs.items():
             fn = getattr(l, name)
@@ -390,3 +394,61 @@ def sq_w8a8_reference(x, s, qw, b):
     qx, a = sq_quantize_activation(x, s)
     acc = int8_matmul_nt(qx, qw)
     return qx, a, acc, rescale_f64(acc, a, b)
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 W8A8 ("How quantization works", the fake-quantization listing and
+# "Mainstream schemes at a glance", FP8 row; "Quantization: Smaller Weights,
+# Same Answers (Mostly)", "What about FP8, MXFP4, NVFP4 and GGUF?").
+# --------------------------------------------------------------------------
+def to_e4m3(a) -> np.ndarray:
+    """E4M3FN code bytes of float32 values (nearest even, saturating at 448)."""
+    a = _f32(a)
+    out = np.empty(a.shape, np.uint8)
+    _check(lib().oq_e4m3_array(_p(a), a.size, _p(out)), "to_e4m3")
+    return out
+
+
+def from_e4m3(b) -> np.ndarray:
+    b = np.ascontiguousarray(b, np.uint8)
+    out = np.empty(b.shape, np.float32)
+    _check(lib().oq_e4m3_decode_array(_p(b), b.size, _p(out)), "from_e4m3")
+    return out
+
+
+def fp8_quantize(x, per_tensor: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """s = max|x| / 448 per row (or one for the whole tensor), q = E4M3(x / s):
+    (codes uint8 [rows, cols], scales f32 [rows], every entry the tensor's
+    scale when per_tensor)."""
+    x = _f32(x)
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    if per_tensor:
+        s = np.empty(1, np.float32)
+        _check(lib().oq_fp8_quantize(_p(x), 1, x.size, x.size, _p(q), _p(s)), "fp8_quantize")
+        return q, np.full(rows, s[0], np.float32)
+    s = np.empty(rows, np.float32)
+    _check(lib().oq_fp8_quantize(_p(x), rows, cols, cols, _p(q), _p(s)), "fp8_quantize")
+    return q, s
+
+
+def fp8_matmul_nt(qa, qb, parallel: bool = False) -> np.ndarray:
+    """acc = decoded(qa) decoded(qb)^T summed in fp64."""
+    qa = np.ascontiguousarray(qa, np.uint8)
+    qb = np.ascontiguousarray(qb, np.uint8)
+    m, k = qa.shape
+    n, k2 = qb.shape
+    assert k == k2
+    acc = np.empty((m, n), np.float64)
+    _check(lib(parallel).oq_fp8_matmul_nt(_p(qa), _p(qb), m, n, k, _p(acc)), "fp8_matmul_nt")
+    return acc
+
+
+def fp8_w8a8_reference(x, qw, b, parallel: bool = False):
+    """Online FP8 W8A8: per-token E4M3 activations, exact product, rescale.
+    Returns (qX, a, y fp64)."""
+    qx, a = fp8_quantize(x)
+    acc = fp8_matmul_nt(qx, qw, parallel)
+    return qx, a, acc * a.astype(np.float64)[:, None] * np.asarray(b, np.float32).astype(np.float64)[None, :]

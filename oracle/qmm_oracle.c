@@ -329,6 +329,100 @@ int oq_pack_codes3(const uint8_t* vals, int64_t rows, int64_t count, uint8_t* ou
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP8 E4M3 (OCP "E4M3FN": 1 sign, 4 exponent bits with bias 7, 3 mantissa  */
+/* bits, no infinities, the only NaN S.1111.111; largest finite 448, smallest */
+/* normal 2^-6, subnormals m 2^-9).  [HQ] "Quantization formats" and its     */
+/* fake-quantization listing (E4M3's maximum is 448); [SW] "What about FP8,  */
+/* MXFP4, NVFP4 and GGUF?".  Conversion from fp32 by the definition: round   */
+/* to nearest, ties to even; a magnitude at or above 448 gives 448 (reading */
+/* R25: nothing above 464 rounds to a finite value, and the listing's        */
+/* quotients never exceed 448 by more than an fp32 rounding).                */
+/* ------------------------------------------------------------------------ */
+uint8_t oq_f32_to_e4m3(float f)
+{
+    const uint8_t sign = signbit(f) ? 0x80u : 0u;
+    double a = fabs((double)f);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7Eu);
+    if (a < ldexp(1.0, -6)) {                       /* subnormal: units of 2^-9  */
+        double r = nearbyint(a * ldexp(1.0, 9));
+        return (uint8_t)(sign | (uint8_t)r);        /* r == 8 is the smallest normal */
+    }
+    int ex;
+    frexp(a, &ex);
+    int e = ex - 1;                                 /* a in [2^e, 2^(e+1))       */
+    double r = nearbyint(ldexp(a, 3 - e));          /* significand in [8, 16]    */
+    if (r == 16.0) {
+        r = 8.0;
+        e += 1;
+    }
+    if (e > 8) return (uint8_t)(sign | 0x7Eu);
+    return (uint8_t)(sign | (uint8_t)((e + 7) << 3) | (uint8_t)(r - 8.0));
+}
+
+float oq_e4m3_to_f32(uint8_t b)
+{
+    const int e = (b >> 3) & 0xF;
+    const int m = b & 7;
+    double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    if (e == 15 && m == 7) v = NAN;
+    return (float)((b & 0x80u) ? -v : v);
+}
+
+int oq_e4m3_array(const float* a, int64_t n, uint8_t* out)
+{
+    if (!a || !out || n < 0) return OQ_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i) out[i] = oq_f32_to_e4m3(a[i]);
+    return OQ_OK;
+}
+
+int oq_e4m3_decode_array(const uint8_t* b, int64_t n, float* out)
+{
+    if (!b || !out || n < 0) return OQ_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i) out[i] = oq_e4m3_to_f32(b[i]);
+    return OQ_OK;
+}
+
+/* FP8 quantization, [HQ] fake_quant_fp8: s = max|x| / 448 over each group of */
+/* `group` consecutive elements (a row: per token / per output channel; the  */
+/* whole tensor as one row: the listing's per-tensor form), q = E4M3(x / s). */
+/* The absmax is floored at 1e-8 as in the integer path (R8, R25).           */
+int oq_fp8_quantize(const float* x, int64_t rows, int64_t cols, int64_t group, uint8_t* q, float* scales)
+{
+    if (!x || !q || !scales || group <= 0 || cols % group != 0) return OQ_BAD_ARG;
+    const int64_t groups_per_row = cols / group;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t g = 0; g < groups_per_row; ++g) {
+            const float* v = x + r * cols + g * group;
+            float amax = 0.0f;
+            for (int64_t i = 0; i < group; ++i) {
+                float a = fabsf(v[i]);
+                if (a > amax) amax = a;
+            }
+            if (amax < 1e-8f) amax = 1e-8f;
+            float s = amax / 448.0f;
+            scales[r * groups_per_row + g] = s;
+            for (int64_t i = 0; i < group; ++i) q[r * cols + g * group + i] = oq_f32_to_e4m3(v[i] / s);
+        }
+    return OQ_OK;
+}
+
+/* FP8 product: acc[m][n] = sum_k e4m3(qa[m][k]) e4m3(qb[n][k]) in fp64 (each */
+/* product of two 4-significant-bit values is exact).                        */
+int oq_fp8_matmul_nt(const uint8_t* qa, const uint8_t* qb, int64_t m, int64_t n, int64_t k, double* acc)
+{
+    if (!qa || !qb || !acc || m < 0 || n < 0 || k < 0) return OQ_BAD_ARG;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double sacc = 0.0;
+            for (int64_t t = 0; t < k; ++t)
+                sacc += (double)oq_e4m3_to_f32(qa[i * k + t]) * (double)oq_e4m3_to_f32(qb[j * k + t]);
+            acc[i * n + j] = sacc;
+        }
+    return OQ_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Reference product C[m][n] = sum_k A[m][k] * B[n][k] in fp64 (B is stored  */
 /* [N, K] like a weight matrix, so C = A B^T).  For the W4A16 matmuls A is   */
 /* the activations and B the dequantized weights: the plain definition of   */

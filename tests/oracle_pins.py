@@ -686,7 +686,97 @@ def check_symmetric_format():
         assert np.array_equal(back, oracle.sym_dequantize(q, s, 128))
 
 
+# --------------------------------------------------------------------------
+# FP8 E4M3.
+# --------------------------------------------------------------------------
+def check_e4m3_conversion():
+    # OCP E4M3 ("E4M3FN"): against torch's own float8_e4m3fn (an independent
+    # implementation) on every code's value and on fp32 inputs over the whole
+    # range below 464 (the midpoint above 448, beyond which rounding would
+    # leave the finite values), including every exact tie between neighbours;
+    # then the definition's landmarks and the saturation reading (R25).
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    dec = oracle.from_e4m3(codes)
+    tdec = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    finite = ~np.isnan(tdec)
+    assert np.array_equal(np.isnan(dec), ~finite) and np.array_equal(dec[finite], tdec[finite])
+    g = np.random.Generator(np.random.PCG64(61))
+    x = (g.standard_normal(400000) * 10.0 ** g.uniform(-4, 2.7, 400000)).astype(np.float32)
+    x = x[np.abs(x) < 464]
+    mids = ((dec[:-1].astype(np.float64) + dec[1:].astype(np.float64)) / 2)
+    mids = mids[np.isfinite(mids) & (np.abs(mids) < 464)].astype(np.float32)
+    for v in (x, mids, -mids):
+        assert np.array_equal(oracle.to_e4m3(v), torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert float(oracle.from_e4m3(np.uint8([0x7E]))[0]) == 448.0           # largest finite
+    assert float(oracle.from_e4m3(np.uint8([0x08]))[0]) == 2.0 ** -6       # smallest normal
+    assert float(oracle.from_e4m3(np.uint8([0x01]))[0]) == 2.0 ** -9       # smallest subnormal
+    assert float(oracle.from_e4m3(np.uint8([0x38]))[0]) == 1.0             # exponent bias 7
+    assert oracle.to_e4m3(np.float32([448.0, 460.0, 464.0, 500.0, 1e6, -1e6])).tolist() == [0x7E] * 5 + [0xFE]
+
+
+def check_fp8_listing():
+    # "How quantization works", fake-quantization listing: s = max|w| / 448,
+    # q = E4M3(w / s); the largest magnitude maps to +-448 exactly, every
+    # weight in E4M3's normal range is within half an E4M3 step (2^-4
+    # relative) of its value, and the page's error ordering on a weight
+    # matrix: INT8 per channel < FP8 per tensor < INT8 per tensor (its table:
+    # 0.0097 < 0.0265 < 0.0362).
+    w, _ = workloads.weight(workloads.WORKLOADS["mlp70b"], 0, shape=(512, 2048))
+    w = w.float().numpy()
+    q, s = oracle.fp8_quantize(w, per_tensor=True)
+    amax = np.float32(np.abs(w).max())
+    assert (s == amax / np.float32(448.0)).all()
+    back = oracle.from_e4m3(q).astype(np.float64) * np.float64(s[0])
+    i = np.unravel_index(np.argmax(np.abs(w)), w.shape)
+    assert abs(float(oracle.from_e4m3(np.uint8([q[i]]))[0])) == 448.0
+    xs = np.abs(w.astype(np.float64)) / np.float64(s[0])
+    normal = xs >= 2.0 ** -6
+    err = np.abs(back - w.astype(np.float64))
+    assert (err[normal] <= 2.0 ** -4 * np.abs(w.astype(np.float64))[normal] * (1 + 1e-6) + 1e-30).all()
+    assert (err[~normal] <= 2.0 ** -10 * np.float64(s[0]) * (1 + 1e-6)).all()
+
+    def rel(a):
+        return np.linalg.norm(a - w.astype(np.float64)) / np.linalg.norm(w.astype(np.float64))
+
+    e_fp8 = rel(back)
+    qt, st = oracle.sym_quantize(w.reshape(1, -1), w.size, 8)
+    e_i8t = rel(oracle.sym_dequantize(qt, st, w.size).reshape(w.shape))
+    qc, sc = oracle.sym_quantize(w, w.shape[1], 8)
+    e_i8c = rel(oracle.sym_dequantize(qc, sc, w.shape[1]))
+    assert e_i8c < e_fp8 < e_i8t, (e_i8c, e_fp8, e_i8t)
+    # per row: one scale per row, each row's largest magnitude at +-448
+    qr, sr = oracle.fp8_quantize(w)
+    assert np.array_equal(sr, (np.abs(w).max(axis=1) / np.float32(448.0)).astype(np.float32))
+    assert (np.abs(oracle.from_e4m3(qr)).max(axis=1) == 448.0).all()
+
+
+def check_fp8_product():
+    # The FP8 product reference: brute force on codes whose values are small
+    # integers and powers of two (every product and sum exact), with distinct
+    # shapes so a transposed operand or a wrong index fails; and the online
+    # W8A8 reference against the dequantized product.
+    g = np.random.Generator(np.random.PCG64(62))
+    vals = np.float32([0, 1, -1, 2, -3, 0.5, 4, -0.25, 7, 12, -16])
+    a = vals[g.integers(0, len(vals), (3, 40))]
+    b = vals[g.integers(0, len(vals), (5, 40))]
+    qa, qb = oracle.to_e4m3(a), oracle.to_e4m3(b)
+    assert np.array_equal(oracle.from_e4m3(qa), a) and np.array_equal(oracle.from_e4m3(qb), b)
+    acc = oracle.fp8_matmul_nt(qa, qb)
+    for i in range(3):
+        for j in range(5):
+            assert acc[i, j] == sum(float(a[i, t]) * float(b[j, t]) for t in range(40))
+    x = g.standard_normal((6, 64)).astype(np.float32)
+    w = (g.standard_normal((7, 64)) * 0.05).astype(np.float32)
+    qw, bw = oracle.fp8_quantize(w)
+    qx, ax, y = oracle.fp8_w8a8_reference(x, qw, bw)
+    xd = oracle.from_e4m3(qx).astype(np.float64) * ax.astype(np.float64)[:, None]
+    wd = oracle.from_e4m3(qw).astype(np.float64) * bw.astype(np.float64)[:, None]
+    assert np.allclose(y, xd @ wd.T, rtol=1e-12, atol=1e-15)
+
+
 ALL_CHECKS = [
+    check_e4m3_conversion, check_fp8_listing, check_fp8_product,
     check_symmetric_format,
     check_f16_conversion, check_f16_scale_grid, check_group_size_sweep, check_bit_width_errors,
     check_codes3_packing,

@@ -58,6 +58,14 @@ MUTANTS = [
     ("codes_from_f32_scale", "if (scale_f16) s = f16_scale(s);", ""),
     ("codes3_bit_order", "int64_t bit = 3 * i + t;", "int64_t bit = 3 * i + (2 - t);"),
     ("sym_zero_point_off_by_one", "zf = half;                       /* R22 */", "zf = half - 1.0f;"),
+    ("e4m3_round_half_away", "double r = nearbyint(ldexp(a, 3 - e));", "double r = round(ldexp(a, 3 - e));"),
+    ("e4m3_bias_8", "return (uint8_t)(sign | (uint8_t)((e + 7) << 3) | (uint8_t)(r - 8.0));",
+     "return (uint8_t)(sign | (uint8_t)((e + 8) << 3) | (uint8_t)(r - 8.0));"),
+    ("e4m3_subnormal_truncated", "double r = nearbyint(a * ldexp(1.0, 9));", "double r = floor(a * ldexp(1.0, 9));"),
+    ("fp8_max_480", "float s = amax / 448.0f;", "float s = amax / 480.0f;"),
+    ("fp8_product_transposed",
+     "sacc += (double)oq_e4m3_to_f32(qa[i * k + t]) * (double)oq_e4m3_to_f32(qb[j * k + t]);",
+     "sacc += (double)oq_e4m3_to_f32(qa[i * k + t]) * (double)oq_e4m3_to_f32(qb[t * n + j % n]);"),
 ]
 
 
@@ -84,7 +92,8 @@ def test_pins_catch_mutant(mid, old, new, source, tmp_path):
                         "oq_pack_nibbles", "oq_pack_codes", "oq_matmul_nt_f64", "oq_int8_matmul_nt", "oq_rescale_f64",
                         "oq_col_absmax", "oq_smooth_factors", "oq_scale_columns_mul", "oq_scale_columns_div",
                         "oq_threads", "oq_quantize_format", "oq_pack_codes3", "oq_f32_to_f16_array",
-                        "oq_f16_to_f32_array"]:
+                        "oq_f16_to_f32_array", "oq_e4m3_array", "oq_e4m3_decode_array", "oq_fp8_quantize",
+                        "oq_fp8_matmul_nt"]:
             f = getattr(mutant, fn_name)
             f.argtypes = getattr(good_lib, fn_name).argtypes
             f.restype = ctypes.c_int
