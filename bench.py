@@ -18,9 +18,13 @@ are resident in HBM before timing starts, for all five workloads:
   (the W8A8 baseline: X read twice), sq_int8_gemm alone (i8-MFMA GEMM and
   rescale to bf16, on activations quantized before timing) and
   smooth_quant_w8a8_gemm (per-token smoothing + INT8 quantization, then the
-  same GEMM);
+  same GEMM); FP8 E4M3 W8A8 on the same shapes: fp8_quantize of the weights,
+  fp8_gemm alone and the online fp8_w8a8_gemm;
   70B-class MLP decode: w4a16_gemv B=8 then B=1 on both matrices (B=1 is the
-  headline), then weight-only INT8 (w8a16_gemv) at B=1 and B=8.
+  headline), then weight-only INT8 (w8a16_gemv) at B=1 and B=8;
+  stored-format variants on the 28672x8192 matrix (binary16 scales, groups of
+  32 and 1024, 3- and 8-bit codes): quantize_groupwise_ex and the B=1
+  wxa16_gemv.
 
 Cache: the last-level cache is 256 MB.  No op reads an operand that anything
 touched within the last 512 MB of traffic: every op reads buffers of its own
@@ -67,6 +71,7 @@ import workloads  # noqa: E402
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0       # dense bf16 MFMA, published
 I8_PEAK_TOPS = 5000.0           # dense int8 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0        # dense fp8 MFMA, published
 COLD_BYTES = 512e6              # twice the 256 MB last-level cache
 COPIES_70B = 4
 
@@ -130,6 +135,17 @@ def w8_kernel_name(B):
 
 def w4_bytes(n, k):
     c, s, z = qmm.w4_sizes(n, k)
+    return c + s + z
+
+
+# Stored-format variants timed on the 28672x8192 matrix: (tag, group, bits, scale dtype).
+VARIANTS = [("g128-4bit-f16scale", 128, 4, torch.float16), ("g32-4bit", 32, 4, torch.float32),
+            ("g1024-4bit", 1024, 4, torch.float32), ("g128-3bit-f16scale", 128, 3, torch.float16),
+            ("g128-8bit-f16scale", 128, 8, torch.float16)]
+
+
+def fmt_bytes(n, k, f):
+    c, s, z = qmm.wq_sizes(n, k, f["group"], f["bits"], f["sdt"])
     return c + s + z
 
 
@@ -228,6 +244,25 @@ def build_ops(dev):
         ops.add(f"dequantize {m['n']}x{m['k']}", deq, w4_bytes(m["n"], m["k"]) + m["n"] * m["k"] * 2, "hbm",
                 "dequantize_g128_kernel", cfg5, reads=lambda i, m=m: [f"{m['key']}[{(i + 3) % C}]"],
                 writes=lambda i, m=m: [f"what_70b{m['idx']}"])
+
+    # ---- stored-format variants on the 28672x8192 matrix ---------------------
+    # quantizer writes copy i%2, the B=1 GEMV (at the end of the step) reads (i+1)%2
+    # the variant quantizers read two further copies of the bf16 weights in turn
+    w0c = [m0["w"].clone() for _ in range(2)]
+    fmts = []
+    for tag, group, bits, sdt in VARIANTS:
+        cps = [qmm.quantize_groupwise_ex(m0["w"], group, bits, sdt) for _ in range(2)]
+        fmts.append(dict(tag=tag, group=group, bits=bits, sdt=sdt, copies=cps, key=f"fmt_{tag}",
+                         x=workloads.activations(wl5, 1, m0["k"], salt=0).to(dev),
+                         y=torch.empty((1, m0["n"]), dtype=torch.bfloat16, device=dev)))
+    for j, f in enumerate(fmts):
+        def quant_fmt(i, f=f, m=m0, w=w0c[j % 2]):
+            c, sc, z = f["copies"][i % 2]
+            ok(lib.quantize_groupwise_ex(P(w), qmm.BF16, m["n"], m["k"], f["group"], f["bits"], qmm._sdt(f["sdt"]),
+                                         0, P(c), P(sc), P(z), S(w)))
+        ops.add(f"quantize_ex {f['tag']} {m0['n']}x{m0['k']}", quant_fmt,
+                m0["n"] * m0["k"] * 2 + fmt_bytes(m0["n"], m0["k"], f), "hbm", "quantize_fmt_kernel", cfg5,
+                reads=lambda i, j=j: [f"bf16_70b0_copy{j % 2}"], writes=lambda i, f=f: [f"{f['key']}[{i % 2}]"])
 
     # ---- single 512x512 fp32 weight: quantize, fp16 GEMV --------------------
     wl1 = workloads.WORKLOADS["tiny"]
@@ -338,6 +373,39 @@ def build_ops(dev):
             "rowquant8_kernel + i8_gemm_kernel", cfg4, reads=lambda i: ["x4[2]", "qw_b", "sm_o"],
             writes=lambda i: ["y4b"], flops=2 * m4 * n4 * k4, peak=I8_PEAK_TOPS)
 
+    # ---- FP8 E4M3 W8A8 on the same shapes ------------------------------------
+    x8in = x4c.to(dev)                           # the online FP8 call's activations
+    w8in = w4c.to(dev)                           # the FP8 weight quantizer's input
+    q8w, s8w = qmm.fp8_quantize(w4[1])           # read by the FP8 GEMM alone
+    q8wb, s8wb = qmm.fp8_quantize(w4[1])         # read by the online FP8 call
+    q8x, s8x = qmm.fp8_quantize(x4[0])
+    q8w_out = torch.empty((n4, k4), dtype=torch.uint8, device=dev)
+    s8w_out = torch.empty(n4, dtype=torch.float32, device=dev)
+    y8a = torch.empty((m4, n4), dtype=torch.bfloat16, device=dev)
+    y8b = torch.empty((m4, n4), dtype=torch.bfloat16, device=dev)
+    ws8 = torch.empty(qmm.sq_workspace_bytes(m4, k4), dtype=torch.uint8, device=dev)
+    cfg4f = "FP8 E4M3 W8A8 2048x4096x4096"
+
+    def fp8_wq(i):
+        ok(lib.fp8_quantize(P(w8in), qmm.BF16, n4, k4, 0, P(q8w_out), P(s8w_out), S(w8in)))
+
+    def fp8_mm(i):
+        ok(lib.fp8_gemm(P(q8x), P(s8x), P(q8w), P(s8w), m4, n4, k4, P(y8a), qmm.BF16, S(q8x)))
+
+    def fp8_online(i):
+        ok(lib.fp8_w8a8_gemm(P(x8in), qmm.BF16, P(q8wb), P(s8wb), m4, n4, k4, P(y8b), qmm.BF16, P(ws8), ws8.numel(),
+                             S(x8in)))
+
+    ops.add(f"fp8_quantize weights {n4}x{k4}", fp8_wq, n4 * k4 * 3 + n4 * 4, "hbm", "rowquant8_kernel (E4M3)", cfg4f,
+            reads=lambda i: ["w8in"], writes=lambda i: ["q8w_out"])
+    ops.add(f"fp8_gemm {m4}x{n4}x{k4}", fp8_mm, m4 * k4 + m4 * 4 + n4 * k4 + n4 * 4 + m4 * n4 * 2, "mfma",
+            "i8_gemm_kernel (fp8)", cfg4f, reads=lambda i: ["q8x", "q8w"], writes=lambda i: ["y8a"],
+            flops=2 * m4 * n4 * k4, peak=FP8_PEAK_TFLOPS)
+    ops.add(f"fp8_w8a8_gemm {m4}x{n4}x{k4}", fp8_online,
+            m4 * k4 * 2 + (m4 * k4 + m4 * 4) * 2 + n4 * k4 + n4 * 4 + m4 * n4 * 2, "mfma",
+            "rowquant8_kernel (E4M3) + i8_gemm_kernel (fp8)", cfg4f, reads=lambda i: ["x8in", "q8wb"],
+            writes=lambda i: ["y8b"], flops=2 * m4 * n4 * k4, peak=FP8_PEAK_TFLOPS)
+
     # ---- 70B-class MLP decode: W4A16 B=8 then B=1, then W8A16 --------------
     for m in mats:
         for B in (1, 8):
@@ -363,6 +431,14 @@ def build_ops(dev):
                     m["n"] * m["k"] + m["n"] * 4 + B * m["k"] * 2 + B * m["n"] * 2, "hbm", w8_kernel_name(B), cfg5,
                     reads=lambda i, m=m, j=j, B=B: [f"w8_70b{m['idx']}[{j}]", f"x{B}w8_70b{m['idx']}"],
                     flops=2 * B * m["n"] * m["k"])
+    for f in fmts:
+        def gemv_fmt(i, f=f, m=m0):
+            c, sc, z = f["copies"][(i + 1) % 2]
+            ok(lib.wxa16_gemv(P(c), P(sc), P(z), m["n"], m["k"], f["group"], f["bits"], qmm._sdt(f["sdt"]), P(f["x"]),
+                              qmm.BF16, 1, P(f["y"]), qmm.BF16, S(c)))
+        ops.add(f"wxa16_gemv B=1 {f['tag']} {m0['n']}x{m0['k']}", gemv_fmt,
+                fmt_bytes(m0["n"], m0["k"], f) + m0["k"] * 2 + m0["n"] * 2, "hbm", "gemv_fmt_kernel", cfg5,
+                reads=lambda i, f=f: [f"{f['key']}[{(i + 1) % 2}]", f"x_{f['key']}"], flops=2 * m0["n"] * m0["k"])
     return ops, mats
 
 
@@ -562,8 +638,11 @@ def main():
             "quantize_GBps_llama7b": gbps(["quantize 4096x4096", "quantize 11008x4096"]),
             "quantize_GBps_gemm_14336x4096": gbps(["quantize 14336x4096"]),
             "gemv_b1_GBps_llama7b": gbps(["w4a16_gemv B=1 4096x4096", "w4a16_gemv B=1 11008x4096"]),
+            "format_variants_GBps": {f"{k.split()[0]} {k.split()[2]}": breakdown[k]["GBps"] for k in breakdown
+                                     if k.startswith("quantize_ex") or k.startswith("wxa16_gemv")},
             "gemm_TFLOPs": {k: v.get("TFLOPs") for k, v in gemm.items()},
             "int8_gemm_TOPS": i8.get("TFLOPs"),
+            "fp8_gemm_TFLOPs": breakdown[[k for k in breakdown if k.startswith("fp8_gemm")][0]].get("TFLOPs"),
             "w8a8_online_TOPS": sq.get("TFLOPs"),
             "weight_copies_rotated_70b": COPIES_70B,
             "min_reuse_MB_hbm_ops": round(min(reuse[o["name"]] for o in ops if o["bound"] == "hbm") / 1e6),

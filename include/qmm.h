@@ -326,6 +326,39 @@ int smooth_quant_w8a8_gemm_noalloc(const void* X, int x_dtype, const float* smoo
                                    const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int y_dtype,
                                    void* stream);
 
+/* ---------------------------------------------------------------------------
+ * FP8 E4M3 W8A8 -- 8-bit floating-point weights and activations on the fp8
+ * matrix cores.  Sources: "How quantization works" (the fake-quantization
+ * listing: s = max|x| / 448, E4M3's largest value, then x / s cast to E4M3;
+ * "Mainstream schemes at a glance", FP8 row: FP8 weights and activations with
+ * dynamic or static scales); "Quantization: Smaller Weights, Same Answers
+ * (Mostly)" ("What about FP8, MXFP4, NVFP4 and GGUF?": E4M3, 4 exponent and 3
+ * mantissa bits, up to 448).
+ * Codes are OCP E4M3 ("E4M3FN": exponent bias 7, no infinities, largest
+ * finite 448) bytes; the conversion of the correctly rounded fp32 quotient
+ * x / s rounds to nearest even and gives +-448 from 448 up.  The absmax is
+ * floored at 1e-8 (as the INT8 path).
+ * ------------------------------------------------------------------------- */
+
+/* q [rows, K] = E4M3(X / s) with s = max(max|X|, 1e-8) / 448 per row
+ * (per_tensor == 0: per token for activations, per output channel for
+ * weights) or for the whole matrix (per_tensor != 0, the listing's form; the
+ * scale is written to every scale[row]).  X QMM_F32 / QMM_BF16 / QMM_F16,
+ * K % 64 == 0. */
+int fp8_quantize(const void* X, int x_dtype, int64_t rows, int64_t K, int per_tensor, uint8_t* q, float* scale,
+                 void* stream);
+
+/* Y [M, N] = (sum_k E4M3(qX[m,k]) E4M3(qW[n,k])) * x_scale[m] * w_scale[n],
+ * products exact, fp32 accumulation, Y QMM_BF16 or QMM_F32.  K % 64 == 0,
+ * K <= 131008. */
+int fp8_gemm(const uint8_t* qX, const float* x_scale, const uint8_t* qW, const float* w_scale, int64_t M, int64_t N,
+             int64_t K, void* Y, int y_dtype, void* stream);
+
+/* The online FP8 step: per-token fp8_quantize of X into `workspace` (at
+ * least sq_workspace_bytes(M, K) bytes, 16-byte aligned), then fp8_gemm. */
+int fp8_w8a8_gemm(const void* X, int x_dtype, const uint8_t* qW, const float* w_scale, int64_t M, int64_t N,
+                  int64_t K, void* Y, int y_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

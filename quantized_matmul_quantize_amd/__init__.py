@@ -24,6 +24,7 @@ __all__ = [
     "w4_repack_from_plain", "w4_repack_to_plain", "w8a16_gemv",
     "sq_smooth_factors", "sq_quantize_weight", "sq_quantize_activation", "sq_quantize_activation_per_tensor",
     "sq_int8_gemm", "sq_workspace_bytes", "smooth_quant_w8a8_gemm", "smooth_quant_w8a8_gemm_noalloc",
+    "fp8_quantize", "fp8_gemm", "fp8_w8a8_gemm",
 ]
 
 F32, F16, BF16, I32 = 0, 1, 2, 3
@@ -75,6 +76,9 @@ _SIGS = {
     "sq_workspace_bytes": ([_I64, _I64], _SZ),
     "smooth_quant_w8a8_gemm": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
     "smooth_quant_w8a8_gemm_noalloc": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
+    "fp8_quantize": ([_P, _I, _I64, _I64, _I, _P, _P, _P], _I),
+    "fp8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
+    "fp8_w8a8_gemm": ([_P, _I, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
 }
 
 
@@ -506,4 +510,60 @@ def smooth_quant_w8a8_gemm_noalloc(X: torch.Tensor, smooth: Optional[torch.Tenso
     M, N, K, dev, out = _online_args(X, smooth, qW, w_scale, out, out_dtype)
     _call("smooth_quant_w8a8_gemm_noalloc", _ptr(X), _dt(X.dtype), _ptr(smooth), _ptr(qW), _ptr(w_scale), M, N, K,
           _ptr(out), _dt(out.dtype), _stream(X))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 W8A8 (codes are torch.uint8 holding OCP E4M3 bytes; view them as
+# torch.float8_e4m3fn to read the values).
+# ---------------------------------------------------------------------------
+def fp8_quantize(X: torch.Tensor, per_tensor: bool = False):
+    """-> (q uint8 [rows, K] E4M3 codes, scale f32 [rows]); s = max|x| / 448 per
+    row, or one for the whole matrix (repeated per row) when per_tensor."""
+    _req(X, "X", _FLOATS, ndim=2)
+    rows, K = X.shape
+    dev = _place(X=X)
+    q = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+    s = torch.empty(rows, dtype=torch.float32, device=dev)
+    _call("fp8_quantize", _ptr(X), _dt(X.dtype), rows, K, int(per_tensor), _ptr(q), _ptr(s), _stream(X))
+    return q, s
+
+
+def fp8_gemm(qX, x_scale, qW, w_scale, out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """Y [M, N] = (E4M3(qX) E4M3(qW)^T) * x_scale[m] * w_scale[n] (fp32 accumulation)."""
+    _req(qX, "qX", (torch.uint8,), ndim=2)
+    M, K = qX.shape
+    _req(qW, "qW", (torch.uint8,), shape=(None, K))
+    N = qW.shape[0]
+    _req(x_scale, "x_scale", (torch.float32,), shape=(M,))
+    _req(w_scale, "w_scale", (torch.float32,), shape=(N,))
+    odt = out.dtype if out is not None else out_dtype
+    _out(out, (M, N), odt)
+    dev = _place(qX=qX, qW=qW, x_scale=x_scale, w_scale=w_scale, out=out)
+    out = _alloc(out, (M, N), odt, dev)
+    _call("fp8_gemm", _ptr(qX), _ptr(x_scale), _ptr(qW), _ptr(w_scale), M, N, K, _ptr(out), _dt(out.dtype),
+          _stream(qX))
+    return out
+
+
+def fp8_w8a8_gemm(X: torch.Tensor, qW, w_scale, out_dtype: torch.dtype = torch.bfloat16,
+                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Online FP8 step: per-token E4M3 quantization of X, then fp8_gemm."""
+    _req(X, "X", _FLOATS, ndim=2)
+    M, K = X.shape
+    _req(qW, "qW", (torch.uint8,), shape=(None, K))
+    N = qW.shape[0]
+    _req(w_scale, "w_scale", (torch.float32,), shape=(N,))
+    odt = out.dtype if out is not None else out_dtype
+    _out(out, (M, N), odt)
+    if workspace is not None:
+        _req(workspace, "workspace", (torch.uint8,), ndim=1)
+        if workspace.numel() < sq_workspace_bytes(M, K):
+            raise ValueError(f"workspace holds {workspace.numel()} bytes; {sq_workspace_bytes(M, K)} needed")
+    dev = _place(X=X, qW=qW, w_scale=w_scale, out=out, workspace=workspace)
+    out = _alloc(out, (M, N), odt, dev)
+    if workspace is None:
+        workspace = torch.empty(sq_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    _call("fp8_w8a8_gemm", _ptr(X), _dt(X.dtype), _ptr(qW), _ptr(w_scale), M, N, K, _ptr(out), _dt(out.dtype),
+          _ptr(workspace), workspace.numel(), _stream(X))
     return out

@@ -366,31 +366,6 @@ __device__ __forceinline__ uint32_t pair_from_bytes(uint32_t w, int b0) {
   }
 }
 
-// The 16 pairs of a lane's 32 codes (weights 2j, 2j+1 in pair j).
-template <int XDT, int BITS>
-__device__ __forceinline__ void pairs32(const Lane32<BITS>& l, uint32_t magic, uint32_t p[16]) {
-  if constexpr (BITS == 4) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) Int4Magic<XDT>::unpack(l.w[c], magic, &p[4 * c]);
-  } else if constexpr (BITS == 8) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      p[2 * c] = pair_from_bytes<XDT>(l.w[c], 0);
-      p[2 * c + 1] = pair_from_bytes<XDT>(l.w[c], 2);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int pos = 6 * j;
-      const int wi = pos >> 5;
-      const int sh = pos & 31;
-      uint32_t f = l.w[wi] >> sh;
-      if (sh > 26) f |= l.w[wi + 1] << (32 - sh);
-      p[j] = pair_from_field6<XDT>(f, magic);
-    }
-  }
-}
-
 template <int YDT>
 __device__ __forceinline__ void store_out(void* y, int64_t idx, float v) {
   if constexpr (YDT == QMM_F32) {
@@ -404,21 +379,93 @@ __device__ __forceinline__ void store_out(void* y, int64_t idx, float v) {
 
 // ----------------------------------------------------------------------------
 // Vector-ALU GEMV for one or two tokens: a block of 4 wavefronts owns 8
-// weight rows; per step a lane takes 32 weights of each row (one group's
-// scale and zero-point per row), converts them to pairs and multiplies with
-// v_dot2 against the activations as loaded; per lane and row the group fold
-// s (sum (off + q) x - (off + z) sum x) is exact in the products.
+// weight rows; per step a lane takes a slice of each row -- 32 weights of 3-
+// or 4-bit codes (12 or 16 bytes), 16 weights of 8-bit codes (16 bytes) --
+// inside one group (one scale and zero-point per row), converts it to pairs
+// and multiplies with v_dot2 against the activations as loaded; per lane and
+// row the group fold s (sum (off + q) x - (off + z) sum x) is exact in the
+// products.  The scale type is a template parameter, so every load of a step
+// is issued before any arithmetic.
 // ----------------------------------------------------------------------------
 constexpr int kFmtWaves = 4;
 constexpr int kFmtRows = 8;
-constexpr int64_t kFmtStepK = kFmtWaves * kWave * 32;
 
-template <int XDT, int YDT, int B, int BITS>
+template <int BITS>
+struct Slice {
+  static constexpr int kWeights = BITS == 8 ? 16 : 32;   // weights of a row per lane per step
+  static constexpr int kWords = BITS == 3 ? 3 : 4;       // code words per lane per row
+  static constexpr int kPairs = kWeights / 2;
+  static constexpr int kXVec = kWeights / 8;             // 16-byte activation loads per token
+  uint32_t w[kWords];
+};
+
+template <int BITS>
+__device__ __forceinline__ void load_slice(const uint8_t* p, Slice<BITS>& sl) {
+  if constexpr (BITS == 3) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    sl.w[0] = __builtin_nontemporal_load(q);
+    sl.w[1] = __builtin_nontemporal_load(q + 1);
+    sl.w[2] = __builtin_nontemporal_load(q + 2);
+  } else {
+    const u32x4 a = ld16_nt(p);
+    sl.w[0] = a.x; sl.w[1] = a.y; sl.w[2] = a.z; sl.w[3] = a.w;
+  }
+}
+
+// Code c (0..31) of a 3-bit slice: bits 3c..3c+2 of the 96-bit string.
+__device__ __forceinline__ uint32_t code3(const uint32_t w[3], int c) {
+  const int pos = 3 * c;
+  const int wi = pos >> 5;
+  const int sh = pos & 31;
+  if (sh <= 29) return __builtin_amdgcn_ubfe(w[wi], sh, 3);
+  return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 7u;
+}
+
+template <int XDT>
+__device__ __forceinline__ uint32_t pair3(uint32_t lo, uint32_t hi, uint32_t magic) {
+  // two 3-bit codes one step below the 4-bit nibble position (Int3Magic)
+  if constexpr (XDT == QMM_BF16) {
+    return (lo << 4) | (hi << 20) | magic;
+  } else {
+    return (lo << 7) | (hi << 23) | magic;
+  }
+}
+
+template <int XDT, int BITS>
+__device__ __forceinline__ void slice_pairs(const Slice<BITS>& sl, uint32_t magic, uint32_t p[Slice<BITS>::kPairs]) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) Int4Magic<XDT>::unpack(sl.w[c], magic, &p[4 * c]);
+  } else if constexpr (BITS == 8) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      p[2 * c] = pair_from_bytes<XDT>(sl.w[c], 0);
+      p[2 * c + 1] = pair_from_bytes<XDT>(sl.w[c], 2);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) p[j] = pair3<XDT>(code3(sl.w, 2 * j), code3(sl.w, 2 * j + 1), magic);
+  }
+}
+
+template <bool S16>
+__device__ __forceinline__ float scale_at(const void* scales, int64_t idx) {
+  if constexpr (S16) {
+    return static_cast<float>(static_cast<const _Float16*>(scales)[idx]);
+  } else {
+    return static_cast<const float*>(scales)[idx];
+  }
+}
+
+template <int XDT, int YDT, int B, int BITS, bool S16>
 __global__ __launch_bounds__(256) void gemv_fmt_kernel(const uint8_t* __restrict__ codes,
                                                        const void* __restrict__ scales,
                                                        const uint8_t* __restrict__ zeros, int64_t N, int64_t K, int lg,
-                                                       int s16, const uint16_t* __restrict__ x, void* __restrict__ y) {
+                                                       const uint16_t* __restrict__ x, void* __restrict__ y) {
   constexpr int R = kFmtRows;
+  using Sl = Slice<BITS>;
+  constexpr int LW = Sl::kWeights;
+  constexpr int64_t kStep = kFmtWaves * kWave * LW;
   using Mg = Int4Magic<XDT>;
   constexpr float kOff = PairOff<XDT, BITS>::value;
   const int lane = threadIdx.x & (kWave - 1);
@@ -428,7 +475,6 @@ __global__ __launch_bounds__(256) void gemv_fmt_kernel(const uint8_t* __restrict
   const int64_t G = K >> lg;
   const int64_t zrb = zero_row_bytes(G, BITS);
   const int64_t crb = code_row_bytes(K, BITS);
-  const bool h16 = s16 != 0;
   int64_t rows[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) rows[r] = (row0 + r < N) ? row0 + r : N - 1;
@@ -438,40 +484,40 @@ __global__ __launch_bounds__(256) void gemv_fmt_kernel(const uint8_t* __restrict
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
 
-  for (int64_t k0 = 0; k0 < K; k0 += kFmtStepK) {
-    if (k0 + wave * (kWave * 32) >= K) break;
-    const int64_t kb_raw = k0 + wave * (kWave * 32) + lane * 32;
+  for (int64_t k0 = 0; k0 < K; k0 += kStep) {
+    if (k0 + wave * (kWave * LW) >= K) break;
+    const int64_t kb_raw = k0 + wave * (kWave * LW) + lane * LW;
     const bool inside = kb_raw < K;
-    const int64_t kb = inside ? kb_raw : K - 32;
-    u32x4 xraw[B][4];
+    const int64_t kb = inside ? kb_raw : K - LW;
+    u32x4 xraw[B][Sl::kXVec];
 #pragma unroll
     for (int b = 0; b < B; ++b)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) xraw[b][c] = ld16(x + b * K + kb + 8 * c);
+      for (int c = 0; c < Sl::kXVec; ++c) xraw[b][c] = ld16(x + b * K + kb + 8 * c);
     const int64_t g = kb >> lg;
     float sc[R];
     uint32_t zb[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      sc[r] = load_scale(scales, rows[r] * G + g, h16);
+      sc[r] = scale_at<S16>(scales, rows[r] * G + g);
       zb[r] = load_zero<BITS>(zeros + rows[r] * zrb, g);
     }
-    Lane32<BITS> cw[R];
+    Sl cw[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) load32<BITS>(codes + rows[r] * crb + kb * BITS / 8, cw[r]);
+    for (int r = 0; r < R; ++r) load_slice<BITS>(codes + rows[r] * crb + kb * BITS / 8, cw[r]);
     __builtin_amdgcn_sched_barrier(0);
     if (!inside) {
 #pragma unroll
       for (int b = 0; b < B; ++b)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) xraw[b][c] = u32x4{0u, 0u, 0u, 0u};
+        for (int c = 0; c < Sl::kXVec; ++c) xraw[b][c] = u32x4{0u, 0u, 0u, 0u};
     }
-    uint32_t xp[B][16];
+    uint32_t xp[B][Sl::kPairs];
     float xs[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < Sl::kXVec; ++c) {
         xp[b][4 * c] = xraw[b][c].x;
         xp[b][4 * c + 1] = xraw[b][c].y;
         xp[b][4 * c + 2] = xraw[b][c].z;
@@ -479,7 +525,7 @@ __global__ __launch_bounds__(256) void gemv_fmt_kernel(const uint8_t* __restrict
       }
       float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) {
+      for (int j = 0; j < Sl::kPairs; j += 2) {
         s0 = dot2<XDT>(xp[b][j], Mg::one_pair, s0);
         s1 = dot2<XDT>(xp[b][j + 1], Mg::one_pair, s1);
       }
@@ -487,14 +533,14 @@ __global__ __launch_bounds__(256) void gemv_fmt_kernel(const uint8_t* __restrict
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      uint32_t p[16];
-      pairs32<XDT, BITS>(cw[r], magic, p);
+      uint32_t p[Sl::kPairs];
+      slice_pairs<XDT, BITS>(cw[r], magic, p);
       const float zo = kOff + static_cast<float>(zb[r]);
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; j += 2) {
+        for (int j = 0; j < Sl::kPairs; j += 2) {
           a0 = dot2<XDT>(p[j], xp[b][j], a0);
           a1 = dot2<XDT>(p[j + 1], xp[b][j + 1], a1);
         }
@@ -582,11 +628,11 @@ __device__ __forceinline__ void load_pairs8(const uint8_t* crow, int64_t k, uint
   }
 }
 
-template <int XDT, int YDT, int BITS>
+template <int XDT, int YDT, int BITS, bool S16>
 __global__ __launch_bounds__(256) void wq_mfma_kernel(const uint8_t* __restrict__ codes,
                                                       const void* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros, int64_t N, int64_t K, int lg,
-                                                      int s16, const uint16_t* __restrict__ x, int64_t M,
+                                                      const uint16_t* __restrict__ x, int64_t M,
                                                       void* __restrict__ y) {
   using Mg = Int4Magic<XDT>;
   constexpr int RT = kMfmaRT;
@@ -602,7 +648,6 @@ __global__ __launch_bounds__(256) void wq_mfma_kernel(const uint8_t* __restrict_
   const int64_t G = K >> lg;
   const int64_t zrb = zero_row_bytes(G, BITS);
   const int64_t crb = code_row_bytes(K, BITS);
-  const bool h16 = s16 != 0;
   const int64_t nch = K >> 5;
   const int64_t per = (nch + kFmtWaves - 1) / kFmtWaves;
   const int64_t cbeg = wave * per;
@@ -641,7 +686,7 @@ __global__ __launch_bounds__(256) void wq_mfma_kernel(const uint8_t* __restrict_
     if (fold) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        sv[rt] = load_scale(scales, srow[rt] * G + g, h16);
+        sv[rt] = scale_at<S16>(scales, srow[rt] * G + g);
         zv[rt] = kOff + static_cast<float>(load_zero<BITS>(zeros + srow[rt] * zrb, g));
       }
     }
@@ -777,19 +822,26 @@ void launch_deq_fmt(const uint8_t* codes, const void* scales, const uint8_t* zer
   }
 }
 
+template <int XDT, int YDT, int BITS, bool S16>
+void launch_mm_fmt_s(const uint8_t* codes, const void* scales, const uint8_t* zeros, int64_t N, int64_t K, int lg,
+                     const uint16_t* x, int64_t M, void* y, hipStream_t s) {
+  if (M == 1) {
+    gemv_fmt_kernel<XDT, YDT, 1, BITS, S16><<<dim3(static_cast<unsigned>(ceil_div(N, kFmtRows))), 256, 0, s>>>(
+        codes, scales, zeros, N, K, lg, x, y);
+  } else if (M == 2) {
+    gemv_fmt_kernel<XDT, YDT, 2, BITS, S16><<<dim3(static_cast<unsigned>(ceil_div(N, kFmtRows))), 256, 0, s>>>(
+        codes, scales, zeros, N, K, lg, x, y);
+  } else {
+    const dim3 grid(static_cast<unsigned>(ceil_div(N, 16 * kMfmaRT)), static_cast<unsigned>(ceil_div(M, 16)));
+    wq_mfma_kernel<XDT, YDT, BITS, S16><<<grid, 256, 0, s>>>(codes, scales, zeros, N, K, lg, x, M, y);
+  }
+}
+
 template <int XDT, int YDT, int BITS>
 void launch_mm_fmt_t(const uint8_t* codes, const void* scales, const uint8_t* zeros, int64_t N, int64_t K, int lg,
                      int s16, const uint16_t* x, int64_t M, void* y, hipStream_t s) {
-  if (M == 1) {
-    gemv_fmt_kernel<XDT, YDT, 1, BITS><<<dim3(static_cast<unsigned>(ceil_div(N, kFmtRows))), 256, 0, s>>>(
-        codes, scales, zeros, N, K, lg, s16, x, y);
-  } else if (M == 2) {
-    gemv_fmt_kernel<XDT, YDT, 2, BITS><<<dim3(static_cast<unsigned>(ceil_div(N, kFmtRows))), 256, 0, s>>>(
-        codes, scales, zeros, N, K, lg, s16, x, y);
-  } else {
-    const dim3 grid(static_cast<unsigned>(ceil_div(N, 16 * kMfmaRT)), static_cast<unsigned>(ceil_div(M, 16)));
-    wq_mfma_kernel<XDT, YDT, BITS><<<grid, 256, 0, s>>>(codes, scales, zeros, N, K, lg, s16, x, M, y);
-  }
+  if (s16) launch_mm_fmt_s<XDT, YDT, BITS, true>(codes, scales, zeros, N, K, lg, x, M, y, s);
+  else launch_mm_fmt_s<XDT, YDT, BITS, false>(codes, scales, zeros, N, K, lg, x, M, y, s);
 }
 
 template <int BITS>

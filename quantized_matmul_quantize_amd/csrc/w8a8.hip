@@ -27,6 +27,7 @@ namespace {
 constexpr float kQ8 = 127.0f;
 constexpr float kAbsFloor = 1e-8f;
 constexpr float kSmoothFloor = 1e-5f;
+constexpr float kFp8Max = 448.0f;   // largest finite E4M3
 // Largest K (a multiple of 64) with 128 * 128 * K < 2^31: no int32 sum can overflow.
 constexpr int64_t kMaxK = 131008;
 
@@ -166,6 +167,40 @@ __device__ __forceinline__ void quant8_int8(const float v[8], float s, float y, 
   *hi = h;
 }
 
+// FP8 E4M3 ("E4M3FN": bias 7, 3 mantissa bits, largest finite 448) code of
+// t, round to nearest even, magnitudes from 448 up giving 448 (reading R25).
+__device__ __forceinline__ uint32_t e4m3_code(float t) {
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {                       // |t| >= 448
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {                 // |t| < 2^-6: multiples of 2^-9, rounded to nearest even
+    code = static_cast<uint32_t>(rintf(__uint_as_float(a) * 512.0f));
+  } else {                                      // keep 3 of the 23 mantissa bits, nearest even
+    const uint32_t keep = a >> 20;
+    const uint32_t rest = a & 0xFFFFFu;
+    const uint32_t up = (rest > 0x80000u) || (rest == 0x80000u && (keep & 1u));
+    code = keep + up - (120u << 3);             // exponent bias 127 -> 7; a carry moves into the exponent
+  }
+  return sign | code;
+}
+
+// E4M3 codes of 8 values with scale s: e4m3(fl32(v / s)), correctly rounded
+// division (the quotient itself is rounded, not only its integer part).
+__device__ __forceinline__ void quant8_fp8(const float v[8], float s, uint32_t* lo, uint32_t* hi) {
+  uint32_t l = 0, h = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t byte = e4m3_code(v[i] / s);
+    if (i < 4) l |= byte << (8 * i);
+    else h |= byte << (8 * (i - 4));
+  }
+  *lo = l;
+  *hi = h;
+}
+
 // Loads chunk c of the batch starting at `base` for every lane (zeros past K)
 // and applies the smoothing; all loads are issued before any arithmetic.
 template <int DT, int MODE, bool SM>
@@ -204,10 +239,13 @@ __device__ __forceinline__ void rq_load_batch(const uint8_t* arow, const float* 
 // tensor: PHASE 1 writes each row's absmax to scale[row]; tensor_scale_kernel
 // turns them into the tensor's scale, stored for every row; PHASE 2 then
 // quantizes each row with scale[row].
-template <int DT, int MODE, bool SM, int PHASE>
+// FMT 1: FP8 E4M3 codes with s = max|x| / 448 ("How quantization works",
+// fake-quantization listing) instead of INT8 with max|x| / 127.
+template <int DT, int MODE, bool SM, int PHASE, int FMT = 0>
 __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restrict__ a, const float* __restrict__ smooth,
                                                         int64_t rows, int64_t K, int8_t* __restrict__ q,
                                                         float* __restrict__ scale) {
+  constexpr float kLevels = FMT == 1 ? kFp8Max : kQ8;
   constexpr int kElem = DT == QMM_F32 ? 4 : 2;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
@@ -233,7 +271,7 @@ __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restric
       if (lane == 0) scale[row] = amax;
       return;
     }
-    s = fmaxf(amax, kAbsFloor) / kQ8;
+    s = fmaxf(amax, kAbsFloor) / kLevels;
     if (lane == 0) scale[row] = s;
   }
   const float r = 1.0f / s;   // correctly rounded reciprocal
@@ -245,7 +283,8 @@ __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restric
       const int64_t k = base + static_cast<int64_t>(c) * (kWave * 8) + lane * 8;
       if (k < K) {
         uint32_t lo, hi;
-        quant8_int8(v[c], s, r, &lo, &hi);
+        if constexpr (FMT == 1) quant8_fp8(v[c], s, &lo, &hi);
+        else quant8_int8(v[c], s, r, &lo, &hi);
         *reinterpret_cast<uint2*>(q + row * K + k) = make_uint2(lo, hi);
       }
     }
@@ -255,6 +294,7 @@ __global__ __launch_bounds__(256) void rowquant8_kernel(const uint8_t* __restric
 // The tensor's scale from the rows' absmax values in scale[0..rows): a =
 // fl32(max(max_m absmax_m, 1e-8) / 127), then written to every scale[m].  One
 // block; the maximum is exact, so the order of the reduction does not matter.
+template <int FMT = 0>
 __global__ __launch_bounds__(256) void tensor_scale_kernel(float* __restrict__ scale, int64_t rows) {
   __shared__ float part[256 / kWave];
   float m = 0.0f;
@@ -264,7 +304,7 @@ __global__ __launch_bounds__(256) void tensor_scale_kernel(float* __restrict__ s
   __syncthreads();
   float a = part[0];
   for (int w = 1; w < static_cast<int>(blockDim.x / kWave); ++w) a = fmaxf(a, part[w]);
-  a = fmaxf(a, kAbsFloor) / kQ8;
+  a = fmaxf(a, kAbsFloor) / (FMT == 1 ? kFp8Max : kQ8);
   for (int64_t i = threadIdx.x; i < rows; i += blockDim.x) scale[i] = a;
 }
 
@@ -340,10 +380,39 @@ constexpr int kP4 = 272;                        // 64 x 4-byte outputs
 constexpr int kEpiWave = 64 * kP4;              // per-wavefront epilogue region (64 rows)
 static_assert(64 * kP2 <= kEpiWave && 8 * kEpiWave <= static_cast<int>(kGemmLds), "epilogue must fit");
 
-template <int YDT>
+// FP8: the same tiles and pipeline with E4M3 operands; each 16-byte fragment
+// (16 k of one row) feeds two v_mfma_f32_16x16x32_fp8_fp8 (8 k each, fp32
+// accumulation): the first takes bytes 0-7 of every lane, the second bytes
+// 8-15, so A and B pair the same k.
+template <bool FP8>
+struct GemmAcc {
+  typedef i32x4 type;
+};
+template <>
+struct GemmAcc<true> {
+  typedef f32x4 type;
+};
+
+template <bool FP8>
+__device__ __forceinline__ void mfma_frag(const i32x4& b, const i32x4& a, typename GemmAcc<FP8>::type& acc) {
+  if constexpr (FP8) {
+    const long b0 = static_cast<long>(static_cast<uint32_t>(b[0])) | (static_cast<long>(b[1]) << 32);
+    const long b1 = static_cast<long>(static_cast<uint32_t>(b[2])) | (static_cast<long>(b[3]) << 32);
+    const long a0 = static_cast<long>(static_cast<uint32_t>(a[0])) | (static_cast<long>(a[1]) << 32);
+    const long a1 = static_cast<long>(static_cast<uint32_t>(a[2])) | (static_cast<long>(a[3]) << 32);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(b0, a0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(b1, a1, acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a, acc, 0, 0, 0);
+  }
+}
+
+template <int YDT, bool FP8 = false>
 __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__ A, const float* __restrict__ ascale,
                                                        const int8_t* __restrict__ B, const float* __restrict__ bscale,
                                                        int64_t M, int64_t N, int64_t K, void* __restrict__ Y) {
+  using Acc = typename GemmAcc<FP8>::type;
+  constexpr int kMfmaPerFrag = FP8 ? 2 : 1;
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -424,11 +493,11 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   };
 
-  i32x4 acc[4][4];
+  Acc acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
   // The epilogue's scales, fetched now so that their latency hides behind
   // the main loop: tile (i, j) register r of lane l is row 16 i + l % 16 and
@@ -465,16 +534,16 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) mfma_frag<FP8>(fb0[j], fa0[i], acc[i][j]);
 #pragma unroll
     for (int g = 0; g < 6; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerFrag, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerFrag, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerFrag, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<kLoadsA8 + kLoadsB8>();
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
@@ -483,10 +552,10 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) mfma_frag<FP8>(fb1[j], fa1[i], acc[i][j]);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerFrag, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
     }
     s0 = s1;
@@ -564,7 +633,7 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 
 bool float_dtype(int dt) { return dt == QMM_F32 || dt == QMM_BF16 || dt == QMM_F16; }
 
-template <int MODE, int PHASE = 0>
+template <int MODE, int PHASE = 0, int FMT = 0>
 int launch_rowquant(const void* a, int dt, const float* smooth, int64_t rows, int64_t K, int8_t* q, float* scale,
                     hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(ceil_div(rows, 4)));
@@ -572,15 +641,15 @@ int launch_rowquant(const void* a, int dt, const float* smooth, int64_t rows, in
   const uint8_t* p = static_cast<const uint8_t*>(a);
   if (smooth) {
     switch (dt) {
-      case QMM_BF16: rowquant8_kernel<QMM_BF16, MODE, true, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
-      case QMM_F16: rowquant8_kernel<QMM_F16, MODE, true, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
-      default: rowquant8_kernel<QMM_F32, MODE, true, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      case QMM_BF16: rowquant8_kernel<QMM_BF16, MODE, true, PHASE, FMT><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      case QMM_F16: rowquant8_kernel<QMM_F16, MODE, true, PHASE, FMT><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      default: rowquant8_kernel<QMM_F32, MODE, true, PHASE, FMT><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
     }
   } else {
     switch (dt) {
-      case QMM_BF16: rowquant8_kernel<QMM_BF16, MODE, false, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
-      case QMM_F16: rowquant8_kernel<QMM_F16, MODE, false, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
-      default: rowquant8_kernel<QMM_F32, MODE, false, PHASE><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      case QMM_BF16: rowquant8_kernel<QMM_BF16, MODE, false, PHASE, FMT><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      case QMM_F16: rowquant8_kernel<QMM_F16, MODE, false, PHASE, FMT><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
+      default: rowquant8_kernel<QMM_F32, MODE, false, PHASE, FMT><<<grid, block, 0, s>>>(p, smooth, rows, K, q, scale); break;
     }
   }
   return launch_status();
@@ -610,16 +679,16 @@ int check_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float*
   return QMM_OK;
 }
 
-template <int YDT>
+template <int YDT, bool FP8 = false>
 void launch_gemm_t(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
                    int64_t K, void* Y, hipStream_t s) {
   // 144 KiB of dynamic LDS; the attribute is cheap to set and idempotent, so
   // it is set on every launch (no per-device bookkeeping).
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&i8_gemm_kernel<YDT>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&i8_gemm_kernel<YDT, FP8>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGemmLds));
   const int64_t tiles = ceil_div(M, kBM) * ceil_div(N, kBN);
   const dim3 grid(static_cast<unsigned>(ceil_div(tiles, kXcds) * kXcds));
-  i8_gemm_kernel<YDT><<<grid, dim3(512), kGemmLds, s>>>(qX, xs, qW, ws, M, N, K, Y);
+  i8_gemm_kernel<YDT, FP8><<<grid, dim3(512), kGemmLds, s>>>(qX, xs, qW, ws, M, N, K, Y);
 }
 
 void launch_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
@@ -629,6 +698,14 @@ void launch_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const floa
     case QMM_F32: launch_gemm_t<QMM_F32>(qX, xs, qW, ws, M, N, K, Y, s); break;
     default: launch_gemm_t<QMM_BF16>(qX, xs, qW, ws, M, N, K, Y, s); break;
   }
+}
+
+void launch_gemm_fp8(const uint8_t* qX, const float* xs, const uint8_t* qW, const float* ws, int64_t M, int64_t N,
+                     int64_t K, void* Y, int ydt, hipStream_t s) {
+  const int8_t* a = reinterpret_cast<const int8_t*>(qX);
+  const int8_t* b = reinterpret_cast<const int8_t*>(qW);
+  if (ydt == QMM_F32) launch_gemm_t<QMM_F32, true>(a, xs, b, ws, M, N, K, Y, s);
+  else launch_gemm_t<QMM_BF16, true>(a, xs, b, ws, M, N, K, Y, s);
 }
 
 }  // namespace
@@ -692,7 +769,7 @@ extern "C" int sq_quantize_activation_per_tensor(const void* X, int x_dtype, con
   hipStream_t s = as_stream(stream);
   st = launch_rowquant<1, 1>(X, x_dtype, smooth, M, K, qX, x_scale, s);
   if (st != QMM_OK) return st;
-  tensor_scale_kernel<<<1, 256, 0, s>>>(x_scale, M);
+  tensor_scale_kernel<0><<<1, 256, 0, s>>>(x_scale, M);
   st = launch_status();
   if (st != QMM_OK) return st;
   return launch_rowquant<1, 2>(X, x_dtype, smooth, M, K, qX, x_scale, s);
@@ -819,4 +896,72 @@ extern "C" int smooth_quant_w8a8_gemm_noalloc(const void* X, int x_dtype, const 
   st = scratch_for(s, &ws);
   if (st != QMM_OK) return st;
   return online_launch(X, x_dtype, smooth, qW, w_scale, M, N, K, Y, y_dtype, ws, s);
+}
+
+// ----------------------------------------------------------------------------
+// FP8 E4M3 W8A8 ("How quantization works", the fake-quantization listing:
+// s = max|x| / 448, q = E4M3(x / s); "Mainstream schemes at a glance": FP8
+// weights and activations with dynamic or static scales).  The row quantizer
+// and the GEMM tiles above with E4M3 codes and fp8 matrix instructions.
+// ----------------------------------------------------------------------------
+namespace qmm {
+namespace {
+
+int check_fp8_gemm(const uint8_t* qX, const float* xs, const uint8_t* qW, const float* ws, int64_t M, int64_t N,
+                   int64_t K, const void* Y, int ydt) {
+  if (!qX || !qW || !Y || !xs || !ws) return QMM_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0) return QMM_EINVAL;
+  if (ydt != QMM_BF16 && ydt != QMM_F32) return (ydt == QMM_F16 || ydt == QMM_I32) ? QMM_EUNSUPPORTED : QMM_EINVAL;
+  if (K % 64 != 0) return QMM_EUNSUPPORTED;
+  if (K > kMaxK) return QMM_ERANGE;
+  if (!aligned(qX, 16) || !aligned(qW, 16) || !aligned(Y, 4) || !aligned(xs, 4) || !aligned(ws, 4))
+    return QMM_EALIGN;
+  return QMM_OK;
+}
+
+}  // namespace
+}  // namespace qmm
+
+extern "C" int fp8_quantize(const void* X, int x_dtype, int64_t rows, int64_t K, int per_tensor, uint8_t* q,
+                            float* scale, void* stream) {
+  int8_t* qq = reinterpret_cast<int8_t*>(q);
+  int st = check_rowquant(X, x_dtype, nullptr, rows, K, qq, scale);
+  if (st != QMM_OK) return st;
+  hipStream_t s = as_stream(stream);
+  if (!per_tensor) return launch_rowquant<1, 0, 1>(X, x_dtype, nullptr, rows, K, qq, scale, s);
+  st = launch_rowquant<1, 1, 1>(X, x_dtype, nullptr, rows, K, qq, scale, s);
+  if (st != QMM_OK) return st;
+  tensor_scale_kernel<1><<<1, 256, 0, s>>>(scale, rows);
+  st = launch_status();
+  if (st != QMM_OK) return st;
+  return launch_rowquant<1, 2, 1>(X, x_dtype, nullptr, rows, K, qq, scale, s);
+}
+
+extern "C" int fp8_gemm(const uint8_t* qX, const float* x_scale, const uint8_t* qW, const float* w_scale, int64_t M,
+                        int64_t N, int64_t K, void* Y, int y_dtype, void* stream) {
+  int st = check_fp8_gemm(qX, x_scale, qW, w_scale, M, N, K, Y, y_dtype);
+  if (st != QMM_OK) return st;
+  launch_gemm_fp8(qX, x_scale, qW, w_scale, M, N, K, Y, y_dtype, as_stream(stream));
+  return launch_status();
+}
+
+extern "C" int fp8_w8a8_gemm(const void* X, int x_dtype, const uint8_t* qW, const float* w_scale, int64_t M, int64_t N,
+                             int64_t K, void* Y, int y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!X || !qW || !w_scale || !Y) return QMM_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0) return QMM_EINVAL;
+  if (!float_dtype(x_dtype)) return x_dtype == QMM_I32 ? QMM_EUNSUPPORTED : QMM_EINVAL;
+  if (y_dtype != QMM_BF16 && y_dtype != QMM_F32)
+    return (y_dtype == QMM_F16 || y_dtype == QMM_I32) ? QMM_EUNSUPPORTED : QMM_EINVAL;
+  if (K % 64 != 0) return QMM_EUNSUPPORTED;
+  if (K > kMaxK) return QMM_ERANGE;
+  if (!aligned(X, 16) || !aligned(qW, 16) || !aligned(w_scale, 4) || !aligned(Y, 4)) return QMM_EALIGN;
+  if (!workspace || workspace_bytes < sq_workspace_bytes(M, K) || !aligned(workspace, 16)) return QMM_EWORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int8_t* qX = reinterpret_cast<int8_t*>(ws);
+  float* xs = reinterpret_cast<float*>(ws + (static_cast<size_t>(M) * static_cast<size_t>(K) + 255u) / 256u * 256u);
+  hipStream_t s = as_stream(stream);
+  int st = launch_rowquant<1, 0, 1>(X, x_dtype, nullptr, M, K, qX, xs, s);
+  if (st != QMM_OK) return st;
+  launch_gemm_fp8(reinterpret_cast<const uint8_t*>(qX), xs, qW, w_scale, M, N, K, Y, y_dtype, s);
+  return launch_status();
 }
