@@ -67,3 +67,11 @@ def random_w4(n: int, k: int, seed: int):
     z = g.integers(0, 16, size=(n, k // 128)).astype(np.uint8)
     s = (g.random((n, k // 128), dtype=np.float32) * np.float32(0.01) + np.float32(1e-4)).astype(np.float32)
     return q, s, z
+
+
+def stratified_rows(n: int, block: int) -> np.ndarray:
+    """One row in every block of `block` consecutive rows, its position in the
+    block cycling through 0..block-1, so a sample meets every output tile of
+    that height (and, across tiles, every position within one)."""
+    starts = np.arange(0, n, block)
+    return np.minimum(starts + (np.arange(len(starts)) % block), n - 1)

@@ -131,6 +131,27 @@ def test_dequantize(dtype, shape):
                       want.view(torch.uint8).numpy() if dtype != "f32" else want.numpy()), dtype
 
 
+@pytest.mark.parametrize("name,index", [("llama7b", 1), ("mlp70b", 0)])
+def test_dequantize_full_size(name, index):
+    # full-size matrices, where the dequantizer's persistent grid strides over
+    # its chunks several times: the GPU's own codes (bit-exact with the
+    # oracle's) dequantized to fp32 and bf16, every element bit for bit
+    wl = workloads.WORKLOADS[name]
+    w, _ = workloads.weight(wl, index)
+    codes, scales, zeros = run_and_compare(w, f"{name}[{index}] for dequantize")
+    q, s, z = oracle.asym_quantize(w.float().numpy())
+    del w
+    ref = oracle.asym_dequantize(q, s, z)
+    for dtype in ("f32", "bf16"):
+        note(f"dequantize full size {name}[{index}] -> {dtype}")
+        got = qmm.dequantize(codes, scales, zeros, dtype=TDT[dtype]).cpu()
+        want = torch.from_numpy(ref).to(TDT[dtype])
+        if dtype == "f32":
+            assert bits_equal(got.numpy(), want.numpy()), first_diff(got.numpy(), want.numpy())
+        else:
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
 def test_roundtrip_error_bound():
     # Quantize on the GPU, dequantize on the GPU: |w - w_hat| <= s/2 (+ fp32 rounding).
     wl = workloads.WORKLOADS["llama7b"]

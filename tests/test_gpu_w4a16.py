@@ -6,7 +6,7 @@ import torch
 import oracle
 import quantized_matmul_quantize_amd as qmm
 import workloads
-from gpu_util import assert_close, note, random_w4
+from gpu_util import assert_close, note, random_w4, stratified_rows
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -88,7 +88,9 @@ def test_gemv_full_size(name, index, B):
     q, s, z = quantized(wl, index)
     n, k = q.shape
     x = workloads.activations(wl, B, k, salt=index)
-    rows = None if B == 1 else np.sort(workloads.rng(50, n).choice(n, 2048, replace=False))
+    # B = 1: every row; more tokens: one row in every block of 8 (the row
+    # blocks of the vector-ALU kernel; each 16- or 32-row tile of the MFMA kernels)
+    rows = None if B == 1 else stratified_rows(n, 8)
     ydt = torch.float16 if wl.x_dtype == "f16" else torch.bfloat16
     gemv_case(q, s, z, x, torch.float32, f"{name}[{index}] B={B} f32", rows=rows)
     gemv_case(q, s, z, x, ydt, f"{name}[{index}] B={B} 16-bit", rows=rows)
@@ -147,13 +149,21 @@ def test_gemm_long_k_fallback(xdt, M, k):
 
 @pytest.mark.parametrize("M", [16, 64, 256])
 def test_gemm_full_size(M):
+    # M = 16 and 64: every output; M = 256: one weight row in every 16 (each
+    # 128-row tile of the shared-tile kernel sampled 8 times, at every row
+    # position within a 16-row MFMA slice), all 256 tokens
     wl = workloads.WORKLOADS["gemm"]
     q, s, z = quantized(wl, 0)
     n, k = q.shape
     x = workloads.activations(wl, M, k)
-    rows = np.sort(workloads.rng(51, M).choice(n, 1024, replace=False))
-    gemv_case(q, s, z, x, torch.bfloat16, f"gemm 14336x4096 M={M}", gemm=True, rows=rows)
-    gemv_case(q, s, z, x, torch.float32, f"gemm 14336x4096 M={M} f32", gemm=True, rows=rows)
+    rows = None if M <= 64 else stratified_rows(n, 16)
+    codes, scales, zeros = upload_w4(q, s, z)
+    xd = x.to(DEV)
+    ref = oracle.w4a16_reference(x.float().numpy(), *(a if rows is None else a[rows] for a in (q, s, z)))
+    for ydt in (torch.bfloat16, torch.float32):
+        note(f"w4a16_gemm 14336x4096 M={M} y={ydt} ({'all rows' if rows is None else f'{len(rows)} rows'})")
+        y = qmm.w4a16_gemm(codes, scales, zeros, xd, out_dtype=ydt).cpu()
+        assert_close(y if rows is None else y[:, rows], ref, f"gemm 14336x4096 M={M} {ydt}")
 
 
 def test_gemm_m1_equals_gemv():

@@ -7,7 +7,7 @@ import torch
 import oracle
 import quantized_matmul_quantize_amd as qmm
 import workloads
-from gpu_util import assert_close, bits_equal, first_diff, note
+from gpu_util import stratified_rows, assert_close, bits_equal, first_diff, note
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -74,7 +74,7 @@ def test_w8a16_after_weight_quantizer():
 @pytest.mark.parametrize("index,B", [(0, 1), (1, 1), (0, 8), (1, 8)])
 def test_w8a16_full_size(index, B):
     # the 70B-class MLP matrices at full size: quantized on the device, codes
-    # and outputs checked on 2048 sampled rows
+    # and outputs checked on one row of every 8-row block
     wl = workloads.WORKLOADS["mlp70b"]
     w, _ = workloads.weight(wl, index)
     n, k = w.shape
@@ -82,7 +82,7 @@ def test_w8a16_full_size(index, B):
     wd = w.to(DEV)
     qd, bd = qmm.sq_quantize_weight(wd)
     del wd
-    rows = np.sort(workloads.rng(96, n).choice(n, 2048, replace=False))
+    rows = stratified_rows(n, 8)          # one row in every 8-row block of the kernels
     qo, bo = oracle.sq_quantize_weight(w[rows].float().numpy(), None)
     qs = qd[torch.from_numpy(rows).to(DEV)].cpu().numpy()
     assert bits_equal(qs, qo), first_diff(qs, qo)

@@ -7,7 +7,7 @@ import torch
 import oracle
 import quantized_matmul_quantize_amd as qmm
 import workloads
-from gpu_util import assert_close, bits_equal, first_diff, note
+from gpu_util import stratified_rows, assert_close, bits_equal, first_diff, note
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -148,7 +148,9 @@ def test_w8a8_pipeline(mkn, ydt):
     torch.cuda.synchronize()
     rs = oracle.smooth_factors(oracle.col_absmax(xf), oracle.col_absmax(wf), 0.5)
     rqw, rb = oracle.sq_quantize_weight(wf, rs)
-    rows = np.arange(m) if m <= 256 else np.sort(workloads.rng(60, m).choice(m, 96, replace=False))
+    # all tokens of the small cases; at 2048 tokens one row in every 32 (each
+    # 256-row output tile sampled 8 times), all 4096 output columns
+    rows = np.arange(m) if m <= 256 else stratified_rows(m, 32)
     rqx, ra = oracle.sq_quantize_activation(xf[rows], rs)
     racc = oracle.int8_matmul_nt(rqx, rqw)
     assert np.array_equal(acc.cpu().numpy()[rows], racc)
