@@ -73,6 +73,7 @@ def lib(parallel: bool = False) -> ctypes.CDLL:
             "oq_e4m3_decode_array": [P, I64, P],
             "oq_fp8_quantize": [P, I64, I64, I64, P, P],
             "oq_fp8_matmul_nt": [P, P, I64, I64, I64, P],
+            "oq_llm_int8": [P, I64, I64, P, P, I64, F, I64, I, P, P, P, P, P],
         }
         for name, argtypes in sigs.items():
             fn = getattr(l, name)
@@ -452,3 +453,33 @@ def fp8_w8a8_reference(x, qw, b, parallel: bool = False):
     qx, a = fp8_quantize(x)
     acc = fp8_matmul_nt(qx, qw, parallel)
     return qx, a, acc * a.astype(np.float64)[:, None] * np.asarray(b, np.float32).astype(np.float64)[None, :]
+
+
+# --------------------------------------------------------------------------
+# LLM.int8() ("Quantization" (Engine Room ch. 15), "The Mathematics": the
+# vector-wise product with the outlier dimensions multiplied in 16-bit;
+# "Quantization: Smaller Weights, Same Answers (Mostly)", outlier family 1).
+# --------------------------------------------------------------------------
+def llm_int8_reference(x, qw, b, threshold: float, max_outliers=None, x_dtype: str = "bf16"):
+    """Mixed-precision decomposition of X W^T with per-output-channel INT8
+    weights (qw [N, K], b [N]) and 16-bit activations x [M, K] (as float32
+    values of `x_dtype`, "bf16" or "f16").  The first `max_outliers` columns
+    (in column order) whose largest |x| over the batch reaches `threshold`
+    are multiplied in 16-bit; the rest go through per-token INT8.
+    Returns (outlier columns int32 [kept], found, qX int8 [M, K], a f32 [M],
+    y fp64 [M, N])."""
+    x = _f32(x)
+    qw = np.ascontiguousarray(qw, np.int8)
+    b = _f32(b).reshape(-1)
+    m, k = x.shape
+    n, k2 = qw.shape
+    assert k == k2 and b.shape == (n,) and x_dtype in ("bf16", "f16")
+    cap = k if max_outliers is None else int(max_outliers)
+    idx = np.zeros(max(cap, 1), np.int32)
+    counts = np.zeros(2, np.int64)
+    qx = np.empty((m, k), np.int8)
+    a = np.empty(m, np.float32)
+    y = np.empty((m, n), np.float64)
+    _check(lib().oq_llm_int8(_p(x), m, k, _p(qw), _p(b), n, float(threshold), cap, int(x_dtype == "bf16"),
+                             _p(idx), _p(counts), _p(qx), _p(a), _p(y)), "llm_int8")
+    return idx[:counts[0]].copy(), int(counts[1]), qx, a, y

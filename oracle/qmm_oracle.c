@@ -45,10 +45,21 @@
  *  R6  clamp after adding the zero-point.
  *  R7  alpha = 0.5 uses sqrtf for both powers; other alpha use powf.
  *  R8  symmetric scales floor the absmax at `floor` (1e-8 in [HQ]).
+ *  R26 an input feature (column of X) is an outlier dimension of a batch when
+ *      some token's |x| in it reaches the threshold tau (>=); tau is an
+ *      argument.
+ *  R27 the weights are stored once, as per-output-channel INT8; the 16-bit
+ *      weight slice of the outlier product is that INT8 weight dequantized
+ *      (q * b) and rounded to the activations' 16-bit type (binary16
+ *      saturating at 65504 as in R24).
+ *  R28 the outlier columns are zero in X_q and take no part in a token's
+ *      absmax.
  */
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -524,6 +535,87 @@ int oq_scale_columns_div(const float* a, const float* s, int64_t rows, int64_t c
     for (int64_t i = 0; i < rows; ++i)
         for (int64_t j = 0; j < cols; ++j) out[i * cols + j] = a[i * cols + j] / s[j];
     return OQ_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* LLM.int8() mixed-precision decomposition.  [ER] "The Mathematics": the    */
+/* vector-wise scheme (one scale per row of X and per column of the product, */
+/* i.e. per output channel of the [N, K] weight) with the outlier feature    */
+/* dimensions removed from the integer product and multiplied in 16-bit,     */
+/* C = S_out (X_q W_q) + X_16 W_16; the history paragraph on LLM.int8() (a   */
+/* handful of systematically large dimensions, more than 99.9% of the values */
+/* still multiplied in 8-bit, half the memory).  [SW] "How do LLM-specific   */
+/* quantization schemes protect against outliers?", family 1.               */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16 value of a finite float: the top 16 bits of its encoding after   */
+/* rounding the 16 dropped bits to nearest, ties to even.                    */
+static float bf16_round(float f)
+{
+    union { float f; uint32_t u; } v;
+    v.f = f;
+    const uint32_t dropped = v.u & 0xFFFFu;
+    uint32_t top = v.u >> 16;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (top & 1u))) top += 1u;
+    v.u = top << 16;
+    return v.f;
+}
+
+/* x [m, k]: the 16-bit activations as floats (exact); qw [n, k] and b [n]:  */
+/* the per-output-channel INT8 weights (R27).  In column order, the first    */
+/* `cap` outlier columns (R26) are carved out; idx[0 .. counts[0]) lists     */
+/* them, counts[1] is the number found (the columns past the cap stay in the */
+/* integer product).  Outputs qx [m, k], a [m] (R28) and y [m, n] in fp64:   */
+/* y = acc * a * b + sum over the outlier columns of x * w16.                */
+int oq_llm_int8(const float* x, int64_t m, int64_t k, const int8_t* qw, const float* b, int64_t n, float tau,
+                int64_t cap, int x_bf16, int32_t* idx, int64_t* counts, int8_t* qx, float* a, double* y)
+{
+    if (!x || !qw || !b || !idx || !counts || !qx || !a || !y || m <= 0 || n <= 0 || k <= 0 || cap < 0)
+        return OQ_BAD_ARG;
+    if (!(tau >= 0.0f)) return OQ_BAD_ARG;
+    float* cx = (float*)malloc((size_t)k * sizeof(float));
+    float* xr = (float*)malloc((size_t)(m * k) * sizeof(float));
+    float* w16 = (float*)malloc((size_t)(n * (cap > 0 ? cap : 1)) * sizeof(float));
+    int32_t* acc = (int32_t*)malloc((size_t)(m * n) * sizeof(int32_t));
+    if (!cx || !xr || !w16 || !acc) {
+        free(cx); free(xr); free(w16); free(acc);
+        return OQ_BAD_ARG;
+    }
+    /* 1. each feature's largest magnitude over the batch's tokens */
+    oq_col_absmax(x, m, k, cx);
+    /* 2. the outlier dimensions, in column order (R26) */
+    int64_t kept = 0, found = 0;
+    for (int64_t j = 0; j < k; ++j)
+        if (cx[j] >= tau) {
+            if (kept < cap) idx[kept++] = (int32_t)j;
+            ++found;
+        }
+    counts[0] = kept;
+    counts[1] = found;
+    /* 3. vector-wise INT8 of the remaining columns: the outlier columns are */
+    /*    zeroed, so they neither set a token's scale nor enter X_q (R28)     */
+    memcpy(xr, x, (size_t)(m * k) * sizeof(float));
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t p = 0; p < kept; ++p) xr[i * k + idx[p]] = 0.0f;
+    oq_sym_quantize(xr, m, k, k, 8, 1e-8f, qx, a);
+    /* 4. the integer product and its rescale by the token and channel scales */
+    int status = oq_int8_matmul_nt(qx, qw, m, n, k, acc);
+    oq_rescale_f64(acc, a, b, m, n, y);
+    /* 5. the 16-bit weight slice of the outlier columns (R27) */
+    for (int64_t j = 0; j < n; ++j)
+        for (int64_t p = 0; p < kept; ++p) {
+            const float w = (float)qw[j * k + idx[p]] * b[j];
+            w16[j * cap + p] = x_bf16 ? bf16_round(w) : oq_f16_bits_to_f32(oq_f32_to_f16_bits(w));
+        }
+    /* 6. the outlier product X_16 W_16, added to the rescaled integer part */
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double s = 0.0;
+            for (int64_t p = 0; p < kept; ++p) s += (double)x[i * k + idx[p]] * (double)w16[j * cap + p];
+            y[i * n + j] += s;
+        }
+    free(cx); free(xr); free(w16); free(acc);
+    return status;
 }
 
 /* Threads the row loops above use: 1 in the serial build. */

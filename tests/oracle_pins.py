@@ -775,7 +775,128 @@ def check_fp8_product():
     assert np.allclose(y, xd @ wd.T, rtol=1e-12, atol=1e-15)
 
 
+# --------------------------------------------------------------------------
+# LLM.int8(): "Quantization" (Engine Room ch. 15), "The Mathematics" and the
+# history of LLM.int8(); "Quantization: Smaller Weights, Same Answers
+# (Mostly)", the outlier families.
+# --------------------------------------------------------------------------
+def _w16(qw, b, x_dtype):
+    """The 16-bit weights q * b (float32 product, one cast by torch)."""
+    import torch
+    wf = qw.astype(np.float32) * np.asarray(b, np.float32)[:, None]
+    return torch.from_numpy(wf).to(torch.bfloat16 if x_dtype == "bf16" else torch.float16).float().numpy()
+
+
+def _llm_case(seed, m=9, k=192, n=11, x_dtype="bf16"):
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = workloads.gaussian(g, (m, k), 1.0)
+    w = workloads.gaussian(g, (n, k), 0.05)
+    x = workloads.to_dtype(x, x_dtype).float().numpy()
+    qw, b = oracle.sq_quantize_weight(w, None)
+    return x, qw, b
+
+
+def check_llm_int8_special_cases():
+    # no outlier dimension (threshold above every |x|): the plain vector-wise
+    # INT8 product; every dimension an outlier: the plain 16-bit product of
+    # the activations with the dequantized weights, the integer part empty
+    for x_dtype in ("bf16", "f16"):
+        x, qw, b = _llm_case(3, x_dtype=x_dtype)
+        idx, found, qx, a, y = oracle.llm_int8_reference(x, qw, b, np.inf, x_dtype=x_dtype)
+        qx0, a0, _, y0 = oracle.sq_w8a8_reference(x, None, qw, b)
+        assert len(idx) == 0 and found == 0
+        assert np.array_equal(qx, qx0) and np.array_equal(a, a0) and np.array_equal(y, y0)
+        idx, found, qx, a, y = oracle.llm_int8_reference(x, qw, b, 0.0, x_dtype=x_dtype)
+        assert idx.tolist() == list(range(x.shape[1])) and found == x.shape[1]
+        assert not qx.any() and (a == np.float32(1e-8) / np.float32(127.0)).all()
+        assert np.array_equal(y, oracle.matmul_nt_f64(x, _w16(qw, b, x_dtype)))
+
+
+def check_llm_int8_decomposition():
+    # C = S_out (X_q W_q) + X_16 W_16: outlier columns planted in some tokens
+    # (one reaching the threshold exactly, one just below it, one in a
+    # single token only), then the result against the vector-wise product of
+    # the remaining columns plus the 16-bit product of the outlier ones
+    for x_dtype in ("bf16", "f16"):
+        x, qw, b = _llm_case(5, x_dtype=x_dtype)
+        tau = 6.0
+        x[:, 17] *= 40.0
+        x[4, 60] = tau                                   # reaches the threshold: outlier
+        x[:, 61] = np.clip(x[:, 61], -5.0, 5.0)
+        x[2, 61] = 5.9375                                # just below it (exact in both types)
+        x[:, 100] = np.clip(x[:, 100], -5.0, 5.0)
+        x[7, 100] = -250.0                               # one token only, negative
+        x[:, 150] *= 9.0
+        cm = np.abs(x).max(axis=0)
+        expect = np.nonzero(cm >= tau)[0]
+        assert {17, 60, 100}.issubset(expect) and 61 not in expect
+        idx, found, qx, a, y = oracle.llm_int8_reference(x, qw, b, tau, x_dtype=x_dtype)
+        assert idx.tolist() == expect.tolist() and found == len(expect)
+        xr = x.copy()
+        xr[:, expect] = 0.0
+        qx0, a0, _, y0 = oracle.sq_w8a8_reference(xr, None, qw, b)
+        assert np.array_equal(qx, qx0) and np.array_equal(a, a0)
+        # the largest-magnitude columns no longer set the token scales
+        assert (a <= np.float32(np.abs(xr).max()) / np.float32(127.0) * (1 + 1e-6)).all()
+        w16 = _w16(qw, b, x_dtype)
+        yo = oracle.matmul_nt_f64(np.ascontiguousarray(x[:, expect]), np.ascontiguousarray(w16[:, expect]))
+        assert np.array_equal(y, y0 + yo)
+
+
+def check_llm_int8_cap_and_permutation():
+    # a cap below the number found keeps the first columns in column order;
+    # the rest stay in the integer product.  Permuting the feature order of
+    # X and W together permutes X_q and leaves the product unchanged.
+    x, qw, b = _llm_case(8, m=13, k=256, n=7)
+    for c in (9, 40, 41, 200):
+        x[3, c] = 30.0 + c
+    idx, found, qx, a, y = oracle.llm_int8_reference(x, qw, b, 6.0, max_outliers=2)
+    assert idx.tolist() == [9, 40] and found == 4
+    xr = x.copy()
+    xr[:, [9, 40]] = 0.0
+    _, a0, _, y0 = oracle.sq_w8a8_reference(xr, None, qw, b)
+    assert np.array_equal(a, a0)
+    yo = oracle.matmul_nt_f64(np.ascontiguousarray(x[:, [9, 40]]), np.ascontiguousarray(_w16(qw, b, "bf16")[:, [9, 40]]))
+    assert np.array_equal(y, y0 + yo)
+    perm = np.random.Generator(np.random.PCG64(2)).permutation(x.shape[1])
+    xp, qwp = np.ascontiguousarray(x[:, perm]), np.ascontiguousarray(qw[:, perm])
+    _, full_found, qx1, a1, y1 = oracle.llm_int8_reference(x, qw, b, 6.0)
+    idxp, foundp, qxp, ap, yp = oracle.llm_int8_reference(xp, qwp, b, 6.0)
+    assert foundp == full_found == 4 and sorted(perm[idxp].tolist()) == [9, 40, 41, 200]
+    assert np.array_equal(qxp, qx1[:, perm]) and np.array_equal(ap, a1)
+    assert np.allclose(yp, y1, rtol=1e-12, atol=1e-12 * np.abs(y1).max())
+
+
+def check_llm_int8_accuracy():
+    # the pages' claim: carving the outlier dimensions out gives INT8
+    # inference with the accuracy of the 16-bit activations.  On activations
+    # with six outlier channels the planted channels are exactly the ones
+    # found, the error stays within 10% of weight-only INT8 (activations
+    # exact) and far below the vector-wise W8A8 product without the
+    # carve-out, and more than 99.8% of the features go through INT8.
+    wl = workloads.WORKLOADS["smoothquant"]
+    x, cols = workloads.sq_activations(wl, 256, 1024)
+    w, _ = workloads.weight(wl, 0, shape=(256, 1024))
+    x = x.float().numpy()
+    w = w.float().numpy()
+    y = oracle.matmul_nt_f64(x, w)
+
+    def rel(yq):
+        return np.linalg.norm(yq - y) / np.linalg.norm(y)
+
+    qw, b = oracle.sq_quantize_weight(w, None)
+    err_w8 = rel(oracle.matmul_nt_f64(x, oracle.sym_dequantize(qw, b[:, None], w.shape[1])))
+    _, _, _, y_plain = oracle.sq_w8a8_reference(x, None, qw, b)
+    idx, found, _, _, y_llm = oracle.llm_int8_reference(x, qw, b, 6.0)
+    assert idx.tolist() == sorted(int(c) for c in cols) and found == 6
+    err_llm, err_plain = rel(y_llm), rel(y_plain)
+    assert err_w8 < err_llm < 1.1 * err_w8, (err_w8, err_llm)
+    assert err_llm < 0.2 * err_plain, (err_llm, err_plain)
+
+
 ALL_CHECKS = [
+    check_llm_int8_special_cases, check_llm_int8_decomposition, check_llm_int8_cap_and_permutation,
+    check_llm_int8_accuracy,
     check_e4m3_conversion, check_fp8_listing, check_fp8_product,
     check_symmetric_format,
     check_f16_conversion, check_f16_scale_grid, check_group_size_sweep, check_bit_width_errors,

@@ -66,6 +66,17 @@ MUTANTS = [
     ("fp8_product_transposed",
      "sacc += (double)oq_e4m3_to_f32(qa[i * k + t]) * (double)oq_e4m3_to_f32(qb[j * k + t]);",
      "sacc += (double)oq_e4m3_to_f32(qa[i * k + t]) * (double)oq_e4m3_to_f32(qb[t * n + j % n]);"),
+    ("llm_outliers_in_absmax", "for (int64_t p = 0; p < kept; ++p) xr[i * k + idx[p]] = 0.0f;", ""),
+    ("llm_threshold_strict", "if (cx[j] >= tau) {", "if (cx[j] > tau) {"),
+    ("llm_outlier_term_dropped", "y[i * n + j] += s;", ""),
+    ("llm_w16_unrounded",
+     "w16[j * cap + p] = x_bf16 ? bf16_round(w) : oq_f16_bits_to_f32(oq_f32_to_f16_bits(w));",
+     "w16[j * cap + p] = w;"),
+    ("llm_bf16_truncates", "if (dropped > 0x8000u || (dropped == 0x8000u && (top & 1u))) top += 1u;", ""),
+    ("llm_cap_keeps_last", "if (kept < cap) idx[kept++] = (int32_t)j;",
+     "idx[kept < cap ? kept++ : cap - 1] = (int32_t)j;"),
+    ("llm_outlier_wrong_column", "s += (double)x[i * k + idx[p]] * (double)w16[j * cap + p];",
+     "s += (double)x[i * k + p] * (double)w16[j * cap + p];"),
 ]
 
 
@@ -93,7 +104,7 @@ def test_pins_catch_mutant(mid, old, new, source, tmp_path):
                         "oq_col_absmax", "oq_smooth_factors", "oq_scale_columns_mul", "oq_scale_columns_div",
                         "oq_threads", "oq_quantize_format", "oq_pack_codes3", "oq_f32_to_f16_array",
                         "oq_f16_to_f32_array", "oq_e4m3_array", "oq_e4m3_decode_array", "oq_fp8_quantize",
-                        "oq_fp8_matmul_nt"]:
+                        "oq_fp8_matmul_nt", "oq_llm_int8"]:
             f = getattr(mutant, fn_name)
             f.argtypes = getattr(good_lib, fn_name).argtypes
             f.restype = ctypes.c_int
