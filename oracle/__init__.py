@@ -30,9 +30,10 @@ GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "
 def build(force: bool = False, parallel: bool = False) -> str:
     """Compile the oracle with gcc (no FMA contraction, no fast-math).
     parallel=True builds the timing-only variant with the row loops of the
-    dequantizer and the matmul reference split over OpenMP threads."""
+    dequantizer and the matmul reference split over OpenMP threads.  A
+    library older than the source is rebuilt."""
     path = _LIB_OMP if parallel else _LIB
-    if force or not os.path.exists(path):
+    if force or not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
         tmp = path + ".tmp"
         subprocess.check_call(["gcc", *GCC_FLAGS, *(["-fopenmp"] if parallel else []), "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, path)
