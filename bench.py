@@ -19,7 +19,8 @@ are resident in HBM before timing starts, for all five workloads:
   rescale to bf16, on activations quantized before timing) and
   smooth_quant_w8a8_gemm (per-token smoothing + INT8 quantization, then the
   same GEMM); FP8 E4M3 W8A8 on the same shapes: fp8_quantize of the weights,
-  fp8_gemm alone and the online fp8_w8a8_gemm;
+  fp8_gemm alone and the online fp8_w8a8_gemm; LLM.int8() (llm_int8_gemm,
+  outlier threshold 6) on the same shapes;
   70B-class MLP decode: w4a16_gemv B=8 then B=1 on both matrices (B=1 is the
   headline), then weight-only INT8 (w8a16_gemv) at B=1 and B=8;
   stored-format variants on the 28672x8192 matrix (binary16 scales, groups of
@@ -406,6 +407,25 @@ def build_ops(dev):
             "rowquant8_kernel (E4M3) + i8_gemm_kernel (fp8)", cfg4f, reads=lambda i: ["x8in", "q8wb"],
             writes=lambda i: ["y8b"], flops=2 * m4 * n4 * k4, peak=FP8_PEAK_TFLOPS)
 
+    # ---- LLM.int8() on the same shapes (outlier threshold 6: the six planted
+    # channels are carved out) -------------------------------------------------
+    xl = x4c.to(dev)                             # the LLM.int8() call's activations
+    qw_l, wsc_l = qmm.sq_quantize_weight(w4[1])  # per-output-channel INT8, no smoothing
+    yl = torch.empty((m4, n4), dtype=torch.bfloat16, device=dev)
+    wsl = torch.empty(qmm.llm_int8_workspace_bytes(m4, n4, k4), dtype=torch.uint8, device=dev)
+    nl = torch.zeros(1, dtype=torch.int32, device=dev)
+    cfg4l = "LLM.int8() 2048x4096x4096, outlier threshold 6"
+
+    def llm_int8(i):
+        ok(lib.llm_int8_gemm(P(xl), qmm.BF16, P(qw_l), P(wsc_l), m4, n4, k4, 6.0, k4, P(yl), qmm.BF16, P(nl),
+                             P(wsl), wsl.numel(), S(xl)))
+
+    ops.add(f"llm_int8_gemm {m4}x{n4}x{k4}", llm_int8,
+            2 * m4 * k4 * 2 + 3 * k4 * 4 + (m4 * k4 + m4 * 4) * 2 + n4 * k4 + n4 * 4 + m4 * n4 * 2, "mfma",
+            "colmax2_kernel + outlier_select_kernel + rowquant8_kernel + outlier_gather_kernel + "
+            "i8_gemm_kernel (outlier epilogue)", cfg4l, reads=lambda i: ["xl", "qw_l"], writes=lambda i: ["yl"],
+            flops=2 * m4 * n4 * k4, peak=I8_PEAK_TOPS)
+
     # ---- 70B-class MLP decode: W4A16 B=8 then B=1, then W8A16 --------------
     for m in mats:
         for B in (1, 8):
@@ -644,6 +664,7 @@ def main():
             "int8_gemm_TOPS": i8.get("TFLOPs"),
             "fp8_gemm_TFLOPs": breakdown[[k for k in breakdown if k.startswith("fp8_gemm")][0]].get("TFLOPs"),
             "w8a8_online_TOPS": sq.get("TFLOPs"),
+            "llm_int8_TOPS": breakdown[[k for k in breakdown if k.startswith("llm_int8_gemm")][0]].get("TFLOPs"),
             "weight_copies_rotated_70b": COPIES_70B,
             "min_reuse_MB_hbm_ops": round(min(reuse[o["name"]] for o in ops if o["bound"] == "hbm") / 1e6),
         },

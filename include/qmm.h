@@ -359,6 +359,60 @@ int fp8_gemm(const uint8_t* qX, const float* x_scale, const uint8_t* qW, const f
 int fp8_w8a8_gemm(const void* X, int x_dtype, const uint8_t* qW, const float* w_scale, int64_t M, int64_t N,
                   int64_t K, void* Y, int y_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* -------------------------------------------------------------------------
+ * LLM.int8() -- vector-wise INT8 with the outlier feature dimensions carved
+ * out and multiplied in 16-bit.  Sources: "Quantization" (Engine Room ch.
+ * 15), "The Mathematics" (the vector-wise scheme, one scale per row of X and
+ * per output channel, with the outlier dimensions removed from the integer
+ * product and added back as a 16-bit product: C = S_out (X_q W_q) +
+ * X_16 W_16) and its history of LLM.int8() (a handful of systematically
+ * large dimensions; more than 99.9% of the values still multiplied in
+ * 8-bit); "Quantization: Smaller Weights, Same Answers (Mostly)" ("How do
+ * LLM-specific quantization schemes protect against outliers?", family 1).
+ * Readings where the pages leave the rule open:
+ *  - a feature (column of X) is an outlier dimension of the batch when some
+ *    token's |x| in it is >= `threshold` (an argument; the tests and the
+ *    benchmark use 6);
+ *  - the weights are stored once, as per-output-channel INT8 (qW, w_scale
+ *    from sq_quantize_weight with no smoothing); the 16-bit weights of an
+ *    outlier column are q * w_scale rounded to the activations' type
+ *    (binary16 saturating at 65504);
+ *  - the outlier columns are zero in X_q and take no part in a token's scale.
+ * At most `max_outliers` columns are carved out: the first ones in column
+ * order; any further outlier columns stay in the INT8 product (their count
+ * is reported, so a caller can tell).  max_outliers above K means K.
+ * X QMM_BF16 or QMM_F16 [M, K] (QMM_F32: QMM_EUNSUPPORTED), K % 64 == 0,
+ * K <= 131008; threshold >= 0 (+inf: no outlier; 0: every column), else
+ * QMM_EINVAL.
+ * ------------------------------------------------------------------------- */
+
+/* Outlier detection alone (the first two steps of llm_int8_gemm):
+ * factor [K] (caller-owned, 4-byte aligned; used as scratch first) receives
+ * +inf for each carved-out column and 1 for every other, index
+ * [max(1, min(max_outliers, K))] the carved-out columns in increasing order,
+ * counts [2] {carved out, found}.  sq_quantize_activation(X, factor) then
+ * gives the call's X_q and token scales. */
+int llm_int8_outliers(const void* X, int x_dtype, int64_t M, int64_t K, float threshold, int64_t max_outliers,
+                      float* factor, int32_t* index, int32_t* counts, void* stream);
+
+/* Bytes of workspace llm_int8_gemm needs: X_q (M K) and the token scales,
+ * the column factors, the outlier list, and the gathered outlier
+ * activations and weights (4 min(max_outliers, K) (M + N) bytes). 0 for
+ * invalid sizes. */
+size_t llm_int8_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t max_outliers);
+
+/* Y [M, N] = acc * x_scale[m] * w_scale[n] + sum over the carved-out
+ * columns j of X[m, j] * W16[n, j], where acc is the exact int32 product of
+ * X_q and qW [N, K]; the 16-bit products are exact and everything is summed
+ * in fp32, then rounded once to Y's type (QMM_BF16 or QMM_F32).
+ * `n_outliers` (device, nullable) receives the number of outlier columns
+ * found.  `workspace`: at least llm_int8_workspace_bytes(M, N, K,
+ * max_outliers) bytes, 16-byte aligned, no clearing needed; QMM_EWORKSPACE
+ * otherwise. */
+int llm_int8_gemm(const void* X, int x_dtype, const int8_t* qW, const float* w_scale, int64_t M, int64_t N,
+                  int64_t K, float threshold, int64_t max_outliers, void* Y, int y_dtype, int32_t* n_outliers,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,6 +25,7 @@ __all__ = [
     "sq_smooth_factors", "sq_quantize_weight", "sq_quantize_activation", "sq_quantize_activation_per_tensor",
     "sq_int8_gemm", "sq_workspace_bytes", "smooth_quant_w8a8_gemm", "smooth_quant_w8a8_gemm_noalloc",
     "fp8_quantize", "fp8_gemm", "fp8_w8a8_gemm",
+    "llm_int8_outliers", "llm_int8_workspace_bytes", "llm_int8_gemm",
 ]
 
 F32, F16, BF16, I32 = 0, 1, 2, 3
@@ -79,6 +80,9 @@ _SIGS = {
     "fp8_quantize": ([_P, _I, _I64, _I64, _I, _P, _P, _P], _I),
     "fp8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "fp8_w8a8_gemm": ([_P, _I, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
+    "llm_int8_outliers": ([_P, _I, _I64, _I64, _F, _I64, _P, _P, _P, _P], _I),
+    "llm_int8_workspace_bytes": ([_I64, _I64, _I64, _I64], _SZ),
+    "llm_int8_gemm": ([_P, _I, _P, _P, _I64, _I64, _I64, _F, _I64, _P, _I, _P, _P, _SZ, _P], _I),
 }
 
 
@@ -566,4 +570,71 @@ def fp8_w8a8_gemm(X: torch.Tensor, qW, w_scale, out_dtype: torch.dtype = torch.b
         workspace = torch.empty(sq_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
     _call("fp8_w8a8_gemm", _ptr(X), _dt(X.dtype), _ptr(qW), _ptr(w_scale), M, N, K, _ptr(out), _dt(out.dtype),
           _ptr(workspace), workspace.numel(), _stream(X))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# LLM.int8(): vector-wise INT8 with the outlier feature dimensions multiplied
+# in 16-bit.  qW / w_scale are the per-output-channel INT8 weights
+# (sq_quantize_weight(W) with no smoothing).
+# ---------------------------------------------------------------------------
+def _llm_args(X, threshold, max_outliers):
+    _req(X, "X", _HALVES, ndim=2)
+    M, K = X.shape
+    if not threshold >= 0.0:
+        raise ValueError(f"threshold must be >= 0, not {threshold}")
+    cap = K if max_outliers is None else int(max_outliers)
+    if cap < 0:
+        raise ValueError(f"max_outliers must be >= 0, not {max_outliers}")
+    return M, K, min(cap, K)
+
+
+def llm_int8_outliers(X: torch.Tensor, threshold: float = 6.0, max_outliers: Optional[int] = None):
+    """Outlier detection: -> (factor f32 [K]: +inf for each carved-out column, 1
+    otherwise; index int32 [kept] in increasing column order; found).  The
+    first `max_outliers` (default K) outlier columns are carved out.
+    Synchronizes with the device to read the counts."""
+    M, K, cap = _llm_args(X, threshold, max_outliers)
+    dev = _place(X=X)
+    factor = torch.empty(K, dtype=torch.float32, device=dev)
+    index = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    counts = torch.empty(2, dtype=torch.int32, device=dev)
+    _call("llm_int8_outliers", _ptr(X), _dt(X.dtype), M, K, float(threshold), cap, _ptr(factor), _ptr(index),
+          _ptr(counts), _stream(X))
+    kept, found = (int(v) for v in counts.cpu())
+    return factor, index[:kept], found
+
+
+def llm_int8_workspace_bytes(M: int, N: int, K: int, max_outliers: Optional[int] = None) -> int:
+    return int(lib().llm_int8_workspace_bytes(M, N, K, K if max_outliers is None else max_outliers))
+
+
+def llm_int8_gemm(X: torch.Tensor, qW, w_scale, threshold: float = 6.0, max_outliers: Optional[int] = None,
+                  out_dtype: torch.dtype = torch.bfloat16, workspace: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, n_outliers: Optional[torch.Tensor] = None):
+    """Y [M, N] = S_out (X_q qW^T) + X_16 W_16^T: per-token INT8 of the columns of X
+    whose largest |x| stays below `threshold`, the others (at most `max_outliers`,
+    default K) multiplied in 16-bit.  `n_outliers` (int32 [1], device, optional)
+    receives the number of outlier columns found."""
+    M, K, cap = _llm_args(X, threshold, max_outliers)
+    _req(qW, "qW", (torch.int8,), shape=(None, K))
+    N = qW.shape[0]
+    _req(w_scale, "w_scale", (torch.float32,), shape=(N,))
+    odt = out.dtype if out is not None else out_dtype
+    if odt not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"out_dtype must be torch.bfloat16 or torch.float32, not {odt}")
+    _out(out, (M, N), odt)
+    if n_outliers is not None:
+        _req(n_outliers, "n_outliers", (torch.int32,), shape=(1,))
+    need = llm_int8_workspace_bytes(M, N, K, cap)
+    if workspace is not None:
+        _req(workspace, "workspace", (torch.uint8,), ndim=1)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes; {need} needed")
+    dev = _place(X=X, qW=qW, w_scale=w_scale, out=out, workspace=workspace, n_outliers=n_outliers)
+    out = _alloc(out, (M, N), odt, dev)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _call("llm_int8_gemm", _ptr(X), _dt(X.dtype), _ptr(qW), _ptr(w_scale), M, N, K, float(threshold), cap,
+          _ptr(out), _dt(out.dtype), _ptr(n_outliers), _ptr(workspace), workspace.numel(), _stream(X))
     return out

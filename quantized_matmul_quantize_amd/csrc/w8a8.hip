@@ -407,10 +407,21 @@ __device__ __forceinline__ void mfma_frag(const i32x4& b, const i32x4& a, typena
   }
 }
 
-template <int YDT, bool FP8 = false>
+// OUTL: LLM.int8()'s 16-bit outlier product is added in the epilogue before
+// the output is rounded: *ocount outlier features, p-th one's activations
+// xo[p M + m] and 16-bit weights wo[p pitch + n] (both held as fp32).
+struct Outliers {
+  const int32_t* count;
+  const float* xo;
+  const float* wo;
+  int64_t pitch;
+};
+
+template <int YDT, bool FP8 = false, bool OUTL = false>
 __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__ A, const float* __restrict__ ascale,
                                                        const int8_t* __restrict__ B, const float* __restrict__ bscale,
-                                                       int64_t M, int64_t N, int64_t K, void* __restrict__ Y) {
+                                                       int64_t M, int64_t N, int64_t K, void* __restrict__ Y,
+                                                       Outliers outl) {
   using Acc = typename GemmAcc<FP8>::type;
   constexpr int kMfmaPerFrag = FP8 ? 2 : 1;
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
@@ -563,19 +574,54 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
   wait_vm<0>();
   __syncthreads();   // the epilogue reuses the LDS
 
-  // Epilogue: Y = acc * a[m] * b[n], four consecutive columns per lane and
-  // tile, staged through LDS so that global stores are whole 16-byte row
-  // segments.
+  // Epilogue: Y = acc * a[m] * b[n] (+ the outlier product), four
+  // consecutive columns per lane and tile, staged through LDS so that global
+  // stores are whole 16-byte row segments.
   int8_t* region = lds + wave * kEpiWave;
+  f32x4 fv[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) fv[i][j][r] = static_cast<float>(acc[i][j][r]) * as[i] * bs[j][r];
+  if constexpr (OUTL) {
+    // rows clamped like the scales; a column group past the end reads the
+    // last four (in the padded pitch) and is discarded at the store
+    const int kept = *outl.count;
+    const float* xrow[4];
+    const float* wcol[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = mw + 16 * i + (lane & 15);
+      xrow[i] = outl.xo + (m < M ? m : M - 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = nw + 16 * j + 4 * (lane >> 4);
+      wcol[j] = outl.wo + (n + 4 <= outl.pitch ? n : outl.pitch - 4);
+    }
+    for (int p = 0; p < kept; ++p) {
+      float xv[4];
+      f32x4 wv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[i] = xrow[i][p * M];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wv[j] = *reinterpret_cast<const f32x4*>(wcol[j] + p * outl.pitch);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) fv[i][j][r] = fmaf(xv[i], wv[j][r], fv[i][j][r]);
+    }
+  }
   if constexpr (YDT == QMM_BF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 f = {static_cast<float>(acc[i][j][0]) * as[i] * bs[j][0],
-                         static_cast<float>(acc[i][j][1]) * as[i] * bs[j][1],
-                         static_cast<float>(acc[i][j][2]) * as[i] * bs[j][2],
-                         static_cast<float>(acc[i][j][3]) * as[i] * bs[j][3]};
+        const f32x4 f = fv[i][j];
         // Round to nearest even, two values per conversion.
         const bf16x2_t lo = __builtin_convertvector(f.xy, bf16x2_t);
         const bf16x2_t hi = __builtin_convertvector(f.zw, bf16x2_t);
@@ -607,7 +653,7 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (YDT == QMM_I32) v[r] = static_cast<uint32_t>(acc[i][j][r]);
-          else v[r] = __float_as_uint(static_cast<float>(acc[i][j][r]) * as[i] * bs[j][r]);
+          else v[r] = __float_as_uint(fv[i][j][r]);
         }
         *reinterpret_cast<u32x4*>(region + (16 * i + (lane & 15)) * kP4 + (16 * j + 4 * (lane >> 4)) * 4) = v;
       }
@@ -679,16 +725,16 @@ int check_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float*
   return QMM_OK;
 }
 
-template <int YDT, bool FP8 = false>
+template <int YDT, bool FP8 = false, bool OUTL = false>
 void launch_gemm_t(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
-                   int64_t K, void* Y, hipStream_t s) {
+                   int64_t K, void* Y, hipStream_t s, Outliers outl = Outliers{nullptr, nullptr, nullptr, 0}) {
   // 144 KiB of dynamic LDS; the attribute is cheap to set and idempotent, so
   // it is set on every launch (no per-device bookkeeping).
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&i8_gemm_kernel<YDT, FP8>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&i8_gemm_kernel<YDT, FP8, OUTL>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGemmLds));
   const int64_t tiles = ceil_div(M, kBM) * ceil_div(N, kBN);
   const dim3 grid(static_cast<unsigned>(ceil_div(tiles, kXcds) * kXcds));
-  i8_gemm_kernel<YDT, FP8><<<grid, dim3(512), kGemmLds, s>>>(qX, xs, qW, ws, M, N, K, Y);
+  i8_gemm_kernel<YDT, FP8, OUTL><<<grid, dim3(512), kGemmLds, s>>>(qX, xs, qW, ws, M, N, K, Y, outl);
 }
 
 void launch_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
@@ -963,5 +1009,218 @@ extern "C" int fp8_w8a8_gemm(const void* X, int x_dtype, const uint8_t* qW, cons
   int st = launch_rowquant<1, 0, 1>(X, x_dtype, nullptr, M, K, qX, xs, s);
   if (st != QMM_OK) return st;
   launch_gemm_fp8(reinterpret_cast<const uint8_t*>(qX), xs, qW, w_scale, M, N, K, Y, y_dtype, s);
+  return launch_status();
+}
+
+// ----------------------------------------------------------------------------
+// LLM.int8() mixed-precision decomposition ("Quantization" (Engine Room ch.
+// 15), "The Mathematics": the vector-wise INT8 product with the outlier
+// feature dimensions removed and multiplied in 16-bit, C = S_out (X_q W_q) +
+// X_16 W_16; "Quantization: Smaller Weights, Same Answers (Mostly)", the
+// first outlier family).  Steps, all on the caller's stream:
+//  1. column maxima of |X| (the calibration kernel above, X alone);
+//  2. one block walks the columns in order: a column whose maximum reaches
+//     the threshold is an outlier dimension; the first `cap` of them get an
+//     index and the factor +inf, every other column the factor 1 (written
+//     over the maxima);
+//  3. the per-token INT8 quantizer with those factors as its smoothing
+//     divisors: x / inf = 0, so the outlier columns are zero in X_q and take
+//     no part in a token's absmax, while x / 1 = x leaves the rest unchanged;
+//  4. the outlier columns of X and their 16-bit weights (the INT8 weight
+//     times its channel scale, rounded to the activations' type) gathered as
+//     fp32 [outlier, token] and [outlier, channel];
+//  5. the INT8 GEMM, its epilogue adding the outlier product before rounding.
+// ----------------------------------------------------------------------------
+namespace qmm {
+namespace {
+
+constexpr int kSelThreads = 1024;
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+// One block.  Chunk of 1024 columns: a ballot per wavefront ranks the
+// outliers inside it, the wavefront counts in LDS give each wavefront's
+// offset, and `base` carries the count of the chunks before.
+__global__ __launch_bounds__(kSelThreads) void outlier_select_kernel(float* __restrict__ cx_factor, int64_t K,
+                                                                     float tau, int64_t cap,
+                                                                     int32_t* __restrict__ idx,
+                                                                     int32_t* __restrict__ counts,
+                                                                     int32_t* __restrict__ found_out) {
+  constexpr int kWaves = kSelThreads / kWave;
+  __shared__ int wsum[kWaves];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int64_t base = 0;
+  for (int64_t c0 = 0; c0 < K; c0 += kSelThreads) {
+    const int64_t j = c0 + threadIdx.x;
+    const bool in = j < K;
+    const bool flag = in && cx_factor[j] >= tau;
+    const uint64_t mask = __ballot(flag);
+    const int below = __popcll(mask & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(mask);
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = wsum[w];
+      total += c;
+      before += (w < wave) ? c : 0;
+    }
+    const int64_t rank = base + before + below;
+    const bool keep = flag && rank < cap;
+    if (keep) idx[rank] = static_cast<int32_t>(j);
+    if (in) cx_factor[j] = keep ? __builtin_inff() : 1.0f;
+    base += total;
+    __syncthreads();   // wsum is rewritten by the next chunk
+  }
+  if (threadIdx.x == 0) {
+    counts[0] = static_cast<int32_t>(base < cap ? base : cap);
+    counts[1] = static_cast<int32_t>(base);
+    if (found_out) *found_out = static_cast<int32_t>(base);
+  }
+}
+
+// The value of v in the 16-bit type XDT (nearest even; binary16 saturates
+// at its largest finite value).
+template <int XDT>
+__device__ __forceinline__ float round16(float v) {
+  if constexpr (XDT == QMM_BF16) return bf16lo_to_f32(f32_to_bf16_bits(v));
+  else return f16lo_to_f32(f32_to_f16_bits(__builtin_amdgcn_fmed3f(v, -65504.0f, 65504.0f)));
+}
+
+// grid.y walks the kept outliers, grid.x the M tokens then the N channels.
+template <int XDT>
+__global__ __launch_bounds__(256) void outlier_gather_kernel(const uint16_t* __restrict__ X,
+                                                             const int8_t* __restrict__ qW,
+                                                             const float* __restrict__ wscale, int64_t M, int64_t N,
+                                                             int64_t K, const int32_t* __restrict__ idx,
+                                                             const int32_t* __restrict__ counts,
+                                                             float* __restrict__ xo, float* __restrict__ wo,
+                                                             int64_t pitch) {
+  const int kept = counts[0];
+  for (int p = blockIdx.y; p < kept; p += gridDim.y) {
+    const int64_t j = idx[p];
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < M + N;
+         t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+      if (t < M) {
+        const uint32_t u = X[t * K + j];
+        xo[p * M + t] = XDT == QMM_BF16 ? bf16lo_to_f32(u) : f16lo_to_f32(u);
+      } else {
+        const int64_t n = t - M;
+        wo[p * pitch + n] = round16<XDT>(static_cast<float>(qW[n * K + j]) * wscale[n]);
+      }
+    }
+  }
+}
+
+// Workspace of the LLM.int8() call, every part at a 256-byte boundary.
+struct LlmLayout {
+  size_t qx, xs, factor, idx, counts, xo, wo, total;
+  int64_t pitch;   // N rounded up to 4 (16-byte rows for the epilogue's loads)
+};
+
+LlmLayout llm_layout(int64_t M, int64_t N, int64_t K, int64_t cap) {
+  auto up = [](size_t b) { return (b + 255u) / 256u * 256u; };
+  const size_t m = static_cast<size_t>(M), k = static_cast<size_t>(K), c = static_cast<size_t>(cap);
+  LlmLayout L;
+  L.pitch = (N + 3) / 4 * 4;
+  size_t off = 0;
+  L.qx = off;     off += up(m * k);
+  L.xs = off;     off += up(m * 4u);
+  L.factor = off; off += up(k * 4u);
+  L.idx = off;    off += up((c > 0 ? c : 1u) * 4u);
+  L.counts = off; off += 256u;
+  L.xo = off;     off += up(c * m * 4u);
+  L.wo = off;     off += up(c * static_cast<size_t>(L.pitch) * 4u);
+  L.total = off;
+  return L;
+}
+
+int check_llm(const void* X, int x_dtype, int64_t M, int64_t K, float tau, int64_t cap) {
+  if (!X) return QMM_EINVAL;
+  if (M <= 0 || K <= 0 || cap < 0) return QMM_EINVAL;
+  if (x_dtype != QMM_BF16 && x_dtype != QMM_F16) return x_dtype == QMM_F32 ? QMM_EUNSUPPORTED : QMM_EINVAL;
+  if (!(tau >= 0.0f)) return QMM_EINVAL;
+  if (K % 64 != 0) return QMM_EUNSUPPORTED;
+  if (K > kMaxK) return QMM_ERANGE;
+  if (!aligned(X, 16)) return QMM_EALIGN;
+  return QMM_OK;
+}
+
+// Steps 1 and 2: factor [K] (1 or +inf), idx [cap], counts {kept, found}.
+int llm_select(const void* X, int x_dtype, int64_t M, int64_t K, float tau, int64_t cap, float* factor,
+               int32_t* idx, int32_t* counts, int32_t* found_out, hipStream_t s) {
+  uint32_t* cx = reinterpret_cast<uint32_t*>(factor);
+  fill_zero_kernel<<<static_cast<unsigned>(ceil_div(K, 256)), 256, 0, s>>>(cx, K);
+  const int64_t bands = ceil_div(M, kCmBand);
+  const dim3 grid(static_cast<unsigned>(ceil_div(K, kCmCols)), static_cast<unsigned>(bands));
+  const uint8_t* xp = static_cast<const uint8_t*>(X);
+  if (x_dtype == QMM_BF16) colmax2_kernel<QMM_BF16, QMM_BF16><<<grid, 256, 0, s>>>(xp, M, xp, 0, K, bands, cx, cx);
+  else colmax2_kernel<QMM_F16, QMM_F16><<<grid, 256, 0, s>>>(xp, M, xp, 0, K, bands, cx, cx);
+  outlier_select_kernel<<<1, kSelThreads, 0, s>>>(factor, K, tau, cap, idx, counts, found_out);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace qmm
+
+extern "C" int llm_int8_outliers(const void* X, int x_dtype, int64_t M, int64_t K, float threshold,
+                                 int64_t max_outliers, float* factor, int32_t* index, int32_t* counts,
+                                 void* stream) {
+  int st = check_llm(X, x_dtype, M, K, threshold, max_outliers);
+  if (st != QMM_OK) return st;
+  if (!factor || !index || !counts) return QMM_EINVAL;
+  if (!aligned(factor, 4) || !aligned(index, 4) || !aligned(counts, 4)) return QMM_EALIGN;
+  const int64_t cap = max_outliers < K ? max_outliers : K;
+  return llm_select(X, x_dtype, M, K, threshold, cap, factor, index, counts, nullptr, as_stream(stream));
+}
+
+extern "C" size_t llm_int8_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t max_outliers) {
+  if (M <= 0 || N <= 0 || K <= 0 || max_outliers < 0) return 0;
+  return llm_layout(M, N, K, max_outliers < K ? max_outliers : K).total;
+}
+
+extern "C" int llm_int8_gemm(const void* X, int x_dtype, const int8_t* qW, const float* w_scale, int64_t M, int64_t N,
+                             int64_t K, float threshold, int64_t max_outliers, void* Y, int y_dtype,
+                             int32_t* n_outliers, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_llm(X, x_dtype, M, K, threshold, max_outliers);
+  if (st != QMM_OK) return st;
+  if (!qW || !w_scale || !Y || N <= 0) return QMM_EINVAL;
+  if (y_dtype != QMM_BF16 && y_dtype != QMM_F32)
+    return (y_dtype == QMM_F16 || y_dtype == QMM_I32) ? QMM_EUNSUPPORTED : QMM_EINVAL;
+  if (!aligned(qW, 16) || !aligned(w_scale, 4) || !aligned(Y, 4) || (n_outliers && !aligned(n_outliers, 4)))
+    return QMM_EALIGN;
+  const int64_t cap = max_outliers < K ? max_outliers : K;
+  const LlmLayout L = llm_layout(M, N, K, cap);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, 16)) return QMM_EWORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int8_t* qX = reinterpret_cast<int8_t*>(ws + L.qx);
+  float* xs = reinterpret_cast<float*>(ws + L.xs);
+  float* factor = reinterpret_cast<float*>(ws + L.factor);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  float* xo = reinterpret_cast<float*>(ws + L.xo);
+  float* wo = reinterpret_cast<float*>(ws + L.wo);
+  hipStream_t s = as_stream(stream);
+  st = llm_select(X, x_dtype, M, K, threshold, cap, factor, idx, counts, n_outliers, s);
+  if (st != QMM_OK) return st;
+  st = launch_rowquant<1>(X, x_dtype, factor, M, K, qX, xs, s);
+  if (st != QMM_OK) return st;
+  const dim3 ggrid(static_cast<unsigned>(ceil_div(M + N, 256) < 1024 ? ceil_div(M + N, 256) : 1024),
+                   static_cast<unsigned>(cap < 64 ? (cap > 0 ? cap : 1) : 64));
+  const uint16_t* x16 = static_cast<const uint16_t*>(X);
+  if (x_dtype == QMM_BF16)
+    outlier_gather_kernel<QMM_BF16><<<ggrid, 256, 0, s>>>(x16, qW, w_scale, M, N, K, idx, counts, xo, wo, L.pitch);
+  else
+    outlier_gather_kernel<QMM_F16><<<ggrid, 256, 0, s>>>(x16, qW, w_scale, M, N, K, idx, counts, xo, wo, L.pitch);
+  st = launch_status();
+  if (st != QMM_OK) return st;
+  const Outliers outl{counts, xo, wo, L.pitch};
+  if (y_dtype == QMM_F32) launch_gemm_t<QMM_F32, false, true>(qX, xs, qW, w_scale, M, N, K, Y, s, outl);
+  else launch_gemm_t<QMM_BF16, false, true>(qX, xs, qW, w_scale, M, N, K, Y, s, outl);
   return launch_status();
 }

@@ -172,6 +172,41 @@ def test_w8a8_argument_errors():
     assert sq(P, BF16, None, P, P, 4, 4, 131136, P, BF16, P, 10**9, None) == ERANGE
 
 
+def test_llm_int8_workspace_and_argument_errors():
+    lib = qmm.lib()
+    ws = lib.llm_int8_workspace_bytes
+    # X_q, token scales, factors, index list, counts, gathered activations and weights (N padded to 4)
+    assert ws(2048, 4096, 4096, 64) == (2048 * 4096 + 2048 * 4 + 4096 * 4 + 256 + 256
+                                        + 64 * 2048 * 4 + 64 * 4096 * 4)
+    assert ws(3, 5, 64, 2) == 256 + 256 + 256 + 256 + 256 + 256 + 256
+    assert ws(4, 8, 128, 10**6) == ws(4, 8, 128, 128)                  # the cap is at most K
+    assert ws(0, 8, 128, 4) == 0 and ws(4, 8, 128, -1) == 0
+    g = lib.llm_int8_gemm
+    need = ws(4, 8, 128, 8)
+    f = ctypes.c_float
+    args = lambda **k: [k.get("X", P), k.get("xdt", BF16), P, P, 4, 8, k.get("K", 128), f(k.get("tau", 6.0)),
+                        k.get("cap", 8), k.get("Y", P), k.get("ydt", BF16), None, k.get("ws", P),
+                        k.get("wsb", need), None]
+    assert g(*args(X=None)) == EINVAL
+    assert g(*args(xdt=F32)) == EUNSUP
+    assert g(*args(xdt=I32)) == EINVAL
+    assert g(*args(ydt=F16)) == EUNSUP
+    assert g(*args(ydt=I32)) == EUNSUP
+    assert g(*args(tau=-1.0)) == EINVAL
+    assert g(*args(tau=float("nan"))) == EINVAL
+    assert g(*args(cap=-1)) == EINVAL
+    assert g(*args(K=100)) == EUNSUP
+    assert g(*args(K=131136, wsb=10**12)) == ERANGE
+    assert g(*args(X=MIS)) == EALIGN
+    assert g(*args(ws=None)) == EWS
+    assert g(*args(wsb=need - 1)) == EWS
+    assert g(*args(ws=MIS)) == EWS
+    o = lib.llm_int8_outliers
+    assert o(P, BF16, 4, 128, f(6.0), 8, None, P, P, None) == EINVAL
+    assert o(P, F32, 4, 128, f(6.0), 8, P, P, P, None) == EUNSUP
+    assert o(P, BF16, 4, 128, f(6.0), 8, P + 2, P, P, None) == EALIGN
+
+
 def test_binding_raises_qmm_error():
     with pytest.raises(qmm.QmmError) as e:
         qmm._call("sq_int8_gemm", P, P, P, P, 4, 4, 131136, P, BF16, None)

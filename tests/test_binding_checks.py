@@ -72,3 +72,17 @@ def test_w8_and_w8a8_checks():
            "w_scale has shape")
     raises(lambda: qmm.smooth_quant_w8a8_gemm_noalloc(t((4, 256), bf16), t((256,), f16), t((8, 256), i8),
                                                       t((8,), f32)), "smooth has dtype")
+
+
+def test_llm_int8_checks():
+    x = t((4, 256), bf16)
+    raises(lambda: qmm.llm_int8_gemm(t((4, 256), f32), t((8, 256), i8), t((8,), f32)), "X has dtype")
+    raises(lambda: qmm.llm_int8_gemm(x, t((8, 128), i8), t((8,), f32)), "qW has shape")
+    raises(lambda: qmm.llm_int8_gemm(x, t((8, 256), i8), t((8,), f32), threshold=-1.0), "threshold")
+    raises(lambda: qmm.llm_int8_gemm(x, t((8, 256), i8), t((8,), f32), threshold=float("nan")), "threshold")
+    raises(lambda: qmm.llm_int8_gemm(x, t((8, 256), i8), t((8,), f32), max_outliers=-2), "max_outliers")
+    raises(lambda: qmm.llm_int8_gemm(x, t((8, 256), i8), t((8,), f32), out_dtype=torch.float16), "out_dtype")
+    raises(lambda: qmm.llm_int8_gemm(x, t((8, 256), i8), t((8,), f32), n_outliers=t((2,), f32)), "n_outliers")
+    raises(lambda: qmm.llm_int8_gemm(x, t((8, 256), i8), t((8,), f32), workspace=t((16,), u8)), "workspace holds")
+    raises(lambda: qmm.llm_int8_gemm(x, t((8, 256), i8), t((8,), f32)), "device tensor")
+    raises(lambda: qmm.llm_int8_outliers(t((4, 256), f16), threshold=-0.5), "threshold")
