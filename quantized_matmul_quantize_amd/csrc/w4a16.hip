@@ -19,10 +19,10 @@
 //    no matrix cores: a lane streams 16 bytes (32 weights) per row per step,
 //    R rows at a time so R x 16 bytes are in flight, with the activation slice
 //    held in registers across those rows.  Used for B <= 2 (decode).
-//  * w4_rows_kernel: 2..64 tokens in 16-token tiles when the weight rows give
-//    every compute unit a block (64 rows) or most of them two (32 rows) on
-//    v_mfma_f32_16x16x32_{bf16,f16}; the block loads each step's codes 4 rows
-//    x 256 contiguous bytes per instruction, its four wavefronts split K.
+//  * w4_rows_kernel: 2..64 tokens in 16-, 32- or 64-token tiles when the
+//    weight rows give most compute units a block (64 rows) or two (32 rows)
+//    on v_mfma_f32_16x16x32_{bf16,f16}; the block loads each step's codes in
+//    runs of 256 or 128 contiguous bytes per row, its wavefronts split K.
 //  * w4_lds_kernel: 2..32 tokens where the rows kernel would leave compute
 //    units idle (and larger batches whose 64 x 128 tiles would not fill the
 //    chip); a block takes 16 or 32 tokens x 32 or 64 weight rows, its four
@@ -692,61 +692,129 @@ __global__ __launch_bounds__(256) void w4_lds_kernel(const uint8_t* __restrict__
 }
 
 // ----------------------------------------------------------------------------
-// MFMA kernel for up to 16 tokens (decode with a small batch).  The block
-// tile is 16 tokens x 16 NT weight rows; K advances 4 groups (512 k) per step
-// and wavefront w computes group 4 step + w, so the four wavefronts split K
-// as in w4_lds_kernel.  The difference is how the weights arrive: the block
-// loads each step's code tile (16 NT rows x 256 bytes) cooperatively, every
-// buffer load covering 4 rows x 256 contiguous bytes, where w4_lds_kernel
-// fetches 64-byte pieces of 16 rows per instruction (a measurably slower
-// stream from HBM).  Activations (16 tokens x 1 KiB per step, one token row
-// per load) and scales (four groups of 16 rows per load, 16 bytes per row)
-// come the same way.
-// S LDS stages (loads S - 1 steps ahead), one barrier per step.  Swizzles: 16-byte piece p of code
-// row r sits at position p ^ (r & 15) of the row (a lane reads piece 4 w + p
-// of row l % 16, so this is already conflict-free), piece p of token row t at
-// p ^ row_swz(t & 15).
+// MFMA kernel for up to 64 tokens when the weight rows give every compute
+// unit a block.  Block tile: 16 TT H tokens x 16 NT weight rows, NW = 4 or 8
+// wavefronts.  K advances KS = 4 / H groups per step; wavefront w takes group
+// KS step + (w % 4) % KS for token slice (w % 4) / KS (TT tiles of 16) and,
+// with eight wavefronts, row half w / 4.  So the KS wavefronts of one token
+// slice split K, and each code slice is expanded once per TT token tiles
+// (TT = 2 halves the unpack work per output against 16-token tiles, and a
+// 64-token block reads every code byte from HBM once instead of four times).
+//   tokens <= 16: TT = 1, H = 1 (KS = 4);  <= 32: TT = 2, H = 1 (KS = 4);
+//   <= 64: TT = 2, H = 2 (KS = 2, so a stage holds 64 tokens x 256 k).
+// The block loads each step's tiles cooperatively, every buffer load writing
+// 1 KiB of LDS directly: codes as 16 / KS rows x KS 64 contiguous bytes,
+// activations as 4 / KS token rows x KS 256 bytes, scales as 16 rows x KS
+// groups per wavefront.  Swizzles (16-byte pieces): code piece p of row r at
+// p ^ cswz(r) (cswz = r & 15 for 256-byte rows, (r >> 1) & 7 for 128-byte
+// rows, so the 16 rows of a fragment read hit 16 different bank groups);
+// activation piece p of token t at p ^ row_swz(t & 15); scales transposed,
+// [group][row], so the 16 rows of a read are consecutive words.
+// S LDS stages (loads S - 1 steps ahead), one barrier per step.  Each block
+// starts its walk over K at its own step (its row tile index mod the step
+// count), so blocks in flight do not all request the same activation lines.
 // ----------------------------------------------------------------------------
-template <int NT, int S>
+template <int NT, int S, int TT, int H, int NW>
 struct RowsCfg {
+  static constexpr int KS = 4 / H;                         // groups per step
+  static constexpr int RS = NW / 4;                        // row splits (wavefronts per K slot and token slice)
+  static constexpr int RT = NT / RS;                       // 16-row tiles per wavefront
   static constexpr int kRows = 16 * NT;
-  static constexpr int kCodeBytes = kRows * 256;        // 4 groups x 64 bytes per row
-  static constexpr int kXBytes = 16 * 1024;             // 16 tokens x 512 k x 2 bytes
-  static constexpr int kScaleBytes = 4 * 64 * 4;        // 64 rows x 4 groups
+  static constexpr int kTokens = 16 * TT * H;
+  static constexpr int kRowBytes = KS * 64;                // a code row's bytes per step
+  static constexpr int kTokBytes = KS * 256;               // a token row's bytes per step
+  static constexpr int kCodeBytes = kRows * kRowBytes;
+  static constexpr int kXBytes = kTokens * kTokBytes;
+  static constexpr int kScaleBytes = NW * 256;             // per wavefront 16 rows x KS groups (+ pad)
   static constexpr int kStageBytes = kCodeBytes + kXBytes + kScaleBytes;
-  static constexpr int kLoads = NT + 4 + 1;              // per wavefront per step
+  static constexpr int kCodeLoads = kCodeBytes / (1024 * NW);   // 1 KiB loads per wavefront per step
+  static constexpr int kXLoads = kXBytes / (1024 * NW);
+  static constexpr int kLoads = kCodeLoads + kXLoads + 1;
   static constexpr int kPartPitch = kRows + 4;
-  static_assert(4 * 16 * kPartPitch * 4 <= S * kStageBytes, "partial tiles fit the stages");
+  static_assert(KS * H == 4 && (KS == 4 || KS == 2), "K slots");
+  static_assert((NW == 4 || NW == 8) && RT * RS == NT, "row split");
+  static_assert(kCodeBytes % (1024 * NW) == 0 && kXBytes % (1024 * NW) == 0 && kCodeLoads > 0 && kXLoads > 0,
+                "whole loads per wavefront");
+  static_assert(KS * kTokens * kPartPitch * 4 <= S * kStageBytes, "partial tiles fit the stages");
+  static_assert((S - 2) * kLoads < 64, "vmcnt range");
 };
 
-template <int XDT, int YDT, int NT, int S>
-__global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict__ codes,
+__device__ __forceinline__ int code_swz_rows(int r, int ks) { return ks == 4 ? (r & 15) : ((r >> 1) & 7); }
+
+// Loop step st of a block whose walk over K starts at step rot.
+__device__ __forceinline__ int rot_step(int st, int rot, int nsteps) {
+  const int d = st + rot;
+  return d >= nsteps ? d - nsteps : d;
+}
+
+// The step-st loads of w4_rows_kernel (all direct to LDS): codes, activations, scales.
+template <class Cfg, int S>
+__device__ __forceinline__ void rows_issue(int st, int nsteps, int rot, uint32_t lbase, int wave,
+                                           __amdgpu_buffer_rsrc_t cr,
+                                           __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t sr, const int* coff,
+                                           const int* xoff, int soff) {
+  // data step of loop step st (the block's rotation of K); past the end: a
+  // reload of the last one, never read
+  const int sc = rot_step(min(st, nsteps - 1), rot, nsteps);
+  const uint32_t stage = lbase + (st % S) * Cfg::kStageBytes;
+  // The scalar offsets go through plain (non-const) ints: a value-dependent
+  // expression in that argument makes clang's host pass reject the builtin
+  // call, which silently drops the kernel's host-side stub.
+  int cso = sc * Cfg::kRowBytes;
+  int xso = sc * Cfg::kTokBytes;
+  int sso = sc * Cfg::KS * 4;
+#pragma unroll
+  for (int q = 0; q < Cfg::kCodeLoads; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_ptr_t)(uintptr_t)(stage + (Cfg::kCodeLoads * wave + q) * 1024),
+                                             16, coff[q], cso, 0, 0);
+#pragma unroll
+  for (int q = 0; q < Cfg::kXLoads; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        xr, (lds_ptr_t)(uintptr_t)(stage + Cfg::kCodeBytes + (Cfg::kXLoads * wave + q) * 1024), 16, xoff[q], xso, 0,
+        0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      sr, (lds_ptr_t)(uintptr_t)(stage + Cfg::kCodeBytes + Cfg::kXBytes + wave * 256), 4, soff, sso, 0, 0);
+}
+
+template <int XDT, int YDT, int NT, int S, int TT, int H, int NW>
+__global__ __launch_bounds__(NW * 64) void w4_rows_kernel(const uint8_t* __restrict__ codes,
                                                       const float* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros, int64_t N, int64_t K,
                                                       const uint16_t* __restrict__ x, int64_t M,
                                                       void* __restrict__ y) {
-  using Cfg = RowsCfg<NT, S>;
+  using Cfg = RowsCfg<NT, S, TT, H, NW>;
+  constexpr int KS = Cfg::KS;
+  constexpr int RT = Cfg::RT;
   constexpr int D = S - 1;
   using Mg = Int4Magic<XDT>;
   constexpr int kRows = Cfg::kRows;
+  constexpr int kTokens = Cfg::kTokens;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int ks = (wave & 3) % KS;
+  const int hs = (wave & 3) / KS;
+  const int rs = wave >> 2;           // this wavefront's row tiles: RT rs .. + RT
   const int G = static_cast<int>(K / kGroup);
   const int zb = (G + 1) / 2;
-  const int nsteps = (G + 3) / 4;
+  const int nsteps = (G + KS - 1) / KS;
 
-  const int64_t mtiles = (M + 15) / 16;
+  const int64_t mtiles = (M + kTokens - 1) / kTokens;
   const int64_t ntiles = (N + kRows - 1) / kRows;
   const int64_t T = mtiles * ntiles;
   const int64_t per = (T + 7) / 8;
   const int64_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= T) return;
   const int64_t n0 = (t / mtiles) * kRows;
-  const int64_t m0 = (t % mtiles) * 16;
+  const int64_t m0 = (t % mtiles) * kTokens;
   const int64_t nrows = (N - n0 < kRows) ? N - n0 : kRows;
-  const int64_t mrows = (M - m0 < 16) ? M - m0 : 16;
+  const int64_t mrows = (M - m0 < kTokens) ? M - m0 : kTokens;
+  // Blocks start their walk over K at different steps, so that the blocks
+  // in flight read different activation lines at any one time (the same
+  // lines requested by every compute unit at once queue on a few L2
+  // channels).  The sum over K is the same for any start.
+  const int rot = static_cast<int>((t / mtiles) % nsteps);
 
   const uint32_t lbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   uint8_t* const ztab = lds + S * Cfg::kStageBytes;
@@ -760,45 +828,37 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(scales + n0 * G), 0, static_cast<int>(nrows) * G * 4, kBufferWord3);
 
-  // Load offsets.  Codes: load q of wavefront w covers rows 4 (NT w + q) ..
-  // +4, lane l row + l/16, piece (l%16) ^ (row & 15).  Activations: load q of
-  // wavefront w is token row 4 w + q, lane l piece l ^ row_swz(token & 15).
-  // Scales: wavefront w loads the step's four groups of rows 16 w .. + 16
-  // (lane l: row 16 w + l / 4, group l % 4), 16 contiguous bytes per row.
-  int coff[4], xoff[4];
+  // Load offsets (lane l writes LDS byte 16 l of its load's kilobyte, or 4 l
+  // for the scales).  Codes: 4 KS lanes per row, slot s = l % (4 KS) takes
+  // source piece s ^ cswz(row).  Activations: 16 KS lanes per token row, slot
+  // s takes piece s ^ row_swz(token).  Scales: lane l is row 16 w + l % 16,
+  // group slot (l / 16) mod KS (for KS = 2 lanes 32..63 repeat 0..31 into the
+  // upper half of the region, never read).
+  int coff[Cfg::kCodeLoads], xoff[Cfg::kXLoads];
 #pragma unroll
-  for (int q = 0; q < NT; ++q) {
-    const int r = 4 * (NT * wave + q) + (lane >> 4);
-    coff[q] = r * kh + (((lane & 15) ^ (r & 15)) * 16);
+  for (int q = 0; q < Cfg::kCodeLoads; ++q) {
+    const int r = (Cfg::kCodeLoads * wave + q) * (16 / KS) + lane / (4 * KS);
+    const int s = lane % (4 * KS);
+    coff[q] = r * kh + ((s ^ code_swz_rows(r, KS)) * 16);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int tr = 4 * wave + q;
-    xoff[q] = tr * kb2 + ((lane ^ row_swz(tr & 15)) * 16);
+  for (int q = 0; q < Cfg::kXLoads; ++q) {
+    const int tr = (Cfg::kXLoads * wave + q) * (4 / KS) + lane / (16 * KS);
+    const int s = lane % (16 * KS);
+    xoff[q] = tr * kb2 + ((s ^ row_swz(tr & 15)) * 16);
   }
-  const int soff = (16 * wave + (lane >> 2)) * G * 4 + (lane & 3) * 4;
-  auto issue = [&](int st) {
-    const int sc = min(st, nsteps - 1);   // past the end: reload the last step (never read)
-    const uint32_t stage = lbase + (st % S) * Cfg::kStageBytes;
-#pragma unroll
-    for (int q = 0; q < NT; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_ptr_t)(uintptr_t)(stage + (NT * wave + q) * 1024), 16,
-                                               coff[q], sc * 256, 0, 0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(uintptr_t)(stage + Cfg::kCodeBytes + (4 * wave + q) * 1024),
-                                               16, xoff[q], sc * 1024, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        sr, (lds_ptr_t)(uintptr_t)(stage + Cfg::kCodeBytes + Cfg::kXBytes + wave * 256), 4, soff, sc * 16, 0, 0);
-  };
+  const int soff = (16 * (wave & 3) + (lane & 15)) * G * 4 + ((lane >> 4) & (KS - 1)) * 4;
 
-  for (int st = 0; st < D; ++st) issue(st);
+
+  for (int st = 0; st < D; ++st) rows_issue<Cfg, S>(st, nsteps, rot, lbase, wave, cr, xr, sr, coff, xoff, soff);
   const int zp = zero_pitch(zb);
-  copy_zeros_to_lds<256>(ztab, zeros + n0 * zb, kRows, zb, zp, static_cast<int>(nrows), tid);
+  copy_zeros_to_lds<NW * 64>(ztab, zeros + n0 * zb, kRows, zb, zp, static_cast<int>(nrows), tid);
 
-  f32x4 acc[NT];
+  f32x4 acc[TT][RT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int j = 0; j < RT; ++j) acc[tt][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const uint32_t magic = vgpr_const(Mg::kMagic);
   const uint32_t ones[4] = {Mg::one_pair, Mg::one_pair, Mg::one_pair, Mg::one_pair};
   const int fr = lane & 15;
@@ -813,54 +873,67 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    issue(st + D);
-    const int g = 4 * st + wave;
+    rows_issue<Cfg, S>(st + D, nsteps, rot, lbase, wave, cr, xr, sr, coff, xoff, soff);
+    const int g = KS * rot_step(st, rot, nsteps) + ks;
     if (g < G) {
       const uint8_t* cg = lds + (st % S) * Cfg::kStageBytes;
       const uint8_t* xg = cg + Cfg::kCodeBytes;
-      const float* sg = reinterpret_cast<const float*>(xg + Cfg::kXBytes);   // [row][4 groups]
-      const int cp = 4 * wave + fp;   // this lane's 16-byte piece of a code row
-      u32x4 cw[NT];
-      float sv[NT], zo[NT];
+      const float* sg = reinterpret_cast<const float*>(xg + Cfg::kXBytes);   // [row tile][group slot][row]
+      u32x4 cw[RT];
+      float sv[RT], zo[RT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      for (int j = 0; j < RT; ++j) {
+        const int nt = RT * rs + j;
         const int r = 16 * nt + fr;
-        cw[nt] = *reinterpret_cast<const u32x4*>(cg + r * 256 + ((cp ^ fr) * 16));
-        sv[nt] = sg[4 * r + wave];
+        cw[j] = *reinterpret_cast<const u32x4*>(cg + r * Cfg::kRowBytes +
+                                                (((4 * ks + fp) ^ code_swz_rows(r, KS)) * 16));
+        sv[j] = sg[64 * nt + 16 * ks + fr];
         const uint32_t zbyte = ztab[r * zp + (g >> 1)];
-        zo[nt] = Mg::offset + static_cast<float>((g & 1) ? (zbyte >> 4) : (zbyte & 15u));
+        zo[j] = Mg::offset + static_cast<float>((g & 1) ? (zbyte >> 4) : (zbyte & 15u));
       }
-      f32x4 part[NT], xs;
+      f32x4 part[TT][RT], xs[TT];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int xp = 16 * wave + 4 * fp + c;   // piece of the token row
-        const u32x4 v = *reinterpret_cast<const u32x4*>(xg + fr * 1024 + ((xp ^ row_swz(fr)) * 16));
-        const uint32_t xa[4] = {v.x, v.y, v.z, v.w};
-        xs = mfma16x16x32<XDT>(xa, ones, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : xs);
+        uint32_t wb[RT][4];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          uint32_t wb[4];
-          Mg::unpack(cw[nt][c], magic, wb);
-          part[nt] = mfma16x16x32<XDT>(xa, wb, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : part[nt]);
+        for (int j = 0; j < RT; ++j) Mg::unpack(cw[j][c], magic, wb[j]);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const int tr = 16 * (TT * hs + tt) + fr;                       // token row of the block
+          const int xp = 16 * ks + 4 * fp + c;                           // piece of the token row
+          const u32x4 v = *reinterpret_cast<const u32x4*>(xg + tr * Cfg::kTokBytes + ((xp ^ row_swz(fr)) * 16));
+          const uint32_t xa[4] = {v.x, v.y, v.z, v.w};
+          xs[tt] = mfma16x16x32<XDT>(xa, ones, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : xs[tt]);
+#pragma unroll
+          for (int j = 0; j < RT; ++j)
+            part[tt][j] = mfma16x16x32<XDT>(xa, wb[j], c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : part[tt][j]);
         }
       }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[nt][e] = fmaf(sv[nt], fmaf(-zo[nt], xs[e], part[nt][e]), acc[nt][e]);
+        for (int j = 0; j < RT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[tt][j][e] = fmaf(sv[j], fmaf(-zo[j], xs[tt][e], part[tt][j][e]), acc[tt][j][e]);
     }
   }
   wait_vm<0>();
   __syncthreads();   // every stage is idle; the LDS now holds the partial tiles
 
+  // Partial tiles [K slot][token][row], summed over the K slots in order.
   float* parts = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) parts[(wave * 16 + 4 * fp + e) * Cfg::kPartPitch + 16 * nt + fr] = acc[nt][e];
+    for (int j = 0; j < RT; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        parts[(ks * kTokens + 16 * (TT * hs + tt) + 4 * fp + e) * Cfg::kPartPitch + 16 * (RT * rs + j) + fr] =
+            acc[tt][j][e];
   __syncthreads();
   constexpr int kOct = kRows / 8;
-  for (int o = tid; o < 16 * kOct; o += 256) {
+  for (int o = tid; o < kTokens * kOct; o += NW * 64) {
     const int r = o / kOct;
     const int c0 = (o % kOct) * 8;
     const int64_t m = m0 + r;
@@ -868,10 +941,9 @@ __global__ __launch_bounds__(256) void w4_rows_kernel(const uint8_t* __restrict_
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float a = parts[(0 * 16 + r) * Cfg::kPartPitch + c0 + j];
-      a += parts[(1 * 16 + r) * Cfg::kPartPitch + c0 + j];
-      a += parts[(2 * 16 + r) * Cfg::kPartPitch + c0 + j];
-      a += parts[(3 * 16 + r) * Cfg::kPartPitch + c0 + j];
+      float a = parts[r * Cfg::kPartPitch + c0 + j];
+#pragma unroll
+      for (int q = 1; q < KS; ++q) a += parts[(q * kTokens + r) * Cfg::kPartPitch + c0 + j];
       v[j] = a;
     }
 #pragma unroll
@@ -1213,34 +1285,45 @@ bool launch_tile_t(const uint8_t* codes, const float* scales, const uint8_t* zer
   return true;
 }
 
-template <int XDT, int YDT, int NT, int S>
+template <int XDT, int YDT, int NT, int S, int TT = 1, int H = 1, int NW = 4>
 bool launch_rows_t(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                    const uint16_t* x, int64_t M, void* y, hipStream_t s) {
-  using Cfg = RowsCfg<NT, S>;
+  using Cfg = RowsCfg<NT, S, TT, H, NW>;
   const int64_t G = K / kGroup;
   const size_t lds = S * static_cast<size_t>(Cfg::kStageBytes) +
                     static_cast<size_t>(Cfg::kRows) * zero_pitch(static_cast<int>((G + 1) / 2));
   if (lds > kLdsBytesMax) return false;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_rows_kernel<XDT, YDT, NT, S>),
+  // the activation buffer of a block tile (tokens x K x 2 bytes) is addressed with 32-bit offsets
+  if (static_cast<int64_t>(Cfg::kTokens) * K * 2 > INT32_MAX) return false;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_rows_kernel<XDT, YDT, NT, S, TT, H, NW>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  const int64_t tiles = ceil_div(M, 16) * ceil_div(N, Cfg::kRows);
+  const int64_t tiles = ceil_div(M, Cfg::kTokens) * ceil_div(N, Cfg::kRows);
   const dim3 grid(static_cast<unsigned>(ceil_div(tiles, 8) * 8));
-  w4_rows_kernel<XDT, YDT, NT, S><<<grid, dim3(kLdsWaves * kWave), lds, s>>>(codes, scales, zeros, N, K, x, M, y);
+  w4_rows_kernel<XDT, YDT, NT, S, TT, H, NW><<<grid, dim3(NW * kWave), lds, s>>>(codes, scales, zeros, N, K, x, M,
+                                                                               y);
   return true;
 }
 
-// The cooperative-load kernel (16-token tiles, up to 64 tokens): 64 weight
-// rows per block when that gives every compute unit a block, 32 rows when
-// that gives most units two; otherwise false (few rows, long K: one block per
-// unit would serialize its steps on the barrier), and the split-K kernel,
-// whose wavefronts run independently, takes the call.  Two stages: measured
-// faster than three to five, which cost blocks per compute unit.
+// The cooperative-load kernel, up to 64 tokens: 64 weight rows per block
+// when that gives at least three quarters of the compute units a block, 32
+// rows when that gives most units two; otherwise false (few rows, long K: one
+// block per unit would serialize its steps on the barrier), and the split-K
+// kernel, whose wavefronts run independently, takes the call.  Token tiles:
+// 16 up to 16 tokens, 32 up to 32, 64 beyond (each code slice read and
+// expanded once per block instead of once per 16 tokens).  Two stages and
+// four wavefronts: on 14336 x 4096 (224 blocks) measured against three or
+// four stages, eight wavefronts (64 or 32 rows each) and 32-row blocks, this
+// was fastest or within noise at 16, 32 and 64 tokens.
 template <int XDT, int YDT>
 bool launch_rows(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                  const uint16_t* x, int64_t M, void* y, hipStream_t s) {
   const int64_t cus = device_cus();
+  if (M > 16 && 4 * ceil_div(M, M > 32 ? 64 : 32) * ceil_div(N, 64) >= 3 * cus) {
+    if (M > 32 && launch_rows_t<XDT, YDT, 4, 2, 2, 2>(codes, scales, zeros, N, K, x, M, y, s)) return true;
+    if (M <= 32 && launch_rows_t<XDT, YDT, 4, 2, 2, 1>(codes, scales, zeros, N, K, x, M, y, s)) return true;
+  }
   const int64_t mt = ceil_div(M, 16);
-  if (mt * ceil_div(N, 64) >= cus) return launch_rows_t<XDT, YDT, 4, 2>(codes, scales, zeros, N, K, x, M, y, s);
+  if (4 * mt * ceil_div(N, 64) >= 3 * cus) return launch_rows_t<XDT, YDT, 4, 2>(codes, scales, zeros, N, K, x, M, y, s);
   if (2 * mt * ceil_div(N, 32) >= 3 * cus) return launch_rows_t<XDT, YDT, 2, 2>(codes, scales, zeros, N, K, x, M, y, s);
   return false;
 }

@@ -122,12 +122,13 @@ def test_gemm_wide_ragged(M):
     gemv_case(q, s, z, x, torch.bfloat16, f"gemm wide M={M} bf16", gemm=True)
 
 
-@pytest.mark.parametrize("n", [12321, 16421], ids=["32-row blocks", "64-row blocks"])
-@pytest.mark.parametrize("M", [3, 16, 40])
-def test_gemm_few_tokens_cooperative(n, M):
-    # enough weight rows for the cooperative-load kernel (up to 64 tokens),
-    # K = 5 groups so its second 4-group step is partly past K; ragged N
-    k = 640
+@pytest.mark.parametrize("n", [12321, 16421], ids=["one block per CU", "two rounds of blocks"])
+@pytest.mark.parametrize("M,k", [(3, 640), (16, 640), (17, 640), (32, 640), (40, 640), (64, 640), (16, 1152),
+                                 (30, 1152), (50, 1152)], ids=lambda v: str(v))
+def test_gemm_few_tokens_cooperative(n, M, k):
+    # enough weight rows for the cooperative-load kernel (up to 64 tokens in
+    # 16-, 32- or 64-token tiles; two or four groups per step): K = 5 or 9
+    # groups, so the last step is partly past K; ragged N and M
     q, s, z = random_w4(n, k, seed=n + M)
     x = workloads.to_dtype(workloads.gaussian(workloads.rng(81, n + M), (M, k), 1.0), "bf16")
     gemv_case(q, s, z, x, torch.float32, f"gemm few tokens n={n} M={M}", gemm=True)
