@@ -462,18 +462,33 @@ def build_ops(dev):
     return ops, mats
 
 
+def kernel_source(text, name):
+    """The text of kernel `name` in a HIP source: from its `void name(` to the
+    brace that closes its body (None if absent)."""
+    i = text.find(f"void {name}(")
+    if i < 0:
+        return None
+    j = text.find("{", text.find(")", i))
+    depth = 0
+    for k in range(j, len(text)):
+        depth += {"{": 1, "}": -1}.get(text[k], 0)
+        if depth == 0:
+            return text[i:k + 1]
+    return None
+
+
 def gemv_traffic():
     """HBM bytes per B=1 GEMV launch from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the
-    kernel's source has changed since the counters were taken."""
+    kernel's own source text has changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "gemv_valu_kernel_traffic.json")
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        body = kernel_source(open(os.path.join(ROOT, rec["source"])).read(), rec["kernel_function"])
     except (OSError, ValueError, KeyError):
         return None
-    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+    if body is None or hashlib.sha256(body.encode()).hexdigest() != rec.get("kernel_sha256"):
         return None
     launches = list(rec["per_launch"].values())
     return round(sum(v["hbm_read_bytes"] + v["hbm_write_bytes"] for v in launches) / len(launches))
