@@ -112,6 +112,19 @@ class HipEvent:
         return ms.value
 
 
+def decode_step_ms(params, batch, bytes_per_weight, bandwidth, flops):
+    """Roofline time of one decode step ("Quantization from Scratch", "What it
+    buys at decode"): every weight is read once from memory and each does 2
+    flops per sequence in the batch; the step takes the longer of the two."""
+    return max(params * bytes_per_weight / bandwidth, 2.0 * params * batch / flops) * 1e3
+
+
+def matmul_bound(tokens, bytes_per_weight, bandwidth=HBM_PEAK_GBPS * 1e9, flops=BF16_PEAK_TFLOPS * 1e12):
+    """'hbm' while reading the weights takes longer than the matrix work on
+    `tokens` tokens (below the ridge of the roofline), else 'mfma'."""
+    return "hbm" if 2.0 * tokens / bytes_per_weight < flops / bandwidth else "mfma"
+
+
 def w4_kernel_name(M, N, dev):
     """Which W4A16 kernel the library picks for M tokens and N weight rows
     (the rule in w4a16.hip's launchers), for labelling only."""
@@ -311,7 +324,7 @@ def build_ops(dev):
             c, s, z = g3[(i + j) % 3]
             ok(lib.w4a16_gemm(P(c), P(s), P(z), n3, k3, 128, P(X), qmm.BF16, M, P(Y), qmm.BF16, S(X)))
         ops.add(f"w4a16_gemm M={M} {n3}x{k3}", gemm, w4_bytes(n3, k3) + M * k3 * 2 + M * n3 * 2,
-                "mfma" if M >= 128 else "hbm", w4_kernel_name(M, n3, dev), cfg3,
+                matmul_bound(M, w4_bytes(n3, k3) / (n3 * k3)), w4_kernel_name(M, n3, dev), cfg3,
                 reads=lambda i, j=j, M=M: [f"w4_gemm[{(i + j) % 3}]", f"x_gemm{M}"], flops=2 * M * n3 * k3)
 
     # ---- SmoothQuant W8A8 ---------------------------------------------------
