@@ -380,10 +380,13 @@ constexpr int kP4 = 272;                        // 64 x 4-byte outputs
 constexpr int kEpiWave = 64 * kP4;              // per-wavefront epilogue region (64 rows)
 static_assert(64 * kP2 <= kEpiWave && 8 * kEpiWave <= static_cast<int>(kGemmLds), "epilogue must fit");
 
-// FP8: the same tiles and pipeline with E4M3 operands; each 16-byte fragment
-// (16 k of one row) feeds two v_mfma_f32_16x16x32_fp8_fp8 (8 k each, fp32
-// accumulation): the first takes bytes 0-7 of every lane, the second bytes
-// 8-15, so A and B pair the same k.
+// FP8: the same tiles, LDS layout and loads with E4M3 operands, but one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per tile and k-step (block scales all
+// 1.0, E8M0 0x7F): a lane passes its 16-byte fragments of both 64-wide
+// chunks as the instruction's 32 bytes.  A and B lanes are filled the same
+// way, so each k of the step meets its partner whatever order the
+// instruction gives the 32 bytes.  (The 16x16x32 fp8 form runs at the bf16
+// rate on gfx950: half the throughput per k.)
 template <bool FP8>
 struct GemmAcc {
   typedef i32x4 type;
@@ -393,18 +396,20 @@ struct GemmAcc<true> {
   typedef f32x4 type;
 };
 
-template <bool FP8>
-__device__ __forceinline__ void mfma_frag(const i32x4& b, const i32x4& a, typename GemmAcc<FP8>::type& acc) {
-  if constexpr (FP8) {
-    const long b0 = static_cast<long>(static_cast<uint32_t>(b[0])) | (static_cast<long>(b[1]) << 32);
-    const long b1 = static_cast<long>(static_cast<uint32_t>(b[2])) | (static_cast<long>(b[3]) << 32);
-    const long a0 = static_cast<long>(static_cast<uint32_t>(a[0])) | (static_cast<long>(a[1]) << 32);
-    const long a1 = static_cast<long>(static_cast<uint32_t>(a[2])) | (static_cast<long>(a[3]) << 32);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(b0, a0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(b1, a1, acc, 0, 0, 0);
-  } else {
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a, acc, 0, 0, 0);
-  }
+__device__ __forceinline__ void mfma_frag(const i32x4& b, const i32x4& a, i32x4& acc) {
+  acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a, acc, 0, 0, 0);
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kUnitScales = 0x7F7F7F7F;   // E8M0 1.0 in every byte
+
+// D += B^T-side x A over the 128 k of one step: fragments (b0, b1) and (a0,
+// a1) of the step's two chunks.
+__device__ __forceinline__ void mfma_fp8_step(const i32x4& b0, const i32x4& b1, const i32x4& a0, const i32x4& a1,
+                                              f32x4& acc) {
+  const i32x8 bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  const i32x8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, acc, 0, 0, 0, kUnitScales, 0, kUnitScales);
 }
 
 // OUTL: LLM.int8()'s 16-bit outlier product is added in the epilogue before
@@ -423,7 +428,6 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
                                                        int64_t M, int64_t N, int64_t K, void* __restrict__ Y,
                                                        Outliers outl) {
   using Acc = typename GemmAcc<FP8>::type;
-  constexpr int kMfmaPerFrag = FP8 ? 2 : 1;
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -536,6 +540,38 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
   barrier();
   read_chunk(fa0, fb0, 0, rd0);
 
+  if constexpr (FP8) {
+    // Per step: issue the loads of step t+2, the 16 MFMAs of step t (their
+    // fragments were read in the previous iteration), then wait for step
+    // t+1's loads, the barrier, and read step t+1's fragments while the
+    // MFMAs run.
+    read_chunk(fa1, fb1, 0, rd1);
+    i32x4 na0[4], nb0[4], na1[4], nb1[4];
+    int s0 = 0;
+    for (int t = 0; t < nsteps; ++t) {
+      const int s1 = (s0 == 2) ? 0 : s0 + 1;
+      const int s2 = (s1 == 2) ? 0 : s1 + 1;
+      issue(t + 2, s2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mfma_fp8_step(fb0[j], fb1[j], fa0[i], fa1[i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<kLoadsA8 + kLoadsB8>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      barrier();
+      read_chunk(na0, nb0, s1, rd0);
+      read_chunk(na1, nb1, s1, rd1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa0[i] = na0[i];
+        fb0[i] = nb0[i];
+        fa1[i] = na1[i];
+        fb1[i] = nb1[i];
+      }
+      s0 = s1;
+    }
+  } else {
   int s0 = 0;
   for (int t = 0; t < nsteps; ++t) {
     const int s1 = (s0 == 2) ? 0 : s0 + 1;
@@ -545,16 +581,16 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mfma_frag<FP8>(fb0[j], fa0[i], acc[i][j]);
+      for (int j = 0; j < 4; ++j) mfma_frag(fb0[j], fa0[i], acc[i][j]);
 #pragma unroll
     for (int g = 0; g < 6; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerFrag, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerFrag, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerFrag, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<kLoadsA8 + kLoadsB8>();
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
@@ -563,13 +599,14 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mfma_frag<FP8>(fb1[j], fa1[i], acc[i][j]);
+      for (int j = 0; j < 4; ++j) mfma_frag(fb1[j], fa1[i], acc[i][j]);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerFrag, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
     }
     s0 = s1;
+  }
   }
   wait_vm<0>();
   __syncthreads();   // the epilogue reuses the LDS
