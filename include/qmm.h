@@ -395,10 +395,10 @@ int fp8_w8a8_gemm(const void* X, int x_dtype, const uint8_t* qW, const float* w_
 int llm_int8_outliers(const void* X, int x_dtype, int64_t M, int64_t K, float threshold, int64_t max_outliers,
                       float* factor, int32_t* index, int32_t* counts, void* stream);
 
-/* Bytes of workspace llm_int8_gemm needs: X_q (M K) and the token scales,
- * the column factors, the outlier list, and the gathered outlier
- * activations and weights (4 min(max_outliers, K) (M + N) bytes). 0 for
- * invalid sizes. */
+/* Bytes of workspace llm_int8_gemm needs: X_q (M K bytes) and the token
+ * scales, the column factors, the outlier list (4 min(max_outliers, K)
+ * bytes) and its counts, each part at a 256-byte boundary; N does not enter.
+ * 0 for invalid sizes. */
 size_t llm_int8_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t max_outliers);
 
 /* Y [M, N] = acc * x_scale[m] * w_scale[n] + sum over the carved-out

@@ -33,14 +33,15 @@ constexpr int64_t kMaxK = 131008;
 
 // ----------------------------------------------------------------------------
 // Column absolute maxima (calibration statistics).  Block = 512 columns x a
-// band of 128 rows: lane l of wavefront w takes columns 8 l .. +8 of rows
-// 32 w .. +32 of the band, eight rows per batch of loads (each row read is 1
+// band of 64 rows: lane l of wavefront w takes columns 8 l .. +8 of rows
+// 16 w .. +16 of the band, eight rows per batch of loads (each row read is 1
 // KiB contiguous per wavefront); the four wavefronts' maxima are combined in
 // LDS and each column gets one atomicMax per block, on the float's bit
-// pattern (non-negative floats order like unsigned integers).
+// pattern (non-negative floats order like unsigned integers).  (64-row bands:
+// a 2048 x 4096 activation matrix alone makes 256 blocks, one per CU.)
 // ----------------------------------------------------------------------------
 constexpr int kCmCols = 512;
-constexpr int64_t kCmBand = 128;
+constexpr int64_t kCmBand = 64;
 
 // Zeroes two arrays of n words in one launch (the column maxima targets).
 __global__ __launch_bounds__(256) void fill_zero2_kernel(uint32_t* __restrict__ p, uint32_t* __restrict__ q,
@@ -413,14 +414,31 @@ __device__ __forceinline__ void mfma_fp8_step(const i32x4& b0, const i32x4& b1, 
 }
 
 // OUTL: LLM.int8()'s 16-bit outlier product is added in the epilogue before
-// the output is rounded: *ocount outlier features, p-th one's activations
-// xo[p M + m] and 16-bit weights wo[p pitch + n] (both held as fp32).
+// the output is rounded.  *count outlier columns idx[0 ..); for column j the
+// activations X[m, j] (16-bit, x_f16 selects fp16 over bf16) and the 16-bit
+// weights, B[n, j] * bscale[n] rounded to X's type.  The first kOutlLds of
+// them are fetched at the start of the kernel (their latency hidden behind the
+// main loop) and kept in LDS past the stages; any further ones are read from
+// global memory in the epilogue.
 struct Outliers {
   const int32_t* count;
-  const float* xo;
-  const float* wo;
-  int64_t pitch;
+  const int32_t* idx;
+  const uint16_t* X;
+  int x_f16;
 };
+constexpr int kOutlLds = 8;
+constexpr size_t kOutlLdsBytes = static_cast<size_t>(kOutlLds) * (kBM + kBN) * 4;   // 12 KiB
+static_assert(kGemmLds + kOutlLdsBytes <= 160 * 1024, "outlier operands fit beside the stages");
+
+// The value of v in X's 16-bit type (nearest even; binary16 saturates at its
+// largest finite value).
+__device__ __forceinline__ float round16(float v, int x_f16) {
+  return x_f16 ? f16lo_to_f32(f32_to_f16_bits(__builtin_amdgcn_fmed3f(v, -65504.0f, 65504.0f)))
+               : bf16lo_to_f32(f32_to_bf16_bits(v));
+}
+__device__ __forceinline__ float x16_value(uint32_t u, int x_f16) {
+  return x_f16 ? f16lo_to_f32(u) : bf16lo_to_f32(u);
+}
 
 template <int YDT, bool FP8 = false, bool OUTL = false>
 __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__ A, const float* __restrict__ ascale,
@@ -534,6 +552,35 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
       bs[j][r] = (YDT == QMM_I32) ? 1.0f : bscale[n < N ? n : N - 1];
     }
 
+  // Outlier operands of this tile (the first kOutlLds columns): thread t
+  // fetches X rows (t + 512 q) % 256 of outlier (t + 512 q) / 256 and weight
+  // columns (t + 512 q) % 128 of outlier (t + 512 q) / 128; they wait in
+  // registers until the stages are free.
+  int okept = 0;
+  uint32_t ox[4];
+  int32_t ow[2];
+  float os[2];
+  if constexpr (OUTL) {
+    okept = *outl.count;
+    const int nk = okept < kOutlLds ? okept : kOutlLds;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int slot = tid + 512 * q;
+      const int p = slot / kBM;
+      const int64_t m = m0 + slot % kBM;
+      ox[q] = (p < nk) ? outl.X[(m < M ? m : M - 1) * K + outl.idx[p]] : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int slot = tid + 512 * q;
+      const int p = slot / kBN;
+      const int64_t n = n0 + slot % kBN;
+      const int64_t nc = n < N ? n : N - 1;
+      ow[q] = (p < nk) ? B[nc * K + outl.idx[p]] : 0;
+      os[q] = (p < nk) ? bscale[nc] : 0.0f;
+    }
+  }
+
   issue(0, 0);
   issue(1, 1);
   wait_vm<kLoadsA8 + kLoadsB8>();
@@ -610,6 +657,21 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
   }
   wait_vm<0>();
   __syncthreads();   // the epilogue reuses the LDS
+  float* olds = reinterpret_cast<float*>(lds + kGemmLds);   // [outlier][256 rows], then [outlier][128 columns]
+  if constexpr (OUTL) {
+    const int nk = okept < kOutlLds ? okept : kOutlLds;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int slot = tid + 512 * q;
+      if (slot / kBM < nk) olds[slot] = x16_value(ox[q], outl.x_f16);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int slot = tid + 512 * q;
+      if (slot / kBN < nk) olds[kOutlLds * kBM + slot] = round16(static_cast<float>(ow[q]) * os[q], outl.x_f16);
+    }
+    __syncthreads();
+  }
 
   // Epilogue: Y = acc * a[m] * b[n] (+ the outlier product), four
   // consecutive columns per lane and tile, staged through LDS so that global
@@ -623,34 +685,47 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
       for (int r = 0; r < 4; ++r) fv[i][j][r] = static_cast<float>(acc[i][j][r]) * as[i] * bs[j][r];
   if constexpr (OUTL) {
-    // rows clamped like the scales; a column group past the end reads the
-    // last four (in the padded pitch) and is discarded at the store
-    const int kept = *outl.count;
-    const float* xrow[4];
-    const float* wcol[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = mw + 16 * i + (lane & 15);
-      xrow[i] = outl.xo + (m < M ? m : M - 1);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = nw + 16 * j + 4 * (lane >> 4);
-      wcol[j] = outl.wo + (n + 4 <= outl.pitch ? n : outl.pitch - 4);
-    }
-    for (int p = 0; p < kept; ++p) {
+    // the block-local rows and columns of this lane's outputs
+    const int nk = okept < kOutlLds ? okept : kOutlLds;
+    for (int p = 0; p < nk; ++p) {
       float xv[4];
       f32x4 wv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = xrow[i][p * M];
+      for (int i = 0; i < 4; ++i) xv[i] = olds[p * kBM + 64 * wm + 16 * i + (lane & 15)];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wv[j] = *reinterpret_cast<const f32x4*>(wcol[j] + p * outl.pitch);
+      for (int j = 0; j < 4; ++j)
+        wv[j] = *reinterpret_cast<const f32x4*>(olds + kOutlLds * kBM + p * kBN + 64 * wn + 16 * j + 4 * (lane >> 4));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) fv[i][j][r] = fmaf(xv[i], wv[j][r], fv[i][j][r]);
+    }
+    // outliers past the LDS copy: straight from X and the weights (rows and
+    // columns clamped; values past M or N are never stored)
+    for (int p = nk; p < okept; ++p) {
+      const int64_t j = outl.idx[p];
+      float xv[4], wv[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = mw + 16 * i + (lane & 15);
+        xv[i] = x16_value(outl.X[(m < M ? m : M - 1) * K + j], outl.x_f16);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t n = nw + 16 * jj + 4 * (lane >> 4) + r;
+          const int64_t nc = n < N ? n : N - 1;
+          wv[jj][r] = round16(static_cast<float>(B[nc * K + j]) * bscale[nc], outl.x_f16);
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) fv[i][jj][r] = fmaf(xv[i], wv[jj][r], fv[i][jj][r]);
     }
   }
   if constexpr (YDT == QMM_BF16) {
@@ -765,13 +840,15 @@ int check_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float*
 template <int YDT, bool FP8 = false, bool OUTL = false>
 void launch_gemm_t(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
                    int64_t K, void* Y, hipStream_t s, Outliers outl = Outliers{nullptr, nullptr, nullptr, 0}) {
-  // 144 KiB of dynamic LDS; the attribute is cheap to set and idempotent, so
-  // it is set on every launch (no per-device bookkeeping).
+  // 144 KiB of dynamic LDS (+12 KiB of outlier operands); the attribute is
+  // cheap to set and idempotent, so it is set on every launch (no per-device
+  // bookkeeping).
+  constexpr size_t lds = kGemmLds + (OUTL ? kOutlLdsBytes : 0);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&i8_gemm_kernel<YDT, FP8, OUTL>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGemmLds));
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   const int64_t tiles = ceil_div(M, kBM) * ceil_div(N, kBN);
   const dim3 grid(static_cast<unsigned>(ceil_div(tiles, kXcds) * kXcds));
-  i8_gemm_kernel<YDT, FP8, OUTL><<<grid, dim3(512), kGemmLds, s>>>(qX, xs, qW, ws, M, N, K, Y, outl);
+  i8_gemm_kernel<YDT, FP8, OUTL><<<grid, dim3(512), lds, s>>>(qX, xs, qW, ws, M, N, K, Y, outl);
 }
 
 void launch_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
@@ -1063,10 +1140,10 @@ extern "C" int fp8_w8a8_gemm(const void* X, int x_dtype, const uint8_t* qW, cons
 //  3. the per-token INT8 quantizer with those factors as its smoothing
 //     divisors: x / inf = 0, so the outlier columns are zero in X_q and take
 //     no part in a token's absmax, while x / 1 = x leaves the rest unchanged;
-//  4. the outlier columns of X and their 16-bit weights (the INT8 weight
-//     times its channel scale, rounded to the activations' type) gathered as
-//     fp32 [outlier, token] and [outlier, channel];
-//  5. the INT8 GEMM, its epilogue adding the outlier product before rounding.
+//  4. the INT8 GEMM: each block fetches its rows' outlier activations and its
+//     columns' 16-bit outlier weights (the INT8 weight times its channel
+//     scale, rounded to the activations' type) at its start, and its epilogue
+//     adds the outlier product before rounding.
 // ----------------------------------------------------------------------------
 namespace qmm {
 namespace {
@@ -1081,38 +1158,49 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p
 
 // One block.  Chunk of 1024 columns: a ballot per wavefront ranks the
 // outliers inside it, the wavefront counts in LDS give each wavefront's
-// offset, and `base` carries the count of the chunks before.
+// offset, and `base` carries the count of the chunks before.  The maxima of
+// four chunks are loaded together (one memory round trip per 4096 columns).
 __global__ __launch_bounds__(kSelThreads) void outlier_select_kernel(float* __restrict__ cx_factor, int64_t K,
                                                                      float tau, int64_t cap,
                                                                      int32_t* __restrict__ idx,
                                                                      int32_t* __restrict__ counts,
                                                                      int32_t* __restrict__ found_out) {
   constexpr int kWaves = kSelThreads / kWave;
+  constexpr int kBatch = 4;
   __shared__ int wsum[kWaves];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   int64_t base = 0;
-  for (int64_t c0 = 0; c0 < K; c0 += kSelThreads) {
-    const int64_t j = c0 + threadIdx.x;
-    const bool in = j < K;
-    const bool flag = in && cx_factor[j] >= tau;
-    const uint64_t mask = __ballot(flag);
-    const int below = __popcll(mask & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(mask);
-    __syncthreads();
-    int before = 0, total = 0;
+  for (int64_t b0 = 0; b0 < K; b0 += kBatch * kSelThreads) {
+    float v[kBatch];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = wsum[w];
-      total += c;
-      before += (w < wave) ? c : 0;
+    for (int c = 0; c < kBatch; ++c) {
+      const int64_t j = b0 + c * kSelThreads + threadIdx.x;
+      v[c] = j < K ? cx_factor[j] : 0.0f;
     }
-    const int64_t rank = base + before + below;
-    const bool keep = flag && rank < cap;
-    if (keep) idx[rank] = static_cast<int32_t>(j);
-    if (in) cx_factor[j] = keep ? __builtin_inff() : 1.0f;
-    base += total;
-    __syncthreads();   // wsum is rewritten by the next chunk
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c) {
+      const int64_t j = b0 + c * kSelThreads + threadIdx.x;
+      const bool in = j < K;
+      const bool flag = in && v[c] >= tau;
+      const uint64_t mask = __ballot(flag);
+      const int below = __popcll(mask & ((1ull << lane) - 1ull));
+      if (lane == 0) wsum[wave] = __popcll(mask);
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int cnt = wsum[w];
+        total += cnt;
+        before += (w < wave) ? cnt : 0;
+      }
+      const int64_t rank = base + before + below;
+      const bool keep = flag && rank < cap;
+      if (keep) idx[rank] = static_cast<int32_t>(j);
+      if (in) cx_factor[j] = keep ? __builtin_inff() : 1.0f;
+      base += total;
+      __syncthreads();   // wsum is rewritten by the next chunk
+    }
   }
   if (threadIdx.x == 0) {
     counts[0] = static_cast<int32_t>(base < cap ? base : cap);
@@ -1121,58 +1209,21 @@ __global__ __launch_bounds__(kSelThreads) void outlier_select_kernel(float* __re
   }
 }
 
-// The value of v in the 16-bit type XDT (nearest even; binary16 saturates
-// at its largest finite value).
-template <int XDT>
-__device__ __forceinline__ float round16(float v) {
-  if constexpr (XDT == QMM_BF16) return bf16lo_to_f32(f32_to_bf16_bits(v));
-  else return f16lo_to_f32(f32_to_f16_bits(__builtin_amdgcn_fmed3f(v, -65504.0f, 65504.0f)));
-}
-
-// grid.y walks the kept outliers, grid.x the M tokens then the N channels.
-template <int XDT>
-__global__ __launch_bounds__(256) void outlier_gather_kernel(const uint16_t* __restrict__ X,
-                                                             const int8_t* __restrict__ qW,
-                                                             const float* __restrict__ wscale, int64_t M, int64_t N,
-                                                             int64_t K, const int32_t* __restrict__ idx,
-                                                             const int32_t* __restrict__ counts,
-                                                             float* __restrict__ xo, float* __restrict__ wo,
-                                                             int64_t pitch) {
-  const int kept = counts[0];
-  for (int p = blockIdx.y; p < kept; p += gridDim.y) {
-    const int64_t j = idx[p];
-    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < M + N;
-         t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-      if (t < M) {
-        const uint32_t u = X[t * K + j];
-        xo[p * M + t] = XDT == QMM_BF16 ? bf16lo_to_f32(u) : f16lo_to_f32(u);
-      } else {
-        const int64_t n = t - M;
-        wo[p * pitch + n] = round16<XDT>(static_cast<float>(qW[n * K + j]) * wscale[n]);
-      }
-    }
-  }
-}
-
 // Workspace of the LLM.int8() call, every part at a 256-byte boundary.
 struct LlmLayout {
-  size_t qx, xs, factor, idx, counts, xo, wo, total;
-  int64_t pitch;   // N rounded up to 4 (16-byte rows for the epilogue's loads)
+  size_t qx, xs, factor, idx, counts, total;
 };
 
-LlmLayout llm_layout(int64_t M, int64_t N, int64_t K, int64_t cap) {
+LlmLayout llm_layout(int64_t M, int64_t K, int64_t cap) {
   auto up = [](size_t b) { return (b + 255u) / 256u * 256u; };
   const size_t m = static_cast<size_t>(M), k = static_cast<size_t>(K), c = static_cast<size_t>(cap);
   LlmLayout L;
-  L.pitch = (N + 3) / 4 * 4;
   size_t off = 0;
   L.qx = off;     off += up(m * k);
   L.xs = off;     off += up(m * 4u);
   L.factor = off; off += up(k * 4u);
   L.idx = off;    off += up((c > 0 ? c : 1u) * 4u);
   L.counts = off; off += 256u;
-  L.xo = off;     off += up(c * m * 4u);
-  L.wo = off;     off += up(c * static_cast<size_t>(L.pitch) * 4u);
   L.total = off;
   return L;
 }
@@ -1218,7 +1269,7 @@ extern "C" int llm_int8_outliers(const void* X, int x_dtype, int64_t M, int64_t 
 
 extern "C" size_t llm_int8_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t max_outliers) {
   if (M <= 0 || N <= 0 || K <= 0 || max_outliers < 0) return 0;
-  return llm_layout(M, N, K, max_outliers < K ? max_outliers : K).total;
+  return llm_layout(M, K, max_outliers < K ? max_outliers : K).total;
 }
 
 extern "C" int llm_int8_gemm(const void* X, int x_dtype, const int8_t* qW, const float* w_scale, int64_t M, int64_t N,
@@ -1232,7 +1283,7 @@ extern "C" int llm_int8_gemm(const void* X, int x_dtype, const int8_t* qW, const
   if (!aligned(qW, 16) || !aligned(w_scale, 4) || !aligned(Y, 4) || (n_outliers && !aligned(n_outliers, 4)))
     return QMM_EALIGN;
   const int64_t cap = max_outliers < K ? max_outliers : K;
-  const LlmLayout L = llm_layout(M, N, K, cap);
+  const LlmLayout L = llm_layout(M, K, cap);
   if (!workspace || workspace_bytes < L.total || !aligned(workspace, 16)) return QMM_EWORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int8_t* qX = reinterpret_cast<int8_t*>(ws + L.qx);
@@ -1240,23 +1291,12 @@ extern "C" int llm_int8_gemm(const void* X, int x_dtype, const int8_t* qW, const
   float* factor = reinterpret_cast<float*>(ws + L.factor);
   int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  float* xo = reinterpret_cast<float*>(ws + L.xo);
-  float* wo = reinterpret_cast<float*>(ws + L.wo);
   hipStream_t s = as_stream(stream);
   st = llm_select(X, x_dtype, M, K, threshold, cap, factor, idx, counts, n_outliers, s);
   if (st != QMM_OK) return st;
   st = launch_rowquant<1>(X, x_dtype, factor, M, K, qX, xs, s);
   if (st != QMM_OK) return st;
-  const dim3 ggrid(static_cast<unsigned>(ceil_div(M + N, 256) < 1024 ? ceil_div(M + N, 256) : 1024),
-                   static_cast<unsigned>(cap < 64 ? (cap > 0 ? cap : 1) : 64));
-  const uint16_t* x16 = static_cast<const uint16_t*>(X);
-  if (x_dtype == QMM_BF16)
-    outlier_gather_kernel<QMM_BF16><<<ggrid, 256, 0, s>>>(x16, qW, w_scale, M, N, K, idx, counts, xo, wo, L.pitch);
-  else
-    outlier_gather_kernel<QMM_F16><<<ggrid, 256, 0, s>>>(x16, qW, w_scale, M, N, K, idx, counts, xo, wo, L.pitch);
-  st = launch_status();
-  if (st != QMM_OK) return st;
-  const Outliers outl{counts, xo, wo, L.pitch};
+  const Outliers outl{counts, idx, static_cast<const uint16_t*>(X), x_dtype == QMM_F16 ? 1 : 0};
   if (y_dtype == QMM_F32) launch_gemm_t<QMM_F32, false, true>(qX, xs, qW, w_scale, M, N, K, Y, s, outl);
   else launch_gemm_t<QMM_BF16, false, true>(qX, xs, qW, w_scale, M, N, K, Y, s, outl);
   return launch_status();

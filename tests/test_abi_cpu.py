@@ -175,10 +175,10 @@ def test_w8a8_argument_errors():
 def test_llm_int8_workspace_and_argument_errors():
     lib = qmm.lib()
     ws = lib.llm_int8_workspace_bytes
-    # X_q, token scales, factors, index list, counts, gathered activations and weights (N padded to 4)
-    assert ws(2048, 4096, 4096, 64) == (2048 * 4096 + 2048 * 4 + 4096 * 4 + 256 + 256
-                                        + 64 * 2048 * 4 + 64 * 4096 * 4)
-    assert ws(3, 5, 64, 2) == 256 + 256 + 256 + 256 + 256 + 256 + 256
+    # X_q, token scales, factors, index list, counts (each at a 256-byte boundary)
+    assert ws(2048, 4096, 4096, 64) == 2048 * 4096 + 2048 * 4 + 4096 * 4 + 256 + 256
+    assert ws(3, 5, 64, 2) == 256 * 5
+    assert ws(2048, 4096, 4096, 4096) == 2048 * 4096 + 2048 * 4 + 4096 * 4 + 4096 * 4 + 256
     assert ws(4, 8, 128, 10**6) == ws(4, 8, 128, 128)                  # the cap is at most K
     assert ws(0, 8, 128, 4) == 0 and ws(4, 8, 128, -1) == 0
     g = lib.llm_int8_gemm

@@ -172,3 +172,17 @@ def test_llm_int8_full_size():
     sel = torch.from_numpy(rows)
     assert_close(y.cpu()[sel], ry, "llm_int8 full size f32")
     assert_close(yb.cpu()[sel], ry, "llm_int8 full size bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_llm_int8_outliers_past_the_staged_ones(dtype):
+    # 23 outlier columns: the GEMM stages the first ones beside its LDS tiles
+    # and reads the rest straight from X and the weights; ragged M and N
+    M, N, K = 300, 390, 1152
+    g = np.random.Generator(np.random.PCG64(31))
+    x = np.clip(workloads.gaussian(g, (M, K), 1.0), -5.0, 5.0)
+    cols = np.sort(g.choice(K, size=23, replace=False))
+    x[g.integers(0, M, size=cols.size), cols] = np.float32(-60.0)
+    qw, b = _weights(N, K, 32)
+    _, ridx = _gemm_case(workloads.to_dtype(x, dtype), dtype, qw, b, None, "f32", "23 outliers")
+    assert len(ridx) == 23
