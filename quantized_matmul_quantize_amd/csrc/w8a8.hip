@@ -340,8 +340,8 @@ __global__ __launch_bounds__(256) void tensor_scale_kernel(float* __restrict__ s
 //   chunk 1: MFMAs on fragments (t, 1) | read fragments (t+1, 0).
 // Every load is issued on every step (clamped past the end, never read), so
 // the explicit wait count is exact.  Rows past M / N lie beyond the buffer
-// resource and read as zero; when K % 128 == 64 the second B chunk of the
-// last step is likewise fetched out of range, so its MFMAs add zero.  Tiles
+// resource and read as zero; when K % 128 == 64 the second chunk of the last
+// step (A and B) is likewise fetched out of range, so its MFMAs add zero.  Tiles
 // are ordered so that the blocks sharing an XCD (block id mod 8) cover a
 // compact 4 x 8 patch of the output and share A and B rows in that XCD's L2.
 //
@@ -470,13 +470,19 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
   // Load q of this wavefront fills half-slice I = loads * wave + q of A (4
   // per wavefront) or of B (2); lane l writes slot 64 (I & 1) + l of slice
   // I / 2, i.e. row r = 8 (I & 1) + l / 8 of that slice, chunk (l % 8) ^ g(r).
-  int aoff[kLoadsA8], boff[kLoadsB8], bz[kLoadsB8];
+  // When K % 128 == 64 the second chunk of the last step lies past the end
+  // of each row (the next row's first bytes): both operands fetch it out of
+  // the buffer's range (zeros), so no value from another row enters a
+  // product -- an fp8 NaN code there would otherwise survive a zero partner.
+  int aoff[kLoadsA8], az[kLoadsA8], boff[kLoadsB8], bz[kLoadsB8];
 #pragma unroll
   for (int q = 0; q < kLoadsA8; ++q) {
     const int I = kLoadsA8 * wave + q;
     const int r = 8 * (I & 1) + (lane >> 3);
     const int row = 16 * (I >> 1) + r;
-    aoff[q] = row * kk + (((lane & 7) ^ swz(r)) * 16);
+    const int c = (lane & 7) ^ swz(r);
+    aoff[q] = row * kk + c * 16;
+    az[q] = (c >= 4) ? kOutOfRange : 0;
   }
 #pragma unroll
   for (int q = 0; q < kLoadsB8; ++q) {
@@ -498,7 +504,7 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
     for (int q = 0; q < kLoadsA8; ++q) {
       const int I = kLoadsA8 * wave + q;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_ptr_t)(uintptr_t)(sbase + (I >> 1) * kSlice + (I & 1) * 1024),
-                                               16, aoff[q], k0, 0, 0);
+                                               16, aoff[q] + (tail ? az[q] : 0), k0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < kLoadsB8; ++q) {

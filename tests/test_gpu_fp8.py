@@ -124,3 +124,29 @@ def test_fp8_argument_errors():
     assert lib.fp8_gemm(P, P, P, P, 4, 4, 64, P, qmm.I32, None) == -2            # no raw int output
     assert lib.fp8_gemm(P, None, P, P, 4, 4, 64, P, qmm.BF16, None) == -1        # scales required
     assert lib.fp8_w8a8_gemm(P, qmm.BF16, P, P, 4, 4, 64, P, qmm.BF16, P, 16, None) == -4   # workspace
+
+
+def test_fp8_gemm_tail_keeps_rows_apart():
+    # K % 128 == 64: the second half of the last k-step lies past the end of
+    # every row (the next row's first bytes).  NaN codes at the start of one
+    # row of each operand must reach only that row's outputs; every other
+    # output equals the exact product.
+    g = np.random.Generator(np.random.PCG64(14))
+    M, N, K = 40, 72, 192
+    vals = np.float32([0, 1, -1, 2, -2, 0.5, 4])
+    a = vals[g.integers(0, len(vals), (M, K))]
+    b = vals[g.integers(0, len(vals), (N, K))]
+    qa, qb = oracle.to_e4m3(a), oracle.to_e4m3(b)
+    qa[7, 0] = 0x7F                                   # E4M3FN NaN
+    qb[11, 3] = 0xFF
+    note("fp8_gemm NaN codes next to the K tail")
+    y = qmm.fp8_gemm(torch.from_numpy(qa).to(DEV), torch.ones(M, device=DEV), torch.from_numpy(qb).to(DEV),
+                     torch.ones(N, device=DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.fp8_matmul_nt(qa, qb)
+    yv = y.cpu().numpy().astype(np.float64)
+    poisoned = np.zeros((M, N), bool)
+    poisoned[7, :] = True
+    poisoned[:, 11] = True
+    assert np.isnan(ref[poisoned]).all() and np.isnan(yv[poisoned]).all()
+    assert np.array_equal(yv[~poisoned], ref[~poisoned])
