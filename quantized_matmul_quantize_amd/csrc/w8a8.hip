@@ -712,26 +712,26 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
     // columns clamped; values past M or N are never stored)
     for (int p = nk; p < okept; ++p) {
       const int64_t j = outl.idx[p];
-      float xv[4], wv[4][4];
+      float xv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t m = mw + 16 * i + (lane & 15);
         xv[i] = x16_value(outl.X[(m < M ? m : M - 1) * K + j], outl.x_f16);
       }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < 4; ++jj) {
+        float wv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int64_t n = nw + 16 * jj + 4 * (lane >> 4) + r;
           const int64_t nc = n < N ? n : N - 1;
-          wv[jj][r] = round16(static_cast<float>(B[nc * K + j]) * bscale[nc], outl.x_f16);
+          wv[r] = round16(static_cast<float>(B[nc * K + j]) * bscale[nc], outl.x_f16);
         }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) fv[i][jj][r] = fmaf(xv[i], wv[jj][r], fv[i][jj][r]);
+          for (int r = 0; r < 4; ++r) fv[i][jj][r] = fmaf(xv[i], wv[r], fv[i][jj][r]);
+      }
     }
   }
   if constexpr (YDT == QMM_BF16) {
