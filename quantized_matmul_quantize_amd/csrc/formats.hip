@@ -32,6 +32,8 @@
 namespace qmm {
 namespace {
 
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
 constexpr int kChunk = 2048;                 // weights of a row per wavefront pass (64 lanes x 32)
 constexpr float kScaleMax16 = 65504.0f;      // largest finite binary16
 
@@ -136,11 +138,9 @@ __device__ __forceinline__ void load32(const uint8_t* p, Lane32<BITS>& l) {
     const u32x4 b = ld16_nt(p + 16);
     l.w[0] = a.x; l.w[1] = a.y; l.w[2] = a.z; l.w[3] = a.w;
     l.w[4] = b.x; l.w[5] = b.y; l.w[6] = b.z; l.w[7] = b.w;
-  } else {
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-    l.w[0] = __builtin_nontemporal_load(q);
-    l.w[1] = __builtin_nontemporal_load(q + 1);
-    l.w[2] = __builtin_nontemporal_load(q + 2);
+  } else {   // one 12-byte access for the 96-bit slice
+    const u32x3 a = __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(p));
+    l.w[0] = a.x; l.w[1] = a.y; l.w[2] = a.z;
   }
 }
 
@@ -152,10 +152,7 @@ __device__ __forceinline__ void store32(uint8_t* p, const Lane32<BITS>& l) {
     st16_nt(p, u32x4{l.w[0], l.w[1], l.w[2], l.w[3]});
     st16_nt(p + 16, u32x4{l.w[4], l.w[5], l.w[6], l.w[7]});
   } else {
-    uint32_t* q = reinterpret_cast<uint32_t*>(p);
-    __builtin_nontemporal_store(l.w[0], q);
-    __builtin_nontemporal_store(l.w[1], q + 1);
-    __builtin_nontemporal_store(l.w[2], q + 2);
+    __builtin_nontemporal_store(u32x3{l.w[0], l.w[1], l.w[2]}, reinterpret_cast<u32x3*>(p));
   }
 }
 
@@ -401,11 +398,9 @@ struct Slice {
 
 template <int BITS>
 __device__ __forceinline__ void load_slice(const uint8_t* p, Slice<BITS>& sl) {
-  if constexpr (BITS == 3) {
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-    sl.w[0] = __builtin_nontemporal_load(q);
-    sl.w[1] = __builtin_nontemporal_load(q + 1);
-    sl.w[2] = __builtin_nontemporal_load(q + 2);
+  if constexpr (BITS == 3) {   // one 12-byte load (dwordx3) for the 96-bit slice
+    const u32x3 a = __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(p));
+    sl.w[0] = a.x; sl.w[1] = a.y; sl.w[2] = a.z;
   } else {
     const u32x4 a = ld16_nt(p);
     sl.w[0] = a.x; sl.w[1] = a.y; sl.w[2] = a.z; sl.w[3] = a.w;
