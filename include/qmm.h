@@ -176,9 +176,12 @@ int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8_t* zeros, 
  *             at 65504, and 1 if that is 0.
  * Storage:
  *  * codes  : 4 bits -- the code words described above; 8 bits -- one byte per
- *             weight, [N, K]; 3 bits -- each row a little-endian bit string,
- *             element i in bits 3i..3i+2, [N, 3K/8] bytes (K % 32 == 0 follows
- *             from the group sizes).
+ *             weight, [N, K]; 3 bits -- [N, 3K/8] bytes, each run of 32
+ *             weights e = 0..31 of a row in three little-endian 32-bit words
+ *             W0..W2: e < 30 in word e / 10 at bit 3 (r / 2) + 16 (r % 2),
+ *             r = e % 10, so consecutive codes sit 16 bits apart; bit t of
+ *             e = 30 at bit 15 of W[t], bit t of e = 31 at bit 31 of W[t]
+ *             (K % 32 == 0 follows from the group sizes).
  *  * scales : [N, G] of scale_dtype.
  *  * zeros  : [N, ceil(G/2)] nibble pairs for 3 and 4 bits (as above), [N, G]
  *             bytes for 8 bits.

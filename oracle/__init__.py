@@ -195,7 +195,9 @@ def f16_to_f32(h) -> np.ndarray:
 
 
 def pack_codes3(vals) -> np.ndarray:
-    """3-bit codes packed along each row as a little-endian bit string (element i in bits 3i..3i+2)."""
+    """3-bit codes in the library's layout: per run of 32 elements of a row, three little-endian words;
+    element e < 30 in word e // 10 at bit 3 (r // 2) + 16 (r % 2), r = e % 10; bit t of element 30
+    (31) at bit 15 (31) of word t."""
     vals = np.ascontiguousarray(vals, np.uint8)
     if vals.ndim == 1:
         vals = vals[None, :]

@@ -316,26 +316,37 @@ int oq_pack_codes(const uint8_t* vals, int64_t rows, int64_t count, uint8_t* out
 }
 
 /* ------------------------------------------------------------------------ */
-/* 3-bit codes: the row is a little-endian bit string, element i in bits     */
-/* 3i..3i+2, i.e. each run of 32 elements fills three 32-bit words.  (The    */
-/* pages count bits per weight, not an order; consecutive packing is the     */
-/* plain one.)  count must be a multiple of 32.                              */
+/* 3-bit codes.  The pages count bits per weight, not an order; the stored   */
+/* layout is the library's, chosen so that two consecutive codes sit 16 bits */
+/* apart in one word.  Each run of 32 elements e = 0..31 of a row fills      */
+/* three little-endian 32-bit words W0, W1, W2 (12 bytes):                   */
+/*   e < 30: word W[e / 10]; with r = e % 10, bits 3 (r / 2) .. +2 when r is */
+/*           even and 16 + 3 (r / 2) .. +2 when r is odd;                    */
+/*   e = 30: bit t of its code is bit 15 of W[t] (t = 0, 1, 2);              */
+/*   e = 31: bit t of its code is bit 31 of W[t].                            */
+/* count must be a multiple of 32.                                           */
 /* ------------------------------------------------------------------------ */
 int oq_pack_codes3(const uint8_t* vals, int64_t rows, int64_t count, uint8_t* out)
 {
     if (!vals || !out || rows < 0 || count < 0 || count % 32 != 0) return OQ_BAD_ARG;
     const int64_t row_bytes = count * 3 / 8;
-    for (int64_t r = 0; r < rows; ++r) {
-        uint8_t* o = out + r * row_bytes;
-        for (int64_t b = 0; b < row_bytes; ++b) o[b] = 0;
-        for (int64_t i = 0; i < count; ++i) {
-            uint32_t v = vals[r * count + i] & 7u;
-            for (int t = 0; t < 3; ++t) {
-                int64_t bit = 3 * i + t;
-                if (v >> t & 1u) o[bit / 8] |= (uint8_t)(1u << (bit % 8));
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t run = 0; run < count / 32; ++run) {
+            const uint8_t* e = vals + r * count + 32 * run;
+            uint32_t w[3] = {0, 0, 0};
+            for (int i = 0; i < 30; ++i) {
+                const int rr = i % 10;
+                const int pos = 3 * (rr / 2) + 16 * (rr % 2);
+                w[i / 10] |= (uint32_t)(e[i] & 7u) << pos;
             }
+            for (int t = 0; t < 3; ++t) {
+                w[t] |= (uint32_t)((e[30] >> t) & 1u) << 15;
+                w[t] |= (uint32_t)((e[31] >> t) & 1u) << 31;
+            }
+            uint8_t* o = out + r * row_bytes + 12 * run;
+            for (int k = 0; k < 3; ++k)
+                for (int b = 0; b < 4; ++b) o[4 * k + b] = (uint8_t)(w[k] >> (8 * b));
         }
-    }
     return OQ_OK;
 }
 

@@ -14,8 +14,11 @@
 // Stored format (fixed by include/qmm.h):
 //  * codes: 4 bits -- the library's code words (element 8w+2i of a row at bits
 //    4i of little-endian word w, element 8w+2i+1 at bits 16+4i); 8 bits -- one
-//    byte per weight; 3 bits -- a little-endian bit string per row, element i
-//    at bits 3i..3i+2 (each run of 32 weights fills three 32-bit words).
+//    byte per weight; 3 bits -- each run of 32 weights e = 0..31 of a row in
+//    three little-endian words W0..W2: e < 30 in word e / 10 at bit
+//    3 (r / 2) + 16 (r % 2), r = e % 10 (so consecutive codes 2m, 2m+1 sit 16
+//    bits apart, like the 4-bit pairs); bit t of e = 30 at bit 15 of W[t],
+//    bit t of e = 31 at bit 31 of W[t].
 //  * scales: [N, G] fp32 or binary16.  The codes are computed with the stored
 //    value: a binary16 scale is the fp32 scale rounded to nearest even
 //    (saturating at 65504), and 1 if that is 0.
@@ -90,24 +93,16 @@ __device__ __forceinline__ void pack32(const float c[32], Lane32<BITS>& out) {
       out.w[j] = word;
     }
   } else {
-    uint64_t lo = 0;
-    uint32_t hi = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t v = static_cast<uint32_t>(c[i]);
-      const int pos = 3 * i;
-      if (pos + 3 <= 64) {
-        lo |= static_cast<uint64_t>(v) << pos;
-      } else if (pos >= 64) {
-        hi |= v << (pos - 64);
-      } else {
-        lo |= static_cast<uint64_t>(v) << pos;
-        hi |= v >> (64 - pos);
-      }
+    for (int j = 0; j < 3; ++j) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int r = 0; r < 10; ++r) word |= static_cast<uint32_t>(c[10 * j + r]) << (3 * (r >> 1) + 16 * (r & 1));
+      const uint32_t v30 = static_cast<uint32_t>(c[30]), v31 = static_cast<uint32_t>(c[31]);
+      word |= ((v30 >> j) & 1u) << 15;
+      word |= ((v31 >> j) & 1u) << 31;
+      out.w[j] = word;
     }
-    out.w[0] = static_cast<uint32_t>(lo);
-    out.w[1] = static_cast<uint32_t>(lo >> 32);
-    out.w[2] = hi;
   }
 }
 
@@ -119,12 +114,12 @@ __device__ __forceinline__ int code_at(const Lane32<BITS>& l, int i) {
   } else if constexpr (BITS == 8) {
     return static_cast<int>((l.w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
   } else {
-    const int pos = 3 * i;
-    const int wi = pos >> 5;
-    const int sh = pos & 31;
-    uint32_t v = l.w[wi] >> sh;
-    if (sh > 29) v |= l.w[wi + 1] << (32 - sh);
-    return static_cast<int>(v & 7u);
+    if (i < 30) {
+      const int r = i % 10;
+      return static_cast<int>((l.w[i / 10] >> (3 * (r >> 1) + 16 * (r & 1))) & 7u);
+    }
+    const int b = i == 30 ? 15 : 31;
+    return static_cast<int>(((l.w[0] >> b) & 1u) | (((l.w[1] >> b) & 1u) << 1) | (((l.w[2] >> b) & 1u) << 2));
   }
 }
 
@@ -341,14 +336,24 @@ struct PairOff {
   static constexpr uint32_t magic = BITS == 3 ? Int3Magic<XDT>::kMagic : Int4Magic<XDT>::kMagic;
 };
 
+// Pair i (0..4) of a 3-bit code word -- the codes at bits 3i and 16 + 3i --
+// moved to the magic's mantissa position with one shift and one AND-OR.
 template <int XDT>
-__device__ __forceinline__ uint32_t pair_from_field6(uint32_t f, uint32_t magic) {
-  // f: two 3-bit codes, the first in bits 0-2, the second in bits 3-5
-  if constexpr (XDT == QMM_BF16) {
-    return ((f & 7u) << 4) | ((f & 0x38u) << 17) | magic;
-  } else {
-    return ((f & 7u) << 7) | ((f & 0x38u) << 20) | magic;
-  }
+__device__ __forceinline__ uint32_t pair3_at(uint32_t w, int i, uint32_t magic) {
+  constexpr int kPos = XDT == QMM_BF16 ? 4 : 7;
+  constexpr uint32_t kMask = 0x00070007u << kPos;
+  const int sh = kPos - 3 * i;
+  return ((sh >= 0 ? w << sh : w >> -sh) & kMask) | magic;
+}
+
+// The run's last pair (codes 30 and 31), one bit from each word's bits 15 and 31.
+template <int XDT>
+__device__ __forceinline__ uint32_t pair3_last(const uint32_t w[3], uint32_t magic) {
+  constexpr int kPos = XDT == QMM_BF16 ? 4 : 7;
+  uint32_t p = ((w[0] >> (15 - kPos)) & (0x00010001u << kPos)) | magic;
+  p |= (w[1] >> (14 - kPos)) & (0x00020002u << kPos);
+  p |= (w[2] >> (13 - kPos)) & (0x00040004u << kPos);
+  return p;
 }
 
 template <int XDT>
@@ -407,24 +412,6 @@ __device__ __forceinline__ void load_slice(const uint8_t* p, Slice<BITS>& sl) {
   }
 }
 
-// Code c (0..31) of a 3-bit slice: bits 3c..3c+2 of the 96-bit string.
-__device__ __forceinline__ uint32_t code3(const uint32_t w[3], int c) {
-  const int pos = 3 * c;
-  const int wi = pos >> 5;
-  const int sh = pos & 31;
-  if (sh <= 29) return __builtin_amdgcn_ubfe(w[wi], sh, 3);
-  return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 7u;
-}
-
-template <int XDT>
-__device__ __forceinline__ uint32_t pair3(uint32_t lo, uint32_t hi, uint32_t magic) {
-  // two 3-bit codes one step below the 4-bit nibble position (Int3Magic)
-  if constexpr (XDT == QMM_BF16) {
-    return (lo << 4) | (hi << 20) | magic;
-  } else {
-    return (lo << 7) | (hi << 23) | magic;
-  }
-}
 
 template <int XDT, int BITS>
 __device__ __forceinline__ void slice_pairs(const Slice<BITS>& sl, uint32_t magic, uint32_t p[Slice<BITS>::kPairs]) {
@@ -439,7 +426,10 @@ __device__ __forceinline__ void slice_pairs(const Slice<BITS>& sl, uint32_t magi
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) p[j] = pair3<XDT>(code3(sl.w, 2 * j), code3(sl.w, 2 * j + 1), magic);
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int i = 0; i < 5; ++i) p[5 * j + i] = pair3_at<XDT>(sl.w[j], i, magic);
+    p[15] = pair3_last<XDT>(sl.w, magic);
   }
 }
 
@@ -609,17 +599,15 @@ __device__ __forceinline__ void load_pairs8(const uint8_t* crow, int64_t k, uint
     p[2] = pair_from_bytes<XDT>(w.y, 0);
     p[3] = pair_from_bytes<XDT>(w.y, 2);
   } else {
-    // 24 bits at bit 3k: inside the chunk's three words (k % 32 in {0, 8, 16, 24})
+    // pairs 4q .. 4q + 3 of the run's 16 (q = (k % 32) / 8)
     const uint32_t* wc = reinterpret_cast<const uint32_t*>(crow + (k >> 5) * 12);
     const int q = static_cast<int>((k >> 3) & 3);
-    const uint32_t w0 = wc[0], w1 = wc[1], w2 = wc[2];
-    uint32_t v;
-    if (q == 0) v = w0;
-    else if (q == 1) v = (w0 >> 24) | (w1 << 8);
-    else if (q == 2) v = (w1 >> 16) | (w2 << 16);
-    else v = w2 >> 8;
+    const uint32_t w[3] = {wc[0], wc[1], wc[2]};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = pair_from_field6<XDT>(v >> (6 * j), magic);
+    for (int j = 0; j < 4; ++j) {
+      const int m = 4 * q + j;
+      p[j] = m == 15 ? pair3_last<XDT>(w, magic) : pair3_at<XDT>(m < 5 ? w[0] : m < 10 ? w[1] : w[2], m % 5, magic);
+    }
   }
 }
 

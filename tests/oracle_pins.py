@@ -650,23 +650,25 @@ def check_bit_width_errors():
 
 
 def check_codes3_packing():
-    # 3-bit codes, a little-endian bit string along the row; the expected
-    # bytes of one run of 32 codes written out by hand.
+    # 3-bit codes in the library's layout (consecutive codes 16 bits apart);
+    # the expected words of one run of 32 codes written out by hand.
     vals = np.array([[1, 2, 3, 4, 5, 6, 7, 0] * 4], np.uint8)
     p = oracle.pack_codes3(vals)
     assert p.shape == (1, 12)
-    # codes 1,2,3,4,5,6,7,0 at bits 0,3,6,...: the 24-bit value
-    # 1 + 2*8 + 3*64 + 4*512 + 5*4096 + 6*32768 + 7*262144 = 0x1F58D1,
-    # bytes D1 58 1F (little-endian), repeated for each group of eight codes
-    assert p[0].tolist() == [0xD1, 0x58, 0x1F] * 4
+    # W0 holds elements 0..9: the even ones 1, 3, 5, 7, 1 at bits 0, 3, 6, 9,
+    # 12 (0x1F59), the odd ones 2, 4, 6, 0, 2 at bits 16, 19, .. (0x21A2 << 16),
+    # and bit 0 of element 30 (= 7) at bit 15; element 31 (= 0) adds nothing.
+    # W1: 3, 5, 7, 1, 3 -> 0x33EB; 4, 6, 0, 2, 4 -> 0x4434.  W2: 5, 7, 1, 3, 5
+    # -> 0x567D; 6, 0, 2, 4, 6 -> 0x6886.
+    assert p.view("<u4")[0].tolist() == [0x21A29F59, 0x4434B3EB, 0x6886D67D]
     v2 = np.zeros((1, 32), np.uint8)
-    v2[0, 10] = 7          # bits 30..32: crosses the first 32-bit word
-    v2[0, 21] = 5          # bits 63..65: crosses the second
-    p2 = oracle.pack_codes3(v2)
-    words = p2.view("<u4")[0]
-    assert words.tolist() == [0xC0000000, 0x80000001, 0x00000002]
-    back = [(int.from_bytes(p2[0].tobytes(), "little") >> (3 * i)) & 7 for i in range(32)]
-    assert back == v2[0].tolist()
+    v2[0, 30] = 6          # 0b110: bit 15 of W1 and W2
+    v2[0, 31] = 3          # 0b011: bit 31 of W0 and W1
+    assert oracle.pack_codes3(v2).view("<u4")[0].tolist() == [0x80000000, 0x80008000, 0x00008000]
+    v3 = np.zeros((2, 64), np.uint8)
+    v3[1, 32 + 13] = 7     # second row, second run: element 13 -> W1 bits 19..21
+    w3 = oracle.pack_codes3(v3).view("<u4")
+    assert w3.shape == (2, 6) and w3[1].tolist() == [0, 0, 0, 0, 0x00380000, 0] and not w3[0].any()
 
 
 def check_symmetric_format():

@@ -56,7 +56,10 @@ MUTANTS = [
      "if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);"),
     ("f16_scale_zero_kept", "if (s16 == 0.0f) s16 = 1.0f;", ""),
     ("codes_from_f32_scale", "if (scale_f16) s = f16_scale(s);", ""),
-    ("codes3_bit_order", "int64_t bit = 3 * i + t;", "int64_t bit = 3 * i + (2 - t);"),
+    ("codes3_halves_swapped", "const int pos = 3 * (rr / 2) + 16 * (rr % 2);",
+     "const int pos = 3 * (rr / 2) + 16 * ((rr + 1) % 2);"),
+    ("codes3_last_pair_words_reversed", "w[t] |= (uint32_t)((e[30] >> t) & 1u) << 15;",
+     "w[2 - t] |= (uint32_t)((e[30] >> t) & 1u) << 15;"),
     ("sym_zero_point_off_by_one", "zf = half;                       /* R22 */", "zf = half - 1.0f;"),
     ("e4m3_round_half_away", "double r = nearbyint(ldexp(a, 3 - e));", "double r = round(ldexp(a, 3 - e));"),
     ("e4m3_bias_8", "return (uint8_t)(sign | (uint8_t)((e + 7) << 3) | (uint8_t)(r - 8.0));",
