@@ -170,13 +170,82 @@ __device__ __forceinline__ float group_max(float v, int L) {
 // (the correction of the 4-bit quantizer), exact division outside
 // [2^-100, 2^100].
 // ----------------------------------------------------------------------------
+// The arithmetic of one lane's 32 weights v (weights kl .. kl + 31 of row n;
+// `active` false for lanes past K, which compute but store nothing).
+template <int BITS, bool SYM>
+__device__ __forceinline__ void quantize_fmt_lane(const float v[32], int lane, int L, int lg, int s16, bool active,
+                                                  int64_t n, int64_t kl, int64_t K, int64_t G, int64_t zrb,
+                                                  uint8_t* __restrict__ codes, void* __restrict__ scales,
+                                                  uint8_t* __restrict__ zeros) {
+  constexpr float kQmax = static_cast<float>((1 << BITS) - 1);
+  constexpr float kHalf = static_cast<float>(1 << (BITS - 1));
+  float s, zf;
+  if constexpr (SYM) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = group_max(amax, L);
+    s = stored_scale(fmaxf(amax, 1e-8f) / (kHalf - 1.0f), s16 != 0);
+    zf = kHalf;
+  } else {
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      lo = fminf(lo, v[i]);
+      hi = fmaxf(hi, v[i]);
+    }
+    lo = group_min(lo, L);
+    hi = group_max(hi, L);
+    float sc = (hi - lo) / kQmax;                    // correctly rounded fp32 division
+    if (sc == 0.0f) sc = 1.0f;
+    s = stored_scale(sc, s16 != 0);
+    zf = fminf(rintf(-lo / s), kQmax);               // beyond kQmax only for a saturated 16-bit scale
+  }
+  const float y = 1.0f / s;
+  const bool scale_ok = (s >= 0x1p-100f) && (s <= 0x1p100f);
+  float cq[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float q0 = v[i] * y;
+    const float r = fmaf(-q0, s, v[i]);
+    cq[i] = rintf(fmaf(r, y, q0)) + zf;
+  }
+  if (__builtin_amdgcn_ballot_w64(!scale_ok)) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float e = rintf(v[i] / s) + zf;
+      if (!scale_ok) cq[i] = e;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) cq[i] = __builtin_amdgcn_fmed3f(cq[i], 0.0f, kQmax);
+  Lane32<BITS> out;
+  pack32<BITS>(cq, out);
+  const float z_next = __shfl_down(zf, L, kWave);      // zero-point of the next group
+  if (active) {
+    store32<BITS>(codes + n * code_row_bytes(K, BITS) + kl * BITS / 8, out);
+    const int64_t g = kl >> lg;
+    if ((lane & (L - 1)) == 0) {
+      if (s16) {
+        static_cast<uint16_t*>(scales)[n * G + g] = static_cast<uint16_t>(f32_to_f16_bits(s));
+      } else {
+        static_cast<float*>(scales)[n * G + g] = s;
+      }
+      if constexpr (BITS == 8) {
+        zeros[n * zrb + g] = static_cast<uint8_t>(zf);
+      } else if ((g & 1) == 0) {
+        const uint32_t zo = (g + 1 < G) ? static_cast<uint32_t>(z_next) : 0u;
+        zeros[n * zrb + (g >> 1)] = static_cast<uint8_t>(static_cast<uint32_t>(zf) | (zo << 4));
+      }
+    }
+  }
+}
+
 template <int DT, int BITS, bool SYM>
 __global__ __launch_bounds__(256) void quantize_fmt_kernel(const uint8_t* __restrict__ w, int64_t N, int64_t K,
                                                            int lg, int s16, uint8_t* __restrict__ codes,
                                                            void* __restrict__ scales, uint8_t* __restrict__ zeros) {
   constexpr int kElem = DT == QMM_F32 ? 4 : 2;
-  constexpr float kQmax = static_cast<float>((1 << BITS) - 1);
-  constexpr float kHalf = static_cast<float>(1 << (BITS - 1));
   const int lane = threadIdx.x & (kWave - 1);
   const int L = 1 << (lg - 5);
   const int64_t G = K >> lg;
@@ -195,66 +264,98 @@ __global__ __launch_bounds__(256) void quantize_fmt_kernel(const uint8_t* __rest
     float v[32];
 #pragma unroll
     for (int q = 0; q < 4; ++q) Vec8<DT>::load(src + q * 8 * kElem, &v[8 * q]);
-    float s, zf;
-    if constexpr (SYM) {
-      float amax = 0.0f;
+    quantize_fmt_lane<BITS, SYM>(v, lane, L, lg, s16, active, n, kl, K, G, zrb, codes, scales, zeros);
+  }
+}
+
+// 16-bit weights: each wavefront's 2048-weight chunk (4 KiB, contiguous in
+// its row) reaches LDS by four buffer loads that each cover 1 KiB
+// contiguously -- every lane loading its own 64 bytes spans 4 KiB per
+// instruction -- double buffered (the next chunk's loads issued before the
+// current one is read).  LDS slots as in the 4-bit quantizer of 16-bit
+// weights: 16-byte piece P (lane l reads pieces 4l .. 4l+3) at slot
+// 64 (P / 64) + 4 m + ((j + m / 4) & 3), m = (P / 4) % 16, j = P % 4, so the
+// four reads of each lane are free of bank conflicts.  Bytes of a chunk past
+// the end of its row read zero.
+constexpr int kFmtChunkBytes = kChunk * 2;
+
+template <int DT, int BITS, bool SYM>
+__global__ __launch_bounds__(256) void quantize_fmt_lds_kernel(const uint8_t* __restrict__ w, int64_t N, int64_t K,
+                                                               int lg, int s16, uint8_t* __restrict__ codes,
+                                                               void* __restrict__ scales,
+                                                               uint8_t* __restrict__ zeros) {
+  static_assert(DT != QMM_F32, "16-bit weights only");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * 2 * kFmtChunkBytes];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int L = 1 << (lg - 5);
+  const int64_t G = K >> lg;
+  const int64_t cpr = (K + kChunk - 1) / kChunk;
+  const int64_t total = N * cpr;
+  const int64_t zrb = zero_row_bytes(G, BITS);
+  const int64_t waves_per_block = blockDim.x / kWave;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * waves_per_block;
+  const uint32_t wbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + wave * 2 * kFmtChunkBytes;
+
+  // Load lane l of instruction q fetches piece 64 q + 4 m + ((l % 4 - m / 4) & 3),
+  // m = l / 4, and writes slot 64 q + l.
+  const int lm = lane >> 2;
+  const int fetch = (4 * lm + (((lane & 3) - (lm >> 2)) & 3)) * 16;
+  auto issue = [&](int64_t c, int buf) {
+    const int64_t n = c / cpr;
+    const int64_t k0 = (c - n * cpr) * kChunk;
+    const int64_t left = (K - k0) * 2;
+    const int bytes = static_cast<int>(left < kFmtChunkBytes ? left : kFmtChunkBytes);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(w + (n * K + k0) * 2), 0, bytes, kBufferWord3);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      amax = group_max(amax, L);
-      s = stored_scale(fmaxf(amax, 1e-8f) / (kHalf - 1.0f), s16 != 0);
-      zf = kHalf;
+    for (int q = 0; q < 4; ++q) {
+      uint32_t dst = wbase + buf * kFmtChunkBytes + q * 1024;
+      int off = fetch + q * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(uintptr_t)dst, 16, off, 0, 0, 0);
+    }
+  };
+  // Reader: lane l's pieces 4l + j are in instruction l / 16, m = l % 16.
+  const int rm = lane & 15;
+  int rd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rd[j] = (lane >> 4) * 1024 + (4 * rm + ((j + (rm >> 2)) & 3)) * 16;
+
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * waves_per_block + wave;
+  int buf = 0;
+  if (c0 < total) issue(c0, 0);
+  for (int64_t c = c0; c < total; c += nwaves, buf ^= 1) {
+    const bool next = c + nwaves < total;   // uniform
+    if (next) {
+      issue(c + nwaves, buf ^ 1);
+      wait_vm<4>();
     } else {
-      float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        lo = fminf(lo, v[i]);
-        hi = fmaxf(hi, v[i]);
-      }
-      lo = group_min(lo, L);
-      hi = group_max(hi, L);
-      float sc = (hi - lo) / kQmax;                    // correctly rounded fp32 division
-      if (sc == 0.0f) sc = 1.0f;
-      s = stored_scale(sc, s16 != 0);
-      zf = fminf(rintf(-lo / s), kQmax);               // beyond kQmax only for a saturated 16-bit scale
+      wait_vm<0>();
     }
-    const float y = 1.0f / s;
-    const bool scale_ok = (s >= 0x1p-100f) && (s <= 0x1p100f);
-    float cq[32];
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint8_t* cb = lds + wave * 2 * kFmtChunkBytes + buf * kFmtChunkBytes;
+    float v[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float q0 = v[i] * y;
-      const float r = fmaf(-q0, s, v[i]);
-      cq[i] = rintf(fmaf(r, y, q0)) + zf;
-    }
-    if (__builtin_amdgcn_ballot_w64(!scale_ok)) {
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 u = *reinterpret_cast<const u32x4*>(cb + rd[j]);
+      const uint32_t a[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float e = rintf(v[i] / s) + zf;
-        if (!scale_ok) cq[i] = e;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) cq[i] = __builtin_amdgcn_fmed3f(cq[i], 0.0f, kQmax);
-    Lane32<BITS> out;
-    pack32<BITS>(cq, out);
-    const float z_next = __shfl_down(zf, L, kWave);      // zero-point of the next group
-    if (active) {
-      store32<BITS>(codes + n * code_row_bytes(K, BITS) + kl * BITS / 8, out);
-      const int64_t g = kl >> lg;
-      if ((lane & (L - 1)) == 0) {
-        if (s16) {
-          static_cast<uint16_t*>(scales)[n * G + g] = static_cast<uint16_t>(f32_to_f16_bits(s));
+      for (int h = 0; h < 4; ++h) {
+        if constexpr (DT == QMM_BF16) {
+          v[8 * j + 2 * h] = bf16lo_to_f32(a[h]);
+          v[8 * j + 2 * h + 1] = bf16hi_to_f32(a[h]);
         } else {
-          static_cast<float*>(scales)[n * G + g] = s;
-        }
-        if constexpr (BITS == 8) {
-          zeros[n * zrb + g] = static_cast<uint8_t>(zf);
-        } else if ((g & 1) == 0) {
-          const uint32_t zo = (g + 1 < G) ? static_cast<uint32_t>(z_next) : 0u;
-          zeros[n * zrb + (g >> 1)] = static_cast<uint8_t>(static_cast<uint32_t>(zf) | (zo << 4));
+          v[8 * j + 2 * h] = f16lo_to_f32(a[h]);
+          v[8 * j + 2 * h + 1] = f16hi_to_f32(a[h]);
         }
       }
     }
+    const int64_t n = c / cpr;
+    const int64_t k = (c - n * cpr) * kChunk + static_cast<int64_t>(lane) * 32;
+    const bool active = k < K;
+    quantize_fmt_lane<BITS, SYM>(v, lane, L, lg, s16, active, n, active ? k : 0, K, G, zrb, codes, scales, zeros);
+    // the LDS reads of this chunk are done before the next iteration's
+    // loads overwrite its buffer (they feed the arithmetic above)
   }
 }
 
@@ -777,10 +878,10 @@ void launch_quant_fmt(const uint8_t* w, int dt, int64_t N, int64_t K, int lg, in
   const dim3 grid(static_cast<unsigned>(fmt_grid(N, K)));
   switch (dt) {
     case QMM_BF16:
-      quantize_fmt_kernel<QMM_BF16, BITS, SYM><<<grid, 256, 0, s>>>(w, N, K, lg, s16, codes, scales, zeros);
+      quantize_fmt_lds_kernel<QMM_BF16, BITS, SYM><<<grid, 256, 0, s>>>(w, N, K, lg, s16, codes, scales, zeros);
       break;
     case QMM_F16:
-      quantize_fmt_kernel<QMM_F16, BITS, SYM><<<grid, 256, 0, s>>>(w, N, K, lg, s16, codes, scales, zeros);
+      quantize_fmt_lds_kernel<QMM_F16, BITS, SYM><<<grid, 256, 0, s>>>(w, N, K, lg, s16, codes, scales, zeros);
       break;
     default:
       quantize_fmt_kernel<QMM_F32, BITS, SYM><<<grid, 256, 0, s>>>(w, N, K, lg, s16, codes, scales, zeros);
