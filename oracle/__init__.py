@@ -75,6 +75,7 @@ def lib(parallel: bool = False) -> ctypes.CDLL:
             "oq_fp8_quantize": [P, I64, I64, I64, P, P],
             "oq_fp8_matmul_nt": [P, P, I64, I64, I64, P],
             "oq_llm_int8": [P, I64, I64, P, P, I64, F, I64, I, P, P, P, P, P],
+            "oq_awq_search": [P, P, I64, I64, I64, P, I64, P, P, P, P, P, P],
         }
         for name, argtypes in sigs.items():
             fn = getattr(l, name)
@@ -486,3 +487,29 @@ def llm_int8_reference(x, qw, b, threshold: float, max_outliers=None, x_dtype: s
     _check(lib().oq_llm_int8(_p(x), m, k, _p(qw), _p(b), n, float(threshold), cap, int(x_dtype == "bf16"),
                              _p(idx), _p(counts), _p(qx), _p(a), _p(y)), "llm_int8")
     return idx[:counts[0]].copy(), int(counts[1]), qx, a, y
+
+
+AWQ_ALPHAS = np.linspace(0.0, 1.0, 11)   # the [QS] awq listing's grid
+
+
+def awq_search_reference(w, x, alphas=None):
+    """AWQ's scaling search for weights w [N, K] and calibration activations
+    x [T, K] (the 16-bit values as float32), INT4 groups of 128 (readings R32,
+    R33).  Returns (err fp64 [len(alphas)], best index, s_best f32 [K], the
+    codes q uint8 [N, K], scales f32 [N, K/128] and zeros uint8 [N, K/128] of
+    W diag(s_best))."""
+    w = _f32(w)
+    x = _f32(x)
+    n, k = w.shape
+    t, k2 = x.shape
+    assert k == k2 and k % 128 == 0
+    a = np.ascontiguousarray(AWQ_ALPHAS if alphas is None else alphas, np.float64).reshape(-1)
+    err = np.empty(a.size, np.float64)
+    best = np.zeros(1, np.int64)
+    s = np.empty(k, np.float32)
+    q = np.empty((n, k), np.uint8)
+    sc = np.empty((n, k // 128), np.float32)
+    z = np.empty((n, k // 128), np.uint8)
+    _check(lib().oq_awq_search(_p(w), _p(x), n, k, t, _p(a), a.size, _p(err), _p(best), _p(s), _p(q), _p(sc),
+                               _p(z)), "awq_search")
+    return err, int(best[0]), s, q, sc, z

@@ -54,6 +54,18 @@
  *      saturating at 65504 as in R24).
  *  R28 the outlier columns are zero in X_q and take no part in a token's
  *      absmax.
+ *  R32 AWQ's error for a candidate alpha is the layer's output error as the
+ *      quantized layer computes it: || X W^T - X_s W_hat^T ||_F^2, X_s the
+ *      activations divided by the scales (the inverse scaling folded into
+ *      the layer's 16-bit input: fp32 quotient, then rounded to bf16) and
+ *      W_hat the dequantized codes of W diag(s); the sums in fp64.  (The
+ *      [QS] listing evaluates the same quantity as sum((D H) * D) with
+ *      D = W - W_hat / s and H from the calibration inputs.)
+ *  R33 AWQ's channel magnitudes are mean |x_j| over the calibration tokens
+ *      in fp64, floored at 1e-8 so that a silent channel keeps a finite
+ *      scale; the scales s = mag^alpha / sqrt(max * min) are computed in
+ *      fp64 and stored in fp32; the weights are quantized to INT4 in groups
+ *      of 128 with fp32 scales (the format of the rest of the path).
  */
 #include <math.h>
 #include <stddef.h>
@@ -626,6 +638,85 @@ int oq_llm_int8(const float* x, int64_t m, int64_t k, const int8_t* qw, const fl
             y[i * n + j] += s;
         }
     free(cx); free(xr); free(w16); free(acc);
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* AWQ's activation-aware scaling search.  [QS] "AWQ: protect the channels   */
+/* that matter" (W x = (W diag(s)) (diag(s)^-1 x), exact in full precision;  */
+/* s_j = mean|x_j|^alpha, one alpha per layer chosen on calibration data) and */
+/* the awq listing after it (s normalized by sqrt(max s * min s), the weights */
+/* W diag(s) quantized group-wise, the candidate of the smallest calibration  */
+/* output error kept).  Readings R32, R33.                                   */
+/* w [n, k] and x [t, k] hold the 16-bit values as floats; alphas[n_alpha].  */
+/* Outputs: err[n_alpha]; *best, the first alpha of the smallest error;      */
+/* s_best[k]; q (unpacked codes), scales, zeros of W diag(s_best).           */
+/* ------------------------------------------------------------------------ */
+int oq_awq_search(const float* w, const float* x, int64_t n, int64_t k, int64_t t, const double* alphas,
+                  int64_t n_alpha, double* err, int64_t* best, float* s_best, uint8_t* q, float* scales,
+                  uint8_t* zeros)
+{
+    if (!w || !x || !alphas || !err || !best || !s_best || !q || !scales || !zeros) return OQ_BAD_ARG;
+    if (n <= 0 || k <= 0 || t <= 0 || n_alpha <= 0 || k % 128 != 0) return OQ_BAD_ARG;
+    const int64_t g = k / 128;
+    double* mag = malloc((size_t)k * sizeof(double));
+    double* p = malloc((size_t)k * sizeof(double));
+    float* s = malloc((size_t)k * sizeof(float));
+    float* ws = malloc((size_t)(n * k) * sizeof(float));
+    float* what = malloc((size_t)(n * k) * sizeof(float));
+    float* xs = malloc((size_t)(t * k) * sizeof(float));
+    double* yref = malloc((size_t)(t * n) * sizeof(double));
+    double* yq = malloc((size_t)(t * n) * sizeof(double));
+    uint8_t* qa = malloc((size_t)(n * k));
+    float* sa = malloc((size_t)(n * g) * sizeof(float));
+    uint8_t* za = malloc((size_t)(n * g));
+    int status = OQ_OK;
+    if (!mag || !p || !s || !ws || !what || !xs || !yref || !yq || !qa || !sa || !za) {
+        status = OQ_BAD_ARG;
+        goto done;
+    }
+    /* channel magnitudes: mean |x_j| over the tokens (R33) */
+    for (int64_t j = 0; j < k; ++j) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < t; ++r) acc += fabs((double)x[r * k + j]);
+        const double m = acc / (double)t;
+        mag[j] = m < 1e-8 ? 1e-8 : m;
+    }
+    oq_matmul_nt_f64(x, w, t, n, k, yref);          /* the full-precision output X W^T */
+    int64_t bi = 0;
+    for (int64_t a = 0; a < n_alpha; ++a) {
+        double mx = 0.0, mn = INFINITY;
+        for (int64_t j = 0; j < k; ++j) {
+            p[j] = pow(mag[j], alphas[a]);
+            if (p[j] > mx) mx = p[j];
+            if (p[j] < mn) mn = p[j];
+        }
+        const double norm = sqrt(mx * mn);
+        for (int64_t j = 0; j < k; ++j) s[j] = (float)(p[j] / norm);
+        oq_scale_columns_mul(w, s, n, k, ws);       /* W diag(s) */
+        oq_asym_quantize(ws, n, k, 128, 4, qa, sa, za);
+        oq_asym_dequantize(qa, sa, za, n, k, 128, what);
+        oq_scale_columns_div(x, s, t, k, xs);       /* diag(s)^-1 folded into the 16-bit input (R32) */
+        for (int64_t i = 0; i < t * k; ++i) xs[i] = bf16_round(xs[i]);
+        oq_matmul_nt_f64(xs, what, t, n, k, yq);
+        double e = 0.0;
+        for (int64_t i = 0; i < t * n; ++i) {
+            const double d = yref[i] - yq[i];
+            e += d * d;
+        }
+        err[a] = e;
+        if (a == 0 || e < err[bi]) {
+            bi = a;
+            memcpy(s_best, s, (size_t)k * sizeof(float));
+            memcpy(q, qa, (size_t)(n * k));
+            memcpy(scales, sa, (size_t)(n * g) * sizeof(float));
+            memcpy(zeros, za, (size_t)(n * g));
+        }
+    }
+    *best = bi;
+done:
+    free(mag); free(p); free(s); free(ws); free(what); free(xs); free(yref); free(yq);
+    free(qa); free(sa); free(za);
     return status;
 }
 

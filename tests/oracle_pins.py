@@ -896,7 +896,80 @@ def check_llm_int8_accuracy():
     assert err_llm < 0.2 * err_plain, (err_llm, err_plain)
 
 
+def _awq_case(seed, n=48, k=256, t=40, salient=None):
+    g = np.random.Generator(np.random.PCG64(seed))
+    w = workloads.to_dtype(workloads.gaussian(g, (n, k), 0.02), "bf16").float().numpy()
+    x = workloads.gaussian(g, (t, k), 1.0)
+    if salient is not None:
+        x[:, salient] *= np.float32(50.0)
+    return w, workloads.to_dtype(x, "bf16").float().numpy()
+
+
+def check_awq_alpha0_is_round_to_nearest():
+    # alpha = 0 gives s = 1 in every channel: the codes are the plain
+    # group-128 quantizer's and the error is ||X (W - W_hat)^T||^2 (here by
+    # numpy's product of the dequantized weights).
+    w, x = _awq_case(1)
+    err, best, s, q, sc, z = oracle.awq_search_reference(w, x, alphas=[0.0])
+    assert best == 0 and np.array_equal(s, np.ones_like(s))
+    q0, s0, z0 = oracle.asym_quantize(w)
+    assert np.array_equal(q, q0) and np.array_equal(sc.view(np.uint32), s0.view(np.uint32)) and np.array_equal(z, z0)
+    w_hat = (q0.astype(np.float64) - np.repeat(z0, 128, axis=1)) * np.repeat(s0.astype(np.float64), 128, axis=1)
+    d = x.astype(np.float64) @ (w.astype(np.float64) - w_hat).T
+    assert np.isclose(err[0], np.sum(d * d), rtol=1e-6)
+
+
+def check_awq_uniform_magnitudes():
+    # every channel with the same mean |x|: s = 1 for every alpha, all errors
+    # equal, and the first alpha is kept -- no channel to protect, nothing to
+    # gain (the pages: the scaling helps where there are outliers, only there)
+    w, _ = _awq_case(2)
+    signs = np.where(np.random.Generator(np.random.PCG64(3)).random((40, 256)) < 0.5, -1.0, 1.0)
+    x = (signs * 0.75).astype(np.float32)
+    err, best, s, _, _, _ = oracle.awq_search_reference(w, x)
+    assert best == 0 and np.all(err == err[0]) and np.array_equal(s, np.ones_like(s))
+
+
+def check_awq_salient_channel():
+    # one input channel 50x larger than the rest: some alpha > 0 cuts the
+    # calibration output error ([QS] "Measured on two real layers": the
+    # scaling helps the layer with large activation outliers)
+    w, x = _awq_case(4, salient=17)
+    err, best, s, _, _, _ = oracle.awq_search_reference(w, x)
+    assert best > 0 and err[best] < 0.7 * err[0], (best, err)
+    assert s[17] == s.max()          # the salient channel gets the largest factor
+
+
+def check_awq_scales_closed_form():
+    # channel j has mean |x| = j + 1 (j < 64: +-(j+1) over two tokens; from
+    # 64 on: 2(j+1) and 0, so the mean and the largest value disagree):
+    # alpha = 1 gives s_j = (j+1) / sqrt(128 * 1), alpha = 1/2 gives
+    # sqrt(j+1) / 128^(1/4).
+    k = 128
+    j = np.arange(k, dtype=np.float64)
+    x = np.zeros((2, k), np.float32)
+    x[0, :64], x[1, :64] = j[:64] + 1, -(j[:64] + 1)
+    x[0, 64:] = 2 * (j[64:] + 1)
+    w, _ = _awq_case(5, n=16, k=k, t=2)
+    _, _, s1, _, _, _ = oracle.awq_search_reference(w, x, alphas=[1.0])
+    assert np.array_equal(s1, ((j + 1) / np.sqrt(128.0)).astype(np.float32))
+    _, _, s2, _, _, _ = oracle.awq_search_reference(w, x, alphas=[0.5])
+    want = (np.sqrt(j + 1) / 128.0 ** 0.25).astype(np.float32)
+    assert np.all(np.abs(s2.view(np.int32) - want.view(np.int32)) <= 1)
+
+
+def check_awq_power_of_two_invariance():
+    # scaling the activations by 4 scales every magnitude alike: the same
+    # factors and choice, the errors 16 times larger
+    w, x = _awq_case(6, salient=3)
+    e1, b1, s1, q1, _, _ = oracle.awq_search_reference(w, x)
+    e4, b4, s4, q4, _, _ = oracle.awq_search_reference(w, 4.0 * x)
+    assert b1 == b4 and np.allclose(s1, s4, rtol=2e-7, atol=0) and np.allclose(e4, 16.0 * e1, rtol=1e-9)
+
+
 ALL_CHECKS = [
+    check_awq_alpha0_is_round_to_nearest, check_awq_uniform_magnitudes, check_awq_salient_channel,
+    check_awq_scales_closed_form, check_awq_power_of_two_invariance,
     check_llm_int8_special_cases, check_llm_int8_decomposition, check_llm_int8_cap_and_permutation,
     check_llm_int8_accuracy,
     check_e4m3_conversion, check_fp8_listing, check_fp8_product,

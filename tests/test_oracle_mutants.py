@@ -56,6 +56,12 @@ MUTANTS = [
      "if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);"),
     ("f16_scale_zero_kept", "if (s16 == 0.0f) s16 = 1.0f;", ""),
     ("codes_from_f32_scale", "if (scale_f16) s = f16_scale(s);", ""),
+    ("awq_no_normalization", "const double norm = sqrt(mx * mn);", "const double norm = 1.0;"),
+    ("awq_last_minimum", "if (a == 0 || e < err[bi]) {", "if (a == 0 || e <= err[bi]) {"),
+    ("awq_input_not_rescaled", "oq_scale_columns_div(x, s, t, k, xs);", "oq_scale_columns_mul(x, s, t, k, xs);"),
+    ("awq_magnitude_max", "for (int64_t r = 0; r < t; ++r) acc += fabs((double)x[r * k + j]);",
+     "for (int64_t r = 0; r < t; ++r) acc = fmax(acc, fabs((double)x[r * k + j]));"),
+    ("awq_alpha_inverted", "p[j] = pow(mag[j], alphas[a]);", "p[j] = pow(mag[j], 1.0 - alphas[a]);"),
     ("codes3_halves_swapped", "const int pos = 3 * (rr / 2) + 16 * (rr % 2);",
      "const int pos = 3 * (rr / 2) + 16 * ((rr + 1) % 2);"),
     ("codes3_last_pair_words_reversed", "w[t] |= (uint32_t)((e[30] >> t) & 1u) << 15;",
@@ -107,7 +113,7 @@ def test_pins_catch_mutant(mid, old, new, source, tmp_path):
                         "oq_col_absmax", "oq_smooth_factors", "oq_scale_columns_mul", "oq_scale_columns_div",
                         "oq_threads", "oq_quantize_format", "oq_pack_codes3", "oq_f32_to_f16_array",
                         "oq_f16_to_f32_array", "oq_e4m3_array", "oq_e4m3_decode_array", "oq_fp8_quantize",
-                        "oq_fp8_matmul_nt", "oq_llm_int8"]:
+                        "oq_fp8_matmul_nt", "oq_llm_int8", "oq_awq_search"]:
             f = getattr(mutant, fn_name)
             f.argtypes = getattr(good_lib, fn_name).argtypes
             f.restype = ctypes.c_int
