@@ -2,7 +2,7 @@
 """Benchmark of the INT4 / INT8 quantized-matmul hot path on one MI355X.
 
 One step runs every stage of the path once, on synthetic seeded inputs that
-are resident in HBM before timing starts, for all five workloads:
+are resident in HBM before timing starts, for all six workloads:
 
   70B-class MLP, bf16 weights 28672x8192 and 8192x28672 (N(0, 0.015), 0.1% of
   entries x10): quantize_groupwise on both, quantize_groupwise_symmetric on
@@ -21,6 +21,8 @@ are resident in HBM before timing starts, for all five workloads:
   same GEMM); FP8 E4M3 W8A8 on the same shapes: fp8_quantize of the weights,
   fp8_gemm alone and the online fp8_w8a8_gemm; LLM.int8() (llm_int8_gemm,
   outlier threshold 6) on the same shapes;
+  AWQ's scaling search (awq_search) on a bf16 4096x4096 layer with 2048
+  calibration tokens (1% of the channels x4..x58) over the 11-point alpha grid;
   70B-class MLP decode: w4a16_gemv B=8 then B=1 on both matrices (B=1 is the
   headline), then weight-only INT8 (w8a16_gemv) at B=1 and B=8;
   stored-format variants on the 28672x8192 matrix (binary16 scales, groups of
@@ -54,6 +56,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import platform
@@ -439,6 +442,40 @@ def build_ops(dev):
             "i8_gemm_kernel (outlier epilogue)", cfg4l, reads=lambda i: ["xl", "qw_l"], writes=lambda i: ["yl"],
             flops=2 * m4 * n4 * k4, peak=I8_PEAK_TOPS)
 
+    # ---- AWQ's scaling search: one 4096x4096 layer, 2048 calibration tokens
+    # with 1% of the channels scaled x4..x58, the 11-point alpha grid --------
+    wla = workloads.WORKLOADS["awq"]
+    na, ka = wla.weights[0]
+    ta = wla.batches[0]
+    wa = workloads.weight(wla)[0].to(dev)
+    xa = workloads.sq_activations(wla, ta, ka, n_channels=ka // 100, lo=4.0, hi=58.0)[0].to(dev)
+    n_al = len(qmm.AWQ_ALPHAS)
+    alphas_h = (ctypes.c_double * n_al)(*qmm.AWQ_ALPHAS)
+    wsa = torch.empty(qmm.awq_workspace_bytes(na, ka, ta, n_al), dtype=torch.uint8, device=dev)
+    ga = ka // qmm.GROUP
+    ca = torch.empty((na, ka // 2), dtype=torch.uint8, device=dev)
+    sca = torch.empty((na, ga), dtype=torch.float32, device=dev)
+    za = torch.empty((na, (ga + 1) // 2), dtype=torch.uint8, device=dev)
+    sma = torch.empty(ka, dtype=torch.float32, device=dev)
+    era = torch.empty(n_al, dtype=torch.float64, device=dev)
+    ba = torch.empty(1, dtype=torch.int64, device=dev)
+    cfga = f"AWQ scaling search {na}x{ka}, {ta} calibration tokens, {n_al} alphas"
+
+    def awq(i):
+        ok(lib.awq_search(P(wa), qmm.BF16, P(xa), qmm.BF16, na, ka, ta, ctypes.cast(alphas_h, ctypes.c_void_p), n_al,
+                          P(ca), P(sca), P(za), P(sma), P(era), P(ba), P(wsa), wsa.numel(), S(xa)))
+
+    # bytes: what the launches move as designed (per alpha: the weights scaled
+    # to fp32 and quantized, the inputs scaled to bf16, the W4A16 product and
+    # the squared error; once: the magnitudes, X W^T, the final quantization)
+    per_alpha = (2 * na * ka + 4 * na * ka) + (4 * na * ka + na * ka // 2 + na * ga * 4 + na * ga // 2) + \
+        (2 * ta * ka + 2 * ta * ka) + (2 * ta * ka + na * ka // 2 + na * ga * 5 + 4 * ta * na) + 8 * ta * na
+    once = 2 * ta * ka + (2 * ta * ka + 2 * na * ka + 4 * ta * na) + (6 * na * ka + 4 * na * ka + na * ka // 2)
+    ops.add(f"awq_search {na}x{ka} T={ta}", awq, n_al * per_alpha + once, "mfma",
+            "awq_* kernels + i8_gemm_kernel (bf16) + quantize_g128_flat_kernel + w4a16 GEMM", cfga,
+            reads=lambda i: ["wa", "xa"], writes=lambda i: ["ca"], flops=2 * ta * na * ka * (n_al + 1),
+            peak=BF16_PEAK_TFLOPS)
+
     # ---- 70B-class MLP decode: W4A16 B=8 then B=1, then W8A16 --------------
     for m in mats:
         for B in (1, 8):
@@ -679,8 +716,9 @@ def main():
             "workload": "70B-class MLP decode: W4A16 GEMV B=1 on INT4 group-128 28672x8192 and 8192x28672 "
                         "(bf16 activations, fp32 accumulation); the same step also runs their quantizer, "
                         "dequantizer, B=8 GEMV and W8A16 GEMV, the 512x512 fp32 and Llama-7B-like quantize + "
-                        "B=1 GEMV, the 14336x4096 quantize + W4A16 GEMM at M=16/64/256 and the SmoothQuant W8A8 "
-                        "2048x4096x4096 path",
+                        "B=1 GEMV, the 14336x4096 quantize + W4A16 GEMM at M=16/64/256 the SmoothQuant W8A8, FP8 "
+                        "W8A8 and LLM.int8() 2048x4096x4096 paths and AWQ's scaling search on a 4096x4096 layer "
+                        "with 2048 calibration tokens",
             "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
             "quantize_GBps": gbps(["quantize 28672x8192", "quantize 8192x28672"]),
             "quantize_GBps_llama7b": gbps(["quantize 4096x4096", "quantize 11008x4096"]),
@@ -693,6 +731,8 @@ def main():
             "fp8_gemm_TFLOPs": breakdown[[k for k in breakdown if k.startswith("fp8_gemm")][0]].get("TFLOPs"),
             "w8a8_online_TOPS": sq.get("TFLOPs"),
             "llm_int8_TOPS": breakdown[[k for k in breakdown if k.startswith("llm_int8_gemm")][0]].get("TFLOPs"),
+            "awq_search_ms": round(breakdown[[k for k in breakdown if k.startswith("awq_search")][0]]["avg_us"] / 1e3,
+                                   3),
             "weight_copies_rotated_70b": COPIES_70B,
             "min_reuse_MB_hbm_ops": round(min(reuse[o["name"]] for o in ops if o["bound"] == "hbm") / 1e6),
         },

@@ -416,6 +416,42 @@ int llm_int8_gemm(const void* X, int x_dtype, const int8_t* qW, const float* w_s
                   int64_t K, float threshold, int64_t max_outliers, void* Y, int y_dtype, int32_t* n_outliers,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * AWQ -- activation-aware scaling search for INT4 weights ("Quantization
+ * from Scratch", "AWQ: protect the channels that matter", and its awq
+ * listing): channels with large activations get their weights scaled up
+ * before quantization and their inputs down by the same factor,
+ * W x = (W diag(s)) (diag(s)^-1 x).  For each alpha of a grid:
+ *   mag_j = max(mean_t |X[t, j]|, 1e-8)            (fp64)
+ *   s     = mag^alpha / sqrt(max_j mag_j^alpha * min_j mag_j^alpha)
+ *                                                   (fp64, stored in fp32)
+ *   codes = quantize_groupwise(fl32(W diag(s)))    (INT4, groups of 128)
+ *   err   = || X W^T - bf16(fl32(X diag(s)^-1)) W_hat^T ||_F^2 over the T
+ *           calibration tokens, in fp64 (the output error as the quantized
+ *           layer computes it: the inverse scaling folded into its 16-bit
+ *           input; X W^T by a bf16 product with fp32 accumulation);
+ * the first alpha of the smallest error is kept.
+ * W : [N, K] QMM_BF16; X : [T, K] QMM_BF16 calibration activations.
+ * alphas : HOST array of n_alpha (1 .. 64) values in [0, 1] (the listing's
+ *          grid is 0, 0.1, .., 1).
+ * Outputs (device): codes / scales / zeros of W diag(s_best) in the INT4
+ * group-128 format above; smooth [K] = s_best (inference divides X by it,
+ * or folds it into the previous operation); err [n_alpha] fp64; best
+ * (int64, the chosen index).  Nothing is copied back to the host.
+ * Errors, all found before any launch: QMM_EINVAL for a null pointer, a
+ * non-positive size or an alpha outside [0, 1]; QMM_EUNSUPPORTED for fp16 or
+ * fp32 operands, K % 128 != 0 or more than 64 alphas; QMM_ERANGE for
+ * K > 2^22 or N, T >= 2^31; QMM_EALIGN for W, X, codes not 16-byte aligned;
+ * QMM_EWORKSPACE for a workspace smaller than awq_workspace_bytes(N, K, T,
+ * n_alpha) (0 for invalid sizes), QMM_EALIGN for one not 256-byte aligned.
+ * The workspace is the caller's device memory, used only during the call
+ * (stream-ordered); the outputs are written on the stream.
+ * ------------------------------------------------------------------------- */
+size_t awq_workspace_bytes(int64_t N, int64_t K, int64_t T, int64_t n_alpha);
+int awq_search(const void* W, int w_dtype, const void* X, int x_dtype, int64_t N, int64_t K, int64_t T,
+               const double* alphas, int64_t n_alpha, uint8_t* codes, float* scales, uint8_t* zeros, float* smooth,
+               double* err, int64_t* best, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,6 +76,7 @@ def lib(parallel: bool = False) -> ctypes.CDLL:
             "oq_fp8_matmul_nt": [P, P, I64, I64, I64, P],
             "oq_llm_int8": [P, I64, I64, P, P, I64, F, I64, I, P, P, P, P, P],
             "oq_awq_search": [P, P, I64, I64, I64, P, I64, P, P, P, P, P, P],
+            "oq_awq_factors": [P, I64, I64, P, I64, P],
         }
         for name, argtypes in sigs.items():
             fn = getattr(l, name)
@@ -489,15 +490,16 @@ def llm_int8_reference(x, qw, b, threshold: float, max_outliers=None, x_dtype: s
     return idx[:counts[0]].copy(), int(counts[1]), qx, a, y
 
 
-AWQ_ALPHAS = np.linspace(0.0, 1.0, 11)   # the [QS] awq listing's grid
+AWQ_ALPHAS = np.array([i / 10 for i in range(11)])   # the [QS] awq listing's grid 0, 0.1, .., 1
 
 
-def awq_search_reference(w, x, alphas=None):
+def awq_search_reference(w, x, alphas=None, parallel: bool = False):
     """AWQ's scaling search for weights w [N, K] and calibration activations
     x [T, K] (the 16-bit values as float32), INT4 groups of 128 (readings R32,
     R33).  Returns (err fp64 [len(alphas)], best index, s_best f32 [K], the
     codes q uint8 [N, K], scales f32 [N, K/128] and zeros uint8 [N, K/128] of
-    W diag(s_best))."""
+    W diag(s_best)).  parallel=True runs the OpenMP build (the same loops per
+    output, the products' rows split over threads)."""
     w = _f32(w)
     x = _f32(x)
     n, k = w.shape
@@ -510,6 +512,16 @@ def awq_search_reference(w, x, alphas=None):
     q = np.empty((n, k), np.uint8)
     sc = np.empty((n, k // 128), np.float32)
     z = np.empty((n, k // 128), np.uint8)
-    _check(lib().oq_awq_search(_p(w), _p(x), n, k, t, _p(a), a.size, _p(err), _p(best), _p(s), _p(q), _p(sc),
+    _check(lib(parallel).oq_awq_search(_p(w), _p(x), n, k, t, _p(a), a.size, _p(err), _p(best), _p(s), _p(q), _p(sc),
                                _p(z)), "awq_search")
     return err, int(best[0]), s, q, sc, z
+
+
+def awq_factors_reference(x, alphas=None):
+    """AWQ's factors s [len(alphas), K] for calibration activations x [T, K] (R33)."""
+    x = _f32(x)
+    t, k = x.shape
+    a = np.ascontiguousarray(AWQ_ALPHAS if alphas is None else alphas, np.float64).reshape(-1)
+    s = np.empty((a.size, k), np.float32)
+    _check(lib().oq_awq_factors(_p(x), k, t, _p(a), a.size, _p(s)), "awq_factors")
+    return s

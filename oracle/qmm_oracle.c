@@ -652,6 +652,37 @@ int oq_llm_int8(const float* x, int64_t m, int64_t k, const int8_t* qw, const fl
 /* Outputs: err[n_alpha]; *best, the first alpha of the smallest error;      */
 /* s_best[k]; q (unpacked codes), scales, zeros of W diag(s_best).           */
 /* ------------------------------------------------------------------------ */
+/* The factors of every alpha: s_all[a * k + j] (R33). */
+int oq_awq_factors(const float* x, int64_t k, int64_t t, const double* alphas, int64_t n_alpha, float* s_all)
+{
+    if (!x || !alphas || !s_all || k <= 0 || t <= 0 || n_alpha <= 0) return OQ_BAD_ARG;
+    double* mag = malloc((size_t)k * sizeof(double));
+    double* p = malloc((size_t)k * sizeof(double));
+    if (!mag || !p) {
+        free(mag); free(p);
+        return OQ_BAD_ARG;
+    }
+    /* channel magnitudes: mean |x_j| over the tokens */
+    for (int64_t j = 0; j < k; ++j) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < t; ++r) acc += fabs((double)x[r * k + j]);
+        const double m = acc / (double)t;
+        mag[j] = m < 1e-8 ? 1e-8 : m;
+    }
+    for (int64_t a = 0; a < n_alpha; ++a) {
+        double mx = 0.0, mn = INFINITY;
+        for (int64_t j = 0; j < k; ++j) {
+            p[j] = pow(mag[j], alphas[a]);
+            if (p[j] > mx) mx = p[j];
+            if (p[j] < mn) mn = p[j];
+        }
+        const double norm = sqrt(mx * mn);
+        for (int64_t j = 0; j < k; ++j) s_all[a * k + j] = (float)(p[j] / norm);
+    }
+    free(mag); free(p);
+    return OQ_OK;
+}
+
 int oq_awq_search(const float* w, const float* x, int64_t n, int64_t k, int64_t t, const double* alphas,
                   int64_t n_alpha, double* err, int64_t* best, float* s_best, uint8_t* q, float* scales,
                   uint8_t* zeros)
@@ -659,9 +690,7 @@ int oq_awq_search(const float* w, const float* x, int64_t n, int64_t k, int64_t 
     if (!w || !x || !alphas || !err || !best || !s_best || !q || !scales || !zeros) return OQ_BAD_ARG;
     if (n <= 0 || k <= 0 || t <= 0 || n_alpha <= 0 || k % 128 != 0) return OQ_BAD_ARG;
     const int64_t g = k / 128;
-    double* mag = malloc((size_t)k * sizeof(double));
-    double* p = malloc((size_t)k * sizeof(double));
-    float* s = malloc((size_t)k * sizeof(float));
+    float* s_all = malloc((size_t)(n_alpha * k) * sizeof(float));
     float* ws = malloc((size_t)(n * k) * sizeof(float));
     float* what = malloc((size_t)(n * k) * sizeof(float));
     float* xs = malloc((size_t)(t * k) * sizeof(float));
@@ -671,28 +700,15 @@ int oq_awq_search(const float* w, const float* x, int64_t n, int64_t k, int64_t 
     float* sa = malloc((size_t)(n * g) * sizeof(float));
     uint8_t* za = malloc((size_t)(n * g));
     int status = OQ_OK;
-    if (!mag || !p || !s || !ws || !what || !xs || !yref || !yq || !qa || !sa || !za) {
+    if (!s_all || !ws || !what || !xs || !yref || !yq || !qa || !sa || !za) {
         status = OQ_BAD_ARG;
         goto done;
     }
-    /* channel magnitudes: mean |x_j| over the tokens (R33) */
-    for (int64_t j = 0; j < k; ++j) {
-        double acc = 0.0;
-        for (int64_t r = 0; r < t; ++r) acc += fabs((double)x[r * k + j]);
-        const double m = acc / (double)t;
-        mag[j] = m < 1e-8 ? 1e-8 : m;
-    }
+    oq_awq_factors(x, k, t, alphas, n_alpha, s_all);
     oq_matmul_nt_f64(x, w, t, n, k, yref);          /* the full-precision output X W^T */
     int64_t bi = 0;
     for (int64_t a = 0; a < n_alpha; ++a) {
-        double mx = 0.0, mn = INFINITY;
-        for (int64_t j = 0; j < k; ++j) {
-            p[j] = pow(mag[j], alphas[a]);
-            if (p[j] > mx) mx = p[j];
-            if (p[j] < mn) mn = p[j];
-        }
-        const double norm = sqrt(mx * mn);
-        for (int64_t j = 0; j < k; ++j) s[j] = (float)(p[j] / norm);
+        const float* s = s_all + a * k;
         oq_scale_columns_mul(w, s, n, k, ws);       /* W diag(s) */
         oq_asym_quantize(ws, n, k, 128, 4, qa, sa, za);
         oq_asym_dequantize(qa, sa, za, n, k, 128, what);
@@ -715,7 +731,7 @@ int oq_awq_search(const float* w, const float* x, int64_t n, int64_t k, int64_t 
     }
     *best = bi;
 done:
-    free(mag); free(p); free(s); free(ws); free(what); free(xs); free(yref); free(yq);
+    free(s_all); free(ws); free(what); free(xs); free(yref); free(yq);
     free(qa); free(sa); free(za);
     return status;
 }

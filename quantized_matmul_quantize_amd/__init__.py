@@ -25,7 +25,7 @@ __all__ = [
     "sq_smooth_factors", "sq_quantize_weight", "sq_quantize_activation", "sq_quantize_activation_per_tensor",
     "sq_int8_gemm", "sq_workspace_bytes", "smooth_quant_w8a8_gemm", "smooth_quant_w8a8_gemm_noalloc",
     "fp8_quantize", "fp8_gemm", "fp8_w8a8_gemm",
-    "llm_int8_outliers", "llm_int8_workspace_bytes", "llm_int8_gemm",
+    "llm_int8_outliers", "llm_int8_workspace_bytes", "llm_int8_gemm", "awq_workspace_bytes", "awq_search",
 ]
 
 F32, F16, BF16, I32 = 0, 1, 2, 3
@@ -82,6 +82,8 @@ _SIGS = {
     "fp8_w8a8_gemm": ([_P, _I, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
     "llm_int8_outliers": ([_P, _I, _I64, _I64, _F, _I64, _P, _P, _P, _P], _I),
     "llm_int8_workspace_bytes": ([_I64, _I64, _I64, _I64], _SZ),
+    "awq_workspace_bytes": ([_I64, _I64, _I64, _I64], _SZ),
+    "awq_search": ([_P, _I, _P, _I, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "llm_int8_gemm": ([_P, _I, _P, _P, _I64, _I64, _I64, _F, _I64, _P, _I, _P, _P, _SZ, _P], _I),
 }
 
@@ -638,3 +640,51 @@ def llm_int8_gemm(X: torch.Tensor, qW, w_scale, threshold: float = 6.0, max_outl
     _call("llm_int8_gemm", _ptr(X), _dt(X.dtype), _ptr(qW), _ptr(w_scale), M, N, K, float(threshold), cap,
           _ptr(out), _dt(out.dtype), _ptr(n_outliers), _ptr(workspace), workspace.numel(), _stream(X))
     return out
+
+
+# ---------------------------------------------------------------------------
+# AWQ scaling search.
+# ---------------------------------------------------------------------------
+AWQ_ALPHAS = tuple(i / 10 for i in range(11))   # 0, 0.1, .., 1: the grid of the awq listing in "Quantization from Scratch"
+
+
+def awq_workspace_bytes(N: int, K: int, T: int, n_alpha: int) -> int:
+    return int(lib().awq_workspace_bytes(N, K, T, n_alpha))
+
+
+def awq_search(W: torch.Tensor, X: torch.Tensor, alphas: Sequence[float] = AWQ_ALPHAS,
+               workspace: Optional[torch.Tensor] = None):
+    """AWQ on bf16 weights W [N, K] with bf16 calibration activations X [T, K]:
+    returns (codes, scales, zeros) of W diag(s_best) in the INT4 group-128
+    format, smooth [K] (= s_best), err fp64 [len(alphas)] and best (int64
+    [1]), all on the device."""
+    _req(W, "W", (torch.bfloat16,), ndim=2)
+    N, K = W.shape
+    _req(X, "X", (torch.bfloat16,), shape=(None, K))
+    T = X.shape[0]
+    a = [float(v) for v in alphas]
+    if not 1 <= len(a) <= 64:
+        raise ValueError(f"takes 1 to 64 alphas, not {len(a)}")
+    if not all(0.0 <= v <= 1.0 for v in a):
+        raise ValueError(f"alphas must lie in [0, 1]: {a}")
+    if K % GROUP != 0:
+        raise ValueError(f"K={K} is not a multiple of {GROUP}")
+    need = awq_workspace_bytes(N, K, T, len(a))
+    if workspace is not None:
+        _req(workspace, "workspace", (torch.uint8,), ndim=1)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes; {need} needed")
+    dev = _place(W=W, X=X, workspace=workspace)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // GROUP), dtype=torch.float32, device=dev)
+    zeros = torch.empty((N, (K // GROUP + 1) // 2), dtype=torch.uint8, device=dev)
+    smooth = torch.empty(K, dtype=torch.float32, device=dev)
+    err = torch.empty(len(a), dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int64, device=dev)
+    host_alphas = (ctypes.c_double * len(a))(*a)
+    _call("awq_search", _ptr(W), _dt(W.dtype), _ptr(X), _dt(X.dtype), N, K, T, ctypes.cast(host_alphas, ctypes.c_void_p),
+          len(a), _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(smooth), _ptr(err), _ptr(best), _ptr(workspace),
+          workspace.numel(), _stream(X))
+    return codes, scales, zeros, smooth, err, best

@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libqmm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "quantize.hip", "w4a16.hip", "w8a8.hip", "w8a16.hip", "formats.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "w4a16.hip", "w8a8.hip", "w8a16.hip", "formats.hip", "awq.hip"]
 
 # Per-source extra flags.  The MFMA kernels keep their accumulators in
 # ordinary VGPRs: with the default accumulator-register form the register

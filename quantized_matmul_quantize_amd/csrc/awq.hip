@@ -1,0 +1,298 @@
+// awq.hip -- AWQ's activation-aware scaling search on the GPU.
+//
+// Source: "Quantization from Scratch: Scale, Zero-Point, GPTQ and AWQ", "AWQ:
+// protect the channels that matter" and the awq listing after it: a few input
+// channels carry much larger activations, so the weights they multiply are
+// scaled up before quantization and the inputs down by the same factor,
+// W x = (W diag(s)) (diag(s)^-1 x); s_j = mean|x_j|^alpha, normalized by
+// sqrt(max s * min s), with one alpha per layer kept from a grid by the
+// calibration output error.
+//
+// For every alpha of the grid (the loop runs on the host, the choice on the
+// device, so nothing waits for the host):
+//   s      = mag^alpha / sqrt(max * min), fp64, stored in fp32;
+//   W_s    = fl32(W diag(s)) -> quantize_groupwise (INT4, groups of 128);
+//   X_s    = bf16(fl32(X / s))  (the inverse scaling folded into the input);
+//   Y_q    = w4a16_gemm(X_s, codes of W_s);
+//   err    = sum (X W^T - Y_q)^2 in fp64, X W^T once by the bf16 product;
+// then the first alpha of the smallest error is selected, and W diag(s_best)
+// quantized into the caller's format buffers.  mag_j = max(mean_t |x_j|,
+// 1e-8) in fp64 (exact sums for activations of ordinary range, so the order
+// of the partial sums does not change it).
+
+#include "qmm_device.h"
+
+namespace qmm {
+namespace {
+
+constexpr int kMagRows = 64;       // rows per partial sum of the channel magnitudes
+constexpr int kErrBlocks = 1024;   // partial sums of one squared error
+constexpr int kMaxAlphas = 64;
+
+__device__ __forceinline__ float x16_to_f32(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+
+// The alpha grid, passed by value (a kernel argument of 512 bytes).
+struct AlphaGrid {
+  double a[kMaxAlphas];
+};
+
+// Partial sums of |x| over rows [kMagRows b, +kMagRows) of each column, fp64.
+__global__ __launch_bounds__(256) void awq_mag_partial_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t K,
+                                                              double* __restrict__ part) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j >= K) return;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kMagRows;
+  const int64_t r1 = (r0 + kMagRows < T) ? r0 + kMagRows : T;
+  double acc = 0.0;
+  for (int64_t r = r0; r < r1; r += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (r + u < r1) ? fabsf(x16_to_f32(x[(r + u) * K + j])) : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += static_cast<double>(v[u]);
+  }
+  part[blockIdx.y * K + j] = acc;
+}
+
+// One block per alpha: mag_j from the partial sums (in order), p_j = mag_j^alpha,
+// s_j = fl32(p_j / sqrt(max p * min p)).
+__global__ __launch_bounds__(256) void awq_scales_kernel(const double* __restrict__ part, int64_t slices, int64_t T,
+                                                         int64_t K, AlphaGrid alphas, float* __restrict__ s_all,
+                                                         double* __restrict__ pbuf) {
+  __shared__ double smax[256], smin[256];
+  const double alpha = alphas.a[blockIdx.x];
+  double* p = pbuf + blockIdx.x * K;
+  double mx = 0.0, mn = INFINITY;
+  for (int64_t j = threadIdx.x; j < K; j += blockDim.x) {
+    double acc = 0.0;
+    for (int64_t b = 0; b < slices; ++b) acc += part[b * K + j];
+    double m = acc / static_cast<double>(T);
+    m = m < 1e-8 ? 1e-8 : m;
+    const double pj = pow(m, alpha);
+    p[j] = pj;
+    mx = fmax(mx, pj);
+    mn = fmin(mn, pj);
+  }
+  smax[threadIdx.x] = mx;
+  smin[threadIdx.x] = mn;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {   // max and min are exact in any order
+    if (static_cast<int>(threadIdx.x) < o) {
+      smax[threadIdx.x] = fmax(smax[threadIdx.x], smax[threadIdx.x + o]);
+      smin[threadIdx.x] = fmin(smin[threadIdx.x], smin[threadIdx.x + o]);
+    }
+    __syncthreads();
+  }
+  const double norm = sqrt(smax[0] * smin[0]);
+  float* s = s_all + blockIdx.x * K;
+  for (int64_t j = threadIdx.x; j < K; j += blockDim.x) s[j] = static_cast<float>(p[j] / norm);
+}
+
+// W_s = fl32(W diag(s)) (fp32 out), eight weights per thread.
+__global__ __launch_bounds__(256) void awq_scale_w_kernel(const uint16_t* __restrict__ w, const float* __restrict__ s,
+                                                          int64_t total8, int64_t K, float* __restrict__ out) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total8;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t e = i * 8;
+    const int64_t j = e % K;
+    const u32x4 v = ld16(w + e);
+    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+    float o[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      o[2 * h] = bf16lo_to_f32(a[h]) * s[j + 2 * h];
+      o[2 * h + 1] = bf16hi_to_f32(a[h]) * s[j + 2 * h + 1];
+    }
+    *reinterpret_cast<f32x4*>(out + e) = f32x4{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<f32x4*>(out + e + 4) = f32x4{o[4], o[5], o[6], o[7]};
+  }
+}
+
+// X_s = bf16(fl32(X / s)), correctly rounded division, eight values per thread.
+__global__ __launch_bounds__(256) void awq_scale_x_kernel(const uint16_t* __restrict__ x, const float* __restrict__ s,
+                                                          int64_t total8, int64_t K, uint16_t* __restrict__ out) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total8;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t e = i * 8;
+    const int64_t j = e % K;
+    const u32x4 v = ld16(x + e);
+    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float lo = bf16lo_to_f32(a[h]) / s[j + 2 * h];
+      const float hi = bf16hi_to_f32(a[h]) / s[j + 2 * h + 1];
+      o[h] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    }
+    *reinterpret_cast<u32x4*>(out + e) = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
+// Partial sums of (a - b)^2 in fp64: block b takes a fixed contiguous range,
+// each thread a fixed stride within it, and the block tree is fixed, so the
+// result does not depend on scheduling.
+__global__ __launch_bounds__(256) void awq_sqerr_kernel(const float* __restrict__ a, const float* __restrict__ b,
+                                                        int64_t n, double* __restrict__ part) {
+  __shared__ double red[256];
+  const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t i1 = (i0 + per < n) ? i0 + per : n;
+  double acc = 0.0;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += blockDim.x) {
+    const double d = static_cast<double>(a[i]) - static_cast<double>(b[i]);
+    acc += d * d;
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (static_cast<int>(threadIdx.x) < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// err[a] = the partial sums in order; best = the first alpha of the smallest
+// error; s_best = its factors.
+__global__ __launch_bounds__(256) void awq_select_kernel(const double* __restrict__ part, int n_alpha,
+                                                         const float* __restrict__ s_all, int64_t K,
+                                                         double* __restrict__ err, int64_t* __restrict__ best,
+                                                         float* __restrict__ s_best) {
+  __shared__ double e_s[kMaxAlphas];
+  __shared__ int b_s;
+  if (static_cast<int>(threadIdx.x) < n_alpha) {
+    double e = 0.0;
+    for (int b = 0; b < kErrBlocks; ++b) e += part[threadIdx.x * kErrBlocks + b];
+    e_s[threadIdx.x] = e;
+    err[threadIdx.x] = e;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int bi = 0;
+    for (int a = 1; a < n_alpha; ++a)
+      if (e_s[a] < e_s[bi]) bi = a;
+    b_s = bi;
+    *best = bi;
+  }
+  __syncthreads();
+  for (int64_t j = threadIdx.x; j < K; j += blockDim.x) s_best[j] = s_all[b_s * K + j];
+}
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Workspace regions, in order.
+struct AwqLayout {
+  size_t mag, pbuf, s_all, ws, xs, codes, scales, zeros, yref, yq, err, total;
+};
+
+AwqLayout awq_layout(int64_t N, int64_t K, int64_t T, int64_t n_alpha) {
+  AwqLayout l;
+  const int64_t G = K / kGroup;
+  size_t o = 0;
+  l.mag = o; o += align256(static_cast<size_t>(ceil_div(T, kMagRows) * K) * sizeof(double));
+  l.pbuf = o; o += align256(static_cast<size_t>(n_alpha * K) * sizeof(double));
+  l.s_all = o; o += align256(static_cast<size_t>(n_alpha * K) * sizeof(float));
+  l.ws = o; o += align256(static_cast<size_t>(N * K) * sizeof(float));
+  l.xs = o; o += align256(static_cast<size_t>(T * K) * 2);
+  l.codes = o; o += align256(static_cast<size_t>(N * K / 2));
+  l.scales = o; o += align256(static_cast<size_t>(N * G) * sizeof(float));
+  l.zeros = o; o += align256(static_cast<size_t>(N * ((G + 1) / 2)));
+  l.yref = o; o += align256(static_cast<size_t>(T * N) * sizeof(float));
+  l.yq = o; o += align256(static_cast<size_t>(T * N) * sizeof(float));
+  l.err = o; o += align256(static_cast<size_t>(n_alpha * kErrBlocks) * sizeof(double));
+  l.total = o;
+  return l;
+}
+
+unsigned grid_for(int64_t items) {
+  const int64_t blocks = ceil_div(items, 256);
+  const int64_t cap = static_cast<int64_t>(device_cus()) * 8;
+  return static_cast<unsigned>(blocks < cap ? blocks : cap);
+}
+
+}  // namespace
+}  // namespace qmm
+
+using namespace qmm;
+
+extern "C" size_t awq_workspace_bytes(int64_t N, int64_t K, int64_t T, int64_t n_alpha) {
+  if (N <= 0 || K <= 0 || T <= 0 || n_alpha <= 0 || n_alpha > kMaxAlphas || K % kGroup != 0) return 0;
+  return awq_layout(N, K, T, n_alpha).total;
+}
+
+extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype, int64_t N, int64_t K, int64_t T,
+                          const double* alphas, int64_t n_alpha, uint8_t* codes, float* scales, uint8_t* zeros,
+                          float* smooth, double* err, int64_t* best, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!W || !X || !alphas || !codes || !scales || !zeros || !smooth || !err || !best) return QMM_EINVAL;
+  if (N <= 0 || K <= 0 || T <= 0 || n_alpha <= 0) return QMM_EINVAL;
+  if (K % kGroup != 0) return QMM_EUNSUPPORTED;
+  if (w_dtype != QMM_BF16 || x_dtype != QMM_BF16)
+    return (w_dtype == QMM_F16 || w_dtype == QMM_F32 || x_dtype == QMM_F16 || x_dtype == QMM_F32) ? QMM_EUNSUPPORTED
+                                                                                                  : QMM_EINVAL;
+  if (n_alpha > kMaxAlphas) return QMM_EUNSUPPORTED;
+  for (int64_t a = 0; a < n_alpha; ++a)
+    if (!(alphas[a] >= 0.0 && alphas[a] <= 1.0)) return QMM_EINVAL;
+  // the bf16 product's 32-bit offsets (256 rows of 2K bytes) and the W4A16 product's
+  if (K > (int64_t(1) << 22) || N > INT32_MAX || T > INT32_MAX) return QMM_ERANGE;
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(smooth, 4) ||
+      !aligned(err, 8) || !aligned(best, 8))
+    return QMM_EALIGN;
+  if (!workspace || workspace_bytes < awq_layout(N, K, T, n_alpha).total) return QMM_EWORKSPACE;
+  if (!aligned(workspace, 256)) return QMM_EALIGN;
+  const AwqLayout L = awq_layout(N, K, T, n_alpha);
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  double* mag = reinterpret_cast<double*>(base + L.mag);
+  double* pbuf = reinterpret_cast<double*>(base + L.pbuf);
+  float* s_all = reinterpret_cast<float*>(base + L.s_all);
+  float* ws = reinterpret_cast<float*>(base + L.ws);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(base + L.xs);
+  uint8_t* qc = base + L.codes;
+  float* qs = reinterpret_cast<float*>(base + L.scales);
+  uint8_t* qz = base + L.zeros;
+  float* yref = reinterpret_cast<float*>(base + L.yref);
+  float* yq = reinterpret_cast<float*>(base + L.yq);
+  double* epart = reinterpret_cast<double*>(base + L.err);
+  hipStream_t s = as_stream(stream);
+  const uint16_t* w = static_cast<const uint16_t*>(W);
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+
+  // channel magnitudes and every alpha's factors
+  const int64_t slices = ceil_div(T, kMagRows);
+  awq_mag_partial_kernel<<<dim3(static_cast<unsigned>(ceil_div(K, 256)), static_cast<unsigned>(slices)), 256, 0, s>>>(
+      x, T, K, mag);
+  AlphaGrid grid{};
+  for (int64_t a = 0; a < n_alpha; ++a) grid.a[a] = alphas[a];
+  awq_scales_kernel<<<static_cast<unsigned>(n_alpha), 256, 0, s>>>(mag, slices, T, K, grid, s_all, pbuf);
+  int st = launch_status();
+  if (st != QMM_OK) return st;
+  // the full-precision output X W^T
+  launch_bf16_gemm(x, w, T, N, K, yref, s);
+  st = launch_status();
+  if (st != QMM_OK) return st;
+
+  const int64_t wn8 = N * K / 8, xn8 = T * K / 8;
+  for (int64_t a = 0; a < n_alpha; ++a) {
+    const float* sa = s_all + a * K;
+    awq_scale_w_kernel<<<grid_for(wn8), 256, 0, s>>>(w, sa, wn8, K, ws);
+    st = launch_status();
+    if (st != QMM_OK) return st;
+    st = quantize_groupwise(ws, QMM_F32, N, K, kGroup, 4, qc, qs, qz, stream);
+    if (st != QMM_OK) return st;
+    awq_scale_x_kernel<<<grid_for(xn8), 256, 0, s>>>(x, sa, xn8, K, xs);
+    st = launch_status();
+    if (st != QMM_OK) return st;
+    st = w4a16_gemm(qc, qs, qz, N, K, kGroup, xs, QMM_BF16, T, yq, QMM_F32, stream);
+    if (st != QMM_OK) return st;
+    awq_sqerr_kernel<<<kErrBlocks, 256, 0, s>>>(yref, yq, T * N, epart + a * kErrBlocks);
+    st = launch_status();
+    if (st != QMM_OK) return st;
+  }
+  awq_select_kernel<<<1, 256, 0, s>>>(epart, static_cast<int>(n_alpha), s_all, K, err, best, smooth);
+  st = launch_status();
+  if (st != QMM_OK) return st;
+  // the chosen alpha's weights in the caller's format
+  awq_scale_w_kernel<<<grid_for(wn8), 256, 0, s>>>(w, smooth, wn8, K, ws);
+  st = launch_status();
+  if (st != QMM_OK) return st;
+  return quantize_groupwise(ws, QMM_F32, N, K, kGroup, 4, codes, scales, zeros, stream);
+}

@@ -28,4 +28,10 @@ int dequantize_fmt(const uint8_t* codes, const void* scales, const uint8_t* zero
 int matmul_fmt(const uint8_t* codes, const void* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
                int bits, int scale_dtype, const void* x, int x_dtype, int64_t M, void* y, int y_dtype, void* stream);
 
+// Plain product Y[M, N] = A[M, K] B[N, K]^T of bf16 operands in fp32
+// (w8a8.hip, the INT8 GEMM's tiles on bf16 matrix instructions).  K % 32 == 0,
+// rows 16-byte aligned, 256 * 2K < 2^31.
+void launch_bf16_gemm(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K, float* Y,
+                      hipStream_t s);
+
 }  // namespace qmm

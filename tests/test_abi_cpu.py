@@ -212,3 +212,37 @@ def test_binding_raises_qmm_error():
         qmm._call("sq_int8_gemm", P, P, P, P, 4, 4, 131136, P, BF16, None)
     assert e.value.status == ERANGE
     assert "QMM_ERANGE" in str(e.value)
+
+
+def test_awq_workspace_and_argument_errors():
+    lib = qmm.lib()
+    ws = lib.awq_workspace_bytes
+    a256 = lambda b: (b + 255) // 256 * 256
+    # magnitude partial sums, every alpha's fp64 powers and fp32 factors, the
+    # scaled fp32 weights, the scaled bf16 inputs, one INT4 format, both fp32
+    # products, the squared-error partial sums
+    n, k, t, na = 4096, 4096, 2048, 11
+    want = (a256(32 * k * 8) + a256(na * k * 8) + a256(na * k * 4) + a256(n * k * 4) + a256(t * k * 2) +
+            a256(n * k // 2) + a256(n * 32 * 4) + a256(n * 16) + 2 * a256(t * n * 4) + a256(na * 1024 * 8))
+    assert ws(n, k, t, na) == want
+    assert ws(0, 128, 4, 1) == 0 and ws(4, 100, 4, 1) == 0 and ws(4, 128, 4, 65) == 0 and ws(4, 128, 4, 0) == 0
+    g = lib.awq_search
+    need = ws(4, 128, 4, 2)
+    al = (ctypes.c_double * 2)(0.0, 1.0)
+    bad = (ctypes.c_double * 2)(0.0, 1.5)
+    args = lambda **k: [k.get("W", P), k.get("wdt", BF16), P, k.get("xdt", BF16), 4, k.get("K", 128), 4,
+                        k.get("al", ctypes.cast(al, ctypes.c_void_p)), k.get("na", 2), P, P, P, P, P, P,
+                        k.get("ws", P), k.get("wsb", need), None]
+    assert g(*args(W=None)) == EINVAL
+    assert g(*args(wdt=F16)) == EUNSUP
+    assert g(*args(xdt=F32)) == EUNSUP
+    assert g(*args(wdt=I32)) == EINVAL
+    assert g(*args(K=100)) == EUNSUP
+    assert g(*args(na=65)) == EUNSUP
+    assert g(*args(na=0)) == EINVAL
+    assert g(*args(al=ctypes.cast(bad, ctypes.c_void_p))) == EINVAL
+    assert g(*args(K=(1 << 22) + 128, wsb=10**15)) == ERANGE
+    assert g(*args(W=MIS)) == EALIGN
+    assert g(*args(ws=None)) == EWS
+    assert g(*args(wsb=need - 1)) == EWS
+    assert g(*args(ws=MIS)) == EALIGN

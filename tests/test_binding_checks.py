@@ -86,3 +86,16 @@ def test_llm_int8_checks():
     raises(lambda: qmm.llm_int8_gemm(x, t((8, 256), i8), t((8,), f32), workspace=t((16,), u8)), "workspace holds")
     raises(lambda: qmm.llm_int8_gemm(x, t((8, 256), i8), t((8,), f32)), "device tensor")
     raises(lambda: qmm.llm_int8_outliers(t((4, 256), f16), threshold=-0.5), "threshold")
+
+
+def test_awq_checks():
+    w, x = t((8, 256), bf16), t((4, 256), bf16)
+    raises(lambda: qmm.awq_search(t((8, 256), f16), x), "W has dtype")
+    raises(lambda: qmm.awq_search(w, t((4, 128), bf16)), "X has shape")
+    raises(lambda: qmm.awq_search(t((8, 200), bf16), t((4, 200), bf16)), "multiple of 128")
+    raises(lambda: qmm.awq_search(w, x, alphas=[]), "1 to 64 alphas")
+    raises(lambda: qmm.awq_search(w, x, alphas=[0.1] * 65), "1 to 64 alphas")
+    raises(lambda: qmm.awq_search(w, x, alphas=[0.5, 1.5]), r"\[0, 1\]")
+    raises(lambda: qmm.awq_search(w, x, alphas=[float("nan")]), r"\[0, 1\]")
+    raises(lambda: qmm.awq_search(w, x, workspace=t((16,), u8)), "workspace holds")
+    raises(lambda: qmm.awq_search(w, x), "device tensor")

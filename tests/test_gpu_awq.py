@@ -1,0 +1,170 @@
+"""GPU parity for AWQ's scaling search ("Quantization from Scratch", "AWQ:
+protect the channels that matter"): the chosen factors and the INT4 codes,
+scales and zero-points of W diag(s) bit for bit against the CPU oracle, every
+alpha's calibration output error within the tolerance of its fp32-accumulated
+products, and the chosen alpha the oracle's (or one whose oracle error ties
+it within that tolerance).  Small ragged shapes, a salient channel, uniform
+magnitudes (every alpha the same, so the first is kept), one alpha (plain
+round-to-nearest), one calibration token, a reversed grid, and the
+4096 x 4096 layer with 2048 calibration tokens."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_matmul_quantize_amd as qmm
+import workloads
+from gpu_util import bits_equal, first_diff, note, stratified_rows
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+# err = sum_i (yref_i - yq_i)^2 over the T x N outputs, both products
+# accumulated in fp32 on the GPU and in fp64 by the oracle.  Each GPU output
+# carries an error delta_i of about sqrt(K) 2^-24 sum_k |x_k w_k| (a random
+# walk of K roundings; both products: twice that, with a margin for the
+# scaled and quantized operands), so err moves by 2 sum_i d_i delta_i +
+# sum_i delta_i^2, d_i = yref_i - yq_i.  With the errors independent of d, the
+# first sum stays within LAMBDA standard deviations, sqrt(err) * rms(delta).
+# At the 4096-wide layer that is ~1e-5 of err; a single output (one token, one
+# row) whose d cancels to almost nothing relies on it entirely.
+LAMBDA = 6.0
+U32 = 2.0 ** -24
+
+
+def _err_tol(w, x, err_ref, rows=None):
+    """Per-alpha tolerance on err (see above); rows: weight rows to estimate
+    rms(sum_k |x_k w_k|) from (default all)."""
+    wf = np.abs(w.float().numpy().astype(np.float64))
+    if rows is not None:
+        wf = wf[rows]
+    xf = np.abs(x.float().numpy().astype(np.float64))
+    k = xf.shape[1]
+    beta = 2.5 * np.sqrt(k) * U32 * float(np.sqrt(np.mean((xf @ wf.T) ** 2)))
+    outputs = x.shape[0] * w.shape[0]
+    return 2 * LAMBDA * np.sqrt(np.asarray(err_ref)) * beta + outputs * beta ** 2 + 1e-12 * np.asarray(err_ref)
+
+
+def _check_err(err, err_ref, w, x, what, rows=None):
+    tol = _err_tol(w, x, err_ref, rows)
+    bad = np.abs(err - err_ref) > tol
+    assert not bad.any(), f"{what} err: got {err[bad]} want {np.asarray(err_ref)[bad]} tolerance {tol[bad]}"
+    return tol
+
+
+def _case(n, k, t, seed, salient=(), spread=None, dtype="bf16"):
+    g = np.random.Generator(np.random.PCG64(seed))
+    w = workloads.to_dtype(workloads.gaussian(g, (n, k), 0.02), dtype)
+    x = workloads.gaussian(g, (t, k), 1.0)
+    for c in salient:
+        x[:, c] *= np.float32(50.0)
+    if spread is not None:
+        workloads.plant_scale_columns(x, g, max(1, k // 100), *spread)
+    return w, workloads.to_dtype(x, dtype)
+
+
+def _run(w, x, alphas, what):
+    note(f"awq_search {what} W={tuple(w.shape)} X={tuple(x.shape)} alphas={len(alphas)}")
+    codes, scales, zeros, smooth, err, best = qmm.awq_search(w.to(DEV), x.to(DEV), alphas)
+    torch.cuda.synchronize()
+    return (codes.cpu().numpy(), scales.cpu().numpy(), zeros.cpu().numpy(), smooth.cpu().numpy(),
+            err.cpu().numpy(), int(best.cpu().item()))
+
+
+def _check_format(w, smooth, codes, scales, zeros, what, rows=None):
+    """codes / scales / zeros == the oracle's group-128 INT4 of fl32(W diag(smooth))."""
+    wf = w.float().numpy()
+    if rows is not None:
+        wf, codes, scales, zeros = wf[rows], codes[rows], scales[rows], zeros[rows]
+    rc, rs, rz = oracle.quantize_groupwise_packed(oracle.scale_columns_mul(wf, smooth))
+    assert bits_equal(scales, rs), f"{what} scales: {first_diff(scales, rs)}"
+    assert bits_equal(zeros, rz), f"{what} zeros: {first_diff(zeros, rz)}"
+    assert bits_equal(codes, rc), f"{what} codes: {first_diff(codes, rc)}"
+
+
+def _check(w, x, alphas, what):
+    codes, scales, zeros, smooth, err, best = _run(w, x, alphas, what)
+    xf = x.float().numpy()
+    rerr, rbest, rs, _, _, _ = oracle.awq_search_reference(w.float().numpy(), xf, alphas)
+    assert best == int(np.argmin(err)), f"{what}: best {best} is not the first minimum of {err}"
+    tol = _check_err(err, rerr, w, x, what)
+    if best != rbest:   # a near tie: the GPU's choice must be as good within the tolerance
+        assert rerr[best] <= rerr[rbest] + tol[best] + tol[rbest], (what, best, rbest, rerr)
+    s_all = oracle.awq_factors_reference(xf, alphas)
+    assert bits_equal(smooth, s_all[best]), f"{what} smooth: {first_diff(smooth, s_all[best])}"
+    if best == rbest:
+        assert bits_equal(smooth, rs)
+    _check_format(w, smooth, codes, scales, zeros, what)
+    return err, best
+
+
+@pytest.mark.parametrize("n,k,t,seed", [(48, 256, 40, 1), (200, 640, 100, 2), (129, 1152, 67, 3), (1, 128, 1, 4)])
+def test_awq_ragged_shapes(n, k, t, seed):
+    w, x = _case(n, k, t, seed, spread=(4.0, 58.0))
+    _check(w, x, list(qmm.AWQ_ALPHAS), f"ragged n={n} k={k} t={t}")
+
+
+def test_awq_salient_channel():
+    w, x = _case(96, 384, 64, 5, salient=(17,))
+    err, best = _check(w, x, list(qmm.AWQ_ALPHAS), "salient channel 17")
+    assert best > 0 and err[best] < err[0]
+
+
+def test_awq_uniform_magnitudes_keeps_first_alpha():
+    # every channel with mean |x| = 0.75: s = 1 for every alpha, so every
+    # alpha computes the same thing and the first is kept
+    w, _ = _case(64, 256, 32, 6)
+    signs = np.where(np.random.Generator(np.random.PCG64(7)).random((32, 256)) < 0.5, -1.0, 1.0)
+    x = workloads.to_dtype((signs * 0.75).astype(np.float32), "bf16")
+    codes, scales, zeros, smooth, err, best = _run(w, x, list(qmm.AWQ_ALPHAS), "uniform magnitudes")
+    assert best == 0 and np.all(err == err[0]) and np.all(smooth == 1.0)
+    rerr, _, _, _, _, _ = oracle.awq_search_reference(w.float().numpy(), x.float().numpy())
+    _check_err(err, rerr, w, x, "uniform magnitudes")
+    _check_format(w, smooth, codes, scales, zeros, "uniform magnitudes")
+
+
+def test_awq_single_alpha_zero_is_round_to_nearest():
+    # alpha = 0: s = 1, the codes are the plain group-128 quantizer's
+    w, x = _case(80, 512, 24, 8, spread=(4.0, 58.0))
+    codes, scales, zeros, smooth, err, best = _run(w, x, [0.0], "alpha 0 only")
+    assert best == 0 and np.all(smooth == 1.0)
+    c0, s0, z0 = qmm.quantize_groupwise(w.to(DEV))
+    assert bits_equal(codes, c0.cpu().numpy()) and bits_equal(scales, s0.cpu().numpy())
+    assert bits_equal(zeros, z0.cpu().numpy())
+    rerr, _, _, _, _, _ = oracle.awq_search_reference(w.float().numpy(), x.float().numpy(), [0.0])
+    _check_err(err, rerr, w, x, "alpha 0 only")
+
+
+def test_awq_reversed_grid():
+    # the grid's order is the caller's: reversed, the same alpha is found at
+    # the mirrored index (unless two alphas tie)
+    w, x = _case(64, 256, 48, 9, salient=(3, 200))
+    grid = list(qmm.AWQ_ALPHAS)
+    err_f, best_f = _check(w, x, grid, "forward grid")
+    err_r, best_r = _check(w, x, grid[::-1], "reversed grid")
+    assert bits_equal(err_r[::-1].copy(), err_f)
+    assert best_r == len(grid) - 1 - best_f or err_f[best_f] == err_f[len(grid) - 1 - best_r]
+
+
+def test_awq_layer_4096():
+    # the 4096 x 4096 layer with 2048 calibration tokens, 1% of the channels
+    # scaled 4x..58x: the factors bit for bit, the whole format bit for bit,
+    # and the oracle's error of the chosen alpha and of its neighbours on the
+    # grid (the oracle's fp64 products over every alpha would take minutes)
+    wl = workloads.WORKLOADS["awq"]
+    n, k = wl.weights[0]
+    t = wl.batches[0]
+    w, _ = workloads.weight(wl)
+    x, _ = workloads.sq_activations(wl, t, k, n_channels=k // 100, lo=4.0, hi=58.0)
+    grid = list(qmm.AWQ_ALPHAS)
+    codes, scales, zeros, smooth, err, best = _run(w, x, grid, "layer 4096x4096, 2048 tokens")
+    assert best == int(np.argmin(err))
+    xf = x.float().numpy()
+    s_all = oracle.awq_factors_reference(xf, grid)
+    assert bits_equal(smooth, s_all[best]), f"smooth: {first_diff(smooth, s_all[best])}"
+    _check_format(w, smooth, codes, scales, zeros, "layer 4096")
+    near = [i for i in (best - 1, best, best + 1) if 0 <= i < len(grid)]
+    rerr, rbest, _, _, _, _ = oracle.awq_search_reference(w.float().numpy(), xf, [grid[i] for i in near],
+                                                          parallel=True)
+    tol = _check_err(err[near], rerr, w, x, "err near the chosen alpha", rows=stratified_rows(n, 64))
+    assert rerr[near.index(best)] <= rerr.min() + 2 * tol.max(), (near, rerr)

@@ -113,7 +113,7 @@ def test_pins_catch_mutant(mid, old, new, source, tmp_path):
                         "oq_col_absmax", "oq_smooth_factors", "oq_scale_columns_mul", "oq_scale_columns_div",
                         "oq_threads", "oq_quantize_format", "oq_pack_codes3", "oq_f32_to_f16_array",
                         "oq_f16_to_f32_array", "oq_e4m3_array", "oq_e4m3_decode_array", "oq_fp8_quantize",
-                        "oq_fp8_matmul_nt", "oq_llm_int8", "oq_awq_search"]:
+                        "oq_fp8_matmul_nt", "oq_llm_int8", "oq_awq_search", "oq_awq_factors"]:
             f = getattr(mutant, fn_name)
             f.argtypes = getattr(good_lib, fn_name).argtypes
             f.restype = ctypes.c_int

@@ -96,7 +96,7 @@ class Workload:
     note: str
 
 
-# The five workloads (sizes, dtypes and distributions as stated for each).
+# The six workloads (sizes, dtypes and distributions as stated for each).
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload(1, "single 512x512 fp32 weight with 4 planted +-0.5 outliers; fp16 GEMV x[1,512]",
                      ((512, 512),), "f32", 0.02, "f16", (1,), "replace4", ""),
@@ -106,6 +106,8 @@ WORKLOADS: Dict[str, Workload] = {
                      ((14336, 4096),), "bf16", 0.02, "bf16", (16, 64, 256), "none", ""),
     "smoothquant": Workload(4, "SmoothQuant W8A8: X 2048x4096 bf16 with 6 outlier channels x50..100, W 4096x4096",
                             ((4096, 4096),), "bf16", 0.02, "bf16", (2048,), "none", ""),
+    "awq": Workload(6, "AWQ scaling search: bf16 W 4096x4096; calibration X 2048x4096 bf16, 1% of the channels x4..x58",
+                    ((4096, 4096),), "bf16", 0.02, "bf16", (2048,), "none", ""),
     "mlp70b": Workload(5, "70B-class MLP decode: bf16 28672x8192 and 8192x28672, 0.1% entries x10; GEMV B=1 and B=8",
                        ((28672, 8192), (8192, 28672)), "bf16", 0.015, "bf16", (1, 8), "scale0.1%", ""),
 }
