@@ -422,7 +422,9 @@ int llm_int8_gemm(const void* X, int x_dtype, const int8_t* qW, const float* w_s
  * listing): channels with large activations get their weights scaled up
  * before quantization and their inputs down by the same factor,
  * W x = (W diag(s)) (diag(s)^-1 x).  For each alpha of a grid:
- *   mag_j = max(mean_t |X[t, j]|, 1e-8)            (fp64)
+ *   mag_j = max(mean_t |X[t, j]|, 1e-8)            (fp64; its sum over the
+ *           tokens is exact, so the same in any order, while a channel's
+ *           nonzero |x| span less than 2^(45 - log2 T) in ratio)
  *   s     = mag^alpha / sqrt(max_j mag_j^alpha * min_j mag_j^alpha)
  *                                                   (fp64, stored in fp32)
  *   codes = quantize_groupwise(fl32(W diag(s)))    (INT4, groups of 128)
@@ -441,7 +443,8 @@ int llm_int8_gemm(const void* X, int x_dtype, const int8_t* qW, const float* w_s
  * Errors, all found before any launch: QMM_EINVAL for a null pointer, a
  * non-positive size or an alpha outside [0, 1]; QMM_EUNSUPPORTED for fp16 or
  * fp32 operands, K % 128 != 0 or more than 64 alphas; QMM_ERANGE for
- * K > 2^22 or N, T >= 2^31; QMM_EALIGN for W, X, codes not 16-byte aligned;
+ * K > 2^22, N >= 2^31 or T > 2^21; QMM_EALIGN for W, X, codes not 16-byte
+ * aligned;
  * QMM_EWORKSPACE for a workspace smaller than awq_workspace_bytes(N, K, T,
  * n_alpha) (0 for invalid sizes), QMM_EALIGN for one not 256-byte aligned.
  * The workspace is the caller's device memory, used only during the call

@@ -490,7 +490,7 @@ def llm_int8_reference(x, qw, b, threshold: float, max_outliers=None, x_dtype: s
     return idx[:counts[0]].copy(), int(counts[1]), qx, a, y
 
 
-AWQ_ALPHAS = np.array([i / 10 for i in range(11)])   # the [QS] awq listing's grid 0, 0.1, .., 1
+AWQ_ALPHAS = np.linspace(0.0, 1.0, 11)   # the [QS] awq listing's grid, its values to the last bit
 
 
 def awq_search_reference(w, x, alphas=None, parallel: bool = False):

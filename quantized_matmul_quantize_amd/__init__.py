@@ -645,7 +645,9 @@ def llm_int8_gemm(X: torch.Tensor, qW, w_scale, threshold: float = 6.0, max_outl
 # ---------------------------------------------------------------------------
 # AWQ scaling search.
 # ---------------------------------------------------------------------------
-AWQ_ALPHAS = tuple(i / 10 for i in range(11))   # 0, 0.1, .., 1: the grid of the awq listing in "Quantization from Scratch"
+# 0, 0.1, .., 1 as numpy's linspace(0, 1, 11) has them (i * 0.1, the last one
+# exactly 1): the grid of the awq listing in "Quantization from Scratch"
+AWQ_ALPHAS = tuple(i * 0.1 for i in range(10)) + (1.0,)
 
 
 def awq_workspace_bytes(N: int, K: int, T: int, n_alpha: int) -> int:

@@ -10,22 +10,27 @@
 //
 // For every alpha of the grid (the loop runs on the host, the choice on the
 // device, so nothing waits for the host):
-//   s      = mag^alpha / sqrt(max * min), fp64, stored in fp32;
-//   W_s    = fl32(W diag(s)) -> quantize_groupwise (INT4, groups of 128);
+//   s      = mag^alpha / sqrt(max * min), fp64, stored in fp32 (all alphas
+//            at once, before the loop);
+//   codes  = group-128 INT4 of fl32(W diag(s)), the product formed inside
+//            the quantizer (no fp32 copy of the scaled weights);
 //   X_s    = bf16(fl32(X / s))  (the inverse scaling folded into the input);
-//   Y_q    = w4a16_gemm(X_s, codes of W_s);
+//   Y_q    = w4a16_gemm(X_s, codes);
 //   err    = sum (X W^T - Y_q)^2 in fp64, X W^T once by the bf16 product;
 // then the first alpha of the smallest error is selected, and W diag(s_best)
 // quantized into the caller's format buffers.  mag_j = max(mean_t |x_j|,
-// 1e-8) in fp64 (exact sums for activations of ordinary range, so the order
-// of the partial sums does not change it).
+// 1e-8) in fp64: the sum of |x| over the tokens is taken over slices of 32
+// rows and the slices in order; it is exact (so equal to any other order's)
+// while each channel's nonzero |x| span less than 2^(45 - log2 T) in ratio
+// (bf16 values carry 8 significant bits), true of any activations with an
+// ordinary dynamic range.
 
 #include "qmm_device.h"
 
 namespace qmm {
 namespace {
 
-constexpr int kMagRows = 64;       // rows per partial sum of the channel magnitudes
+constexpr int kMagRows = 32;       // rows per partial sum of the channel magnitudes
 constexpr int kErrBlocks = 1024;   // partial sums of one squared error
 constexpr int kMaxAlphas = 64;
 
@@ -54,24 +59,23 @@ __global__ __launch_bounds__(256) void awq_mag_partial_kernel(const uint16_t* __
   part[blockIdx.y * K + j] = acc;
 }
 
-// One block per alpha: mag_j from the partial sums (in order), p_j = mag_j^alpha,
-// s_j = fl32(p_j / sqrt(max p * min p)).
-__global__ __launch_bounds__(256) void awq_scales_kernel(const double* __restrict__ part, int64_t slices, int64_t T,
-                                                         int64_t K, AlphaGrid alphas, float* __restrict__ s_all,
-                                                         double* __restrict__ pbuf) {
+// Block (b, a): mag_j of its 256 columns from the partial sums (in order),
+// p_j = mag_j^alpha_a, and the block's max and min of p.
+__global__ __launch_bounds__(256) void awq_pow_kernel(const double* __restrict__ part, int64_t slices, int64_t T,
+                                                      int64_t K, AlphaGrid alphas, double* __restrict__ pbuf,
+                                                      double* __restrict__ bmax, double* __restrict__ bmin) {
   __shared__ double smax[256], smin[256];
-  const double alpha = alphas.a[blockIdx.x];
-  double* p = pbuf + blockIdx.x * K;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   double mx = 0.0, mn = INFINITY;
-  for (int64_t j = threadIdx.x; j < K; j += blockDim.x) {
+  if (j < K) {
     double acc = 0.0;
     for (int64_t b = 0; b < slices; ++b) acc += part[b * K + j];
     double m = acc / static_cast<double>(T);
     m = m < 1e-8 ? 1e-8 : m;
-    const double pj = pow(m, alpha);
-    p[j] = pj;
-    mx = fmax(mx, pj);
-    mn = fmin(mn, pj);
+    const double pj = pow(m, alphas.a[blockIdx.y]);
+    pbuf[blockIdx.y * K + j] = pj;
+    mx = pj;
+    mn = pj;
   }
   smax[threadIdx.x] = mx;
   smin[threadIdx.x] = mn;
@@ -83,29 +87,40 @@ __global__ __launch_bounds__(256) void awq_scales_kernel(const double* __restric
     }
     __syncthreads();
   }
-  const double norm = sqrt(smax[0] * smin[0]);
-  float* s = s_all + blockIdx.x * K;
-  for (int64_t j = threadIdx.x; j < K; j += blockDim.x) s[j] = static_cast<float>(p[j] / norm);
+  if (threadIdx.x == 0) {
+    bmax[blockIdx.y * gridDim.x + blockIdx.x] = smax[0];
+    bmin[blockIdx.y * gridDim.x + blockIdx.x] = smin[0];
+  }
 }
 
-// W_s = fl32(W diag(s)) (fp32 out), eight weights per thread.
-__global__ __launch_bounds__(256) void awq_scale_w_kernel(const uint16_t* __restrict__ w, const float* __restrict__ s,
-                                                          int64_t total8, int64_t K, float* __restrict__ out) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total8;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t e = i * 8;
-    const int64_t j = e % K;
-    const u32x4 v = ld16(w + e);
-    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
-    float o[8];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      o[2 * h] = bf16lo_to_f32(a[h]) * s[j + 2 * h];
-      o[2 * h + 1] = bf16hi_to_f32(a[h]) * s[j + 2 * h + 1];
-    }
-    *reinterpret_cast<f32x4*>(out + e) = f32x4{o[0], o[1], o[2], o[3]};
-    *reinterpret_cast<f32x4*>(out + e + 4) = f32x4{o[4], o[5], o[6], o[7]};
+// One block per alpha: norm = sqrt(max p * min p) over the blocks' extremes.
+__global__ __launch_bounds__(256) void awq_norm_kernel(const double* __restrict__ bmax, const double* __restrict__ bmin,
+                                                       int64_t nb, double* __restrict__ norm) {
+  __shared__ double smax[256], smin[256];
+  double mx = 0.0, mn = INFINITY;
+  for (int64_t b = threadIdx.x; b < nb; b += blockDim.x) {
+    mx = fmax(mx, bmax[blockIdx.x * nb + b]);
+    mn = fmin(mn, bmin[blockIdx.x * nb + b]);
   }
+  smax[threadIdx.x] = mx;
+  smin[threadIdx.x] = mn;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (static_cast<int>(threadIdx.x) < o) {
+      smax[threadIdx.x] = fmax(smax[threadIdx.x], smax[threadIdx.x + o]);
+      smin[threadIdx.x] = fmin(smin[threadIdx.x], smin[threadIdx.x + o]);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) norm[blockIdx.x] = sqrt(smax[0] * smin[0]);
+}
+
+// s[a, j] = fl32(p[a, j] / norm[a]).
+__global__ __launch_bounds__(256) void awq_factor_kernel(const double* __restrict__ pbuf,
+                                                         const double* __restrict__ norm, int64_t K,
+                                                         float* __restrict__ s_all) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j < K) s_all[blockIdx.y * K + j] = static_cast<float>(pbuf[blockIdx.y * K + j] / norm[blockIdx.y]);
 }
 
 // X_s = bf16(fl32(X / s)), correctly rounded division, eight values per thread.
@@ -151,21 +166,30 @@ __global__ __launch_bounds__(256) void awq_sqerr_kernel(const float* __restrict_
   if (threadIdx.x == 0) part[blockIdx.x] = red[0];
 }
 
-// err[a] = the partial sums in order; best = the first alpha of the smallest
-// error; s_best = its factors.
-__global__ __launch_bounds__(256) void awq_select_kernel(const double* __restrict__ part, int n_alpha,
-                                                         const float* __restrict__ s_all, int64_t K,
-                                                         double* __restrict__ err, int64_t* __restrict__ best,
-                                                         float* __restrict__ s_best) {
+// err[a] = the partial sums of alpha a by one fixed tree; best = the first
+// alpha of the smallest error; s_best = its factors, into the caller's
+// buffer and the workspace copy the final quantization reads.
+__global__ __launch_bounds__(kErrBlocks) void awq_select_kernel(const double* __restrict__ part, int n_alpha,
+                                                                const float* __restrict__ s_all, int64_t K,
+                                                                double* __restrict__ err, int64_t* __restrict__ best,
+                                                                float* __restrict__ s_best,
+                                                                float* __restrict__ s_copy) {
+  __shared__ double red[kErrBlocks];
   __shared__ double e_s[kMaxAlphas];
   __shared__ int b_s;
-  if (static_cast<int>(threadIdx.x) < n_alpha) {
-    double e = 0.0;
-    for (int b = 0; b < kErrBlocks; ++b) e += part[threadIdx.x * kErrBlocks + b];
-    e_s[threadIdx.x] = e;
-    err[threadIdx.x] = e;
+  for (int a = 0; a < n_alpha; ++a) {
+    red[threadIdx.x] = part[a * kErrBlocks + threadIdx.x];
+    __syncthreads();
+    for (int o = kErrBlocks / 2; o > 0; o >>= 1) {
+      if (static_cast<int>(threadIdx.x) < o) red[threadIdx.x] += red[threadIdx.x + o];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+      e_s[a] = red[0];
+      err[a] = red[0];
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (threadIdx.x == 0) {
     int bi = 0;
     for (int a = 1; a < n_alpha; ++a)
@@ -174,24 +198,32 @@ __global__ __launch_bounds__(256) void awq_select_kernel(const double* __restric
     *best = bi;
   }
   __syncthreads();
-  for (int64_t j = threadIdx.x; j < K; j += blockDim.x) s_best[j] = s_all[b_s * K + j];
+  for (int64_t j = threadIdx.x; j < K; j += blockDim.x) {
+    const float v = s_all[b_s * K + j];
+    s_best[j] = v;
+    s_copy[j] = v;
+  }
 }
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Workspace regions, in order.
 struct AwqLayout {
-  size_t mag, pbuf, s_all, ws, xs, codes, scales, zeros, yref, yq, err, total;
+  size_t mag, pbuf, bmax, bmin, norm, s_all, s_best, xs, codes, scales, zeros, yref, yq, err, total;
 };
 
 AwqLayout awq_layout(int64_t N, int64_t K, int64_t T, int64_t n_alpha) {
   AwqLayout l;
   const int64_t G = K / kGroup;
+  const int64_t nb = ceil_div(K, 256);
   size_t o = 0;
   l.mag = o; o += align256(static_cast<size_t>(ceil_div(T, kMagRows) * K) * sizeof(double));
   l.pbuf = o; o += align256(static_cast<size_t>(n_alpha * K) * sizeof(double));
+  l.bmax = o; o += align256(static_cast<size_t>(n_alpha * nb) * sizeof(double));
+  l.bmin = o; o += align256(static_cast<size_t>(n_alpha * nb) * sizeof(double));
+  l.norm = o; o += align256(static_cast<size_t>(n_alpha) * sizeof(double));
   l.s_all = o; o += align256(static_cast<size_t>(n_alpha * K) * sizeof(float));
-  l.ws = o; o += align256(static_cast<size_t>(N * K) * sizeof(float));
+  l.s_best = o; o += align256(static_cast<size_t>(K) * sizeof(float));
   l.xs = o; o += align256(static_cast<size_t>(T * K) * 2);
   l.codes = o; o += align256(static_cast<size_t>(N * K / 2));
   l.scales = o; o += align256(static_cast<size_t>(N * G) * sizeof(float));
@@ -233,7 +265,8 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   for (int64_t a = 0; a < n_alpha; ++a)
     if (!(alphas[a] >= 0.0 && alphas[a] <= 1.0)) return QMM_EINVAL;
   // the bf16 product's 32-bit offsets (256 rows of 2K bytes) and the W4A16 product's
-  if (K > (int64_t(1) << 22) || N > INT32_MAX || T > INT32_MAX) return QMM_ERANGE;
+  // and the magnitude slices' grid rows (T / 32 < 2^16)
+  if (K > (int64_t(1) << 22) || N > INT32_MAX || T > (int64_t(1) << 21)) return QMM_ERANGE;
   if (!aligned(W, 16) || !aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(smooth, 4) ||
       !aligned(err, 8) || !aligned(best, 8))
     return QMM_EALIGN;
@@ -243,8 +276,11 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   uint8_t* base = static_cast<uint8_t*>(workspace);
   double* mag = reinterpret_cast<double*>(base + L.mag);
   double* pbuf = reinterpret_cast<double*>(base + L.pbuf);
+  double* bmax = reinterpret_cast<double*>(base + L.bmax);
+  double* bmin = reinterpret_cast<double*>(base + L.bmin);
+  double* norm = reinterpret_cast<double*>(base + L.norm);
   float* s_all = reinterpret_cast<float*>(base + L.s_all);
-  float* ws = reinterpret_cast<float*>(base + L.ws);
+  float* s_copy = reinterpret_cast<float*>(base + L.s_best);
   uint16_t* xs = reinterpret_cast<uint16_t*>(base + L.xs);
   uint8_t* qc = base + L.codes;
   float* qs = reinterpret_cast<float*>(base + L.scales);
@@ -258,11 +294,13 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
 
   // channel magnitudes and every alpha's factors
   const int64_t slices = ceil_div(T, kMagRows);
-  awq_mag_partial_kernel<<<dim3(static_cast<unsigned>(ceil_div(K, 256)), static_cast<unsigned>(slices)), 256, 0, s>>>(
-      x, T, K, mag);
+  const unsigned nb = static_cast<unsigned>(ceil_div(K, 256));
+  awq_mag_partial_kernel<<<dim3(nb, static_cast<unsigned>(slices)), 256, 0, s>>>(x, T, K, mag);
   AlphaGrid grid{};
   for (int64_t a = 0; a < n_alpha; ++a) grid.a[a] = alphas[a];
-  awq_scales_kernel<<<static_cast<unsigned>(n_alpha), 256, 0, s>>>(mag, slices, T, K, grid, s_all, pbuf);
+  awq_pow_kernel<<<dim3(nb, static_cast<unsigned>(n_alpha)), 256, 0, s>>>(mag, slices, T, K, grid, pbuf, bmax, bmin);
+  awq_norm_kernel<<<static_cast<unsigned>(n_alpha), 256, 0, s>>>(bmax, bmin, nb, norm);
+  awq_factor_kernel<<<dim3(nb, static_cast<unsigned>(n_alpha)), 256, 0, s>>>(pbuf, norm, K, s_all);
   int st = launch_status();
   if (st != QMM_OK) return st;
   // the full-precision output X W^T
@@ -270,14 +308,10 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   st = launch_status();
   if (st != QMM_OK) return st;
 
-  const int64_t wn8 = N * K / 8, xn8 = T * K / 8;
+  const int64_t xn8 = T * K / 8;
   for (int64_t a = 0; a < n_alpha; ++a) {
     const float* sa = s_all + a * K;
-    awq_scale_w_kernel<<<grid_for(wn8), 256, 0, s>>>(w, sa, wn8, K, ws);
-    st = launch_status();
-    if (st != QMM_OK) return st;
-    st = quantize_groupwise(ws, QMM_F32, N, K, kGroup, 4, qc, qs, qz, stream);
-    if (st != QMM_OK) return st;
+    launch_quantize_colscaled(w, sa, N, K, qc, qs, qz, s);
     awq_scale_x_kernel<<<grid_for(xn8), 256, 0, s>>>(x, sa, xn8, K, xs);
     st = launch_status();
     if (st != QMM_OK) return st;
@@ -287,12 +321,10 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
     st = launch_status();
     if (st != QMM_OK) return st;
   }
-  awq_select_kernel<<<1, 256, 0, s>>>(epart, static_cast<int>(n_alpha), s_all, K, err, best, smooth);
+  awq_select_kernel<<<1, kErrBlocks, 0, s>>>(epart, static_cast<int>(n_alpha), s_all, K, err, best, smooth, s_copy);
   st = launch_status();
   if (st != QMM_OK) return st;
   // the chosen alpha's weights in the caller's format
-  awq_scale_w_kernel<<<grid_for(wn8), 256, 0, s>>>(w, smooth, wn8, K, ws);
-  st = launch_status();
-  if (st != QMM_OK) return st;
-  return quantize_groupwise(ws, QMM_F32, N, K, kGroup, 4, codes, scales, zeros, stream);
+  launch_quantize_colscaled(w, s_copy, N, K, codes, scales, zeros, s);
+  return launch_status();
 }

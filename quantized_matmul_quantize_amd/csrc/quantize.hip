@@ -151,11 +151,18 @@ __global__ __launch_bounds__(256) void quantize_g128_flat_kernel(const uint8_t* 
 // the four reads of each lane are free of bank conflicts.
 constexpr int kQChunkBytes = 16 * kGroup * 2;   // 4 KiB of 16-bit weights
 
-template <int DT, bool SYM>
+//
+// CS = true quantizes fl32(w * colscale[column]) instead of w (one fp32
+// product per weight, the factors read through the cache; G = groups per
+// row locates a group's columns): AWQ's scaled weights without a stored
+// fp32 copy of them.
+template <int DT, bool SYM, bool CS = false>
 __global__ __launch_bounds__(256) void quantize_g128_lds_kernel(const uint8_t* __restrict__ w, int64_t total_groups,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales,
-                                                                uint8_t* __restrict__ zeros) {
+                                                                uint8_t* __restrict__ zeros,
+                                                                const float* __restrict__ colscale = nullptr,
+                                                                int64_t G = 0) {
   static_assert(DT != QMM_F32, "16-bit weights only");
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * 2 * kQChunkBytes];
   const int lane = threadIdx.x & (kWave - 1);
@@ -217,6 +224,17 @@ __global__ __launch_bounds__(256) void quantize_g128_lds_kernel(const uint8_t* _
     }
     const int64_t gi = c * 16 + (lane >> 2);
     const bool active = gi < total_groups;
+    if constexpr (CS) {
+      const float* cs = colscale + (gi % G) * kGroup + part * 32;   // in [0, K) for idle lanes too
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x4 f = *reinterpret_cast<const f32x4*>(cs + 4 * q);
+        v[4 * q] = v[4 * q] * f.x;
+        v[4 * q + 1] = v[4 * q + 1] * f.y;
+        v[4 * q + 2] = v[4 * q + 2] * f.z;
+        v[4 * q + 3] = v[4 * q + 3] * f.w;
+      }
+    }
     float lo = 0.0f, hi = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -247,12 +265,13 @@ __global__ __launch_bounds__(256) void quantize_g128_lds_kernel(const uint8_t* _
   }
 }
 
-template <int DT, bool SYM>
+template <int DT, bool SYM, bool CS = false>
 __global__ __launch_bounds__(256) void quantize_g128_kernel(const uint8_t* __restrict__ w, int64_t K, int64_t G,
                                                             int64_t chunks_per_row, int64_t total_chunks,
                                                             uint32_t* __restrict__ codes,
                                                             float* __restrict__ scales,
-                                                            uint8_t* __restrict__ zeros, int64_t zeros_row_bytes) {
+                                                            uint8_t* __restrict__ zeros, int64_t zeros_row_bytes,
+                                                            const float* __restrict__ colscale = nullptr) {
   constexpr int kElemBytes = DT == QMM_F32 ? 4 : 2;
   const int lane = threadIdx.x & (kWave - 1);
   const int gl = lane >> 4;     // group of the chunk handled by this DPP row
@@ -271,6 +290,14 @@ __global__ __launch_bounds__(256) void quantize_g128_kernel(const uint8_t* __res
     // Unconditional load (idle lanes re-read this row's first group) so the
     // load is not split by a branch; idle lanes store nothing.
     Vec8<DT>::load(w + (active ? e : n * K + part * 8) * kElemBytes, v);
+    if constexpr (CS) {   // fl32(w * colscale[column]), as the LDS kernel
+      const float* cs = colscale + (active ? g : 0) * kGroup + part * 8;
+      const f32x4 f0 = *reinterpret_cast<const f32x4*>(cs);
+      const f32x4 f1 = *reinterpret_cast<const f32x4*>(cs + 4);
+      const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = v[i] * f[i];
+    }
     // Group range, widened to contain 0.
     float lo = fminf(fminf(fminf(0.0f, v[0]), fminf(v[1], v[2])), fminf(fminf(v[3], v[4]), fminf(v[5], v[6])));
     float hi = fmaxf(fmaxf(fmaxf(0.0f, v[0]), fmaxf(v[1], v[2])), fmaxf(fmaxf(v[3], v[4]), fmaxf(v[5], v[6])));
@@ -414,6 +441,27 @@ int quantize_launch(const void* W, int w_dtype, int64_t N, int64_t K, int group,
 }
 
 }  // namespace
+
+void launch_quantize_colscaled(const uint16_t* W, const float* colscale, int64_t N, int64_t K, uint8_t* codes,
+                               float* scales, uint8_t* zeros, hipStream_t s) {
+  const int64_t G = K / kGroup;
+  const uint8_t* w = reinterpret_cast<const uint8_t*>(W);
+  const dim3 block(256);
+  if (G % 2 == 0) {
+    const int64_t T = N * G;
+    int64_t blocks = ceil_div(ceil_div(T, 16), 4);
+    const int64_t cap = static_cast<int64_t>(device_cus()) * 16;
+    if (blocks > cap) blocks = cap;
+    quantize_g128_lds_kernel<QMM_BF16, false, true><<<dim3(static_cast<unsigned>(blocks)), block, 0, s>>>(
+        w, T, codes, scales, zeros, colscale, G);
+    return;
+  }
+  const int64_t chunks_per_row = ceil_div(G, 4);
+  const int64_t total = N * chunks_per_row;
+  quantize_g128_kernel<QMM_BF16, false, true><<<dim3(static_cast<unsigned>(chunk_grid(total))), block, 0, s>>>(
+      w, K, G, chunks_per_row, total, reinterpret_cast<uint32_t*>(codes), scales, zeros, ceil_div(G, 2), colscale);
+}
+
 }  // namespace qmm
 
 extern "C" int quantize_groupwise(const void* W, int w_dtype, int64_t N, int64_t K, int group, int bits,

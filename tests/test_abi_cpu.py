@@ -218,12 +218,14 @@ def test_awq_workspace_and_argument_errors():
     lib = qmm.lib()
     ws = lib.awq_workspace_bytes
     a256 = lambda b: (b + 255) // 256 * 256
-    # magnitude partial sums, every alpha's fp64 powers and fp32 factors, the
-    # scaled fp32 weights, the scaled bf16 inputs, one INT4 format, both fp32
-    # products, the squared-error partial sums
+    # magnitude partial sums (32-row slices), every alpha's fp64 powers, their
+    # per-256-column maxima and minima, the norms, the fp32 factors, the chosen
+    # factors, the scaled bf16 inputs, one INT4 format, both fp32 products, the
+    # squared-error partial sums
     n, k, t, na = 4096, 4096, 2048, 11
-    want = (a256(32 * k * 8) + a256(na * k * 8) + a256(na * k * 4) + a256(n * k * 4) + a256(t * k * 2) +
-            a256(n * k // 2) + a256(n * 32 * 4) + a256(n * 16) + 2 * a256(t * n * 4) + a256(na * 1024 * 8))
+    want = (a256(64 * k * 8) + a256(na * k * 8) + 2 * a256(na * 16 * 8) + a256(na * 8) + a256(na * k * 4) +
+            a256(k * 4) + a256(t * k * 2) + a256(n * k // 2) + a256(n * 32 * 4) + a256(n * 16) +
+            2 * a256(t * n * 4) + a256(na * 1024 * 8))
     assert ws(n, k, t, na) == want
     assert ws(0, 128, 4, 1) == 0 and ws(4, 100, 4, 1) == 0 and ws(4, 128, 4, 65) == 0 and ws(4, 128, 4, 0) == 0
     g = lib.awq_search
@@ -242,6 +244,8 @@ def test_awq_workspace_and_argument_errors():
     assert g(*args(na=0)) == EINVAL
     assert g(*args(al=ctypes.cast(bad, ctypes.c_void_p))) == EINVAL
     assert g(*args(K=(1 << 22) + 128, wsb=10**15)) == ERANGE
+    assert g(P, BF16, P, BF16, 4, 128, (1 << 21) + 1, ctypes.cast(al, ctypes.c_void_p), 2, P, P, P, P, P, P,
+             P, 10**15, None) == ERANGE
     assert g(*args(W=MIS)) == EALIGN
     assert g(*args(ws=None)) == EWS
     assert g(*args(wsb=need - 1)) == EWS

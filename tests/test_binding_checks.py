@@ -99,3 +99,9 @@ def test_awq_checks():
     raises(lambda: qmm.awq_search(w, x, alphas=[float("nan")]), r"\[0, 1\]")
     raises(lambda: qmm.awq_search(w, x, workspace=t((16,), u8)), "workspace holds")
     raises(lambda: qmm.awq_search(w, x), "device tensor")
+
+
+def test_awq_default_grid_is_the_listings():
+    # numpy's linspace(0, 1, 11) values, to the last bit (0.30000000000000004 ...)
+    import numpy as np
+    assert np.array_equal(np.array(qmm.AWQ_ALPHAS), np.linspace(0.0, 1.0, 11))
