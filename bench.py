@@ -44,7 +44,11 @@ library launches on torch's current stream), created without the system
 fence so that recording them leaves the caches alone; the two B=1 GEMVs of
 the 70B matrices run back to back inside one event pair and share its time.
 `value` is their effective bandwidth: algorithmic bytes (packed codes,
-scales, zero-points, activations in, outputs out) over kernel time.
+scales, zero-points, activations in, outputs out) over kernel time.  Each
+op's breakdown entry gives the mean, median, p10 and p90 over the timed
+steps; `config.plain_read_GBps` is a plain 1 GiB streaming read (the
+library's `qmm_stream_read`, after the timed steps), as context for the HBM
+fractions.
 
 CPU baseline: the plain C oracle's reference for the same B=1 GEMVs
 (dequantize + fp64 product), single-threaded, and its OpenMP build over all
@@ -673,7 +677,9 @@ def main():
         ms = [per_step_events[i][j0][0].elapsed_time(per_step_events[i][j1][1]) / size for i in range(args.steps)]
         avg_us = 1e3 * float(np.mean(ms))
         rec = {"config": op["config"], "kernel": op["kernel"], "avg_us": round(avg_us, 3),
-               "median_us": round(1e3 * float(np.median(ms)), 3), "alg_bytes": op["bytes"],
+               "median_us": round(1e3 * float(np.median(ms)), 3),
+               "p10_us": round(1e3 * float(np.percentile(ms, 10)), 3),
+               "p90_us": round(1e3 * float(np.percentile(ms, 90)), 3), "alg_bytes": op["bytes"],
                "GBps": round(op["bytes"] / avg_us / 1e3, 2),
                "hbm_frac": round(op["bytes"] / avg_us / 1e3 / HBM_PEAK_GBPS, 4)}
         if op["flops"]:
@@ -685,6 +691,22 @@ def main():
         if size > 1:
             rec["timing"] = f"back to back with {size - 1} other launch(es), one event pair, time split evenly"
         breakdown[op["name"]] = rec
+
+    # Context, not a denominator: the library's plain streaming read
+    # (qmm_stream_read) over 1 GiB, median of 10, after the timed steps.
+    lib = qmm.lib()
+    big = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    xo = torch.empty(1, dtype=torch.int32, device=dev)
+    rd = []
+    for _ in range(12):
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record()
+        ok(lib.qmm_stream_read(P(big), big.numel(), P(xo), S(big)))
+        e1.record()
+        rd.append((e0, e1))
+    torch.cuda.synchronize()
+    plain_read = (1 << 30) / (float(np.median([a.elapsed_time(b) for a, b in rd[2:]])) * 1e-3) / 1e9
+    del big
 
     gemv1 = [k for k in breakdown if k.startswith("w4a16_gemv B=1 28672") or k.startswith("w4a16_gemv B=1 8192")]
     g_bytes = sum(breakdown[k]["alg_bytes"] for k in gemv1)
@@ -720,6 +742,7 @@ def main():
                         "W8A8 and LLM.int8() 2048x4096x4096 paths and AWQ's scaling search on a 4096x4096 layer "
                         "with 2048 calibration tokens",
             "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+            "plain_read_GBps": round(plain_read, 1),
             "quantize_GBps": gbps(["quantize 28672x8192", "quantize 8192x28672"]),
             "quantize_GBps_llama7b": gbps(["quantize 4096x4096", "quantize 11008x4096"]),
             "quantize_GBps_gemm_14336x4096": gbps(["quantize 14336x4096"]),

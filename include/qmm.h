@@ -66,6 +66,17 @@ const char* qmm_status_string(int status);
 /* ABI version: major * 10000 + minor * 100 + patch. */
 int qmm_version(void);
 
+/* Diagnostics: a plain streaming read of `bytes` bytes of device memory at
+ * `data`, every 16-byte piece once, folded into *out (device, uint32) as the
+ * XOR of all 32-bit words so that no load can be dropped.  For measuring the
+ * bandwidth a plain read reaches on this GPU, the practical ceiling of the
+ * HBM-bound kernels above (decode time is the weight bytes over that
+ * bandwidth: "Quantization from Scratch", "What it buys at decode").  Two
+ * launches on the stream (a one-thread clear of *out, then the read).
+ * QMM_EINVAL for a null pointer or bytes == 0; QMM_EALIGN unless data is
+ * 16-byte aligned, bytes % 16 == 0 and out 4-byte aligned. */
+int qmm_stream_read(const void* data, size_t bytes, uint32_t* out, void* stream);
+
 /* Byte sizes of the INT4 format for a [N, K] weight with the given group size.
  * Any output pointer may be NULL.  QMM_EINVAL if N, K <= 0, group <= 0 or
  * K % group != 0.  Host-only. */

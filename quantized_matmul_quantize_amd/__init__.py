@@ -25,7 +25,7 @@ __all__ = [
     "sq_smooth_factors", "sq_quantize_weight", "sq_quantize_activation", "sq_quantize_activation_per_tensor",
     "sq_int8_gemm", "sq_workspace_bytes", "smooth_quant_w8a8_gemm", "smooth_quant_w8a8_gemm_noalloc",
     "fp8_quantize", "fp8_gemm", "fp8_w8a8_gemm",
-    "llm_int8_outliers", "llm_int8_workspace_bytes", "llm_int8_gemm", "awq_workspace_bytes", "awq_search",
+    "llm_int8_outliers", "llm_int8_workspace_bytes", "llm_int8_gemm", "awq_workspace_bytes", "awq_search", "stream_read",
 ]
 
 F32, F16, BF16, I32 = 0, 1, 2, 3
@@ -83,6 +83,7 @@ _SIGS = {
     "llm_int8_outliers": ([_P, _I, _I64, _I64, _F, _I64, _P, _P, _P, _P], _I),
     "llm_int8_workspace_bytes": ([_I64, _I64, _I64, _I64], _SZ),
     "awq_workspace_bytes": ([_I64, _I64, _I64, _I64], _SZ),
+    "qmm_stream_read": ([_P, _SZ, _P, _P], _I),
     "awq_search": ([_P, _I, _P, _I, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "llm_int8_gemm": ([_P, _I, _P, _P, _I64, _I64, _I64, _F, _I64, _P, _I, _P, _P, _SZ, _P], _I),
 }
@@ -690,3 +691,18 @@ def awq_search(W: torch.Tensor, X: torch.Tensor, alphas: Sequence[float] = AWQ_A
           len(a), _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(smooth), _ptr(err), _ptr(best), _ptr(workspace),
           workspace.numel(), _stream(X))
     return codes, scales, zeros, smooth, err, best
+
+
+def stream_read(data: torch.Tensor) -> torch.Tensor:
+    """Read every byte of a contiguous device tensor once (a plain streaming
+    read, for measuring bandwidth); returns the XOR of its 32-bit words as a
+    uint32-valued int32 tensor [1] on the device."""
+    if not isinstance(data, torch.Tensor):
+        raise ValueError("data must be a torch.Tensor")
+    nbytes = data.numel() * data.element_size()
+    if nbytes == 0 or nbytes % 16 != 0:
+        raise ValueError(f"data must hold a positive multiple of 16 bytes, not {nbytes}")
+    dev = _place(data=data)
+    out = torch.empty(1, dtype=torch.int32, device=dev)
+    _call("qmm_stream_read", _ptr(data), nbytes, _ptr(out), _stream(data))
+    return out

@@ -1024,16 +1024,26 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
   const int G = static_cast<int>(K / kGroup);
   const int zb = (G + 1) / 2;
 
-  // Tile order as in the kernel above: consecutive tiles per XCD, token tiles
-  // fastest, so the blocks sharing a weight slice run together on one XCD.
+  // Tile order: consecutive tiles per XCD, in bands of gm token tiles whose
+  // activations (gm x BM x K x 2 bytes) fit in about 2 MiB of the XCD's L2;
+  // within a band the token tiles run fastest, so the blocks sharing a weight
+  // slice run together and the band's activations are fetched from memory
+  // once rather than once per weight slice.  (With every token tile in one
+  // band this is token tiles fastest over the whole matrix.)
   const int64_t mtiles = (M + BM - 1) / BM;
   const int64_t ntiles = (N + kTileN - 1) / kTileN;
   const int64_t T = mtiles * ntiles;
   const int64_t per = (T + 7) / 8;
   const int64_t t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= T) return;
-  const int64_t n0 = (t / mtiles) * kTileN;
-  const int64_t m0 = (t % mtiles) * BM;
+  const int64_t band_cap = (int64_t{2} << 20) / (int64_t{BM} * K * 2);
+  const int64_t gm_max = band_cap > 1 ? band_cap : 1;
+  const int64_t band = t / (gm_max * ntiles);
+  const int64_t m_first = band * gm_max;
+  const int64_t gm = (mtiles - m_first < gm_max) ? mtiles - m_first : gm_max;
+  const int64_t r = t - band * gm_max * ntiles;
+  const int64_t n0 = (r / gm) * kTileN;
+  const int64_t m0 = (m_first + r % gm) * BM;
   const int64_t nrows = (N - n0 < kTileN) ? N - n0 : kTileN;
   const int64_t mrows = (M - m0 < BM) ? M - m0 : BM;
 
