@@ -967,9 +967,28 @@ def check_awq_power_of_two_invariance():
     assert b1 == b4 and np.allclose(s1, s4, rtol=2e-7, atol=0) and np.allclose(e4, 16.0 * e1, rtol=1e-9)
 
 
+def check_awq_listing_error():
+    # [QS]'s awq listing scores alpha by sum((D @ H) * D) with D = W - Q / s,
+    # Q the round-to-nearest codes of W * s dequantized, and H from the
+    # calibration inputs (here X^T X in fp64 by numpy): the same layer output
+    # error ||X W^T - X diag(s)^-1 W_hat^T||^2.  The oracle folds diag(s)^-1
+    # into the bf16 input instead (R32), which moves the error by the input's
+    # rounding only (up to ~1e-3 of it here: the salient channel makes the
+    # outputs large against their error); a wrong Q, a missing / s or another
+    # H would move it by far more than the 1e-2 allowed.
+    w, x = _awq_case(8, salient=11)
+    h = x.astype(np.float64).T @ x.astype(np.float64)
+    for alpha in (0.3, 0.7):
+        err, _, s, q, sc, z = oracle.awq_search_reference(w, x, alphas=[alpha])
+        w_hat = (q.astype(np.float64) - np.repeat(z, 128, axis=1)) * np.repeat(sc.astype(np.float64), 128, axis=1)
+        d = w.astype(np.float64) - w_hat / s.astype(np.float64)[None, :]
+        e = float(np.sum((d @ h) * d))
+        assert abs(err[0] - e) <= 1e-2 * e, (alpha, err[0], e)
+
+
 ALL_CHECKS = [
     check_awq_alpha0_is_round_to_nearest, check_awq_uniform_magnitudes, check_awq_salient_channel,
-    check_awq_scales_closed_form, check_awq_power_of_two_invariance,
+    check_awq_scales_closed_form, check_awq_power_of_two_invariance, check_awq_listing_error,
     check_llm_int8_special_cases, check_llm_int8_decomposition, check_llm_int8_cap_and_permutation,
     check_llm_int8_accuracy,
     check_e4m3_conversion, check_fp8_listing, check_fp8_product,
