@@ -34,45 +34,65 @@ constexpr int kMagRows = 32;       // rows per partial sum of the channel magnit
 constexpr int kErrBlocks = 1024;   // partial sums of one squared error
 constexpr int kMaxAlphas = 64;
 
-__device__ __forceinline__ float x16_to_f32(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
-
 // The alpha grid, passed by value (a kernel argument of 512 bytes).
 struct AlphaGrid {
   double a[kMaxAlphas];
 };
 
-// Partial sums of |x| over rows [kMagRows b, +kMagRows) of each column, fp64.
+// Partial sums of |x| over rows [kMagRows b, +kMagRows) of each column,
+// fp64; a thread takes 8 consecutive columns (one 16-byte load per row).
 __global__ __launch_bounds__(256) void awq_mag_partial_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t K,
                                                               double* __restrict__ part) {
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (j >= K) return;
+  const int64_t j0 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
+  if (j0 >= K) return;
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kMagRows;
   const int64_t r1 = (r0 + kMagRows < T) ? r0 + kMagRows : T;
-  double acc = 0.0;
+  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
   for (int64_t r = r0; r < r1; r += 8) {
-    float v[8];
+    u32x4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = (r + u < r1) ? fabsf(x16_to_f32(x[(r + u) * K + j])) : 0.0f;
+    for (int u = 0; u < 8; ++u) v[u] = (r + u < r1) ? ld16(x + (r + u) * K + j0) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += static_cast<double>(v[u]);
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        acc[2 * h] += static_cast<double>(fabsf(bf16lo_to_f32(w[h])));
+        acc[2 * h + 1] += static_cast<double>(fabsf(bf16hi_to_f32(w[h])));
+      }
+    }
   }
-  part[blockIdx.y * K + j] = acc;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) part[blockIdx.y * K + j0 + c] = acc[c];
 }
 
-// Block (b, a): mag_j of its 256 columns from the partial sums (in order),
-// p_j = mag_j^alpha_a, and the block's max and min of p.
-__global__ __launch_bounds__(256) void awq_pow_kernel(const double* __restrict__ part, int64_t slices, int64_t T,
-                                                      int64_t K, AlphaGrid alphas, double* __restrict__ pbuf,
-                                                      double* __restrict__ bmax, double* __restrict__ bmin) {
+// mag_j = max(sum of the partial sums in order / T, 1e-8).
+__global__ __launch_bounds__(256) void awq_mag_kernel(const double* __restrict__ part, int64_t slices, int64_t T,
+                                                      int64_t K, double* __restrict__ mag) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j >= K) return;
+  double acc = 0.0;
+  for (int64_t b = 0; b < slices; b += 8) {   // eight loads in flight, then their sums in order
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (b + u < slices) ? part[(b + u) * K + j] : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  const double m = acc / static_cast<double>(T);
+  mag[j] = m < 1e-8 ? 1e-8 : m;
+}
+
+// Block (b, a): p_j = mag_j^alpha_a for its 256 columns, and the block's max
+// and min of p.
+__global__ __launch_bounds__(256) void awq_pow_kernel(const double* __restrict__ mag, int64_t K, AlphaGrid alphas,
+                                                      double* __restrict__ pbuf, double* __restrict__ bmax,
+                                                      double* __restrict__ bmin) {
   __shared__ double smax[256], smin[256];
   const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   double mx = 0.0, mn = INFINITY;
   if (j < K) {
-    double acc = 0.0;
-    for (int64_t b = 0; b < slices; ++b) acc += part[b * K + j];
-    double m = acc / static_cast<double>(T);
-    m = m < 1e-8 ? 1e-8 : m;
-    const double pj = pow(m, alphas.a[blockIdx.y]);
+    const double pj = pow(mag[j], alphas.a[blockIdx.y]);
     pbuf[blockIdx.y * K + j] = pj;
     mx = pj;
     mn = pj;
@@ -166,30 +186,31 @@ __global__ __launch_bounds__(256) void awq_sqerr_kernel(const float* __restrict_
   if (threadIdx.x == 0) part[blockIdx.x] = red[0];
 }
 
-// err[a] = the partial sums of alpha a by one fixed tree; best = the first
-// alpha of the smallest error; s_best = its factors, into the caller's
-// buffer and the workspace copy the final quantization reads.
+// err[a] = the partial sums of alpha a by one fixed order: wavefront w
+// takes alphas w, w + 16, ..; its lane l sums partials l, l + 64, .. in turn,
+// then the 64 lane sums are added by a fixed butterfly.  best = the first
+// alpha of the smallest error; s_best = its factors, into the caller's buffer
+// and the workspace copy the final quantization reads.
 __global__ __launch_bounds__(kErrBlocks) void awq_select_kernel(const double* __restrict__ part, int n_alpha,
                                                                 const float* __restrict__ s_all, int64_t K,
                                                                 double* __restrict__ err, int64_t* __restrict__ best,
                                                                 float* __restrict__ s_best,
                                                                 float* __restrict__ s_copy) {
-  __shared__ double red[kErrBlocks];
   __shared__ double e_s[kMaxAlphas];
   __shared__ int b_s;
-  for (int a = 0; a < n_alpha; ++a) {
-    red[threadIdx.x] = part[a * kErrBlocks + threadIdx.x];
-    __syncthreads();
-    for (int o = kErrBlocks / 2; o > 0; o >>= 1) {
-      if (static_cast<int>(threadIdx.x) < o) red[threadIdx.x] += red[threadIdx.x + o];
-      __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  constexpr int kWaves = kErrBlocks / kWave;
+  for (int a = wave; a < n_alpha; a += kWaves) {
+    double v = 0.0;
+    for (int b = lane; b < kErrBlocks; b += kWave) v += part[a * kErrBlocks + b];
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);   // every lane ends with the same sum
+    if (lane == 0) {
+      e_s[a] = v;
+      err[a] = v;
     }
-    if (threadIdx.x == 0) {
-      e_s[a] = red[0];
-      err[a] = red[0];
-    }
-    __syncthreads();
   }
+  __syncthreads();
   if (threadIdx.x == 0) {
     int bi = 0;
     for (int a = 1; a < n_alpha; ++a)
@@ -209,7 +230,7 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Workspace regions, in order.
 struct AwqLayout {
-  size_t mag, pbuf, bmax, bmin, norm, s_all, s_best, xs, codes, scales, zeros, yref, yq, err, total;
+  size_t part, mag, pbuf, bmax, bmin, norm, s_all, s_best, xs, codes, scales, zeros, yref, yq, err, total;
 };
 
 AwqLayout awq_layout(int64_t N, int64_t K, int64_t T, int64_t n_alpha) {
@@ -217,7 +238,8 @@ AwqLayout awq_layout(int64_t N, int64_t K, int64_t T, int64_t n_alpha) {
   const int64_t G = K / kGroup;
   const int64_t nb = ceil_div(K, 256);
   size_t o = 0;
-  l.mag = o; o += align256(static_cast<size_t>(ceil_div(T, kMagRows) * K) * sizeof(double));
+  l.part = o; o += align256(static_cast<size_t>(ceil_div(T, kMagRows) * K) * sizeof(double));
+  l.mag = o; o += align256(static_cast<size_t>(K) * sizeof(double));
   l.pbuf = o; o += align256(static_cast<size_t>(n_alpha * K) * sizeof(double));
   l.bmax = o; o += align256(static_cast<size_t>(n_alpha * nb) * sizeof(double));
   l.bmin = o; o += align256(static_cast<size_t>(n_alpha * nb) * sizeof(double));
@@ -274,6 +296,7 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   if (!aligned(workspace, 256)) return QMM_EALIGN;
   const AwqLayout L = awq_layout(N, K, T, n_alpha);
   uint8_t* base = static_cast<uint8_t*>(workspace);
+  double* mpart = reinterpret_cast<double*>(base + L.part);
   double* mag = reinterpret_cast<double*>(base + L.mag);
   double* pbuf = reinterpret_cast<double*>(base + L.pbuf);
   double* bmax = reinterpret_cast<double*>(base + L.bmax);
@@ -295,10 +318,12 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   // channel magnitudes and every alpha's factors
   const int64_t slices = ceil_div(T, kMagRows);
   const unsigned nb = static_cast<unsigned>(ceil_div(K, 256));
-  awq_mag_partial_kernel<<<dim3(nb, static_cast<unsigned>(slices)), 256, 0, s>>>(x, T, K, mag);
+  awq_mag_partial_kernel<<<dim3(static_cast<unsigned>(ceil_div(K, 2048)), static_cast<unsigned>(slices)), 256, 0, s>>>(
+      x, T, K, mpart);
+  awq_mag_kernel<<<nb, 256, 0, s>>>(mpart, slices, T, K, mag);
   AlphaGrid grid{};
   for (int64_t a = 0; a < n_alpha; ++a) grid.a[a] = alphas[a];
-  awq_pow_kernel<<<dim3(nb, static_cast<unsigned>(n_alpha)), 256, 0, s>>>(mag, slices, T, K, grid, pbuf, bmax, bmin);
+  awq_pow_kernel<<<dim3(nb, static_cast<unsigned>(n_alpha)), 256, 0, s>>>(mag, K, grid, pbuf, bmax, bmin);
   awq_norm_kernel<<<static_cast<unsigned>(n_alpha), 256, 0, s>>>(bmax, bmin, nb, norm);
   awq_factor_kernel<<<dim3(nb, static_cast<unsigned>(n_alpha)), 256, 0, s>>>(pbuf, norm, K, s_all);
   int st = launch_status();
