@@ -82,10 +82,10 @@ def _check_format(w, smooth, codes, scales, zeros, what, rows=None):
     assert bits_equal(codes, rc), f"{what} codes: {first_diff(codes, rc)}"
 
 
-def _check(w, x, alphas, what):
+def _check(w, x, alphas, what, parallel=False):
     codes, scales, zeros, smooth, err, best = _run(w, x, alphas, what)
     xf = x.float().numpy()
-    rerr, rbest, rs, _, _, _ = oracle.awq_search_reference(w.float().numpy(), xf, alphas)
+    rerr, rbest, rs, _, _, _ = oracle.awq_search_reference(w.float().numpy(), xf, alphas, parallel=parallel)
     assert best == int(np.argmin(err)), f"{what}: best {best} is not the first minimum of {err}"
     tol = _check_err(err, rerr, w, x, what)
     if best != rbest:   # a near tie: the GPU's choice must be as good within the tolerance
@@ -168,3 +168,12 @@ def test_awq_layer_4096():
                                                           parallel=True)
     tol = _check_err(err[near], rerr, w, x, "err near the chosen alpha", rows=stratified_rows(n, 64))
     assert rerr[near.index(best)] <= rerr.min() + 2 * tol.max(), (near, rerr)
+
+
+def test_awq_qwen_layer_shape():
+    # the shape of the MLP down projections "Quantization from Scratch"
+    # measures AWQ on ("Measured on two real layers": 4864-wide inputs, 896
+    # outputs), with 2048 calibration tokens and the pages' channel spread
+    # (largest mean |x| ~58x the median)
+    w, x = _case(896, 4864, 2048, 10, spread=(4.0, 58.0))
+    _check(w, x, list(qmm.AWQ_ALPHAS), "896x4864, 2048 tokens", parallel=True)
