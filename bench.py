@@ -48,7 +48,9 @@ scales, zero-points, activations in, outputs out) over kernel time.  Each
 op's breakdown entry gives the mean, median, p10 and p90 over the timed
 steps; `config.plain_read_GBps` is a plain 1 GiB streaming read (the
 library's `qmm_stream_read`, after the timed steps), as context for the HBM
-fractions.
+fractions, and `config.vendor_library_gemms` the ROCm BLAS libraries' INT8
+and bf16 GEMM rates at 2048x4096x4096 (through torch), as context for the
+MFMA fractions.
 
 CPU baseline: the plain C oracle's reference for the same B=1 GEMVs
 (dequantize + fp64 product), single-threaded, and its OpenMP build over all
@@ -598,6 +600,41 @@ def cpu_baseline(min_seconds=(8.0, 6.0), max_reps=40):
             "cpu_model": model, "nproc": nproc}
 
 
+def vendor_gemms(dev):
+    """Context, not a denominator: the ROCm BLAS libraries (through torch) on
+    the INT8 and bf16 products of the same 2048x4096x4096 shape, median of 20
+    after 5 warm-up calls; None where the library call is unavailable."""
+    m, n, k = 2048, 4096, 4096
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    out = {}
+
+    def median_us(fn):
+        for _ in range(5):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+
+    try:
+        a8 = torch.randint(-128, 128, (m, k), dtype=torch.int8, device=dev, generator=g)
+        b8 = torch.randint(-128, 128, (n, k), dtype=torch.int8, device=dev, generator=g)
+        us = median_us(lambda: torch._int_mm(a8, b8.t()))
+        out["int8_TOPS"] = round(2 * m * n * k / us / 1e6, 1)
+    except Exception:   # the context figure is optional
+        out["int8_TOPS"] = None
+    a16 = torch.randn(m, k, device=dev, generator=g).to(torch.bfloat16)
+    b16 = torch.randn(n, k, device=dev, generator=g).to(torch.bfloat16)
+    us = median_us(lambda: torch.matmul(a16, b16.t()))
+    out["bf16_TFLOPs"] = round(2 * m * n * k / us / 1e6, 1)
+    out["shape"] = f"{m}x{n}x{k} (torch._int_mm / torch.matmul)"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -707,6 +744,7 @@ def main():
     torch.cuda.synchronize()
     plain_read = (1 << 30) / (float(np.median([a.elapsed_time(b) for a, b in rd[2:]])) * 1e-3) / 1e9
     del big
+    vendor = vendor_gemms(dev)
 
     gemv1 = [k for k in breakdown if k.startswith("w4a16_gemv B=1 28672") or k.startswith("w4a16_gemv B=1 8192")]
     g_bytes = sum(breakdown[k]["alg_bytes"] for k in gemv1)
@@ -743,6 +781,7 @@ def main():
                         "with 2048 calibration tokens",
             "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
             "plain_read_GBps": round(plain_read, 1),
+            "vendor_library_gemms": vendor,
             "quantize_GBps": gbps(["quantize 28672x8192", "quantize 8192x28672"]),
             "quantize_GBps_llama7b": gbps(["quantize 4096x4096", "quantize 11008x4096"]),
             "quantize_GBps_gemm_14336x4096": gbps(["quantize 14336x4096"]),
