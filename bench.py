@@ -632,6 +632,16 @@ def vendor_gemms(dev):
     us = median_us(lambda: torch.matmul(a16, b16.t()))
     out["bf16_TFLOPs"] = round(2 * m * n * k / us / 1e6, 1)
     out["shape"] = f"{m}x{n}x{k} (torch._int_mm / torch.matmul)"
+    # the dense bf16 product the W4A16 GEMM replaces: 14336x4096 bf16 weights
+    # (four copies, 470 MB, rotated so that each call reads them from memory)
+    wd = [torch.randn(14336, 4096, device=dev, generator=g).to(torch.bfloat16) for _ in range(4)]
+    dense = {}
+    for mm in (16, 64, 256):
+        xd = torch.randn(mm, 4096, device=dev, generator=g).to(torch.bfloat16)
+        it = iter(range(1 << 30))
+        dense[f"M={mm}"] = round(median_us(lambda: torch.matmul(xd, wd[next(it) % 4].t())), 2)
+    out["dense_bf16_gemm_14336x4096_us"] = dense
+    del wd
     return out
 
 
