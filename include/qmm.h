@@ -435,16 +435,18 @@ int llm_int8_gemm(const void* X, int x_dtype, const int8_t* qW, const float* w_s
  * W x = (W diag(s)) (diag(s)^-1 x).  For each alpha of a grid:
  *   mag_j = max(mean_t |X[t, j]|, 1e-8)            (fp64; its sum over the
  *           tokens is exact, so the same in any order, while a channel's
- *           nonzero |x| span less than 2^(45 - log2 T) in ratio)
+ *           nonzero |x| span less than 2^(42 - log2 T) in ratio)
  *   s     = mag^alpha / sqrt(max_j mag_j^alpha * min_j mag_j^alpha)
  *                                                   (fp64, stored in fp32)
  *   codes = quantize_groupwise(fl32(W diag(s)))    (INT4, groups of 128)
- *   err   = || X W^T - bf16(fl32(X diag(s)^-1)) W_hat^T ||_F^2 over the T
+ *   err   = || X W^T - h16(fl32(X diag(s)^-1)) W_hat^T ||_F^2 over the T
  *           calibration tokens, in fp64 (the output error as the quantized
  *           layer computes it: the inverse scaling folded into its 16-bit
- *           input; X W^T by a bf16 product with fp32 accumulation);
+ *           input, h16 = rounding to X's type, binary16 saturating at
+ *           65504; X W^T by a 16-bit product with fp32 accumulation);
  * the first alpha of the smallest error is kept.
- * W : [N, K] QMM_BF16; X : [T, K] QMM_BF16 calibration activations.
+ * W : [N, K] and X : [T, K] calibration activations, both QMM_BF16 or both
+ * QMM_F16.
  * alphas : HOST array of n_alpha (1 .. 64) values in [0, 1] (the listing's
  *          grid is 0, 0.1, .., 1).
  * Outputs (device): codes / scales / zeros of W diag(s_best) in the INT4
@@ -452,8 +454,9 @@ int llm_int8_gemm(const void* X, int x_dtype, const int8_t* qW, const float* w_s
  * or folds it into the previous operation); err [n_alpha] fp64; best
  * (int64, the chosen index).  Nothing is copied back to the host.
  * Errors, all found before any launch: QMM_EINVAL for a null pointer, a
- * non-positive size or an alpha outside [0, 1]; QMM_EUNSUPPORTED for fp16 or
- * fp32 operands, K % 128 != 0 or more than 64 alphas; QMM_ERANGE for
+ * non-positive size or an alpha outside [0, 1]; QMM_EUNSUPPORTED for fp32
+ * operands, W and X of different types, K % 128 != 0 or more than 64
+ * alphas; QMM_ERANGE for
  * K > 2^22, N >= 2^31 or T > 2^21; QMM_EALIGN for W, X, codes not 16-byte
  * aligned;
  * QMM_EWORKSPACE for a workspace smaller than awq_workspace_bytes(N, K, T,

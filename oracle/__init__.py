@@ -75,7 +75,7 @@ def lib(parallel: bool = False) -> ctypes.CDLL:
             "oq_fp8_quantize": [P, I64, I64, I64, P, P],
             "oq_fp8_matmul_nt": [P, P, I64, I64, I64, P],
             "oq_llm_int8": [P, I64, I64, P, P, I64, F, I64, I, P, P, P, P, P],
-            "oq_awq_search": [P, P, I64, I64, I64, P, I64, P, P, P, P, P, P],
+            "oq_awq_search": [P, P, I64, I64, I64, P, I64, P, P, P, P, P, P, I],
             "oq_awq_factors": [P, I64, I64, P, I64, P],
         }
         for name, argtypes in sigs.items():
@@ -493,10 +493,10 @@ def llm_int8_reference(x, qw, b, threshold: float, max_outliers=None, x_dtype: s
 AWQ_ALPHAS = np.linspace(0.0, 1.0, 11)   # the [QS] awq listing's grid, its values to the last bit
 
 
-def awq_search_reference(w, x, alphas=None, parallel: bool = False):
+def awq_search_reference(w, x, alphas=None, parallel: bool = False, x_dtype: str = "bf16"):
     """AWQ's scaling search for weights w [N, K] and calibration activations
-    x [T, K] (the 16-bit values as float32), INT4 groups of 128 (readings R32,
-    R33).  Returns (err fp64 [len(alphas)], best index, s_best f32 [K], the
+    x [T, K] (the 16-bit values as float32; x_dtype, "bf16" or "f16", is the
+    type X / s is rounded to), INT4 groups of 128 (readings R32, R33).  Returns (err fp64 [len(alphas)], best index, s_best f32 [K], the
     codes q uint8 [N, K], scales f32 [N, K/128] and zeros uint8 [N, K/128] of
     W diag(s_best)).  parallel=True runs the OpenMP build (the same loops per
     output, the products' rows split over threads)."""
@@ -505,6 +505,7 @@ def awq_search_reference(w, x, alphas=None, parallel: bool = False):
     n, k = w.shape
     t, k2 = x.shape
     assert k == k2 and k % 128 == 0
+    assert x_dtype in ("bf16", "f16")
     a = np.ascontiguousarray(AWQ_ALPHAS if alphas is None else alphas, np.float64).reshape(-1)
     err = np.empty(a.size, np.float64)
     best = np.zeros(1, np.int64)
@@ -513,7 +514,7 @@ def awq_search_reference(w, x, alphas=None, parallel: bool = False):
     sc = np.empty((n, k // 128), np.float32)
     z = np.empty((n, k // 128), np.uint8)
     _check(lib(parallel).oq_awq_search(_p(w), _p(x), n, k, t, _p(a), a.size, _p(err), _p(best), _p(s), _p(q), _p(sc),
-                               _p(z)), "awq_search")
+                                       _p(z), 1 if x_dtype == "f16" else 0), "awq_search")
     return err, int(best[0]), s, q, sc, z
 
 

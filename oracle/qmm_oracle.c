@@ -57,7 +57,9 @@
  *  R32 AWQ's error for a candidate alpha is the layer's output error as the
  *      quantized layer computes it: || X W^T - X_s W_hat^T ||_F^2, X_s the
  *      activations divided by the scales (the inverse scaling folded into
- *      the layer's 16-bit input: fp32 quotient, then rounded to bf16) and
+ *      the layer's 16-bit input: fp32 quotient, then rounded to the
+ *      activations' own type, bf16 or binary16, binary16 saturating at
+ *      65504 as in R24) and
  *      W_hat the dequantized codes of W diag(s); the sums in fp64.  (The
  *      [QS] listing evaluates the same quantity as sum((D H) * D) with
  *      D = W - W_hat / s and H from the calibration inputs.)
@@ -685,7 +687,7 @@ int oq_awq_factors(const float* x, int64_t k, int64_t t, const double* alphas, i
 
 int oq_awq_search(const float* w, const float* x, int64_t n, int64_t k, int64_t t, const double* alphas,
                   int64_t n_alpha, double* err, int64_t* best, float* s_best, uint8_t* q, float* scales,
-                  uint8_t* zeros)
+                  uint8_t* zeros, int x_f16)
 {
     if (!w || !x || !alphas || !err || !best || !s_best || !q || !scales || !zeros) return OQ_BAD_ARG;
     if (n <= 0 || k <= 0 || t <= 0 || n_alpha <= 0 || k % 128 != 0) return OQ_BAD_ARG;
@@ -713,7 +715,8 @@ int oq_awq_search(const float* w, const float* x, int64_t n, int64_t k, int64_t 
         oq_asym_quantize(ws, n, k, 128, 4, qa, sa, za);
         oq_asym_dequantize(qa, sa, za, n, k, 128, what);
         oq_scale_columns_div(x, s, t, k, xs);       /* diag(s)^-1 folded into the 16-bit input (R32) */
-        for (int64_t i = 0; i < t * k; ++i) xs[i] = bf16_round(xs[i]);
+        for (int64_t i = 0; i < t * k; ++i)
+            xs[i] = x_f16 ? oq_f16_bits_to_f32(oq_f32_to_f16_bits(xs[i])) : bf16_round(xs[i]);
         oq_matmul_nt_f64(xs, what, t, n, k, yq);
         double e = 0.0;
         for (int64_t i = 0; i < t * n; ++i) {

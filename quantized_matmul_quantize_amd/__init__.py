@@ -657,13 +657,13 @@ def awq_workspace_bytes(N: int, K: int, T: int, n_alpha: int) -> int:
 
 def awq_search(W: torch.Tensor, X: torch.Tensor, alphas: Sequence[float] = AWQ_ALPHAS,
                workspace: Optional[torch.Tensor] = None):
-    """AWQ on bf16 weights W [N, K] with bf16 calibration activations X [T, K]:
-    returns (codes, scales, zeros) of W diag(s_best) in the INT4 group-128
-    format, smooth [K] (= s_best), err fp64 [len(alphas)] and best (int64
-    [1]), all on the device."""
-    _req(W, "W", (torch.bfloat16,), ndim=2)
+    """AWQ on 16-bit weights W [N, K] with calibration activations X [T, K] of
+    the same type (bf16 or fp16): returns (codes, scales, zeros) of
+    W diag(s_best) in the INT4 group-128 format, smooth [K] (= s_best), err
+    fp64 [len(alphas)] and best (int64 [1]), all on the device."""
+    _req(W, "W", _HALVES, ndim=2)
     N, K = W.shape
-    _req(X, "X", (torch.bfloat16,), shape=(None, K))
+    _req(X, "X", (W.dtype,), shape=(None, K))
     T = X.shape[0]
     a = [float(v) for v in alphas]
     if not 1 <= len(a) <= 64:

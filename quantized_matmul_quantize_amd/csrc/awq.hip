@@ -14,16 +14,17 @@
 //            at once, before the loop);
 //   codes  = group-128 INT4 of fl32(W diag(s)), the product formed inside
 //            the quantizer (no fp32 copy of the scaled weights);
-//   X_s    = bf16(fl32(X / s))  (the inverse scaling folded into the input);
+//   X_s    = fl32(X / s) rounded to X's 16-bit type, bf16 or binary16
+//            (the inverse scaling folded into the input);
 //   Y_q    = w4a16_gemm(X_s, codes);
-//   err    = sum (X W^T - Y_q)^2 in fp64, X W^T once by the bf16 product;
+//   err    = sum (X W^T - Y_q)^2 in fp64, X W^T once by the 16-bit product;
 // then the first alpha of the smallest error is selected, and W diag(s_best)
 // quantized into the caller's format buffers.  mag_j = max(mean_t |x_j|,
 // 1e-8) in fp64: the sum of |x| over the tokens is taken over slices of 32
 // rows and the slices in order; it is exact (so equal to any other order's)
-// while each channel's nonzero |x| span less than 2^(45 - log2 T) in ratio
-// (bf16 values carry 8 significant bits), true of any activations with an
-// ordinary dynamic range.
+// while each channel's nonzero |x| span less than 2^(42 - log2 T) in ratio
+// (16-bit values carry at most 11 significant bits, fp64 53), true of any
+// activations with an ordinary dynamic range.
 
 #include "qmm_device.h"
 
@@ -39,8 +40,29 @@ struct AlphaGrid {
   double a[kMaxAlphas];
 };
 
+// The two 16-bit halves of a word as fp32 (XDT: QMM_BF16 or QMM_F16).
+template <int XDT>
+__device__ __forceinline__ float h16_lo(uint32_t w) {
+  if constexpr (XDT == QMM_F16) return f16lo_to_f32(w);
+  else return bf16lo_to_f32(w);
+}
+template <int XDT>
+__device__ __forceinline__ float h16_hi(uint32_t w) {
+  if constexpr (XDT == QMM_F16) return f16hi_to_f32(w);
+  else return bf16hi_to_f32(w);
+}
+
+// fl32 v rounded to the 16-bit type (nearest even; binary16 saturating at its
+// largest finite value), as bits in the low half.
+template <int XDT>
+__device__ __forceinline__ uint32_t h16_bits(float v) {
+  if constexpr (XDT == QMM_F16) return f32_to_f16_bits(__builtin_amdgcn_fmed3f(v, -65504.0f, 65504.0f));
+  else return f32_to_bf16_bits(v);
+}
+
 // Partial sums of |x| over rows [kMagRows b, +kMagRows) of each column,
 // fp64; a thread takes 8 consecutive columns (one 16-byte load per row).
+template <int XDT>
 __global__ __launch_bounds__(256) void awq_mag_partial_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t K,
                                                               double* __restrict__ part) {
   const int64_t j0 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
@@ -57,8 +79,8 @@ __global__ __launch_bounds__(256) void awq_mag_partial_kernel(const uint16_t* __
       const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        acc[2 * h] += static_cast<double>(fabsf(bf16lo_to_f32(w[h])));
-        acc[2 * h + 1] += static_cast<double>(fabsf(bf16hi_to_f32(w[h])));
+        acc[2 * h] += static_cast<double>(fabsf(h16_lo<XDT>(w[h])));
+        acc[2 * h + 1] += static_cast<double>(fabsf(h16_hi<XDT>(w[h])));
       }
     }
   }
@@ -143,7 +165,9 @@ __global__ __launch_bounds__(256) void awq_factor_kernel(const double* __restric
   if (j < K) s_all[blockIdx.y * K + j] = static_cast<float>(pbuf[blockIdx.y * K + j] / norm[blockIdx.y]);
 }
 
-// X_s = bf16(fl32(X / s)), correctly rounded division, eight values per thread.
+// X_s = h16(fl32(X / s)) in X's own 16-bit type, correctly rounded division,
+// eight values per thread.
+template <int XDT>
 __global__ __launch_bounds__(256) void awq_scale_x_kernel(const uint16_t* __restrict__ x, const float* __restrict__ s,
                                                           int64_t total8, int64_t K, uint16_t* __restrict__ out) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total8;
@@ -155,9 +179,9 @@ __global__ __launch_bounds__(256) void awq_scale_x_kernel(const uint16_t* __rest
     uint32_t o[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float lo = bf16lo_to_f32(a[h]) / s[j + 2 * h];
-      const float hi = bf16hi_to_f32(a[h]) / s[j + 2 * h + 1];
-      o[h] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+      const float lo = h16_lo<XDT>(a[h]) / s[j + 2 * h];
+      const float hi = h16_hi<XDT>(a[h]) / s[j + 2 * h + 1];
+      o[h] = h16_bits<XDT>(lo) | (h16_bits<XDT>(hi) << 16);
     }
     *reinterpret_cast<u32x4*>(out + e) = u32x4{o[0], o[1], o[2], o[3]};
   }
@@ -280,9 +304,10 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   if (!W || !X || !alphas || !codes || !scales || !zeros || !smooth || !err || !best) return QMM_EINVAL;
   if (N <= 0 || K <= 0 || T <= 0 || n_alpha <= 0) return QMM_EINVAL;
   if (K % kGroup != 0) return QMM_EUNSUPPORTED;
-  if (w_dtype != QMM_BF16 || x_dtype != QMM_BF16)
-    return (w_dtype == QMM_F16 || w_dtype == QMM_F32 || x_dtype == QMM_F16 || x_dtype == QMM_F32) ? QMM_EUNSUPPORTED
-                                                                                                  : QMM_EINVAL;
+  const bool h16w = w_dtype == QMM_BF16 || w_dtype == QMM_F16;
+  const bool h16x = x_dtype == QMM_BF16 || x_dtype == QMM_F16;
+  if (!(h16w || w_dtype == QMM_F32) || !(h16x || x_dtype == QMM_F32)) return QMM_EINVAL;
+  if (!h16w || !h16x || w_dtype != x_dtype) return QMM_EUNSUPPORTED;   // fp32, or two 16-bit types
   if (n_alpha > kMaxAlphas) return QMM_EUNSUPPORTED;
   for (int64_t a = 0; a < n_alpha; ++a)
     if (!(alphas[a] >= 0.0 && alphas[a] <= 1.0)) return QMM_EINVAL;
@@ -318,8 +343,9 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   // channel magnitudes and every alpha's factors
   const int64_t slices = ceil_div(T, kMagRows);
   const unsigned nb = static_cast<unsigned>(ceil_div(K, 256));
-  awq_mag_partial_kernel<<<dim3(static_cast<unsigned>(ceil_div(K, 2048)), static_cast<unsigned>(slices)), 256, 0, s>>>(
-      x, T, K, mpart);
+  const dim3 mgrid(static_cast<unsigned>(ceil_div(K, 2048)), static_cast<unsigned>(slices));
+  if (x_dtype == QMM_F16) awq_mag_partial_kernel<QMM_F16><<<mgrid, 256, 0, s>>>(x, T, K, mpart);
+  else awq_mag_partial_kernel<QMM_BF16><<<mgrid, 256, 0, s>>>(x, T, K, mpart);
   awq_mag_kernel<<<nb, 256, 0, s>>>(mpart, slices, T, K, mag);
   AlphaGrid grid{};
   for (int64_t a = 0; a < n_alpha; ++a) grid.a[a] = alphas[a];
@@ -329,18 +355,19 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   int st = launch_status();
   if (st != QMM_OK) return st;
   // the full-precision output X W^T
-  launch_bf16_gemm(x, w, T, N, K, yref, s);
+  launch_h16_gemm(x, w, x_dtype, T, N, K, yref, s);
   st = launch_status();
   if (st != QMM_OK) return st;
 
   const int64_t xn8 = T * K / 8;
   for (int64_t a = 0; a < n_alpha; ++a) {
     const float* sa = s_all + a * K;
-    launch_quantize_colscaled(w, sa, N, K, qc, qs, qz, s);
-    awq_scale_x_kernel<<<grid_for(xn8), 256, 0, s>>>(x, sa, xn8, K, xs);
+    launch_quantize_colscaled(w, w_dtype, sa, N, K, qc, qs, qz, s);
+    if (x_dtype == QMM_F16) awq_scale_x_kernel<QMM_F16><<<grid_for(xn8), 256, 0, s>>>(x, sa, xn8, K, xs);
+    else awq_scale_x_kernel<QMM_BF16><<<grid_for(xn8), 256, 0, s>>>(x, sa, xn8, K, xs);
     st = launch_status();
     if (st != QMM_OK) return st;
-    st = w4a16_gemm(qc, qs, qz, N, K, kGroup, xs, QMM_BF16, T, yq, QMM_F32, stream);
+    st = w4a16_gemm(qc, qs, qz, N, K, kGroup, xs, x_dtype, T, yq, QMM_F32, stream);
     if (st != QMM_OK) return st;
     awq_sqerr_kernel<<<kErrBlocks, 256, 0, s>>>(yref, yq, T * N, epart + a * kErrBlocks);
     st = launch_status();
@@ -350,6 +377,6 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   st = launch_status();
   if (st != QMM_OK) return st;
   // the chosen alpha's weights in the caller's format
-  launch_quantize_colscaled(w, s_copy, N, K, codes, scales, zeros, s);
+  launch_quantize_colscaled(w, w_dtype, s_copy, N, K, codes, scales, zeros, s);
   return launch_status();
 }

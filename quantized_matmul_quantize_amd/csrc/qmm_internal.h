@@ -28,17 +28,17 @@ int dequantize_fmt(const uint8_t* codes, const void* scales, const uint8_t* zero
 int matmul_fmt(const uint8_t* codes, const void* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
                int bits, int scale_dtype, const void* x, int x_dtype, int64_t M, void* y, int y_dtype, void* stream);
 
-// Group-128 asymmetric INT4 of fl32(W[n, k] * colscale[k]) for bf16 W
-// (quantize.hip, the quantizer kernels with a per-column factor), into the
-// format of quantize_groupwise.  K % 128 == 0; W, colscale, codes 16-byte
-// aligned.  No argument checks: the caller's.
-void launch_quantize_colscaled(const uint16_t* W, const float* colscale, int64_t N, int64_t K, uint8_t* codes,
-                               float* scales, uint8_t* zeros, hipStream_t s);
+// Group-128 asymmetric INT4 of fl32(W[n, k] * colscale[k]) for 16-bit W
+// (w_dtype QMM_BF16 or QMM_F16; quantize.hip, the quantizer kernels with a
+// per-column factor), into the format of quantize_groupwise.  K % 128 == 0;
+// W, colscale, codes 16-byte aligned.  No argument checks: the caller's.
+void launch_quantize_colscaled(const uint16_t* W, int w_dtype, const float* colscale, int64_t N, int64_t K,
+                               uint8_t* codes, float* scales, uint8_t* zeros, hipStream_t s);
 
-// Plain product Y[M, N] = A[M, K] B[N, K]^T of bf16 operands in fp32
-// (w8a8.hip, the INT8 GEMM's tiles on bf16 matrix instructions).  K % 32 == 0,
-// rows 16-byte aligned, 256 * 2K < 2^31.
-void launch_bf16_gemm(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K, float* Y,
-                      hipStream_t s);
+// Plain product Y[M, N] = A[M, K] B[N, K]^T of 16-bit operands (dtype
+// QMM_BF16 or QMM_F16) in fp32 (w8a8.hip, the INT8 GEMM's tiles on 16-bit
+// matrix instructions).  K % 32 == 0, rows 16-byte aligned, 256 * 2K < 2^31.
+void launch_h16_gemm(const uint16_t* A, const uint16_t* B, int dtype, int64_t M, int64_t N, int64_t K, float* Y,
+                     hipStream_t s);
 
 }  // namespace qmm

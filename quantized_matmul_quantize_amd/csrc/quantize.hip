@@ -442,24 +442,35 @@ int quantize_launch(const void* W, int w_dtype, int64_t N, int64_t K, int group,
 
 }  // namespace
 
-void launch_quantize_colscaled(const uint16_t* W, const float* colscale, int64_t N, int64_t K, uint8_t* codes,
-                               float* scales, uint8_t* zeros, hipStream_t s) {
+namespace {
+
+template <int DT>
+void launch_colscaled_t(const uint8_t* w, const float* colscale, int64_t N, int64_t K, uint8_t* codes, float* scales,
+                        uint8_t* zeros, hipStream_t s) {
   const int64_t G = K / kGroup;
-  const uint8_t* w = reinterpret_cast<const uint8_t*>(W);
   const dim3 block(256);
   if (G % 2 == 0) {
     const int64_t T = N * G;
     int64_t blocks = ceil_div(ceil_div(T, 16), 4);
     const int64_t cap = static_cast<int64_t>(device_cus()) * 16;
     if (blocks > cap) blocks = cap;
-    quantize_g128_lds_kernel<QMM_BF16, false, true><<<dim3(static_cast<unsigned>(blocks)), block, 0, s>>>(
+    quantize_g128_lds_kernel<DT, false, true><<<dim3(static_cast<unsigned>(blocks)), block, 0, s>>>(
         w, T, codes, scales, zeros, colscale, G);
     return;
   }
   const int64_t chunks_per_row = ceil_div(G, 4);
   const int64_t total = N * chunks_per_row;
-  quantize_g128_kernel<QMM_BF16, false, true><<<dim3(static_cast<unsigned>(chunk_grid(total))), block, 0, s>>>(
+  quantize_g128_kernel<DT, false, true><<<dim3(static_cast<unsigned>(chunk_grid(total))), block, 0, s>>>(
       w, K, G, chunks_per_row, total, reinterpret_cast<uint32_t*>(codes), scales, zeros, ceil_div(G, 2), colscale);
+}
+
+}  // namespace
+
+void launch_quantize_colscaled(const uint16_t* W, int w_dtype, const float* colscale, int64_t N, int64_t K,
+                               uint8_t* codes, float* scales, uint8_t* zeros, hipStream_t s) {
+  const uint8_t* w = reinterpret_cast<const uint8_t*>(W);
+  if (w_dtype == QMM_F16) launch_colscaled_t<QMM_F16>(w, colscale, N, K, codes, scales, zeros, s);
+  else launch_colscaled_t<QMM_BF16>(w, colscale, N, K, codes, scales, zeros, s);
 }
 
 }  // namespace qmm

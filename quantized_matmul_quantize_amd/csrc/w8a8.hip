@@ -405,13 +405,28 @@ __device__ __forceinline__ void mfma_frag(const i32x4& b, const i32x4& a, i32x4&
   acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a, acc, 0, 0, 0);
 }
 
-// BF16: the same 16-byte fragments of a 64-byte chunk hold 8 bf16 values
-// (32 k per chunk across the four lane groups), one
-// v_mfma_f32_16x16x32_bf16 per chunk -- the kernel's tiles, loads and LDS
-// layout are byte-based, so a 16-bit operand of K elements is a K * 2 byte row.
-__device__ __forceinline__ void mfma_frag(const i32x4& b, const i32x4& a, f32x4& acc) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b), __builtin_bit_cast(bf16x8_t, a),
-                                                acc, 0, 0, 0);
+// H16 = QMM_BF16 or QMM_F16: the same 16-byte fragments of a 64-byte chunk
+// hold 8 16-bit values (32 k per chunk across the four lane groups), one
+// v_mfma_f32_16x16x32_{bf16,f16} per chunk -- the kernel's tiles, loads and
+// LDS layout are byte-based, so a 16-bit operand of K elements is a K * 2
+// byte row.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+template <int H16>
+__device__ __forceinline__ void mfma_frag16(const i32x4& b, const i32x4& a, f32x4& acc) {
+  if constexpr (H16 == QMM_F16)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, b), __builtin_bit_cast(f16x8_t, a), acc,
+                                                 0, 0, 0);
+  else
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b), __builtin_bit_cast(bf16x8_t, a),
+                                                  acc, 0, 0, 0);
+}
+
+// One chunk's product: INT8 (int32 accumulators) or 16-bit operands (fp32).
+template <int H16, class Acc>
+__device__ __forceinline__ void mfma_chunk(const i32x4& b, const i32x4& a, Acc& acc) {
+  if constexpr (H16 != 0) mfma_frag16<H16>(b, a, acc);
+  else mfma_frag(b, a, acc);
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -453,13 +468,14 @@ __device__ __forceinline__ float x16_value(uint32_t u, int x_f16) {
   return x_f16 ? f16lo_to_f32(u) : bf16lo_to_f32(u);
 }
 
-template <int YDT, bool FP8 = false, bool OUTL = false, bool BF16 = false>
+template <int YDT, bool FP8 = false, bool OUTL = false, int H16 = 0>
 __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__ A, const float* __restrict__ ascale,
                                                        const int8_t* __restrict__ B, const float* __restrict__ bscale,
                                                        int64_t M, int64_t N, int64_t K, void* __restrict__ Y,
                                                        Outliers outl) {
-  static_assert(!(BF16 && (FP8 || OUTL)), "bf16 operands: the plain product");
-  using Acc = typename GemmAcc<FP8 || BF16>::type;
+  static_assert(H16 == 0 || ((H16 == QMM_BF16 || H16 == QMM_F16) && !FP8 && !OUTL),
+                "16-bit operands: the plain product");
+  using Acc = typename GemmAcc<FP8 || H16 != 0>::type;
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -562,14 +578,14 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = mw + 16 * i + (lane & 15);
-    as[i] = (YDT == QMM_I32 || BF16) ? 1.0f : ascale[m < M ? m : M - 1];
+    as[i] = (YDT == QMM_I32 || H16 != 0) ? 1.0f : ascale[m < M ? m : M - 1];
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t n = nw + 16 * j + 4 * (lane >> 4) + r;
-      bs[j][r] = (YDT == QMM_I32 || BF16) ? 1.0f : bscale[n < N ? n : N - 1];
+      bs[j][r] = (YDT == QMM_I32 || H16 != 0) ? 1.0f : bscale[n < N ? n : N - 1];
     }
 
   // Outlier operands of this tile (the first kOutlLds columns): thread t
@@ -648,7 +664,7 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mfma_frag(fb0[j], fa0[i], acc[i][j]);
+      for (int j = 0; j < 4; ++j) mfma_chunk<H16>(fb0[j], fa0[i], acc[i][j]);
 #pragma unroll
     for (int g = 0; g < 6; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
@@ -666,7 +682,7 @@ __global__ __launch_bounds__(512) void i8_gemm_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mfma_frag(fb1[j], fa1[i], acc[i][j]);
+      for (int j = 0; j < 4; ++j) mfma_chunk<H16>(fb1[j], fa1[i], acc[i][j]);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
@@ -857,18 +873,18 @@ int check_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float*
   return QMM_OK;
 }
 
-template <int YDT, bool FP8 = false, bool OUTL = false, bool BF16 = false>
+template <int YDT, bool FP8 = false, bool OUTL = false, int H16 = 0>
 void launch_gemm_t(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
                    int64_t K, void* Y, hipStream_t s, Outliers outl = Outliers{nullptr, nullptr, nullptr, 0}) {
   // 144 KiB of dynamic LDS (+12 KiB of outlier operands); the attribute is
   // cheap to set and idempotent, so it is set on every launch (no per-device
   // bookkeeping).
   constexpr size_t lds = kGemmLds + (OUTL ? kOutlLdsBytes : 0);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&i8_gemm_kernel<YDT, FP8, OUTL, BF16>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&i8_gemm_kernel<YDT, FP8, OUTL, H16>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   const int64_t tiles = ceil_div(M, kBM) * ceil_div(N, kBN);
   const dim3 grid(static_cast<unsigned>(ceil_div(tiles, kXcds) * kXcds));
-  i8_gemm_kernel<YDT, FP8, OUTL, BF16><<<grid, dim3(512), lds, s>>>(qX, xs, qW, ws, M, N, K, Y, outl);
+  i8_gemm_kernel<YDT, FP8, OUTL, H16><<<grid, dim3(512), lds, s>>>(qX, xs, qW, ws, M, N, K, Y, outl);
 }
 
 void launch_gemm(const int8_t* qX, const float* xs, const int8_t* qW, const float* ws, int64_t M, int64_t N,
@@ -890,10 +906,14 @@ void launch_gemm_fp8(const uint8_t* qX, const float* xs, const uint8_t* qW, cons
 
 }  // namespace
 
-void launch_bf16_gemm(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K, float* Y,
-                      hipStream_t s) {
-  launch_gemm_t<QMM_F32, false, false, true>(reinterpret_cast<const int8_t*>(A), nullptr,
-                                             reinterpret_cast<const int8_t*>(B), nullptr, M, N, 2 * K, Y, s);
+void launch_h16_gemm(const uint16_t* A, const uint16_t* B, int dtype, int64_t M, int64_t N, int64_t K, float* Y,
+                     hipStream_t s) {
+  if (dtype == QMM_F16)
+    launch_gemm_t<QMM_F32, false, false, QMM_F16>(reinterpret_cast<const int8_t*>(A), nullptr,
+                                                  reinterpret_cast<const int8_t*>(B), nullptr, M, N, 2 * K, Y, s);
+  else
+    launch_gemm_t<QMM_F32, false, false, QMM_BF16>(reinterpret_cast<const int8_t*>(A), nullptr,
+                                                   reinterpret_cast<const int8_t*>(B), nullptr, M, N, 2 * K, Y, s);
 }
 }  // namespace qmm
 

@@ -986,9 +986,31 @@ def check_awq_listing_error():
         assert abs(err[0] - e) <= 1e-2 * e, (alpha, err[0], e)
 
 
+def check_awq_f16_input():
+    # binary16 activations (R32: X / s rounded to the activations' own type):
+    # at alpha = 0 nothing is rounded and the error is numpy's
+    # ||X (W - W_hat)^T||^2 exactly as in bf16; at alpha = 1/2 the binary16
+    # rounding (3 more bits than bf16) leaves the error closer to the
+    # listing's unrounded sum((D H) * D) than the bf16 rounding does
+    w, x = _awq_case(9, salient=5)
+    x16 = workloads.to_dtype(x, "f16").float().numpy()
+    err, best, s, q, sc, z = oracle.awq_search_reference(w, x16, alphas=[0.0], x_dtype="f16")
+    w_hat = (q.astype(np.float64) - np.repeat(z, 128, axis=1)) * np.repeat(sc.astype(np.float64), 128, axis=1)
+    d = x16.astype(np.float64) @ (w.astype(np.float64) - w_hat).T
+    assert np.isclose(err[0], np.sum(d * d), rtol=1e-6)
+    h = x16.astype(np.float64).T @ x16.astype(np.float64)
+    e16, _, s, q, sc, z = oracle.awq_search_reference(w, x16, alphas=[0.5], x_dtype="f16")
+    eb, _, sb, qb, _, _ = oracle.awq_search_reference(w, x16, alphas=[0.5], x_dtype="bf16")
+    assert np.array_equal(s, sb) and np.array_equal(q, qb)      # the factors and codes do not depend on it
+    w_hat = (q.astype(np.float64) - np.repeat(z, 128, axis=1)) * np.repeat(sc.astype(np.float64), 128, axis=1)
+    dd = w.astype(np.float64) - w_hat / s.astype(np.float64)[None, :]
+    e = float(np.sum((dd @ h) * dd))
+    assert abs(e16[0] - e) < abs(eb[0] - e), (e16[0], eb[0], e)
+
+
 ALL_CHECKS = [
     check_awq_alpha0_is_round_to_nearest, check_awq_uniform_magnitudes, check_awq_salient_channel,
-    check_awq_scales_closed_form, check_awq_power_of_two_invariance, check_awq_listing_error,
+    check_awq_scales_closed_form, check_awq_power_of_two_invariance, check_awq_listing_error, check_awq_f16_input,
     check_llm_int8_special_cases, check_llm_int8_decomposition, check_llm_int8_cap_and_permutation,
     check_llm_int8_accuracy,
     check_e4m3_conversion, check_fp8_listing, check_fp8_product,

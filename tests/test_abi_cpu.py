@@ -236,7 +236,8 @@ def test_awq_workspace_and_argument_errors():
                         k.get("al", ctypes.cast(al, ctypes.c_void_p)), k.get("na", 2), P, P, P, P, P, P,
                         k.get("ws", P), k.get("wsb", need), None]
     assert g(*args(W=None)) == EINVAL
-    assert g(*args(wdt=F16)) == EUNSUP
+    assert g(*args(wdt=F16)) == EUNSUP                                   # bf16 X with fp16 W
+    assert g(*args(wdt=F32, xdt=F32)) == EUNSUP
     assert g(*args(xdt=F32)) == EUNSUP
     assert g(*args(wdt=I32)) == EINVAL
     assert g(*args(K=100)) == EUNSUP

@@ -90,7 +90,8 @@ def test_llm_int8_checks():
 
 def test_awq_checks():
     w, x = t((8, 256), bf16), t((4, 256), bf16)
-    raises(lambda: qmm.awq_search(t((8, 256), f16), x), "W has dtype")
+    raises(lambda: qmm.awq_search(t((8, 256), f32), x), "W has dtype")
+    raises(lambda: qmm.awq_search(t((8, 256), f16), x), "X has dtype")          # two 16-bit types
     raises(lambda: qmm.awq_search(w, t((4, 128), bf16)), "X has shape")
     raises(lambda: qmm.awq_search(t((8, 200), bf16), t((4, 200), bf16)), "multiple of 128")
     raises(lambda: qmm.awq_search(w, x, alphas=[]), "1 to 64 alphas")

@@ -5,8 +5,10 @@ alpha's calibration output error within the tolerance of its fp32-accumulated
 products, and the chosen alpha the oracle's (or one whose oracle error ties
 it within that tolerance).  Small ragged shapes, a salient channel, uniform
 magnitudes (every alpha the same, so the first is kept), one alpha (plain
-round-to-nearest), one calibration token, a reversed grid, and the
-4096 x 4096 layer with 2048 calibration tokens."""
+round-to-nearest), one calibration token, a reversed grid, binary16
+activations (with X / s saturating at 65504), the 896 x 4864 layer shape of
+the pages' measurements and the 4096 x 4096 layer with 2048 calibration
+tokens."""
 import numpy as np
 import pytest
 import torch
@@ -82,12 +84,22 @@ def _check_format(w, smooth, codes, scales, zeros, what, rows=None):
     assert bits_equal(codes, rc), f"{what} codes: {first_diff(codes, rc)}"
 
 
-def _check(w, x, alphas, what, parallel=False):
+def _xdt(x):
+    return "f16" if x.dtype == torch.float16 else "bf16"
+
+
+def _check(w, x, alphas, what, parallel=False, err_rtol=None):
     codes, scales, zeros, smooth, err, best = _run(w, x, alphas, what)
     xf = x.float().numpy()
-    rerr, rbest, rs, _, _, _ = oracle.awq_search_reference(w.float().numpy(), xf, alphas, parallel=parallel)
+    rerr, rbest, rs, _, _, _ = oracle.awq_search_reference(w.float().numpy(), xf, alphas, parallel=parallel,
+                                                           x_dtype=_xdt(x))
     assert best == int(np.argmin(err)), f"{what}: best {best} is not the first minimum of {err}"
-    tol = _check_err(err, rerr, w, x, what)
+    if err_rtol is None:
+        tol = _check_err(err, rerr, w, x, what)
+    else:
+        assert np.all(np.isfinite(err)), f"{what}: err {err}"
+        tol = err_rtol * np.abs(rerr)
+        assert np.all(np.abs(err - rerr) <= tol), f"{what} err: got {err} want {rerr}"
     if best != rbest:   # a near tie: the GPU's choice must be as good within the tolerance
         assert rerr[best] <= rerr[rbest] + tol[best] + tol[rbest], (what, best, rbest, rerr)
     s_all = oracle.awq_factors_reference(xf, alphas)
@@ -98,15 +110,43 @@ def _check(w, x, alphas, what, parallel=False):
     return err, best
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("n,k,t,seed", [(48, 256, 40, 1), (200, 640, 100, 2), (129, 1152, 67, 3), (1, 128, 1, 4)])
-def test_awq_ragged_shapes(n, k, t, seed):
-    w, x = _case(n, k, t, seed, spread=(4.0, 58.0))
-    _check(w, x, list(qmm.AWQ_ALPHAS), f"ragged n={n} k={k} t={t}")
+def test_awq_ragged_shapes(n, k, t, seed, dtype):
+    w, x = _case(n, k, t, seed, spread=(4.0, 58.0), dtype=dtype)
+    _check(w, x, list(qmm.AWQ_ALPHAS), f"ragged n={n} k={k} t={t} {dtype}")
 
 
-def test_awq_salient_channel():
-    w, x = _case(96, 384, 64, 5, salient=(17,))
-    err, best = _check(w, x, list(qmm.AWQ_ALPHAS), "salient channel 17")
+def test_awq_f16_input_saturates():
+    # binary16: X / s past 65504 saturates there (R32 with R24).  Channel 0
+    # holds 60000 in every token (the largest magnitude), channel 1 +-0.001
+    # (the smallest), channel 2 a single 65000 among 9000 tokens: at alpha = 1
+    # its factor is mag_2 / sqrt(max * min) ~ 0.93, so 65000 / s ~ 70000.
+    t, k = 9000, 128
+    g = np.random.Generator(np.random.PCG64(11))
+    w = workloads.to_dtype(workloads.gaussian(g, (16, k), 0.02), "f16")
+    x = workloads.gaussian(g, (t, k), 1.0)
+    x[:, 0] = np.float32(60000.0)
+    x[:, 1] = np.where(g.random(t) < 0.5, -1.0, 1.0).astype(np.float32) * np.float32(0.001)
+    x[:, 2] = 0.0
+    x[17, 2] = np.float32(65000.0)
+    x = workloads.to_dtype(x, "f16")
+    s1 = oracle.awq_factors_reference(x.float().numpy(), [1.0])[0]
+    assert 65000.0 / s1[2] > 65504.0
+    # Factors, codes and choice bit for bit; the error finite (an infinite
+    # X / s would make it inf or NaN) and within 1e-2: the one 65504 entry
+    # times the binary16 products' offset of 1024 (the codes enter as 1024 + q,
+    # the zero-point's share taken back from the row sum) puts ~6.8e7 into an
+    # fp32 partial sum whose rounding (8 at that size) the group scale of ~20
+    # then carries into that token's outputs, far past the bound derived for
+    # ordinary activations.
+    _check(w, x, [1.0, 0.5], "binary16 saturation", err_rtol=1e-2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_awq_salient_channel(dtype):
+    w, x = _case(96, 384, 64, 5, salient=(17,), dtype=dtype)
+    err, best = _check(w, x, list(qmm.AWQ_ALPHAS), f"salient channel 17 {dtype}")
     assert best > 0 and err[best] < err[0]
 
 

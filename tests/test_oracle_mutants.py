@@ -62,6 +62,8 @@ MUTANTS = [
     ("awq_magnitude_max", "for (int64_t r = 0; r < t; ++r) acc += fabs((double)x[r * k + j]);",
      "for (int64_t r = 0; r < t; ++r) acc = fmax(acc, fabs((double)x[r * k + j]));"),
     ("awq_alpha_inverted", "p[j] = pow(mag[j], alphas[a]);", "p[j] = pow(mag[j], 1.0 - alphas[a]);"),
+    ("awq_f16_input_rounded_bf16", "xs[i] = x_f16 ? oq_f16_bits_to_f32(oq_f32_to_f16_bits(xs[i])) : bf16_round(xs[i]);",
+     "xs[i] = bf16_round(xs[i]);"),
     ("codes3_halves_swapped", "const int pos = 3 * (rr / 2) + 16 * (rr % 2);",
      "const int pos = 3 * (rr / 2) + 16 * ((rr + 1) % 2);"),
     ("codes3_last_pair_words_reversed", "w[t] |= (uint32_t)((e[30] >> t) & 1u) << 15;",
