@@ -187,19 +187,35 @@ __global__ __launch_bounds__(256) void awq_scale_x_kernel(const uint16_t* __rest
   }
 }
 
-// Partial sums of (a - b)^2 in fp64: block b takes a fixed contiguous range,
-// each thread a fixed stride within it, and the block tree is fixed, so the
-// result does not depend on scheduling.
+// Partial sums of (a - b)^2 in fp64: block b takes a fixed contiguous range
+// (a multiple of 4 elements long, so 16-byte aligned), each thread four
+// consecutive elements at a fixed stride within it, and the block tree is
+// fixed, so the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void awq_sqerr_kernel(const float* __restrict__ a, const float* __restrict__ b,
                                                         int64_t n, double* __restrict__ part) {
   __shared__ double red[256];
-  const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t per = (n + 4 * gridDim.x - 1) / (4 * gridDim.x) * 4;
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * per;
   const int64_t i1 = (i0 + per < n) ? i0 + per : n;
   double acc = 0.0;
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += blockDim.x) {
-    const double d = static_cast<double>(a[i]) - static_cast<double>(b[i]);
-    acc += d * d;
+  for (int64_t i = i0 + 4 * threadIdx.x; i < i1; i += 4 * blockDim.x) {
+    if (i + 4 <= i1) {
+      const f32x4 va = *reinterpret_cast<const f32x4*>(a + i);
+      const f32x4 vb = *reinterpret_cast<const f32x4*>(b + i);
+      const double d0 = static_cast<double>(va.x) - static_cast<double>(vb.x);
+      const double d1 = static_cast<double>(va.y) - static_cast<double>(vb.y);
+      const double d2 = static_cast<double>(va.z) - static_cast<double>(vb.z);
+      const double d3 = static_cast<double>(va.w) - static_cast<double>(vb.w);
+      acc += d0 * d0;
+      acc += d1 * d1;
+      acc += d2 * d2;
+      acc += d3 * d3;
+    } else {
+      for (int64_t e = i; e < i1; ++e) {
+        const double d = static_cast<double>(a[e]) - static_cast<double>(b[e]);
+        acc += d * d;
+      }
+    }
   }
   red[threadIdx.x] = acc;
   __syncthreads();

@@ -198,6 +198,14 @@ __global__ __launch_bounds__(256) void quantize_g128_lds_kernel(const uint8_t* _
   if (c0 < nchunks) issue(c0, 0);
   for (int64_t c = c0; c < nchunks; c += nwaves, buf ^= 1) {
     const bool next = c + nwaves < nchunks;   // uniform
+    // CS: this chunk's column factors are requested before the next chunk's
+    // loads, so the wait below covers them too (loads complete in order).
+    f32x4 fcs[CS ? 8 : 1];
+    if constexpr (CS) {
+      const float* cs = colscale + ((c * 16 + (lane >> 2)) % G) * kGroup + part * 32;   // in [0, K), idle lanes too
+#pragma unroll
+      for (int q = 0; q < 8; ++q) fcs[q] = *reinterpret_cast<const f32x4*>(cs + 4 * q);
+    }
     if (next) {
       issue(c + nwaves, buf ^ 1);
       wait_vm<4>();
@@ -225,10 +233,9 @@ __global__ __launch_bounds__(256) void quantize_g128_lds_kernel(const uint8_t* _
     const int64_t gi = c * 16 + (lane >> 2);
     const bool active = gi < total_groups;
     if constexpr (CS) {
-      const float* cs = colscale + (gi % G) * kGroup + part * 32;   // in [0, K) for idle lanes too
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const f32x4 f = *reinterpret_cast<const f32x4*>(cs + 4 * q);
+        const f32x4 f = fcs[q];
         v[4 * q] = v[4 * q] * f.x;
         v[4 * q + 1] = v[4 * q + 1] * f.y;
         v[4 * q + 2] = v[4 * q + 2] * f.z;
