@@ -217,3 +217,24 @@ def test_awq_qwen_layer_shape():
     # (largest mean |x| ~58x the median)
     w, x = _case(896, 4864, 2048, 10, spread=(4.0, 58.0))
     _check(w, x, list(qmm.AWQ_ALPHAS), "896x4864, 2048 tokens", parallel=True)
+
+
+def test_awq_workspace_reuse_and_determinism():
+    # one caller workspace for two calls (the second smaller), against fresh
+    # workspaces: every output bit for bit, so nothing leaks from one call
+    # into the next and the sums are taken in a fixed order
+    big_w, big_x = _case(160, 512, 90, 12, spread=(4.0, 58.0))
+    small_w, small_x = _case(64, 256, 30, 13, salient=(7,))
+    grid = list(qmm.AWQ_ALPHAS)
+    need = qmm.awq_workspace_bytes(160, 512, 90, len(grid))
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)   # stale contents
+    note("awq_search shared workspace, two calls")
+    first = qmm.awq_search(big_w.to(DEV), big_x.to(DEV), grid, workspace=ws)
+    second = qmm.awq_search(small_w.to(DEV), small_x.to(DEV), grid, workspace=ws)
+    fresh_first = qmm.awq_search(big_w.to(DEV), big_x.to(DEV), grid)
+    fresh_second = qmm.awq_search(small_w.to(DEV), small_x.to(DEV), grid)
+    torch.cuda.synchronize()
+    for got, want, what in ((first, fresh_first, "first"), (second, fresh_second, "second")):
+        for g_, w_, name in zip(got, want, ("codes", "scales", "zeros", "smooth", "err", "best")):
+            a, b = g_.cpu().numpy(), w_.cpu().numpy()
+            assert bits_equal(a, b), f"{what} call {name}: {first_diff(a, b)}"
