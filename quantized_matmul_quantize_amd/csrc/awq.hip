@@ -328,8 +328,8 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   for (int64_t a = 0; a < n_alpha; ++a)
     if (!(alphas[a] >= 0.0 && alphas[a] <= 1.0)) return QMM_EINVAL;
   // the 16-bit product's 32-bit offsets (256 rows of 2K bytes), the W4A16
-  // product's, and the magnitude slices' grid rows (T / 32 <= 2^16)
-  if (K > (int64_t(1) << 22) || N > INT32_MAX || T > (int64_t(1) << 21)) return QMM_ERANGE;
+  // product's, and the magnitude slices' grid rows (at most 65535 slices)
+  if (K > (int64_t(1) << 22) || N > INT32_MAX || T > int64_t{65535} * kMagRows) return QMM_ERANGE;
   if (!aligned(W, 16) || !aligned(X, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(smooth, 4) ||
       !aligned(err, 8) || !aligned(best, 8))
     return QMM_EALIGN;

@@ -245,7 +245,7 @@ def test_awq_workspace_and_argument_errors():
     assert g(*args(na=0)) == EINVAL
     assert g(*args(al=ctypes.cast(bad, ctypes.c_void_p))) == EINVAL
     assert g(*args(K=(1 << 22) + 128, wsb=10**15)) == ERANGE
-    assert g(P, BF16, P, BF16, 4, 128, (1 << 21) + 1, ctypes.cast(al, ctypes.c_void_p), 2, P, P, P, P, P, P,
+    assert g(P, BF16, P, BF16, 4, 128, 65535 * 32 + 1, ctypes.cast(al, ctypes.c_void_p), 2, P, P, P, P, P, P,
              P, 10**15, None) == ERANGE
     assert g(*args(W=MIS)) == EALIGN
     assert g(*args(ws=None)) == EWS
