@@ -122,6 +122,19 @@ def test_gemm_wide_ragged(M):
     gemv_case(q, s, z, x, torch.bfloat16, f"gemm wide M={M} bf16", gemm=True)
 
 
+@pytest.mark.parametrize("M,n,k,xdt", [(2048, 4096, 4096, "bf16"), (1100, 6600, 1152, "f16"), (512, 33000, 640, "bf16")],
+                         ids=["M2048-4096x4096", "M1100-6600x1152-f16", "M512-33000x640"])
+def test_gemm_large_batch(M, n, k, xdt):
+    # prefill-sized batches (the shared-tile kernel with many token tiles):
+    # ragged M and N, an odd number of groups, both activation types; the
+    # 4096-row case on rows that meet every 128-row tile
+    q, s, z = random_w4(n, k, seed=M + n)
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(83, M + k), (M, k), 1.0), xdt)
+    rows = stratified_rows(n, 128) if M * n * k > 10 ** 10 else None
+    gemv_case(q, s, z, x, torch.float32, f"gemm large M={M}", gemm=True, rows=rows)
+    gemv_case(q, s, z, x, TDT[xdt], f"gemm large M={M} {xdt}", gemm=True, rows=rows)
+
+
 @pytest.mark.parametrize("n", [12321, 16421], ids=["one block per CU", "two rounds of blocks"])
 @pytest.mark.parametrize("M,k", [(3, 640), (16, 640), (17, 640), (32, 640), (40, 640), (64, 640), (16, 1152),
                                  (30, 1152), (50, 1152)], ids=lambda v: str(v))
