@@ -958,6 +958,17 @@ def check_awq_scales_closed_form():
     assert np.all(np.abs(s2.view(np.int32) - want.view(np.int32)) <= 1)
 
 
+def check_awq_factors_entry():
+    # the factors-only entry gives every alpha's factors: the searched alpha's
+    # row is the search's s_best bit for bit, and alpha = 0 is all ones
+    w, x = _awq_case(10, salient=9)
+    err, best, s, _, _, _ = oracle.awq_search_reference(w, x)
+    s_all = oracle.awq_factors_reference(x)
+    assert s_all.shape == (len(oracle.AWQ_ALPHAS), x.shape[1])
+    assert np.array_equal(s_all[best].view(np.uint32), s.view(np.uint32))
+    assert np.all(s_all[0] == 1.0)
+
+
 def check_awq_power_of_two_invariance():
     # scaling the activations by 4 scales every magnitude alike: the same
     # factors and choice, the errors 16 times larger
@@ -1011,6 +1022,7 @@ def check_awq_f16_input():
 ALL_CHECKS = [
     check_awq_alpha0_is_round_to_nearest, check_awq_uniform_magnitudes, check_awq_salient_channel,
     check_awq_scales_closed_form, check_awq_power_of_two_invariance, check_awq_listing_error, check_awq_f16_input,
+    check_awq_factors_entry,
     check_llm_int8_special_cases, check_llm_int8_decomposition, check_llm_int8_cap_and_permutation,
     check_llm_int8_accuracy,
     check_e4m3_conversion, check_fp8_listing, check_fp8_product,
