@@ -471,15 +471,17 @@ def build_ops(dev):
         ok(lib.awq_search(P(wa), qmm.BF16, P(xa), qmm.BF16, na, ka, ta, ctypes.cast(alphas_h, ctypes.c_void_p), n_al,
                           P(ca), P(sca), P(za), P(sma), P(era), P(ba), P(wsa), wsa.numel(), S(xa)))
 
-    # bytes: what the launches move as designed (per alpha: the weights scaled
-    # to fp32 and quantized, the inputs scaled to bf16, the W4A16 product and
-    # the squared error; once: the magnitudes, X W^T, the final quantization)
-    per_alpha = (2 * na * ka + 4 * na * ka) + (4 * na * ka + na * ka // 2 + na * ga * 4 + na * ga // 2) + \
-        (2 * ta * ka + 2 * ta * ka) + (2 * ta * ka + na * ka // 2 + na * ga * 5 + 4 * ta * na) + 8 * ta * na
-    once = 2 * ta * ka + (2 * ta * ka + 2 * na * ka + 4 * ta * na) + (6 * na * ka + 4 * na * ka + na * ka // 2)
+    # bytes: what the launches move as designed (per alpha: the weights read
+    # and quantized with the factors applied on the fly, the inputs scaled to
+    # bf16, the W4A16 product into fp32 and the squared error against X W^T;
+    # once: the magnitudes, X W^T, the final quantization)
+    fmt_a = na * ka // 2 + na * ga * 4 + na * ga // 2
+    per_alpha = (2 * na * ka + fmt_a) + (2 * ta * ka + 2 * ta * ka) + (2 * ta * ka + fmt_a + 4 * ta * na) + \
+        8 * ta * na
+    once = 2 * ta * ka + (2 * ta * ka + 2 * na * ka + 4 * ta * na) + (2 * na * ka + fmt_a)
     ops.add(f"awq_search {na}x{ka} T={ta}", awq, n_al * per_alpha + once, "mfma",
-            "awq_* kernels + i8_gemm_kernel (bf16) + quantize_g128_flat_kernel + w4a16 GEMM", cfga,
-            reads=lambda i: ["wa", "xa"], writes=lambda i: ["ca"], flops=2 * ta * na * ka * (n_al + 1),
+            "awq_* kernels + i8_gemm_kernel (bf16) + quantize_g128_lds_kernel (column factors) + w4_tile_kernel",
+            cfga, reads=lambda i: ["wa", "xa"], writes=lambda i: ["ca"], flops=2 * ta * na * ka * (n_al + 1),
             peak=BF16_PEAK_TFLOPS)
 
     # ---- 70B-class MLP decode: W4A16 B=8 then B=1, then W8A16 --------------
