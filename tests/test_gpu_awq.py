@@ -238,3 +238,11 @@ def test_awq_workspace_reuse_and_determinism():
         for g_, w_, name in zip(got, want, ("codes", "scales", "zeros", "smooth", "err", "best")):
             a, b = g_.cpu().numpy(), w_.cpu().numpy()
             assert bits_equal(a, b), f"{what} call {name}: {first_diff(a, b)}"
+
+
+def test_awq_many_alphas():
+    # 64 alphas (the most a call takes; the selection sums four per
+    # wavefront) in an irregular order, against the oracle
+    w, x = _case(72, 384, 50, 14, spread=(4.0, 58.0))
+    grid = list(np.random.Generator(np.random.PCG64(15)).random(64))
+    _check(w, x, grid, "64 alphas")
