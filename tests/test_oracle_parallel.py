@@ -20,3 +20,18 @@ def test_parallel_build_is_bit_identical():
     wp = oracle.asym_dequantize(q, s, z, parallel=True)
     assert np.array_equal(w1.view(np.uint32), wp.view(np.uint32))
     assert oracle.threads(parallel=False) == 1 and oracle.threads(parallel=True) >= 1
+
+
+def test_parallel_awq_search_is_bit_identical():
+    # the AWQ search's products split over threads (the large parity cases
+    # use it): every output bit for bit against the serial oracle
+    g = np.random.Generator(np.random.PCG64(6))
+    w = (g.standard_normal((40, 256)) * 0.02).astype(np.float32)
+    x = g.standard_normal((33, 256)).astype(np.float32)
+    x[:, 5] *= np.float32(30.0)
+    for xdt in ("bf16", "f16"):
+        serial = oracle.awq_search_reference(w, x, x_dtype=xdt)
+        par = oracle.awq_search_reference(w, x, parallel=True, x_dtype=xdt)
+        assert serial[1] == par[1]
+        for a, b in zip(serial[:1] + serial[2:], par[:1] + par[2:]):
+            assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
