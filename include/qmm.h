@@ -458,7 +458,7 @@ int llm_int8_gemm(const void* X, int x_dtype, const int8_t* qW, const float* w_s
  * operands, W and X of different types, K % 128 != 0 or more than 64
  * alphas; QMM_ERANGE for
  * K > 2^22, N >= 2^31 or T > 2097120; QMM_EALIGN for W, X, codes not 16-byte
- * aligned;
+ * aligned, scales or smooth not 4-byte, err or best not 8-byte aligned;
  * QMM_EWORKSPACE for a workspace smaller than awq_workspace_bytes(N, K, T,
  * n_alpha) (0 for invalid sizes), QMM_EALIGN for one not 256-byte aligned.
  * The workspace is the caller's device memory, used only during the call
