@@ -552,6 +552,80 @@ def gemv_traffic():
     return round(sum(v["hbm_read_bytes"] + v["hbm_write_bytes"] for v in launches) / len(launches))
 
 
+def summarize_profiles(d):
+    """The per-kernel table of profiles/bench_step_all_kernels.md (printed) and
+    profiles/gemv_valu_kernel_traffic.json (written) from one profiling set in
+    directory d, laid out as that file's rocprofv3 commands write it: the
+    kernel trace (trace/bench_results.db) and the counter runs fetch, write,
+    cfetch, cwrite (the plain-copy calibration), mfma, lds and valu."""
+    import collections
+    import csv
+    import hashlib
+    import re
+    import sqlite3
+
+    def short(n):
+        n = re.sub(r"^void ", "", n.replace("qmm::(anonymous namespace)::", "").replace("(anonymous namespace)::", ""))
+        return re.sub(r"\(.*$", "", n)
+
+    def rows(run):
+        return list(csv.DictReader(open(os.path.join(d, run, "run_counter_collection.csv"))))
+
+    def pmc(run):
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in rows(run):
+            agg[(short(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        return agg
+
+    mean = lambda v: sum(v) / len(v)
+    dur = collections.defaultdict(list)
+    db = sqlite3.connect(os.path.join(d, "trace", "bench_results.db"))
+    for name, grid, t in db.execute("select name, grid_x*grid_y*grid_z, duration from kernels").fetchall():
+        dur[(short(name), grid)].append(t / 1e3)
+    total = sum(sum(v) for v in dur.values())
+    copy = 256 << 20   # --calibrate-copy's buffer
+    fscale = copy / (mean([float(r["Counter_Value"]) for r in rows("cfetch") if "copyBuffer" in r["Kernel_Name"]]) * 1024)
+    wscale = copy / (mean([float(r["Counter_Value"]) for r in rows("cwrite") if "copyBuffer" in r["Kernel_Name"]]) * 1024)
+    F, W, Mf, L, V = pmc("fetch"), pmc("write"), pmc("mfma"), pmc("lds"), pmc("valu")
+    for (k, g), v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        if k.startswith("at::native") or "elementwise" in k or "distribution" in k:
+            continue
+        t = mean(v)
+        rd, wr = F.get((k, g), {}).get("FETCH_SIZE"), W.get((k, g), {}).get("WRITE_SIZE")
+        rds = f"{mean(rd) * 1024 * fscale / 2**20:.1f}" if rd else "-"
+        wrs = f"{mean(wr) * 1024 * wscale / 2**20:.1f}" if wr else "-"
+        m, mf = Mf.get((k, g), {}), "-"
+        if m.get("SQ_VALU_MFMA_BUSY_CYCLES") and m.get("GRBM_GUI_ACTIVE"):
+            busy = mean(m["SQ_VALU_MFMA_BUSY_CYCLES"]) / (mean(m["GRBM_GUI_ACTIVE"]) / 8 * 1024)
+            ops = 512 * sum(mean(m.get(c, [0])) for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_I8",
+                                                          "SQ_INSTS_VALU_MFMA_MOPS_F8"))
+            if busy > 0.001:
+                mf = f"{100 * busy:.1f}% ({ops / (t * 1e-6) / 1e12:.0f} T/s)"
+        l, ld = L.get((k, g), {}), "-"
+        if l.get("SQ_LDS_IDX_ACTIVE") and mean(l["SQ_LDS_IDX_ACTIVE"]) > 0:
+            ld = f"{100 * mean(l['SQ_LDS_BANK_CONFLICT']) / mean(l['SQ_LDS_IDX_ACTIVE']):.1f}%"
+        vv = V.get((k, g), {})
+        va = f"{mean(vv['SQ_INSTS_VALU']) / 1e6:.2f}" if vv.get("SQ_INSTS_VALU") else "-"
+        print(f"| `{k}` | {g} | {len(v)} | {t:.2f} | {min(v):.2f} | {max(v):.2f} | {100 * sum(v) / total:.1f}% | "
+              f"{rds} | {wrs} | {mf} | {ld} | {va} |")
+    # the headline kernel's traffic per launch, keyed to its source text
+    grids = {917504: "28672x8192", 262144: "8192x28672"}
+    per = collections.defaultdict(lambda: {"f": [], "w": []})
+    for key, run, sc in (("f", "fetch", fscale), ("w", "write", wscale)):
+        for r in rows(run):
+            if "gemv_valu_kernel<2, 2, 1, 8>" in r["Kernel_Name"] and int(r["Grid_Size"]) in grids:
+                per[grids[int(r["Grid_Size"])]][key].append(float(r["Counter_Value"]) * 1024 * sc)
+    src = "quantized_matmul_quantize_amd/csrc/w4a16.hip"
+    body = kernel_source(open(os.path.join(ROOT, src)).read(), "gemv_valu_kernel")
+    rec = {"kernel": "gemv_valu_kernel<bf16, bf16, B=1, R=8, W=4>", "kernel_function": "gemv_valu_kernel",
+           "source": src, "kernel_sha256": hashlib.sha256(body.encode()).hexdigest(),
+           "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+           "per_launch": {k: {"hbm_read_bytes": round(mean(v["f"])), "hbm_write_bytes": round(mean(v["w"])),
+                              "launches": len(v["f"])} for k, v in per.items()},
+           "summary": "profiles/bench_step_all_kernels.md"}
+    json.dump(rec, open(os.path.join(ROOT, "profiles", "gemv_valu_kernel_traffic.json"), "w"), indent=1)
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -655,7 +729,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 256 MiB (5 times), to scale HBM byte counters")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="print the per-kernel profile table and write the GEMV traffic record from a profiling set "
+                         "(no GPU used)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
