@@ -613,11 +613,11 @@ def summarize_profiles(d):
     per = collections.defaultdict(lambda: {"f": [], "w": []})
     for key, run, sc in (("f", "fetch", fscale), ("w", "write", wscale)):
         for r in rows(run):
-            if "gemv_valu_kernel<2, 2, 1, 8>" in r["Kernel_Name"] and int(r["Grid_Size"]) in grids:
+            if "gemv_valu_kernel<2, 2, 1, 8, 4>" in r["Kernel_Name"] and int(r["Grid_Size"]) in grids:
                 per[grids[int(r["Grid_Size"])]][key].append(float(r["Counter_Value"]) * 1024 * sc)
     src = "quantized_matmul_quantize_amd/csrc/w4a16.hip"
     body = kernel_source(open(os.path.join(ROOT, src)).read(), "gemv_valu_kernel")
-    rec = {"kernel": "gemv_valu_kernel<bf16, bf16, B=1, R=8, W=4>", "kernel_function": "gemv_valu_kernel",
+    rec = {"kernel": "gemv_valu_kernel<bf16, bf16, B=1, R=8, KW=4>", "kernel_function": "gemv_valu_kernel",
            "source": src, "kernel_sha256": hashlib.sha256(body.encode()).hexdigest(),
            "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
            "per_launch": {k: {"hbm_read_bytes": round(mean(v["f"])), "hbm_write_bytes": round(mean(v["w"])),

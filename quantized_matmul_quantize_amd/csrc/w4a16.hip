@@ -88,18 +88,25 @@ __device__ __forceinline__ void copy_zeros_to_lds(uint8_t* dst, const uint8_t* _
 // Vector-ALU GEMV.
 // ----------------------------------------------------------------------------
 constexpr int kValuWaves = 4;
-constexpr int kLaneK = 32;                                   // weights per lane per row per step
-constexpr int64_t kValuStepK = kValuWaves * kWave * kLaneK;  // 8192
+constexpr int kLaneK = 32;   // weights per lane per row per step
 
-template <int XDT, int YDT, int B, int R>
+// KW of the four wavefronts split K (a block step covers KW x 2048 weights of
+// a row); the other 4 / KW take further sets of R rows, so that a short K
+// (4096: KW = 2) still gives every wavefront work.
+template <int XDT, int YDT, int B, int R, int KW>
 __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restrict__ codes,
                                                         const float* __restrict__ scales,
                                                         const uint8_t* __restrict__ zeros, int64_t N, int64_t K,
                                                         const uint16_t* __restrict__ x, void* __restrict__ y) {
+  static_assert(KW == 1 || KW == 2 || KW == 4, "K split");
+  constexpr int kSets = kValuWaves / KW;   // row sets per block
+  constexpr uint32_t kStepK = KW * kWave * kLaneK;
   using Mg = Int4Magic<XDT>;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * R;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int kslot = wave % KW;
+  const int rset = wave / KW;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * kSets + rset) * R;
   const uint32_t magic = vgpr_const(Mg::kMagic);
   const int64_t G = K / kGroup;
   const int64_t zrow = (G + 1) / 2;
@@ -123,12 +130,12 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
 
-  for (uint32_t k0 = 0; k0 < static_cast<uint32_t>(kk); k0 += static_cast<uint32_t>(kValuStepK)) {
+  for (uint32_t k0 = 0; k0 < static_cast<uint32_t>(kk); k0 += kStepK) {
     // A wavefront with no lane inside K skips the step; in a partly covered
     // step the lanes past K load the last 32 weights (in bounds) and take
     // zero activations, so the step runs without a divergent branch.
-    if (k0 + static_cast<uint32_t>(wave * (kWave * kLaneK)) >= static_cast<uint32_t>(kk)) break;
-    const uint32_t kb_raw = k0 + static_cast<uint32_t>(wave * (kWave * kLaneK) + lane * kLaneK);
+    if (k0 + static_cast<uint32_t>(kslot * (kWave * kLaneK)) >= static_cast<uint32_t>(kk)) break;
+    const uint32_t kb_raw = k0 + static_cast<uint32_t>(kslot * (kWave * kLaneK) + lane * kLaneK);
     const bool inside = kb_raw < static_cast<uint32_t>(kk);
     const uint32_t kb = inside ? kb_raw : static_cast<uint32_t>(kk - kLaneK);
     {
@@ -228,14 +235,16 @@ __global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t* __restric
       }
   }
   __syncthreads();
-  if (threadIdx.x < R * B) {
-    const int r = threadIdx.x / B;
-    const int b = threadIdx.x % B;
-    const int64_t row = row0 + r;
+  if (threadIdx.x < kSets * R * B) {
+    const int set = threadIdx.x / (R * B);
+    const int i = threadIdx.x % (R * B);
+    const int r = i / B;
+    const int b = i % B;
+    const int64_t row = (static_cast<int64_t>(blockIdx.x) * kSets + set) * R + r;
     if (row < N) {
       float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kValuWaves; ++w) v += red[w][threadIdx.x];
+      for (int w = 0; w < KW; ++w) v += red[set * KW + w][i];
       store_y<YDT>(y, static_cast<int64_t>(b) * N + row, v);
     }
   }
@@ -1196,12 +1205,22 @@ int check_common(const uint8_t* codes, const float* scales, const uint8_t* zeros
   return QMM_OK;
 }
 
+template <int XDT, int YDT, int B, int KW>
+void launch_valu_kw(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                    const uint16_t* x, void* y, hipStream_t s) {
+  constexpr int R = 8;   // rows per wavefront: 8 x 16 bytes in flight per lane
+  const dim3 grid(static_cast<unsigned>(ceil_div(N, R * (kValuWaves / KW))));
+  gemv_valu_kernel<XDT, YDT, B, R, KW><<<grid, dim3(kValuWaves * kWave), 0, s>>>(codes, scales, zeros, N, K, x, y);
+}
+
+// Four wavefronts along K once a row has more than 6144 weights, two above
+// 2048, else one.
 template <int XDT, int YDT, int B>
 void launch_valu(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                  const uint16_t* x, void* y, hipStream_t s) {
-  constexpr int R = 8;   // rows per block: 8 x 16 bytes in flight per lane
-  const dim3 grid(static_cast<unsigned>(ceil_div(N, R)));
-  gemv_valu_kernel<XDT, YDT, B, R><<<grid, dim3(kValuWaves * kWave), 0, s>>>(codes, scales, zeros, N, K, x, y);
+  if (K > 6144) launch_valu_kw<XDT, YDT, B, 4>(codes, scales, zeros, N, K, x, y, s);
+  else if (K > 2048) launch_valu_kw<XDT, YDT, B, 2>(codes, scales, zeros, N, K, x, y, s);
+  else launch_valu_kw<XDT, YDT, B, 1>(codes, scales, zeros, N, K, x, y, s);
 }
 
 template <int XDT, int YDT>

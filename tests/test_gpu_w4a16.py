@@ -57,6 +57,20 @@ def test_gemv_long_k(k):
         gemv_case(q, s, z, x, TDT[xdt], f"long K {xdt} 16-bit")
 
 
+@pytest.mark.parametrize("k", [128, 1152, 2048, 2176, 4096, 6144, 6272])
+@pytest.mark.parametrize("B", [1, 2])
+def test_gemv_k_split_boundaries(k, B):
+    # The single-token kernel splits K over one, two or four wavefronts by K
+    # (at most 2048, at most 6144, above); the other wavefronts of a block take
+    # more rows.  Row counts not a multiple of a block's rows leave sets empty.
+    for n in (5, 45, 77):
+        q, s, z = random_w4(n, k, seed=n * 7 + k + B)
+        for xdt in ("bf16", "f16"):
+            x = workloads.to_dtype(workloads.gaussian(workloads.rng(81, k + n), (B, k), 1.0), xdt)
+            gemv_case(q, s, z, x, torch.float32, f"K split {xdt}")
+            gemv_case(q, s, z, x, TDT[xdt], f"K split {xdt} 16-bit")
+
+
 def test_gemv_one_row_one_group():
     q, s, z = random_w4(1, 128, seed=1)
     x = workloads.to_dtype(workloads.gaussian(workloads.rng(1, 1), (1, 128), 1.0), "bf16")
