@@ -166,10 +166,15 @@ __global__ __launch_bounds__(256) void awq_factor_kernel(const double* __restric
 }
 
 // X_s = h16(fl32(X / s)) in X's own 16-bit type, correctly rounded division,
-// eight values per thread.
+// eight values per thread.  Also the per-group sums of the rounded outputs, xsum[t][g] (fp32), for
+// the products' zero-point term: the 16 lanes of a group (consecutive
+// threads, 8 values each) add their sums by a fixed butterfly.  The thread
+// count and the grid stride are multiples of 16 and K of 128, so a group's
+// lanes are always active together.
 template <int XDT>
 __global__ __launch_bounds__(256) void awq_scale_x_kernel(const uint16_t* __restrict__ x, const float* __restrict__ s,
-                                                          int64_t total8, int64_t K, uint16_t* __restrict__ out) {
+                                                          int64_t total8, int64_t K, uint16_t* __restrict__ out,
+                                                          float* __restrict__ xsum) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total8;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t e = i * 8;
@@ -177,13 +182,19 @@ __global__ __launch_bounds__(256) void awq_scale_x_kernel(const uint16_t* __rest
     const u32x4 v = ld16(x + e);
     const uint32_t a[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[4];
+    float sum = 0.0f;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const float lo = h16_lo<XDT>(a[h]) / s[j + 2 * h];
       const float hi = h16_hi<XDT>(a[h]) / s[j + 2 * h + 1];
       o[h] = h16_bits<XDT>(lo) | (h16_bits<XDT>(hi) << 16);
+      sum += h16_lo<XDT>(o[h]);
+      sum += h16_hi<XDT>(o[h]);
     }
     *reinterpret_cast<u32x4*>(out + e) = u32x4{o[0], o[1], o[2], o[3]};
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) sum += __shfl_xor(sum, m, kWave);
+    if ((i & 15) == 0) xsum[e / kGroup] = sum;   // [t][g] = element e / 128 of the row-major sums
   }
 }
 
@@ -270,7 +281,7 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Workspace regions, in order.
 struct AwqLayout {
-  size_t part, mag, pbuf, bmax, bmin, norm, s_all, s_best, xs, codes, scales, zeros, yref, yq, err, total;
+  size_t part, mag, pbuf, bmax, bmin, norm, s_all, s_best, xs, xsum, codes, scales, zeros, yref, yq, err, total;
 };
 
 AwqLayout awq_layout(int64_t N, int64_t K, int64_t T, int64_t n_alpha) {
@@ -287,6 +298,7 @@ AwqLayout awq_layout(int64_t N, int64_t K, int64_t T, int64_t n_alpha) {
   l.s_all = o; o += align256(static_cast<size_t>(n_alpha * K) * sizeof(float));
   l.s_best = o; o += align256(static_cast<size_t>(K) * sizeof(float));
   l.xs = o; o += align256(static_cast<size_t>(T * K) * 2);
+  l.xsum = o; o += align256(static_cast<size_t>(T * G) * sizeof(float));
   l.codes = o; o += align256(static_cast<size_t>(N * K / 2));
   l.scales = o; o += align256(static_cast<size_t>(N * G) * sizeof(float));
   l.zeros = o; o += align256(static_cast<size_t>(N * ((G + 1) / 2)));
@@ -346,6 +358,7 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   float* s_all = reinterpret_cast<float*>(base + L.s_all);
   float* s_copy = reinterpret_cast<float*>(base + L.s_best);
   uint16_t* xs = reinterpret_cast<uint16_t*>(base + L.xs);
+  float* xsum = reinterpret_cast<float*>(base + L.xsum);
   uint8_t* qc = base + L.codes;
   float* qs = reinterpret_cast<float*>(base + L.scales);
   uint8_t* qz = base + L.zeros;
@@ -379,11 +392,11 @@ extern "C" int awq_search(const void* W, int w_dtype, const void* X, int x_dtype
   for (int64_t a = 0; a < n_alpha; ++a) {
     const float* sa = s_all + a * K;
     launch_quantize_colscaled(w, w_dtype, sa, N, K, qc, qs, qz, s);
-    if (x_dtype == QMM_F16) awq_scale_x_kernel<QMM_F16><<<grid_for(xn8), 256, 0, s>>>(x, sa, xn8, K, xs);
-    else awq_scale_x_kernel<QMM_BF16><<<grid_for(xn8), 256, 0, s>>>(x, sa, xn8, K, xs);
+    if (x_dtype == QMM_F16) awq_scale_x_kernel<QMM_F16><<<grid_for(xn8), 256, 0, s>>>(x, sa, xn8, K, xs, xsum);
+    else awq_scale_x_kernel<QMM_BF16><<<grid_for(xn8), 256, 0, s>>>(x, sa, xn8, K, xs, xsum);
     st = launch_status();
     if (st != QMM_OK) return st;
-    st = w4a16_gemm(qc, qs, qz, N, K, kGroup, xs, x_dtype, T, yq, QMM_F32, stream);
+    st = w4a16_gemm_colsums(qc, qs, qz, N, K, xs, xsum, x_dtype, T, yq, s);
     if (st != QMM_OK) return st;
     awq_sqerr_kernel<<<kErrBlocks, 256, 0, s>>>(yref, yq, T * N, epart + a * kErrBlocks);
     st = launch_status();

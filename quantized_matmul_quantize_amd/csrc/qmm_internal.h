@@ -41,4 +41,13 @@ void launch_quantize_colscaled(const uint16_t* W, int w_dtype, const float* cols
 void launch_h16_gemm(const uint16_t* A, const uint16_t* B, int dtype, int64_t M, int64_t N, int64_t K, float* Y,
                      hipStream_t s);
 
+// The W4A16 product of w4a16_gemm into fp32 Y with the caller's column sums
+// xsum [M][K / 128] (the per-group sums of X's rows, exactly as X holds them;
+// w4a16.hip): where w4a16_gemm would run its shared-tile kernel that kernel
+// reads them instead of recomputing them, elsewhere this is w4a16_gemm.
+// Arguments as w4a16_gemm (group 128, x_dtype QMM_BF16 or QMM_F16), xsum
+// 16-byte aligned; returns its status.
+int w4a16_gemm_colsums(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                       const uint16_t* X, const float* xsum, int x_dtype, int64_t M, float* Y, hipStream_t s);
+
 }  // namespace qmm

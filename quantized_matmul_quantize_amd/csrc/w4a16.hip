@@ -976,20 +976,26 @@ __global__ __launch_bounds__(NW * 64) void w4_rows_kernel(const uint8_t* __restr
 //  * scales, 256 bytes per wavefront: its 32 rows, loaded twice over.
 // Two blocks of BM = 64 fit a compute unit (about 75 KiB each at K = 4096),
 // so each SIMD interleaves the ALU work of one wavefront with the matrix work
-// of another.
+// of another.  XS: the caller supplies the column sums X_g ([M][G] fp32, the
+// sums of the activations exactly as the kernel reads them); each slot then
+// also holds the tile's BM sums of its group, loaded like the scales, and
+// the wavefronts skip the 4 MT matrix instructions per group that would
+// otherwise recompute them (each of the four wavefronts the same ones).
 // ----------------------------------------------------------------------------
 constexpr int kTileN = 128;
 constexpr int kTileD = 2;
 constexpr int kTileSlots = kTileD + 1;
 
-template <int BM>
+template <int BM, bool XS = false>
 struct TileCfg {
   static constexpr int kXBytes = BM * kGroup * 2;
   static constexpr int kCodeBytes = kTileN * kGroup / 2;          // 8 KiB
   static constexpr int kScaleBytes = kLdsWaves * 256;
-  static constexpr int kSlotBytes = kXBytes + kCodeBytes + kScaleBytes;
+  static constexpr int kSumBytes = XS ? BM * 4 : 0;               // the tile's column sums of the group
+  static constexpr int kSlotBytes = kXBytes + kCodeBytes + kScaleBytes + kSumBytes;
   static constexpr int kXLoads = BM / 16;                          // per wavefront per group
-  static constexpr int kLoads = kXLoads + 2 + 1;
+  static constexpr int kLoads = kXLoads + 2 + 1 + (XS ? 1 : 0);
+  static_assert(!XS || BM == kWave, "one 4-byte load per lane holds the tile's sums");
   static constexpr int kPartPitch = kTileN + 4;
   static_assert(BM * kPartPitch * 4 <= kTileSlots * kSlotBytes, "output tile fits the slots");
 };
@@ -998,11 +1004,12 @@ struct TileCfg {
 // group that is never read) into slot i % kTileSlots, kLoads instructions.
 // (The LDS destinations are cast in place: in the host pass a function
 // template that calls lds_at is dropped from overload resolution.)
-template <int BM>
+template <int BM, bool XS>
 __device__ __forceinline__ void tile_issue(int i, int G, int wave, uint32_t lbase, __amdgpu_buffer_rsrc_t xr,
-                                           __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr, const int* xoff,
-                                           const int* coff, int soff) {
-  using Cfg = TileCfg<BM>;
+                                           __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr,
+                                           __amdgpu_buffer_rsrc_t qr, const int* xoff, const int* coff, int soff,
+                                           int qoff) {
+  using Cfg = TileCfg<BM, XS>;
   const int g = min(i, G - 1);
   const uint32_t slot = lbase + (i % kTileSlots) * Cfg::kSlotBytes;
 #pragma unroll
@@ -1015,15 +1022,20 @@ __device__ __forceinline__ void tile_issue(int i, int G, int wave, uint32_t lbas
                                              16, coff[q], g * 64, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       sr, (lds_ptr_t)(uintptr_t)(slot + Cfg::kXBytes + Cfg::kCodeBytes + wave * 256), 4, soff, g * 4, 0, 0);
+  // Every wavefront writes the same BM sums (lane l: token l), so each one's
+  // own wait covers them.
+  if constexpr (XS)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        qr, (lds_ptr_t)(uintptr_t)(slot + Cfg::kXBytes + Cfg::kCodeBytes + Cfg::kScaleBytes), 4, qoff, g * 4, 0, 0);
 }
 
-template <int XDT, int YDT, int BM>
+template <int XDT, int YDT, int BM, bool XS = false>
 __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict__ codes,
                                                       const float* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros, int64_t N, int64_t K,
                                                       const uint16_t* __restrict__ x, int64_t M,
-                                                      void* __restrict__ y) {
-  using Cfg = TileCfg<BM>;
+                                                      void* __restrict__ y, const float* __restrict__ xsum = nullptr) {
+  using Cfg = TileCfg<BM, XS>;
   using Mg = Int4Magic<XDT>;
   constexpr int MT = BM / 16;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -1068,6 +1080,10 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
       const_cast<uint8_t*>(codes + n0 * (K / 2)), 0, static_cast<int>(nrows) * kh, kBufferWord3);
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(scales + n0 * G), 0, static_cast<int>(nrows) * G * 4, kBufferWord3);
+  // Column sums, rows m0 .. m0 + mrows of [M][G] (tokens past M read 0).
+  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(XS ? xsum + m0 * G : scales), 0, XS ? static_cast<int>(mrows) * G * 4 : 0, kBufferWord3);
+  const int qoff = lane * G * 4;
 
   // Load q of this wavefront: activation rows 4 (wave MT + q) .. +4, code
   // slice 2 wave + q, and its 32 scale rows (lane l: row 32 wave + l % 32).
@@ -1086,7 +1102,7 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
   const int soff = (32 * wave + (lane & 31)) * G * 4;
 
 
-  for (int i = 0; i < kTileD; ++i) tile_issue<BM>(i, G, wave, lbase, xr, cr, sr, xoff, coff, soff);
+  for (int i = 0; i < kTileD; ++i) tile_issue<BM, XS>(i, G, wave, lbase, xr, cr, sr, qr, xoff, coff, soff, qoff);
   const int zp = zero_pitch(zb);
   copy_zeros_to_lds<256>(ztab, zeros + n0 * zb, kTileN, zb, zp, static_cast<int>(nrows), tid);
 
@@ -1110,7 +1126,7 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    tile_issue<BM>(i + kTileD, G, wave, lbase, xr, cr, sr, xoff, coff, soff);
+    tile_issue<BM, XS>(i + kTileD, G, wave, lbase, xr, cr, sr, qr, xoff, coff, soff, qoff);
     const uint8_t* xg = lds + (i % kTileSlots) * Cfg::kSlotBytes;
     const uint8_t* cg = xg + Cfg::kXBytes;
     const float* sg = reinterpret_cast<const float*>(cg + Cfg::kCodeBytes + wave * 256);
@@ -1124,6 +1140,12 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
       zo[nt] = Mg::offset + static_cast<float>((i & 1) ? (zbyte >> 4) : (zbyte & 15u));
     }
     f32x4 part[MT][2], xs[MT];
+    if constexpr (XS) {
+      // D lane l of token tile mt needs the sums of tokens 16 mt + 4 (l / 16) .. + 4
+      const float* qg = reinterpret_cast<const float*>(cg + Cfg::kCodeBytes + Cfg::kScaleBytes);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xs[mt] = *reinterpret_cast<const f32x4*>(qg + 16 * mt + 4 * fp);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint32_t xa[MT][4];
@@ -1135,9 +1157,11 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
         xa[mt][2] = v.z;
         xa[mt][3] = v.w;
       }
+      if constexpr (!XS) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        xs[mt] = mfma16x16x32<XDT>(xa[mt], ones, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : xs[mt]);
+        for (int mt = 0; mt < MT; ++mt)
+          xs[mt] = mfma16x16x32<XDT>(xa[mt], ones, c == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : xs[mt]);
+      }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         uint32_t wb[4];
@@ -1314,6 +1338,31 @@ bool launch_tile_t(const uint8_t* codes, const float* scales, const uint8_t* zer
   return true;
 }
 
+// The shared-tile kernel with the caller's column sums (fp32 out); false
+// (nothing launched) where w4a16_gemm would not choose that kernel: up to
+// 64 tokens, fewer 64 x 128 tiles than compute units, or a zero-point table
+// too large for LDS.
+template <int XDT>
+bool launch_tile_colsums(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                         const uint16_t* x, const float* xsum, int64_t M, float* y, hipStream_t s) {
+  using Cfg = TileCfg<64, true>;
+  if (M <= 64 || ceil_div(M, 64) * ceil_div(N, kTileN) < static_cast<int64_t>(device_cus())) return false;
+  const int64_t G = K / kGroup;
+  // the plain kernel's LDS must fit too, or w4a16_gemm would not pick it
+  const size_t plain = static_cast<size_t>(kTileSlots) * TileCfg<64>::kSlotBytes +
+                       static_cast<size_t>(kTileN) * zero_pitch(static_cast<int>((G + 1) / 2));
+  const size_t lds = static_cast<size_t>(kTileSlots) * Cfg::kSlotBytes +
+                     static_cast<size_t>(kTileN) * zero_pitch(static_cast<int>((G + 1) / 2));
+  if (plain > kLdsBytesMax || lds > kLdsBytesMax) return false;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_tile_kernel<XDT, QMM_F32, 64, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  const int64_t tiles = ceil_div(M, 64) * ceil_div(N, kTileN);
+  const dim3 grid(static_cast<unsigned>(ceil_div(tiles, 8) * 8));
+  w4_tile_kernel<XDT, QMM_F32, 64, true><<<grid, dim3(kLdsWaves * kWave), lds, s>>>(codes, scales, zeros, N, K, x, M,
+                                                                                    y, xsum);
+  return true;
+}
+
 template <int XDT, int YDT, int NT, int S, int TT = 1, int H = 1, int NW = 4>
 bool launch_rows_t(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                    const uint16_t* x, int64_t M, void* y, hipStream_t s) {
@@ -1422,6 +1471,22 @@ extern "C" int w4a16_gemv(const uint8_t* codes, const float* scales, const uint8
   }
   return launch_status();
 }
+
+namespace qmm {
+
+int w4a16_gemm_colsums(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                       const uint16_t* X, const float* xsum, int x_dtype, int64_t M, float* Y, hipStream_t s) {
+  int st = check_common(codes, scales, zeros, N, K, kGroup, X, x_dtype, M, Y, QMM_F32);
+  if (st != QMM_OK) return st;
+  if (!xsum || !aligned(xsum, 16)) return QMM_EINVAL;
+  const bool done = x_dtype == QMM_BF16
+                        ? launch_tile_colsums<QMM_BF16>(codes, scales, zeros, N, K, X, xsum, M, Y, s)
+                        : launch_tile_colsums<QMM_F16>(codes, scales, zeros, N, K, X, xsum, M, Y, s);
+  if (done) return launch_status();
+  return w4a16_gemm(codes, scales, zeros, N, K, kGroup, X, x_dtype, M, Y, QMM_F32, s);
+}
+
+}  // namespace qmm
 
 extern "C" int w4a16_gemm(const uint8_t* codes, const float* scales, const uint8_t* zeros, int64_t N, int64_t K,
                           int group, const void* X, int x_dtype, int64_t M, void* Y, int y_dtype, void* stream) {

@@ -220,11 +220,11 @@ def test_awq_workspace_and_argument_errors():
     a256 = lambda b: (b + 255) // 256 * 256
     # magnitude partial sums (32-row slices), the magnitudes, every alpha's
     # fp64 powers, their per-256-column maxima and minima, the norms, the fp32
-    # factors, the chosen factors, the scaled bf16 inputs, one INT4 format,
-    # both fp32 products, the squared-error partial sums
+    # factors, the chosen factors, the scaled bf16 inputs and their per-group
+    # sums, one INT4 format, both fp32 products, the squared-error partial sums
     n, k, t, na = 4096, 4096, 2048, 11
     want = (a256(64 * k * 8) + a256(k * 8) + a256(na * k * 8) + 2 * a256(na * 16 * 8) + a256(na * 8) + a256(na * k * 4) +
-            a256(k * 4) + a256(t * k * 2) + a256(n * k // 2) + a256(n * 32 * 4) + a256(n * 16) +
+            a256(k * 4) + a256(t * k * 2) + a256(t * 32 * 4) + a256(n * k // 2) + a256(n * 32 * 4) + a256(n * 16) +
             2 * a256(t * n * 4) + a256(na * 1024 * 8))
     assert ws(n, k, t, na) == want
     assert ws(0, 128, 4, 1) == 0 and ws(4, 100, 4, 1) == 0 and ws(4, 128, 4, 65) == 0 and ws(4, 128, 4, 0) == 0
