@@ -50,7 +50,10 @@ steps; `config.plain_read_GBps` is a plain 1 GiB streaming read (the
 library's `qmm_stream_read`, after the timed steps), as context for the HBM
 fractions, and `config.vendor_library_gemms` the ROCm BLAS libraries' INT8
 and bf16 GEMM rates at 2048x4096x4096 (through torch), as context for the
-MFMA fractions.
+MFMA fractions.  `config.headline_after_flush` times the two B=1 GEMVs
+again after the timed steps, each pair right after a 1 GiB read with
+ordinary (cache-allocating) loads, as a check that the headline is not
+served from the last-level cache.
 
 CPU baseline: the plain C oracle's reference for the same B=1 GEMVs
 (dequantize + fp64 product), single-threaded, and its OpenMP build over all
@@ -843,6 +846,31 @@ def main():
     g_us = sum(breakdown[k]["avg_us"] for k in gemv1)
     value = g_bytes / g_us / 1e3
 
+    # Cross-check of the headline's cache state: the two B=1 GEMVs again,
+    # back to back as in the step, each pair right after a 1 GiB read with
+    # ordinary loads (torch's max reduction), which allocate in the
+    # last-level cache and so evict whatever the GEMVs could find there.
+    # The GEMVs' own nontemporal loads do not displace it, so the in-step
+    # rotation alone could not show this.
+    flush_src = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    head = [op for op in ops if op["name"] in gemv1]
+    fl = []
+    for r in range(12):
+        torch.amax(flush_src)
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record()
+        for op in head:
+            op["fn"](args.warmup + args.steps + r)
+        e1.record()
+        fl.append((e0, e1))
+    torch.cuda.synchronize()
+    flushed_us = 1e3 * float(np.median([a.elapsed_time(b) for a, b in fl[2:]]))
+    del flush_src
+    after_flush = {"GBps": round(g_bytes / flushed_us / 1e3, 2),
+                   "hbm_frac": round(g_bytes / flushed_us / 1e3 / HBM_PEAK_GBPS, 4),
+                   "pair_us": round(flushed_us, 3),
+                   "note": "both B=1 GEMVs back to back after a 1 GiB cache-allocating read, median of 10"}
+
     def gbps(prefixes):
         ks = [k for k in breakdown if any(k.startswith(p) for p in prefixes)]
         return round(sum(breakdown[k]["alg_bytes"] for k in ks) / sum(breakdown[k]["avg_us"] for k in ks) / 1e3, 2)
@@ -873,6 +901,7 @@ def main():
                         "with 2048 calibration tokens",
             "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
             "plain_read_GBps": round(plain_read, 1),
+            "headline_after_flush": after_flush,
             "vendor_library_gemms": vendor,
             "quantize_GBps": gbps(["quantize 28672x8192", "quantize 8192x28672"]),
             "quantize_GBps_llama7b": gbps(["quantize 4096x4096", "quantize 11008x4096"]),
