@@ -154,9 +154,12 @@ def w4_kernel_name(M, N, dev):
     return "w4_lds_kernel"
 
 
-def w8_kernel_name(B):
-    """w8a16_gemv's dispatch: vector ALUs for one or two tokens, matrix cores from three."""
-    return "w8_gemv_kernel" if B <= 2 else "w8_mfma_kernel"
+def w8_kernel_name(B, K):
+    """w8a16_gemv's dispatch: vector ALUs for one or two tokens, matrix cores
+    from three (LDS-staged weights when K is a multiple of 256)."""
+    if B <= 2:
+        return "w8_gemv_kernel"
+    return "w8_lds_kernel" if K % 256 == 0 else "w8_mfma_kernel"
 
 
 def w4_bytes(n, k):
@@ -509,7 +512,7 @@ def build_ops(dev):
                 ok(lib.w8a16_gemv(P(q), P(b), m["n"], m["k"], P(m[f"x{B}w8"]), qmm.BF16, B, P(m[f"y{B}w8"]),
                                   qmm.BF16, S(q)))
             ops.add(f"w8a16_gemv B={B} {m['n']}x{m['k']}", w8,
-                    m["n"] * m["k"] + m["n"] * 4 + B * m["k"] * 2 + B * m["n"] * 2, "hbm", w8_kernel_name(B), cfg5,
+                    m["n"] * m["k"] + m["n"] * 4 + B * m["k"] * 2 + B * m["n"] * 2, "hbm", w8_kernel_name(B, m["k"]), cfg5,
                     reads=lambda i, m=m, j=j, B=B: [f"w8_70b{m['idx']}[{j}]", f"x{B}w8_70b{m['idx']}"],
                     flops=2 * B * m["n"] * m["k"])
     for f in fmts:

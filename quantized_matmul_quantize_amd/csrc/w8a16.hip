@@ -21,7 +21,13 @@
 //    are the A operand of v_mfma_f32_16x16x32_{bf16,f16} straight from
 //    registers (converted as above), the activations the B operand as loaded;
 //    a block of four wavefronts owns 16 rows, each wavefront a contiguous
-//    quarter of K, summed through LDS at the end.
+//    quarter of K, summed through LDS at the end.  Used when K is not a
+//    multiple of 256.
+//  * w8_lds_kernel: the same operands and block shape for K a multiple of
+//    256, with each wavefront's weights brought into a private LDS ring in
+//    runs of 256 contiguous bytes per row (the register kernel's loads cover
+//    16 rows x 64 bytes per instruction, a pattern that streams from HBM
+//    well below the contiguous one).
 
 #include "qmm_device.h"
 
@@ -250,6 +256,138 @@ __global__ __launch_bounds__(NW * 64) void w8_mfma_kernel(const int8_t* __restri
   }
 }
 
+// Staged MFMA kernel for K a multiple of 256.  Same operands and block shape
+// as w8_mfma_kernel (16 rows, four wavefronts over contiguous quarters of
+// K), but a wavefront brings each 256-k step of its 16 rows into a private
+// LDS ring by direct buffer loads of 4 rows x 256 contiguous bytes each
+// (1 KiB per instruction) instead of loading 16 rows x 64 bytes per
+// instruction into registers: the second pattern streams from HBM at well
+// under the first's rate.  Chunk d (16 bytes) of row r sits at
+// position d ^ lds_row_swz(r) of the row's 256 bytes; lane l then reads row
+// l%16, chunk 4(l/16) + c for c = 0..3, a read the swizzle keeps free of
+// bank conflicts.  Weights (two-slot ring) and activations (the B operand,
+// two register sets) are requested one step ahead; lanes of token columns
+// past B load nothing (zeros from past the buffer resource), so at B = 8
+// half the activation loads move no data.
+__host__ __device__ constexpr int lds_row_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+constexpr int kW8StageBytes = 16 * 256;   // 16 rows x 256 k of int8 weights
+
+template <int XDT, int YDT>
+__global__ __launch_bounds__(256) void w8_lds_kernel(const int8_t* __restrict__ qW, const float* __restrict__ w_scale,
+                                                     int64_t N, int64_t K, const uint16_t* __restrict__ x, int64_t B,
+                                                     void* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kW8Waves][2][kW8StageBytes];
+  __shared__ float red[kW8Waves][4][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int l16 = lane & 15;
+  const int quad = lane >> 4;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int nrows = static_cast<int>((N - row0 < 16) ? N - row0 : 16);
+  const int64_t ta = (l16 < B) ? l16 : B - 1;   // an in-range row; columns past B read zeros (load_x)
+  const int kk = static_cast<int>(K);           // K <= 2^24 (checked on the host)
+  const int nsteps = kk / 256;
+  const int sper = (nsteps + kW8Waves - 1) / kW8Waves;
+  const int sbeg = wave * sper;
+  const int send = (sbeg + sper < nsteps) ? sbeg + sper : nsteps;
+  const int ns = send > sbeg ? send - sbeg : 0;   // this wavefront's steps
+
+  // Rows past N lie past the resource's byte count and read as zero.
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(qW + row0 * K), 0, nrows * kk, kBufferWord3);
+  // Load j of a step: lane L writes LDS bytes [16 L, 16 L + 16) of the
+  // step's kilobyte j, i.e. row 4 j + L/16 at position L%16, which holds
+  // chunk (L%16) ^ lds_row_swz(row).
+  int woff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    woff[j] = r * kk + 16 * ((lane & 15) ^ lds_row_swz(r));
+  }
+  const uint32_t rbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[wave][0][0]));
+  auto issue = [&](int i) {   // step sbeg + i of this wavefront, clamped to its last (a reload, never read)
+    const int st = sbeg + (i < ns ? i : ns - 1);
+    const uint32_t dst = rbase + (i & 1) * kW8StageBytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(uintptr_t)(dst + j * 1024), 16, woff[j], st * 256, 0,
+                                               0);
+  };
+  // Activations through a buffer resource over the B token rows, so that a
+  // step past this wavefront's range, or a token column past B (offset past
+  // the resource), reads zeros.
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), 0, static_cast<int>(B) * kk * 2, kBufferWord3);
+  const int xoff = static_cast<int>(ta * K + 16 * (4 * quad)) * 2;
+  constexpr int kPastX = 1 << 30;   // beyond B * K * 2 <= 2^28 bytes
+  auto load_x = [&](int i, u32x4 (&xv)[4][2]) {   // activations of step i, zeros past the range
+    const int vo = (i < ns && l16 < B) ? xoff + (sbeg + i) * 512 : kPastX;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      xv[c][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, vo + 32 * c, 0, 0));
+      xv[c][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, vo + 32 * c + 16, 0, 0));
+    }
+  };
+  const int rd = l16 * 256;
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](int slot, const u32x4 (&xv)[4][2]) {
+    const uint8_t* stg = &ring[wave][0][0] + slot * kW8StageBytes;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(stg + rd + 16 * ((4 * quad + c) ^ lds_row_swz(l16)));
+      const uint32_t a0[4] = {i8_pair<XDT, 0>(w.x), i8_pair<XDT, 1>(w.x), i8_pair<XDT, 0>(w.y), i8_pair<XDT, 1>(w.y)};
+      const uint32_t a1[4] = {i8_pair<XDT, 0>(w.z), i8_pair<XDT, 1>(w.z), i8_pair<XDT, 0>(w.w), i8_pair<XDT, 1>(w.w)};
+      acc = mfma16x16x32_w8<XDT>(a0, xv[c][0], acc);
+      acc = mfma16x16x32_w8<XDT>(a1, xv[c][1], acc);
+    }
+  };
+  // Steps go in pairs, step i in ring slot i & 1 with activation set i & 1;
+  // each is requested one step ahead, so before step i is computed only step
+  // i + 1's twelve loads (eight activation, four weight) may be in flight.
+  // The second step of a pair is computed even past the range, with zero
+  // activations (its weights: a reload of the last step), so both halves run
+  // unconditionally and their loads stay where they are issued.
+  u32x4 xa[4][2], xb[4][2];
+  if (ns > 0) {
+    load_x(0, xa);
+    issue(0);
+  }
+  for (int i = 0; i < ns; i += 2) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): ring slot 1 has been read
+    load_x(i + 1, xb);
+    issue(i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<12>();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    compute(0, xa);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // ring slot 0 has been read
+    load_x(i + 2, xa);
+    issue(i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<12>();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    compute(1, xb);
+  }
+  wait_vm<0>();
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+  __syncthreads();
+  {
+    const int i = threadIdx.x >> 6;          // 256 threads: one D value each
+    const int l = threadIdx.x & (kWave - 1);
+    const int64_t row = row0 + 4 * (l >> 4) + i;
+    const int64_t t = l & 15;
+    if (row < N && t < B) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kW8Waves; ++w) v += red[w][i][l];
+      store_out<YDT>(y, t * N + row, v * w_scale[row]);
+    }
+  }
+}
+
 template <int XDT, int YDT, int B>
 void launch_w8_b(const int8_t* qW, const float* ws, int64_t N, int64_t K, const uint16_t* x, void* y,
                  hipStream_t s) {
@@ -267,9 +405,13 @@ void launch_w8(int64_t B, const int8_t* qW, const float* ws, int64_t N, int64_t 
   } else if (B == 2) {
     launch_w8_b<XDT, YDT, 2>(qW, ws, N, K, x, y, s);
   } else {
-    // Four wavefronts per block (eight measured no faster on 8192 x 28672).
+    // Four wavefronts per block (eight measured no faster on 8192 x 28672);
+    // whole 256-k steps go through the LDS-staged kernel.
     const dim3 grid(static_cast<unsigned>(ceil_div(N, 16)));
-    w8_mfma_kernel<XDT, YDT, 4><<<grid, dim3(4 * kWave), 0, s>>>(qW, ws, N, K, x, B, y);
+    if (K % 256 == 0)
+      w8_lds_kernel<XDT, YDT><<<grid, dim3(4 * kWave), 0, s>>>(qW, ws, N, K, x, B, y);
+    else
+      w8_mfma_kernel<XDT, YDT, 4><<<grid, dim3(4 * kWave), 0, s>>>(qW, ws, N, K, x, B, y);
   }
 }
 

@@ -45,6 +45,21 @@ def test_w8a16_small(xdt, ysame, B, shape):
     w8_case(q, b, x, TDT[xdt] if ysame else torch.float32, f"small {xdt}")
 
 
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+@pytest.mark.parametrize("ysame", [True, False], ids=["y=x", "y=f32"])
+@pytest.mark.parametrize("B", [3, 5, 8])
+@pytest.mark.parametrize("shape", [(1, 256), (37, 768), (130, 1280), (16, 4352), (45, 8448)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_w8a16_staged(xdt, ysame, B, shape):
+    # K a multiple of 256 (the LDS-staged matrix-core kernel): one step (three
+    # wavefronts idle), three and five steps over four wavefronts (one or two
+    # idle or short), 17 and 33 steps; rows ragged around the 16-row block
+    n, k = shape
+    q, b = random_w8(n, k, seed=n * 11 + k + B)
+    x = workloads.to_dtype(workloads.gaussian(workloads.rng(96, n + k + B), (B, k), 1.0), xdt)
+    w8_case(q, b, x, TDT[xdt] if ysame else torch.float32, f"staged {xdt}")
+
+
 def test_w8a16_extreme_codes():
     # every weight at -128 or 127 and large activations: the fp32 sums of the
     # exact products stay within the bound
