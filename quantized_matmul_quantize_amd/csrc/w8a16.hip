@@ -276,8 +276,9 @@ template <int XDT, int YDT>
 __global__ __launch_bounds__(256) void w8_lds_kernel(const int8_t* __restrict__ qW, const float* __restrict__ w_scale,
                                                      int64_t N, int64_t K, const uint16_t* __restrict__ x, int64_t B,
                                                      void* __restrict__ y) {
+  // 32 KiB per block, so five blocks share a compute unit; the reduction at
+  // the end reuses the ring.
   __shared__ __attribute__((aligned(16))) uint8_t ring[kW8Waves][2][kW8StageBytes];
-  __shared__ float red[kW8Waves][4][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   const int l16 = lane & 15;
@@ -370,7 +371,9 @@ __global__ __launch_bounds__(256) void w8_lds_kernel(const int8_t* __restrict__ 
     compute(1, xb);
   }
   wait_vm<0>();
+  __syncthreads();   // every wavefront is done with its ring
 
+  float (*red)[4][kWave] = reinterpret_cast<float (*)[4][kWave]>(&ring[0][0][0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
   __syncthreads();
