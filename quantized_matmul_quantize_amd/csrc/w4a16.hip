@@ -974,16 +974,17 @@ __global__ __launch_bounds__(NW * 64) void w4_rows_kernel(const uint8_t* __restr
 //  * activations, BM rows x 256 bytes, chunk j of row r at position j ^ row_swz(r);
 //  * codes, 8 slices of 16 rows x 64 bytes, part p of row r at 4 r + (p ^ code_swz(r));
 //  * scales, 256 bytes per wavefront: its 32 rows, loaded twice over.
-// Two blocks of BM = 64 fit a compute unit (about 75 KiB each at K = 4096),
-// so each SIMD interleaves the ALU work of one wavefront with the matrix work
-// of another.  XS: the caller supplies the column sums X_g ([M][G] fp32, the
+// Two slots (one group ahead): three blocks of BM = 64 fit a compute unit
+// (about 51 KiB each at K = 4096), so each SIMD interleaves the ALU work of
+// one wavefront with the matrix work of two others; three slots (75 KiB, two
+// blocks per unit) measured 5-7% slower.  XS: the caller supplies the column sums X_g ([M][G] fp32, the
 // sums of the activations exactly as the kernel reads them); each slot then
 // also holds the tile's BM sums of its group, loaded like the scales, and
 // the wavefronts skip the 4 MT matrix instructions per group that would
 // otherwise recompute them (each of the four wavefronts the same ones).
 // ----------------------------------------------------------------------------
 constexpr int kTileN = 128;
-constexpr int kTileD = 2;
+constexpr int kTileD = 1;
 constexpr int kTileSlots = kTileD + 1;
 
 template <int BM, bool XS = false>
