@@ -977,7 +977,7 @@ __global__ __launch_bounds__(NW * 64) void w4_rows_kernel(const uint8_t* __restr
 // Two slots (one group ahead): three blocks of BM = 64 fit a compute unit
 // (about 51 KiB each at K = 4096), so each SIMD interleaves the ALU work of
 // one wavefront with the matrix work of two others; three slots (75 KiB, two
-// blocks per unit) measured 5-7% slower.  XS: the caller supplies the column sums X_g ([M][G] fp32, the
+// blocks per unit) measured slower (AWQ's M = 2048 products by ~7%).  XS: the caller supplies the column sums X_g ([M][G] fp32, the
 // sums of the activations exactly as the kernel reads them); each slot then
 // also holds the tile's BM sums of its group, loaded like the scales, and
 // the wavefronts skip the 4 MT matrix instructions per group that would
