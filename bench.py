@@ -853,8 +853,9 @@ def main():
     # back to back as in the step, each pair right after a 1 GiB read with
     # ordinary loads (torch's max reduction), which allocate in the
     # last-level cache and so evict whatever the GEMVs could find there.
-    # The GEMVs' own nontemporal loads do not displace it, so the in-step
-    # rotation alone could not show this.
+    # The step's streaming kernels read with nontemporal loads, which
+    # allocate little in that cache, so the bytes counted by the in-step
+    # rotation do not by themselves prove it cold.
     flush_src = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     head = [op for op in ops if op["name"] in gemv1]
     fl = []
